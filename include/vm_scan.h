@@ -1,0 +1,179 @@
+/*
+ * vm_scan.h -- C ABI of the selective-scan hot path for vision Mamba
+ * backbones (Vim bidirectional blocks, EfficientVMamba atrous ES2D, FastVim
+ * pooled scan) on AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensors are dense, contiguous, row-major, in the shapes given at each
+ *    call, and live in device memory of the current HIP device.  The caller
+ *    owns every buffer; the library never frees or keeps a pointer past the
+ *    call.  Outputs must not overlap any input (checked: VM_ERR_ALIAS).
+ *  - dtype selects the storage of the token tensors (u, delta, z, B, C, x,
+ *    streams, out): VM_F32 or VM_BF16.  A, D and delta_bias are always fp32.
+ *    Arithmetic is fp32 (bf16 inputs are widened exactly; bf16 outputs are
+ *    rounded to nearest even).  BF16 B and C must be 4-byte aligned.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *    default stream).  Argument checks run on the host first and nothing is
+ *    launched when they fail.  Kernel-side faults surface at the caller's next
+ *    synchronisation; VM_ERR_HIP reports a launch failure.
+ *  - No data-dependent checks run on the device: A <= 0, finite inputs and a
+ *    non-negative step size are preconditions of the method, and NaN / Inf
+ *    propagate by IEEE rules.
+ *  - Some calls need temporary device memory (noted at the call); it comes
+ *    from a stream-ordered pool owned by the library and is released on the
+ *    same stream before the call returns (VM_ERR_ALLOC if unavailable).
+ *  - Calls are thread-safe.
+ *
+ * The pages this follows (cited by title and section):
+ *  [Vim]  "Vision Mamba: Bidirectional State Space Models for Images"
+ *  [EVM]  "EfficientVMamba: Atrous Selective Scan for Light Weight Visual Mamba"
+ *  [FVim] "Fast Vision Mamba: Pooling Spatial Dimensions for Accelerated
+ *         Processing"
+ */
+#ifndef VM_SCAN_H
+#define VM_SCAN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of token tensors. */
+enum { VM_F32 = 0, VM_BF16 = 1 };
+
+/* Status codes returned by every entry point. */
+enum {
+  VM_OK = 0,
+  VM_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  VM_ERR_SHAPE = 2,       /* a size is <= 0, or an element count overflows   */
+  VM_ERR_DTYPE = 3,       /* unknown dtype                                    */
+  VM_ERR_FLAG = 4,        /* a flag is not 0/1, or pool_axis not 0/1          */
+  VM_ERR_ALIAS = 5,       /* the output overlaps an input                     */
+  VM_ERR_UNSUPPORTED = 6, /* dstate outside [1, 16], or a non-finite scale    */
+  VM_ERR_HIP = 7,         /* a HIP launch or runtime call failed              */
+  VM_ERR_ALLOC = 8,       /* temporary device memory could not be obtained    */
+  VM_ERR_ALIGN = 9        /* a bf16 B or C pointer is not 4-byte aligned      */
+};
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *vm_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int vm_version(void);
+
+/*
+ * One scan direction, in the argument order of the selective-scan function
+ * on [Vim] implementation row 4 ("Keep a running state, then read it"):
+ *   u           [batch, dim, seqlen]    token content (dtype)
+ *   delta       [batch, dim, seqlen]    step-size pre-activation (dtype),
+ *                                       before bias and softplus
+ *   A           [dim, dstate]  fp32     decay; A = -exp(A_log), so A <= 0
+ *   B, C        [batch, dstate, seqlen] input write / output read (dtype),
+ *                                       shared by all channels of a batch row
+ *   D           [dim]          fp32     direct skip (required)
+ *   delta_bias  [dim]          fp32     added to delta before softplus; NULL = 0
+ * For vm_pool_scan_repeat the shapes differ (see there).
+ */
+typedef struct vm_scan_dir {
+  const void *u;
+  const void *delta;
+  const float *A;
+  const void *B;
+  const void *C;
+  const float *D;
+  const float *delta_bias;
+} vm_scan_dir;
+
+/*
+ * Selective scan, one direction ([Vim] "A state retains, writes, and reads"
+ * and implementation row 4).  For every (b, d), from a zero state:
+ *   dt_t   = softplus(delta_t + bias_d)   (delta_softplus = 1)
+ *          = delta_t + bias_d             (delta_softplus = 0)
+ *   h_t,n  = exp(dt_t A_d,n) h_t-1,n + dt_t B_b,n,t u_t
+ *   y_t    = sum_n C_b,n,t h_t,n + D_d u_t
+ *   out_t  = y_t * SiLU(z_t)   (z != NULL),   y_t otherwise
+ * reverse = 1 visits t = seqlen-1 .. 0 instead, which equals reversing every
+ * token tensor, scanning forward and reversing the result ([Vim] "Two scans
+ * meet at the same token").  All tensors stay in original token order.
+ *   z, out: [batch, dim, seqlen] (dtype).  dstate in [1, 16].
+ */
+int vm_selective_scan_fwd(const vm_scan_dir *p, const void *z, void *out,
+                          int64_t batch, int64_t dim, int64_t seqlen,
+                          int64_t dstate, int dtype, int delta_softplus,
+                          int reverse, void *stream);
+
+/*
+ * Bidirectional scan with the aligned combine and shared gate ([Vim] "Two
+ * scans meet at the same token", "Inside the released Vim block",
+ * implementation row 5):
+ *   out = combine_scale * (y_fwd + y_bwd) * SiLU(z)
+ * y_fwd is the forward scan of `fwd`; y_bwd is the reversed-order scan of
+ * `bwd` (its own u, delta, A, B, C, D, bias), returned in original order.
+ * combine_scale = 0.5 is the released averaging model, 1 the summed form.
+ * z may be NULL (no gate).  out: [batch, dim, seqlen] (dtype).
+ * Long sequences (seqlen > 256) take temporary fp32 memory of
+ * batch*dim*seqlen*4 bytes when dtype is VM_BF16.
+ */
+int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
+                      const void *z, float combine_scale, void *out,
+                      int64_t batch, int64_t dim, int64_t seqlen,
+                      int64_t dstate, int dtype, int delta_softplus,
+                      void *stream);
+
+/*
+ * Number of steps of each p = 2 atrous group: ceil(H/2) * ceil(W/2)
+ * ([EVM] implementation row 1).  Returns -VM_ERR_SHAPE for H or W <= 0.
+ * Pure host function.
+ */
+int64_t vm_atrous_group_len(int64_t height, int64_t width);
+
+/*
+ * Atrous gather, p = 2 ([EVM] "Four shorter sequences, one dense output",
+ * implementation row 1).  x [batch, channels, H, W] -> streams
+ * [batch, 4, channels, Lg].  Group k has offset (row, col) = (0,0), (1,0),
+ * (0,1), (1,1); groups 0 and 2 walk the half grid row-major, 1 and 3
+ * column-major.  The map is padded right/bottom to even size; padded steps
+ * hold +0.0.  A bit-exact copy.
+ */
+int vm_atrous_gather(const void *x, void *streams, int64_t batch,
+                     int64_t channels, int64_t height, int64_t width,
+                     int dtype, void *stream);
+
+/*
+ * Atrous scatter / merge ([EVM] "Merge restores coordinates instead of adding
+ * directions", implementation row 3): the inverse routing, then a crop of the
+ * padding.  streams [batch, 4, channels, Lg] -> y [batch, channels, H, W];
+ * each valid coordinate takes its single owner's value; nothing is summed.
+ * A bit-exact copy.
+ */
+int vm_atrous_scatter(const void *streams, void *y, int64_t batch,
+                      int64_t channels, int64_t height, int64_t width,
+                      int dtype, void *stream);
+
+/*
+ * FastVim pooled scan ([FVim] "Methodology"): mean-pool u over one spatial
+ * axis, run the selective scan on the pooled tokens (forward, plus backward
+ * when bwd != NULL), repeat the result along the pooled axis, gate with the
+ * full-resolution SiLU(z):
+ *   out[b,d,i,j] = combine_scale * (y_fwd + y_bwd)[b,d,p] * SiLU(z[b,d,i,j])
+ *   p = i, Lp = H for pool_axis = 0 (mean over W)
+ *   p = j, Lp = W for pool_axis = 1 (mean over H)
+ * Per direction: u [batch, dim, H, W] (full resolution), delta [batch, dim,
+ * Lp], B and C [batch, dstate, Lp] (the pooled tokens' projections), A, D,
+ * delta_bias as for vm_selective_scan_fwd.  The D skip acts on the pooled u.
+ * z, out: [batch, dim, H, W].  z may be NULL.  Takes temporary fp32 memory of
+ * 3*batch*dim*Lp*4 bytes.
+ */
+int vm_pool_scan_repeat(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
+                        const void *z, float combine_scale, void *out,
+                        int64_t batch, int64_t dim, int64_t height,
+                        int64_t width, int64_t dstate, int pool_axis,
+                        int dtype, int delta_softplus, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VM_SCAN_H */

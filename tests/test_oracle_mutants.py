@@ -1,0 +1,51 @@
+"""Plants plausible mistakes in a copy of the oracle's C source (on the CPU)
+and checks that the oracle pins in test_oracle.py catch every one of them."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "vm_oracle.c")
+
+# (name, original text, planted mistake)
+MUTANTS = [
+    ("drop_D_skip", "y[t] = acc + D * u[t];", "y[t] = acc;"),
+    ("exp_sign", "double retain = exp(dt * A[n]);", "double retain = exp(-dt * A[n]);"),
+    ("B_C_swapped", "double write = dt * B[n * L + t] * u[t];", "double write = dt * C[n * L + t] * u[t];"),
+    ("bias_dropped", "double x = delta[t] + bias;", "double x = delta[t];"),
+    ("read_before_update", "      h[n] = retain * h[n] + write;\n      acc += C[n * L + t] * h[n];",
+     "      acc += C[n * L + t] * h[n];\n      h[n] = retain * h[n] + write;"),
+    ("no_softplus", "return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));", "return x;"),
+    ("reverse_keeps_B_order", "flip_rows(Bb, Bf, N, L);", "memcpy(Bf, Bb, sizeof(double) * (size_t)(N * L));"),
+    ("gate_is_sigmoid", "return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
+    ("bidir_no_scale", "double y = (yf[i] + yb[i]) * scale;", "double y = (yf[i] + yb[i]);"),
+    ("bidir_bwd_not_reversed", "N, delta_softplus, 1, yb);\n  if (s == 0)\n    for",
+     "N, delta_softplus, 0, yb);\n  if (s == 0)\n    for"),
+    ("odd_groups_row_major", "if (group % 2 == 0) {", "if (1) {"),
+    ("offsets_swapped", "static const int off_row[4] = {0, 1, 0, 1};", "static const int off_row[4] = {0, 0, 1, 1};"),
+    ("pad_not_zero", "? plane[rr[t] * W + cc[t]] : 0.0;", "? plane[rr[t] * W + cc[t]] : 1.0;"),
+    ("pool_wrong_extent", "pooled[r * H + i] = s / (double)W;", "pooled[r * H + i] = s / (double)H;"),
+    ("repeat_wrong_axis", "int64_t p = axis == 0 ? i : j;", "int64_t p = axis == 0 ? (j % Lp) : (i % Lp);"),
+]
+
+
+def test_mutant_list_applies():
+    src = open(SRC).read()
+    for name, old, new in MUTANTS:
+        assert src.count(old) == 1, name
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    src = open(SRC).read().replace(old, new)
+    c = tmp_path / "mutant.c"
+    c.write_text(src)
+    so = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", str(c), "-o", str(so), "-lm"])
+    env = dict(os.environ, VM_ORACLE_LIB=str(so), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutant {name} survived the oracle pins:\n{r.stdout[-2000:]}"
