@@ -12,7 +12,7 @@
  *  - dtype selects the storage of the token tensors (u, delta, z, B, C, x,
  *    streams, out): VM_F32 or VM_BF16.  A, D and delta_bias are always fp32.
  *    Arithmetic is fp32 (bf16 inputs are widened exactly; bf16 outputs are
- *    rounded to nearest even).  BF16 B and C must be 4-byte aligned.
+ *    rounded to nearest even).
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *    default stream).  Argument checks run on the host first and nothing is
  *    launched when they fail.  Kernel-side faults surface at the caller's next
@@ -53,8 +53,7 @@ enum {
   VM_ERR_ALIAS = 5,       /* the output overlaps an input                     */
   VM_ERR_UNSUPPORTED = 6, /* dstate outside [1, 16], or a non-finite scale    */
   VM_ERR_HIP = 7,         /* a HIP launch or runtime call failed              */
-  VM_ERR_ALLOC = 8,       /* temporary device memory could not be obtained    */
-  VM_ERR_ALIGN = 9        /* a bf16 B or C pointer is not 4-byte aligned      */
+  VM_ERR_ALLOC = 8        /* temporary device memory could not be obtained    */
 };
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -98,6 +97,7 @@ typedef struct vm_scan_dir {
  * token tensor, scanning forward and reversing the result ([Vim] "Two scans
  * meet at the same token").  All tensors stay in original token order.
  *   z, out: [batch, dim, seqlen] (dtype).  dstate in [1, 16].
+ * Temporary memory: with VM_BF16, fp32 copies of B and C.
  */
 int vm_selective_scan_fwd(const vm_scan_dir *p, const void *z, void *out,
                           int64_t batch, int64_t dim, int64_t seqlen,
@@ -113,8 +113,9 @@ int vm_selective_scan_fwd(const vm_scan_dir *p, const void *z, void *out,
  * `bwd` (its own u, delta, A, B, C, D, bias), returned in original order.
  * combine_scale = 0.5 is the released averaging model, 1 the summed form.
  * z may be NULL (no gate).  out: [batch, dim, seqlen] (dtype).
- * Long sequences (seqlen > 256) take temporary fp32 memory of
- * batch*dim*seqlen*4 bytes when dtype is VM_BF16.
+ * Temporary memory: with VM_BF16, fp32 copies of the four B/C tensors; for
+ * sequences too long for the on-chip exchange buffer (seqlen > ~250), an fp32
+ * [batch, dim, seqlen] exchange buffer (VM_F32 reuses `out` for it).
  */
 int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
                       const void *z, float combine_scale, void *out,
@@ -163,8 +164,9 @@ int vm_atrous_scatter(const void *streams, void *y, int64_t batch,
  * Per direction: u [batch, dim, H, W] (full resolution), delta [batch, dim,
  * Lp], B and C [batch, dstate, Lp] (the pooled tokens' projections), A, D,
  * delta_bias as for vm_selective_scan_fwd.  The D skip acts on the pooled u.
- * z, out: [batch, dim, H, W].  z may be NULL.  Takes temporary fp32 memory of
- * 3*batch*dim*Lp*4 bytes.
+ * z, out: [batch, dim, H, W].  z may be NULL.  Temporary memory: fp32
+ * [batch, dim, Lp] buffers for the pooled u of each direction and the scan
+ * result (plus fp32 copies of delta, B and C with VM_BF16).
  */
 int vm_pool_scan_repeat(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
                         const void *z, float combine_scale, void *out,

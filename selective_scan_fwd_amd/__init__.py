@@ -1,0 +1,251 @@
+"""Selective-scan hot path for vision Mamba backbones on AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/vm_scan.h (libvmscan.so, built
+in-tree by ``selective_scan_fwd_amd.build``).  The functions here only check
+tensor shapes / dtypes / devices and marshal pointers; every step of the
+computation runs in the library's HIP kernels on the current torch stream.
+PyTorch supplies device memory and the stream.  There is no fallback: if the
+library is missing or fails to load, every call raises.
+
+Names and argument order follow the C ABI:
+  vm_selective_scan_fwd, vm_bidir_scan_fwd, vm_atrous_gather,
+  vm_atrous_scatter, vm_pool_scan_repeat, vm_atrous_group_len.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libvmscan.so")
+
+VM_F32, VM_BF16 = 0, 1
+VM_OK = 0
+STATUS_NAMES = {0: "VM_OK", 1: "VM_ERR_NULL", 2: "VM_ERR_SHAPE", 3: "VM_ERR_DTYPE", 4: "VM_ERR_FLAG",
+                5: "VM_ERR_ALIAS", 6: "VM_ERR_UNSUPPORTED", 7: "VM_ERR_HIP", 8: "VM_ERR_ALLOC"}
+
+EXPORTED = ("vm_status_string", "vm_version", "vm_selective_scan_fwd", "vm_bidir_scan_fwd",
+            "vm_atrous_group_len", "vm_atrous_gather", "vm_atrous_scatter", "vm_pool_scan_repeat")
+
+
+class VmScanDir(ctypes.Structure):
+    """struct vm_scan_dir (one scan direction's device pointers)."""
+    _fields_ = [("u", ctypes.c_void_p), ("delta", ctypes.c_void_p), ("A", ctypes.c_void_p),
+                ("B", ctypes.c_void_p), ("C", ctypes.c_void_p), ("D", ctypes.c_void_p),
+                ("delta_bias", ctypes.c_void_p)]
+
+
+class VmError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library():
+    """Load libvmscan.so and declare the C signatures.  Raises if absent."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is not built; run selective_scan_fwd_amd.build.build() "
+                                   "(or __graft_entry__.build()) first")
+            lib = ctypes.CDLL(LIB_PATH)
+            P, I64, I, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+            D = ctypes.POINTER(VmScanDir)
+            lib.vm_status_string.argtypes = [I]
+            lib.vm_status_string.restype = ctypes.c_char_p
+            lib.vm_version.argtypes = []
+            lib.vm_version.restype = I
+            lib.vm_selective_scan_fwd.argtypes = [D, P, P, I64, I64, I64, I64, I, I, I, P]
+            lib.vm_bidir_scan_fwd.argtypes = [D, D, P, F, P, I64, I64, I64, I64, I, I, P]
+            lib.vm_atrous_group_len.argtypes = [I64, I64]
+            lib.vm_atrous_group_len.restype = I64
+            lib.vm_atrous_gather.argtypes = [P, P, I64, I64, I64, I64, I, P]
+            lib.vm_atrous_scatter.argtypes = [P, P, I64, I64, I64, I64, I, P]
+            lib.vm_pool_scan_repeat.argtypes = [D, D, P, F, P, I64, I64, I64, I64, I64, I, I, I, P]
+            for name in ("vm_selective_scan_fwd", "vm_bidir_scan_fwd", "vm_atrous_gather",
+                         "vm_atrous_scatter", "vm_pool_scan_repeat"):
+                getattr(lib, name).restype = I
+            _lib = lib
+    return _lib
+
+
+def vm_status_string(status: int) -> str:
+    return load_library().vm_status_string(int(status)).decode()
+
+
+def vm_version() -> int:
+    return int(load_library().vm_version())
+
+
+def _check(status, what):
+    if status != VM_OK:
+        raise VmError(status, f"{what}: {vm_status_string(status)}")
+
+
+# ---------------------------------------------------------------- marshalling
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return VM_F32
+    if t.dtype == torch.bfloat16:
+        return VM_BF16
+    raise TypeError(f"token tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _direction(p, batch, dim, u_shape, tok_len, dstate, dt, device, name):
+    """Validate one direction dict and return (VmScanDir, keepalive)."""
+    u = _dev(p["u"], f"{name}.u", dt, u_shape, device)
+    delta = _dev(p["delta"], f"{name}.delta", dt, (batch, dim, tok_len), device)
+    A = _dev(p["A"], f"{name}.A", torch.float32, (dim, dstate), device)
+    B = _dev(p["B"], f"{name}.B", dt, (batch, dstate, tok_len), device)
+    C = _dev(p["C"], f"{name}.C", dt, (batch, dstate, tok_len), device)
+    D = _dev(p["D"], f"{name}.D", torch.float32, (dim,), device)
+    bias = p.get("delta_bias")
+    if bias is not None:
+        bias = _dev(bias, f"{name}.delta_bias", torch.float32, (dim,), device)
+    s = VmScanDir(u.data_ptr(), delta.data_ptr(), A.data_ptr(), B.data_ptr(), C.data_ptr(),
+                  D.data_ptr(), bias.data_ptr() if bias is not None else None)
+    return s, (u, delta, A, B, C, D, bias)
+
+
+# ---------------------------------------------------------------- entry points
+def vm_selective_scan_fwd(u, delta, A, B, C, D, z=None, delta_bias=None, delta_softplus=True,
+                          reverse=False, out=None):
+    """One-direction selective scan; returns out shaped like u.
+    u, delta, z: [batch, dim, L]; A: [dim, N] fp32; B, C: [batch, N, L];
+    D, delta_bias: [dim] fp32.  reverse=True visits t = L-1 .. 0."""
+    dt = u.dtype
+    batch, dim, L = u.shape
+    N = A.shape[-1]
+    d, keep = _direction(dict(u=u, delta=delta, A=A, B=B, C=C, D=D, delta_bias=delta_bias),
+                         batch, dim, (batch, dim, L), L, N, dt, u.device, "p")
+    if z is not None:
+        _dev(z, "z", dt, u.shape, u.device)
+    out = torch.empty_like(u) if out is None else _dev(out, "out", dt, u.shape, u.device)
+    with torch.cuda.device(u.device):
+        st = load_library().vm_selective_scan_fwd(ctypes.byref(d), _ptr(z), _ptr(out), batch, dim, L, N,
+                                                  _dtype_code(u), int(bool(delta_softplus)),
+                                                  int(bool(reverse)), _stream(u.device))
+    _check(st, "vm_selective_scan_fwd")
+    return out
+
+
+def vm_bidir_scan_fwd(fwd, bwd, z=None, combine_scale=1.0, delta_softplus=True, out=None):
+    """Bidirectional scan: combine_scale * (y_fwd + y_bwd) * SiLU(z).
+    fwd / bwd: dicts with u, delta, A, B, C, D, delta_bias (original token order)."""
+    u = fwd["u"]
+    dt = u.dtype
+    batch, dim, L = u.shape
+    N = fwd["A"].shape[-1]
+    df, kf = _direction(fwd, batch, dim, (batch, dim, L), L, N, dt, u.device, "fwd")
+    db, kb = _direction(bwd, batch, dim, (batch, dim, L), L, N, dt, u.device, "bwd")
+    if z is not None:
+        _dev(z, "z", dt, u.shape, u.device)
+    out = torch.empty_like(u) if out is None else _dev(out, "out", dt, u.shape, u.device)
+    with torch.cuda.device(u.device):
+        st = load_library().vm_bidir_scan_fwd(ctypes.byref(df), ctypes.byref(db), _ptr(z),
+                                              float(combine_scale), _ptr(out), batch, dim, L, N,
+                                              _dtype_code(u), int(bool(delta_softplus)),
+                                              _stream(u.device))
+    _check(st, "vm_bidir_scan_fwd")
+    return out
+
+
+def vm_atrous_group_len(height: int, width: int) -> int:
+    n = int(load_library().vm_atrous_group_len(int(height), int(width)))
+    if n < 0:
+        raise VmError(-n, f"vm_atrous_group_len: {vm_status_string(-n)}")
+    return n
+
+
+def vm_atrous_gather(x, out=None):
+    """x [batch, ch, H, W] -> streams [batch, 4, ch, ceil(H/2)*ceil(W/2)]."""
+    _dev(x, "x")
+    batch, ch, H, W = x.shape
+    shape = (batch, 4, ch, vm_atrous_group_len(H, W))
+    out = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else \
+        _dev(out, "streams", x.dtype, shape, x.device)
+    with torch.cuda.device(x.device):
+        st = load_library().vm_atrous_gather(_ptr(x), _ptr(out), batch, ch, H, W, _dtype_code(x),
+                                             _stream(x.device))
+    _check(st, "vm_atrous_gather")
+    return out
+
+
+def vm_atrous_scatter(streams, height, width, out=None):
+    """streams [batch, 4, ch, Lg] -> y [batch, ch, height, width]."""
+    _dev(streams, "streams")
+    batch, four, ch, Lg = streams.shape
+    if four != 4 or Lg != vm_atrous_group_len(height, width):
+        raise ValueError("streams must be [batch, 4, ch, ceil(H/2)*ceil(W/2)]")
+    shape = (batch, ch, height, width)
+    out = torch.empty(shape, dtype=streams.dtype, device=streams.device) if out is None else \
+        _dev(out, "y", streams.dtype, shape, streams.device)
+    with torch.cuda.device(streams.device):
+        st = load_library().vm_atrous_scatter(_ptr(streams), _ptr(out), batch, ch, height, width,
+                                              _dtype_code(streams), _stream(streams.device))
+    _check(st, "vm_atrous_scatter")
+    return out
+
+
+def vm_pool_scan_repeat(fwd, bwd=None, z=None, combine_scale=1.0, pool_axis=0, delta_softplus=True,
+                        out=None):
+    """FastVim pooled scan.  Per direction: u [batch, dim, H, W], delta
+    [batch, dim, Lp], B/C [batch, N, Lp] (Lp = H for pool_axis 0, W for 1).
+    Returns [batch, dim, H, W]."""
+    u = fwd["u"]
+    dt = u.dtype
+    batch, dim, H, W = u.shape
+    Lp = H if pool_axis == 0 else W
+    N = fwd["A"].shape[-1]
+    df, kf = _direction(fwd, batch, dim, (batch, dim, H, W), Lp, N, dt, u.device, "fwd")
+    pb = None
+    if bwd is not None:
+        db, kb = _direction(bwd, batch, dim, (batch, dim, H, W), Lp, N, dt, u.device, "bwd")
+        pb = ctypes.byref(db)
+    if z is not None:
+        _dev(z, "z", dt, u.shape, u.device)
+    out = torch.empty_like(u) if out is None else _dev(out, "out", dt, u.shape, u.device)
+    with torch.cuda.device(u.device):
+        st = load_library().vm_pool_scan_repeat(ctypes.byref(df), pb, _ptr(z), float(combine_scale),
+                                                _ptr(out), batch, dim, H, W, N, int(pool_axis),
+                                                _dtype_code(u), int(bool(delta_softplus)),
+                                                _stream(u.device))
+    _check(st, "vm_pool_scan_repeat")
+    return out
+
+
+__all__ = ["vm_selective_scan_fwd", "vm_bidir_scan_fwd", "vm_atrous_gather", "vm_atrous_scatter",
+           "vm_pool_scan_repeat", "vm_atrous_group_len", "vm_status_string", "vm_version",
+           "VmScanDir", "VmError", "load_library", "LIB_PATH", "EXPORTED"]

@@ -1,0 +1,347 @@
+// C ABI of the selective-scan library (declared in include/vm_scan.h):
+// host-side argument checks, temporary memory from a library-owned
+// stream-ordered pool, and kernel dispatch.  Every check runs before any HIP
+// call, so a rejected call launches nothing and touches no device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <vector>
+
+#include "vm_internal.h"
+#include "vm_scan.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+constexpr int64_t kMaxElems = int64_t{1} << 40;
+
+struct Span {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi)
+};
+Span span(const void *p, int64_t bytes) {
+  Span s;
+  if (p != nullptr) {
+    s.lo = reinterpret_cast<uintptr_t>(p);
+    s.hi = s.lo + static_cast<uintptr_t>(bytes);
+  }
+  return s;
+}
+bool overlaps(Span a, Span b) { return a.lo != 0 && b.lo != 0 && a.lo < b.hi && b.lo < a.hi; }
+
+bool dims_ok(std::initializer_list<int64_t> dims, int64_t *prod) {
+  int64_t p = 1;
+  for (int64_t d : dims) {
+    if (d <= 0 || d > kMaxDim) return false;
+    if (p > kMaxElems / d) return false;
+    p *= d;
+  }
+  *prod = p;
+  return true;
+}
+
+bool flag_ok(int f) { return f == 0 || f == 1; }
+
+// Checks of one scan direction.  u_elems / tok_elems: elements of u and of
+// delta; bc_elems: elements of B and C; dim, dstate: parameter shapes.
+int check_dir(const vm_scan_dir *p, int64_t u_elems, int64_t tok_elems, int64_t bc_elems,
+              int64_t dim, int64_t dstate, int esize, Span out, bool bias_ok_null = true) {
+  (void)bias_ok_null;
+  if (p == nullptr || p->u == nullptr || p->delta == nullptr || p->A == nullptr ||
+      p->B == nullptr || p->C == nullptr || p->D == nullptr)
+    return VM_ERR_NULL;
+  const Span ins[] = {span(p->u, u_elems * esize), span(p->delta, tok_elems * esize),
+                      span(p->A, dim * dstate * 4), span(p->B, bc_elems * esize),
+                      span(p->C, bc_elems * esize), span(p->D, dim * 4),
+                      span(p->delta_bias, dim * 4)};
+  for (const Span &s : ins)
+    if (overlaps(s, out)) return VM_ERR_ALIAS;
+  return VM_OK;
+}
+
+// ---------------------------------------------------------------- workspace
+std::mutex g_pool_mu;
+std::map<int, hipMemPool_t> g_pools;
+
+hipError_t pool_for_current_device(hipMemPool_t *out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_pool_mu);
+  auto it = g_pools.find(dev);
+  if (it != g_pools.end()) {
+    *out = it->second;
+    return hipSuccess;
+  }
+  hipMemPoolProps props = {};
+  props.allocType = hipMemAllocationTypePinned;
+  props.handleTypes = hipMemHandleTypeNone;
+  props.location.type = hipMemLocationTypeDevice;
+  props.location.id = dev;
+  hipMemPool_t pool;
+  e = hipMemPoolCreate(&pool, &props);
+  if (e != hipSuccess) return e;
+  uint64_t keep = UINT64_MAX;  // keep freed blocks cached for the next call
+  e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+  if (e != hipSuccess) return e;
+  g_pools[dev] = pool;
+  *out = pool;
+  return hipSuccess;
+}
+
+// Temporary fp32 buffers that live on `stream` for the duration of one call.
+class Scratch {
+ public:
+  explicit Scratch(hipStream_t s) : s_(s) {}
+  ~Scratch() {
+    for (void *p : ptrs_) (void)hipFreeAsync(p, s_);
+  }
+  float *get(int64_t floats, int *status) {
+    if (*status != VM_OK) return nullptr;
+    hipMemPool_t pool;
+    void *p = nullptr;
+    if (pool_for_current_device(&pool) != hipSuccess ||
+        hipMallocFromPoolAsync(&p, static_cast<size_t>(floats) * 4, pool, s_) != hipSuccess) {
+      (void)hipGetLastError();
+      *status = VM_ERR_ALLOC;
+      return nullptr;
+    }
+    ptrs_.push_back(p);
+    return static_cast<float *>(p);
+  }
+
+ private:
+  hipStream_t s_;
+  std::vector<void *> ptrs_;
+};
+
+int hip_status(hipError_t e) { return e == hipSuccess ? VM_OK : VM_ERR_HIP; }
+
+// fp32 view of a token tensor: the tensor itself (fp32) or a widened copy.
+const float *as_f32(const void *src, int64_t n, bool bf16, Scratch &ws, hipStream_t s,
+                    int *status) {
+  if (!bf16) return static_cast<const float *>(src);
+  float *dst = ws.get(n, status);
+  if (*status == VM_OK) *status = hip_status(vmk::launch_to_f32(src, dst, n, s));
+  return dst;
+}
+
+// B and C of one direction packed step-major into fp32 [batch, L, 32].
+const float *pack_bc(const vm_scan_dir *p, int64_t batch, int64_t dstate, int64_t L, bool bf16,
+                     Scratch &ws, hipStream_t s, int *status) {
+  float *bc = ws.get(batch * L * vmk::kBCStride, status);
+  if (*status == VM_OK)
+    *status = hip_status(vmk::launch_bc_pack(p->B, p->C, bc, batch, dstate, L, bf16, s));
+  return bc;
+}
+
+vmk::DirPtrs dir_ptrs(const vm_scan_dir *p, const float *BC) {
+  vmk::DirPtrs d;
+  d.u = p->u;
+  d.delta = p->delta;
+  d.A = p->A;
+  d.BC = BC;
+  d.D = p->D;
+  d.bias = p->delta_bias;
+  return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *vm_status_string(int status) {
+  switch (status) {
+    case VM_OK: return "VM_OK";
+    case VM_ERR_NULL: return "VM_ERR_NULL: a required pointer is NULL";
+    case VM_ERR_SHAPE: return "VM_ERR_SHAPE: a size is <= 0 or an element count overflows";
+    case VM_ERR_DTYPE: return "VM_ERR_DTYPE: unknown dtype";
+    case VM_ERR_FLAG: return "VM_ERR_FLAG: a flag is not 0 or 1";
+    case VM_ERR_ALIAS: return "VM_ERR_ALIAS: the output overlaps an input";
+    case VM_ERR_UNSUPPORTED: return "VM_ERR_UNSUPPORTED: dstate outside [1, 16] or non-finite scale";
+    case VM_ERR_HIP: return "VM_ERR_HIP: a HIP launch or runtime call failed";
+    case VM_ERR_ALLOC: return "VM_ERR_ALLOC: temporary device memory unavailable";
+    default: return "unknown status";
+  }
+}
+
+int vm_version(void) { return 10000; }
+
+int64_t vm_atrous_group_len(int64_t height, int64_t width) {
+  if (height <= 0 || width <= 0 || height > kMaxDim || width > kMaxDim) return -VM_ERR_SHAPE;
+  return ((height + 1) / 2) * ((width + 1) / 2);
+}
+
+int vm_selective_scan_fwd(const vm_scan_dir *p, const void *z, void *out, int64_t batch,
+                          int64_t dim, int64_t seqlen, int64_t dstate, int dtype,
+                          int delta_softplus, int reverse, void *stream) {
+  if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;
+  if (!flag_ok(delta_softplus) || !flag_ok(reverse)) return VM_ERR_FLAG;
+  int64_t tok = 0, bc = 0;
+  if (!dims_ok({batch, dim, seqlen}, &tok) || dstate <= 0) return VM_ERR_SHAPE;
+  if (dstate > 16) return VM_ERR_UNSUPPORTED;
+  if (!dims_ok({batch, dstate, seqlen}, &bc)) return VM_ERR_SHAPE;
+  if (out == nullptr) return VM_ERR_NULL;
+  const int es = dtype == VM_BF16 ? 2 : 4;
+  const Span so = span(out, tok * es);
+  int st = check_dir(p, tok, tok, bc, dim, dstate, es, so);
+  if (st != VM_OK) return st;
+  if (overlaps(span(z, tok * es), so)) return VM_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == VM_BF16;
+  Scratch ws(s);
+  const float *BC = pack_bc(p, batch, dstate, seqlen, bf16, ws, s, &st);
+  if (st != VM_OK) return st;
+  vmk::ScanArgs a = {};
+  a.dir[0] = a.dir[1] = dir_ptrs(p, BC);
+  a.z = z;
+  a.out = out;
+  a.batch = batch;
+  a.dim = dim;
+  a.L = seqlen;
+  a.dstate = static_cast<int>(dstate);
+  a.softplus = delta_softplus;
+  a.reverse = reverse;
+  a.scale = 1.0f;
+  const vmk::ScanPlan plan = vmk::plan_scan(batch, dim, seqlen, a.dstate, 1);
+  return hip_status(vmk::launch_scan(plan, a, bf16, s));
+}
+
+int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void *z,
+                      float combine_scale, void *out, int64_t batch, int64_t dim,
+                      int64_t seqlen, int64_t dstate, int dtype, int delta_softplus,
+                      void *stream) {
+  if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;
+  if (!flag_ok(delta_softplus)) return VM_ERR_FLAG;
+  int64_t tok = 0, bc = 0;
+  if (!dims_ok({batch, dim, seqlen}, &tok) || dstate <= 0) return VM_ERR_SHAPE;
+  if (dstate > 16 || !std::isfinite(combine_scale)) return VM_ERR_UNSUPPORTED;
+  if (!dims_ok({batch, dstate, seqlen}, &bc)) return VM_ERR_SHAPE;
+  if (out == nullptr) return VM_ERR_NULL;
+  const int es = dtype == VM_BF16 ? 2 : 4;
+  const Span so = span(out, tok * es);
+  int st = check_dir(fwd, tok, tok, bc, dim, dstate, es, so);
+  if (st == VM_OK) st = check_dir(bwd, tok, tok, bc, dim, dstate, es, so);
+  if (st != VM_OK) return st;
+  if (overlaps(span(z, tok * es), so)) return VM_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == VM_BF16;
+  Scratch ws(s);
+  const float *BCf = pack_bc(fwd, batch, dstate, seqlen, bf16, ws, s, &st);
+  const float *BCb = pack_bc(bwd, batch, dstate, seqlen, bf16, ws, s, &st);
+  if (st != VM_OK) return st;
+  vmk::ScanArgs a = {};
+  a.dir[0] = dir_ptrs(fwd, BCf);
+  a.dir[1] = dir_ptrs(bwd, BCb);
+  a.z = z;
+  a.out = out;
+  a.batch = batch;
+  a.dim = dim;
+  a.L = seqlen;
+  a.dstate = static_cast<int>(dstate);
+  a.softplus = delta_softplus;
+  a.reverse = 0;
+  a.scale = combine_scale;
+  const vmk::ScanPlan plan = vmk::plan_scan(batch, dim, seqlen, a.dstate, 2);
+  if (plan.xmode == vmk::kXGlobal) {
+    a.xglobal = bf16 ? ws.get(tok, &st) : static_cast<float *>(out);
+    if (st != VM_OK) return st;
+  }
+  return hip_status(vmk::launch_scan(plan, a, bf16, s));
+}
+
+int vm_atrous_gather(const void *x, void *streams, int64_t batch, int64_t channels,
+                     int64_t height, int64_t width, int dtype, void *stream) {
+  if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;
+  int64_t n_in = 0, n_out = 0;
+  const int64_t Lg = vm_atrous_group_len(height, width);
+  if (Lg <= 0 || !dims_ok({batch, channels, height, width}, &n_in) ||
+      !dims_ok({batch, 4, channels, Lg}, &n_out))
+    return VM_ERR_SHAPE;
+  if (x == nullptr || streams == nullptr) return VM_ERR_NULL;
+  const int es = dtype == VM_BF16 ? 2 : 4;
+  if (overlaps(span(x, n_in * es), span(streams, n_out * es))) return VM_ERR_ALIAS;
+  return hip_status(vmk::launch_atrous_gather(x, streams, batch, channels, height, width,
+                                              dtype == VM_BF16, static_cast<hipStream_t>(stream)));
+}
+
+int vm_atrous_scatter(const void *streams, void *y, int64_t batch, int64_t channels,
+                      int64_t height, int64_t width, int dtype, void *stream) {
+  if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;
+  int64_t n_out = 0, n_in = 0;
+  const int64_t Lg = vm_atrous_group_len(height, width);
+  if (Lg <= 0 || !dims_ok({batch, channels, height, width}, &n_out) ||
+      !dims_ok({batch, 4, channels, Lg}, &n_in))
+    return VM_ERR_SHAPE;
+  if (streams == nullptr || y == nullptr) return VM_ERR_NULL;
+  const int es = dtype == VM_BF16 ? 2 : 4;
+  if (overlaps(span(streams, n_in * es), span(y, n_out * es))) return VM_ERR_ALIAS;
+  return hip_status(vmk::launch_atrous_scatter(streams, y, batch, channels, height, width,
+                                               dtype == VM_BF16, static_cast<hipStream_t>(stream)));
+}
+
+int vm_pool_scan_repeat(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void *z,
+                        float combine_scale, void *out, int64_t batch, int64_t dim,
+                        int64_t height, int64_t width, int64_t dstate, int pool_axis,
+                        int dtype, int delta_softplus, void *stream) {
+  if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;
+  if (!flag_ok(delta_softplus) || !flag_ok(pool_axis)) return VM_ERR_FLAG;
+  const int64_t Lp = pool_axis == 0 ? height : width;
+  int64_t full = 0, pooled = 0, bc = 0;
+  if (!dims_ok({batch, dim, height, width}, &full) || !dims_ok({batch, dim, Lp}, &pooled) ||
+      dstate <= 0)
+    return VM_ERR_SHAPE;
+  if (dstate > 16 || !std::isfinite(combine_scale)) return VM_ERR_UNSUPPORTED;
+  if (!dims_ok({batch, dstate, Lp}, &bc)) return VM_ERR_SHAPE;
+  if (out == nullptr) return VM_ERR_NULL;
+  const int es = dtype == VM_BF16 ? 2 : 4;
+  const Span so = span(out, full * es);
+  int st = check_dir(fwd, full, pooled, bc, dim, dstate, es, so);
+  if (st == VM_OK && bwd != nullptr) st = check_dir(bwd, full, pooled, bc, dim, dstate, es, so);
+  if (st != VM_OK) return st;
+  if (overlaps(span(z, full * es), so)) return VM_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == VM_BF16;
+  const int ndir = bwd != nullptr ? 2 : 1;
+  const vm_scan_dir *dirs[2] = {fwd, bwd};
+  Scratch ws(s);
+  float *y = ws.get(pooled, &st);
+  vmk::ScanArgs a = {};
+  for (int k = 0; k < ndir; ++k) {
+    const vm_scan_dir *p = dirs[k];
+    float *ubar = ws.get(pooled, &st);
+    if (st != VM_OK) return st;
+    st = hip_status(vmk::launch_mean_pool(p->u, ubar, batch * dim, height, width, pool_axis,
+                                          bf16, s));
+    const float *dl = as_f32(p->delta, pooled, bf16, ws, s, &st);
+    const float *BC = pack_bc(p, batch, dstate, Lp, bf16, ws, s, &st);
+    if (st != VM_OK) return st;
+    vmk::DirPtrs d = dir_ptrs(p, BC);
+    d.u = ubar;
+    d.delta = dl;
+    a.dir[k] = d;
+  }
+  if (ndir == 1) a.dir[1] = a.dir[0];
+  a.z = nullptr;
+  a.out = y;
+  a.batch = batch;
+  a.dim = dim;
+  a.L = Lp;
+  a.dstate = static_cast<int>(dstate);
+  a.softplus = delta_softplus;
+  a.reverse = 0;
+  a.scale = 1.0f;
+  const vmk::ScanPlan plan = vmk::plan_scan(batch, dim, Lp, a.dstate, ndir);
+  if (plan.xmode == vmk::kXGlobal) a.xglobal = y;
+  st = hip_status(vmk::launch_scan(plan, a, /*bf16=*/false, s));
+  if (st != VM_OK) return st;
+  return hip_status(vmk::launch_repeat_gate(y, z, out, batch * dim, height, width, pool_axis,
+                                            combine_scale, bf16, s));
+}
+
+}  // extern "C"

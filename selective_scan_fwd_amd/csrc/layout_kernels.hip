@@ -1,0 +1,258 @@
+// Index-exact data movement around the scan:
+//  * p = 2 atrous gather / scatter (EfficientVMamba page, "Four shorter
+//    sequences, one dense output" and "Merge restores coordinates instead of
+//    adding directions"),
+//  * mean pooling over one grid axis and the repeat + SiLU gate back to the
+//    full grid (FastVim summary, "Methodology"),
+//  * bf16 -> fp32 widening of small side tensors, and the step-major packing
+//    of B and C the scan kernel reads with scalar loads.
+// All of these are HBM-bound streaming kernels: every element is read once
+// and written once with coalesced accesses.
+#include "vm_internal.h"
+
+namespace vmk {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPlaneLds = 16384;  // floats of a staged H x W plane (64 KB)
+
+// Step t of group k -> (row, col) on the padded grid.  Offsets (0,0), (1,0),
+// (0,1), (1,1); even groups walk the half grid row-major, odd ones
+// column-major.
+__device__ __forceinline__ void route(int k, int t, int hr, int hc, int &y, int &x) {
+  int r, c;
+  if ((k & 1) == 0) { r = t / hc; c = t - r * hc; }
+  else { c = t / hr; r = t - c * hr; }
+  y = 2 * r + (k & 1);
+  x = 2 * c + (k >> 1);
+}
+
+// One workgroup per (b, c) plane: stage the plane in LDS with coalesced
+// loads, then emit the four streams with coalesced stores.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+atrous_gather_kernel(const T *__restrict__ x, T *__restrict__ streams, int64_t ch, int H, int W,
+                     int staged) {
+  extern __shared__ unsigned char plane_raw[];
+  T *plane = reinterpret_cast<T *>(plane_raw);  // H * W values when staged
+  const int64_t pid = blockIdx.x;               // b * ch + c
+  const int64_t b = pid / ch, c = pid - b * ch;
+  const int hr = (H + 1) / 2, hc = (W + 1) / 2, Lg = hr * hc;
+  const T *src = x + pid * H * W;
+  if (staged) {
+    for (int i = threadIdx.x; i < H * W; i += kThreads) plane[i] = src[i];
+    __syncthreads();
+  }
+  for (int k = 0; k < 4; ++k) {
+    T *dst = streams + ((b * 4 + k) * ch + c) * Lg;
+    for (int t = threadIdx.x; t < Lg; t += kThreads) {
+      int yy, xx;
+      route(k, t, hr, hc, yy, xx);
+      T v = T(0);
+      if (yy < H && xx < W) v = staged ? plane[yy * W + xx] : src[yy * W + xx];
+      dst[t] = v;
+    }
+  }
+}
+
+// Inverse routing: every valid (row, col) has exactly one owner, group
+// k = (row & 1) + 2 (col & 1) at step t of that group; copy it, write each
+// output once (no sums).  Stores are coalesced over the plane.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+atrous_scatter_kernel(const T *__restrict__ streams, T *__restrict__ y, int64_t ch, int H, int W) {
+  const int64_t pid = blockIdx.x;
+  const int64_t b = pid / ch, c = pid - b * ch;
+  const int hr = (H + 1) / 2, hc = (W + 1) / 2, Lg = hr * hc;
+  T *dst = y + pid * H * W;
+  for (int i = threadIdx.x; i < H * W; i += kThreads) {
+    const int yy = i / W, xx = i - (i / W) * W;
+    const int k = (yy & 1) + 2 * (xx & 1);
+    const int r = yy >> 1, cc = xx >> 1;
+    const int t = (k & 1) == 0 ? r * hc + cc : cc * hr + r;
+    dst[i] = streams[((b * 4 + k) * ch + c) * Lg + t];
+  }
+}
+
+// Mean over one axis of each H x W grid: one workgroup per grid row (b, d).
+// axis 0 (mean over W): wave w sums grid rows w, w+4, ...; lanes stride the
+// row and the partial sums are reduced across the wave.  axis 1 (mean over
+// H): threads own columns and sum down the rows in index order.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+mean_pool_kernel(const T *__restrict__ u, float *__restrict__ pooled, int H, int W, int axis,
+                 float inv) {
+  const int64_t r = blockIdx.x;
+  const T *g = u + r * static_cast<int64_t>(H) * W;
+  if (axis == 0) {
+    float *dst = pooled + r * H;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int i = wave; i < H; i += kThreads / 64) {
+      float s = 0.0f;
+      for (int j = lane; j < W; j += 64) s += to_f32(g[static_cast<int64_t>(i) * W + j]);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+      if (lane == 0) dst[i] = s * inv;
+    }
+  } else {
+    float *dst = pooled + r * W;
+    for (int j = threadIdx.x; j < W; j += kThreads) {
+      float s = 0.0f;
+      for (int i = 0; i < H; ++i) s += to_f32(g[static_cast<int64_t>(i) * W + j]);
+      dst[j] = s * inv;
+    }
+  }
+}
+
+// out[r, i, j] = scale * y[r, p] * SiLU(z[r, i, j]),  p = i (axis 0) or j.
+// One workgroup per grid (row r); threads walk the flat grid with coalesced
+// accesses and track (i, j) incrementally (no per-element division).
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+repeat_gate_kernel(const float *__restrict__ y, const T *__restrict__ z, T *__restrict__ out,
+                   int H, int W, int axis, float scale) {
+  const int64_t r = blockIdx.x;
+  const int hw = H * W;
+  const int Lp = axis == 0 ? H : W;
+  const float *yr = y + r * Lp;
+  const T *zr = z != nullptr ? z + r * static_cast<int64_t>(hw) : nullptr;
+  T *outr = out + r * static_cast<int64_t>(hw);
+  int i = threadIdx.x / W, j = threadIdx.x - (threadIdx.x / W) * W;
+  for (int e = threadIdx.x; e < hw; e += kThreads) {
+    float v = scale * yr[axis == 0 ? i : j];
+    if (zr != nullptr) v *= silu_f(to_f32(zr[e]));
+    outr[e] = from_f32<T>(v);
+    j += kThreads;
+    while (j >= W) { j -= W; ++i; }
+  }
+}
+
+__global__ void __launch_bounds__(kThreads)
+to_f32_kernel(const bf16_t *__restrict__ src, float *__restrict__ dst, int64_t n) {
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; e < n;
+       e += static_cast<int64_t>(gridDim.x) * kThreads)
+    dst[e] = to_f32(src[e]);
+}
+
+// B, C [batch, dstate, L] (T) -> BC [batch, L, 32] fp32.  One workgroup per
+// (b, 64-step tile): rows of B and C are read coalesced along t into LDS,
+// then each step's 128-byte record is written coalesced.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+bc_pack_kernel(const T *__restrict__ B, const T *__restrict__ C, float *__restrict__ BC,
+               int dstate, int64_t L, int tiles) {
+  __shared__ float tile[2 * 16][65];
+  const int64_t b = blockIdx.x / tiles;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x - b * tiles) * 64;
+  for (int e = threadIdx.x; e < 2 * 16 * 64; e += kThreads) {
+    const int slot = e >> 6, tt = e & 63;
+    const int n = slot & 15;
+    const int64_t t = t0 + tt;
+    float v = 0.0f;
+    if (n < dstate && t < L) {
+      const T *src = slot < 16 ? B : C;
+      v = to_f32(src[(b * dstate + n) * L + t]);
+    }
+    tile[slot][tt] = v;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 64 * 2 * 16; e += kThreads) {
+    const int tt = e >> 5, slot = e & 31;
+    const int64_t t = t0 + tt;
+    if (t < L) BC[(b * L + t) * kBCStride + slot] = tile[slot][tt];
+  }
+}
+
+unsigned stream_grid(int64_t n) {
+  int64_t g = (n + kThreads - 1) / kThreads;
+  const int64_t cap = 256 * 64;   // 64 workgroups per CU, grid-stride beyond
+  return static_cast<unsigned>(g < cap ? g : cap);
+}
+
+}  // namespace
+
+hipError_t launch_atrous_gather(const void *x, void *streams, int64_t batch, int64_t ch,
+                                int64_t H, int64_t W, bool bf16, hipStream_t s) {
+  const int64_t planes = batch * ch;
+  if (planes == 0) return hipSuccess;
+  const int staged = (H * W <= kPlaneLds) ? 1 : 0;
+  const size_t lds = staged ? static_cast<size_t>(H * W) * (bf16 ? 2 : 4) : 0;
+  if (bf16)
+    hipLaunchKernelGGL(atrous_gather_kernel<bf16_t>, dim3(planes), dim3(kThreads), lds, s,
+                       static_cast<const bf16_t *>(x), static_cast<bf16_t *>(streams), ch,
+                       static_cast<int>(H), static_cast<int>(W), staged);
+  else
+    hipLaunchKernelGGL(atrous_gather_kernel<float>, dim3(planes), dim3(kThreads), lds, s,
+                       static_cast<const float *>(x), static_cast<float *>(streams), ch,
+                       static_cast<int>(H), static_cast<int>(W), staged);
+  return hipGetLastError();
+}
+
+hipError_t launch_atrous_scatter(const void *streams, void *y, int64_t batch, int64_t ch,
+                                 int64_t H, int64_t W, bool bf16, hipStream_t s) {
+  const int64_t planes = batch * ch;
+  if (planes == 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(atrous_scatter_kernel<bf16_t>, dim3(planes), dim3(kThreads), 0, s,
+                       static_cast<const bf16_t *>(streams), static_cast<bf16_t *>(y), ch,
+                       static_cast<int>(H), static_cast<int>(W));
+  else
+    hipLaunchKernelGGL(atrous_scatter_kernel<float>, dim3(planes), dim3(kThreads), 0, s,
+                       static_cast<const float *>(streams), static_cast<float *>(y), ch,
+                       static_cast<int>(H), static_cast<int>(W));
+  return hipGetLastError();
+}
+
+hipError_t launch_mean_pool(const void *u, float *pooled, int64_t rows, int64_t H, int64_t W,
+                            int axis, bool bf16, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const float inv = static_cast<float>(1.0 / static_cast<double>(axis == 0 ? W : H));
+  if (bf16)
+    hipLaunchKernelGGL(mean_pool_kernel<bf16_t>, dim3(rows), dim3(kThreads), 0, s,
+                       static_cast<const bf16_t *>(u), pooled, static_cast<int>(H),
+                       static_cast<int>(W), axis, inv);
+  else
+    hipLaunchKernelGGL(mean_pool_kernel<float>, dim3(rows), dim3(kThreads), 0, s,
+                       static_cast<const float *>(u), pooled, static_cast<int>(H),
+                       static_cast<int>(W), axis, inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_repeat_gate(const float *y, const void *z, void *out, int64_t rows, int64_t H,
+                              int64_t W, int axis, float scale, bool bf16, hipStream_t s) {
+  if (rows * H * W == 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(repeat_gate_kernel<bf16_t>, dim3(static_cast<unsigned>(rows)), dim3(kThreads),
+                       0, s, y, static_cast<const bf16_t *>(z), static_cast<bf16_t *>(out),
+                       static_cast<int>(H), static_cast<int>(W), axis, scale);
+  else
+    hipLaunchKernelGGL(repeat_gate_kernel<float>, dim3(static_cast<unsigned>(rows)), dim3(kThreads),
+                       0, s, y, static_cast<const float *>(z), static_cast<float *>(out),
+                       static_cast<int>(H), static_cast<int>(W), axis, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_bc_pack(const void *B, const void *C, float *BC, int64_t batch, int64_t dstate,
+                          int64_t L, bool bf16, hipStream_t s) {
+  const int64_t tiles = (L + 63) / 64;
+  if (batch * tiles == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(batch * tiles));
+  if (bf16)
+    hipLaunchKernelGGL(bc_pack_kernel<bf16_t>, grid, dim3(kThreads), 0, s,
+                       static_cast<const bf16_t *>(B), static_cast<const bf16_t *>(C), BC,
+                       static_cast<int>(dstate), L, static_cast<int>(tiles));
+  else
+    hipLaunchKernelGGL(bc_pack_kernel<float>, grid, dim3(kThreads), 0, s,
+                       static_cast<const float *>(B), static_cast<const float *>(C), BC,
+                       static_cast<int>(dstate), L, static_cast<int>(tiles));
+  return hipGetLastError();
+}
+
+hipError_t launch_to_f32(const void *src, float *dst, int64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(to_f32_kernel, dim3(stream_grid(n)), dim3(kThreads), 0, s,
+                     static_cast<const bf16_t *>(src), dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace vmk

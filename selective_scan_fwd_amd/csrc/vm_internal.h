@@ -1,0 +1,120 @@
+// Internal declarations shared by the HIP kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vmk {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Rows (channels) per wave and per row block: one lane owns one channel.
+constexpr int kRows = 64;
+
+// bf16 values are carried as raw 16-bit patterns.
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// Round to nearest, ties to even; NaN stays a (quiet) NaN.
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// Hardware 2^x (v_exp_f32) and log2 (v_log_f32), reciprocal (v_rcp_f32).
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(x) = max(x, 0) + log1p(e^-|x|).  log1p(e) is taken as
+// log(s) - ((s - 1) - e) / s with s = fl(1 + e): the second term removes the
+// rounding error of s to first order, so small e keeps full relative accuracy.
+__device__ __forceinline__ float softplus_f(float x) {
+  float e = hw_exp2(-__builtin_fabsf(x) * kLog2e);
+  float s = 1.0f + e;
+  float l = hw_log2(s) * kLn2;
+  float corr = ((s - 1.0f) - e) * hw_rcp(s);
+  return __builtin_fmaxf(x, 0.0f) + (l - corr);
+}
+
+// SiLU(z) = z * sigmoid(z) = z / (1 + e^-z).
+__device__ __forceinline__ float silu_f(float z) {
+  return z * hw_rcp(1.0f + hw_exp2(-z * kLog2e));
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs of an MI355X.  Give
+// each XCD a contiguous range of logical blocks, so that neighbouring row
+// blocks of one batch row (which share B and C) meet in the same L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  constexpr int kXcd = 8;
+  int q = nblocks / kXcd, r = nblocks % kXcd;
+  int x = bid % kXcd, k = bid / kXcd;
+  return x * q + (x < r ? x : r) + k;
+}
+
+// ---------------------------------------------------------------- scan
+// B and C of one direction packed step-major: BC[b, t, 0..15] = B[b, 0..15, t]
+// and BC[b, t, 16..31] = C[b, 0..15, t], fp32, zero for states >= dstate.
+// One 128-byte record per (b, t) lets a wave fetch its states' B and C for a
+// step with scalar loads off a single base pointer.
+constexpr int kBCStride = 32;
+
+struct DirPtrs {
+  const void *u;        // [batch, dim, L] (Tin)
+  const void *delta;    // [batch, dim, L] (Tin)
+  const float *A;       // [dim, dstate]
+  const float *BC;      // [batch, L, 32] fp32 (packed B and C)
+  const float *D;       // [dim]
+  const float *bias;    // [dim] or nullptr
+};
+
+struct ScanArgs {
+  DirPtrs dir[2];
+  const void *z;        // [batch, dim, L] (Tin) or nullptr
+  void *out;            // [batch, dim, L] (Tin)
+  float *xglobal;       // fp32 [batch, dim, L] exchange buffer (long bidirectional)
+  int64_t batch, dim, L;
+  int dstate;
+  int softplus;
+  int reverse;          // one-direction scans only
+  float scale;          // bidirectional combine scale
+};
+
+enum XMode { kXNone = 0, kXLds = 1, kXGlobal = 2 };
+
+struct ScanPlan {
+  int S;        // state groups (waves) per direction
+  int T;        // tile length (steps between workgroup barriers)
+  int dirs;     // 1 or 2
+  int xmode;    // XMode
+  size_t lds;   // dynamic LDS bytes
+  int threads;  // workgroup size
+  int64_t blocks;
+};
+
+ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t L, int dstate, int dirs);
+hipError_t launch_scan(const ScanPlan &plan, const ScanArgs &args, bool bf16, hipStream_t s);
+
+// ---------------------------------------------------------------- layout
+hipError_t launch_atrous_gather(const void *x, void *streams, int64_t batch, int64_t ch,
+                                int64_t H, int64_t W, bool bf16, hipStream_t s);
+hipError_t launch_atrous_scatter(const void *streams, void *y, int64_t batch, int64_t ch,
+                                 int64_t H, int64_t W, bool bf16, hipStream_t s);
+hipError_t launch_mean_pool(const void *u, float *pooled, int64_t rows, int64_t H, int64_t W,
+                            int axis, bool bf16, hipStream_t s);
+hipError_t launch_repeat_gate(const float *y, const void *z, void *out, int64_t rows, int64_t H,
+                              int64_t W, int axis, float scale, bool bf16, hipStream_t s);
+hipError_t launch_to_f32(const void *src, float *dst, int64_t n, hipStream_t s);
+hipError_t launch_bc_pack(const void *B, const void *C, float *BC, int64_t batch, int64_t dstate,
+                          int64_t L, bool bf16, hipStream_t s);
+
+}  // namespace vmk

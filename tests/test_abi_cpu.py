@@ -1,0 +1,144 @@
+"""CPU-only checks of the C ABI: the library loads, exports every function the
+header declares, and its host-side argument checks return the documented
+status codes without launching anything (no GPU is touched on these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_scan_fwd_amd as vm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vm_scan.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(vm_[a-z0-9_]+)\s*\(", src)))
+
+
+def _status_codes():
+    src = open(HEADER).read()
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"\b(VM_(?:OK|ERR_[A-Z]+))\s*=\s*(\d+)", src)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(vm.LIB_PATH):
+        from selective_scan_fwd_amd import build
+        build.build()
+    return vm.load_library()
+
+
+def test_exports_match_header(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(vm.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    codes = _status_codes()
+    assert codes["VM_OK"] == 0 and len(codes) == len(vm.STATUS_NAMES)
+    for name, code in codes.items():
+        assert vm.STATUS_NAMES[code] == name
+        assert vm.vm_status_string(code).startswith(name)
+    assert vm.vm_status_string(999) == "unknown status"
+    assert vm.vm_version() >= 10000
+
+
+def test_group_len(lib):
+    assert vm.vm_atrous_group_len(56, 56) == 784
+    assert vm.vm_atrous_group_len(57, 57) == 841
+    assert vm.vm_atrous_group_len(3, 5) == 6
+    assert vm.vm_atrous_group_len(1, 1) == 1
+    assert lib.vm_atrous_group_len(0, 4) == -2
+    assert lib.vm_atrous_group_len(4, -1) == -2
+
+
+FAKE = 1 << 40          # plausible-looking but never dereferenced device addresses
+
+
+def _dir(base):
+    # non-overlapping fake pointers: each tensor gets its own 2^32-byte window
+    return vm.VmScanDir(*(base + k * (1 << 32) for k in range(7)))
+
+
+def _scan(lib, d=None, z=None, out=FAKE * 3, batch=2, dim=4, L=5, N=16, dtype=0, sp=1, rev=0):
+    d = _dir(FAKE) if d is None else d
+    return lib.vm_selective_scan_fwd(ctypes.byref(d), z, out, batch, dim, L, N, dtype, sp, rev, None)
+
+
+def test_scan_argument_checks(lib):
+    assert lib.vm_selective_scan_fwd(None, None, FAKE * 3, 2, 4, 5, 16, 0, 1, 0, None) == 1
+    assert _scan(lib, out=None) == 1
+    d = _dir(FAKE)
+    d.B = None
+    assert _scan(lib, d=d) == 1
+    d = _dir(FAKE)
+    d.D = None
+    assert _scan(lib, d=d) == 1
+    assert _scan(lib, batch=0) == 2
+    assert _scan(lib, dim=-3) == 2
+    assert _scan(lib, L=0) == 2
+    assert _scan(lib, N=0) == 2
+    assert _scan(lib, batch=1 << 40, dim=1 << 20) == 2          # element count overflow
+    assert _scan(lib, N=17) == 6
+    assert _scan(lib, dtype=2) == 3
+    assert _scan(lib, sp=2) == 4
+    assert _scan(lib, rev=-1) == 4
+    # output overlapping an input
+    d = _dir(FAKE)
+    assert _scan(lib, d=d, out=d.u) == 5
+    assert _scan(lib, d=d, out=d.delta + 8) == 5
+    assert _scan(lib, d=d, out=d.B) == 5
+    assert _scan(lib, z=FAKE * 3, out=FAKE * 3) == 5
+
+
+def test_bidir_argument_checks(lib):
+    f, b = _dir(FAKE), _dir(FAKE * 2)
+
+    def call(fwd=f, bwd=b, z=None, scale=1.0, out=FAKE * 3, N=16, dtype=0, sp=1):
+        pf = ctypes.byref(fwd) if fwd is not None else None
+        pb = ctypes.byref(bwd) if bwd is not None else None
+        return lib.vm_bidir_scan_fwd(pf, pb, z, scale, out, 2, 4, 5, N, dtype, sp, None)
+
+    assert call(fwd=None) == 1
+    assert call(bwd=None) == 1
+    assert call(scale=float("nan")) == 6
+    assert call(scale=float("inf")) == 6
+    assert call(N=32) == 6
+    assert call(dtype=-1) == 3
+    assert call(sp=3) == 4
+    assert call(out=b.C) == 5
+
+
+def test_atrous_argument_checks(lib):
+    assert lib.vm_atrous_gather(None, FAKE * 3, 1, 1, 4, 4, 0, None) == 1
+    assert lib.vm_atrous_gather(FAKE, None, 1, 1, 4, 4, 0, None) == 1
+    assert lib.vm_atrous_gather(FAKE, FAKE * 3, 1, 1, 0, 4, 0, None) == 2
+    assert lib.vm_atrous_gather(FAKE, FAKE * 3, 1, 1, 4, 4, 5, None) == 3
+    assert lib.vm_atrous_gather(FAKE, FAKE + 16, 1, 1, 4, 4, 0, None) == 5
+    assert lib.vm_atrous_scatter(FAKE, FAKE * 3, 1, 0, 4, 4, 0, None) == 2
+    assert lib.vm_atrous_scatter(FAKE, None, 1, 1, 4, 4, 0, None) == 1
+    assert lib.vm_atrous_scatter(FAKE, FAKE + 60, 1, 1, 4, 4, 0, None) == 5
+
+
+def test_pool_argument_checks(lib):
+    f, b = _dir(FAKE), _dir(FAKE * 2)
+
+    def call(fwd=f, bwd=b, axis=0, H=8, W=6, N=16, out=FAKE * 3, sp=1, dtype=0, scale=0.5):
+        pf = ctypes.byref(fwd) if fwd is not None else None
+        pb = ctypes.byref(bwd) if bwd is not None else None
+        return lib.vm_pool_scan_repeat(pf, pb, None, scale, out, 2, 4, H, W, N, axis, dtype, sp, None)
+
+    assert call(fwd=None) == 1
+    assert call(axis=2) == 4
+    assert call(H=0) == 2
+    assert call(N=0) == 2
+    assert call(N=20) == 6
+    assert call(scale=float("nan")) == 6
+    assert call(dtype=9) == 3
+    assert call(out=f.u + 4) == 5

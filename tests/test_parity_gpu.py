@@ -1,0 +1,337 @@
+"""GPU parity of every C-ABI entry point against the fp64 CPU oracle.
+
+Scan outputs must agree within max relative error 1e-4 (fp32) / 2e-2 (bf16
+inputs), measured as max |got - ref| / max(|ref|, 0.1 rms(ref)); gather and
+scatter must be bit-exact.  Small cases span several tiles, several row
+blocks and ragged tails; full-size cases check sampled rows of the workloads
+at their real shapes.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_scan_fwd_amd as vm
+from selective_scan_fwd_amd import workloads as wl
+
+from _helpers import BF16_TOL, FP32_TOL, assert_close, bits_equal, host, host_dir, sub_dir
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
+
+
+def _case(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if DEV is None:
+        pytest.fail("GPU test run without a visible GPU")
+    vm.load_library()
+
+
+# ---------------------------------------------------------------- one direction
+@pytest.mark.parametrize("batch,dim,L,N", [(1, 1, 1, 16), (2, 130, 77, 16), (3, 64, 8, 16),
+                                           (2, 70, 33, 5), (1, 96, 197, 1), (2, 33, 150, 16)])
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("gated", [True, False])
+def test_single_fp32(batch, dim, L, N, reverse, gated):
+    _case(f"single fp32 b{batch} d{dim} L{L} N{N} rev{reverse} gated{gated}")
+    p, z = wl.single_inputs(100 + L, batch, dim, L, N, device=DEV, gated=gated, perturb=True)
+    out = vm.vm_selective_scan_fwd(**p, z=z, reverse=reverse)
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan(**host_dir(p), z=host(z), reverse=reverse)
+    assert_close(host(out), ref, FP32_TOL, "single")
+
+
+def test_single_no_softplus_and_no_bias():
+    _case("single no softplus")
+    p, z = wl.single_inputs(5, 2, 70, 45, device=DEV)
+    p["delta"] = torch.rand_like(p["delta"]) * 0.2
+    p["delta_bias"] = None
+    out = vm.vm_selective_scan_fwd(**p, z=z, delta_softplus=False)
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan(**host_dir(p), z=host(z), delta_softplus=False)
+    assert_close(host(out), ref, FP32_TOL, "no softplus")
+
+
+def test_single_extreme_steps():
+    # softplus far in both tails: dt ~ e^-30 (no update) and dt ~ 30 (memoryless)
+    _case("single extreme steps")
+    p, z = wl.single_inputs(6, 1, 64, 40, device=DEV)
+    p["delta"][:, :, ::3] = -30.0
+    p["delta"][:, :, 1::3] = 30.0
+    out = vm.vm_selective_scan_fwd(**p, z=z)
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan(**host_dir(p), z=host(z))
+    assert_close(host(out), ref, FP32_TOL, "extreme")
+
+
+def test_single_bf16():
+    _case("single bf16")
+    p, z = wl.single_inputs(7, 2, 100, 90, device=DEV, dtype=torch.bfloat16, perturb=True)
+    out = vm.vm_selective_scan_fwd(**p, z=z)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.bfloat16
+    ref = oracle.selective_scan(**host_dir(p), z=host(z))
+    assert_close(host(out), ref, BF16_TOL, "single bf16")
+
+
+# ---------------------------------------------------------------- bidirectional
+# Shapes chosen to cover: one tile (joint midpoint), odd / even tile counts,
+# the LDS exchange with 8- and 4-step tiles, the global exchange (long L),
+# and both state splits (S = 4 on few row blocks, S = 2 on >= 512 blocks).
+BIDIR_CASES = [
+    (1, 1, 1), (2, 70, 2), (2, 70, 16), (2, 70, 77), (2, 130, 197), (2, 70, 300),
+    (512, 64, 20), (512, 64, 197), (256, 128, 300),
+]
+
+
+@pytest.mark.parametrize("batch,dim,L", BIDIR_CASES)
+def test_bidir_fp32(batch, dim, L):
+    _case(f"bidir fp32 b{batch} d{dim} L{L}")
+    fwd, bwd, z = wl.bidir_inputs(200 + L, batch, dim, L, device=DEV, perturb=True)
+    for scale in (1.0, 0.5):
+        out = vm.vm_bidir_scan_fwd(fwd, bwd, z=z, combine_scale=scale)
+        torch.cuda.synchronize()
+        ref = oracle.bidir_scan(host_dir(fwd), host_dir(bwd), z=host(z), combine_scale=scale)
+        assert_close(host(out), ref, FP32_TOL, f"bidir s={scale}")
+
+
+def test_bidir_ungated_small_dstate():
+    _case("bidir ungated N=3")
+    fwd, bwd, _ = wl.bidir_inputs(9, 2, 66, 41, dstate=3, device=DEV, gated=False, perturb=True)
+    out = vm.vm_bidir_scan_fwd(fwd, bwd, z=None, combine_scale=0.5)
+    torch.cuda.synchronize()
+    ref = oracle.bidir_scan(host_dir(fwd), host_dir(bwd), z=None, combine_scale=0.5)
+    assert_close(host(out), ref, FP32_TOL, "bidir N=3")
+
+
+@pytest.mark.parametrize("L", [50, 333])
+def test_bidir_bf16(L):
+    _case(f"bidir bf16 L{L}")
+    fwd, bwd, z = wl.bidir_inputs(11 + L, 2, 100, L, device=DEV, dtype=torch.bfloat16, perturb=True)
+    out = vm.vm_bidir_scan_fwd(fwd, bwd, z=z)
+    torch.cuda.synchronize()
+    ref = oracle.bidir_scan(host_dir(fwd), host_dir(bwd), z=host(z))
+    assert_close(host(out), ref, BF16_TOL, "bidir bf16")
+
+
+def test_bidir_matches_two_single_calls():
+    # the fused kernel equals (fwd scan + reverse scan) * scale * gate from the
+    # one-direction entry point, within rounding
+    _case("bidir vs two singles")
+    fwd, bwd, z = wl.bidir_inputs(12, 2, 64, 90, device=DEV, perturb=True)
+    yf = vm.vm_selective_scan_fwd(**fwd)
+    yb = vm.vm_selective_scan_fwd(**bwd, reverse=True)
+    both = vm.vm_bidir_scan_fwd(fwd, bwd, z=z, combine_scale=0.5)
+    torch.cuda.synchronize()
+    zz = host(z)
+    comp = 0.5 * (host(yf) + host(yb)) * (zz / (1 + np.exp(-zz)))
+    assert_close(host(both), comp, FP32_TOL, "fused vs composed")
+
+
+def test_deterministic():
+    _case("determinism")
+    fwd, bwd, z = wl.bidir_inputs(13, 4, 128, 197, device=DEV)
+    a = vm.vm_bidir_scan_fwd(fwd, bwd, z=z)
+    b = vm.vm_bidir_scan_fwd(fwd, bwd, z=z)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- atrous
+SHAPES = [(4, 6), (3, 5), (1, 1), (2, 3), (5, 2), (1, 7), (6, 1), (56, 56), (57, 57), (130, 9)]
+
+
+@pytest.mark.parametrize("H,W", SHAPES)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_atrous_bit_exact(H, W, dtype):
+    _case(f"atrous {H}x{W} {dtype}")
+    g = wl.generator(300 + H * 31 + W, DEV)
+    x = torch.randn((2, 3, H, W), generator=g, device=DEV).to(dtype)
+    s = vm.vm_atrous_gather(x)
+    y = vm.vm_atrous_scatter(s, H, W)
+    torch.cuda.synchronize()
+    ref = oracle.atrous_gather(host(x))
+    assert bits_equal(s, ref)                              # pads are +0.0, values copied
+    assert torch.equal(y.view(torch.int16 if dtype == torch.bfloat16 else torch.int32),
+                       x.view(torch.int16 if dtype == torch.bfloat16 else torch.int32))
+    # scatter alone against the oracle on arbitrary stream contents
+    s2 = torch.randn(s.shape, generator=g, device=DEV).to(dtype)
+    y2 = vm.vm_atrous_scatter(s2, H, W)
+    torch.cuda.synchronize()
+    assert bits_equal(y2, oracle.atrous_scatter(host(s2), H, W))
+
+
+def test_atrous_pad_is_positive_zero():
+    _case("atrous pad sign")
+    x = -torch.ones((1, 1, 3, 5), device=DEV)
+    s = vm.vm_atrous_gather(x)
+    torch.cuda.synchronize()
+    sv = host(s)
+    pads = sv == 0
+    assert int(pads.sum()) == 9
+    assert not np.any(np.signbit(sv[pads]))
+
+
+@pytest.mark.parametrize("H,W", [(7, 10), (56, 56)])
+def test_es2d_pipeline(H, W):
+    _case(f"es2d pipeline {H}x{W}")
+    batch, ch = 2, 70
+    x, p = wl.es2d_inputs(400 + H, batch, ch, H, W, device=DEV, perturb=True)
+    s = vm.vm_atrous_gather(x)
+    Lg = s.shape[-1]
+    y = vm.vm_selective_scan_fwd(s.reshape(4 * batch, ch, Lg), **p)
+    out = vm.vm_atrous_scatter(y.reshape(batch, 4, ch, Lg), H, W)
+    torch.cuda.synchronize()
+    hs = oracle.atrous_gather(host(x))
+    hy = oracle.selective_scan(hs.reshape(4 * batch, ch, Lg), **host_dir(p))
+    ref = oracle.atrous_scatter(hy.reshape(batch, 4, ch, Lg), H, W)
+    assert_close(host(out), ref, FP32_TOL, "es2d")
+
+
+# ---------------------------------------------------------------- pooled
+@pytest.mark.parametrize("axis", [0, 1])
+@pytest.mark.parametrize("bidir", [True, False])
+@pytest.mark.parametrize("gated", [True, False])
+def test_pool_scan_repeat_fp32(axis, bidir, gated):
+    _case(f"pool axis{axis} bidir{bidir} gated{gated}")
+    fwd, bwd, z = wl.fastvim_inputs(500 + axis, 2, 70, 12, 10, axis, device=DEV, perturb=True)
+    out = vm.vm_pool_scan_repeat(fwd, bwd if bidir else None, z=z if gated else None,
+                                 combine_scale=0.5, pool_axis=axis)
+    torch.cuda.synchronize()
+    ref = oracle.pool_scan_repeat(host_dir(fwd), host_dir(bwd) if bidir else None,
+                                  z=host(z) if gated else None, combine_scale=0.5, pool_axis=axis)
+    assert_close(host(out), ref, FP32_TOL, "pool")
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+def test_pool_repeat_indexing_bit_exact(axis):
+    # integer-valued u, B = 0, D = 1, no gate: out = s * (mean_f + mean_b),
+    # exact in fp32 and fp64 (sums < 2^24, division by a power of two)
+    _case(f"pool bit-exact axis{axis}")
+    H, W = 8, 16
+    fwd, bwd, _ = wl.fastvim_inputs(600 + axis, 2, 3, H, W, axis, device=DEV)
+    for p in (fwd, bwd):
+        p["u"] = torch.randint(-8, 9, p["u"].shape, device=DEV).float()
+        p["B"] = torch.zeros_like(p["B"])
+        p["D"] = torch.ones_like(p["D"])
+    out = vm.vm_pool_scan_repeat(fwd, bwd, z=None, combine_scale=0.5, pool_axis=axis)
+    torch.cuda.synchronize()
+    ref = oracle.pool_scan_repeat(host_dir(fwd), host_dir(bwd), z=None, combine_scale=0.5,
+                                  pool_axis=axis)
+    assert np.array_equal(host(out), ref)
+
+
+def test_pool_bf16():
+    _case("pool bf16")
+    fwd, bwd, z = wl.fastvim_inputs(700, 2, 70, 16, 12, 1, device=DEV, dtype=torch.bfloat16)
+    out = vm.vm_pool_scan_repeat(fwd, bwd, z=z, pool_axis=1)
+    torch.cuda.synchronize()
+    ref = oracle.pool_scan_repeat(host_dir(fwd), host_dir(bwd), z=host(z), pool_axis=1)
+    assert_close(host(out), ref, BF16_TOL, "pool bf16")
+
+
+# ---------------------------------------------------------------- full-size workloads
+def test_full_vim_tiny_bidir():
+    w = wl.WORKLOADS[1]
+    _case(f"full {w.name}")
+    fwd, bwd, z = wl.bidir_inputs(1001, w.batch, w.dim, w.seqlen, device=DEV, perturb=True)
+    out = vm.vm_bidir_scan_fwd(fwd, bwd, z=z, combine_scale=w.combine_scale)
+    torch.cuda.synchronize()
+    bsel = [0, 1, 31, 64, 100, 127]
+    dsel = list(range(w.dim))
+    ref = oracle.bidir_scan(sub_dir(host_dir(fwd), bsel, dsel), sub_dir(host_dir(bwd), bsel, dsel),
+                            z=host(z)[bsel][:, dsel], combine_scale=w.combine_scale)
+    assert_close(host(out[bsel]), ref, FP32_TOL, "vim-t full (sampled batches)")
+
+
+def test_full_single():
+    w = wl.WORKLOADS[0]
+    _case(f"full {w.name}")
+    p, z = wl.single_inputs(1000, w.batch, w.dim, w.seqlen, device=DEV)
+    out = vm.vm_selective_scan_fwd(**p, z=z)
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan(**host_dir(p), z=host(z))
+    assert_close(host(out), ref, FP32_TOL, "single full")
+
+
+def test_full_vim_small_bf16():
+    w = wl.WORKLOADS[2]
+    _case(f"full {w.name}")
+    fwd, bwd, z = wl.bidir_inputs(1002, w.batch, w.dim, w.seqlen, device=DEV,
+                                  dtype=torch.bfloat16, perturb=True)
+    out = vm.vm_bidir_scan_fwd(fwd, bwd, z=z)
+    torch.cuda.synchronize()
+    bsel = [0, 15]
+    dsel = list(range(0, w.dim, 7)) + [w.dim - 1]
+    hf, hb = host_dir(fwd), host_dir(bwd)
+    ref = oracle.bidir_scan(sub_dir(hf, bsel, dsel), sub_dir(hb, bsel, dsel), z=host(z)[bsel][:, dsel])
+    assert_close(host(out)[bsel][:, dsel], ref, BF16_TOL, "vim-s bf16 full (sampled)")
+
+
+@pytest.mark.parametrize("size", [56, 57])
+def test_full_es2d(size):
+    w = wl.WORKLOADS[3]
+    _case(f"full {w.name} {size}")
+    x, p = wl.es2d_inputs(1003 + size, w.batch, w.dim, size, size, device=DEV)
+    s = vm.vm_atrous_gather(x)
+    Lg = s.shape[-1]
+    y = vm.vm_selective_scan_fwd(s.reshape(4 * w.batch, w.dim, Lg), **p)
+    out = vm.vm_atrous_scatter(y.reshape(w.batch, 4, w.dim, Lg), size, size)
+    torch.cuda.synchronize()
+    # gather / scatter bit-exact over the whole batch
+    assert np.array_equal(host(s), oracle.atrous_gather(host(x)))
+    bsel = [0, 37, 63]
+    rows = [4 * b + k for b in bsel for k in range(4)]
+    hp = host_dir(p)
+    hs = oracle.atrous_gather(host(x)[bsel])
+    hy = oracle.selective_scan(hs.reshape(4 * len(bsel), w.dim, Lg),
+                               hp["delta"][rows], hp["A"], hp["B"][rows], hp["C"][rows], hp["D"],
+                               delta_bias=hp["delta_bias"])
+    ref = oracle.atrous_scatter(hy.reshape(len(bsel), 4, w.dim, Lg), size, size)
+    assert_close(host(out)[bsel], ref, FP32_TOL, f"es2d full {size}")
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+def test_full_fastvim_pooled(axis):
+    w = wl.WORKLOADS[4]
+    _case(f"full {w.name} pooled axis{axis}")
+    fwd, bwd, z = wl.fastvim_inputs(1004, w.batch, w.dim, w.height, w.width, axis, device=DEV)
+    out = vm.vm_pool_scan_repeat(fwd, bwd, z=z, combine_scale=w.combine_scale, pool_axis=axis)
+    torch.cuda.synchronize()
+    bsel, dsel = [0, 127], [0, 1, 190, 383]
+    hf = {k: host(v[bsel][:, dsel]) if k in ("u", "delta") else None for k, v in fwd.items()}
+    hb = {k: host(v[bsel][:, dsel]) if k in ("u", "delta") else None for k, v in bwd.items()}
+    for h, p in ((hf, fwd), (hb, bwd)):
+        h["A"], h["D"], h["delta_bias"] = host(p["A"])[dsel], host(p["D"])[dsel], host(p["delta_bias"])[dsel]
+        h["B"], h["C"] = host(p["B"][bsel]), host(p["C"][bsel])
+    ref = oracle.pool_scan_repeat(hf, hb, z=host(z[bsel][:, dsel]), combine_scale=w.combine_scale,
+                                  pool_axis=axis)
+    assert_close(host(out[bsel][:, dsel]), ref, FP32_TOL, f"fastvim pooled axis{axis}")
+
+
+def test_full_fastvim_unpooled():
+    w = wl.WORKLOADS[4]
+    _case(f"full {w.name} unpooled L={w.height * w.width}")
+    fwd, bwd, z = wl.fastvim_inputs(1004, w.batch, w.dim, w.height, w.width, 0, device=DEV,
+                                    full_resolution=True)
+    L = w.height * w.width
+    for p in (fwd, bwd):
+        p["u"] = p["u"].reshape(w.batch, w.dim, L)
+    zf = z.reshape(w.batch, w.dim, L)
+    out = vm.vm_bidir_scan_fwd(fwd, bwd, z=zf, combine_scale=w.combine_scale)
+    torch.cuda.synchronize()
+    bsel, dsel = [5, 120], [0, 100, 383]
+    ref = oracle.bidir_scan(sub_dir({k: host(v[bsel]) if k in ("u", "delta", "B", "C") else host(v)
+                                     for k, v in fwd.items()}, list(range(2)), dsel),
+                            sub_dir({k: host(v[bsel]) if k in ("u", "delta", "B", "C") else host(v)
+                                     for k, v in bwd.items()}, list(range(2)), dsel),
+                            z=host(zf[bsel][:, dsel]), combine_scale=w.combine_scale)
+    assert_close(host(out[bsel][:, dsel]), ref, FP32_TOL, "fastvim unpooled (sampled)")
