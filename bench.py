@@ -1,0 +1,343 @@
+"""Benchmark of the selective-scan hot path on one MI355X.
+
+One step = one pass of the hot path over one batch of synthetic input.  The
+default workload is the bidirectional Vim-Tiny block scan (fp32, batch 128,
+L = 197 with the middle CLS token, d_inner 384, d_state 16): one
+vm_bidir_scan_fwd call, which is a single kernel launch (B and C arrive
+token-major, as the block's projection produces them).
+
+Reported on one JSON line: whole-job throughput in algorithmic HBM GB/s (each
+input read once, the output written once), tokens*channels/s, the roofline
+record of the scan kernel (kernel time from HIP events recorded around every
+launch on the launch stream; HBM traffic from the committed rocprofv3 counter
+summary when it belongs to the current kernel source), and the fp64 CPU
+oracle timed on the host's cores on the same workload.
+
+Inputs are resident in HBM before timing; the step cycles through several
+independent input sets so that consecutive steps cannot be served from the
+256 MB Infinity Cache.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+# VALU issue ceiling with packed fp32 forms disabled: 256 CUs x 4 SIMDs x 16
+# lanes x 2.4 GHz = 39.3 T lane-slots/s.  v_exp_f32 measured at half the FMA
+# issue rate on gfx950, i.e. 2 slots.
+VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+SLOTS_PER_STATE_STEP = 6         # dt*A, exp (2 slots), dt*u*B, state fma, readout fma
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["selective_scan_fwd_amd/csrc/scan_kernel.hip",
+                  "selective_scan_fwd_amd/csrc/vm_internal.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1,
+                    help="0 single, 1 Vim-T bidir (default), 2 bf16 L=4097, 3 ES2D 56x56, "
+                         "4 FastVim pooled (axes alternate per step), 5 FastVim unpooled L=16384")
+    ap.add_argument("--sets", type=int, default=0, help="input sets to cycle (0 = auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--seed", type=int, default=1001)
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run --steps plain device copies of MIB MiB "
+                         "(reference reading for the HBM byte counters)")
+    return ap.parse_args()
+
+
+def copy_calibration(mib, steps):
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.randn(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": steps}))
+
+
+# ---------------------------------------------------------------- workloads
+def algorithmic_bytes_scan(batch, dim, L, N, es, dirs, gated):
+    """Bytes a scan must move: u and delta per direction, z, out once; B and C
+    once per (batch, token) and direction; A, D, bias once per direction."""
+    tok = batch * dim * L
+    per_dir = 2 * tok * es + 2 * batch * L * N * es + dim * N * 4 + 2 * dim * 4
+    return dirs * per_dir + (tok * es if gated else 0) + tok * es
+
+
+def build_step(cfg, seed, sets, dev):
+    """Returns (step_fn(i), info dict, cpu_fn(budget_s) -> (seconds, bytes, tokens, threads, desc))."""
+    import torch
+
+    import selective_scan_fwd_amd as vm
+    from selective_scan_fwd_amd import workloads as wl
+
+    N = wl.DSTATE
+    if cfg in (0, 1, 2):
+        w = wl.WORKLOADS[cfg]
+        dt = wl.torch_dtype(w.dtype)
+        es = 2 if w.dtype == "bf16" else 4
+        dirs = 2 if w.kind == "bidir" else 1
+        inputs = []
+        for k in range(sets):
+            if dirs == 2:
+                inputs.append(wl.bidir_inputs(seed + k, w.batch, w.dim, w.seqlen, device=dev, dtype=dt))
+            else:
+                p, z = wl.single_inputs(seed + k, w.batch, w.dim, w.seqlen, device=dev, dtype=dt)
+                inputs.append((p, None, z))
+        outs = [torch.empty_like(inputs[k][0]["u"]) for k in range(sets)]
+
+        def step(i):
+            f, b, z = inputs[i % sets]
+            if dirs == 2:
+                vm.vm_bidir_scan_fwd(f, b, z=z, combine_scale=w.combine_scale, out=outs[i % sets])
+            else:
+                vm.vm_selective_scan_fwd(**f, z=z, out=outs[i % sets])
+
+        nbytes = algorithmic_bytes_scan(w.batch, w.dim, w.seqlen, N, es, dirs, True)
+        tokens = w.batch * w.dim * w.seqlen
+        slots = dirs * tokens * N * SLOTS_PER_STATE_STEP
+        info = dict(workload=w.name, batch=w.batch, dim=w.dim, seqlen=w.seqlen, dstate=N,
+                    directions=dirs, combine_scale=w.combine_scale, dtype=w.dtype,
+                    bc_layout="token-major")
+
+        def cpu(budget):
+            import oracle
+            f, b, z = inputs[0]
+            sub = max(1, min(w.batch, w.batch))          # whole workload, repeated in time
+            hf = {k: (v[:sub].double().cpu().numpy() if k in ("u", "delta", "B", "C") else
+                      (v.double().cpu().numpy() if v is not None else None)) for k, v in f.items()}
+            hz = z[:sub].double().cpu().numpy()
+            if dirs == 2:
+                hb = {k: (v[:sub].double().cpu().numpy() if k in ("u", "delta", "B", "C") else
+                          (v.double().cpu().numpy() if v is not None else None)) for k, v in b.items()}
+                run = lambda: oracle.bidir_scan(hf, hb, z=hz, combine_scale=w.combine_scale)
+            else:
+                run = lambda: oracle.selective_scan(**hf, z=hz)
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                run()
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= budget or reps >= 100:
+                    break
+            frac = sub / w.batch
+            return el / reps, nbytes * frac, tokens * frac, oracle.num_threads(), \
+                f"fp64 oracle on the whole workload ({sub} of {w.batch} batch rows), {reps} repetitions"
+
+        return step, info, cpu, nbytes, tokens, slots
+
+    if cfg == 3:
+        w = wl.WORKLOADS[3]
+        H = W = w.sizes[0]
+        inputs = [wl.es2d_inputs(seed + k, w.batch, w.dim, H, W, device=dev) for k in range(sets)]
+        Lg = ((H + 1) // 2) * ((W + 1) // 2)
+        streams = [torch.empty((w.batch, 4, w.dim, Lg), device=dev) for _ in range(sets)]
+        ys = [torch.empty((4 * w.batch, w.dim, Lg), device=dev) for _ in range(sets)]
+        outs = [torch.empty((w.batch, w.dim, H, W), device=dev) for _ in range(sets)]
+
+        def step(i):
+            x, p = inputs[i % sets]
+            s = vm.vm_atrous_gather(x, out=streams[i % sets])
+            y = vm.vm_selective_scan_fwd(s.view(4 * w.batch, w.dim, Lg), **p, out=ys[i % sets])
+            vm.vm_atrous_scatter(y.view(w.batch, 4, w.dim, Lg), H, W, out=outs[i % sets])
+
+        plane = w.batch * w.dim * H * W * 4
+        streams_b = w.batch * 4 * w.dim * Lg * 4
+        scan_b = algorithmic_bytes_scan(4 * w.batch, w.dim, Lg, N, 4, 1, False)
+        nbytes = (plane + streams_b) + scan_b + (streams_b + plane)
+        tokens = w.batch * w.dim * H * W
+        slots = 4 * w.batch * w.dim * Lg * N * SLOTS_PER_STATE_STEP
+        info = dict(workload=f"{w.name}@{H}x{W}", batch=w.batch, dim=w.dim, height=H, width=W,
+                    group_len=Lg, dstate=N, kernels="gather+scan+scatter")
+
+        def cpu(budget):
+            import oracle
+            x, p = inputs[0]
+            sub = 8
+            hx = x[:sub].double().cpu().numpy()
+            rows = slice(0, 4 * sub)
+            hp = {k: (v[rows].double().cpu().numpy() if k in ("delta", "B", "C") else
+                      v.double().cpu().numpy()) for k, v in p.items()}
+
+            def run():
+                s = oracle.atrous_gather(hx)
+                y = oracle.selective_scan(s.reshape(4 * sub, w.dim, Lg), **hp)
+                oracle.atrous_scatter(y.reshape(sub, 4, w.dim, Lg), H, W)
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                run()
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= budget or reps >= 100:
+                    break
+            frac = sub / w.batch
+            return el / reps, nbytes * frac, tokens * frac, oracle.num_threads(), \
+                f"fp64 oracle gather+scan+scatter on {sub} of {w.batch} batch rows, {reps} repetitions"
+
+        return step, info, cpu, nbytes, tokens, slots
+
+    if cfg in (4, 5):
+        w = wl.WORKLOADS[4]
+        H, W = w.height, w.width
+        L = H * W
+        if cfg == 4:
+            inputs = [wl.fastvim_inputs(seed, w.batch, w.dim, H, W, axis, device=dev) for axis in (0, 1)]
+            out = torch.empty((w.batch, w.dim, H, W), device=dev)
+
+            def step(i):
+                f, b, z = inputs[i % 2]
+                vm.vm_pool_scan_repeat(f, b, z=z, combine_scale=w.combine_scale, pool_axis=i % 2, out=out)
+
+            tok_full = w.batch * w.dim * L
+            Lp = H
+            nbytes = (2 * tok_full + tok_full + tok_full) * 4 + \
+                2 * (w.batch * w.dim * Lp * 4 + 2 * w.batch * Lp * N * 4 + w.dim * (N + 2) * 4)
+            slots = 2 * w.batch * w.dim * Lp * N * SLOTS_PER_STATE_STEP
+            info = dict(workload=f"{w.name}-pooled", batch=w.batch, dim=w.dim, height=H, width=W,
+                        pooled_len=Lp, dstate=N, pool_axis="alternating 0/1",
+                        kernels="pool x2 + bidir scan + repeat-gate")
+        else:
+            f, b, z = wl.fastvim_inputs(seed, w.batch, w.dim, H, W, 0, device=dev, full_resolution=True)
+            for p in (f, b):
+                p["u"] = p["u"].view(w.batch, w.dim, L)
+            zf = z.view(w.batch, w.dim, L)
+            out = torch.empty_like(zf)
+
+            def step(i):
+                vm.vm_bidir_scan_fwd(f, b, z=zf, combine_scale=w.combine_scale, out=out)
+
+            nbytes = algorithmic_bytes_scan(w.batch, w.dim, L, N, 4, 2, True)
+            slots = 2 * w.batch * w.dim * L * N * SLOTS_PER_STATE_STEP
+            info = dict(workload=f"{w.name}-unpooled", batch=w.batch, dim=w.dim, seqlen=L, dstate=N)
+        tokens = w.batch * w.dim * L
+        return step, info, None, nbytes, tokens, slots
+
+    raise SystemExit(f"unknown --config {cfg}")
+
+
+def load_traffic(source_hash, workload):
+    """HBM bytes per launch of the scan kernel from the committed counter
+    summary, if it was taken on the current kernel source and this workload."""
+    path = os.path.join(PROFILE_DIR, "scan_kernel_counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("kernel_source_hash") != source_hash:
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the scan shards by batch rows with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import selective_scan_fwd_amd as vm
+
+    if args.copy_calib:
+        copy_calibration(args.copy_calib, args.steps)
+        return
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    vm.load_library()
+    dev = torch.device("cuda:0")
+    sets = args.sets or (3 if args.config in (0, 1, 2, 3) else 1)
+    step, info, cpu_fn, nbytes, tokens, slots = build_step(args.config, args.seed, sets, dev)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    launch_ms = sum(ev_ms) / len(ev_ms)
+
+    ms_per_step = 1e3 * wall / args.steps
+    value = nbytes / (wall / args.steps) / 1e9
+    achieved_gbs = nbytes / (launch_ms * 1e-3) / 1e9
+    achieved_tslots = slots / (launch_ms * 1e-3) / 1e12
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(src_hash, info["workload"])
+    hbm = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    alu = {"bound": "alu", "achieved": round(achieved_tslots, 2), "peak": round(VALU_PEAK_TSLOTS, 2),
+           "unit": "T VALU lane-slots/s", "frac": round(achieved_tslots / VALU_PEAK_TSLOTS, 4),
+           "traffic": traffic}
+    # The roofline reported is the one the kernel sits closest to.
+    roof, other = (alu, hbm) if alu["frac"] >= hbm["frac"] else (hbm, alu)
+
+    cpu = None
+    if cpu_fn is not None and args.cpu_seconds > 0:
+        sec, cbytes, ctok, threads, desc = cpu_fn(args.cpu_seconds)
+        cpu = {"value": round(cbytes / sec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": desc, "seconds_per_pass": round(sec, 4),
+               "tokens_ch_per_s": round(ctok / sec, 1)}
+
+    line = {
+        "metric": "selective-scan HBM GB/s (% peak) + tokens*ch/s, bidir Vim-T B=128 L=197",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": dict(info, input_sets=sets),
+        "tokens_ch_per_s": round(tokens / (wall / args.steps), 1),
+        "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "kernel_ms_events": round(launch_ms, 5),
+        "roofline": roof,
+        "roofline_other": other,
+        "cpu_baseline": cpu,
+        "kernel_source_hash": src_hash,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -73,6 +73,15 @@ int vm_version(void);
  *                                       shared by all channels of a batch row
  *   D           [dim]          fp32     direct skip (required)
  *   delta_bias  [dim]          fp32     added to delta before softplus; NULL = 0
+ *   bc_stride   storage of B and C:
+ *                 0   dense [batch, dstate, seqlen] as written above;
+ *                 >0  token-major: element (b, n, t) at (b*seqlen + t)*bc_stride
+ *                     + n, i.e. the [batch, dstate, seqlen] tensors are
+ *                     transposed views of [batch, seqlen, >= dstate] memory.
+ *                     This is how the page's projection produces B and C (it
+ *                     splits the projected tokens and passes transposed
+ *                     views); both layouts are read in place.
+ *                     Requires bc_stride >= dstate.
  * For vm_pool_scan_repeat the shapes differ (see there).
  */
 typedef struct vm_scan_dir {
@@ -83,6 +92,7 @@ typedef struct vm_scan_dir {
   const void *C;
   const float *D;
   const float *delta_bias;
+  int64_t bc_stride;
 } vm_scan_dir;
 
 /*
@@ -97,7 +107,6 @@ typedef struct vm_scan_dir {
  * token tensor, scanning forward and reversing the result ([Vim] "Two scans
  * meet at the same token").  All tensors stay in original token order.
  *   z, out: [batch, dim, seqlen] (dtype).  dstate in [1, 16].
- * Temporary memory: with VM_BF16, fp32 copies of B and C.
  */
 int vm_selective_scan_fwd(const vm_scan_dir *p, const void *z, void *out,
                           int64_t batch, int64_t dim, int64_t seqlen,
@@ -113,9 +122,9 @@ int vm_selective_scan_fwd(const vm_scan_dir *p, const void *z, void *out,
  * `bwd` (its own u, delta, A, B, C, D, bias), returned in original order.
  * combine_scale = 0.5 is the released averaging model, 1 the summed form.
  * z may be NULL (no gate).  out: [batch, dim, seqlen] (dtype).
- * Temporary memory: with VM_BF16, fp32 copies of the four B/C tensors; for
- * sequences too long for the on-chip exchange buffer (seqlen > ~250), an fp32
- * [batch, dim, seqlen] exchange buffer (VM_F32 reuses `out` for it).
+ * Temporary memory: for sequences too long for the on-chip exchange buffer
+ * (seqlen > ~250), an fp32 [batch, dim, seqlen] exchange buffer when dtype is
+ * VM_BF16 (VM_F32 reuses `out` for it).
  */
 int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
                       const void *z, float combine_scale, void *out,
@@ -166,7 +175,7 @@ int vm_atrous_scatter(const void *streams, void *y, int64_t batch,
  * delta_bias as for vm_selective_scan_fwd.  The D skip acts on the pooled u.
  * z, out: [batch, dim, H, W].  z may be NULL.  Temporary memory: fp32
  * [batch, dim, Lp] buffers for the pooled u of each direction and the scan
- * result (plus fp32 copies of delta, B and C with VM_BF16).
+ * result, and fp32 copies of delta, B and C with VM_BF16.
  */
 int vm_pool_scan_repeat(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
                         const void *z, float combine_scale, void *out,

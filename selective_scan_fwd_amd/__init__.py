@@ -35,7 +35,7 @@ class VmScanDir(ctypes.Structure):
     """struct vm_scan_dir (one scan direction's device pointers)."""
     _fields_ = [("u", ctypes.c_void_p), ("delta", ctypes.c_void_p), ("A", ctypes.c_void_p),
                 ("B", ctypes.c_void_p), ("C", ctypes.c_void_p), ("D", ctypes.c_void_p),
-                ("delta_bias", ctypes.c_void_p)]
+                ("delta_bias", ctypes.c_void_p), ("bc_stride", ctypes.c_int64)]
 
 
 class VmError(RuntimeError):
@@ -115,6 +115,25 @@ def _dev(t: torch.Tensor, name: str, dtype=None, shape=None, device=None):
     return t
 
 
+def _bc(t: torch.Tensor, name: str, dtype, shape, device):
+    """B or C [batch, N, L]: dense, or a transposed view of token-major
+    [batch, L, >= N] memory.  Returns the C ABI's bc_stride (0 = dense)."""
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.device != device:
+        raise ValueError(f"{name} must be a tensor on {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    batch, n, L = shape
+    if t.is_contiguous():
+        return 0
+    sb, sn, st = t.stride()
+    if sn == 1 and st >= n and (sb == L * st or batch == 1):
+        return st
+    raise ValueError(f"{name} must be dense [batch, N, L] or a transposed view of token-major "
+                     f"[batch, L, >= N] memory (strides {t.stride()})")
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -128,14 +147,17 @@ def _direction(p, batch, dim, u_shape, tok_len, dstate, dt, device, name):
     u = _dev(p["u"], f"{name}.u", dt, u_shape, device)
     delta = _dev(p["delta"], f"{name}.delta", dt, (batch, dim, tok_len), device)
     A = _dev(p["A"], f"{name}.A", torch.float32, (dim, dstate), device)
-    B = _dev(p["B"], f"{name}.B", dt, (batch, dstate, tok_len), device)
-    C = _dev(p["C"], f"{name}.C", dt, (batch, dstate, tok_len), device)
+    B, C = p["B"], p["C"]
+    sB = _bc(B, f"{name}.B", dt, (batch, dstate, tok_len), device)
+    sC = _bc(C, f"{name}.C", dt, (batch, dstate, tok_len), device)
+    if sB != sC:
+        raise ValueError(f"{name}.B and {name}.C must share one layout (bc strides {sB} vs {sC})")
     D = _dev(p["D"], f"{name}.D", torch.float32, (dim,), device)
     bias = p.get("delta_bias")
     if bias is not None:
         bias = _dev(bias, f"{name}.delta_bias", torch.float32, (dim,), device)
     s = VmScanDir(u.data_ptr(), delta.data_ptr(), A.data_ptr(), B.data_ptr(), C.data_ptr(),
-                  D.data_ptr(), bias.data_ptr() if bias is not None else None)
+                  D.data_ptr(), bias.data_ptr() if bias is not None else None, sB)
     return s, (u, delta, A, B, C, D, bias)
 
 
@@ -143,8 +165,10 @@ def _direction(p, batch, dim, u_shape, tok_len, dstate, dt, device, name):
 def vm_selective_scan_fwd(u, delta, A, B, C, D, z=None, delta_bias=None, delta_softplus=True,
                           reverse=False, out=None):
     """One-direction selective scan; returns out shaped like u.
-    u, delta, z: [batch, dim, L]; A: [dim, N] fp32; B, C: [batch, N, L];
-    D, delta_bias: [dim] fp32.  reverse=True visits t = L-1 .. 0."""
+    u, delta, z: [batch, dim, L]; A: [dim, N] fp32; B, C: [batch, N, L]
+    (dense, or transposed views of token-major [batch, L, N] memory, which
+    the kernels read directly); D, delta_bias: [dim] fp32.
+    reverse=True visits t = L-1 .. 0."""
     dt = u.dtype
     batch, dim, L = u.shape
     N = A.shape[-1]

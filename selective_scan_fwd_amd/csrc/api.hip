@@ -44,17 +44,26 @@ bool dims_ok(std::initializer_list<int64_t> dims, int64_t *prod) {
 
 bool flag_ok(int f) { return f == 0 || f == 1; }
 
+// Element extent of B or C: dense [batch, dstate, L], or token-major with
+// stride bcs (last element at ((batch*L - 1)*bcs + dstate - 1)).
+int64_t bc_extent(int64_t batch, int64_t dstate, int64_t L, int64_t bcs) {
+  return bcs > 0 ? (batch * L - 1) * bcs + dstate : batch * dstate * L;
+}
+
 // Checks of one scan direction.  u_elems / tok_elems: elements of u and of
-// delta; bc_elems: elements of B and C; dim, dstate: parameter shapes.
-int check_dir(const vm_scan_dir *p, int64_t u_elems, int64_t tok_elems, int64_t bc_elems,
-              int64_t dim, int64_t dstate, int esize, Span out, bool bias_ok_null = true) {
-  (void)bias_ok_null;
+// delta; L: length of delta, B and C; dim, dstate: parameter shapes.
+int check_dir(const vm_scan_dir *p, int64_t u_elems, int64_t tok_elems, int64_t batch, int64_t L,
+              int64_t dim, int64_t dstate, int esize, Span out) {
   if (p == nullptr || p->u == nullptr || p->delta == nullptr || p->A == nullptr ||
       p->B == nullptr || p->C == nullptr || p->D == nullptr)
     return VM_ERR_NULL;
+  int64_t unused = 0;
+  if (p->bc_stride < 0 || (p->bc_stride > 0 && p->bc_stride < dstate)) return VM_ERR_SHAPE;
+  if (p->bc_stride > 0 && !dims_ok({batch, L, p->bc_stride}, &unused)) return VM_ERR_SHAPE;
+  const int64_t bc = bc_extent(batch, dstate, L, p->bc_stride);
   const Span ins[] = {span(p->u, u_elems * esize), span(p->delta, tok_elems * esize),
-                      span(p->A, dim * dstate * 4), span(p->B, bc_elems * esize),
-                      span(p->C, bc_elems * esize), span(p->D, dim * 4),
+                      span(p->A, dim * dstate * 4), span(p->B, bc * esize),
+                      span(p->C, bc * esize), span(p->D, dim * 4),
                       span(p->delta_bias, dim * 4)};
   for (const Span &s : ins)
     if (overlaps(s, out)) return VM_ERR_ALIAS;
@@ -98,19 +107,20 @@ class Scratch {
   ~Scratch() {
     for (void *p : ptrs_) (void)hipFreeAsync(p, s_);
   }
-  float *get(int64_t floats, int *status) {
+  void *bytes(int64_t n, int *status) {
     if (*status != VM_OK) return nullptr;
     hipMemPool_t pool;
     void *p = nullptr;
     if (pool_for_current_device(&pool) != hipSuccess ||
-        hipMallocFromPoolAsync(&p, static_cast<size_t>(floats) * 4, pool, s_) != hipSuccess) {
+        hipMallocFromPoolAsync(&p, static_cast<size_t>(n), pool, s_) != hipSuccess) {
       (void)hipGetLastError();
       *status = VM_ERR_ALLOC;
       return nullptr;
     }
     ptrs_.push_back(p);
-    return static_cast<float *>(p);
+    return p;
   }
+  float *get(int64_t floats, int *status) { return static_cast<float *>(bytes(floats * 4, status)); }
 
  private:
   hipStream_t s_;
@@ -128,23 +138,34 @@ const float *as_f32(const void *src, int64_t n, bool bf16, Scratch &ws, hipStrea
   return dst;
 }
 
-// B and C of one direction packed step-major into fp32 [batch, L, 32].
-const float *pack_bc(const vm_scan_dir *p, int64_t batch, int64_t dstate, int64_t L, bool bf16,
-                     Scratch &ws, hipStream_t s, int *status) {
-  float *bc = ws.get(batch * L * vmk::kBCStride, status);
-  if (*status == VM_OK)
-    *status = hip_status(vmk::launch_bc_pack(p->B, p->C, bc, batch, dstate, L, bf16, s));
-  return bc;
-}
-
-vmk::DirPtrs dir_ptrs(const vm_scan_dir *p, const float *BC) {
-  vmk::DirPtrs d;
+// Pointers and B/C strides of one direction for the scan kernel, which reads
+// dense [batch, dstate, L] and token-major B and C alike.  widen_bc: the
+// kernel runs in fp32 on bf16 B and C (pooled path), so they are widened into
+// temporary memory with the same layout first.
+vmk::DirPtrs resolve_dir(const vm_scan_dir *p, int64_t batch, int64_t dstate, int64_t L,
+                         bool widen_bc, Scratch &ws, hipStream_t s, int *status) {
+  vmk::DirPtrs d = {};
   d.u = p->u;
   d.delta = p->delta;
   d.A = p->A;
-  d.BC = BC;
   d.D = p->D;
   d.bias = p->delta_bias;
+  d.B = p->B;
+  d.C = p->C;
+  if (p->bc_stride > 0) {
+    d.bsb = L * p->bc_stride;
+    d.bsn = 1;
+    d.bst = p->bc_stride;
+  } else {
+    d.bsb = dstate * L;
+    d.bsn = L;
+    d.bst = 1;
+  }
+  if (widen_bc) {
+    const int64_t n = bc_extent(batch, dstate, L, p->bc_stride);
+    d.B = as_f32(p->B, n, true, ws, s, status);
+    d.C = as_f32(p->C, n, true, ws, s, status);
+  }
   return d;
 }
 
@@ -186,17 +207,16 @@ int vm_selective_scan_fwd(const vm_scan_dir *p, const void *z, void *out, int64_
   if (out == nullptr) return VM_ERR_NULL;
   const int es = dtype == VM_BF16 ? 2 : 4;
   const Span so = span(out, tok * es);
-  int st = check_dir(p, tok, tok, bc, dim, dstate, es, so);
+  int st = check_dir(p, tok, tok, batch, seqlen, dim, dstate, es, so);
   if (st != VM_OK) return st;
   if (overlaps(span(z, tok * es), so)) return VM_ERR_ALIAS;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == VM_BF16;
   Scratch ws(s);
-  const float *BC = pack_bc(p, batch, dstate, seqlen, bf16, ws, s, &st);
-  if (st != VM_OK) return st;
   vmk::ScanArgs a = {};
-  a.dir[0] = a.dir[1] = dir_ptrs(p, BC);
+  a.dir[0] = a.dir[1] = resolve_dir(p, batch, dstate, seqlen, false, ws, s, &st);
+  if (st != VM_OK) return st;
   a.z = z;
   a.out = out;
   a.batch = batch;
@@ -223,20 +243,18 @@ int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
   if (out == nullptr) return VM_ERR_NULL;
   const int es = dtype == VM_BF16 ? 2 : 4;
   const Span so = span(out, tok * es);
-  int st = check_dir(fwd, tok, tok, bc, dim, dstate, es, so);
-  if (st == VM_OK) st = check_dir(bwd, tok, tok, bc, dim, dstate, es, so);
+  int st = check_dir(fwd, tok, tok, batch, seqlen, dim, dstate, es, so);
+  if (st == VM_OK) st = check_dir(bwd, tok, tok, batch, seqlen, dim, dstate, es, so);
   if (st != VM_OK) return st;
   if (overlaps(span(z, tok * es), so)) return VM_ERR_ALIAS;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == VM_BF16;
   Scratch ws(s);
-  const float *BCf = pack_bc(fwd, batch, dstate, seqlen, bf16, ws, s, &st);
-  const float *BCb = pack_bc(bwd, batch, dstate, seqlen, bf16, ws, s, &st);
-  if (st != VM_OK) return st;
   vmk::ScanArgs a = {};
-  a.dir[0] = dir_ptrs(fwd, BCf);
-  a.dir[1] = dir_ptrs(bwd, BCb);
+  a.dir[0] = resolve_dir(fwd, batch, dstate, seqlen, false, ws, s, &st);
+  a.dir[1] = resolve_dir(bwd, batch, dstate, seqlen, false, ws, s, &st);
+  if (st != VM_OK) return st;
   a.z = z;
   a.out = out;
   a.batch = batch;
@@ -248,8 +266,14 @@ int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
   a.scale = combine_scale;
   const vmk::ScanPlan plan = vmk::plan_scan(batch, dim, seqlen, a.dstate, 2);
   if (plan.xmode == vmk::kXGlobal) {
-    a.xglobal = bf16 ? ws.get(tok, &st) : static_cast<float *>(out);
-    if (st != VM_OK) return st;
+    // fp32 output with line-aligned rows doubles as the exchange buffer
+    a.xstride = vmk::xchg_global_stride(seqlen);
+    if (!bf16 && a.xstride == seqlen && reinterpret_cast<uintptr_t>(out) % 128 == 0) {
+      a.xglobal = static_cast<float *>(out);
+    } else {
+      a.xglobal = ws.get(batch * dim * a.xstride, &st);
+      if (st != VM_OK) return st;
+    }
   }
   return hip_status(vmk::launch_scan(plan, a, bf16, s));
 }
@@ -300,8 +324,8 @@ int vm_pool_scan_repeat(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const vo
   if (out == nullptr) return VM_ERR_NULL;
   const int es = dtype == VM_BF16 ? 2 : 4;
   const Span so = span(out, full * es);
-  int st = check_dir(fwd, full, pooled, bc, dim, dstate, es, so);
-  if (st == VM_OK && bwd != nullptr) st = check_dir(bwd, full, pooled, bc, dim, dstate, es, so);
+  int st = check_dir(fwd, full, pooled, batch, Lp, dim, dstate, es, so);
+  if (st == VM_OK && bwd != nullptr) st = check_dir(bwd, full, pooled, batch, Lp, dim, dstate, es, so);
   if (st != VM_OK) return st;
   if (overlaps(span(z, full * es), so)) return VM_ERR_ALIAS;
 
@@ -319,9 +343,8 @@ int vm_pool_scan_repeat(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const vo
     st = hip_status(vmk::launch_mean_pool(p->u, ubar, batch * dim, height, width, pool_axis,
                                           bf16, s));
     const float *dl = as_f32(p->delta, pooled, bf16, ws, s, &st);
-    const float *BC = pack_bc(p, batch, dstate, Lp, bf16, ws, s, &st);
+    vmk::DirPtrs d = resolve_dir(p, batch, dstate, Lp, bf16, ws, s, &st);
     if (st != VM_OK) return st;
-    vmk::DirPtrs d = dir_ptrs(p, BC);
     d.u = ubar;
     d.delta = dl;
     a.dir[k] = d;
@@ -337,7 +360,11 @@ int vm_pool_scan_repeat(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const vo
   a.reverse = 0;
   a.scale = 1.0f;
   const vmk::ScanPlan plan = vmk::plan_scan(batch, dim, Lp, a.dstate, ndir);
-  if (plan.xmode == vmk::kXGlobal) a.xglobal = y;
+  if (plan.xmode == vmk::kXGlobal) {
+    a.xstride = vmk::xchg_global_stride(Lp);
+    a.xglobal = ws.get(batch * dim * a.xstride, &st);
+    if (st != VM_OK) return st;
+  }
   st = hip_status(vmk::launch_scan(plan, a, /*bf16=*/false, s));
   if (st != VM_OK) return st;
   return hip_status(vmk::launch_repeat_gate(y, z, out, batch * dim, height, width, pool_axis,

@@ -4,8 +4,7 @@
 //    adding directions"),
 //  * mean pooling over one grid axis and the repeat + SiLU gate back to the
 //    full grid (FastVim summary, "Methodology"),
-//  * bf16 -> fp32 widening of small side tensors, and the step-major packing
-//    of B and C the scan kernel reads with scalar loads.
+//  * bf16 -> fp32 widening of small side tensors.
 // All of these are HBM-bound streaming kernels: every element is read once
 // and written once with coalesced accesses.
 #include "vm_internal.h"
@@ -134,35 +133,6 @@ to_f32_kernel(const bf16_t *__restrict__ src, float *__restrict__ dst, int64_t n
     dst[e] = to_f32(src[e]);
 }
 
-// B, C [batch, dstate, L] (T) -> BC [batch, L, 32] fp32.  One workgroup per
-// (b, 64-step tile): rows of B and C are read coalesced along t into LDS,
-// then each step's 128-byte record is written coalesced.
-template <typename T>
-__global__ void __launch_bounds__(kThreads)
-bc_pack_kernel(const T *__restrict__ B, const T *__restrict__ C, float *__restrict__ BC,
-               int dstate, int64_t L, int tiles) {
-  __shared__ float tile[2 * 16][65];
-  const int64_t b = blockIdx.x / tiles;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x - b * tiles) * 64;
-  for (int e = threadIdx.x; e < 2 * 16 * 64; e += kThreads) {
-    const int slot = e >> 6, tt = e & 63;
-    const int n = slot & 15;
-    const int64_t t = t0 + tt;
-    float v = 0.0f;
-    if (n < dstate && t < L) {
-      const T *src = slot < 16 ? B : C;
-      v = to_f32(src[(b * dstate + n) * L + t]);
-    }
-    tile[slot][tt] = v;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < 64 * 2 * 16; e += kThreads) {
-    const int tt = e >> 5, slot = e & 31;
-    const int64_t t = t0 + tt;
-    if (t < L) BC[(b * L + t) * kBCStride + slot] = tile[slot][tt];
-  }
-}
-
 unsigned stream_grid(int64_t n) {
   int64_t g = (n + kThreads - 1) / kThreads;
   const int64_t cap = 256 * 64;   // 64 workgroups per CU, grid-stride beyond
@@ -229,22 +199,6 @@ hipError_t launch_repeat_gate(const float *y, const void *z, void *out, int64_t 
     hipLaunchKernelGGL(repeat_gate_kernel<float>, dim3(static_cast<unsigned>(rows)), dim3(kThreads),
                        0, s, y, static_cast<const float *>(z), static_cast<float *>(out),
                        static_cast<int>(H), static_cast<int>(W), axis, scale);
-  return hipGetLastError();
-}
-
-hipError_t launch_bc_pack(const void *B, const void *C, float *BC, int64_t batch, int64_t dstate,
-                          int64_t L, bool bf16, hipStream_t s) {
-  const int64_t tiles = (L + 63) / 64;
-  if (batch * tiles == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(batch * tiles));
-  if (bf16)
-    hipLaunchKernelGGL(bc_pack_kernel<bf16_t>, grid, dim3(kThreads), 0, s,
-                       static_cast<const bf16_t *>(B), static_cast<const bf16_t *>(C), BC,
-                       static_cast<int>(dstate), L, static_cast<int>(tiles));
-  else
-    hipLaunchKernelGGL(bc_pack_kernel<float>, grid, dim3(kThreads), 0, s,
-                       static_cast<const float *>(B), static_cast<const float *>(C), BC,
-                       static_cast<int>(dstate), L, static_cast<int>(tiles));
   return hipGetLastError();
 }
 

@@ -62,17 +62,13 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
 }
 
 // ---------------------------------------------------------------- scan
-// B and C of one direction packed step-major: BC[b, t, 0..15] = B[b, 0..15, t]
-// and BC[b, t, 16..31] = C[b, 0..15, t], fp32, zero for states >= dstate.
-// One 128-byte record per (b, t) lets a wave fetch its states' B and C for a
-// step with scalar loads off a single base pointer.
-constexpr int kBCStride = 32;
-
 struct DirPtrs {
   const void *u;        // [batch, dim, L] (Tin)
   const void *delta;    // [batch, dim, L] (Tin)
   const float *A;       // [dim, dstate]
-  const float *BC;      // [batch, L, 32] fp32 (packed B and C)
+  const void *B;        // element (b, n, t) at b*bsb + n*bsn + t*bst (Tin)
+  const void *C;        // same layout as B
+  int64_t bsb, bsn, bst;
   const float *D;       // [dim]
   const float *bias;    // [dim] or nullptr
 };
@@ -81,7 +77,8 @@ struct ScanArgs {
   DirPtrs dir[2];
   const void *z;        // [batch, dim, L] (Tin) or nullptr
   void *out;            // [batch, dim, L] (Tin)
-  float *xglobal;       // fp32 [batch, dim, L] exchange buffer (long bidirectional)
+  float *xglobal;       // fp32 exchange rows (long bidirectional), row stride xstride
+  int64_t xstride;
   int64_t batch, dim, L;
   int dstate;
   int softplus;
@@ -92,16 +89,19 @@ struct ScanArgs {
 enum XMode { kXNone = 0, kXLds = 1, kXGlobal = 2 };
 
 struct ScanPlan {
-  int S;        // state groups (waves) per direction
-  int T;        // tile length (steps between workgroup barriers)
+  int S;        // lanes sharing one channel's 16 states (state split)
+  int T;        // tile length in steps
   int dirs;     // 1 or 2
   int xmode;    // XMode
-  size_t lds;   // dynamic LDS bytes
-  int threads;  // workgroup size
+  size_t lds;   // dynamic LDS bytes per wave
+  int threads;  // workgroup size (one wave)
   int64_t blocks;
 };
 
 ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t L, int dstate, int dirs);
+// Row stride (floats) of the global exchange buffer: rows padded to whole
+// 128-byte lines so that no two channels' parked partials share a line.
+int64_t xchg_global_stride(int64_t L);
 hipError_t launch_scan(const ScanPlan &plan, const ScanArgs &args, bool bf16, hipStream_t s);
 
 // ---------------------------------------------------------------- layout
@@ -114,7 +114,5 @@ hipError_t launch_mean_pool(const void *u, float *pooled, int64_t rows, int64_t 
 hipError_t launch_repeat_gate(const float *y, const void *z, void *out, int64_t rows, int64_t H,
                               int64_t W, int axis, float scale, bool bf16, hipStream_t s);
 hipError_t launch_to_f32(const void *src, float *dst, int64_t n, hipStream_t s);
-hipError_t launch_bc_pack(const void *B, const void *C, float *BC, int64_t batch, int64_t dstate,
-                          int64_t L, bool bf16, hipStream_t s);
 
 }  // namespace vmk

@@ -16,6 +16,12 @@ Distributions (the same for every workload):
 ``perturb=True`` multiplies A by (1 + 0.25 U(0,1)) and D by (1 + 0.25 N(0,1))
 per element so that parity tests catch swapped directions or parameters.
 
+B and C are returned with shape [batch, N, L] as the pages index them.  With
+``bc_layout="token"`` (the default) they are transposed views of token-major
+[batch, L, N] storage, which is how the page's projection produces them (it
+splits the projected tokens and passes transposed views to the scan); with
+``bc_layout="dense"`` they are contiguous [batch, N, L] tensors.
+
 Token geometry (Vision Mamba page, "From pixels to position-aware tokens"):
 a 224x224 image with 16x16 windows gives 14x14 = 196 patches plus a middle
 CLS token, L = 197; a 1024x1024 image gives 64x64 + 1 = 4097.
@@ -76,6 +82,19 @@ def _normal(g, shape, device, dtype):
     return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(dtype)
 
 
+def _bc_pair(g, batch, dstate, L, device, dtype, bc_layout):
+    """B, C of shape [batch, dstate, L] in the requested storage layout."""
+    if bc_layout == "token":
+        B = _normal(g, (batch, L, dstate), device, dtype).transpose(1, 2)
+        C = _normal(g, (batch, L, dstate), device, dtype).transpose(1, 2)
+    elif bc_layout == "dense":
+        B = _normal(g, (batch, dstate, L), device, dtype)
+        C = _normal(g, (batch, dstate, L), device, dtype)
+    else:
+        raise ValueError(bc_layout)
+    return B, C
+
+
 def scan_params(g, dim, dstate=DSTATE, device="cpu", perturb=False):
     """A [dim, dstate], D [dim], delta_bias [dim] (always fp32)."""
     A = -torch.arange(1, dstate + 1, device=device, dtype=torch.float32).repeat(dim, 1)
@@ -88,39 +107,38 @@ def scan_params(g, dim, dstate=DSTATE, device="cpu", perturb=False):
 
 
 def scan_direction(g, batch, dim, seqlen, dstate=DSTATE, device="cpu", dtype=torch.float32,
-                   perturb=False, u_shape=None, delta_len=None):
+                   perturb=False, u_shape=None, delta_len=None, bc_layout="token"):
     """One direction's tensors: u, delta [batch, dim, L]; B, C [batch, dstate, L];
     A, D, delta_bias.  u_shape / delta_len override the u shape and the length
     of delta/B/C (FastVim: full-resolution u, pooled delta/B/C)."""
     L = seqlen if delta_len is None else delta_len
     u = _normal(g, u_shape or (batch, dim, seqlen), device, dtype)
     delta = _normal(g, (batch, dim, L), device, dtype)
-    B = _normal(g, (batch, dstate, L), device, dtype)
-    C = _normal(g, (batch, dstate, L), device, dtype)
+    B, C = _bc_pair(g, batch, dstate, L, device, dtype, bc_layout)
     A, D, bias = scan_params(g, dim, dstate, device, perturb)
     return dict(u=u, delta=delta, A=A, B=B, C=C, D=D, delta_bias=bias)
 
 
 def single_inputs(seed, batch, dim, seqlen, dstate=DSTATE, device="cpu", dtype=torch.float32,
-                  gated=True, perturb=False):
+                  gated=True, perturb=False, bc_layout="token"):
     g = generator(seed, device)
-    p = scan_direction(g, batch, dim, seqlen, dstate, device, dtype, perturb)
+    p = scan_direction(g, batch, dim, seqlen, dstate, device, dtype, perturb, bc_layout=bc_layout)
     z = _normal(g, (batch, dim, seqlen), device, dtype) if gated else None
     return p, z
 
 
 def bidir_inputs(seed, batch, dim, seqlen, dstate=DSTATE, device="cpu", dtype=torch.float32,
-                 gated=True, perturb=False):
+                 gated=True, perturb=False, bc_layout="token"):
     """Forward then backward direction (each with its own parameters), then z."""
     g = generator(seed, device)
-    fwd = scan_direction(g, batch, dim, seqlen, dstate, device, dtype, False)
-    bwd = scan_direction(g, batch, dim, seqlen, dstate, device, dtype, perturb)
+    fwd = scan_direction(g, batch, dim, seqlen, dstate, device, dtype, False, bc_layout=bc_layout)
+    bwd = scan_direction(g, batch, dim, seqlen, dstate, device, dtype, perturb, bc_layout=bc_layout)
     z = _normal(g, (batch, dim, seqlen), device, dtype) if gated else None
     return fwd, bwd, z
 
 
 def es2d_inputs(seed, batch, channels, height, width, dstate=DSTATE, device="cpu",
-                dtype=torch.float32, perturb=False):
+                dtype=torch.float32, perturb=False, bc_layout="token"):
     """Feature map x [batch, channels, H, W] and the per-group scan's delta
     [4*batch, channels, Lg] and B, C [4*batch, dstate, Lg], drawn directly in
     gathered layout (pad steps included), plus A, D, delta_bias."""
@@ -128,14 +146,13 @@ def es2d_inputs(seed, batch, channels, height, width, dstate=DSTATE, device="cpu
     Lg = ((height + 1) // 2) * ((width + 1) // 2)
     x = _normal(g, (batch, channels, height, width), device, dtype)
     delta = _normal(g, (4 * batch, channels, Lg), device, dtype)
-    B = _normal(g, (4 * batch, dstate, Lg), device, dtype)
-    C = _normal(g, (4 * batch, dstate, Lg), device, dtype)
+    B, C = _bc_pair(g, 4 * batch, dstate, Lg, device, dtype, bc_layout)
     A, D, bias = scan_params(g, channels, dstate, device, perturb)
     return x, dict(delta=delta, A=A, B=B, C=C, D=D, delta_bias=bias)
 
 
 def fastvim_inputs(seed, batch, dim, height, width, pool_axis, dstate=DSTATE, device="cpu",
-                   dtype=torch.float32, perturb=False, full_resolution=False):
+                   dtype=torch.float32, perturb=False, full_resolution=False, bc_layout="token"):
     """Per direction: full-resolution u [batch, dim, H, W], pooled-token delta
     [batch, dim, Lp] and B, C [batch, dstate, Lp]; then z [batch, dim, H, W].
     With full_resolution=True the directions instead carry delta [batch, dim,
@@ -148,8 +165,7 @@ def fastvim_inputs(seed, batch, dim, height, width, pool_axis, dstate=DSTATE, de
     for k in range(2):
         u = _normal(g, (batch, dim, height, width), device, dtype)
         delta = _normal(g, (batch, dim, L), device, dtype)
-        B = _normal(g, (batch, dstate, L), device, dtype)
-        C = _normal(g, (batch, dstate, L), device, dtype)
+        B, C = _bc_pair(g, batch, dstate, L, device, dtype, bc_layout)
         A, D, bias = scan_params(g, dim, dstate, device, perturb and k == 1)
         dirs.append(dict(u=u, delta=delta, A=A, B=B, C=C, D=D, delta_bias=bias))
     z = _normal(g, (batch, dim, height, width), device, dtype)

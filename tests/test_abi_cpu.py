@@ -95,6 +95,15 @@ def test_scan_argument_checks(lib):
     assert _scan(lib, d=d, out=d.delta + 8) == 5
     assert _scan(lib, d=d, out=d.B) == 5
     assert _scan(lib, z=FAKE * 3, out=FAKE * 3) == 5
+    # token-major B / C: stride must cover dstate; overlap uses the strided extent
+    d = _dir(FAKE)
+    d.bc_stride = -1
+    assert _scan(lib, d=d) == 2
+    d.bc_stride = 15
+    assert _scan(lib, d=d) == 2
+    d = _dir(FAKE)
+    d.bc_stride = 1 << 20                 # B extent = (2*5-1) * 2^20 + 16 elements
+    assert _scan(lib, d=d, out=d.B + 4 * (9 << 20)) == 5
 
 
 def test_bidir_argument_checks(lib):

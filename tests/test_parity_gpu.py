@@ -40,9 +40,11 @@ def _need_gpu():
                                            (2, 70, 33, 5), (1, 96, 197, 1), (2, 33, 150, 16)])
 @pytest.mark.parametrize("reverse", [False, True])
 @pytest.mark.parametrize("gated", [True, False])
-def test_single_fp32(batch, dim, L, N, reverse, gated):
-    _case(f"single fp32 b{batch} d{dim} L{L} N{N} rev{reverse} gated{gated}")
-    p, z = wl.single_inputs(100 + L, batch, dim, L, N, device=DEV, gated=gated, perturb=True)
+@pytest.mark.parametrize("bc_layout", ["token", "dense"])
+def test_single_fp32(batch, dim, L, N, reverse, gated, bc_layout):
+    _case(f"single fp32 b{batch} d{dim} L{L} N{N} rev{reverse} gated{gated} bc {bc_layout}")
+    p, z = wl.single_inputs(100 + L, batch, dim, L, N, device=DEV, gated=gated, perturb=True,
+                            bc_layout=bc_layout)
     out = vm.vm_selective_scan_fwd(**p, z=z, reverse=reverse)
     torch.cuda.synchronize()
     ref = oracle.selective_scan(**host_dir(p), z=host(z), reverse=reverse)
@@ -93,9 +95,11 @@ BIDIR_CASES = [
 
 
 @pytest.mark.parametrize("batch,dim,L", BIDIR_CASES)
-def test_bidir_fp32(batch, dim, L):
-    _case(f"bidir fp32 b{batch} d{dim} L{L}")
-    fwd, bwd, z = wl.bidir_inputs(200 + L, batch, dim, L, device=DEV, perturb=True)
+@pytest.mark.parametrize("bc_layout", ["token", "dense"])
+def test_bidir_fp32(batch, dim, L, bc_layout):
+    _case(f"bidir fp32 b{batch} d{dim} L{L} bc {bc_layout}")
+    fwd, bwd, z = wl.bidir_inputs(200 + L, batch, dim, L, device=DEV, perturb=True,
+                                  bc_layout=bc_layout)
     for scale in (1.0, 0.5):
         out = vm.vm_bidir_scan_fwd(fwd, bwd, z=z, combine_scale=scale)
         torch.cuda.synchronize()
@@ -113,13 +117,33 @@ def test_bidir_ungated_small_dstate():
 
 
 @pytest.mark.parametrize("L", [50, 333])
-def test_bidir_bf16(L):
-    _case(f"bidir bf16 L{L}")
-    fwd, bwd, z = wl.bidir_inputs(11 + L, 2, 100, L, device=DEV, dtype=torch.bfloat16, perturb=True)
+@pytest.mark.parametrize("bc_layout", ["token", "dense"])
+def test_bidir_bf16(L, bc_layout):
+    _case(f"bidir bf16 L{L} bc {bc_layout}")
+    fwd, bwd, z = wl.bidir_inputs(11 + L, 2, 100, L, device=DEV, dtype=torch.bfloat16, perturb=True,
+                                  bc_layout=bc_layout)
     out = vm.vm_bidir_scan_fwd(fwd, bwd, z=z)
     torch.cuda.synchronize()
     ref = oracle.bidir_scan(host_dir(fwd), host_dir(bwd), z=host(z))
     assert_close(host(out), ref, BF16_TOL, "bidir bf16")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_projection_split_layout(dtype):
+    # B and C as the page's projection yields them: slices of one token-major
+    # [batch, L, rank + 2N] tensor, passed as transposed views (token stride 44)
+    _case(f"projection-split B/C {dtype}")
+    batch, dim, L, N, rank = 2, 96, 70, 16, 12
+    fwd, bwd, z = wl.bidir_inputs(14, batch, dim, L, device=DEV, dtype=dtype, perturb=True)
+    for p in (fwd, bwd):
+        proj = torch.randn((batch, L, rank + 2 * N), device=DEV).to(dtype)
+        p["B"] = proj[:, :, rank:rank + N].transpose(1, 2)
+        p["C"] = proj[:, :, rank + N:].transpose(1, 2)
+        assert p["B"].stride() == (L * (rank + 2 * N), 1, rank + 2 * N)
+    out = vm.vm_bidir_scan_fwd(fwd, bwd, z=z)
+    torch.cuda.synchronize()
+    ref = oracle.bidir_scan(host_dir(fwd), host_dir(bwd), z=host(z))
+    assert_close(host(out), ref, FP32_TOL if dtype == torch.float32 else BF16_TOL, "proj split")
 
 
 def test_bidir_matches_two_single_calls():
