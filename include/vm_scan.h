@@ -51,7 +51,10 @@ enum {
   VM_ERR_DTYPE = 3,       /* unknown dtype                                    */
   VM_ERR_FLAG = 4,        /* a flag is not 0/1, or pool_axis not 0/1          */
   VM_ERR_ALIAS = 5,       /* the output overlaps an input                     */
-  VM_ERR_UNSUPPORTED = 6, /* dstate outside [1, 16], or a non-finite scale    */
+  VM_ERR_UNSUPPORTED = 6, /* dstate outside [1, 16], a non-finite scale, or
+                             sizes past the kernel's 32-bit offsets: 32 rows
+                             of seqlen + 16 steps, or one batch row of B or C,
+                             must span < 2 GiB                               */
   VM_ERR_HIP = 7,         /* a HIP launch or runtime call failed              */
   VM_ERR_ALLOC = 8        /* temporary device memory could not be obtained    */
 };

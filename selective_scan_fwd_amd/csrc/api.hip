@@ -181,7 +181,7 @@ const char *vm_status_string(int status) {
     case VM_ERR_DTYPE: return "VM_ERR_DTYPE: unknown dtype";
     case VM_ERR_FLAG: return "VM_ERR_FLAG: a flag is not 0 or 1";
     case VM_ERR_ALIAS: return "VM_ERR_ALIAS: the output overlaps an input";
-    case VM_ERR_UNSUPPORTED: return "VM_ERR_UNSUPPORTED: dstate outside [1, 16] or non-finite scale";
+    case VM_ERR_UNSUPPORTED: return "VM_ERR_UNSUPPORTED: dstate outside [1, 16], non-finite scale, or sizes past the 32-bit in-kernel offsets";
     case VM_ERR_HIP: return "VM_ERR_HIP: a HIP launch or runtime call failed";
     case VM_ERR_ALLOC: return "VM_ERR_ALLOC: temporary device memory unavailable";
     default: return "unknown status";
@@ -227,6 +227,7 @@ int vm_selective_scan_fwd(const vm_scan_dir *p, const void *z, void *out, int64_
   a.reverse = reverse;
   a.scale = 1.0f;
   const vmk::ScanPlan plan = vmk::plan_scan(batch, dim, seqlen, a.dstate, 1);
+  if (!vmk::scan_offsets_fit(plan, a, bf16)) return VM_ERR_UNSUPPORTED;
   return hip_status(vmk::launch_scan(plan, a, bf16, s));
 }
 
@@ -275,6 +276,7 @@ int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
       if (st != VM_OK) return st;
     }
   }
+  if (!vmk::scan_offsets_fit(plan, a, bf16)) return VM_ERR_UNSUPPORTED;
   return hip_status(vmk::launch_scan(plan, a, bf16, s));
 }
 
@@ -365,6 +367,7 @@ int vm_pool_scan_repeat(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const vo
     a.xglobal = ws.get(batch * dim * a.xstride, &st);
     if (st != VM_OK) return st;
   }
+  if (!vmk::scan_offsets_fit(plan, a, /*bf16=*/false)) return VM_ERR_UNSUPPORTED;
   st = hip_status(vmk::launch_scan(plan, a, /*bf16=*/false, s));
   if (st != VM_OK) return st;
   return hip_status(vmk::launch_repeat_gate(y, z, out, batch * dim, height, width, pool_axis,

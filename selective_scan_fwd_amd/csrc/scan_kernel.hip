@@ -75,6 +75,20 @@ __device__ __forceinline__ void state_step(float (&h)[NS], const float (&A2)[NS]
   }
 }
 
+// Ties a loaded value to this point of the program: nothing computed from it
+// can be scheduled earlier (next to its load), where the wait for the load
+// would also wait for the loads issued after it.
+__device__ __forceinline__ float pin(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+// The same for a computed offset, which then reaches the memory instruction
+// as one register (no splitting of the access by the select that chose it).
+__device__ __forceinline__ uint32_t pin_u(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Workgroup barrier that orders LDS only: global loads issued before it stay
 // in flight.
 __device__ __forceinline__ void lds_barrier() {
@@ -93,22 +107,53 @@ struct Layout {
   static constexpr int WAVE = PREP + BC + PART;           // floats per wave
 };
 
-// Row stride of the LDS exchange block: >= L and congruent to T mod 32, so
-// that a combine instruction (T consecutive steps of 64/T channels) hits 32
-// distinct banks.
-__host__ __device__ inline int xchg_stride(int64_t L, int T) {
-  return static_cast<int>(L + (((T - L) % 32) + 32) % 32);
+// Row stride of the LDS exchange block for n parked steps: >= n and
+// congruent to T mod 32, so that a combine instruction (T consecutive steps
+// of 64/T channels) hits 32 distinct banks.
+__host__ __device__ inline int xchg_stride(int64_t n, int T) {
+  return static_cast<int>(n + (((T - n) % 32) + 32) % 32);
 }
 
+// ---- buffer access.  Token tensors, B, C and the exchange rows are read
+// and written through buffer resources (base address and byte size in
+// scalar registers, a 32-bit byte offset per lane).  An offset at or past
+// the size reads 0 and drops a store, so masked elements need neither a
+// branch nor a select, and every lane issues the same memory instructions.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOob = 0x80000000u;   // past every resource (sizes < 2 GiB)
+
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+template <typename Tin> __device__ __forceinline__ float bload(Rsrc r, uint32_t off);
+template <> __device__ __forceinline__ float bload<float>(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
+}
+template <> __device__ __forceinline__ float bload<bf16_t>(Rsrc r, uint32_t off) {
+  return to_f32(static_cast<bf16_t>(__builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, 0)));
+}
+template <typename Tin> __device__ __forceinline__ void bstore(Rsrc r, uint32_t off, float v);
+template <> __device__ __forceinline__ void bstore<float>(Rsrc r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, static_cast<int>(off), 0, 0);
+}
+template <> __device__ __forceinline__ void bstore<bf16_t>(Rsrc r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(from_f32<bf16_t>(v)), r,
+                                        static_cast<int>(off), 0, 0);
+}
+
+// Register budget: 3 waves per SIMD at a two-lane state split, 4 at four.
 template <typename Tin, int SPLIT, int DIRS, int XMODE, int T>
-__global__ void __launch_bounds__(64 * DIRS)
+__global__ void __launch_bounds__(64 * DIRS) __attribute__((amdgpu_waves_per_eu(SPLIT == 2 ? 3 : 4)))
 scan_kernel(const ScanArgs p) {
   constexpr int NS = 16 / SPLIT;                 // states per lane
   constexpr int R = 64 / SPLIT;                  // channels per workgroup
   constexpr int PE = R * T / 64;                 // staged (dt, u) elements per lane per tile
-  constexpr int BE = T / 2;                      // staged B/C values per lane per tile
+  constexpr int BQ = T / 4;                      // B (and C) loads per lane per tile
+  constexpr uint32_t ES = sizeof(Tin);
   using Lay = Layout<T, R>;
-  static_assert(NS >= 4 && NS <= 8 && R % 16 == 0 && T % 2 == 0 && (R * T) % 64 == 0, "shape");
+  static_assert(NS >= 4 && NS <= 8 && R % 16 == 0 && T % 4 == 0 && (R * T) % 64 == 0, "shape");
+  static_assert(DIRS == 1 ? XMODE == kXNone : XMODE != kXNone, "mode");
 
   extern __shared__ float smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -120,30 +165,41 @@ scan_kernel(const ScanArgs p) {
 
   const int sp = lane / R;                       // state group
   const int r = lane % R;                        // channel within the block
-  const int dir = wave;                          // 0 forward, 1 backward
-  const bool rev = DIRS == 2 ? dir == 1 : p.reverse != 0;
+  const bool rev = DIRS == 2 ? wave == 1 : p.reverse != 0;
+  const bool fwd_wave = DIRS == 2 && wave == 0;
 
-  const int64_t dim = p.dim, L = p.L;
+  const int64_t dim = p.dim;
+  const int L = static_cast<int>(p.L);
   const int nrb = static_cast<int>((dim + R - 1) / R);
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int b = blk / nrb;
   const int d0 = (blk - b * nrb) * R;
   const int rows = static_cast<int>(dim - d0 < R ? dim - d0 : R);
-  const int nt = static_cast<int>((L + T - 1) / T);
+  const int nt = (L + T - 1) / T;
+  const int half = (nt + 1) / 2;                 // forward wave's first-visit tiles
   const int XS = xchg_stride(L, T);
   const int dstate = p.dstate;
+  const bool gated = p.z != nullptr;
 
-  const DirPtrs P = p.dir[DIRS == 2 ? wave : 0];  // wave-uniform selection
-  const Tin *__restrict__ gu = static_cast<const Tin *>(P.u);
-  const Tin *__restrict__ gdl = static_cast<const Tin *>(P.delta);
-  const Tin *__restrict__ gB = static_cast<const Tin *>(P.B);
-  const Tin *__restrict__ gC = static_cast<const Tin *>(P.C);
-  const Tin *__restrict__ gz = static_cast<const Tin *>(p.z);
-  Tin *__restrict__ gout = static_cast<Tin *>(p.out);
-  float *__restrict__ gx = p.xglobal;
-  const int64_t rowbase = (static_cast<int64_t>(b) * dim + d0) * L;  // element (b, d0, 0)
-  const int64_t xbase = (static_cast<int64_t>(b) * dim + d0) * p.xstride;
-  const int64_t bcbase = static_cast<int64_t>(b) * P.bsb;
+  // Resources: the block's [rows x L] slab of each token tensor (rows past
+  // dim are out of range), one batch row of B and C, the block's exchange
+  // rows (kXGlobal).
+  const DirPtrs P = p.dir[DIRS == 2 ? wave : 0];
+  const int64_t rowbase = (static_cast<int64_t>(b) * dim + d0) * L;
+  const uint32_t slab = static_cast<uint32_t>(rows) * static_cast<uint32_t>(L) * ES;
+  const Rsrc rU = make_rsrc(static_cast<const Tin *>(P.u) + rowbase, slab);
+  const Rsrc rD = make_rsrc(static_cast<const Tin *>(P.delta) + rowbase, slab);
+  const Rsrc rZ = make_rsrc(gated ? static_cast<const Tin *>(p.z) + rowbase : nullptr, gated ? slab : 0);
+  const Rsrc rO = make_rsrc(static_cast<Tin *>(p.out) + rowbase, slab);
+  const uint32_t bcext = (static_cast<uint32_t>(dstate - 1) * static_cast<uint32_t>(P.bsn) +
+                          static_cast<uint32_t>(L - 1) * static_cast<uint32_t>(P.bst) + 1) * ES;
+  const Rsrc rB = make_rsrc(static_cast<const Tin *>(P.B) + static_cast<int64_t>(b) * P.bsb, bcext);
+  const Rsrc rC = make_rsrc(static_cast<const Tin *>(P.C) + static_cast<int64_t>(b) * P.bsb, bcext);
+  const uint32_t xstride = static_cast<uint32_t>(p.xstride);
+  float *const xrow = XMODE == kXGlobal ? p.xglobal + (static_cast<int64_t>(b) * dim + d0) * p.xstride
+                                        : nullptr;
+  const uint32_t xbytes = static_cast<uint32_t>(rows) * xstride * 4u;
+  const Rsrc rX = make_rsrc(xrow, XMODE == kXGlobal ? xbytes : 0u);
 
   // ---- scan role: channel d0 + r, states n0 .. n0 + NS - 1 (states at or
   // beyond dstate have A = 0 and zero B/C, so they stay at zero)
@@ -161,198 +217,238 @@ scan_kernel(const ScanArgs p) {
   const int rl = lane & 15;
   const int bc_slot = rl < NS ? n0 + rl : (rl < 2 * NS ? 16 + n0 + rl - NS : 0);
 
-  // ---- staging role: element e = lane + 64 i of the R x T tile, (srow, sq)
-  // with the visit position sq fastest
-  int srow[PE], sq[PE];
+  // ---- staging role.  Element e = lane + 64 i of the R x T tile is (row
+  // srow_i = e / T, visit position sq = e % T); every element of a lane has
+  // the same sq, hence the same step offset tq within its tile (sq forward,
+  // T-1-sq backward): step t = jT + tq of tile j.  Per element: the byte
+  // offset of its step in tile 0 (rows past dim are past the slab), its
+  // exchange offsets and its bias.
+  const int sq = lane % T;
+  const int tq = rev ? T - 1 - sq : sq;
+  int srow[PE];
+  uint32_t ob[PE], oxl[PE], oxg[PE];
   float sbias[PE];
 #pragma unroll
   for (int i = 0; i < PE; ++i) {
-    const int e = lane + 64 * i;
-    srow[i] = e / T;
-    sq[i] = e % T;
+    srow[i] = lane / T + i * (64 / T);
+    ob[i] = (static_cast<uint32_t>(srow[i]) * static_cast<uint32_t>(L) + tq) * ES;
+    oxl[i] = static_cast<uint32_t>(srow[i] * XS + tq);
+    oxg[i] = (static_cast<uint32_t>(srow[i]) * xstride + tq) * 4u;
     sbias[i] = (P.bias != nullptr && srow[i] < rows) ? P.bias[d0 + srow[i]] : 0.0f;
   }
+  // B and C: load i of a lane covers visit position q = lane / 16 + 4 i and
+  // state n = lane % 16 (past dstate: out of range, so it stages 0).
+  const int n_bc = lane % 16;
+  uint32_t bo[BQ];
+#pragma unroll
+  for (int i = 0; i < BQ; ++i) {
+    const int q = lane / 16 + 4 * i;
+    const int qt = rev ? T - 1 - q : q;
+    bo[i] = n_bc < dstate ? (static_cast<uint32_t>(n_bc) * static_cast<uint32_t>(P.bsn) +
+                             static_cast<uint32_t>(qt) * static_cast<uint32_t>(P.bst)) * ES
+                          : kOob;
+  }
+  const uint32_t bst_bytes = static_cast<uint32_t>(P.bst) * ES;
 
-  // Tile of iteration k and the step at visit position q of tile j.
   auto tile_of = [&](int k) __attribute__((always_inline)) { return rev ? nt - 1 - k : k; };
-  auto step_of = [&](int j, int q) __attribute__((always_inline)) {
-    return static_cast<int64_t>(j) * T + (rev ? T - 1 - q : q);
+  // Byte offset of element i in tile j (jT = j T), or out of range for steps past L.
+  auto tok_off = [&](int i, int jT, bool in_seq) __attribute__((always_inline)) {
+    return pin_u(in_seq ? ob[i] + static_cast<uint32_t>(jT) * ES : kOob);
   };
 
-  // Raw global values of two tiles in flight (index = tile parity).  The loads
-  // are unconditional, at clamped in-bounds addresses, and nothing consumes
-  // them before the tile is staged: straight-line code with a static count of
-  // loads in flight lets the wait for an older tile leave the prefetch just
-  // issued in flight.  Which staged elements are real is kept as a bit mask
-  // (bit i: element i of the lane lies inside the row block and the sequence).
-  float ru[2][PE], rd[2][PE], rbc[2][BE];
-  unsigned okm[2];
-  const int lastrow = rows - 1;
-  bool bc_ok[BE];                                // B/C slot holds a real state
-#pragma unroll
-  for (int i = 0; i < BE; ++i) bc_ok[i] = ((lane + 64 * i) % 16) < dstate;
+  // Raw global values of two tiles in flight (index = tile parity).  Nothing
+  // reads them before the tile is staged: with a static count of loads in
+  // flight, the wait for an older tile leaves the prefetch just issued in
+  // flight.
+  float ru[2][PE], rd[2][PE], rb[2][BQ], rc[2][BQ];
 
   auto stage_load = [&](int k, auto par) __attribute__((always_inline)) {
     constexpr int Q = decltype(par)::value;
-    const int j = tile_of(k);
-    unsigned m = 0;
+    const int jT = tile_of(k) * T;
+    const bool in_seq = tq < L - jT;
 #pragma unroll
     for (int i = 0; i < PE; ++i) {
-      const int64_t t = step_of(j, sq[i]);
-      m |= (srow[i] < rows && t < L) ? 1u << i : 0u;
-      const int64_t off = rowbase + static_cast<int64_t>(srow[i] < rows ? srow[i] : lastrow) * L +
-                          (t < L ? t : L - 1);
-      ru[Q][i] = to_f32(gu[off]);
-      rd[Q][i] = to_f32(gdl[off]);
+      const uint32_t o = tok_off(i, jT, in_seq);
+      ru[Q][i] = bload<Tin>(rU, o);
+      rd[Q][i] = bload<Tin>(rD, o);
     }
-    okm[Q] = m;
+    const uint32_t tb = static_cast<uint32_t>(jT) * bst_bytes;
 #pragma unroll
-    for (int i = 0; i < BE; ++i) {
-      const int e = lane + 64 * i;               // (q, slot) of the T x 32 block
-      const int q = e / 32, slot = e % 32, n = slot % 16;
-      const int64_t t = step_of(j, q);
-      const int64_t off = bcbase + (n < dstate ? n : dstate - 1) * P.bsn + (t < L ? t : L - 1) * P.bst;
-      rbc[Q][i] = to_f32((slot < 16 ? gB : gC)[off]);
+    for (int i = 0; i < BQ; ++i) {
+      rb[Q][i] = bload<Tin>(rB, bo[i] + tb);
+      rc[Q][i] = bload<Tin>(rC, bo[i] + tb);
     }
   };
 
-  // Steps past L and channels past dim stage dt = u = 0, so the state stays
-  // where it is (zero before the first real step); B/C slots of states past
-  // dstate stage 0.  softplus is evaluated unconditionally and selected, which
-  // keeps the loop body free of branches.
+  // Steps past L and channels past dim stage u = 0, so the state only decays
+  // where it is zero (before the first real step) or no longer read; states
+  // past dstate stage B = C = 0.
   auto stage_store = [&](auto par) __attribute__((always_inline)) {
     constexpr int Q = decltype(par)::value;
     const bool sp_on = p.softplus != 0;
 #pragma unroll
     for (int i = 0; i < PE; ++i) {
-      const bool ok = (okm[Q] >> i) & 1u;
-      const float x = rd[Q][i] + sbias[i];
-      const float sx = softplus_f(x);
-      const float dtv = ok ? (sp_on ? sx : x) : 0.0f;
-      const float uv = ok ? ru[Q][i] : 0.0f;
-      *reinterpret_cast<float2 *>(prep + srow[i] * Lay::PSTR + 2 * sq[i]) = make_float2(dtv, uv);
+      const float x = pin(rd[Q][i]) + sbias[i];
+      const float dtv = sp_on ? softplus_f(x) : x;
+      *reinterpret_cast<float2 *>(prep + srow[i] * Lay::PSTR + 2 * sq) = make_float2(dtv, pin(ru[Q][i]));
     }
 #pragma unroll
-    for (int i = 0; i < BE; ++i) bcs[lane + 64 * i] = bc_ok[i] ? rbc[Q][i] : 0.0f;
+    for (int i = 0; i < BQ; ++i) {
+      float *const q = bcs + (lane / 16 + 4 * i) * 32 + n_bc;
+      q[0] = pin(rb[Q][i]);
+      q[16] = pin(rc[Q][i]);
+    }
   };
 
+  // The staged tile is read back into registers right after it is staged, so
+  // the LDS latency overlaps the finishing work of the previous tile.
   const float *const pr_lane = prep + r * Lay::PSTR;
   const float *const bc_lane = bcs + bc_slot;
   float *const part_lane = part + lane * Lay::QSTR;
+  float2 dus[T];
+  float bcv[T];
+  auto read_tile = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < T; ++q) {
+      dus[q] = *reinterpret_cast<const float2 *>(pr_lane + 2 * q);
+      bcv[q] = bc_lane[q * 32];
+    }
+  };
 
   auto do_scan = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < T; ++q) {
-      const float2 du = *reinterpret_cast<const float2 *>(pr_lane + 2 * q);
-      const float bc = bc_lane[q * 32];
-      const float dt = du.x, u = du.y;
+      const float dt = dus[q].x, u = dus[q].y;
       const float dtu = dt * u;
       float y = Dd * u;
-      state_step<NS, 0>(h, A2, dt, dtu, bc, y);
+      state_step<NS, 0>(h, A2, dt, dtu, bcv[q], y);
       part_lane[q] = y;
     }
   };
 
-  // Finishing a tile needs the gate (one direction) or the gate and the
-  // parked partials (long bidirectional); they are loaded ahead of the scan.
-  float zr[PE], xr[PE];
-  auto comb_load = [&](int k, bool second) __attribute__((always_inline)) {
-    // (z absent: u stands in as an always-valid address; the value is unused)
-    if (XMODE == kXLds || (XMODE == kXGlobal && !second)) return;
-    const Tin *const gzl = gz != nullptr ? gz : gu;
-    const int j = tile_of(k);
+  // Finishing a tile: its SPLIT partial sums per element, plus the gate
+  // (one direction; second visits) and the partner's parked sums (second
+  // visits).  Global values are loaded at the start of the iteration, LDS
+  // ones right after the scan.  kXLds parks both waves' first visits in the
+  // LDS block [R][XS] and finishes there in place; kXGlobal parks in global
+  // memory and finishes into out.
+  float zr[PE], xp[PE], ps[PE][SPLIT];
+  auto comb_load = [&](int k, auto second) __attribute__((always_inline)) {
+    constexpr bool SECOND = decltype(second)::value;
+    const int jT = tile_of(k) * T;
+    const bool in_seq = tq < L - jT;
 #pragma unroll
     for (int i = 0; i < PE; ++i) {
-      const int64_t t = step_of(j, sq[i]);
-      const int64_t tc = t < L ? t : L - 1;
-      const int64_t rc = srow[i] < rows ? srow[i] : lastrow;
-      zr[i] = to_f32(gzl[rowbase + rc * L + tc]);
-      xr[i] = XMODE == kXGlobal ? gx[xbase + rc * p.xstride + tc] : 0.0f;
+      if (DIRS == 1 || SECOND) zr[i] = bload<Tin>(rZ, tok_off(i, jT, in_seq));
+      if (XMODE == kXGlobal && SECOND) xp[i] = bload<float>(rX, oxg[i] + static_cast<uint32_t>(jT) * 4u);
     }
   };
-
-  auto do_combine = [&](int k, bool second) __attribute__((always_inline)) {
-    const int j = tile_of(k);
+  auto comb_read = [&](int k, auto second) __attribute__((always_inline)) {
+    constexpr bool SECOND = decltype(second)::value;
+    const int jT = tile_of(k) * T;
 #pragma unroll
     for (int i = 0; i < PE; ++i) {
-      const int row = srow[i], q = sq[i];
-      const int64_t t = step_of(j, q);
-      if (row >= rows || t >= L) continue;
-      float y = 0.0f;
 #pragma unroll
-      for (int s = 0; s < SPLIT; ++s) y += part[(s * R + row) * Lay::QSTR + q];
-      if (DIRS == 1) {
-        const float g = gz != nullptr ? silu_f(zr[i]) : 1.0f;
-        gout[rowbase + static_cast<int64_t>(row) * L + t] = from_f32<Tin>(y * g);
+      for (int s = 0; s < SPLIT; ++s) ps[i][s] = part[(s * R + srow[i]) * Lay::QSTR + sq];
+      if (XMODE == kXLds && SECOND) xp[i] = xlds[oxl[i] + jT];
+    }
+  };
+  auto do_combine = [&](int k, auto second) __attribute__((always_inline)) {
+    constexpr bool SECOND = decltype(second)::value;
+    const int jT = tile_of(k) * T;
+    const bool in_seq = tq < L - jT;
+#pragma unroll
+    for (int i = 0; i < PE; ++i) {
+      float y = ps[i][0];
+#pragma unroll
+      for (int s = 1; s < SPLIT; ++s) y += ps[i][s];
+      if (DIRS == 1 || SECOND) {
+        const float g = gated ? silu_f(pin(zr[i])) : 1.0f;
+        const float v = DIRS == 1 ? y * g : p.scale * (pin(xp[i]) + y) * g;
+        // rows past dim and steps past L: out of range, or the LDS block's padding
+        if (XMODE == kXLds) xlds[oxl[i] + jT] = v;
+        else bstore<Tin>(rO, tok_off(i, jT, in_seq), v);
       } else if (XMODE == kXLds) {
-        float *xp = xlds + row * XS + t;
-        *xp = second ? *xp + y : y;
-      } else if (!second) {
-        gx[xbase + static_cast<int64_t>(row) * p.xstride + t] = y;
+        xlds[oxl[i] + jT] = y;
       } else {
-        const float g = gz != nullptr ? silu_f(zr[i]) : 1.0f;
-        gout[rowbase + static_cast<int64_t>(row) * L + t] = from_f32<Tin>(p.scale * (y + xr[i]) * g);
+        bstore<float>(rX, oxg[i] + static_cast<uint32_t>(jT) * 4u, y);
       }
     }
   };
 
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
+  using First = std::integral_constant<bool, false>;
+  using Second = std::integral_constant<bool, true>;
 
-  // Tiles of phase 1: forward ceil(nt/2), backward the rest (first visits).
-  const int half = (nt + 1) / 2;
-  const int n1 = DIRS == 1 ? nt : (dir == 0 ? half : nt - half);
-
-  // One iteration k (register parity Q): issue the finishing loads of k and
-  // the loads of tile k+2, scan k, stage k+1, combine k.  A wave's LDS
-  // traffic executes in program order, so none of this needs a barrier.  The
-  // prefetch and the staging run on every iteration (past the end they repeat
-  // the last tile, whose staged copy is never scanned): a load issued under a
-  // branch would make the count of loads in flight path-dependent, and the
-  // wait before staging would then also wait for the prefetch.
-  auto iteration = [&](int k, auto par) __attribute__((always_inline)) {
-    constexpr int Q = decltype(par)::value;
-    using Qn = std::integral_constant<int, 1 - Q>;
-    const bool second = k >= n1;
-    if (DIRS == 2 && k == n1) {
-      // midpoint: every first visit of both waves is parked
-      if (XMODE == kXGlobal) __syncthreads();
-      else lds_barrier();
-    }
+  // One iteration k (register parity Q): finishing loads of k, prefetch of
+  // tile k+2, scan k, partial reads of k, stage and read back k+1, combine
+  // k.  A wave's LDS traffic executes in program order, so none of this
+  // needs a barrier.  The prefetch and the staging run on every iteration
+  // (past the end they repeat the last tile, whose staged copy is never
+  // scanned): a load issued under a branch would make the count of loads in
+  // flight path-dependent.
+  auto iteration = [&](int k, auto par, auto second) __attribute__((always_inline)) {
+    using Qn = std::integral_constant<int, 1 - decltype(par)::value>;
     comb_load(k, second);
     stage_load(k + 2 < nt ? k + 2 : nt - 1, par);
     do_scan();
+    comb_read(k, second);
     stage_store(Qn());
+    read_tile();
     do_combine(k, second);
+  };
+  // Iterations k0 .. k1-1 of one phase, unrolled by two with the parity of k.
+  auto run = [&](int k0, int k1, auto second) __attribute__((always_inline)) {
+    int k = k0;
+    if ((k & 1) && k < k1) iteration(k++, P1(), second);
+    for (; k + 1 < k1; k += 2) {
+      iteration(k, P0(), second);
+      iteration(k + 1, P1(), second);
+    }
+    if (k < k1) iteration(k, P0(), second);
   };
 
   stage_load(0, P0());
   stage_load(nt > 1 ? 1 : 0, P1());
   stage_store(P0());
-  int k = 0;
-  for (; k + 1 < nt; k += 2) {
-    iteration(k, P0());
-    iteration(k + 1, P1());
-  }
-  if (k < nt) iteration(k, P0());
-  if (DIRS == 2 && n1 == nt) {                 // a wave with no second-phase tiles
-    if (XMODE == kXGlobal) __syncthreads();
-    else lds_barrier();
+  read_tile();
+  if (DIRS == 1) {
+    run(0, nt, First());
+    return;
   }
 
-  // ---- short bidirectional sequences: gate and write the workgroup's whole
-  // [rows x L] slab of out in flat order (coalesced, whole lines).
-  if (DIRS == 2 && XMODE == kXLds) {
+  // Phase 1 has the forward wave on the first ceil(nt/2) tiles and the
+  // backward wave on the rest (first visits, parked); after the barrier each
+  // wave finishes its remaining tiles against the other's parked sums and
+  // writes the output.
+  const int n1 = fwd_wave ? half : nt - half;
+  run(0, n1, First());
+  if (XMODE == kXLds) lds_barrier();
+  else __syncthreads();
+  run(n1, nt, Second());
+
+  // ---- short sequences: the block's [rows x L] slab of out is complete in
+  // LDS (scaled and gated); write it in flat order (coalesced, whole lines).
+  if (XMODE == kXLds) {
     lds_barrier();
-    const int64_t n = static_cast<int64_t>(rows) * L;
+    constexpr int NT = 64 * DIRS, U = 4;
+    const int n = rows * L;
     const int tid = threadIdx.x;
-    int fr = tid / static_cast<int>(L), ft = tid % static_cast<int>(L);
-    for (int64_t f = tid; f < n; f += 64 * DIRS) {
-      float y = p.scale * xlds[fr * XS + ft];
-      if (gz != nullptr) y *= silu_f(to_f32(gz[rowbase + f]));
-      gout[rowbase + f] = from_f32<Tin>(y);
-      ft += 64 * DIRS;
-      while (ft >= L) { ft -= static_cast<int>(L); ++fr; }
+    int fr = tid / L, ft = tid % L;
+    for (int f0 = tid; f0 < n; f0 += U * NT) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {          // reads first, so their latency overlaps
+        v[u] = xlds[(fr < R ? fr : R - 1) * XS + ft];
+        ft += NT;
+        while (ft >= L) { ft -= L; ++fr; }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int f = f0 + u * NT;
+        bstore<Tin>(rO, pin_u(f < n ? static_cast<uint32_t>(f) * ES : kOob), v[u]);
+      }
     }
   }
 }
@@ -374,14 +470,13 @@ hipError_t launch_one(const ScanPlan &plan, const ScanArgs &a, hipStream_t s) {
 
 template <typename Tin, int SPLIT>
 hipError_t dispatch_mode(const ScanPlan &plan, const ScanArgs &a, hipStream_t s) {
-  if (plan.dirs == 1) return launch_one<Tin, SPLIT, 1, kXNone, 16>(plan, a, s);
+  if (plan.dirs == 1) return launch_one<Tin, SPLIT, 1, kXNone, 8>(plan, a, s);
   if (plan.xmode == kXLds) return launch_one<Tin, SPLIT, 2, kXLds, 8>(plan, a, s);
   return launch_one<Tin, SPLIT, 2, kXGlobal, 8>(plan, a, s);
 }
 
 template <typename Tin>
 hipError_t dispatch_dtype(const ScanPlan &plan, const ScanArgs &a, hipStream_t s) {
-  if (plan.S == 2) return dispatch_mode<Tin, 2>(plan, a, s);
   return dispatch_mode<Tin, 4>(plan, a, s);
 }
 
@@ -399,16 +494,17 @@ ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t L, int dstate, int dirs) 
   ScanPlan pl{};
   pl.dirs = dirs;
   pl.threads = 64 * dirs;
-  // Split each channel's 16 states over 2 lanes, or over 4 when that leaves
-  // fewer than two waves per SIMD.
-  auto waves = [&](int split) { return batch * ((dim * split + 63) / 64) * dirs; };
-  pl.S = waves(2) >= 2048 ? 2 : 4;
+  // Each channel's 16 states are split over 4 lanes: a two-lane split needs
+  // fewer instructions per state but leaves half the waves, and measured
+  // slower on every workload tried (fewer waves to hide latency, and a
+  // larger LDS exchange per workgroup).
+  pl.S = 4;
   pl.blocks = batch * ((dim + 64 / pl.S - 1) / (64 / pl.S));
   if (dirs == 1) {
-    pl.T = 16;
+    pl.T = 8;
     pl.xmode = kXNone;
   } else {
-    // On-chip exchange while four workgroups still fit a CU's 160 KB LDS.
+    // On-chip exchange while at least four workgroups fit a CU's 160 KB LDS.
     pl.T = 8;
     pl.xmode = lds_bytes(pl.S, 2, 8, kXLds, L) <= 40 * 1024 ? kXLds : kXGlobal;
   }
@@ -417,6 +513,25 @@ ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t L, int dstate, int dirs) 
 }
 
 int64_t xchg_global_stride(int64_t L) { return (L + 31) / 32 * 32; }
+
+// The kernel addresses a workgroup's rows, a batch row of B and C, and its
+// exchange rows through buffer resources with byte offsets below 2^31
+// (offsets may run one tile past the data).
+bool scan_offsets_fit(const ScanPlan &plan, const ScanArgs &a, bool bf16) {
+  const uint64_t lim = uint64_t{1} << 31;
+  const uint64_t es = bf16 ? 2 : 4;
+  const uint64_t R = 64 / plan.S;
+  const uint64_t Lt = static_cast<uint64_t>(a.L) + plan.T;
+  if (R * Lt * es >= lim) return false;
+  for (int k = 0; k < plan.dirs; ++k) {
+    const DirPtrs &d = a.dir[k];
+    const uint64_t ext = static_cast<uint64_t>(a.dstate - 1) * static_cast<uint64_t>(d.bsn) +
+                         Lt * static_cast<uint64_t>(d.bst) + 1;
+    if (ext * es >= lim) return false;
+  }
+  if (plan.xmode == kXGlobal && R * static_cast<uint64_t>(a.xstride) * 4 >= lim) return false;
+  return true;
+}
 
 hipError_t launch_scan(const ScanPlan &plan, const ScanArgs &args, bool bf16, hipStream_t s) {
   if (plan.blocks <= 0) return hipSuccess;

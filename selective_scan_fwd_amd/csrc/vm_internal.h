@@ -36,14 +36,15 @@ __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf
 __device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // softplus(x) = max(x, 0) + log1p(e^-|x|).  log1p(e) is taken as
-// log(s) - ((s - 1) - e) / s with s = fl(1 + e): the second term removes the
-// rounding error of s to first order, so small e keeps full relative accuracy.
+// log(s) - ((s - 1) - e) with s = fl(1 + e): the second term is the rounding
+// error of s, which removes it to first order; leaving out its division by s
+// changes the result by at most 2^-24 * e / (1 + e), below fp32 resolution of
+// log1p(e).  Small e thus keeps full relative accuracy.
 __device__ __forceinline__ float softplus_f(float x) {
   float e = hw_exp2(-__builtin_fabsf(x) * kLog2e);
   float s = 1.0f + e;
-  float l = hw_log2(s) * kLn2;
-  float corr = ((s - 1.0f) - e) * hw_rcp(s);
-  return __builtin_fmaxf(x, 0.0f) + (l - corr);
+  float corr = (s - 1.0f) - e;
+  return __builtin_fmaxf(x, 0.0f) + __builtin_fmaf(hw_log2(s), kLn2, -corr);
 }
 
 // SiLU(z) = z * sigmoid(z) = z / (1 + e^-z).
@@ -86,6 +87,8 @@ struct ScanArgs {
   float scale;          // bidirectional combine scale
 };
 
+// Where a bidirectional scan parks first-visit sums: in LDS (short
+// sequences) or in fp32 global memory.
 enum XMode { kXNone = 0, kXLds = 1, kXGlobal = 2 };
 
 struct ScanPlan {
@@ -102,6 +105,8 @@ ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t L, int dstate, int dirs);
 // Row stride (floats) of the global exchange buffer: rows padded to whole
 // 128-byte lines so that no two channels' parked partials share a line.
 int64_t xchg_global_stride(int64_t L);
+// Whether every in-kernel offset of this launch fits 32 bits.
+bool scan_offsets_fit(const ScanPlan &plan, const ScanArgs &args, bool bf16);
 hipError_t launch_scan(const ScanPlan &plan, const ScanArgs &args, bool bf16, hipStream_t s);
 
 // ---------------------------------------------------------------- layout

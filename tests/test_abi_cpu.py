@@ -86,6 +86,7 @@ def test_scan_argument_checks(lib):
     assert _scan(lib, N=0) == 2
     assert _scan(lib, batch=1 << 40, dim=1 << 20) == 2          # element count overflow
     assert _scan(lib, N=17) == 6
+    assert _scan(lib, batch=1, L=1 << 26) == 6                  # past the 32-bit in-kernel offsets
     assert _scan(lib, dtype=2) == 3
     assert _scan(lib, sp=2) == 4
     assert _scan(lib, rev=-1) == 4
