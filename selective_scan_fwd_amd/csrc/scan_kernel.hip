@@ -34,6 +34,7 @@
 //    whole, once.  Long sequences park in fp32 global memory (rows padded to
 //    whole cache lines) and finish tile by tile.
 #include <type_traits>
+#include <utility>
 
 #include "vm_internal.h"
 
@@ -64,13 +65,16 @@ VM_FMAC_BCAST(8) VM_FMAC_BCAST(9) VM_FMAC_BCAST(10) VM_FMAC_BCAST(11)
 VM_FMAC_BCAST(12) VM_FMAC_BCAST(13) VM_FMAC_BCAST(14) VM_FMAC_BCAST(15)
 #undef VM_FMAC_BCAST
 
+// One step of the lane's NS states: h_j <- 2^(dt A2_j) h_j + dtu B_j and
+// y = sum_j C_j h_j (B_j, C_j broadcast from lanes j and NS + j of the row).
 template <int NS, int J>
 __device__ __forceinline__ void state_step(float (&h)[NS], const float (&A2)[NS], float dt,
                                            float dtu, float bc, float &y) {
   if constexpr (J < NS) {
     const float dA = hw_exp2(dt * A2[J]);
     h[J] = __builtin_fmaf(dA, h[J], dtu * row_bcast<J>(bc));
-    fmac_row_bcast<NS + J>(y, bc, h[J]);
+    if constexpr (J == 0) y = row_bcast<NS>(bc) * h[0];
+    else fmac_row_bcast<NS + J>(y, bc, h[J]);
     state_step<NS, J + 1>(h, A2, dt, dtu, bc, y);
   }
 }
@@ -89,6 +93,16 @@ __device__ __forceinline__ uint32_t pin_u(uint32_t v) {
   return v;
 }
 
+// Calls f(std::integral_constant<int, I>()) for I = 0 .. N-1 in order.
+template <typename F, int... I>
+__device__ __forceinline__ void for_slots_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>()), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void for_slots(F &&f) {
+  for_slots_impl(f, std::make_integer_sequence<int, N>());
+}
+
 // Workgroup barrier that orders LDS only: global loads issued before it stay
 // in flight.
 __device__ __forceinline__ void lds_barrier() {
@@ -99,12 +113,13 @@ __device__ __forceinline__ void lds_barrier() {
 
 template <int T, int R>
 struct Layout {
-  static constexpr int PSTR = 2 * T + 2;                  // (dt, u) per row; PSTR/2 odd
+  static constexpr int PSTR = 2 * T + 2;                  // (dt, dt u) per row; PSTR/2 odd
   static constexpr int QSTR = T + 1;                      // partials per lane, odd
   static constexpr int PREP = R * PSTR;
+  static constexpr int UST = R * T;                       // u per row, for the D u skip
   static constexpr int BC = 32 * T;                       // B in slots 0..15, C in 16..31
   static constexpr int PART = 64 * QSTR;
-  static constexpr int WAVE = PREP + BC + PART;           // floats per wave
+  static constexpr int WAVE = PREP + UST + BC + PART;     // floats per wave
 };
 
 // Row stride of the LDS exchange block for n parked steps: >= n and
@@ -151,6 +166,7 @@ scan_kernel(const ScanArgs p) {
   constexpr int PE = R * T / 64;                 // staged (dt, u) elements per lane per tile
   constexpr int BQ = T / 4;                      // B (and C) loads per lane per tile
   constexpr uint32_t ES = sizeof(Tin);
+  constexpr int NB = 3;                          // tiles in flight (prefetch distance)
   using Lay = Layout<T, R>;
   static_assert(NS >= 4 && NS <= 8 && R % 16 == 0 && T % 4 == 0 && (R * T) % 64 == 0, "shape");
   static_assert(DIRS == 1 ? XMODE == kXNone : XMODE != kXNone, "mode");
@@ -159,7 +175,8 @@ scan_kernel(const ScanArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   float *const prep = smem + wave * Lay::WAVE;   // [R][PSTR]
-  float *const bcs = prep + Lay::PREP;           // [T][32]
+  float *const ust = prep + Lay::PREP;           // [R][T]
+  float *const bcs = ust + Lay::UST;             // [T][32]
   float *const part = bcs + Lay::BC;             // [64 lanes][QSTR]
   float *const xlds = smem + DIRS * Lay::WAVE;   // [R][XS]   (kXLds)
 
@@ -203,16 +220,18 @@ scan_kernel(const ScanArgs p) {
 
   // ---- scan role: channel d0 + r, states n0 .. n0 + NS - 1 (states at or
   // beyond dstate have A = 0 and zero B/C, so they stay at zero)
+  // Parameters are read through resources too (rows past dim and states past
+  // dstate read 0), so that all of them are in flight at once with the first
+  // tiles instead of one load round trip after another.
   const int n0 = sp * NS;
-  const bool lane_ok = r < rows;
+  const Rsrc rA = make_rsrc(P.A + static_cast<int64_t>(d0) * dstate,
+                            static_cast<uint32_t>(rows * dstate) * 4u);
+  const Rsrc rDp = make_rsrc(P.D + d0, static_cast<uint32_t>(rows) * 4u);
+  const Rsrc rBias = make_rsrc(P.bias != nullptr ? P.bias + d0 : nullptr,
+                               P.bias != nullptr ? static_cast<uint32_t>(rows) * 4u : 0u);
   float A2[NS], h[NS];
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    const int n = n0 + j;
-    A2[j] = (lane_ok && n < dstate) ? P.A[static_cast<int64_t>(d0 + r) * dstate + n] * kLog2e : 0.0f;
-    h[j] = 0.0f;
-  }
-  const float Dd = (lane_ok && sp == 0) ? P.D[d0 + r] : 0.0f;
+  for (int j = 0; j < NS; ++j) h[j] = 0.0f;
   // lane j of each 16-lane row holds B[n0 + j] (j < NS) or C[n0 + j - NS]
   const int rl = lane & 15;
   const int bc_slot = rl < NS ? n0 + rl : (rl < 2 * NS ? 16 + n0 + rl - NS : 0);
@@ -227,14 +246,13 @@ scan_kernel(const ScanArgs p) {
   const int tq = rev ? T - 1 - sq : sq;
   int srow[PE];
   uint32_t ob[PE], oxl[PE], oxg[PE];
-  float sbias[PE];
+  float sbias[PE], sD[PE];
 #pragma unroll
   for (int i = 0; i < PE; ++i) {
     srow[i] = lane / T + i * (64 / T);
     ob[i] = (static_cast<uint32_t>(srow[i]) * static_cast<uint32_t>(L) + tq) * ES;
     oxl[i] = static_cast<uint32_t>(srow[i] * XS + tq);
     oxg[i] = (static_cast<uint32_t>(srow[i]) * xstride + tq) * 4u;
-    sbias[i] = (P.bias != nullptr && srow[i] < rows) ? P.bias[d0 + srow[i]] : 0.0f;
   }
   // B and C: load i of a lane covers visit position q = lane / 16 + 4 i and
   // state n = lane % 16 (past dstate: out of range, so it stages 0).
@@ -256,11 +274,11 @@ scan_kernel(const ScanArgs p) {
     return pin_u(in_seq ? ob[i] + static_cast<uint32_t>(jT) * ES : kOob);
   };
 
-  // Raw global values of two tiles in flight (index = tile parity).  Nothing
-  // reads them before the tile is staged: with a static count of loads in
-  // flight, the wait for an older tile leaves the prefetch just issued in
-  // flight.
-  float ru[2][PE], rd[2][PE], rb[2][BQ], rc[2][BQ];
+  // Raw global values of NB tiles in flight (tile m in slot m % NB).
+  // Nothing reads them before the tile is staged: with a static count of
+  // loads in flight, the wait for an older tile leaves the later prefetches
+  // in flight.
+  float ru[NB][PE], rd[NB][PE], rb[NB][BQ], rc[NB][BQ];
 
   auto stage_load = [&](int k, auto par) __attribute__((always_inline)) {
     constexpr int Q = decltype(par)::value;
@@ -280,17 +298,20 @@ scan_kernel(const ScanArgs p) {
     }
   };
 
-  // Steps past L and channels past dim stage u = 0, so the state only decays
-  // where it is zero (before the first real step) or no longer read; states
-  // past dstate stage B = C = 0.
+  // Stages (dt, dt u) for the scan and u for the skip term.  Steps past L
+  // and channels past dim stage u = 0, so the state only decays where it is
+  // zero (before the first real step) or no longer read; states past dstate
+  // stage B = C = 0.
   auto stage_store = [&](auto par) __attribute__((always_inline)) {
     constexpr int Q = decltype(par)::value;
     const bool sp_on = p.softplus != 0;
 #pragma unroll
     for (int i = 0; i < PE; ++i) {
       const float x = pin(rd[Q][i]) + sbias[i];
+      const float uv = pin(ru[Q][i]);
       const float dtv = sp_on ? softplus_f(x) : x;
-      *reinterpret_cast<float2 *>(prep + srow[i] * Lay::PSTR + 2 * sq) = make_float2(dtv, pin(ru[Q][i]));
+      *reinterpret_cast<float2 *>(prep + srow[i] * Lay::PSTR + 2 * sq) = make_float2(dtv, dtv * uv);
+      ust[srow[i] * T + sq] = uv;
     }
 #pragma unroll
     for (int i = 0; i < BQ; ++i) {
@@ -318,29 +339,28 @@ scan_kernel(const ScanArgs p) {
   auto do_scan = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < T; ++q) {
-      const float dt = dus[q].x, u = dus[q].y;
-      const float dtu = dt * u;
-      float y = Dd * u;
-      state_step<NS, 0>(h, A2, dt, dtu, bcv[q], y);
+      float y;
+      state_step<NS, 0>(h, A2, dus[q].x, dus[q].y, bcv[q], y);
       part_lane[q] = y;
     }
   };
 
-  // Finishing a tile: its SPLIT partial sums per element, plus the gate
-  // (one direction; second visits) and the partner's parked sums (second
-  // visits).  Global values are loaded at the start of the iteration, LDS
-  // ones right after the scan.  kXLds parks both waves' first visits in the
-  // LDS block [R][XS] and finishes there in place; kXGlobal parks in global
-  // memory and finishes into out.
-  float zr[PE], xp[PE], ps[PE][SPLIT];
-  auto comb_load = [&](int k, auto second) __attribute__((always_inline)) {
+  // Finishing a tile: its SPLIT partial sums and the skip D u per element,
+  // plus the gate (one direction; second visits) and the partner's parked
+  // sums (second visits).  The global values of tile k are loaded one
+  // iteration ahead (slot k % NB), the LDS ones right after the scan.  kXLds
+  // parks both waves' first visits in the LDS block [R][XS] and finishes
+  // there in place; kXGlobal parks in global memory and finishes into out.
+  float zr[NB][PE], xg[NB][PE], xl[PE], uk[PE], ps[PE][SPLIT];
+  auto comb_load = [&](int k, auto slot, auto second) __attribute__((always_inline)) {
+    constexpr int Q = decltype(slot)::value;
     constexpr bool SECOND = decltype(second)::value;
     const int jT = tile_of(k) * T;
     const bool in_seq = tq < L - jT;
 #pragma unroll
     for (int i = 0; i < PE; ++i) {
-      if (DIRS == 1 || SECOND) zr[i] = bload<Tin>(rZ, tok_off(i, jT, in_seq));
-      if (XMODE == kXGlobal && SECOND) xp[i] = bload<float>(rX, oxg[i] + static_cast<uint32_t>(jT) * 4u);
+      if (DIRS == 1 || SECOND) zr[Q][i] = bload<Tin>(rZ, tok_off(i, jT, in_seq));
+      if (XMODE == kXGlobal && SECOND) xg[Q][i] = bload<float>(rX, oxg[i] + static_cast<uint32_t>(jT) * 4u);
     }
   };
   auto comb_read = [&](int k, auto second) __attribute__((always_inline)) {
@@ -350,10 +370,12 @@ scan_kernel(const ScanArgs p) {
     for (int i = 0; i < PE; ++i) {
 #pragma unroll
       for (int s = 0; s < SPLIT; ++s) ps[i][s] = part[(s * R + srow[i]) * Lay::QSTR + sq];
-      if (XMODE == kXLds && SECOND) xp[i] = xlds[oxl[i] + jT];
+      uk[i] = ust[srow[i] * T + sq];
+      if (XMODE == kXLds && SECOND) xl[i] = xlds[oxl[i] + jT];
     }
   };
-  auto do_combine = [&](int k, auto second) __attribute__((always_inline)) {
+  auto do_combine = [&](int k, auto slot, auto second) __attribute__((always_inline)) {
+    constexpr int Q = decltype(slot)::value;
     constexpr bool SECOND = decltype(second)::value;
     const int jT = tile_of(k) * T;
     const bool in_seq = tq < L - jT;
@@ -362,9 +384,11 @@ scan_kernel(const ScanArgs p) {
       float y = ps[i][0];
 #pragma unroll
       for (int s = 1; s < SPLIT; ++s) y += ps[i][s];
+      y = __builtin_fmaf(sD[i], uk[i], y);
       if (DIRS == 1 || SECOND) {
-        const float g = gated ? silu_f(pin(zr[i])) : 1.0f;
-        const float v = DIRS == 1 ? y * g : p.scale * (pin(xp[i]) + y) * g;
+        const float g = gated ? silu_f(pin(zr[Q][i])) : 1.0f;
+        const float other = XMODE == kXLds ? xl[i] : XMODE == kXGlobal ? pin(xg[Q][i]) : 0.0f;
+        const float v = DIRS == 1 ? y * g : p.scale * (other + y) * g;
         // rows past dim and steps past L: out of range, or the LDS block's padding
         if (XMODE == kXLds) xlds[oxl[i] + jT] = v;
         else bstore<Tin>(rO, tok_off(i, jT, in_seq), v);
@@ -376,44 +400,60 @@ scan_kernel(const ScanArgs p) {
     }
   };
 
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
   using First = std::integral_constant<bool, false>;
   using Second = std::integral_constant<bool, true>;
 
-  // One iteration k (register parity Q): finishing loads of k, prefetch of
-  // tile k+2, scan k, partial reads of k, stage and read back k+1, combine
-  // k.  A wave's LDS traffic executes in program order, so none of this
-  // needs a barrier.  The prefetch and the staging run on every iteration
-  // (past the end they repeat the last tile, whose staged copy is never
-  // scanned): a load issued under a branch would make the count of loads in
-  // flight path-dependent.
-  auto iteration = [&](int k, auto par, auto second) __attribute__((always_inline)) {
-    using Qn = std::integral_constant<int, 1 - decltype(par)::value>;
-    comb_load(k, second);
-    stage_load(k + 2 < nt ? k + 2 : nt - 1, par);
+  // One iteration k (slot Q = k % NB): finishing loads of k+1, prefetch of
+  // tile k+NB into the slot tile k has left, scan k, partial reads of k,
+  // stage and read back k+1, combine k.  A wave's LDS traffic executes in
+  // program order, so none of this needs a barrier.  The prefetch and the
+  // staging run on every iteration (past the end they repeat the last tile,
+  // whose staged copy is never scanned): a load issued under a branch would
+  // make the count of loads in flight path-dependent.
+  auto iteration = [&](int k, auto slot, auto second) __attribute__((always_inline)) {
+    using Qn = std::integral_constant<int, (decltype(slot)::value + 1) % NB>;
+    comb_load(k + 1 < nt ? k + 1 : nt - 1, Qn(), second);
+    stage_load(k + NB < nt ? k + NB : nt - 1, slot);
     do_scan();
     comb_read(k, second);
     stage_store(Qn());
     read_tile();
-    do_combine(k, second);
+    do_combine(k, slot, second);
   };
-  // Iterations k0 .. k1-1 of one phase, unrolled by two with the parity of k.
+  // Iterations k0 .. k1-1 of one phase, unrolled NB times so that every
+  // slot index is a compile-time constant.
   auto run = [&](int k0, int k1, auto second) __attribute__((always_inline)) {
     int k = k0;
-    if ((k & 1) && k < k1) iteration(k++, P1(), second);
-    for (; k + 1 < k1; k += 2) {
-      iteration(k, P0(), second);
-      iteration(k + 1, P1(), second);
-    }
-    if (k < k1) iteration(k, P0(), second);
+    for_slots<NB>([&](auto s) __attribute__((always_inline)) {       // up to a multiple of NB
+      if (decltype(s)::value > 0 && k < k1 && k % NB == decltype(s)::value) iteration(k++, s, second);
+    });
+    for (; k + NB <= k1; k += NB)
+      for_slots<NB>([&](auto s) __attribute__((always_inline)) { iteration(k + decltype(s)::value, s, second); });
+    for_slots<NB>([&](auto s) __attribute__((always_inline)) {       // the rest
+      if (decltype(s)::value < NB - 1 && k < k1) iteration(k++, s, second);
+    });
   };
 
-  stage_load(0, P0());
-  stage_load(nt > 1 ? 1 : 0, P1());
-  stage_store(P0());
+  // First tiles, then the parameters, all in flight together.
+  for_slots<NB>([&](auto s) __attribute__((always_inline)) {
+    stage_load(decltype(s)::value < nt ? decltype(s)::value : nt - 1, s);
+  });
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int n = n0 + j;
+    A2[j] = bload<float>(rA, n < dstate ? static_cast<uint32_t>(r * dstate + n) * 4u : kOob);
+  }
+#pragma unroll
+  for (int i = 0; i < PE; ++i) {
+    sbias[i] = bload<float>(rBias, static_cast<uint32_t>(srow[i]) * 4u);
+    sD[i] = bload<float>(rDp, static_cast<uint32_t>(srow[i]) * 4u);
+  }
+#pragma unroll
+  for (int j = 0; j < NS; ++j) A2[j] = pin(A2[j]) * kLog2e;
+  stage_store(std::integral_constant<int, 0>());
   read_tile();
   if (DIRS == 1) {
+    comb_load(0, std::integral_constant<int, 0>(), First());
     run(0, nt, First());
     return;
   }
@@ -426,6 +466,10 @@ scan_kernel(const ScanArgs p) {
   run(0, n1, First());
   if (XMODE == kXLds) lds_barrier();
   else __syncthreads();
+  // finishing loads of the first second-phase tile (slot n1 % NB)
+  for_slots<NB>([&](auto s) __attribute__((always_inline)) {
+    if (n1 < nt && n1 % NB == decltype(s)::value) comb_load(n1, s, Second());
+  });
   run(n1, nt, Second());
 
   // ---- short sequences: the block's [rows x L] slab of out is complete in
@@ -482,7 +526,7 @@ hipError_t dispatch_dtype(const ScanPlan &plan, const ScanArgs &a, hipStream_t s
 
 size_t lds_bytes(int split, int dirs, int T, int xmode, int64_t L) {
   const int R = 64 / split;
-  size_t f = static_cast<size_t>(dirs) * (R * (2 * T + 2) + 32 * T + 64 * (T + 1));
+  size_t f = static_cast<size_t>(dirs) * (R * (2 * T + 2) + R * T + 32 * T + 64 * (T + 1));
   if (xmode == kXLds) f += static_cast<size_t>(R) * xchg_stride(L, T);
   return f * sizeof(float);
 }
