@@ -35,6 +35,7 @@ VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
 SLOTS_PER_STATE_STEP = 6         # dt*A, exp (2 slots), dt*u*B, state fma, readout fma
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["selective_scan_fwd_amd/csrc/scan_kernel.hip",
+                  "selective_scan_fwd_amd/csrc/layout_kernels.hip",
                   "selective_scan_fwd_amd/csrc/vm_internal.h"]
 
 
@@ -237,8 +238,9 @@ def build_step(cfg, seed, sets, dev):
 
 
 def load_traffic(source_hash, workload):
-    """HBM bytes per launch of the scan kernel from the committed counter
-    summary, if it was taken on the current kernel source and this workload."""
+    """HBM bytes per step (the scan kernel; every kernel of the step for the
+    multi-kernel workloads) from the committed counter summary, if it was
+    taken on the current kernel sources and this workload."""
     path = os.path.join(PROFILE_DIR, "scan_kernel_counters.json")
     try:
         with open(path) as f:
