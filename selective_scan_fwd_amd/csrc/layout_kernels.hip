@@ -73,19 +73,82 @@ atrous_scatter_kernel(const T *__restrict__ streams, T *__restrict__ y, int64_t 
   }
 }
 
-// Mean over one axis of each H x W grid: one workgroup per grid row (b, d).
-// axis 0 (mean over W): wave w sums grid rows w, w+4, ...; lanes stride the
-// row and the partial sums are reduced across the wave.  axis 1 (mean over
-// H): threads own columns and sum down the rows in index order.
+// Four consecutive values as fp32 (one 16-byte or 8-byte load).
+__device__ __forceinline__ float4 load4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ float4 load4(const bf16_t *p) {
+  const uint2 v = *reinterpret_cast<const uint2 *>(p);
+  return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                     __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+}
+__device__ __forceinline__ void store4(float *p, float4 v) { *reinterpret_cast<float4 *>(p) = v; }
+__device__ __forceinline__ void store4(bf16_t *p, float4 v) {
+  const uint32_t a = from_f32<bf16_t>(v.x) | (static_cast<uint32_t>(from_f32<bf16_t>(v.y)) << 16);
+  const uint32_t b = from_f32<bf16_t>(v.z) | (static_cast<uint32_t>(from_f32<bf16_t>(v.w)) << 16);
+  *reinterpret_cast<uint2 *>(p) = make_uint2(a, b);
+}
+
+// Mean over one axis of each H x W grid: one workgroup per grid (b, d),
+// sum times fl(1 / extent).
+//  * Vector path (W % 4 == 0, aligned): each thread reads four consecutive
+//    values at a time; kThreads/(W/4) grid rows are read per pass, U passes
+//    in flight.  axis 0 (mean over W): the W/4 threads of a grid row reduce
+//    their partial sums across lanes.  axis 1 (mean over H): the row groups'
+//    column partials meet in LDS and are added in group order.
+//  * Scalar path otherwise.
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
 mean_pool_kernel(const T *__restrict__ u, float *__restrict__ pooled, int H, int W, int axis,
-                 float inv) {
+                 float inv, int vec) {
+  __shared__ float part[kThreads * 4];
   const int64_t r = blockIdx.x;
   const T *g = u + r * static_cast<int64_t>(H) * W;
+  const int tid = threadIdx.x;
+  if (vec) {
+    const int q = W / 4;                        // threads per grid row (power of two, <= 64)
+    const int rows_per_pass = kThreads / q;
+    const int rr = tid / q, cq = tid - rr * q;
+    constexpr int U = 4;
+    if (axis == 0) {
+      float *dst = pooled + r * H;
+      for (int i0 = 0; i0 < H; i0 += U * rows_per_pass) {
+        float s[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {           // loads of U grid rows in flight
+          const int i = i0 + u * rows_per_pass + rr;
+          s[u] = 0.0f;
+          if (i < H) {
+            const float4 v = load4(g + static_cast<int64_t>(i) * W + 4 * cq);
+            s[u] = (v.x + v.y) + (v.z + v.w);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * rows_per_pass + rr;
+          for (int off = q / 2; off > 0; off >>= 1) s[u] += __shfl_xor(s[u], off, q);
+          if (cq == 0 && i < H) dst[i] = s[u] * inv;
+        }
+      }
+    } else {
+      float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 4
+      for (int i = rr; i < H; i += rows_per_pass) {
+        const float4 v = load4(g + static_cast<int64_t>(i) * W + 4 * cq);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      }
+      reinterpret_cast<float4 *>(part)[tid] = acc;
+      __syncthreads();
+      float *dst = pooled + r * W;
+      for (int j = tid; j < W; j += kThreads) {
+        float s = 0.0f;
+        for (int k = 0; k < rows_per_pass; ++k) s += part[(k * q + j / 4) * 4 + (j & 3)];
+        dst[j] = s * inv;
+      }
+    }
+    return;
+  }
   if (axis == 0) {
     float *dst = pooled + r * H;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = tid >> 6, lane = tid & 63;
     for (int i = wave; i < H; i += kThreads / 64) {
       float s = 0.0f;
       for (int j = lane; j < W; j += 64) s += to_f32(g[static_cast<int64_t>(i) * W + j]);
@@ -95,7 +158,7 @@ mean_pool_kernel(const T *__restrict__ u, float *__restrict__ pooled, int H, int
     }
   } else {
     float *dst = pooled + r * W;
-    for (int j = threadIdx.x; j < W; j += kThreads) {
+    for (int j = tid; j < W; j += kThreads) {
       float s = 0.0f;
       for (int i = 0; i < H; ++i) s += to_f32(g[static_cast<int64_t>(i) * W + j]);
       dst[j] = s * inv;
@@ -104,18 +167,51 @@ mean_pool_kernel(const T *__restrict__ u, float *__restrict__ pooled, int H, int
 }
 
 // out[r, i, j] = scale * y[r, p] * SiLU(z[r, i, j]),  p = i (axis 0) or j.
-// One workgroup per grid (row r); threads walk the flat grid with coalesced
-// accesses and track (i, j) incrementally (no per-element division).
+// One workgroup per grid (row r).  Vector path (W % 4 == 0, aligned): four
+// consecutive elements per thread and U of them in flight; otherwise the
+// threads walk the flat grid tracking (i, j) incrementally.
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
 repeat_gate_kernel(const float *__restrict__ y, const T *__restrict__ z, T *__restrict__ out,
-                   int H, int W, int axis, float scale) {
+                   int H, int W, int axis, float scale, int vec) {
   const int64_t r = blockIdx.x;
   const int hw = H * W;
   const int Lp = axis == 0 ? H : W;
   const float *yr = y + r * Lp;
   const T *zr = z != nullptr ? z + r * static_cast<int64_t>(hw) : nullptr;
   T *outr = out + r * static_cast<int64_t>(hw);
+  if (vec) {
+    constexpr int U = 4;
+    const int n4 = hw / 4;
+    for (int e0 = threadIdx.x; e0 < n4; e0 += U * kThreads) {
+      float4 zv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * kThreads;
+        zv[u] = (zr != nullptr && e < n4) ? load4(zr + 4 * e) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * kThreads;
+        if (e >= n4) break;
+        const int i = (4 * e) / W, j = 4 * e - i * W;
+        float4 v;
+        if (axis == 0) {
+          const float a = scale * yr[i];
+          v = make_float4(a, a, a, a);
+        } else {
+          const float4 a = *reinterpret_cast<const float4 *>(yr + j);
+          v = make_float4(scale * a.x, scale * a.y, scale * a.z, scale * a.w);
+        }
+        if (zr != nullptr) {
+          v.x *= silu_f(zv[u].x); v.y *= silu_f(zv[u].y);
+          v.z *= silu_f(zv[u].z); v.w *= silu_f(zv[u].w);
+        }
+        store4(outr + 4 * e, v);
+      }
+    }
+    return;
+  }
   int i = threadIdx.x / W, j = threadIdx.x - (threadIdx.x / W) * W;
   for (int e = threadIdx.x; e < hw; e += kThreads) {
     float v = scale * yr[axis == 0 ? i : j];
@@ -173,32 +269,46 @@ hipError_t launch_atrous_scatter(const void *streams, void *y, int64_t batch, in
   return hipGetLastError();
 }
 
+// Four-wide accesses need W % 4 == 0, aligned rows, and (for the lane
+// reduction and the LDS combine) W / 4 a power of two no larger than 64.
+int vec_ok(const void *a, const void *b, const void *c, int64_t W, bool bf16) {
+  const uintptr_t al = bf16 ? 8 : 16;
+  const int64_t q = W / 4;
+  const bool pow2 = q > 0 && q <= 64 && (q & (q - 1)) == 0;
+  return (W % 4 == 0 && pow2 && reinterpret_cast<uintptr_t>(a) % al == 0 &&
+          reinterpret_cast<uintptr_t>(b) % al == 0 && reinterpret_cast<uintptr_t>(c) % 16 == 0)
+             ? 1 : 0;
+}
+
 hipError_t launch_mean_pool(const void *u, float *pooled, int64_t rows, int64_t H, int64_t W,
                             int axis, bool bf16, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const float inv = static_cast<float>(1.0 / static_cast<double>(axis == 0 ? W : H));
+  const int vec = vec_ok(u, u, pooled, W, bf16);
   if (bf16)
     hipLaunchKernelGGL(mean_pool_kernel<bf16_t>, dim3(rows), dim3(kThreads), 0, s,
                        static_cast<const bf16_t *>(u), pooled, static_cast<int>(H),
-                       static_cast<int>(W), axis, inv);
+                       static_cast<int>(W), axis, inv, vec);
   else
     hipLaunchKernelGGL(mean_pool_kernel<float>, dim3(rows), dim3(kThreads), 0, s,
                        static_cast<const float *>(u), pooled, static_cast<int>(H),
-                       static_cast<int>(W), axis, inv);
+                       static_cast<int>(W), axis, inv, vec);
   return hipGetLastError();
 }
 
 hipError_t launch_repeat_gate(const float *y, const void *z, void *out, int64_t rows, int64_t H,
                               int64_t W, int axis, float scale, bool bf16, hipStream_t s) {
   if (rows * H * W == 0) return hipSuccess;
+  const int vec = vec_ok(z != nullptr ? z : out, out, y, W, bf16) &&
+                  (axis == 0 || (W * 4) % 16 == 0);
   if (bf16)
     hipLaunchKernelGGL(repeat_gate_kernel<bf16_t>, dim3(static_cast<unsigned>(rows)), dim3(kThreads),
                        0, s, y, static_cast<const bf16_t *>(z), static_cast<bf16_t *>(out),
-                       static_cast<int>(H), static_cast<int>(W), axis, scale);
+                       static_cast<int>(H), static_cast<int>(W), axis, scale, vec);
   else
     hipLaunchKernelGGL(repeat_gate_kernel<float>, dim3(static_cast<unsigned>(rows)), dim3(kThreads),
                        0, s, y, static_cast<const float *>(z), static_cast<float *>(out),
-                       static_cast<int>(H), static_cast<int>(W), axis, scale);
+                       static_cast<int>(H), static_cast<int>(W), axis, scale, vec);
   return hipGetLastError();
 }
 

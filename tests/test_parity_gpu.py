@@ -221,12 +221,15 @@ def test_es2d_pipeline(H, W):
 
 
 # ---------------------------------------------------------------- pooled
+# (12, 10): scalar pooling path; (12, 32) and (40, 8): four-wide path with
+# 8 and 2 threads per grid row and a ragged last pass.
+@pytest.mark.parametrize("H,W", [(12, 10), (12, 32), (40, 8)])
 @pytest.mark.parametrize("axis", [0, 1])
 @pytest.mark.parametrize("bidir", [True, False])
 @pytest.mark.parametrize("gated", [True, False])
-def test_pool_scan_repeat_fp32(axis, bidir, gated):
-    _case(f"pool axis{axis} bidir{bidir} gated{gated}")
-    fwd, bwd, z = wl.fastvim_inputs(500 + axis, 2, 70, 12, 10, axis, device=DEV, perturb=True)
+def test_pool_scan_repeat_fp32(H, W, axis, bidir, gated):
+    _case(f"pool {H}x{W} axis{axis} bidir{bidir} gated{gated}")
+    fwd, bwd, z = wl.fastvim_inputs(500 + axis, 2, 70, H, W, axis, device=DEV, perturb=True)
     out = vm.vm_pool_scan_repeat(fwd, bwd if bidir else None, z=z if gated else None,
                                  combine_scale=0.5, pool_axis=axis)
     torch.cuda.synchronize()
@@ -253,12 +256,13 @@ def test_pool_repeat_indexing_bit_exact(axis):
     assert np.array_equal(host(out), ref)
 
 
-def test_pool_bf16():
-    _case("pool bf16")
-    fwd, bwd, z = wl.fastvim_inputs(700, 2, 70, 16, 12, 1, device=DEV, dtype=torch.bfloat16)
-    out = vm.vm_pool_scan_repeat(fwd, bwd, z=z, pool_axis=1)
+@pytest.mark.parametrize("H,W,axis", [(16, 12, 1), (20, 16, 0), (20, 16, 1)])
+def test_pool_bf16(H, W, axis):
+    _case(f"pool bf16 {H}x{W} axis{axis}")
+    fwd, bwd, z = wl.fastvim_inputs(700, 2, 70, H, W, axis, device=DEV, dtype=torch.bfloat16)
+    out = vm.vm_pool_scan_repeat(fwd, bwd, z=z, pool_axis=axis)
     torch.cuda.synchronize()
-    ref = oracle.pool_scan_repeat(host_dir(fwd), host_dir(bwd), z=host(z), pool_axis=1)
+    ref = oracle.pool_scan_repeat(host_dir(fwd), host_dir(bwd), z=host(z), pool_axis=axis)
     assert_close(host(out), ref, BF16_TOL, "pool bf16")
 
 
