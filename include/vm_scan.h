@@ -126,8 +126,10 @@ int vm_selective_scan_fwd(const vm_scan_dir *p, const void *z, void *out,
  * combine_scale = 0.5 is the released averaging model, 1 the summed form.
  * z may be NULL (no gate).  out: [batch, dim, seqlen] (dtype).
  * Temporary memory: for sequences too long for the on-chip exchange buffer
- * (seqlen > ~250), an fp32 [batch, dim, seqlen] exchange buffer when dtype is
- * VM_BF16 (VM_F32 reuses `out` for it).
+ * (seqlen above about 480), an fp32 [batch, dim, seqlen rounded up to 32]
+ * exchange buffer from the library's stream-ordered pool.  With VM_F32, a
+ * seqlen that is a multiple of 32 and a 128-byte aligned `out`, `out` itself
+ * serves as the exchange buffer and nothing is allocated.
  */
 int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
                       const void *z, float combine_scale, void *out,

@@ -157,9 +157,10 @@ template <> __device__ __forceinline__ void bstore<bf16_t>(Rsrc r, uint32_t off,
                                         static_cast<int>(off), 0, 0);
 }
 
-// Register budget: 3 waves per SIMD at a two-lane state split, 4 at four.
+// Register budget: 4 waves per SIMD with 8-step tiles, 2 with 16-step tiles
+// (whose three tiles in flight and staged copies need about 190 VGPRs).
 template <typename Tin, int SPLIT, int DIRS, int XMODE, int T>
-__global__ void __launch_bounds__(64 * DIRS) __attribute__((amdgpu_waves_per_eu(SPLIT == 2 ? 3 : 4)))
+__global__ void __launch_bounds__(64 * DIRS) __attribute__((amdgpu_waves_per_eu(T == 16 ? 2 : 4)))
 scan_kernel(const ScanArgs p) {
   constexpr int NS = 16 / SPLIT;                 // states per lane
   constexpr int R = 64 / SPLIT;                  // channels per workgroup
@@ -514,9 +515,9 @@ hipError_t launch_one(const ScanPlan &plan, const ScanArgs &a, hipStream_t s) {
 
 template <typename Tin, int SPLIT>
 hipError_t dispatch_mode(const ScanPlan &plan, const ScanArgs &a, hipStream_t s) {
-  if (plan.dirs == 1) return launch_one<Tin, SPLIT, 1, kXNone, 8>(plan, a, s);
+  if (plan.dirs == 1) return launch_one<Tin, SPLIT, 1, kXNone, 16>(plan, a, s);
   if (plan.xmode == kXLds) return launch_one<Tin, SPLIT, 2, kXLds, 8>(plan, a, s);
-  return launch_one<Tin, SPLIT, 2, kXGlobal, 8>(plan, a, s);
+  return launch_one<Tin, SPLIT, 2, kXGlobal, 16>(plan, a, s);
 }
 
 template <typename Tin>
@@ -544,13 +545,16 @@ ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t L, int dstate, int dirs) 
   // larger LDS exchange per workgroup).
   pl.S = 4;
   pl.blocks = batch * ((dim + 64 / pl.S - 1) / (64 / pl.S));
+  // Tile length: 16 steps where the registers allow it (one direction, or
+  // the global exchange: longer row segments per load and half the per-tile
+  // overhead); 8 for the on-chip exchange, whose LDS footprint grows with T.
   if (dirs == 1) {
-    pl.T = 8;
+    pl.T = 16;
     pl.xmode = kXNone;
   } else {
     // On-chip exchange while at least four workgroups fit a CU's 160 KB LDS.
-    pl.T = 8;
     pl.xmode = lds_bytes(pl.S, 2, 8, kXLds, L) <= 40 * 1024 ? kXLds : kXGlobal;
+    pl.T = pl.xmode == kXLds ? 8 : 16;
   }
   pl.lds = lds_bytes(pl.S, dirs, pl.T, pl.xmode, L);
   return pl;
