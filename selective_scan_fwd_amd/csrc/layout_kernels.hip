@@ -17,13 +17,44 @@ constexpr int kPlaneLds = 16384;  // floats of a staged H x W plane (64 KB)
 
 // Step t of group k -> (row, col) on the padded grid.  Offsets (0,0), (1,0),
 // (0,1), (1,1); even groups walk the half grid row-major, odd ones
-// column-major.
-__device__ __forceinline__ void route(int k, int t, int hr, int hc, int &y, int &x) {
-  int r, c;
-  if ((k & 1) == 0) { r = t / hc; c = t - r * hc; }
-  else { c = t / hr; r = t - c * hr; }
-  y = 2 * r + (k & 1);
-  x = 2 * c + (k >> 1);
+// column-major.  Position t = a * n + b of a walk with n entries per line
+// is tracked incrementally: a thread's next element is kThreads further,
+// i.e. (a, b) += (kThreads / n, kThreads % n) with one carry, so no element
+// pays an integer division.
+struct Walk {
+  int a, b, da, db, n;
+  __device__ void init(int t, int n_) {
+    n = n_;
+    a = t / n;
+    b = t - a * n;
+    da = kThreads / n;
+    db = kThreads - da * n;
+  }
+  __device__ void next() {
+    a += da;
+    b += db;
+    if (b >= n) { b -= n; ++a; }
+  }
+};
+
+// n consecutive values from global memory into LDS, U loads in flight per
+// thread before the first LDS store.
+template <typename T>
+__device__ __forceinline__ void copy_to_lds(T *dst, const T *__restrict__ src, int n) {
+  constexpr int U = 8;
+  for (int i0 = threadIdx.x; i0 < n; i0 += U * kThreads) {
+    T v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kThreads;
+      v[u] = i < n ? src[i] : T(0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kThreads;
+      if (i < n) dst[i] = v[u];
+    }
+  }
 }
 
 // One workgroup per (b, c) plane: stage the plane in LDS with coalesced
@@ -39,14 +70,16 @@ atrous_gather_kernel(const T *__restrict__ x, T *__restrict__ streams, int64_t c
   const int hr = (H + 1) / 2, hc = (W + 1) / 2, Lg = hr * hc;
   const T *src = x + pid * H * W;
   if (staged) {
-    for (int i = threadIdx.x; i < H * W; i += kThreads) plane[i] = src[i];
+    copy_to_lds(plane, src, H * W);
     __syncthreads();
   }
   for (int k = 0; k < 4; ++k) {
     T *dst = streams + ((b * 4 + k) * ch + c) * Lg;
-    for (int t = threadIdx.x; t < Lg; t += kThreads) {
-      int yy, xx;
-      route(k, t, hr, hc, yy, xx);
+    Walk w;
+    w.init(threadIdx.x, (k & 1) == 0 ? hc : hr);   // (r, c) or (c, r)
+    for (int t = threadIdx.x; t < Lg; t += kThreads, w.next()) {
+      const int r = (k & 1) == 0 ? w.a : w.b, cc = (k & 1) == 0 ? w.b : w.a;
+      const int yy = 2 * r + (k & 1), xx = 2 * cc + (k >> 1);
       T v = T(0);
       if (yy < H && xx < W) v = staged ? plane[yy * W + xx] : src[yy * W + xx];
       dst[t] = v;
@@ -56,20 +89,31 @@ atrous_gather_kernel(const T *__restrict__ x, T *__restrict__ streams, int64_t c
 
 // Inverse routing: every valid (row, col) has exactly one owner, group
 // k = (row & 1) + 2 (col & 1) at step t of that group; copy it, write each
-// output once (no sums).  Stores are coalesced over the plane.
+// output once (no sums).  When the plane's four streams fit in LDS they are
+// staged there first with coalesced loads; the plane is then written with
+// coalesced stores.
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
-atrous_scatter_kernel(const T *__restrict__ streams, T *__restrict__ y, int64_t ch, int H, int W) {
+atrous_scatter_kernel(const T *__restrict__ streams, T *__restrict__ y, int64_t ch, int H, int W,
+                      int staged) {
+  extern __shared__ unsigned char st_raw[];
+  T *st = reinterpret_cast<T *>(st_raw);        // [4][Lg] when staged
   const int64_t pid = blockIdx.x;
   const int64_t b = pid / ch, c = pid - b * ch;
   const int hr = (H + 1) / 2, hc = (W + 1) / 2, Lg = hr * hc;
+  if (staged) {
+    for (int k = 0; k < 4; ++k) copy_to_lds(st + k * Lg, streams + ((b * 4 + k) * ch + c) * Lg, Lg);
+    __syncthreads();
+  }
   T *dst = y + pid * H * W;
-  for (int i = threadIdx.x; i < H * W; i += kThreads) {
-    const int yy = i / W, xx = i - (i / W) * W;
+  Walk w;
+  w.init(threadIdx.x, W);                       // (row, col) of the plane
+  for (int i = threadIdx.x; i < H * W; i += kThreads, w.next()) {
+    const int yy = w.a, xx = w.b;
     const int k = (yy & 1) + 2 * (xx & 1);
     const int r = yy >> 1, cc = xx >> 1;
     const int t = (k & 1) == 0 ? r * hc + cc : cc * hr + r;
-    dst[i] = streams[((b * 4 + k) * ch + c) * Lg + t];
+    dst[i] = staged ? st[k * Lg + t] : streams[((b * 4 + k) * ch + c) * Lg + t];
   }
 }
 
@@ -258,14 +302,17 @@ hipError_t launch_atrous_scatter(const void *streams, void *y, int64_t batch, in
                                  int64_t H, int64_t W, bool bf16, hipStream_t s) {
   const int64_t planes = batch * ch;
   if (planes == 0) return hipSuccess;
+  const int64_t Lg = ((H + 1) / 2) * ((W + 1) / 2);
+  const int staged = (4 * Lg <= kPlaneLds) ? 1 : 0;
+  const size_t lds = staged ? static_cast<size_t>(4 * Lg) * (bf16 ? 2 : 4) : 0;
   if (bf16)
-    hipLaunchKernelGGL(atrous_scatter_kernel<bf16_t>, dim3(planes), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(atrous_scatter_kernel<bf16_t>, dim3(planes), dim3(kThreads), lds, s,
                        static_cast<const bf16_t *>(streams), static_cast<bf16_t *>(y), ch,
-                       static_cast<int>(H), static_cast<int>(W));
+                       static_cast<int>(H), static_cast<int>(W), staged);
   else
-    hipLaunchKernelGGL(atrous_scatter_kernel<float>, dim3(planes), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(atrous_scatter_kernel<float>, dim3(planes), dim3(kThreads), lds, s,
                        static_cast<const float *>(streams), static_cast<float *>(y), ch,
-                       static_cast<int>(H), static_cast<int>(W));
+                       static_cast<int>(H), static_cast<int>(W), staged);
   return hipGetLastError();
 }
 
