@@ -88,9 +88,13 @@ def test_single_bf16():
 # Shapes chosen to cover: one tile (joint midpoint), odd / even tile counts,
 # the LDS exchange with 8- and 4-step tiles, the global exchange (long L),
 # and both state splits (S = 4 on few row blocks, S = 2 on >= 512 blocks).
+# L = 456 is the longest sequence of the on-chip exchange (its LDS block is
+# 16 x 456 floats); 457 and 500 take the global exchange through a pool
+# buffer, 512 (fp32, L % 32 == 0) parks in `out` itself.
 BIDIR_CASES = [
     (1, 1, 1), (2, 70, 2), (2, 70, 16), (2, 70, 77), (2, 130, 197), (2, 70, 300),
     (512, 64, 20), (512, 64, 197), (256, 128, 300),
+    (2, 40, 456), (2, 40, 457), (1, 33, 500), (2, 20, 512),
 ]
 
 
@@ -278,6 +282,25 @@ def test_full_vim_tiny_bidir():
     ref = oracle.bidir_scan(sub_dir(host_dir(fwd), bsel, dsel), sub_dir(host_dir(bwd), bsel, dsel),
                             z=host(z)[bsel][:, dsel], combine_scale=w.combine_scale)
     assert_close(host(out[bsel]), ref, FP32_TOL, "vim-t full (sampled batches)")
+
+
+@pytest.mark.parametrize("bidir", [False, True])
+def test_long_sequence(bidir):
+    # 2^20 steps (the offsets stay far from the 2 GiB resource limit, which
+    # the host rejects before launch): every element, against the oracle
+    L = 1 << 20
+    _case(f"long sequence L={L} bidir={bidir}")
+    if bidir:
+        fwd, bwd, z = wl.bidir_inputs(1300, 1, 16, L, device=DEV, perturb=True)
+        out = vm.vm_bidir_scan_fwd(fwd, bwd, z=z)
+        torch.cuda.synchronize()
+        ref = oracle.bidir_scan(host_dir(fwd), host_dir(bwd), z=host(z))
+    else:
+        p, z = wl.single_inputs(1301, 1, 16, L, device=DEV)
+        out = vm.vm_selective_scan_fwd(**p, z=z, reverse=True)
+        torch.cuda.synchronize()
+        ref = oracle.selective_scan(**host_dir(p), z=host(z), reverse=True)
+    assert_close(host(out), ref, FP32_TOL, "long")
 
 
 def test_full_single():
