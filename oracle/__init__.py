@@ -57,9 +57,12 @@ def _load():
             lib.vmo_mean_pool.argtypes = [_D] + [_I64] * 4 + [ctypes.c_int, _D]
             lib.vmo_pool_scan_repeat.argtypes = ([_D] * 15 + [ctypes.c_double] + [_I64] * 5
                                                  + [ctypes.c_int] * 2 + [_D])
+            _D4 = _D * 4
+            lib.vmo_ss2d_scan.argtypes = ([_D] + [_D4] * 6 + [_D, ctypes.c_double] + [_I64] * 5
+                                          + [ctypes.c_int, _D])
             for name in ("vmo_selective_scan", "vmo_bidir_scan", "vmo_atrous_route",
                          "vmo_atrous_gather", "vmo_atrous_scatter", "vmo_mean_pool",
-                         "vmo_pool_scan_repeat"):
+                         "vmo_pool_scan_repeat", "vmo_ss2d_scan"):
                 getattr(lib, name).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -197,4 +200,28 @@ def pool_scan_repeat(fwd, bwd, z=None, combine_scale=1.0, pool_axis=0, delta_sof
                                         _p(z), float(combine_scale), batch, dim, H, W, N,
                                         int(pool_axis), int(bool(delta_softplus)), _p(out)),
            "pool_scan_repeat")
+    return out
+
+
+def ss2d_scan(u, dirs, z=None, combine_scale=1.0, delta_softplus=True):
+    """Four-direction 2-D scan with summed merge ("Norm or Direction?" page,
+    section 3, "2D Selective Scan (SS2D)"; EfficientVMamba page, "Merge
+    restores coordinates instead of adding directions").  u, z: [batch, dim,
+    H, W].  dirs: four dicts with delta, A, B, C, D, delta_bias; directions 0
+    and 1 (row-major, then reversed) index delta, B, C by row-major step
+    [batch, dim or N, H*W], directions 2 and 3 (column-major, then reversed)
+    by column-major step.  Returns float64 [batch, dim, H, W]."""
+    u, z = _f64(u), _f64(z)
+    batch, dim, H, W = u.shape
+    ds = [_dir(p) for p in dirs]
+    assert len(ds) == 4
+    N = ds[0][2].shape[1]
+    for _, d, A, B, C, D, _b in ds:
+        assert d.shape == (batch, dim, H * W) and A.shape == (dim, N)
+        assert B.shape == (batch, N, H * W) and C.shape == B.shape and D.shape == (dim,)
+    arr = lambda i: (_D * 4)(*[_p(x[i]) for x in ds])
+    out = np.empty_like(u)
+    _check(_load().vmo_ss2d_scan(_p(u), arr(1), arr(2), arr(3), arr(4), arr(5), arr(6), _p(z),
+                                 float(combine_scale), batch, dim, H, W, N,
+                                 int(bool(delta_softplus)), _p(out)), "ss2d_scan")
     return out

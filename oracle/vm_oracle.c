@@ -378,3 +378,60 @@ int vmo_pool_scan_repeat(const double *uf, const double *df, const double *Af,
   free(pf); free(pb); free(yf); free(yb);
   return s;
 }
+
+/*
+ * Four-direction 2-D selective scan with aligned summation ("Norm or
+ * Direction? Decoding Vision Mambas for High-Resolution Vision", section 3
+ * "Background", paragraph "2D Selective Scan (SS2D)": the feature map is
+ * traversed top-to-bottom, bottom-to-top, left-to-right and right-to-left,
+ * each sequence goes through its own S6 scan and the outputs are put back
+ * in the 2-D layout; [EVM] "Merge restores coordinates instead of adding
+ * directions": in dense SS2D every pixel receives an output from every
+ * direction and the aligned outputs are summed).
+ *
+ * Direction k = 0 visits the H x W grid row-major (step t at pixel
+ * (t / W, t % W)), k = 1 the same order reversed, k = 2 column-major (step t
+ * at pixel (t % H, t / H)), k = 3 that order reversed.  u is the one map
+ * [batch][dim][H][W] all four traverse.  Direction k's delta_k, B_k, C_k are
+ * indexed by the step of its base order (row-major for k = 0, 1,
+ * column-major for k = 2, 3), like the two directions of vmo_bidir_scan;
+ * each direction has its own A, D and bias.
+ *
+ * Here each traversal is written out as a list of pixel positions, u is
+ * gathered along it, scanned with vmo_selective_scan (reverse = 1 for the
+ * reversed orders) and the result is added back at the same positions:
+ *   out = scale * (sum_k y_k) * SiLU(z)      (z may be NULL)
+ */
+int vmo_ss2d_scan(const double *u, const double *const delta[4],
+                  const double *const A[4], const double *const B[4],
+                  const double *const C[4], const double *const D[4],
+                  const double *const bias[4], const double *z, double scale,
+                  int64_t batch, int64_t dim, int64_t H, int64_t W, int64_t N,
+                  int delta_softplus, double *out) {
+  if (!u || !out || batch <= 0 || dim <= 0 || H <= 0 || W <= 0 || N <= 0)
+    return VMO_EBADARG;
+  for (int k = 0; k < 4; ++k)
+    if (!delta[k] || !A[k] || !B[k] || !C[k] || !D[k]) return VMO_EBADARG;
+  const int64_t L = H * W, rows = batch * dim;
+  int64_t *pos = (int64_t *)malloc(sizeof(int64_t) * (size_t)L);
+  double *uk = (double *)malloc(sizeof(double) * (size_t)(rows * L));
+  double *yk = (double *)malloc(sizeof(double) * (size_t)(rows * L));
+  int s = (pos && uk && yk) ? 0 : VMO_ENOMEM;
+  for (int64_t e = 0; s == 0 && e < rows * L; ++e) out[e] = 0.0;
+  for (int k = 0; s == 0 && k < 4; ++k) {
+    for (int64_t t = 0; t < L; ++t)   /* pixel (i, j) as flat i * W + j */
+      pos[t] = k < 2 ? t : (t % H) * W + t / H;
+    for (int64_t r = 0; r < rows; ++r)
+      for (int64_t t = 0; t < L; ++t) uk[r * L + t] = u[r * L + pos[t]];
+    s = vmo_selective_scan(uk, delta[k], A[k], B[k], C[k], D[k], NULL, bias[k],
+                           batch, dim, L, N, delta_softplus, k % 2, yk);
+    for (int64_t r = 0; s == 0 && r < rows; ++r)
+      for (int64_t t = 0; t < L; ++t) out[r * L + pos[t]] += yk[r * L + t];
+  }
+  for (int64_t e = 0; s == 0 && e < rows * L; ++e) {
+    double y = scale * out[e];
+    out[e] = z ? y * silu(z[e]) : y;
+  }
+  free(pos); free(uk); free(yk);
+  return s;
+}

@@ -392,3 +392,62 @@ def test_pool_repeat_broadcast_axis(axis):
     silu = z / (1 + np.exp(-z))
     want = (y[:, :, :, None] if axis == 0 else y[:, :, None, :]) * silu
     _close(out, want, 1e-12)
+
+
+# ---------------------------------------------------------------- SS2D
+def _ss2d_dirs(rng, batch, dim, H, W, N):
+    return [dict(delta=rng.standard_normal((batch, dim, H * W)) * 0.5,
+                 A=-rng.uniform(0.2, 3.0, size=(dim, N)),
+                 B=rng.standard_normal((batch, N, H * W)),
+                 C=rng.standard_normal((batch, N, H * W)),
+                 D=rng.standard_normal(dim),
+                 delta_bias=rng.uniform(-1.5, 0.5, size=dim)) for _ in range(4)]
+
+
+def test_ss2d_brute_force():
+    # four traversals written out here as pixel lists: left-to-right rows,
+    # their reverse, top-to-bottom columns, their reverse; each scanned by the
+    # materialised-kernel brute force and summed back at its pixels
+    rng = _rng(41)
+    batch, dim, H, W, N = 2, 2, 2, 3, 3
+    u = rng.standard_normal((batch, dim, H, W))
+    z = rng.standard_normal((batch, dim, H, W))
+    dirs = _ss2d_dirs(rng, batch, dim, H, W, N)
+    rows = [(i, j) for i in range(H) for j in range(W)]
+    cols = [(i, j) for j in range(W) for i in range(H)]
+    want = np.zeros((batch, dim, H, W))
+    for k in range(4):
+        order = rows if k < 2 else cols
+        uk = np.stack([u[:, :, i, j] for (i, j) in order], axis=-1)
+        yk = _brute(dict(dirs[k], u=uk), reverse=(k % 2 == 1))
+        for t, (i, j) in enumerate(order):
+            want[:, :, i, j] += yk[:, :, t]
+    want = 0.5 * want * z / (1.0 + np.exp(-z))
+    got = oracle.ss2d_scan(u, dirs, z=z, combine_scale=0.5)
+    _close(got, want, 1e-12)
+
+
+@pytest.mark.parametrize("H,W", [(1, 7), (6, 1)])
+def test_ss2d_line_is_twice_bidir(H, W):
+    # on a single row or column both traversal orders coincide: with the
+    # column directions given the row directions' parameters, SS2D is twice
+    # the bidirectional scan
+    rng = _rng(42 + H)
+    u = rng.standard_normal((1, 3, H, W))
+    d = _ss2d_dirs(rng, 1, 3, H, W, 4)
+    dirs = [d[0], d[1], d[0], d[1]]
+    got = oracle.ss2d_scan(u, dirs)
+    flat = u.reshape(1, 3, H * W)
+    want = 2.0 * oracle.bidir_scan(dict(d[0], u=flat), dict(d[1], u=flat))
+    _close(got.reshape(1, 3, H * W), want, 1e-12)
+
+
+def test_ss2d_transpose_symmetry():
+    # the column traversals of u are the row traversals of u transposed
+    rng = _rng(43)
+    u = rng.standard_normal((2, 2, 3, 5))
+    z = rng.standard_normal(u.shape)
+    d = _ss2d_dirs(rng, 2, 2, 3, 5, 4)
+    got = oracle.ss2d_scan(u, d, z=z)
+    tr = oracle.ss2d_scan(u.transpose(0, 1, 3, 2), [d[2], d[3], d[0], d[1]], z=z.transpose(0, 1, 3, 2))
+    _close(got, tr.transpose(0, 1, 3, 2), 1e-12)

@@ -28,6 +28,9 @@ MUTANTS = [
     ("pad_not_zero", "? plane[rr[t] * W + cc[t]] : 0.0;", "? plane[rr[t] * W + cc[t]] : 1.0;"),
     ("pool_wrong_extent", "pooled[r * H + i] = s / (double)W;", "pooled[r * H + i] = s / (double)H;"),
     ("repeat_wrong_axis", "int64_t p = axis == 0 ? i : j;", "int64_t p = axis == 0 ? (j % Lp) : (i % Lp);"),
+    ("ss2d_columns_as_rows", "pos[t] = k < 2 ? t : (t % H) * W + t / H;", "pos[t] = t;"),
+    ("ss2d_no_reverse", "N, delta_softplus, k % 2, yk);", "N, delta_softplus, 0, yk);"),
+    ("ss2d_overwrite_not_sum", "out[r * L + pos[t]] += yk[r * L + t];", "out[r * L + pos[t]] = yk[r * L + t];"),
 ]
 
 
