@@ -54,7 +54,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1,
                     help="0 single, 1 Vim-T bidir (default), 2 bf16 L=4097, 3 ES2D 56x56, "
-                         "4 FastVim pooled (axes alternate per step), 5 FastVim unpooled L=16384")
+                         "4 FastVim pooled (axes alternate per step), 5 FastVim unpooled L=16384, "
+                         "6 SS2D four-direction scan 56x56")
     ap.add_argument("--sets", type=int, default=0, help="input sets to cycle (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
@@ -234,6 +235,47 @@ def build_step(cfg, seed, sets, dev):
         tokens = w.batch * w.dim * L
         return step, info, None, nbytes, tokens, slots
 
+    if cfg == 6:
+        w = wl.WORKLOADS[5]
+        H, W = w.height, w.width
+        L = H * W
+        inputs = [wl.ss2d_inputs(seed + k, w.batch, w.dim, H, W, device=dev) for k in range(sets)]
+        outs = [torch.empty((w.batch, w.dim, H, W), device=dev) for _ in range(sets)]
+
+        def step(i):
+            u, dirs, z = inputs[i % sets]
+            vm.vm_ss2d_scan_fwd(u, dirs, z=z, combine_scale=w.combine_scale, out=outs[i % sets])
+
+        tok = w.batch * w.dim * L
+        # u, z and out once; delta, B, C and the parameters once per traversal
+        nbytes = 3 * tok * 4 + 4 * (tok * 4 + 2 * w.batch * L * N * 4 + w.dim * (N + 2) * 4)
+        tokens = tok
+        slots = 4 * tok * N * SLOTS_PER_STATE_STEP
+        info = dict(workload=w.name, batch=w.batch, dim=w.dim, height=H, width=W, dstate=N,
+                    directions=4, kernels="transpose + 2 bidir scans + merge")
+
+        def cpu(budget):
+            import oracle
+            u, dirs, z = inputs[0]
+            sub = 1
+            hu = u[:sub].double().cpu().numpy()
+            hz = z[:sub].double().cpu().numpy()
+            hd = [{k: (v[:sub].double().cpu().numpy() if k in ("delta", "B", "C") else
+                       v.double().cpu().numpy()) for k, v in p.items()} for p in dirs]
+            run = lambda: oracle.ss2d_scan(hu, hd, z=hz, combine_scale=w.combine_scale)
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                run()
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= budget or reps >= 100:
+                    break
+            frac = sub / w.batch
+            return el / reps, nbytes * frac, tokens * frac, oracle.num_threads(), \
+                f"fp64 oracle SS2D on {sub} of {w.batch} batch rows, {reps} repetitions"
+
+        return step, info, cpu, nbytes, tokens, slots
+
     raise SystemExit(f"unknown --config {cfg}")
 
 
@@ -272,7 +314,7 @@ def main():
         sys.exit(1)
     vm.load_library()
     dev = torch.device("cuda:0")
-    sets = args.sets or (3 if args.config in (0, 1, 2, 3) else 1)
+    sets = args.sets or (3 if args.config in (0, 1, 2, 3, 6) else 1)
     step, info, cpu_fn, nbytes, tokens, slots = build_step(args.config, args.seed, sets, dev)
     torch.cuda.synchronize()
 

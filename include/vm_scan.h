@@ -1,7 +1,7 @@
 /*
  * vm_scan.h -- C ABI of the selective-scan hot path for vision Mamba
  * backbones (Vim bidirectional blocks, EfficientVMamba atrous ES2D, FastVim
- * pooled scan) on AMD Instinct MI355X (gfx950).
+ * pooled scan, four-direction SS2D) on AMD Instinct MI355X (gfx950).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -30,6 +30,8 @@
  *  [EVM]  "EfficientVMamba: Atrous Selective Scan for Light Weight Visual Mamba"
  *  [FVim] "Fast Vision Mamba: Pooling Spatial Dimensions for Accelerated
  *         Processing"
+ *  [NoD]  "Norm or Direction? Decoding Vision Mambas for High-Resolution
+ *         Vision"
  */
 #ifndef VM_SCAN_H
 #define VM_SCAN_H
@@ -52,9 +54,11 @@ enum {
   VM_ERR_FLAG = 4,        /* a flag is not 0/1, or pool_axis not 0/1          */
   VM_ERR_ALIAS = 5,       /* the output overlaps an input                     */
   VM_ERR_UNSUPPORTED = 6, /* dstate outside [1, 16], a non-finite scale, or
-                             sizes past the kernel's 32-bit offsets: 32 rows
-                             of seqlen + 16 steps, or one batch row of B or C,
-                             must span < 2 GiB                               */
+                             sizes past the kernels' 32-bit offsets or grid
+                             limits: 32 rows of seqlen + 16 steps, or one
+                             batch row of B or C, must span < 2 GiB; the map
+                             calls (atrous, pooled, SS2D) take at most
+                             2^24 - 1 planes (batch * channels)              */
   VM_ERR_HIP = 7,         /* a HIP launch or runtime call failed              */
   VM_ERR_ALLOC = 8        /* temporary device memory could not be obtained    */
 };
@@ -187,6 +191,35 @@ int vm_pool_scan_repeat(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
                         int64_t batch, int64_t dim, int64_t height,
                         int64_t width, int64_t dstate, int pool_axis,
                         int dtype, int delta_softplus, void *stream);
+
+/*
+ * Four-direction 2-D selective scan with summed merge ([NoD] section 3,
+ * "2D Selective Scan (SS2D)": four traversals of the map, one S6 scan each,
+ * outputs restored to the map and merged; the merge of full SS2D adds the
+ * four aligned outputs, [EVM] "Merge restores coordinates instead of adding
+ * directions"):
+ *   traversal 0: row-major, pixel (i, j) at step i*W + j
+ *   traversal 1: traversal 0 reversed
+ *   traversal 2: column-major, pixel (i, j) at step j*H + i
+ *   traversal 3: traversal 2 reversed
+ *   out[b,d,i,j] = combine_scale * sum_k y_k[b,d,(i,j)] * SiLU(z[b,d,i,j])
+ * u, z, out: [batch, dim, H, W] (dtype); z may be NULL.  dirs[4]: the four
+ * traversals' parameters; dirs[k].u is ignored (every traversal reads u).
+ * delta [batch, dim, H*W] and B, C [batch, dstate, H*W] (or token-major, see
+ * bc_stride) are indexed by traversal step: row-major for traversals 0 and 1,
+ * column-major for 2 and 3.  A traversal's D skip adds D * u at each pixel,
+ * so the merged skip is (D_0 + D_1 + D_2 + D_3) * u.  The H and W 32-pixel
+ * tile counts multiplied must not exceed 65535 (VM_ERR_UNSUPPORTED).
+ * Temporary memory: fp32 [batch, dim, H, W] buffers for the transposed u and
+ * the column traversals' sum, plus (VM_BF16) the row traversals' sum and fp32
+ * copies of u, delta, B and C, plus the exchange buffers of long sequences as
+ * in vm_bidir_scan_fwd.
+ */
+int vm_ss2d_scan_fwd(const vm_scan_dir *dirs, const void *u, const void *z,
+                     float combine_scale, void *out, int64_t batch,
+                     int64_t dim, int64_t height, int64_t width,
+                     int64_t dstate, int dtype, int delta_softplus,
+                     void *stream);
 
 #ifdef __cplusplus
 }

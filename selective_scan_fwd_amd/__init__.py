@@ -9,7 +9,8 @@ library is missing or fails to load, every call raises.
 
 Names and argument order follow the C ABI:
   vm_selective_scan_fwd, vm_bidir_scan_fwd, vm_atrous_gather,
-  vm_atrous_scatter, vm_pool_scan_repeat, vm_atrous_group_len.
+  vm_atrous_scatter, vm_pool_scan_repeat, vm_ss2d_scan_fwd,
+  vm_atrous_group_len.
 """
 from __future__ import annotations
 
@@ -28,7 +29,8 @@ STATUS_NAMES = {0: "VM_OK", 1: "VM_ERR_NULL", 2: "VM_ERR_SHAPE", 3: "VM_ERR_DTYP
                 5: "VM_ERR_ALIAS", 6: "VM_ERR_UNSUPPORTED", 7: "VM_ERR_HIP", 8: "VM_ERR_ALLOC"}
 
 EXPORTED = ("vm_status_string", "vm_version", "vm_selective_scan_fwd", "vm_bidir_scan_fwd",
-            "vm_atrous_group_len", "vm_atrous_gather", "vm_atrous_scatter", "vm_pool_scan_repeat")
+            "vm_atrous_group_len", "vm_atrous_gather", "vm_atrous_scatter", "vm_pool_scan_repeat",
+            "vm_ss2d_scan_fwd")
 
 
 class VmScanDir(ctypes.Structure):
@@ -70,8 +72,9 @@ def load_library():
             lib.vm_atrous_gather.argtypes = [P, P, I64, I64, I64, I64, I, P]
             lib.vm_atrous_scatter.argtypes = [P, P, I64, I64, I64, I64, I, P]
             lib.vm_pool_scan_repeat.argtypes = [D, D, P, F, P, I64, I64, I64, I64, I64, I, I, I, P]
+            lib.vm_ss2d_scan_fwd.argtypes = [D, P, P, F, P, I64, I64, I64, I64, I64, I, I, P]
             for name in ("vm_selective_scan_fwd", "vm_bidir_scan_fwd", "vm_atrous_gather",
-                         "vm_atrous_scatter", "vm_pool_scan_repeat"):
+                         "vm_atrous_scatter", "vm_pool_scan_repeat", "vm_ss2d_scan_fwd"):
                 getattr(lib, name).restype = I
             _lib = lib
     return _lib
@@ -270,6 +273,37 @@ def vm_pool_scan_repeat(fwd, bwd=None, z=None, combine_scale=1.0, pool_axis=0, d
     return out
 
 
+def vm_ss2d_scan_fwd(u, dirs, z=None, combine_scale=1.0, delta_softplus=True, out=None):
+    """Four-direction 2-D scan with summed merge.  u, z: [batch, dim, H, W].
+    dirs: four dicts with delta, A, B, C, D, delta_bias (a "u" key is
+    ignored); traversals 0 / 1 are row-major forward / reversed, 2 / 3
+    column-major forward / reversed, and each indexes its delta [batch, dim,
+    H*W] and B, C [batch, N, H*W] by its own traversal step.
+    Returns combine_scale * (sum of the four aligned outputs) * SiLU(z)."""
+    _dev(u, "u")
+    dt = u.dtype
+    batch, dim, H, W = u.shape
+    if len(dirs) != 4:
+        raise ValueError("dirs must hold four traversals")
+    N = dirs[0]["A"].shape[-1]
+    arr = (VmScanDir * 4)()
+    keep = []
+    for k, p in enumerate(dirs):
+        d, kp = _direction(dict(p, u=u), batch, dim, (batch, dim, H, W), H * W, N, dt, u.device,
+                           f"dirs[{k}]")
+        arr[k] = d
+        keep.append(kp)
+    if z is not None:
+        _dev(z, "z", dt, u.shape, u.device)
+    out = torch.empty_like(u) if out is None else _dev(out, "out", dt, u.shape, u.device)
+    with torch.cuda.device(u.device):
+        st = load_library().vm_ss2d_scan_fwd(arr, _ptr(u), _ptr(z), float(combine_scale), _ptr(out),
+                                             batch, dim, H, W, N, _dtype_code(u),
+                                             int(bool(delta_softplus)), _stream(u.device))
+    _check(st, "vm_ss2d_scan_fwd")
+    return out
+
+
 __all__ = ["vm_selective_scan_fwd", "vm_bidir_scan_fwd", "vm_atrous_gather", "vm_atrous_scatter",
-           "vm_pool_scan_repeat", "vm_atrous_group_len", "vm_status_string", "vm_version",
+           "vm_pool_scan_repeat", "vm_ss2d_scan_fwd", "vm_atrous_group_len", "vm_status_string", "vm_version",
            "VmScanDir", "VmError", "load_library", "LIB_PATH", "EXPORTED"]

@@ -17,6 +17,10 @@ namespace {
 
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
 constexpr int64_t kMaxElems = int64_t{1} << 40;
+// The map kernels (gather, scatter, pool, repeat, transpose, merge) run one
+// 256-thread workgroup per [H, W] plane on grid x: planes * 256 work-items
+// must stay below 2^32.
+constexpr int64_t kMaxPlanes = (int64_t{1} << 24) - 1;
 
 struct Span {
   uintptr_t lo = 0, hi = 0;  // [lo, hi)
@@ -169,6 +173,25 @@ vmk::DirPtrs resolve_dir(const vm_scan_dir *p, int64_t batch, int64_t dstate, in
   return d;
 }
 
+// Plans and launches a bidirectional scan whose arguments are filled in
+// except for the exchange buffer.  fp32 output with line-aligned rows
+// doubles as the exchange buffer; otherwise it comes from the pool.
+int launch_bidir(vmk::ScanArgs &a, bool bf16, Scratch &ws, hipStream_t s) {
+  const vmk::ScanPlan plan = vmk::plan_scan(a.batch, a.dim, a.L, a.dstate, 2);
+  int st = VM_OK;
+  if (plan.xmode == vmk::kXGlobal) {
+    a.xstride = vmk::xchg_global_stride(a.L);
+    if (!bf16 && a.xstride == a.L && reinterpret_cast<uintptr_t>(a.out) % 128 == 0) {
+      a.xglobal = static_cast<float *>(a.out);
+    } else {
+      a.xglobal = ws.get(a.batch * a.dim * a.xstride, &st);
+      if (st != VM_OK) return st;
+    }
+  }
+  if (!vmk::scan_offsets_fit(plan, a, bf16)) return VM_ERR_UNSUPPORTED;
+  return hip_status(vmk::launch_scan(plan, a, bf16, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,7 +204,7 @@ const char *vm_status_string(int status) {
     case VM_ERR_DTYPE: return "VM_ERR_DTYPE: unknown dtype";
     case VM_ERR_FLAG: return "VM_ERR_FLAG: a flag is not 0 or 1";
     case VM_ERR_ALIAS: return "VM_ERR_ALIAS: the output overlaps an input";
-    case VM_ERR_UNSUPPORTED: return "VM_ERR_UNSUPPORTED: dstate outside [1, 16], non-finite scale, or sizes past the 32-bit in-kernel offsets";
+    case VM_ERR_UNSUPPORTED: return "VM_ERR_UNSUPPORTED: dstate outside [1, 16], non-finite scale, or sizes past the kernels' 32-bit offsets or grid limits";
     case VM_ERR_HIP: return "VM_ERR_HIP: a HIP launch or runtime call failed";
     case VM_ERR_ALLOC: return "VM_ERR_ALLOC: temporary device memory unavailable";
     default: return "unknown status";
@@ -265,19 +288,7 @@ int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
   a.softplus = delta_softplus;
   a.reverse = 0;
   a.scale = combine_scale;
-  const vmk::ScanPlan plan = vmk::plan_scan(batch, dim, seqlen, a.dstate, 2);
-  if (plan.xmode == vmk::kXGlobal) {
-    // fp32 output with line-aligned rows doubles as the exchange buffer
-    a.xstride = vmk::xchg_global_stride(seqlen);
-    if (!bf16 && a.xstride == seqlen && reinterpret_cast<uintptr_t>(out) % 128 == 0) {
-      a.xglobal = static_cast<float *>(out);
-    } else {
-      a.xglobal = ws.get(batch * dim * a.xstride, &st);
-      if (st != VM_OK) return st;
-    }
-  }
-  if (!vmk::scan_offsets_fit(plan, a, bf16)) return VM_ERR_UNSUPPORTED;
-  return hip_status(vmk::launch_scan(plan, a, bf16, s));
+  return launch_bidir(a, bf16, ws, s);
 }
 
 int vm_atrous_gather(const void *x, void *streams, int64_t batch, int64_t channels,
@@ -288,6 +299,7 @@ int vm_atrous_gather(const void *x, void *streams, int64_t batch, int64_t channe
   if (Lg <= 0 || !dims_ok({batch, channels, height, width}, &n_in) ||
       !dims_ok({batch, 4, channels, Lg}, &n_out))
     return VM_ERR_SHAPE;
+  if (batch * channels > kMaxPlanes) return VM_ERR_UNSUPPORTED;
   if (x == nullptr || streams == nullptr) return VM_ERR_NULL;
   const int es = dtype == VM_BF16 ? 2 : 4;
   if (overlaps(span(x, n_in * es), span(streams, n_out * es))) return VM_ERR_ALIAS;
@@ -303,6 +315,7 @@ int vm_atrous_scatter(const void *streams, void *y, int64_t batch, int64_t chann
   if (Lg <= 0 || !dims_ok({batch, channels, height, width}, &n_out) ||
       !dims_ok({batch, 4, channels, Lg}, &n_in))
     return VM_ERR_SHAPE;
+  if (batch * channels > kMaxPlanes) return VM_ERR_UNSUPPORTED;
   if (streams == nullptr || y == nullptr) return VM_ERR_NULL;
   const int es = dtype == VM_BF16 ? 2 : 4;
   if (overlaps(span(streams, n_in * es), span(y, n_out * es))) return VM_ERR_ALIAS;
@@ -321,7 +334,8 @@ int vm_pool_scan_repeat(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const vo
   if (!dims_ok({batch, dim, height, width}, &full) || !dims_ok({batch, dim, Lp}, &pooled) ||
       dstate <= 0)
     return VM_ERR_SHAPE;
-  if (dstate > 16 || !std::isfinite(combine_scale)) return VM_ERR_UNSUPPORTED;
+  if (dstate > 16 || !std::isfinite(combine_scale) || batch * dim > kMaxPlanes)
+    return VM_ERR_UNSUPPORTED;
   if (!dims_ok({batch, dstate, Lp}, &bc)) return VM_ERR_SHAPE;
   if (out == nullptr) return VM_ERR_NULL;
   const int es = dtype == VM_BF16 ? 2 : 4;
@@ -372,6 +386,69 @@ int vm_pool_scan_repeat(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const vo
   if (st != VM_OK) return st;
   return hip_status(vmk::launch_repeat_gate(y, z, out, batch * dim, height, width, pool_axis,
                                             combine_scale, bf16, s));
+}
+
+int vm_ss2d_scan_fwd(const vm_scan_dir *dirs, const void *u, const void *z, float combine_scale,
+                     void *out, int64_t batch, int64_t dim, int64_t height, int64_t width,
+                     int64_t dstate, int dtype, int delta_softplus, void *stream) {
+  if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;
+  if (!flag_ok(delta_softplus)) return VM_ERR_FLAG;
+  int64_t tok = 0, bc = 0;
+  if (!dims_ok({batch, dim, height, width}, &tok) || dstate <= 0) return VM_ERR_SHAPE;
+  const int64_t L = height * width;
+  if (dstate > 16 || !std::isfinite(combine_scale) || batch * dim > kMaxPlanes)
+    return VM_ERR_UNSUPPORTED;
+  if (!dims_ok({batch, dstate, L}, &bc)) return VM_ERR_SHAPE;
+  // merge / transpose grids: 32 x 32 tiles of one map on grid y
+  if (((height + 31) / 32) * ((width + 31) / 32) > 65535) return VM_ERR_UNSUPPORTED;
+  if (dirs == nullptr || u == nullptr || out == nullptr) return VM_ERR_NULL;
+  const int es = dtype == VM_BF16 ? 2 : 4;
+  const Span so = span(out, tok * es);
+  vm_scan_dir d[4];
+  int st = VM_OK;
+  for (int k = 0; k < 4 && st == VM_OK; ++k) {
+    d[k] = dirs[k];
+    d[k].u = u;                     // the one map every traversal reads
+    st = check_dir(&d[k], tok, tok, batch, L, dim, dstate, es, so);
+  }
+  if (st != VM_OK) return st;
+  if (overlaps(span(z, tok * es), so)) return VM_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == VM_BF16;
+  Scratch ws(s);
+  // The scans run in fp32: bf16 inputs are widened first.  Rows (traversals
+  // 0, 1) scan u as it is; columns (2, 3) scan its transpose.
+  const float *u32 = as_f32(u, tok, bf16, ws, s, &st);
+  float *ut = ws.get(tok, &st);
+  float *yc = ws.get(tok, &st);
+  float *yr = bf16 ? ws.get(tok, &st) : static_cast<float *>(out);
+  if (st != VM_OK) return st;
+  st = hip_status(vmk::launch_transpose(u32, ut, batch * dim, height, width, false, s));
+  for (int pass = 0; pass < 2 && st == VM_OK; ++pass) {
+    vmk::ScanArgs a = {};
+    for (int k = 0; k < 2; ++k) {
+      const vm_scan_dir *p = &d[2 * pass + k];
+      vmk::DirPtrs dp = resolve_dir(p, batch, dstate, L, bf16, ws, s, &st);
+      dp.u = pass == 0 ? u32 : ut;
+      dp.delta = as_f32(p->delta, tok, bf16, ws, s, &st);
+      a.dir[k] = dp;
+    }
+    if (st != VM_OK) return st;
+    a.z = nullptr;
+    a.out = pass == 0 ? yr : yc;
+    a.batch = batch;
+    a.dim = dim;
+    a.L = L;
+    a.dstate = static_cast<int>(dstate);
+    a.softplus = delta_softplus;
+    a.reverse = 0;
+    a.scale = 1.0f;
+    st = launch_bidir(a, /*bf16=*/false, ws, s);
+  }
+  if (st != VM_OK) return st;
+  return hip_status(vmk::launch_ss2d_merge(yr, yc, z, out, batch * dim, height, width,
+                                           combine_scale, bf16, s));
 }
 
 }  // extern "C"

@@ -4,7 +4,10 @@
 //    adding directions"),
 //  * mean pooling over one grid axis and the repeat + SiLU gate back to the
 //    full grid (FastVim summary, "Methodology"),
-//  * bf16 -> fp32 widening of small side tensors.
+//  * the transposes around the column traversals of the four-direction 2-D
+//    scan and its summed merge ("Norm or Direction?" page, section 3,
+//    "2D Selective Scan (SS2D)"),
+//  * bf16 -> fp32 widening of side tensors.
 // All of these are HBM-bound streaming kernels: every element is read once
 // and written once with coalesced accesses.
 #include "vm_internal.h"
@@ -266,6 +269,64 @@ repeat_gate_kernel(const float *__restrict__ y, const T *__restrict__ z, T *__re
   }
 }
 
+// ---- four-direction 2-D scan: the column traversals run on the transposed
+// map, and their outputs meet the row traversals' outputs transposed back.
+// Both passes move 32 x 32 tiles through LDS so that reads and writes are
+// coalesced on either side.
+constexpr int kTile = 32;
+
+// out[p][j][i] = in[p][i][j] for a [P][H][W] stack of maps.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+transpose_kernel(const T *__restrict__ in, T *__restrict__ out, int H, int W, int tiles_w) {
+  __shared__ T tile[kTile][kTile + 1];
+  const int64_t pl = blockIdx.x;
+  const int ti = blockIdx.y / tiles_w, tj = blockIdx.y - (blockIdx.y / tiles_w) * tiles_w;
+  const int i0 = ti * kTile, j0 = tj * kTile;
+  const int tx = threadIdx.x % kTile, ty = threadIdx.x / kTile;   // 32 x 8 threads
+  const T *src = in + pl * H * W;
+  T *dst = out + pl * H * W;
+  for (int r = ty; r < kTile; r += kThreads / kTile) {
+    const int i = i0 + r, j = j0 + tx;
+    if (i < H && j < W) tile[r][tx] = src[static_cast<int64_t>(i) * W + j];
+  }
+  __syncthreads();
+  for (int r = ty; r < kTile; r += kThreads / kTile) {
+    const int j = j0 + r, i = i0 + tx;
+    if (i < H && j < W) dst[static_cast<int64_t>(j) * H + i] = tile[tx][r];
+  }
+}
+
+// out[p][i][j] = scale * (yr[p][i][j] + yc[p][j][i]) * SiLU(z[p][i][j]):
+// yr holds the row traversals' sum ([P][H][W], fp32, may be out itself),
+// yc the column traversals' ([P][W][H], fp32).  z may be NULL.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+ss2d_merge_kernel(const float *yr, const float *__restrict__ yc, const T *__restrict__ z, T *out,
+                  int H, int W, int tiles_w, float scale) {
+  __shared__ float tile[kTile][kTile + 1];
+  const int64_t pl = blockIdx.x;
+  const int ti = blockIdx.y / tiles_w, tj = blockIdx.y - (blockIdx.y / tiles_w) * tiles_w;
+  const int i0 = ti * kTile, j0 = tj * kTile;
+  const int tx = threadIdx.x % kTile, ty = threadIdx.x / kTile;
+  const float *c = yc + pl * H * W;
+  for (int r = ty; r < kTile; r += kThreads / kTile) {   // yc rows j, contiguous in i
+    const int j = j0 + r, i = i0 + tx;
+    if (i < H && j < W) tile[r][tx] = c[static_cast<int64_t>(j) * H + i];
+  }
+  __syncthreads();
+  const int64_t base = pl * H * W;
+  for (int r = ty; r < kTile; r += kThreads / kTile) {   // out rows i, contiguous in j
+    const int i = i0 + r, j = j0 + tx;
+    if (i < H && j < W) {
+      const int64_t e = base + static_cast<int64_t>(i) * W + j;
+      float v = scale * (yr[e] + tile[tx][r]);
+      if (z != nullptr) v *= silu_f(to_f32(z[e]));
+      out[e] = from_f32<T>(v);
+    }
+  }
+}
+
 __global__ void __launch_bounds__(kThreads)
 to_f32_kernel(const bf16_t *__restrict__ src, float *__restrict__ dst, int64_t n) {
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; e < n;
@@ -356,6 +417,39 @@ hipError_t launch_repeat_gate(const float *y, const void *z, void *out, int64_t 
     hipLaunchKernelGGL(repeat_gate_kernel<float>, dim3(static_cast<unsigned>(rows)), dim3(kThreads),
                        0, s, y, static_cast<const float *>(z), static_cast<float *>(out),
                        static_cast<int>(H), static_cast<int>(W), axis, scale, vec);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const void *in, void *out, int64_t planes, int64_t H, int64_t W, bool bf16,
+                            hipStream_t s) {
+  if (planes * H * W == 0) return hipSuccess;
+  const int th = static_cast<int>((H + kTile - 1) / kTile), tw = static_cast<int>((W + kTile - 1) / kTile);
+  const dim3 grid(static_cast<unsigned>(planes), static_cast<unsigned>(th * tw));
+  if (bf16)
+    hipLaunchKernelGGL(transpose_kernel<bf16_t>, grid, dim3(kThreads), 0, s,
+                       static_cast<const bf16_t *>(in), static_cast<bf16_t *>(out),
+                       static_cast<int>(H), static_cast<int>(W), tw);
+  else
+    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(kThreads), 0, s,
+                       static_cast<const float *>(in), static_cast<float *>(out),
+                       static_cast<int>(H), static_cast<int>(W), tw);
+  return hipGetLastError();
+}
+
+hipError_t launch_ss2d_merge(const float *yr, const float *yc, const void *z, void *out,
+                             int64_t planes, int64_t H, int64_t W, float scale, bool bf16,
+                             hipStream_t s) {
+  if (planes * H * W == 0) return hipSuccess;
+  const int th = static_cast<int>((H + kTile - 1) / kTile), tw = static_cast<int>((W + kTile - 1) / kTile);
+  const dim3 grid(static_cast<unsigned>(planes), static_cast<unsigned>(th * tw));
+  if (bf16)
+    hipLaunchKernelGGL(ss2d_merge_kernel<bf16_t>, grid, dim3(kThreads), 0, s, yr, yc,
+                       static_cast<const bf16_t *>(z), static_cast<bf16_t *>(out),
+                       static_cast<int>(H), static_cast<int>(W), tw, scale);
+  else
+    hipLaunchKernelGGL(ss2d_merge_kernel<float>, grid, dim3(kThreads), 0, s, yr, yc,
+                       static_cast<const float *>(z), static_cast<float *>(out),
+                       static_cast<int>(H), static_cast<int>(W), tw, scale);
   return hipGetLastError();
 }
 

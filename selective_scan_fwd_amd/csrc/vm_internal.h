@@ -119,5 +119,13 @@ hipError_t launch_mean_pool(const void *u, float *pooled, int64_t rows, int64_t 
 hipError_t launch_repeat_gate(const float *y, const void *z, void *out, int64_t rows, int64_t H,
                               int64_t W, int axis, float scale, bool bf16, hipStream_t s);
 hipError_t launch_to_f32(const void *src, float *dst, int64_t n, hipStream_t s);
+// [planes][H][W] -> [planes][W][H]
+hipError_t launch_transpose(const void *in, void *out, int64_t planes, int64_t H, int64_t W, bool bf16,
+                            hipStream_t s);
+// out = scale * (yr + transpose(yc)) * SiLU(z); yr [planes][H][W] fp32 (may
+// be out), yc [planes][W][H] fp32, z / out in the token dtype.
+hipError_t launch_ss2d_merge(const float *yr, const float *yc, const void *z, void *out,
+                             int64_t planes, int64_t H, int64_t W, float scale, bool bf16,
+                             hipStream_t s);
 
 }  // namespace vmk

@@ -39,13 +39,13 @@ DSTATE = 16
 class Workload:
     index: int
     name: str
-    kind: str            # "single" | "bidir" | "es2d" | "fastvim"
+    kind: str            # "single" | "bidir" | "es2d" | "fastvim" | "ss2d"
     dtype: str           # "f32" | "bf16"
     batch: int
     dim: int
     seqlen: int = 0      # single / bidir
     sizes: tuple = ()    # es2d: square map sizes
-    height: int = 0      # fastvim grid
+    height: int = 0      # fastvim / ss2d grid
     width: int = 0
     gated: bool = True
     combine_scale: float = 1.0
@@ -65,6 +65,8 @@ WORKLOADS = {
                 seqlen=patch_tokens(1024, 16, 16)),
     3: Workload(3, "es2d_fp32_b64_c192_56_57", "es2d", "f32", 64, 192, sizes=(56, 57), gated=False),
     4: Workload(4, "fastvim_fp32_b128_d384_128x128", "fastvim", "f32", 128, 384, height=128, width=128),
+    # dense four-direction counterpart of the ES2D stage above (same map and channels)
+    5: Workload(5, "ss2d_fp32_b64_c192_56x56", "ss2d", "f32", 64, 192, height=56, width=56),
 }
 
 
@@ -170,3 +172,22 @@ def fastvim_inputs(seed, batch, dim, height, width, pool_axis, dstate=DSTATE, de
         dirs.append(dict(u=u, delta=delta, A=A, B=B, C=C, D=D, delta_bias=bias))
     z = _normal(g, (batch, dim, height, width), device, dtype)
     return dirs[0], dirs[1], z
+
+
+def ss2d_inputs(seed, batch, dim, height, width, dstate=DSTATE, device="cpu", dtype=torch.float32,
+                gated=True, perturb=False, bc_layout="token"):
+    """Feature map u [batch, dim, H, W], four traversals' delta [batch, dim,
+    H*W], B, C [batch, dstate, H*W] (drawn in each traversal's own step
+    order), A, D, delta_bias, then z [batch, dim, H, W].  perturb applies to
+    traversals 1 and 3, so that the four parameter sets differ."""
+    g = generator(seed, device)
+    L = height * width
+    u = _normal(g, (batch, dim, height, width), device, dtype)
+    dirs = []
+    for k in range(4):
+        delta = _normal(g, (batch, dim, L), device, dtype)
+        B, C = _bc_pair(g, batch, dstate, L, device, dtype, bc_layout)
+        A, D, bias = scan_params(g, dim, dstate, device, perturb and k % 2 == 1)
+        dirs.append(dict(delta=delta, A=A, B=B, C=C, D=D, delta_bias=bias))
+    z = _normal(g, (batch, dim, height, width), device, dtype) if gated else None
+    return u, dirs, z

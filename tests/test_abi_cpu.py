@@ -152,3 +152,44 @@ def test_pool_argument_checks(lib):
     assert call(scale=float("nan")) == 6
     assert call(dtype=9) == 3
     assert call(out=f.u + 4) == 5
+
+
+def test_ss2d_argument_checks(lib):
+    dirs = (vm.VmScanDir * 4)(*(_dir(FAKE * (k + 4)) for k in range(4)))
+
+    def call(d=dirs, u=FAKE, z=None, scale=1.0, out=FAKE * 3, H=6, W=5, N=16, dtype=0, sp=1):
+        return lib.vm_ss2d_scan_fwd(d, u, z, scale, out, 2, 4, H, W, N, dtype, sp, None)
+
+    assert call(d=None) == 1
+    assert call(u=None) == 1
+    assert call(out=None) == 1
+    bad = (vm.VmScanDir * 4)(*(_dir(FAKE * (k + 4)) for k in range(4)))
+    bad[3].C = None
+    assert call(d=bad) == 1
+    bad = (vm.VmScanDir * 4)(*(_dir(FAKE * (k + 4)) for k in range(4)))
+    bad[2].u = None                          # ignored (every traversal reads u): the call
+    assert call(d=bad, z=FAKE * 3) == 5      # gets past the pointer checks to the z alias
+    assert call(H=0) == 2
+    assert call(W=-1) == 2
+    assert call(N=0) == 2
+    assert call(N=17) == 6
+    assert call(scale=float("nan")) == 6
+    assert call(H=40000, W=40000) == 6       # more than 65535 tiles of 32 x 32 pixels
+    assert call(dtype=4) == 3
+    assert call(sp=-1) == 4
+    assert call(out=FAKE + 8) == 5           # overlaps u
+    assert call(out=dirs[2].delta) == 5
+    assert call(out=dirs[1].B + 4) == 5
+    assert call(z=FAKE * 3, out=FAKE * 3) == 5
+
+
+def test_plane_count_limit(lib):
+    # map kernels run one workgroup per plane on grid x: at most 2^24 - 1 planes
+    big = 1 << 12
+    assert lib.vm_atrous_gather(FAKE, FAKE * 3, big, big, 2, 2, 0, None) == 6
+    assert lib.vm_atrous_scatter(FAKE, FAKE * 3, big, big, 2, 2, 0, None) == 6
+    f = _dir(FAKE)
+    assert lib.vm_pool_scan_repeat(ctypes.byref(f), None, None, 1.0, FAKE * 3, big, big, 2, 2, 16,
+                                   0, 0, 1, None) == 6
+    dirs = (vm.VmScanDir * 4)(*(_dir(FAKE * (k + 4)) for k in range(4)))
+    assert lib.vm_ss2d_scan_fwd(dirs, FAKE, None, 1.0, FAKE * 3, big, big, 2, 2, 16, 0, 1, None) == 6

@@ -386,3 +386,71 @@ def test_full_fastvim_unpooled():
                                      for k, v in bwd.items()}, list(range(2)), dsel),
                             z=host(zf[bsel][:, dsel]), combine_scale=w.combine_scale)
     assert_close(host(out[bsel][:, dsel]), ref, FP32_TOL, "fastvim unpooled (sampled)")
+
+
+# ---------------------------------------------------------------- SS2D
+def _ss2d_ref(u, dirs, z, scale=1.0, softplus=True, bsel=None, dsel=None):
+    hu, hz = host(u), host(z)
+    hd = [host_dir(p) for p in dirs]
+    if bsel is not None:
+        hu, hz = hu[bsel][:, dsel], (hz[bsel][:, dsel] if hz is not None else None)
+        hd = [sub_dir(p, bsel, dsel) for p in hd]
+    return oracle.ss2d_scan(hu, hd, z=hz, combine_scale=scale, delta_softplus=softplus)
+
+
+# (1, 1) degenerate map; (3, 5) and (33, 17) ragged 32 x 32 transpose tiles;
+# (7, 10) single tile; (12, 32) wide rows; (20, 32) and (24, 25): 640 and 600
+# steps, past the on-chip exchange (line-aligned and ragged global exchange).
+@pytest.mark.parametrize("H,W", [(1, 1), (3, 5), (7, 10), (12, 32), (33, 17), (20, 32), (24, 25)])
+@pytest.mark.parametrize("bc_layout", ["token", "dense"])
+def test_ss2d_fp32(H, W, bc_layout):
+    _case(f"ss2d fp32 {H}x{W} bc {bc_layout}")
+    u, dirs, z = wl.ss2d_inputs(800 + H * W, 2, 70, H, W, device=DEV, perturb=True, bc_layout=bc_layout)
+    out = vm.vm_ss2d_scan_fwd(u, dirs, z=z, combine_scale=0.5)
+    torch.cuda.synchronize()
+    assert_close(host(out), _ss2d_ref(u, dirs, z, 0.5), FP32_TOL, f"ss2d {H}x{W}")
+
+
+def test_ss2d_ungated_no_softplus():
+    _case("ss2d ungated no softplus 9x6")
+    u, dirs, _ = wl.ss2d_inputs(850, 2, 33, 9, 6, dstate=7, device=DEV, gated=False, perturb=True)
+    for p in dirs:
+        p["delta"] = torch.rand_like(p["delta"]) * 0.2
+        p["delta_bias"] = None
+    out = vm.vm_ss2d_scan_fwd(u, dirs, z=None, combine_scale=1.0, delta_softplus=False)
+    torch.cuda.synchronize()
+    ref = _ss2d_ref(u, dirs, None, 1.0, softplus=False)
+    assert_close(host(out), ref, FP32_TOL, "ss2d ungated")
+
+
+def test_ss2d_column_routing_bit_exact():
+    # B = 0 and D_k = 1: every traversal returns u at its own pixel, so the
+    # merged output is exactly 4u (any misrouted pixel breaks equality)
+    _case("ss2d routing bit-exact 13x37")
+    u, dirs, _ = wl.ss2d_inputs(860, 2, 5, 13, 37, device=DEV, gated=False)
+    for p in dirs:
+        p["B"] = torch.zeros_like(p["B"])
+        p["D"] = torch.ones_like(p["D"])
+    out = vm.vm_ss2d_scan_fwd(u, dirs, z=None)
+    torch.cuda.synchronize()
+    assert bits_equal(out, _ss2d_ref(u, dirs, None))
+
+
+@pytest.mark.parametrize("H,W", [(12, 10), (20, 32)])
+def test_ss2d_bf16(H, W):
+    _case(f"ss2d bf16 {H}x{W}")
+    u, dirs, z = wl.ss2d_inputs(870 + H, 2, 70, H, W, device=DEV, dtype=torch.bfloat16)
+    out = vm.vm_ss2d_scan_fwd(u, dirs, z=z)
+    torch.cuda.synchronize()
+    assert_close(host(out), _ss2d_ref(u, dirs, z), BF16_TOL, "ss2d bf16")
+
+
+def test_full_ss2d():
+    w = wl.WORKLOADS[5]
+    _case(f"full {w.name}")
+    u, dirs, z = wl.ss2d_inputs(1005, w.batch, w.dim, w.height, w.width, device=DEV, perturb=True)
+    out = vm.vm_ss2d_scan_fwd(u, dirs, z=z, combine_scale=w.combine_scale)
+    torch.cuda.synchronize()
+    bsel, dsel = [0, 63], [0, 17, 100, 191]
+    ref = _ss2d_ref(u, dirs, z, w.combine_scale, bsel=bsel, dsel=dsel)
+    assert_close(host(out)[bsel][:, dsel], ref, FP32_TOL, "ss2d full (sampled)")
