@@ -45,9 +45,9 @@ def _load():
             build()
             lib = ctypes.CDLL(_LIB_PATH)
             lib.vmo_num_threads.restype = ctypes.c_int
-            lib.vmo_selective_scan.argtypes = [_D] * 8 + [_I64] * 4 + [ctypes.c_int] * 2 + [_D]
+            lib.vmo_selective_scan.argtypes = [_D] * 8 + [_I64] * 4 + [ctypes.c_int] * 3 + [_D]
             lib.vmo_bidir_scan.argtypes = ([_D] * 15 + [ctypes.c_double] + [_I64] * 4
-                                           + [ctypes.c_int] + [_D])
+                                           + [ctypes.c_int] * 2 + [_D])
             lib.vmo_atrous_group_len.argtypes = [_I64, _I64]
             lib.vmo_atrous_group_len.restype = _I64
             lib.vmo_atrous_route.argtypes = [_I64, _I64, ctypes.c_int,
@@ -56,10 +56,10 @@ def _load():
             lib.vmo_atrous_scatter.argtypes = [_D] + [_I64] * 4 + [_D]
             lib.vmo_mean_pool.argtypes = [_D] + [_I64] * 4 + [ctypes.c_int, _D]
             lib.vmo_pool_scan_repeat.argtypes = ([_D] * 15 + [ctypes.c_double] + [_I64] * 5
-                                                 + [ctypes.c_int] * 2 + [_D])
+                                                 + [ctypes.c_int] * 3 + [_D])
             _D4 = _D * 4
             lib.vmo_ss2d_scan.argtypes = ([_D] + [_D4] * 6 + [_D, ctypes.c_double] + [_I64] * 5
-                                          + [ctypes.c_int, _D])
+                                          + [ctypes.c_int] * 2 + [_D])
             for name in ("vmo_selective_scan", "vmo_bidir_scan", "vmo_atrous_route",
                          "vmo_atrous_gather", "vmo_atrous_scatter", "vmo_mean_pool",
                          "vmo_pool_scan_repeat", "vmo_ss2d_scan"):
@@ -89,11 +89,13 @@ def _check(status, what):
 
 
 def selective_scan(u, delta, A, B, C, D, z=None, delta_bias=None,
-                   delta_softplus=True, reverse=False):
+                   delta_softplus=True, reverse=False, zoh=False):
     """One-direction scan (Vim page, implementation row 4; reverse = the
     backward direction of "Two scans meet at the same token", done literally
     as flip, scan, flip).  u, delta, z: [batch, dim, L]; A: [dim, N];
-    B, C: [batch, N, L]; D, delta_bias: [dim].  Returns float64 [batch, dim, L]."""
+    B, C: [batch, N, L]; D, delta_bias: [dim].  zoh=True writes with the
+    zero-order-hold coefficient expm1(dt A) / A instead of dt ("Norm or
+    Direction?" page, section 3, eq. 2).  Returns float64 [batch, dim, L]."""
     u, delta, A, B, C, D, z, delta_bias = map(_f64, (u, delta, A, B, C, D, z, delta_bias))
     batch, dim, L = u.shape
     N = A.shape[1]
@@ -104,7 +106,7 @@ def selective_scan(u, delta, A, B, C, D, z=None, delta_bias=None,
     out = np.empty_like(u)
     _check(_load().vmo_selective_scan(_p(u), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z),
                                       _p(delta_bias), batch, dim, L, N, int(bool(delta_softplus)),
-                                      int(bool(reverse)), _p(out)), "selective_scan")
+                                      int(bool(zoh)), int(bool(reverse)), _p(out)), "selective_scan")
     return out
 
 
@@ -113,7 +115,7 @@ def _dir(p):
     return [_f64(p.get(k)) for k in ("u", "delta", "A", "B", "C", "D", "delta_bias")]
 
 
-def bidir_scan(fwd, bwd, z=None, combine_scale=1.0, delta_softplus=True):
+def bidir_scan(fwd, bwd, z=None, combine_scale=1.0, delta_softplus=True, zoh=False):
     """Bidirectional scan (Vim page, "Two scans meet at the same token" and
     implementation row 5): scale * (y_fwd + flip(scan(flip(bwd)))) * SiLU(z).
     fwd / bwd: dicts with u, delta, A, B, C, D, delta_bias (original order)."""
@@ -128,7 +130,7 @@ def bidir_scan(fwd, bwd, z=None, combine_scale=1.0, delta_softplus=True):
     _check(_load().vmo_bidir_scan(_p(uf), _p(df), _p(Af), _p(Bf), _p(Cf), _p(Df), _p(bf),
                                   _p(ub), _p(db), _p(Ab), _p(Bb), _p(Cb), _p(Db), _p(bb),
                                   _p(z), float(combine_scale), batch, dim, L, N,
-                                  int(bool(delta_softplus)), _p(out)), "bidir_scan")
+                                  int(bool(delta_softplus)), int(bool(zoh)), _p(out)), "bidir_scan")
     return out
 
 
@@ -181,7 +183,8 @@ def mean_pool(u, axis):
     return out
 
 
-def pool_scan_repeat(fwd, bwd, z=None, combine_scale=1.0, pool_axis=0, delta_softplus=True):
+def pool_scan_repeat(fwd, bwd, z=None, combine_scale=1.0, pool_axis=0, delta_softplus=True,
+                     zoh=False):
     """FastVim pooled scan (FastVim summary, "Methodology"): pool u, scan the
     pooled sequence forward (and backward if bwd is given), repeat along the
     pooled axis, gate with SiLU(z) at full resolution.  fwd/bwd u are
@@ -198,12 +201,13 @@ def pool_scan_repeat(fwd, bwd, z=None, combine_scale=1.0, pool_axis=0, delta_sof
     _check(_load().vmo_pool_scan_repeat(_p(uf), _p(df), _p(Af), _p(Bf), _p(Cf), _p(Df), _p(bf),
                                         _p(ub), _p(db), _p(Ab), _p(Bb), _p(Cb), _p(Db), _p(bb),
                                         _p(z), float(combine_scale), batch, dim, H, W, N,
-                                        int(pool_axis), int(bool(delta_softplus)), _p(out)),
+                                        int(pool_axis), int(bool(delta_softplus)), int(bool(zoh)),
+                                        _p(out)),
            "pool_scan_repeat")
     return out
 
 
-def ss2d_scan(u, dirs, z=None, combine_scale=1.0, delta_softplus=True):
+def ss2d_scan(u, dirs, z=None, combine_scale=1.0, delta_softplus=True, zoh=False):
     """Four-direction 2-D scan with summed merge ("Norm or Direction?" page,
     section 3, "2D Selective Scan (SS2D)"; EfficientVMamba page, "Merge
     restores coordinates instead of adding directions").  u, z: [batch, dim,
@@ -223,5 +227,5 @@ def ss2d_scan(u, dirs, z=None, combine_scale=1.0, delta_softplus=True):
     out = np.empty_like(u)
     _check(_load().vmo_ss2d_scan(_p(u), arr(1), arr(2), arr(3), arr(4), arr(5), arr(6), _p(z),
                                  float(combine_scale), batch, dim, H, W, N,
-                                 int(bool(delta_softplus)), _p(out)), "ss2d_scan")
+                                 int(bool(delta_softplus)), int(bool(zoh)), _p(out)), "ss2d_scan")
     return out

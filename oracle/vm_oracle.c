@@ -19,6 +19,9 @@
  *         "What the selective state carries", implementation rows 1-3.
  *  [FVim] "Fast Vision Mamba: Pooling Spatial Dimensions for Accelerated
  *         Processing" (gptget.net summary): "Methodology" and "Key Findings".
+ *  [NoD]  "Norm or Direction? Decoding Vision Mambas for High-Resolution
+ *         Vision": section 3 "Background" (eq. 1-2, and "2D Selective Scan
+ *         (SS2D)").
  *
  * Readings where the pages leave a step open are listed at each function.
  * Every function returns 0 on success and a negative value on bad arguments.
@@ -55,22 +58,37 @@ static double softplus(double x) {
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
 /*
+ * Input coefficient of the state write for step size dt and decay a.
+ * Released recurrence ([Vim] "A state retains, writes, and reads" and row 4):
+ * dt, i.e. the write is dt * B * u.  Exact zero-order hold ([NoD] eq. 2 for a
+ * diagonal A; the same passage of [Vim] states the scalar form): with A, B and
+ * u held constant over the step, the write is (exp(dt a) - 1) / a * B * u,
+ * whose limit at a = 0 is dt * B * u.  expm1 keeps the digits that
+ * exp(dt a) - 1 cancels when dt a is small.
+ */
+static double write_coef(double dt, double a, int zoh) {
+  if (!zoh) return dt;
+  return a != 0.0 ? expm1(dt * a) / a : dt;
+}
+
+/*
  * One channel of one sequence, visited in increasing t from a zero state
  * ([Vim] "A state retains, writes, and reads": each directional scan starts
  * from zero; row 4 equations):
  *
  *   x_t   = delta_t + bias
  *   dt_t  = softplus(x_t)  if delta_softplus, else x_t
- *   h_t,n = exp(dt_t * A_n) * h_{t-1,n} + dt_t * B_n,t * u_t
+ *   h_t,n = exp(dt_t * A_n) * h_{t-1,n} + k(dt_t, A_n) * B_n,t * u_t
  *   y_t   = sum_n C_n,t * h_t,n + D * u_t
  *
+ * with k = write_coef (dt_t, or the zero-order-hold coefficient when zoh).
  * u, delta, y: [L] with element stride 1.  A: [N].  B, C: [N][L] (the batch's
  * slice, shared by every channel).  h: scratch of N doubles.
  */
 static void scan_channel(const double *u, const double *delta, const double *A,
                          const double *B, const double *C, double D,
-                         double bias, int delta_softplus, int64_t L, int64_t N,
-                         double *h, double *y) {
+                         double bias, int delta_softplus, int zoh, int64_t L,
+                         int64_t N, double *h, double *y) {
   for (int64_t n = 0; n < N; ++n) h[n] = 0.0;
   for (int64_t t = 0; t < L; ++t) {
     double x = delta[t] + bias;
@@ -78,7 +96,7 @@ static void scan_channel(const double *u, const double *delta, const double *A,
     double acc = 0.0;
     for (int64_t n = 0; n < N; ++n) {
       double retain = exp(dt * A[n]);
-      double write = dt * B[n * L + t] * u[t];
+      double write = write_coef(dt, A[n], zoh) * B[n * L + t] * u[t];
       h[n] = retain * h[n] + write;
       acc += C[n * L + t] * h[n];
     }
@@ -98,6 +116,7 @@ static void flip_rows(const double *src, double *dst, int64_t rows, int64_t L) {
  *   B, C: [batch][N][L]                   D, delta_bias: [dim]
  * z and delta_bias may be NULL (no gate / zero bias).  With z the output is
  * y * SiLU(z) ([Vim] row 4 returns the gated output when z is given).
+ * zoh != 0 selects the zero-order-hold input coefficient (write_coef).
  *
  * reverse != 0 is the backward direction of [Vim] "Two scans meet at the same
  * token" and row 5: the whole sequence (every token tensor, including z) is
@@ -109,7 +128,7 @@ int vmo_selective_scan(const double *u, const double *delta, const double *A,
                        const double *B, const double *C, const double *D,
                        const double *z, const double *delta_bias,
                        int64_t batch, int64_t dim, int64_t L, int64_t N,
-                       int delta_softplus, int reverse, double *out) {
+                       int delta_softplus, int zoh, int reverse, double *out) {
   if (!u || !delta || !A || !B || !C || !D || !out) return VMO_EBADARG;
   if (batch <= 0 || dim <= 0 || L <= 0 || N <= 0) return VMO_EBADARG;
   int status = 0;
@@ -140,8 +159,8 @@ int vmo_selective_scan(const double *u, const double *delta, const double *A,
       const double *Bb = B + b * N * L, *Cb = C + b * N * L;
       double bias = delta_bias ? delta_bias[d] : 0.0;
       if (!reverse) {
-        scan_channel(ur, dr, A + d * N, Bb, Cb, D[d], bias, delta_softplus, L,
-                     N, h, ybuf);
+        scan_channel(ur, dr, A + d * N, Bb, Cb, D[d], bias, delta_softplus, zoh,
+                     L, N, h, ybuf);
         for (int64_t t = 0; t < L; ++t)
           out[row * L + t] = zr ? ybuf[t] * silu(zr[t]) : ybuf[t];
       } else {
@@ -153,8 +172,8 @@ int vmo_selective_scan(const double *u, const double *delta, const double *A,
         flip_rows(ur, uf, 1, L);
         flip_rows(dr, df, 1, L);
         if (zr) flip_rows(zr, zf, 1, L);
-        scan_channel(uf, df, A + d * N, Bf, Cf, D[d], bias, delta_softplus, L,
-                     N, h, ybuf);
+        scan_channel(uf, df, A + d * N, Bf, Cf, D[d], bias, delta_softplus, zoh,
+                     L, N, h, ybuf);
         if (zr)
           for (int64_t t = 0; t < L; ++t) ybuf[t] *= silu(zf[t]);
         flip_rows(ybuf, out + row * L, 1, L);
@@ -182,17 +201,17 @@ int vmo_bidir_scan(const double *uf, const double *df, const double *Af,
                    const double *Ab, const double *Bb, const double *Cb,
                    const double *Db, const double *biasb, const double *z,
                    double scale, int64_t batch, int64_t dim, int64_t L,
-                   int64_t N, int delta_softplus, double *out) {
+                   int64_t N, int delta_softplus, int zoh, double *out) {
   if (!out || batch <= 0 || dim <= 0 || L <= 0) return VMO_EBADARG;
   size_t total = (size_t)(batch * dim * L);
   double *yf = (double *)malloc(sizeof(double) * total);
   double *yb = (double *)malloc(sizeof(double) * total);
   if (!yf || !yb) { free(yf); free(yb); return VMO_ENOMEM; }
   int s = vmo_selective_scan(uf, df, Af, Bf, Cf, Df, NULL, biasf, batch, dim, L,
-                             N, delta_softplus, 0, yf);
+                             N, delta_softplus, zoh, 0, yf);
   if (s == 0)
     s = vmo_selective_scan(ub, db, Ab, Bb, Cb, Db, NULL, biasb, batch, dim, L,
-                           N, delta_softplus, 1, yb);
+                           N, delta_softplus, zoh, 1, yb);
   if (s == 0)
     for (size_t i = 0; i < total; ++i) {
       double y = (yf[i] + yb[i]) * scale;
@@ -343,7 +362,8 @@ int vmo_pool_scan_repeat(const double *uf, const double *df, const double *Af,
                          const double *Cb, const double *Db,
                          const double *biasb, const double *z, double scale,
                          int64_t batch, int64_t dim, int64_t H, int64_t W,
-                         int64_t N, int axis, int delta_softplus, double *out) {
+                         int64_t N, int axis, int delta_softplus, int zoh,
+                         double *out) {
   if (!uf || !out || batch <= 0 || dim <= 0 || H <= 0 || W <= 0 ||
       (axis != 0 && axis != 1))
     return VMO_EBADARG;
@@ -357,12 +377,12 @@ int vmo_pool_scan_repeat(const double *uf, const double *df, const double *Af,
   if (s == 0) s = vmo_mean_pool(uf, batch, dim, H, W, axis, pf);
   if (s == 0)
     s = vmo_selective_scan(pf, df, Af, Bf, Cf, Df, NULL, biasf, batch, dim, Lp,
-                           N, delta_softplus, 0, yf);
+                           N, delta_softplus, zoh, 0, yf);
   if (s == 0 && ub) {
     s = vmo_mean_pool(ub, batch, dim, H, W, axis, pb);
     if (s == 0)
       s = vmo_selective_scan(pb, db, Ab, Bb, Cb, Db, NULL, biasb, batch, dim,
-                             Lp, N, delta_softplus, 1, yb);
+                             Lp, N, delta_softplus, zoh, 1, yb);
   }
   if (s == 0) {
     for (int64_t r = 0; r < batch * dim; ++r)
@@ -407,7 +427,7 @@ int vmo_ss2d_scan(const double *u, const double *const delta[4],
                   const double *const C[4], const double *const D[4],
                   const double *const bias[4], const double *z, double scale,
                   int64_t batch, int64_t dim, int64_t H, int64_t W, int64_t N,
-                  int delta_softplus, double *out) {
+                  int delta_softplus, int zoh, double *out) {
   if (!u || !out || batch <= 0 || dim <= 0 || H <= 0 || W <= 0 || N <= 0)
     return VMO_EBADARG;
   for (int k = 0; k < 4; ++k)
@@ -424,7 +444,7 @@ int vmo_ss2d_scan(const double *u, const double *const delta[4],
     for (int64_t r = 0; r < rows; ++r)
       for (int64_t t = 0; t < L; ++t) uk[r * L + t] = u[r * L + pos[t]];
     s = vmo_selective_scan(uk, delta[k], A[k], B[k], C[k], D[k], NULL, bias[k],
-                           batch, dim, L, N, delta_softplus, k % 2, yk);
+                           batch, dim, L, N, delta_softplus, zoh, k % 2, yk);
     for (int64_t r = 0; s == 0 && r < rows; ++r)
       for (int64_t t = 0; t < L; ++t) out[r * L + pos[t]] += yk[r * L + t];
   }

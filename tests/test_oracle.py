@@ -451,3 +451,114 @@ def test_ss2d_transpose_symmetry():
     got = oracle.ss2d_scan(u, d, z=z)
     tr = oracle.ss2d_scan(u.transpose(0, 1, 3, 2), [d[2], d[3], d[0], d[1]], z=z.transpose(0, 1, 3, 2))
     _close(got, tr.transpose(0, 1, 3, 2), 1e-12)
+
+
+# ---------------------------------------------------------------- zero-order hold
+# ("Norm or Direction?" page, section 3, eq. 1-2; Vim page, "A state retains,
+# writes, and reads": the exact zero-order-hold input coefficient)
+def _van_loan(a, dt):
+    """Exact discretisation of h' = a h + b u over one step of length dt with
+    b u held constant: exp([[a, 1], [0, 0]] dt) = [[exp(a dt), g], [0, 1]],
+    g = integral_0^dt exp(a s) ds (Van Loan's block-matrix exponential,
+    evaluated by scipy's Pade expm)."""
+    from scipy.linalg import expm
+    m = expm(np.array([[a * dt, dt], [0.0, 0.0]]))
+    return m[0, 0], m[0, 1]
+
+
+def _zoh_ref(p, z=None, delta_softplus=True, reverse=False):
+    """Sequential scan with per-step (Abar, Bbar) from _van_loan, plain loops."""
+    u, dl, A, B, C, D = p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"]
+    bias = p.get("delta_bias")
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    out = np.zeros((batch, dim, L))
+    for b in range(batch):
+        for d in range(dim):
+            h = [0.0] * N
+            order = range(L - 1, -1, -1) if reverse else range(L)
+            for t in order:
+                x = dl[b, d, t] + (bias[d] if bias is not None else 0.0)
+                dt = _softplus_ref(x) if delta_softplus else x
+                acc = 0.0
+                for n in range(N):
+                    abar, g = _van_loan(A[d, n], dt)
+                    h[n] = abar * h[n] + g * B[b, n, t] * u[b, d, t]
+                    acc += C[b, n, t] * h[n]
+                y = acc + D[d] * u[b, d, t]
+                if z is not None:
+                    y *= z[b, d, t] / (1.0 + math.exp(-z[b, d, t]))
+                out[b, d, t] = y
+    return out
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_zoh_van_loan(reverse):
+    rng = _rng(60 + reverse)
+    p = _rand_dir(rng, 2, 3, 9, 4)
+    z = rng.standard_normal(p["u"].shape)
+    got = oracle.selective_scan(**p, z=z, reverse=reverse, zoh=True)
+    _close(got, _zoh_ref(p, z=z, reverse=reverse), 1e-12)
+    # and it is not the released recurrence
+    assert np.max(np.abs(got - oracle.selective_scan(**p, z=z, reverse=reverse))) > 1e-3
+
+
+def test_zoh_small_step_keeps_digits():
+    # dt A = -2e-7: exp(dt A) - 1 would lose about 9 of fp64's 16 digits; the
+    # comparison is relative to this channel's own (tiny) output
+    rng = _rng(62)
+    p = _rand_dir(rng, 1, 1, 6, 3, bias=False)
+    p["delta"] = np.full((1, 1, 6), 1e-7)
+    p["A"] = np.array([[-2.0, -0.5, -3.0]])
+    p["D"] = np.zeros(1)
+    got = oracle.selective_scan(**p, delta_softplus=False, zoh=True)
+    ref = _zoh_ref(p, delta_softplus=False)
+    assert np.max(np.abs(got - ref)) <= 1e-13 * np.max(np.abs(ref))
+
+
+def test_zoh_constant_input_closed_form():
+    # constant dt, B, u, C: the zero-order hold is exact, so h after t+1 steps
+    # is the ODE solution h(T) = (b u / a) (exp(a T) - 1) at T = (t+1) dt
+    L, N, dt = 12, 3, 0.3
+    a = np.array([-0.5, -1.0, -2.5])
+    bv, cv, uv, Dv = np.array([0.7, -1.2, 2.0]), np.array([1.5, 0.4, -0.8]), 1.3, 0.25
+    p = dict(u=np.full((1, 1, L), uv), delta=np.full((1, 1, L), dt), A=a[None, :],
+             B=np.repeat(bv[None, :, None], L, axis=2), C=np.repeat(cv[None, :, None], L, axis=2),
+             D=np.array([Dv]), delta_bias=None)
+    got = oracle.selective_scan(**p, delta_softplus=False, zoh=True)[0, 0]
+    T = dt * np.arange(1, L + 1)
+    h = (bv * uv / a)[None, :] * np.expm1(a[None, :] * T[:, None])
+    _close(got, h @ cv + Dv * uv, 1e-12)
+
+
+def test_zoh_zero_A_is_euler():
+    # the coefficient's limit at A = 0 is dt: both discretisations coincide,
+    # and at A = -1e-200 they agree to rounding
+    rng = _rng(63)
+    p = _rand_dir(rng, 2, 2, 7, 3)
+    p["A"] = np.zeros_like(p["A"])
+    assert np.array_equal(oracle.selective_scan(**p, zoh=True), oracle.selective_scan(**p))
+    p["A"] = np.full_like(p["A"], -1e-200)
+    _close(oracle.selective_scan(**p, zoh=True), oracle.selective_scan(**p), 1e-14)
+
+
+def test_zoh_reaches_bidir_pool_and_ss2d():
+    rng = _rng(64)
+    f, b = _rand_dir(rng, 1, 2, 6, 3), _rand_dir(rng, 1, 2, 6, 3)
+    z = rng.standard_normal(f["u"].shape)
+    got = oracle.bidir_scan(f, b, z=z, combine_scale=0.5, zoh=True)
+    want = 0.5 * (_zoh_ref(f) + _zoh_ref(b, reverse=True)) * z / (1.0 + np.exp(-z))
+    _close(got, want, 1e-12)
+    # pooled: mean over W (axis 0), scan, repeat
+    H, W = 3, 4
+    pf = _rand_dir(rng, 1, 2, H, 3)
+    pf["u"] = rng.standard_normal((1, 2, H, W))
+    got = oracle.pool_scan_repeat(pf, None, zoh=True)
+    want = _zoh_ref(dict(pf, u=pf["u"].mean(axis=3)))
+    _close(got, np.repeat(want[..., None], W, axis=3), 1e-12)
+    # SS2D on a single row: every traversal is a plain row scan
+    u = rng.standard_normal((1, 2, 1, 5))
+    d = _ss2d_dirs(rng, 1, 2, 1, 5, 3)
+    flat = u.reshape(1, 2, 5)
+    want = sum(_zoh_ref(dict(d[k], u=flat), reverse=k % 2 == 1) for k in range(4))
+    _close(oracle.ss2d_scan(u, d, zoh=True).reshape(1, 2, 5), want, 1e-12)

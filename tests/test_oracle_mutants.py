@@ -13,7 +13,8 @@ SRC = os.path.join(ROOT, "oracle", "vm_oracle.c")
 MUTANTS = [
     ("drop_D_skip", "y[t] = acc + D * u[t];", "y[t] = acc;"),
     ("exp_sign", "double retain = exp(dt * A[n]);", "double retain = exp(-dt * A[n]);"),
-    ("B_C_swapped", "double write = dt * B[n * L + t] * u[t];", "double write = dt * C[n * L + t] * u[t];"),
+    ("B_C_swapped", "double write = write_coef(dt, A[n], zoh) * B[n * L + t] * u[t];",
+     "double write = write_coef(dt, A[n], zoh) * C[n * L + t] * u[t];"),
     ("bias_dropped", "double x = delta[t] + bias;", "double x = delta[t];"),
     ("read_before_update", "      h[n] = retain * h[n] + write;\n      acc += C[n * L + t] * h[n];",
      "      acc += C[n * L + t] * h[n];\n      h[n] = retain * h[n] + write;"),
@@ -21,15 +22,24 @@ MUTANTS = [
     ("reverse_keeps_B_order", "flip_rows(Bb, Bf, N, L);", "memcpy(Bf, Bb, sizeof(double) * (size_t)(N * L));"),
     ("gate_is_sigmoid", "return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
     ("bidir_no_scale", "double y = (yf[i] + yb[i]) * scale;", "double y = (yf[i] + yb[i]);"),
-    ("bidir_bwd_not_reversed", "N, delta_softplus, 1, yb);\n  if (s == 0)\n    for",
-     "N, delta_softplus, 0, yb);\n  if (s == 0)\n    for"),
+    ("bidir_bwd_not_reversed", "N, delta_softplus, zoh, 1, yb);\n  if (s == 0)\n    for",
+     "N, delta_softplus, zoh, 0, yb);\n  if (s == 0)\n    for"),
     ("odd_groups_row_major", "if (group % 2 == 0) {", "if (1) {"),
     ("offsets_swapped", "static const int off_row[4] = {0, 1, 0, 1};", "static const int off_row[4] = {0, 0, 1, 1};"),
     ("pad_not_zero", "? plane[rr[t] * W + cc[t]] : 0.0;", "? plane[rr[t] * W + cc[t]] : 1.0;"),
     ("pool_wrong_extent", "pooled[r * H + i] = s / (double)W;", "pooled[r * H + i] = s / (double)H;"),
     ("repeat_wrong_axis", "int64_t p = axis == 0 ? i : j;", "int64_t p = axis == 0 ? (j % Lp) : (i % Lp);"),
     ("ss2d_columns_as_rows", "pos[t] = k < 2 ? t : (t % H) * W + t / H;", "pos[t] = t;"),
-    ("ss2d_no_reverse", "N, delta_softplus, k % 2, yk);", "N, delta_softplus, 0, yk);"),
+    ("ss2d_no_reverse", "N, delta_softplus, zoh, k % 2, yk);", "N, delta_softplus, zoh, 0, yk);"),
+    ("zoh_ignored", "if (!zoh) return dt;", "return dt;"),
+    ("zoh_no_divide", "return a != 0.0 ? expm1(dt * a) / a : dt;", "return a != 0.0 ? expm1(dt * a) : dt;"),
+    ("zoh_exp_minus_one", "return a != 0.0 ? expm1(dt * a) / a : dt;",
+     "return a != 0.0 ? (exp(dt * a) - 1.0) / a : dt;"),
+    ("zoh_dropped_in_bidir", "N, delta_softplus, zoh, 1, yb);\n  if (s == 0)\n    for",
+     "N, delta_softplus, 0, 1, yb);\n  if (s == 0)\n    for"),
+    ("zoh_dropped_in_pool", "Lp,\n                           N, delta_softplus, zoh, 0, yf);",
+     "Lp,\n                           N, delta_softplus, 0, 0, yf);"),
+    ("zoh_dropped_in_ss2d", "N, delta_softplus, zoh, k % 2, yk);", "N, delta_softplus, 0, k % 2, yk);"),
     ("ss2d_overwrite_not_sum", "out[r * L + pos[t]] += yk[r * L + t];", "out[r * L + pos[t]] = yk[r * L + t];"),
 ]
 
