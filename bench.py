@@ -33,6 +33,8 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 # issue rate on gfx950, i.e. 2 slots.
 VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
 SLOTS_PER_STATE_STEP = 6         # dt*A, exp (2 slots), dt*u*B, state fma, readout fma
+# (with --zoh the same count is used: the ALU fraction is then relative to the
+# released recurrence's work, not to the longer zero-order-hold coefficient)
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["selective_scan_fwd_amd/csrc/scan_kernel.hip",
                   "selective_scan_fwd_amd/csrc/layout_kernels.hip",
@@ -57,6 +59,8 @@ def parse():
                          "4 FastVim pooled (axes alternate per step), 5 FastVim unpooled L=16384, "
                          "6 SS2D four-direction scan 56x56")
     ap.add_argument("--sets", type=int, default=0, help="input sets to cycle (0 = auto)")
+    ap.add_argument("--zoh", action="store_true",
+                    help="zero-order-hold input coefficient instead of dt (the released model uses dt)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--seed", type=int, default=1001)
@@ -87,7 +91,7 @@ def algorithmic_bytes_scan(batch, dim, L, N, es, dirs, gated):
     return dirs * per_dir + (tok * es if gated else 0) + tok * es
 
 
-def build_step(cfg, seed, sets, dev):
+def build_step(cfg, seed, sets, dev, zoh=False):
     """Returns (step_fn(i), info dict, cpu_fn(budget_s) -> (seconds, bytes, tokens, threads, desc))."""
     import torch
 
@@ -112,9 +116,9 @@ def build_step(cfg, seed, sets, dev):
         def step(i):
             f, b, z = inputs[i % sets]
             if dirs == 2:
-                vm.vm_bidir_scan_fwd(f, b, z=z, combine_scale=w.combine_scale, out=outs[i % sets])
+                vm.vm_bidir_scan_fwd(f, b, z=z, combine_scale=w.combine_scale, out=outs[i % sets], zoh=zoh)
             else:
-                vm.vm_selective_scan_fwd(**f, z=z, out=outs[i % sets])
+                vm.vm_selective_scan_fwd(**f, z=z, out=outs[i % sets], zoh=zoh)
 
         nbytes = algorithmic_bytes_scan(w.batch, w.dim, w.seqlen, N, es, dirs, True)
         tokens = w.batch * w.dim * w.seqlen
@@ -133,9 +137,9 @@ def build_step(cfg, seed, sets, dev):
             if dirs == 2:
                 hb = {k: (v[:sub].double().cpu().numpy() if k in ("u", "delta", "B", "C") else
                           (v.double().cpu().numpy() if v is not None else None)) for k, v in b.items()}
-                run = lambda: oracle.bidir_scan(hf, hb, z=hz, combine_scale=w.combine_scale)
+                run = lambda: oracle.bidir_scan(hf, hb, z=hz, combine_scale=w.combine_scale, zoh=zoh)
             else:
-                run = lambda: oracle.selective_scan(**hf, z=hz)
+                run = lambda: oracle.selective_scan(**hf, z=hz, zoh=zoh)
             reps, t0 = 0, time.perf_counter()
             while True:
                 run()
@@ -161,7 +165,7 @@ def build_step(cfg, seed, sets, dev):
         def step(i):
             x, p = inputs[i % sets]
             s = vm.vm_atrous_gather(x, out=streams[i % sets])
-            y = vm.vm_selective_scan_fwd(s.view(4 * w.batch, w.dim, Lg), **p, out=ys[i % sets])
+            y = vm.vm_selective_scan_fwd(s.view(4 * w.batch, w.dim, Lg), **p, out=ys[i % sets], zoh=zoh)
             vm.vm_atrous_scatter(y.view(w.batch, 4, w.dim, Lg), H, W, out=outs[i % sets])
 
         plane = w.batch * w.dim * H * W * 4
@@ -184,7 +188,7 @@ def build_step(cfg, seed, sets, dev):
 
             def run():
                 s = oracle.atrous_gather(hx)
-                y = oracle.selective_scan(s.reshape(4 * sub, w.dim, Lg), **hp)
+                y = oracle.selective_scan(s.reshape(4 * sub, w.dim, Lg), **hp, zoh=zoh)
                 oracle.atrous_scatter(y.reshape(sub, 4, w.dim, Lg), H, W)
             reps, t0 = 0, time.perf_counter()
             while True:
@@ -209,7 +213,8 @@ def build_step(cfg, seed, sets, dev):
 
             def step(i):
                 f, b, z = inputs[i % 2]
-                vm.vm_pool_scan_repeat(f, b, z=z, combine_scale=w.combine_scale, pool_axis=i % 2, out=out)
+                vm.vm_pool_scan_repeat(f, b, z=z, combine_scale=w.combine_scale, pool_axis=i % 2, out=out,
+                                       zoh=zoh)
 
             tok_full = w.batch * w.dim * L
             Lp = H
@@ -227,7 +232,7 @@ def build_step(cfg, seed, sets, dev):
             out = torch.empty_like(zf)
 
             def step(i):
-                vm.vm_bidir_scan_fwd(f, b, z=zf, combine_scale=w.combine_scale, out=out)
+                vm.vm_bidir_scan_fwd(f, b, z=zf, combine_scale=w.combine_scale, out=out, zoh=zoh)
 
             nbytes = algorithmic_bytes_scan(w.batch, w.dim, L, N, 4, 2, True)
             slots = 2 * w.batch * w.dim * L * N * SLOTS_PER_STATE_STEP
@@ -244,7 +249,7 @@ def build_step(cfg, seed, sets, dev):
 
         def step(i):
             u, dirs, z = inputs[i % sets]
-            vm.vm_ss2d_scan_fwd(u, dirs, z=z, combine_scale=w.combine_scale, out=outs[i % sets])
+            vm.vm_ss2d_scan_fwd(u, dirs, z=z, combine_scale=w.combine_scale, out=outs[i % sets], zoh=zoh)
 
         tok = w.batch * w.dim * L
         # u, z and out once; delta, B, C and the parameters once per traversal
@@ -262,7 +267,7 @@ def build_step(cfg, seed, sets, dev):
             hz = z[:sub].double().cpu().numpy()
             hd = [{k: (v[:sub].double().cpu().numpy() if k in ("delta", "B", "C") else
                        v.double().cpu().numpy()) for k, v in p.items()} for p in dirs]
-            run = lambda: oracle.ss2d_scan(hu, hd, z=hz, combine_scale=w.combine_scale)
+            run = lambda: oracle.ss2d_scan(hu, hd, z=hz, combine_scale=w.combine_scale, zoh=zoh)
             reps, t0 = 0, time.perf_counter()
             while True:
                 run()
@@ -315,7 +320,9 @@ def main():
     vm.load_library()
     dev = torch.device("cuda:0")
     sets = args.sets or (3 if args.config in (0, 1, 2, 3, 6) else 1)
-    step, info, cpu_fn, nbytes, tokens, slots = build_step(args.config, args.seed, sets, dev)
+    step, info, cpu_fn, nbytes, tokens, slots = build_step(args.config, args.seed, sets, dev, args.zoh)
+    if args.zoh:
+        info = dict(info, discretization="zoh")
     torch.cuda.synchronize()
 
     for i in range(args.warmup):

@@ -51,7 +51,8 @@ enum {
   VM_ERR_NULL = 1,        /* a required pointer is NULL                      */
   VM_ERR_SHAPE = 2,       /* a size is <= 0, or an element count overflows   */
   VM_ERR_DTYPE = 3,       /* unknown dtype                                    */
-  VM_ERR_FLAG = 4,        /* a flag is not 0/1, or pool_axis not 0/1          */
+  VM_ERR_FLAG = 4,        /* a flag or pool_axis is not 0/1, or options has
+                             unknown bits                                     */
   VM_ERR_ALIAS = 5,       /* the output overlaps an input                     */
   VM_ERR_UNSUPPORTED = 6, /* dstate outside [1, 16], a non-finite scale, or
                              sizes past the kernels' 32-bit offsets or grid
@@ -62,6 +63,21 @@ enum {
   VM_ERR_HIP = 7,         /* a HIP launch or runtime call failed              */
   VM_ERR_ALLOC = 8        /* temporary device memory could not be obtained    */
 };
+
+/*
+ * Options of the scan entry points (`options`, bitwise OR; any other bit is
+ * VM_ERR_FLAG):
+ *   VM_DELTA_SOFTPLUS  dt = softplus(delta + bias); without it dt = delta + bias
+ *   VM_ZOH             write with the exact zero-order-hold coefficient
+ *                      (exp(dt A) - 1) / A in place of dt ([NoD] section 3,
+ *                      eq. 2, for diagonal A; [Vim] "A state retains, writes,
+ *                      and reads" gives the scalar form and notes that the
+ *                      released recurrence uses dt).  Its A -> 0 limit is dt.
+ *                      Evaluated in fp32 to within about 5e-7 relative,
+ *                      including small dt A, where exp(dt A) - 1 would cancel.
+ * The released Vim model is options = VM_DELTA_SOFTPLUS.
+ */
+enum { VM_DELTA_SOFTPLUS = 1, VM_ZOH = 2 };
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *vm_status_string(int status);
@@ -105,9 +121,10 @@ typedef struct vm_scan_dir {
 /*
  * Selective scan, one direction ([Vim] "A state retains, writes, and reads"
  * and implementation row 4).  For every (b, d), from a zero state:
- *   dt_t   = softplus(delta_t + bias_d)   (delta_softplus = 1)
- *          = delta_t + bias_d             (delta_softplus = 0)
- *   h_t,n  = exp(dt_t A_d,n) h_t-1,n + dt_t B_b,n,t u_t
+ *   dt_t   = softplus(delta_t + bias_d)   (options & VM_DELTA_SOFTPLUS)
+ *          = delta_t + bias_d             (otherwise)
+ *   h_t,n  = exp(dt_t A_d,n) h_t-1,n + k_t,n B_b,n,t u_t
+ *   k_t,n  = dt_t, or (exp(dt_t A_d,n) - 1) / A_d,n with VM_ZOH
  *   y_t    = sum_n C_b,n,t h_t,n + D_d u_t
  *   out_t  = y_t * SiLU(z_t)   (z != NULL),   y_t otherwise
  * reverse = 1 visits t = seqlen-1 .. 0 instead, which equals reversing every
@@ -117,7 +134,7 @@ typedef struct vm_scan_dir {
  */
 int vm_selective_scan_fwd(const vm_scan_dir *p, const void *z, void *out,
                           int64_t batch, int64_t dim, int64_t seqlen,
-                          int64_t dstate, int dtype, int delta_softplus,
+                          int64_t dstate, int dtype, int options,
                           int reverse, void *stream);
 
 /*
@@ -138,7 +155,7 @@ int vm_selective_scan_fwd(const vm_scan_dir *p, const void *z, void *out,
 int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
                       const void *z, float combine_scale, void *out,
                       int64_t batch, int64_t dim, int64_t seqlen,
-                      int64_t dstate, int dtype, int delta_softplus,
+                      int64_t dstate, int dtype, int options,
                       void *stream);
 
 /*
@@ -190,7 +207,7 @@ int vm_pool_scan_repeat(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
                         const void *z, float combine_scale, void *out,
                         int64_t batch, int64_t dim, int64_t height,
                         int64_t width, int64_t dstate, int pool_axis,
-                        int dtype, int delta_softplus, void *stream);
+                        int dtype, int options, void *stream);
 
 /*
  * Four-direction 2-D selective scan with summed merge ([NoD] section 3,
@@ -218,7 +235,7 @@ int vm_pool_scan_repeat(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
 int vm_ss2d_scan_fwd(const vm_scan_dir *dirs, const void *u, const void *z,
                      float combine_scale, void *out, int64_t batch,
                      int64_t dim, int64_t height, int64_t width,
-                     int64_t dstate, int dtype, int delta_softplus,
+                     int64_t dstate, int dtype, int options,
                      void *stream);
 
 #ifdef __cplusplus

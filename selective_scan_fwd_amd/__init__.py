@@ -24,6 +24,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libvmscan.so")
 
 VM_F32, VM_BF16 = 0, 1
+VM_DELTA_SOFTPLUS, VM_ZOH = 1, 2
 VM_OK = 0
 STATUS_NAMES = {0: "VM_OK", 1: "VM_ERR_NULL", 2: "VM_ERR_SHAPE", 3: "VM_ERR_DTYPE", 4: "VM_ERR_FLAG",
                 5: "VM_ERR_ALIAS", 6: "VM_ERR_UNSUPPORTED", 7: "VM_ERR_HIP", 8: "VM_ERR_ALLOC"}
@@ -141,6 +142,10 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _options(delta_softplus, zoh):
+    return (VM_DELTA_SOFTPLUS if delta_softplus else 0) | (VM_ZOH if zoh else 0)
+
+
 def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
@@ -166,12 +171,14 @@ def _direction(p, batch, dim, u_shape, tok_len, dstate, dt, device, name):
 
 # ---------------------------------------------------------------- entry points
 def vm_selective_scan_fwd(u, delta, A, B, C, D, z=None, delta_bias=None, delta_softplus=True,
-                          reverse=False, out=None):
+                          reverse=False, out=None, zoh=False):
     """One-direction selective scan; returns out shaped like u.
     u, delta, z: [batch, dim, L]; A: [dim, N] fp32; B, C: [batch, N, L]
     (dense, or transposed views of token-major [batch, L, N] memory, which
     the kernels read directly); D, delta_bias: [dim] fp32.
-    reverse=True visits t = L-1 .. 0."""
+    reverse=True visits t = L-1 .. 0.  zoh=True writes with the zero-order-hold
+    coefficient (exp(dt A) - 1) / A instead of dt (every scan entry point
+    takes delta_softplus and zoh)."""
     dt = u.dtype
     batch, dim, L = u.shape
     N = A.shape[-1]
@@ -182,13 +189,13 @@ def vm_selective_scan_fwd(u, delta, A, B, C, D, z=None, delta_bias=None, delta_s
     out = torch.empty_like(u) if out is None else _dev(out, "out", dt, u.shape, u.device)
     with torch.cuda.device(u.device):
         st = load_library().vm_selective_scan_fwd(ctypes.byref(d), _ptr(z), _ptr(out), batch, dim, L, N,
-                                                  _dtype_code(u), int(bool(delta_softplus)),
+                                                  _dtype_code(u), _options(delta_softplus, zoh),
                                                   int(bool(reverse)), _stream(u.device))
     _check(st, "vm_selective_scan_fwd")
     return out
 
 
-def vm_bidir_scan_fwd(fwd, bwd, z=None, combine_scale=1.0, delta_softplus=True, out=None):
+def vm_bidir_scan_fwd(fwd, bwd, z=None, combine_scale=1.0, delta_softplus=True, out=None, zoh=False):
     """Bidirectional scan: combine_scale * (y_fwd + y_bwd) * SiLU(z).
     fwd / bwd: dicts with u, delta, A, B, C, D, delta_bias (original token order)."""
     u = fwd["u"]
@@ -203,7 +210,7 @@ def vm_bidir_scan_fwd(fwd, bwd, z=None, combine_scale=1.0, delta_softplus=True, 
     with torch.cuda.device(u.device):
         st = load_library().vm_bidir_scan_fwd(ctypes.byref(df), ctypes.byref(db), _ptr(z),
                                               float(combine_scale), _ptr(out), batch, dim, L, N,
-                                              _dtype_code(u), int(bool(delta_softplus)),
+                                              _dtype_code(u), _options(delta_softplus, zoh),
                                               _stream(u.device))
     _check(st, "vm_bidir_scan_fwd")
     return out
@@ -247,7 +254,7 @@ def vm_atrous_scatter(streams, height, width, out=None):
 
 
 def vm_pool_scan_repeat(fwd, bwd=None, z=None, combine_scale=1.0, pool_axis=0, delta_softplus=True,
-                        out=None):
+                        out=None, zoh=False):
     """FastVim pooled scan.  Per direction: u [batch, dim, H, W], delta
     [batch, dim, Lp], B/C [batch, N, Lp] (Lp = H for pool_axis 0, W for 1).
     Returns [batch, dim, H, W]."""
@@ -267,13 +274,13 @@ def vm_pool_scan_repeat(fwd, bwd=None, z=None, combine_scale=1.0, pool_axis=0, d
     with torch.cuda.device(u.device):
         st = load_library().vm_pool_scan_repeat(ctypes.byref(df), pb, _ptr(z), float(combine_scale),
                                                 _ptr(out), batch, dim, H, W, N, int(pool_axis),
-                                                _dtype_code(u), int(bool(delta_softplus)),
+                                                _dtype_code(u), _options(delta_softplus, zoh),
                                                 _stream(u.device))
     _check(st, "vm_pool_scan_repeat")
     return out
 
 
-def vm_ss2d_scan_fwd(u, dirs, z=None, combine_scale=1.0, delta_softplus=True, out=None):
+def vm_ss2d_scan_fwd(u, dirs, z=None, combine_scale=1.0, delta_softplus=True, out=None, zoh=False):
     """Four-direction 2-D scan with summed merge.  u, z: [batch, dim, H, W].
     dirs: four dicts with delta, A, B, C, D, delta_bias (a "u" key is
     ignored); traversals 0 / 1 are row-major forward / reversed, 2 / 3
@@ -299,7 +306,7 @@ def vm_ss2d_scan_fwd(u, dirs, z=None, combine_scale=1.0, delta_softplus=True, ou
     with torch.cuda.device(u.device):
         st = load_library().vm_ss2d_scan_fwd(arr, _ptr(u), _ptr(z), float(combine_scale), _ptr(out),
                                              batch, dim, H, W, N, _dtype_code(u),
-                                             int(bool(delta_softplus)), _stream(u.device))
+                                             _options(delta_softplus, zoh), _stream(u.device))
     _check(st, "vm_ss2d_scan_fwd")
     return out
 

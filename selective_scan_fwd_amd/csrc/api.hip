@@ -47,6 +47,7 @@ bool dims_ok(std::initializer_list<int64_t> dims, int64_t *prod) {
 }
 
 bool flag_ok(int f) { return f == 0 || f == 1; }
+bool options_ok(int o) { return (o & ~(VM_DELTA_SOFTPLUS | VM_ZOH)) == 0; }
 
 // Element extent of B or C: dense [batch, dstate, L], or token-major with
 // stride bcs (last element at ((batch*L - 1)*bcs + dstate - 1)).
@@ -202,7 +203,7 @@ const char *vm_status_string(int status) {
     case VM_ERR_NULL: return "VM_ERR_NULL: a required pointer is NULL";
     case VM_ERR_SHAPE: return "VM_ERR_SHAPE: a size is <= 0 or an element count overflows";
     case VM_ERR_DTYPE: return "VM_ERR_DTYPE: unknown dtype";
-    case VM_ERR_FLAG: return "VM_ERR_FLAG: a flag is not 0 or 1";
+    case VM_ERR_FLAG: return "VM_ERR_FLAG: a flag is not 0 or 1, or unknown option bits";
     case VM_ERR_ALIAS: return "VM_ERR_ALIAS: the output overlaps an input";
     case VM_ERR_UNSUPPORTED: return "VM_ERR_UNSUPPORTED: dstate outside [1, 16], non-finite scale, or sizes past the kernels' 32-bit offsets or grid limits";
     case VM_ERR_HIP: return "VM_ERR_HIP: a HIP launch or runtime call failed";
@@ -220,9 +221,9 @@ int64_t vm_atrous_group_len(int64_t height, int64_t width) {
 
 int vm_selective_scan_fwd(const vm_scan_dir *p, const void *z, void *out, int64_t batch,
                           int64_t dim, int64_t seqlen, int64_t dstate, int dtype,
-                          int delta_softplus, int reverse, void *stream) {
+                          int options, int reverse, void *stream) {
   if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;
-  if (!flag_ok(delta_softplus) || !flag_ok(reverse)) return VM_ERR_FLAG;
+  if (!options_ok(options) || !flag_ok(reverse)) return VM_ERR_FLAG;
   int64_t tok = 0, bc = 0;
   if (!dims_ok({batch, dim, seqlen}, &tok) || dstate <= 0) return VM_ERR_SHAPE;
   if (dstate > 16) return VM_ERR_UNSUPPORTED;
@@ -246,7 +247,8 @@ int vm_selective_scan_fwd(const vm_scan_dir *p, const void *z, void *out, int64_
   a.dim = dim;
   a.L = seqlen;
   a.dstate = static_cast<int>(dstate);
-  a.softplus = delta_softplus;
+  a.softplus = (options & VM_DELTA_SOFTPLUS) != 0;
+  a.zoh = (options & VM_ZOH) != 0;
   a.reverse = reverse;
   a.scale = 1.0f;
   const vmk::ScanPlan plan = vmk::plan_scan(batch, dim, seqlen, a.dstate, 1);
@@ -256,10 +258,10 @@ int vm_selective_scan_fwd(const vm_scan_dir *p, const void *z, void *out, int64_
 
 int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void *z,
                       float combine_scale, void *out, int64_t batch, int64_t dim,
-                      int64_t seqlen, int64_t dstate, int dtype, int delta_softplus,
+                      int64_t seqlen, int64_t dstate, int dtype, int options,
                       void *stream) {
   if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;
-  if (!flag_ok(delta_softplus)) return VM_ERR_FLAG;
+  if (!options_ok(options)) return VM_ERR_FLAG;
   int64_t tok = 0, bc = 0;
   if (!dims_ok({batch, dim, seqlen}, &tok) || dstate <= 0) return VM_ERR_SHAPE;
   if (dstate > 16 || !std::isfinite(combine_scale)) return VM_ERR_UNSUPPORTED;
@@ -285,7 +287,8 @@ int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
   a.dim = dim;
   a.L = seqlen;
   a.dstate = static_cast<int>(dstate);
-  a.softplus = delta_softplus;
+  a.softplus = (options & VM_DELTA_SOFTPLUS) != 0;
+  a.zoh = (options & VM_ZOH) != 0;
   a.reverse = 0;
   a.scale = combine_scale;
   return launch_bidir(a, bf16, ws, s);
@@ -326,9 +329,9 @@ int vm_atrous_scatter(const void *streams, void *y, int64_t batch, int64_t chann
 int vm_pool_scan_repeat(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void *z,
                         float combine_scale, void *out, int64_t batch, int64_t dim,
                         int64_t height, int64_t width, int64_t dstate, int pool_axis,
-                        int dtype, int delta_softplus, void *stream) {
+                        int dtype, int options, void *stream) {
   if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;
-  if (!flag_ok(delta_softplus) || !flag_ok(pool_axis)) return VM_ERR_FLAG;
+  if (!options_ok(options) || !flag_ok(pool_axis)) return VM_ERR_FLAG;
   const int64_t Lp = pool_axis == 0 ? height : width;
   int64_t full = 0, pooled = 0, bc = 0;
   if (!dims_ok({batch, dim, height, width}, &full) || !dims_ok({batch, dim, Lp}, &pooled) ||
@@ -372,7 +375,8 @@ int vm_pool_scan_repeat(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const vo
   a.dim = dim;
   a.L = Lp;
   a.dstate = static_cast<int>(dstate);
-  a.softplus = delta_softplus;
+  a.softplus = (options & VM_DELTA_SOFTPLUS) != 0;
+  a.zoh = (options & VM_ZOH) != 0;
   a.reverse = 0;
   a.scale = 1.0f;
   const vmk::ScanPlan plan = vmk::plan_scan(batch, dim, Lp, a.dstate, ndir);
@@ -390,9 +394,9 @@ int vm_pool_scan_repeat(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const vo
 
 int vm_ss2d_scan_fwd(const vm_scan_dir *dirs, const void *u, const void *z, float combine_scale,
                      void *out, int64_t batch, int64_t dim, int64_t height, int64_t width,
-                     int64_t dstate, int dtype, int delta_softplus, void *stream) {
+                     int64_t dstate, int dtype, int options, void *stream) {
   if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;
-  if (!flag_ok(delta_softplus)) return VM_ERR_FLAG;
+  if (!options_ok(options)) return VM_ERR_FLAG;
   int64_t tok = 0, bc = 0;
   if (!dims_ok({batch, dim, height, width}, &tok) || dstate <= 0) return VM_ERR_SHAPE;
   const int64_t L = height * width;
@@ -441,7 +445,8 @@ int vm_ss2d_scan_fwd(const vm_scan_dir *dirs, const void *u, const void *z, floa
     a.dim = dim;
     a.L = L;
     a.dstate = static_cast<int>(dstate);
-    a.softplus = delta_softplus;
+    a.softplus = (options & VM_DELTA_SOFTPLUS) != 0;
+    a.zoh = (options & VM_ZOH) != 0;
     a.reverse = 0;
     a.scale = 1.0f;
     st = launch_bidir(a, /*bf16=*/false, ws, s);

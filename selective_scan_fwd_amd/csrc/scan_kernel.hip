@@ -5,7 +5,9 @@
 // implementation rows 4-5): for each channel d of batch row b, from a zero
 // state, dt = softplus(delta + bias), h_n <- exp(dt A_n) h_n + dt B_n u,
 // y = sum_n C_n h_n + D u; the backward direction visits t = L-1..0 and the
-// two directions are summed, scaled and gated by SiLU(z).
+// two directions are summed, scaled and gated by SiLU(z).  Optionally the
+// write uses the zero-order-hold coefficient (exp(dt A_n) - 1) / A_n in place
+// of dt ("Norm or Direction?" page, section 3, eq. 2).
 //
 // Work decomposition (MI355X-first):
 //  * A workgroup owns R consecutive channels of one batch row and runs one
@@ -76,6 +78,38 @@ __device__ __forceinline__ void state_step(float (&h)[NS], const float (&A2)[NS]
     if constexpr (J == 0) y = row_bcast<NS>(bc) * h[0];
     else fmac_row_bcast<NS + J>(y, bc, h[J]);
     state_step<NS, J + 1>(h, A2, dt, dtu, bc, y);
+  }
+}
+
+// The same step with the zero-order-hold write k_j u B_j, k_j = expm1(x) / A_j
+// for x = dt A_j (here u arrives in place of dt u).  For |x| < 1/8 the
+// coefficient is dt g(x) with g(x) = expm1(x) / x from its Taylor series to
+// x^4 (truncation below 5e-8 relative); above, (2^x2 - 1) / A_j, where the
+// rounding of 2^x2 costs at most about 5e-7 relative because |expm1(x)| is
+// then at least 0.117.  Both are computed and one is selected per state.
+// iA_j = 1 / A_j (0 where A_j = 0, whose |x| = 0 takes the series).
+template <int NS, int J>
+__device__ __forceinline__ void state_step_zoh(float (&h)[NS], const float (&A2)[NS],
+                                               const float (&iA)[NS], float dt, float u,
+                                               float bc, float &y) {
+  if constexpr (J < NS) {
+    constexpr float kLn2 = 0.6931471805599453f;
+    constexpr float c1 = kLn2 / 2, c2 = kLn2 * kLn2 / 6, c3 = kLn2 * kLn2 * kLn2 / 24,
+                    c4 = kLn2 * kLn2 * kLn2 * kLn2 / 120;
+    constexpr float kThr2 = 0.125f * kLog2e;            // |x| < 1/8 in units of x2 = x log2(e)
+    const float x2 = dt * A2[J];
+    const float dA = hw_exp2(x2);
+    float g = __builtin_fmaf(x2, c4, c3);
+    g = __builtin_fmaf(x2, g, c2);
+    g = __builtin_fmaf(x2, g, c1);
+    g = __builtin_fmaf(x2, g, 1.0f);
+    const float k_small = g * dt;
+    const float k_large = __builtin_fmaf(dA, iA[J], -iA[J]);
+    const float k = __builtin_fabsf(x2) < kThr2 ? k_small : k_large;
+    h[J] = __builtin_fmaf(dA, h[J], k * (u * row_bcast<J>(bc)));
+    if constexpr (J == 0) y = row_bcast<NS>(bc) * h[0];
+    else fmac_row_bcast<NS + J>(y, bc, h[J]);
+    state_step_zoh<NS, J + 1>(h, A2, iA, dt, u, bc, y);
   }
 }
 
@@ -159,7 +193,7 @@ template <> __device__ __forceinline__ void bstore<bf16_t>(Rsrc r, uint32_t off,
 
 // Register budget: 4 waves per SIMD with 8-step tiles, 2 with 16-step tiles
 // (whose three tiles in flight and staged copies need about 190 VGPRs).
-template <typename Tin, int SPLIT, int DIRS, int XMODE, int T>
+template <typename Tin, int SPLIT, int DIRS, int XMODE, int T, bool ZOH>
 __global__ void __launch_bounds__(64 * DIRS) __attribute__((amdgpu_waves_per_eu(T == 16 ? 2 : 4)))
 scan_kernel(const ScanArgs p) {
   constexpr int NS = 16 / SPLIT;                 // states per lane
@@ -230,7 +264,7 @@ scan_kernel(const ScanArgs p) {
   const Rsrc rDp = make_rsrc(P.D + d0, static_cast<uint32_t>(rows) * 4u);
   const Rsrc rBias = make_rsrc(P.bias != nullptr ? P.bias + d0 : nullptr,
                                P.bias != nullptr ? static_cast<uint32_t>(rows) * 4u : 0u);
-  float A2[NS], h[NS];
+  float A2[NS], iA[NS], h[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) h[j] = 0.0f;
   // lane j of each 16-lane row holds B[n0 + j] (j < NS) or C[n0 + j - NS]
@@ -299,7 +333,8 @@ scan_kernel(const ScanArgs p) {
     }
   };
 
-  // Stages (dt, dt u) for the scan and u for the skip term.  Steps past L
+  // Stages (dt, dt u) for the scan ((dt, u) with the zero-order hold) and u
+  // for the skip term.  Steps past L
   // and channels past dim stage u = 0, so the state only decays where it is
   // zero (before the first real step) or no longer read; states past dstate
   // stage B = C = 0.
@@ -311,7 +346,8 @@ scan_kernel(const ScanArgs p) {
       const float x = pin(rd[Q][i]) + sbias[i];
       const float uv = pin(ru[Q][i]);
       const float dtv = sp_on ? softplus_f(x) : x;
-      *reinterpret_cast<float2 *>(prep + srow[i] * Lay::PSTR + 2 * sq) = make_float2(dtv, dtv * uv);
+      *reinterpret_cast<float2 *>(prep + srow[i] * Lay::PSTR + 2 * sq) =
+          make_float2(dtv, ZOH ? uv : dtv * uv);
       ust[srow[i] * T + sq] = uv;
     }
 #pragma unroll
@@ -341,7 +377,8 @@ scan_kernel(const ScanArgs p) {
 #pragma unroll
     for (int q = 0; q < T; ++q) {
       float y;
-      state_step<NS, 0>(h, A2, dus[q].x, dus[q].y, bcv[q], y);
+      if constexpr (ZOH) state_step_zoh<NS, 0>(h, A2, iA, dus[q].x, dus[q].y, bcv[q], y);
+      else state_step<NS, 0>(h, A2, dus[q].x, dus[q].y, bcv[q], y);
       part_lane[q] = y;
     }
   };
@@ -450,7 +487,11 @@ scan_kernel(const ScanArgs p) {
     sD[i] = bload<float>(rDp, static_cast<uint32_t>(srow[i]) * 4u);
   }
 #pragma unroll
-  for (int j = 0; j < NS; ++j) A2[j] = pin(A2[j]) * kLog2e;
+  for (int j = 0; j < NS; ++j) {
+    const float a = pin(A2[j]);
+    if constexpr (ZOH) iA[j] = a != 0.0f ? 1.0f / a : 0.0f;
+    A2[j] = a * kLog2e;
+  }
   stage_store(std::integral_constant<int, 0>());
   read_tile();
   if (DIRS == 1) {
@@ -498,9 +539,9 @@ scan_kernel(const ScanArgs p) {
   }
 }
 
-template <typename Tin, int SPLIT, int DIRS, int XMODE, int T>
+template <typename Tin, int SPLIT, int DIRS, int XMODE, int T, bool ZOH>
 hipError_t launch_one(const ScanPlan &plan, const ScanArgs &a, hipStream_t s) {
-  auto kern = scan_kernel<Tin, SPLIT, DIRS, XMODE, T>;
+  auto kern = scan_kernel<Tin, SPLIT, DIRS, XMODE, T, ZOH>;
   static bool attr_set = false;  // benign race: the attribute value is idempotent
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -513,16 +554,16 @@ hipError_t launch_one(const ScanPlan &plan, const ScanArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename Tin, int SPLIT>
+template <typename Tin, int SPLIT, bool ZOH>
 hipError_t dispatch_mode(const ScanPlan &plan, const ScanArgs &a, hipStream_t s) {
-  if (plan.dirs == 1) return launch_one<Tin, SPLIT, 1, kXNone, 16>(plan, a, s);
-  if (plan.xmode == kXLds) return launch_one<Tin, SPLIT, 2, kXLds, 8>(plan, a, s);
-  return launch_one<Tin, SPLIT, 2, kXGlobal, 16>(plan, a, s);
+  if (plan.dirs == 1) return launch_one<Tin, SPLIT, 1, kXNone, 16, ZOH>(plan, a, s);
+  if (plan.xmode == kXLds) return launch_one<Tin, SPLIT, 2, kXLds, 8, ZOH>(plan, a, s);
+  return launch_one<Tin, SPLIT, 2, kXGlobal, 16, ZOH>(plan, a, s);
 }
 
 template <typename Tin>
 hipError_t dispatch_dtype(const ScanPlan &plan, const ScanArgs &a, hipStream_t s) {
-  return dispatch_mode<Tin, 4>(plan, a, s);
+  return a.zoh ? dispatch_mode<Tin, 4, true>(plan, a, s) : dispatch_mode<Tin, 4, false>(plan, a, s);
 }
 
 size_t lds_bytes(int split, int dirs, int T, int xmode, int64_t L) {

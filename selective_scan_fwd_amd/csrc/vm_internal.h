@@ -83,6 +83,7 @@ struct ScanArgs {
   int64_t batch, dim, L;
   int dstate;
   int softplus;
+  int zoh;              // zero-order-hold input coefficient instead of dt
   int reverse;          // one-direction scans only
   float scale;          // bidirectional combine scale
 };

@@ -88,7 +88,8 @@ def test_scan_argument_checks(lib):
     assert _scan(lib, N=17) == 6
     assert _scan(lib, batch=1, L=1 << 26) == 6                  # past the 32-bit in-kernel offsets
     assert _scan(lib, dtype=2) == 3
-    assert _scan(lib, sp=2) == 4
+    assert _scan(lib, sp=4) == 4                                # unknown option bit
+    assert _scan(lib, sp=-1) == 4
     assert _scan(lib, rev=-1) == 4
     # output overlapping an input
     d = _dir(FAKE)
@@ -121,7 +122,7 @@ def test_bidir_argument_checks(lib):
     assert call(scale=float("inf")) == 6
     assert call(N=32) == 6
     assert call(dtype=-1) == 3
-    assert call(sp=3) == 4
+    assert call(sp=8) == 4
     assert call(out=b.C) == 5
 
 

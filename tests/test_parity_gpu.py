@@ -454,3 +454,80 @@ def test_full_ss2d():
     bsel, dsel = [0, 63], [0, 17, 100, 191]
     ref = _ss2d_ref(u, dirs, z, w.combine_scale, bsel=bsel, dsel=dsel)
     assert_close(host(out)[bsel][:, dsel], ref, FP32_TOL, "ss2d full (sampled)")
+
+
+# ---------------------------------------------------------------- zero-order hold
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("L", [77, 600])
+def test_zoh_single_fp32(reverse, L):
+    _case(f"zoh single fp32 L{L} rev{reverse}")
+    p, z = wl.single_inputs(1500 + L, 2, 70, L, device=DEV, perturb=True)
+    out = vm.vm_selective_scan_fwd(**p, z=z, reverse=reverse, zoh=True)
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan(**host_dir(p), z=host(z), reverse=reverse, zoh=True)
+    assert_close(host(out), ref, FP32_TOL, "zoh single")
+
+
+def test_zoh_branch_boundary():
+    # dt A spread over [-0.6, -0.002] without softplus: both sides of the
+    # |dt A| = 1/8 switch between the series and exp(dt A) - 1, plus A = 0
+    # states (dstate 5 of 16 lanes' worth: padded states too)
+    _case("zoh branch boundary")
+    p, z = wl.single_inputs(1510, 2, 40, 64, dstate=5, device=DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(1511)
+    p["delta"] = 0.01 + 0.3 * torch.rand(p["delta"].shape, generator=g, device=DEV)
+    p["delta_bias"] = None
+    p["A"] = -(0.2 + 1.8 * torch.rand(p["A"].shape, generator=g, device=DEV))
+    p["A"][:, 0] = 0.0
+    out = vm.vm_selective_scan_fwd(**p, z=z, delta_softplus=False, zoh=True)
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan(**host_dir(p), z=host(z), delta_softplus=False, zoh=True)
+    assert_close(host(out), ref, FP32_TOL, "zoh boundary")
+
+
+@pytest.mark.parametrize("L", [197, 600])
+def test_zoh_bidir_fp32(L):
+    _case(f"zoh bidir fp32 L{L}")
+    fwd, bwd, z = wl.bidir_inputs(1520 + L, 2, 70, L, device=DEV, perturb=True)
+    out = vm.vm_bidir_scan_fwd(fwd, bwd, z=z, combine_scale=0.5, zoh=True)
+    torch.cuda.synchronize()
+    ref = oracle.bidir_scan(host_dir(fwd), host_dir(bwd), z=host(z), combine_scale=0.5, zoh=True)
+    assert_close(host(out), ref, FP32_TOL, "zoh bidir")
+
+
+def test_zoh_bidir_bf16():
+    _case("zoh bidir bf16 L333")
+    fwd, bwd, z = wl.bidir_inputs(1530, 2, 70, 333, device=DEV, dtype=torch.bfloat16)
+    out = vm.vm_bidir_scan_fwd(fwd, bwd, z=z, zoh=True)
+    torch.cuda.synchronize()
+    ref = oracle.bidir_scan(host_dir(fwd), host_dir(bwd), z=host(z), zoh=True)
+    assert_close(host(out), ref, BF16_TOL, "zoh bidir bf16")
+
+
+def test_zoh_pool_and_ss2d():
+    _case("zoh pool 12x32 axis1 and ss2d 9x14")
+    fwd, bwd, z = wl.fastvim_inputs(1540, 2, 70, 12, 32, 1, device=DEV, perturb=True)
+    out = vm.vm_pool_scan_repeat(fwd, bwd, z=z, pool_axis=1, zoh=True)
+    u, dirs, z2 = wl.ss2d_inputs(1541, 2, 70, 9, 14, device=DEV, perturb=True)
+    out2 = vm.vm_ss2d_scan_fwd(u, dirs, z=z2, zoh=True)
+    torch.cuda.synchronize()
+    ref = oracle.pool_scan_repeat(host_dir(fwd), host_dir(bwd), z=host(z), pool_axis=1, zoh=True)
+    assert_close(host(out), ref, FP32_TOL, "zoh pool")
+    assert_close(host(out2), _ss2d_ref_zoh(u, dirs, z2), FP32_TOL, "zoh ss2d")
+
+
+def _ss2d_ref_zoh(u, dirs, z):
+    return oracle.ss2d_scan(host(u), [host_dir(p) for p in dirs], z=host(z), zoh=True)
+
+
+def test_full_vim_tiny_bidir_zoh():
+    w = wl.WORKLOADS[1]
+    _case(f"full {w.name} zoh")
+    fwd, bwd, z = wl.bidir_inputs(1550, w.batch, w.dim, w.seqlen, device=DEV, perturb=True)
+    out = vm.vm_bidir_scan_fwd(fwd, bwd, z=z, combine_scale=w.combine_scale, zoh=True)
+    torch.cuda.synchronize()
+    bsel, dsel = [0, 77, 127], list(range(w.dim))
+    ref = oracle.bidir_scan(sub_dir(host_dir(fwd), bsel, dsel), sub_dir(host_dir(bwd), bsel, dsel),
+                            z=host(z)[bsel][:, dsel], combine_scale=w.combine_scale, zoh=True)
+    assert_close(host(out[bsel]), ref, FP32_TOL, "vim-t zoh full (sampled batches)")
