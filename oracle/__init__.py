@@ -60,9 +60,10 @@ def _load():
             _D4 = _D * 4
             lib.vmo_ss2d_scan.argtypes = ([_D] + [_D4] * 6 + [_D, ctypes.c_double] + [_I64] * 5
                                           + [ctypes.c_int] * 2 + [_D])
+            lib.vmo_causal_conv1d_silu.argtypes = [_D] * 3 + [_I64] * 3 + [ctypes.c_int, _D]
             for name in ("vmo_selective_scan", "vmo_bidir_scan", "vmo_atrous_route",
                          "vmo_atrous_gather", "vmo_atrous_scatter", "vmo_mean_pool",
-                         "vmo_pool_scan_repeat", "vmo_ss2d_scan"):
+                         "vmo_pool_scan_repeat", "vmo_ss2d_scan", "vmo_causal_conv1d_silu"):
                 getattr(lib, name).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -107,6 +108,20 @@ def selective_scan(u, delta, A, B, C, D, z=None, delta_bias=None,
     _check(_load().vmo_selective_scan(_p(u), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z),
                                       _p(delta_bias), batch, dim, L, N, int(bool(delta_softplus)),
                                       int(bool(zoh)), int(bool(reverse)), _p(out)), "selective_scan")
+    return out
+
+
+def causal_conv1d_silu(x, w, bias=None, reverse=False):
+    """Depthwise causal conv of width 4 plus bias, then SiLU (Vim page,
+    "Inside the released Vim block"); reverse=True is the backward branch's
+    (flip, convolve, flip back).  x: [batch, dim, L]; w: [dim, 4] (w[:, 3] on
+    the current token); bias: [dim].  Returns float64 [batch, dim, L]."""
+    x, w, bias = _f64(x), _f64(w), _f64(bias)
+    batch, dim, L = x.shape
+    assert w.shape == (dim, 4) and (bias is None or bias.shape == (dim,))
+    out = np.empty_like(x)
+    _check(_load().vmo_causal_conv1d_silu(_p(x), _p(w), _p(bias), batch, dim, L,
+                                          int(bool(reverse)), _p(out)), "causal_conv1d_silu")
     return out
 
 

@@ -185,6 +185,48 @@ int vmo_selective_scan(const double *u, const double *delta, const double *A,
 }
 
 /*
+ * Depthwise causal convolution of kernel width 4 with bias, then SiLU, on
+ * each channel's token sequence ([Vim] "Inside the released Vim block": the
+ * content of each branch passes through its own depthwise kernel-four causal
+ * Conv1d, then SiLU; the substitution list of the Vim page's reference code
+ * states it as a grouped conv1d with left padding, then SiLU):
+ *
+ *   v_t = bias + sum_{k=0..3} w[k] * x_{t-3+k}   (x_s = 0 for s < 0)
+ *   out_t = SiLU(v_t)
+ *
+ * so w[3] weights the current token and w[0] the token three steps back.
+ * reverse != 0 is the backward branch, which reverses the sequence before its
+ * convolution: here literally flip, convolve causally, flip back, so the
+ * output is in original token order.
+ *   x, out: [batch][dim][L]     w: [dim][4]     bias: [dim] (NULL = 0)
+ */
+int vmo_causal_conv1d_silu(const double *x, const double *w, const double *bias,
+                           int64_t batch, int64_t dim, int64_t L, int reverse,
+                           double *out) {
+  if (!x || !w || !out || batch <= 0 || dim <= 0 || L <= 0) return VMO_EBADARG;
+  double *src = (double *)malloc(sizeof(double) * (size_t)L);
+  double *dst = (double *)malloc(sizeof(double) * (size_t)L);
+  if (!src || !dst) { free(src); free(dst); return VMO_ENOMEM; }
+  for (int64_t row = 0; row < batch * dim; ++row) {
+    const int64_t d = row % dim;
+    if (reverse) flip_rows(x + row * L, src, 1, L);
+    else memcpy(src, x + row * L, sizeof(double) * (size_t)L);
+    for (int64_t t = 0; t < L; ++t) {
+      double v = bias ? bias[d] : 0.0;
+      for (int k = 0; k < 4; ++k) {
+        const int64_t s = t - 3 + k;
+        if (s >= 0) v += w[d * 4 + k] * src[s];
+      }
+      dst[t] = silu(v);
+    }
+    if (reverse) flip_rows(dst, out + row * L, 1, L);
+    else memcpy(out + row * L, dst, sizeof(double) * (size_t)L);
+  }
+  free(src); free(dst);
+  return 0;
+}
+
+/*
  * Bidirectional combine ([Vim] "Two scans meet at the same token", row 5,
  * and "Inside the released Vim block"):
  *   out = scale * (Y_fwd + flip(Y_bwd_on_flipped_input)) * SiLU(z)

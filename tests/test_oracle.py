@@ -562,3 +562,60 @@ def test_zoh_reaches_bidir_pool_and_ss2d():
     flat = u.reshape(1, 2, 5)
     want = sum(_zoh_ref(dict(d[k], u=flat), reverse=k % 2 == 1) for k in range(4))
     _close(oracle.ss2d_scan(u, d, zoh=True).reshape(1, 2, 5), want, 1e-12)
+
+
+# ---------------------------------------------------------------- causal conv1d + SiLU
+# (Vim page, "Inside the released Vim block": depthwise, kernel four, causal,
+# then SiLU; the backward branch convolves the reversed sequence)
+def _silu(v):
+    return v / (1.0 + np.exp(-v))
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_conv_matches_torch_conv1d(reverse):
+    import torch
+    rng = _rng(70 + reverse)
+    batch, dim, L = 2, 5, 11
+    x, w, b = rng.standard_normal((batch, dim, L)), rng.standard_normal((dim, 4)), rng.standard_normal(dim)
+    xt = torch.from_numpy(x)
+    if reverse:
+        xt = torch.flip(xt, dims=[-1])
+    v = torch.nn.functional.conv1d(xt, torch.from_numpy(w)[:, None, :], torch.from_numpy(b),
+                                   padding=3, groups=dim)[..., :L]
+    want = torch.nn.functional.silu(v)
+    if reverse:
+        want = torch.flip(want, dims=[-1])
+    _close(oracle.causal_conv1d_silu(x, w, b, reverse=reverse), want.numpy(), 1e-13)
+
+
+def test_conv_matches_numpy_convolve():
+    rng = _rng(72)
+    x, w = rng.standard_normal((1, 3, 9)), rng.standard_normal((3, 4))
+    got = oracle.causal_conv1d_silu(x, w)
+    for d in range(3):
+        _close(got[0, d], _silu(np.convolve(x[0, d], w[d, ::-1])[:9]), 1e-13)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_conv_impulse_response(reverse):
+    # a unit impulse at t0 reaches t0 (weight w[3]) and the next three steps
+    # in scan order (w[2], w[1], w[0]); every other token sees only the bias
+    L, t0, bias = 10, 4, 0.3
+    w = np.array([[0.5, -1.25, 2.0, 0.75]])
+    x = np.zeros((1, 1, L))
+    x[0, 0, t0] = 1.0
+    got = oracle.causal_conv1d_silu(x, w, np.array([bias]), reverse=reverse)[0, 0]
+    want = np.full(L, _silu(bias))
+    for j in range(4):
+        t = t0 - j if reverse else t0 + j
+        want[t] = _silu(bias + w[0, 3 - j])
+    _close(got, want, 1e-14)
+
+
+def test_conv_first_tokens_see_zero_padding():
+    # the first three tokens have fewer than four real predecessors: the
+    # missing ones count as zero (left padding), so a constant input ramps up
+    x = np.ones((1, 1, 6))
+    w = np.array([[1.0, 2.0, 4.0, 8.0]])
+    got = oracle.causal_conv1d_silu(x, w)[0, 0]
+    _close(got, _silu(np.array([8.0, 12.0, 14.0, 15.0, 15.0, 15.0])), 1e-14)

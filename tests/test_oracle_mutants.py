@@ -40,6 +40,12 @@ MUTANTS = [
     ("zoh_dropped_in_pool", "Lp,\n                           N, delta_softplus, zoh, 0, yf);",
      "Lp,\n                           N, delta_softplus, 0, 0, yf);"),
     ("zoh_dropped_in_ss2d", "N, delta_softplus, zoh, k % 2, yk);", "N, delta_softplus, 0, k % 2, yk);"),
+    ("conv_taps_reversed", "if (s >= 0) v += w[d * 4 + k] * src[s];", "if (s >= 0) v += w[d * 4 + 3 - k] * src[s];"),
+    ("conv_no_silu", "dst[t] = silu(v);", "dst[t] = v;"),
+    ("conv_shifted_window", "const int64_t s = t - 3 + k;", "const int64_t s = t - 4 + k;"),
+    ("conv_reverse_not_flipped_back", "if (reverse) flip_rows(dst, out + row * L, 1, L);",
+     "if (0) flip_rows(dst, out + row * L, 1, L);"),
+    ("conv_bias_dropped", "double v = bias ? bias[d] : 0.0;", "double v = 0.0;"),
     ("ss2d_overwrite_not_sum", "out[r * L + pos[t]] += yk[r * L + t];", "out[r * L + pos[t]] = yk[r * L + t];"),
 ]
 
