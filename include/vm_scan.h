@@ -105,6 +105,19 @@ int vm_version(void);
  *                     splits the projected tokens and passes transposed
  *                     views); both layouts are read in place.
  *                     Requires bc_stride >= dstate.
+ *   conv_w      [dim, 4]       fp32     NULL: u is the scan input as given.
+ *                                       Non-NULL: u holds the content x before
+ *                                       the block's depthwise causal conv, and
+ *                                       the scan input is computed on the fly
+ *                                       as SiLU(conv(x)) (vm_causal_conv1d_silu,
+ *                                       with this direction's reverse sense);
+ *                                       the D skip uses that input.  Only
+ *                                       vm_selective_scan_fwd and
+ *                                       vm_bidir_scan_fwd (both directions or
+ *                                       neither) accept it; elsewhere
+ *                                       VM_ERR_UNSUPPORTED.
+ *   conv_b      [dim]          fp32     conv bias; NULL = 0 (ignored without
+ *                                       conv_w)
  * For vm_pool_scan_repeat the shapes differ (see there).
  */
 typedef struct vm_scan_dir {
@@ -116,6 +129,8 @@ typedef struct vm_scan_dir {
   const float *D;
   const float *delta_bias;
   int64_t bc_stride;
+  const float *conv_w;
+  const float *conv_b;
 } vm_scan_dir;
 
 /*
@@ -157,6 +172,28 @@ int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
                       int64_t batch, int64_t dim, int64_t seqlen,
                       int64_t dstate, int dtype, int options,
                       void *stream);
+
+/*
+ * Depthwise causal convolution of width 4 with bias, then SiLU: the step
+ * that produces the scan input u from the block's content x ([Vim] "Inside
+ * the released Vim block": each branch's content passes through its own
+ * kernel-four causal Conv1d, then SiLU; the backward branch reverses the
+ * sequence first).  For every row (b, d):
+ *   forward      u_t = SiLU(bias_d + sum_k w_d,k x_{t-3+k})
+ *   reverse = 1  u_t = SiLU(bias_d + sum_k w_d,k x_{t+3-k})
+ * with x = 0 outside [0, seqlen): w_d,3 weights the current token, w_d,0 the
+ * token three steps earlier in the direction's visit order, and the
+ * convolution does not reach across rows.
+ *   x, out [batch, dim, seqlen] (dtype); w [dim, 4] fp32; bias [dim] fp32
+ *   (NULL = 0).  The same result feeds the block's projections of delta, B
+ *   and C; the scan entry points can recompute it from x (conv_w).
+ * Limits: batch * dim <= 2^24 - 1 and seqlen <= 65535 * 1024
+ * (VM_ERR_UNSUPPORTED).
+ */
+int vm_causal_conv1d_silu(const void *x, const float *w, const float *bias,
+                          void *out, int64_t batch, int64_t dim,
+                          int64_t seqlen, int reverse, int dtype,
+                          void *stream);
 
 /*
  * Number of steps of each p = 2 atrous group: ceil(H/2) * ceil(W/2)

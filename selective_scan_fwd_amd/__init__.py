@@ -10,7 +10,7 @@ library is missing or fails to load, every call raises.
 Names and argument order follow the C ABI:
   vm_selective_scan_fwd, vm_bidir_scan_fwd, vm_atrous_gather,
   vm_atrous_scatter, vm_pool_scan_repeat, vm_ss2d_scan_fwd,
-  vm_atrous_group_len.
+  vm_causal_conv1d_silu, vm_atrous_group_len.
 """
 from __future__ import annotations
 
@@ -31,14 +31,15 @@ STATUS_NAMES = {0: "VM_OK", 1: "VM_ERR_NULL", 2: "VM_ERR_SHAPE", 3: "VM_ERR_DTYP
 
 EXPORTED = ("vm_status_string", "vm_version", "vm_selective_scan_fwd", "vm_bidir_scan_fwd",
             "vm_atrous_group_len", "vm_atrous_gather", "vm_atrous_scatter", "vm_pool_scan_repeat",
-            "vm_ss2d_scan_fwd")
+            "vm_ss2d_scan_fwd", "vm_causal_conv1d_silu")
 
 
 class VmScanDir(ctypes.Structure):
     """struct vm_scan_dir (one scan direction's device pointers)."""
     _fields_ = [("u", ctypes.c_void_p), ("delta", ctypes.c_void_p), ("A", ctypes.c_void_p),
                 ("B", ctypes.c_void_p), ("C", ctypes.c_void_p), ("D", ctypes.c_void_p),
-                ("delta_bias", ctypes.c_void_p), ("bc_stride", ctypes.c_int64)]
+                ("delta_bias", ctypes.c_void_p), ("bc_stride", ctypes.c_int64),
+                ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p)]
 
 
 class VmError(RuntimeError):
@@ -74,8 +75,10 @@ def load_library():
             lib.vm_atrous_scatter.argtypes = [P, P, I64, I64, I64, I64, I, P]
             lib.vm_pool_scan_repeat.argtypes = [D, D, P, F, P, I64, I64, I64, I64, I64, I, I, I, P]
             lib.vm_ss2d_scan_fwd.argtypes = [D, P, P, F, P, I64, I64, I64, I64, I64, I, I, P]
+            lib.vm_causal_conv1d_silu.argtypes = [P, P, P, P, I64, I64, I64, I, I, P]
             for name in ("vm_selective_scan_fwd", "vm_bidir_scan_fwd", "vm_atrous_gather",
-                         "vm_atrous_scatter", "vm_pool_scan_repeat", "vm_ss2d_scan_fwd"):
+                         "vm_atrous_scatter", "vm_pool_scan_repeat", "vm_ss2d_scan_fwd",
+                         "vm_causal_conv1d_silu"):
                 getattr(lib, name).restype = I
             _lib = lib
     return _lib
@@ -164,25 +167,37 @@ def _direction(p, batch, dim, u_shape, tok_len, dstate, dt, device, name):
     bias = p.get("delta_bias")
     if bias is not None:
         bias = _dev(bias, f"{name}.delta_bias", torch.float32, (dim,), device)
+    cw, cb = p.get("conv_w"), p.get("conv_b")
+    if cw is not None:
+        cw = _dev(cw, f"{name}.conv_w", torch.float32, (dim, 4), device)
+        if cb is not None:
+            cb = _dev(cb, f"{name}.conv_b", torch.float32, (dim,), device)
+    else:
+        cb = None
+    ptr = lambda t: t.data_ptr() if t is not None else None
     s = VmScanDir(u.data_ptr(), delta.data_ptr(), A.data_ptr(), B.data_ptr(), C.data_ptr(),
-                  D.data_ptr(), bias.data_ptr() if bias is not None else None, sB)
-    return s, (u, delta, A, B, C, D, bias)
+                  D.data_ptr(), ptr(bias), sB, ptr(cw), ptr(cb))
+    return s, (u, delta, A, B, C, D, bias, cw, cb)
 
 
 # ---------------------------------------------------------------- entry points
 def vm_selective_scan_fwd(u, delta, A, B, C, D, z=None, delta_bias=None, delta_softplus=True,
-                          reverse=False, out=None, zoh=False):
+                          reverse=False, out=None, zoh=False, conv_w=None, conv_b=None):
     """One-direction selective scan; returns out shaped like u.
     u, delta, z: [batch, dim, L]; A: [dim, N] fp32; B, C: [batch, N, L]
     (dense, or transposed views of token-major [batch, L, N] memory, which
     the kernels read directly); D, delta_bias: [dim] fp32.
     reverse=True visits t = L-1 .. 0.  zoh=True writes with the zero-order-hold
     coefficient (exp(dt A) - 1) / A instead of dt (every scan entry point
-    takes delta_softplus and zoh)."""
+    takes delta_softplus and zoh).  conv_w [dim, 4] (and conv_b [dim]): u is
+    the content before the block's causal conv and the scan runs on
+    SiLU(conv(u)) computed in the kernel (vm_scan_dir.conv_w; direction dicts
+    of vm_bidir_scan_fwd take the same keys)."""
     dt = u.dtype
     batch, dim, L = u.shape
     N = A.shape[-1]
-    d, keep = _direction(dict(u=u, delta=delta, A=A, B=B, C=C, D=D, delta_bias=delta_bias),
+    d, keep = _direction(dict(u=u, delta=delta, A=A, B=B, C=C, D=D, delta_bias=delta_bias,
+                              conv_w=conv_w, conv_b=conv_b),
                          batch, dim, (batch, dim, L), L, N, dt, u.device, "p")
     if z is not None:
         _dev(z, "z", dt, u.shape, u.device)
@@ -213,6 +228,25 @@ def vm_bidir_scan_fwd(fwd, bwd, z=None, combine_scale=1.0, delta_softplus=True, 
                                               _dtype_code(u), _options(delta_softplus, zoh),
                                               _stream(u.device))
     _check(st, "vm_bidir_scan_fwd")
+    return out
+
+
+def vm_causal_conv1d_silu(x, w, bias=None, reverse=False, out=None):
+    """u = SiLU(depthwise causal conv of width 4 (+ bias)) per row of
+    x [batch, dim, L]; w [dim, 4] fp32 (w[:, 3] on the current token);
+    reverse=True convolves in reversed order (the backward branch)."""
+    _dev(x, "x")
+    dim = x.shape[1]
+    _dev(w, "w", torch.float32, (dim, 4), x.device)
+    if bias is not None:
+        _dev(bias, "bias", torch.float32, (dim,), x.device)
+    out = torch.empty_like(x) if out is None else _dev(out, "out", x.dtype, x.shape, x.device)
+    batch, dim, L = x.shape
+    with torch.cuda.device(x.device):
+        st = load_library().vm_causal_conv1d_silu(_ptr(x), _ptr(w), _ptr(bias), _ptr(out), batch, dim,
+                                                  L, int(bool(reverse)), _dtype_code(x),
+                                                  _stream(x.device))
+    _check(st, "vm_causal_conv1d_silu")
     return out
 
 
@@ -312,5 +346,5 @@ def vm_ss2d_scan_fwd(u, dirs, z=None, combine_scale=1.0, delta_softplus=True, ou
 
 
 __all__ = ["vm_selective_scan_fwd", "vm_bidir_scan_fwd", "vm_atrous_gather", "vm_atrous_scatter",
-           "vm_pool_scan_repeat", "vm_ss2d_scan_fwd", "vm_atrous_group_len", "vm_status_string", "vm_version",
+           "vm_pool_scan_repeat", "vm_ss2d_scan_fwd", "vm_causal_conv1d_silu", "vm_atrous_group_len", "vm_status_string", "vm_version",
            "VmScanDir", "VmError", "load_library", "LIB_PATH", "EXPORTED"]

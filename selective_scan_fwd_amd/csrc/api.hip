@@ -69,7 +69,8 @@ int check_dir(const vm_scan_dir *p, int64_t u_elems, int64_t tok_elems, int64_t 
   const Span ins[] = {span(p->u, u_elems * esize), span(p->delta, tok_elems * esize),
                       span(p->A, dim * dstate * 4), span(p->B, bc * esize),
                       span(p->C, bc * esize), span(p->D, dim * 4),
-                      span(p->delta_bias, dim * 4)};
+                      span(p->delta_bias, dim * 4), span(p->conv_w, dim * 16),
+                      span(p->conv_b, dim * 4)};
   for (const Span &s : ins)
     if (overlaps(s, out)) return VM_ERR_ALIAS;
   return VM_OK;
@@ -157,6 +158,8 @@ vmk::DirPtrs resolve_dir(const vm_scan_dir *p, int64_t batch, int64_t dstate, in
   d.bias = p->delta_bias;
   d.B = p->B;
   d.C = p->C;
+  d.cw = p->conv_w;
+  d.cb = p->conv_b;
   if (p->bc_stride > 0) {
     d.bsb = L * p->bc_stride;
     d.bsn = 1;
@@ -178,7 +181,7 @@ vmk::DirPtrs resolve_dir(const vm_scan_dir *p, int64_t batch, int64_t dstate, in
 // except for the exchange buffer.  fp32 output with line-aligned rows
 // doubles as the exchange buffer; otherwise it comes from the pool.
 int launch_bidir(vmk::ScanArgs &a, bool bf16, Scratch &ws, hipStream_t s) {
-  const vmk::ScanPlan plan = vmk::plan_scan(a.batch, a.dim, a.L, a.dstate, 2);
+  const vmk::ScanPlan plan = vmk::plan_scan(a.batch, a.dim, a.L, a.dstate, 2, a.conv != 0);
   int st = VM_OK;
   if (plan.xmode == vmk::kXGlobal) {
     a.xstride = vmk::xchg_global_stride(a.L);
@@ -251,7 +254,8 @@ int vm_selective_scan_fwd(const vm_scan_dir *p, const void *z, void *out, int64_
   a.zoh = (options & VM_ZOH) != 0;
   a.reverse = reverse;
   a.scale = 1.0f;
-  const vmk::ScanPlan plan = vmk::plan_scan(batch, dim, seqlen, a.dstate, 1);
+  a.conv = p->conv_w != nullptr;
+  const vmk::ScanPlan plan = vmk::plan_scan(batch, dim, seqlen, a.dstate, 1, a.conv != 0);
   if (!vmk::scan_offsets_fit(plan, a, bf16)) return VM_ERR_UNSUPPORTED;
   return hip_status(vmk::launch_scan(plan, a, bf16, s));
 }
@@ -272,6 +276,7 @@ int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
   int st = check_dir(fwd, tok, tok, batch, seqlen, dim, dstate, es, so);
   if (st == VM_OK) st = check_dir(bwd, tok, tok, batch, seqlen, dim, dstate, es, so);
   if (st != VM_OK) return st;
+  if ((fwd->conv_w == nullptr) != (bwd->conv_w == nullptr)) return VM_ERR_UNSUPPORTED;
   if (overlaps(span(z, tok * es), so)) return VM_ERR_ALIAS;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -291,7 +296,27 @@ int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
   a.zoh = (options & VM_ZOH) != 0;
   a.reverse = 0;
   a.scale = combine_scale;
+  a.conv = fwd->conv_w != nullptr;
   return launch_bidir(a, bf16, ws, s);
+}
+
+int vm_causal_conv1d_silu(const void *x, const float *w, const float *bias, void *out,
+                          int64_t batch, int64_t dim, int64_t seqlen, int reverse, int dtype,
+                          void *stream) {
+  if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;
+  if (!flag_ok(reverse)) return VM_ERR_FLAG;
+  int64_t tok = 0;
+  if (!dims_ok({batch, dim, seqlen}, &tok)) return VM_ERR_SHAPE;
+  // one workgroup per (row, 1024-step chunk): rows on grid x, chunks on y
+  if (batch * dim > kMaxPlanes || (seqlen + 1023) / 1024 > 65535) return VM_ERR_UNSUPPORTED;
+  if (x == nullptr || w == nullptr || out == nullptr) return VM_ERR_NULL;
+  const int es = dtype == VM_BF16 ? 2 : 4;
+  const Span so = span(out, tok * es);
+  if (overlaps(span(x, tok * es), so) || overlaps(span(w, dim * 16), so) ||
+      overlaps(span(bias, dim * 4), so))
+    return VM_ERR_ALIAS;
+  return hip_status(vmk::launch_conv1d_silu(x, w, bias, out, batch * dim, seqlen, dim, reverse,
+                                            dtype == VM_BF16, static_cast<hipStream_t>(stream)));
 }
 
 int vm_atrous_gather(const void *x, void *streams, int64_t batch, int64_t channels,
@@ -346,6 +371,7 @@ int vm_pool_scan_repeat(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const vo
   int st = check_dir(fwd, full, pooled, batch, Lp, dim, dstate, es, so);
   if (st == VM_OK && bwd != nullptr) st = check_dir(bwd, full, pooled, batch, Lp, dim, dstate, es, so);
   if (st != VM_OK) return st;
+  if (fwd->conv_w != nullptr || (bwd != nullptr && bwd->conv_w != nullptr)) return VM_ERR_UNSUPPORTED;
   if (overlaps(span(z, full * es), so)) return VM_ERR_ALIAS;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -379,7 +405,7 @@ int vm_pool_scan_repeat(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const vo
   a.zoh = (options & VM_ZOH) != 0;
   a.reverse = 0;
   a.scale = 1.0f;
-  const vmk::ScanPlan plan = vmk::plan_scan(batch, dim, Lp, a.dstate, ndir);
+  const vmk::ScanPlan plan = vmk::plan_scan(batch, dim, Lp, a.dstate, ndir, false);
   if (plan.xmode == vmk::kXGlobal) {
     a.xstride = vmk::xchg_global_stride(Lp);
     a.xglobal = ws.get(batch * dim * a.xstride, &st);
@@ -414,6 +440,7 @@ int vm_ss2d_scan_fwd(const vm_scan_dir *dirs, const void *u, const void *z, floa
     d[k] = dirs[k];
     d[k].u = u;                     // the one map every traversal reads
     st = check_dir(&d[k], tok, tok, batch, L, dim, dstate, es, so);
+    if (st == VM_OK && d[k].conv_w != nullptr) st = VM_ERR_UNSUPPORTED;
   }
   if (st != VM_OK) return st;
   if (overlaps(span(z, tok * es), so)) return VM_ERR_ALIAS;

@@ -7,6 +7,8 @@
 //  * the transposes around the column traversals of the four-direction 2-D
 //    scan and its summed merge ("Norm or Direction?" page, section 3,
 //    "2D Selective Scan (SS2D)"),
+//  * the depthwise width-4 causal convolution + SiLU that produces the scan
+//    input u (Vision Mamba page, "Inside the released Vim block"),
 //  * bf16 -> fp32 widening of side tensors.
 // All of these are HBM-bound streaming kernels: every element is read once
 // and written once with coalesced accesses.
@@ -327,6 +329,45 @@ ss2d_merge_kernel(const float *yr, const float *__restrict__ yc, const T *__rest
   }
 }
 
+// u[t] = SiLU(cb + sum_k w[k] x[t - 3 + k]) on each row (x outside the row
+// is 0); reverse: the same in reversed order, u[t] = SiLU(cb + sum_k w[k]
+// x[t + 3 - k]).  One workgroup per (row, chunk of kConvChunk steps): the
+// chunk's inputs with a 3-step margin on each side go through LDS, so every
+// input is read from HBM once and each output is one LDS window.
+constexpr int kConvChunk = 4 * kThreads;
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+conv1d_silu_kernel(const T *__restrict__ x, const float *__restrict__ w, const float *__restrict__ cb,
+                   T *__restrict__ out, int64_t L, int64_t dim, int reverse) {
+  __shared__ float tile[kConvChunk + 6];
+  const int64_t row = blockIdx.x;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.y) * kConvChunk;
+  const T *xr = x + row * L;
+  for (int i = threadIdx.x; i < kConvChunk + 6; i += kThreads) {
+    const int64_t t = c0 - 3 + i;
+    tile[i] = (t >= 0 && t < L) ? to_f32(xr[t]) : 0.0f;
+  }
+  __syncthreads();
+  const int64_t d = row % dim;
+  const float w0 = w[4 * d], w1 = w[4 * d + 1], w2 = w[4 * d + 2], w3 = w[4 * d + 3];
+  const float b = cb != nullptr ? cb[d] : 0.0f;
+  const int dir = reverse ? -1 : 1;           // direction of "earlier" in visit order
+  T *orow = out + row * L;
+#pragma unroll
+  for (int j = 0; j < kConvChunk / kThreads; ++j) {
+    const int i = threadIdx.x + j * kThreads;
+    if (c0 + i < L) {
+      const float *c = tile + i + 3;          // x[c0 + i]
+      float v = __builtin_fmaf(w3, c[0], b);
+      v = __builtin_fmaf(w2, c[-dir], v);
+      v = __builtin_fmaf(w1, c[-2 * dir], v);
+      v = __builtin_fmaf(w0, c[-3 * dir], v);
+      orow[c0 + i] = from_f32<T>(silu_f(v));
+    }
+  }
+}
+
 __global__ void __launch_bounds__(kThreads)
 to_f32_kernel(const bf16_t *__restrict__ src, float *__restrict__ dst, int64_t n) {
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; e < n;
@@ -450,6 +491,22 @@ hipError_t launch_ss2d_merge(const float *yr, const float *yc, const void *z, vo
     hipLaunchKernelGGL(ss2d_merge_kernel<float>, grid, dim3(kThreads), 0, s, yr, yc,
                        static_cast<const float *>(z), static_cast<float *>(out),
                        static_cast<int>(H), static_cast<int>(W), tw, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv1d_silu(const void *x, const float *w, const float *cb, void *out,
+                              int64_t rows, int64_t L, int64_t dim, int reverse, bool bf16,
+                              hipStream_t s) {
+  if (rows * L == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(rows), static_cast<unsigned>((L + kConvChunk - 1) / kConvChunk));
+  if (bf16)
+    hipLaunchKernelGGL(conv1d_silu_kernel<bf16_t>, grid, dim3(kThreads), 0, s,
+                       static_cast<const bf16_t *>(x), w, cb, static_cast<bf16_t *>(out), L, dim,
+                       reverse);
+  else
+    hipLaunchKernelGGL(conv1d_silu_kernel<float>, grid, dim3(kThreads), 0, s,
+                       static_cast<const float *>(x), w, cb, static_cast<float *>(out), L, dim,
+                       reverse);
   return hipGetLastError();
 }
 

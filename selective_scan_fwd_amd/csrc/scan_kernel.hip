@@ -7,7 +7,10 @@
 // y = sum_n C_n h_n + D u; the backward direction visits t = L-1..0 and the
 // two directions are summed, scaled and gated by SiLU(z).  Optionally the
 // write uses the zero-order-hold coefficient (exp(dt A_n) - 1) / A_n in place
-// of dt ("Norm or Direction?" page, section 3, eq. 2).
+// of dt ("Norm or Direction?" page, section 3, eq. 2), and optionally the
+// scan input is computed in the staging pass as u = SiLU(conv(x)), the
+// depthwise width-4 causal convolution of the released Vim block ("Inside the
+// released Vim block"), causal in each direction's own visit order.
 //
 // Work decomposition (MI355X-first):
 //  * A workgroup owns R consecutive channels of one batch row and runs one
@@ -145,7 +148,7 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int T, int R>
+template <int T, int R, bool CV>
 struct Layout {
   static constexpr int PSTR = 2 * T + 2;                  // (dt, dt u) per row; PSTR/2 odd
   static constexpr int QSTR = T + 1;                      // partials per lane, odd
@@ -153,7 +156,9 @@ struct Layout {
   static constexpr int UST = R * T;                       // u per row, for the D u skip
   static constexpr int BC = 32 * T;                       // B in slots 0..15, C in 16..31
   static constexpr int PART = 64 * QSTR;
-  static constexpr int WAVE = PREP + UST + BC + PART;     // floats per wave
+  static constexpr int XH = T + 4;                        // conv input row: 3 halo, T, 1 spare
+  static constexpr int CX = CV ? R * XH : 0;
+  static constexpr int WAVE = PREP + UST + BC + PART + CX;  // floats per wave
 };
 
 // Row stride of the LDS exchange block for n parked steps: >= n and
@@ -191,18 +196,23 @@ template <> __device__ __forceinline__ void bstore<bf16_t>(Rsrc r, uint32_t off,
                                         static_cast<int>(off), 0, 0);
 }
 
-// Register budget: 4 waves per SIMD with 8-step tiles, 2 with 16-step tiles
-// (whose three tiles in flight and staged copies need about 190 VGPRs).
-template <typename Tin, int SPLIT, int DIRS, int XMODE, int T, bool ZOH>
-__global__ void __launch_bounds__(64 * DIRS) __attribute__((amdgpu_waves_per_eu(T == 16 ? 2 : 4)))
+// Register budget: 4 waves per SIMD with 8-step tiles (3 with the fused
+// conv, whose weights and carried inputs do not fit 128 VGPRs), 2 with
+// 16-step tiles (whose three tiles in flight and staged copies need about
+// 190 VGPRs, 240 with the conv).
+template <typename Tin, int SPLIT, int DIRS, int XMODE, int T, int OPT>
+__global__ void __launch_bounds__(64 * DIRS)
+__attribute__((amdgpu_waves_per_eu(T == 16 ? 2 : ((OPT & kOptConv) != 0 ? 3 : 4))))
 scan_kernel(const ScanArgs p) {
+  constexpr bool ZOH = (OPT & kOptZoh) != 0;
+  constexpr bool CONV = (OPT & kOptConv) != 0;
   constexpr int NS = 16 / SPLIT;                 // states per lane
   constexpr int R = 64 / SPLIT;                  // channels per workgroup
   constexpr int PE = R * T / 64;                 // staged (dt, u) elements per lane per tile
   constexpr int BQ = T / 4;                      // B (and C) loads per lane per tile
   constexpr uint32_t ES = sizeof(Tin);
   constexpr int NB = 3;                          // tiles in flight (prefetch distance)
-  using Lay = Layout<T, R>;
+  using Lay = Layout<T, R, CONV>;
   static_assert(NS >= 4 && NS <= 8 && R % 16 == 0 && T % 4 == 0 && (R * T) % 64 == 0, "shape");
   static_assert(DIRS == 1 ? XMODE == kXNone : XMODE != kXNone, "mode");
 
@@ -213,6 +223,7 @@ scan_kernel(const ScanArgs p) {
   float *const ust = prep + Lay::PREP;           // [R][T]
   float *const bcs = ust + Lay::UST;             // [T][32]
   float *const part = bcs + Lay::BC;             // [64 lanes][QSTR]
+  float *const xs = part + Lay::PART;            // [R][XH] conv input (CONV)
   float *const xlds = smem + DIRS * Lay::WAVE;   // [R][XS]   (kXLds)
 
   const int sp = lane / R;                       // state group
@@ -264,6 +275,10 @@ scan_kernel(const ScanArgs p) {
   const Rsrc rDp = make_rsrc(P.D + d0, static_cast<uint32_t>(rows) * 4u);
   const Rsrc rBias = make_rsrc(P.bias != nullptr ? P.bias + d0 : nullptr,
                                P.bias != nullptr ? static_cast<uint32_t>(rows) * 4u : 0u);
+  const Rsrc rCw = make_rsrc(CONV ? P.cw + static_cast<int64_t>(d0) * 4 : nullptr,
+                             CONV ? static_cast<uint32_t>(rows) * 16u : 0u);
+  const Rsrc rCb = make_rsrc(CONV && P.cb != nullptr ? P.cb + d0 : nullptr,
+                             CONV && P.cb != nullptr ? static_cast<uint32_t>(rows) * 4u : 0u);
   float A2[NS], iA[NS], h[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) h[j] = 0.0f;
@@ -282,12 +297,20 @@ scan_kernel(const ScanArgs p) {
   int srow[PE];
   uint32_t ob[PE], oxl[PE], oxg[PE];
   float sbias[PE], sD[PE];
+  // Conv (CONV): the element's weights and bias, its raw input of the
+  // previous tile, and where that value goes: the halo slot (visit position
+  // T-3+h of the previous tile, stored at h) for the last three positions,
+  // else the row's spare slot.
+  float cw[PE][4], cb[PE], xprev[PE];
+  int hx[PE];
 #pragma unroll
   for (int i = 0; i < PE; ++i) {
     srow[i] = lane / T + i * (64 / T);
     ob[i] = (static_cast<uint32_t>(srow[i]) * static_cast<uint32_t>(L) + tq) * ES;
     oxl[i] = static_cast<uint32_t>(srow[i] * XS + tq);
     oxg[i] = (static_cast<uint32_t>(srow[i]) * xstride + tq) * 4u;
+    xprev[i] = 0.0f;                             // zero padding before the first step
+    hx[i] = srow[i] * Lay::XH + (sq >= T - 3 ? sq - (T - 3) : T + 3);
   }
   // B and C: load i of a lane covers visit position q = lane / 16 + 4 i and
   // state n = lane % 16 (past dstate: out of range, so it stages 0).
@@ -334,17 +357,46 @@ scan_kernel(const ScanArgs p) {
   };
 
   // Stages (dt, dt u) for the scan ((dt, u) with the zero-order hold) and u
-  // for the skip term.  Steps past L
+  // for the skip term, for tile kt.  Steps past L
   // and channels past dim stage u = 0, so the state only decays where it is
   // zero (before the first real step) or no longer read; states past dstate
   // stage B = C = 0.
-  auto stage_store = [&](auto par) __attribute__((always_inline)) {
+  // CONV: the loaded values are the conv input x.  The wave writes the
+  // tile's x (row slots 3..T+2, in visit order) and the previous tile's last
+  // three (slots 0..2), then reads each element's three predecessors back:
+  // u = SiLU(cb + w0 x[-3] + w1 x[-2] + w2 x[-1] + w3 x[0]).  A wave's LDS
+  // accesses execute in program order, so the writes land before the reads.
+  auto stage_store = [&](auto par, int kt) __attribute__((always_inline)) {
     constexpr int Q = decltype(par)::value;
     const bool sp_on = p.softplus != 0;
+    float uin[PE];
+    if constexpr (CONV) {
+      float xc[PE];
+#pragma unroll
+      for (int i = 0; i < PE; ++i) {
+        xc[i] = pin(ru[Q][i]);
+        xs[hx[i]] = xprev[i];
+        xs[srow[i] * Lay::XH + 3 + sq] = xc[i];
+        xprev[i] = xc[i];
+      }
+      const bool in_seq = tq < L - tile_of(kt) * T;
+#pragma unroll
+      for (int i = 0; i < PE; ++i) {
+        const float *const xr = xs + srow[i] * Lay::XH + sq;
+        float v = __builtin_fmaf(cw[i][3], xc[i], cb[i]);
+        v = __builtin_fmaf(cw[i][2], xr[2], v);
+        v = __builtin_fmaf(cw[i][1], xr[1], v);
+        v = __builtin_fmaf(cw[i][0], xr[0], v);
+        uin[i] = in_seq ? silu_f(v) : 0.0f;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PE; ++i) uin[i] = pin(ru[Q][i]);
+    }
 #pragma unroll
     for (int i = 0; i < PE; ++i) {
       const float x = pin(rd[Q][i]) + sbias[i];
-      const float uv = pin(ru[Q][i]);
+      const float uv = uin[i];
       const float dtv = sp_on ? softplus_f(x) : x;
       *reinterpret_cast<float2 *>(prep + srow[i] * Lay::PSTR + 2 * sq) =
           make_float2(dtv, ZOH ? uv : dtv * uv);
@@ -454,7 +506,7 @@ scan_kernel(const ScanArgs p) {
     stage_load(k + NB < nt ? k + NB : nt - 1, slot);
     do_scan();
     comb_read(k, second);
-    stage_store(Qn());
+    stage_store(Qn(), k + 1 < nt ? k + 1 : nt - 1);
     read_tile();
     do_combine(k, slot, second);
   };
@@ -485,6 +537,12 @@ scan_kernel(const ScanArgs p) {
   for (int i = 0; i < PE; ++i) {
     sbias[i] = bload<float>(rBias, static_cast<uint32_t>(srow[i]) * 4u);
     sD[i] = bload<float>(rDp, static_cast<uint32_t>(srow[i]) * 4u);
+    if constexpr (CONV) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        cw[i][k] = bload<float>(rCw, static_cast<uint32_t>(srow[i] * 4 + k) * 4u);
+      cb[i] = bload<float>(rCb, static_cast<uint32_t>(srow[i]) * 4u);
+    }
   }
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
@@ -492,7 +550,7 @@ scan_kernel(const ScanArgs p) {
     if constexpr (ZOH) iA[j] = a != 0.0f ? 1.0f / a : 0.0f;
     A2[j] = a * kLog2e;
   }
-  stage_store(std::integral_constant<int, 0>());
+  stage_store(std::integral_constant<int, 0>(), 0);
   read_tile();
   if (DIRS == 1) {
     comb_load(0, std::integral_constant<int, 0>(), First());
@@ -539,9 +597,9 @@ scan_kernel(const ScanArgs p) {
   }
 }
 
-template <typename Tin, int SPLIT, int DIRS, int XMODE, int T, bool ZOH>
+template <typename Tin, int SPLIT, int DIRS, int XMODE, int T, int OPT>
 hipError_t launch_one(const ScanPlan &plan, const ScanArgs &a, hipStream_t s) {
-  auto kern = scan_kernel<Tin, SPLIT, DIRS, XMODE, T, ZOH>;
+  auto kern = scan_kernel<Tin, SPLIT, DIRS, XMODE, T, OPT>;
   static bool attr_set = false;  // benign race: the attribute value is idempotent
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -554,28 +612,34 @@ hipError_t launch_one(const ScanPlan &plan, const ScanArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename Tin, int SPLIT, bool ZOH>
+template <typename Tin, int SPLIT, int OPT>
 hipError_t dispatch_mode(const ScanPlan &plan, const ScanArgs &a, hipStream_t s) {
-  if (plan.dirs == 1) return launch_one<Tin, SPLIT, 1, kXNone, 16, ZOH>(plan, a, s);
-  if (plan.xmode == kXLds) return launch_one<Tin, SPLIT, 2, kXLds, 8, ZOH>(plan, a, s);
-  return launch_one<Tin, SPLIT, 2, kXGlobal, 16, ZOH>(plan, a, s);
+  if (plan.dirs == 1) return launch_one<Tin, SPLIT, 1, kXNone, 16, OPT>(plan, a, s);
+  if (plan.xmode == kXLds) return launch_one<Tin, SPLIT, 2, kXLds, 8, OPT>(plan, a, s);
+  return launch_one<Tin, SPLIT, 2, kXGlobal, 16, OPT>(plan, a, s);
 }
 
 template <typename Tin>
 hipError_t dispatch_dtype(const ScanPlan &plan, const ScanArgs &a, hipStream_t s) {
-  return a.zoh ? dispatch_mode<Tin, 4, true>(plan, a, s) : dispatch_mode<Tin, 4, false>(plan, a, s);
+  switch ((a.zoh ? kOptZoh : 0) | (a.conv ? kOptConv : 0)) {
+    case 0: return dispatch_mode<Tin, 4, 0>(plan, a, s);
+    case kOptZoh: return dispatch_mode<Tin, 4, kOptZoh>(plan, a, s);
+    case kOptConv: return dispatch_mode<Tin, 4, kOptConv>(plan, a, s);
+    default: return dispatch_mode<Tin, 4, kOptZoh | kOptConv>(plan, a, s);
+  }
 }
 
-size_t lds_bytes(int split, int dirs, int T, int xmode, int64_t L) {
+size_t lds_bytes(int split, int dirs, int T, int xmode, int64_t L, bool conv) {
   const int R = 64 / split;
-  size_t f = static_cast<size_t>(dirs) * (R * (2 * T + 2) + R * T + 32 * T + 64 * (T + 1));
+  size_t f = static_cast<size_t>(dirs) * (R * (2 * T + 2) + R * T + 32 * T + 64 * (T + 1) +
+                                          (conv ? R * (T + 4) : 0));
   if (xmode == kXLds) f += static_cast<size_t>(R) * xchg_stride(L, T);
   return f * sizeof(float);
 }
 
 }  // namespace
 
-ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t L, int dstate, int dirs) {
+ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t L, int dstate, int dirs, bool conv) {
   (void)dstate;
   ScanPlan pl{};
   pl.dirs = dirs;
@@ -594,10 +658,10 @@ ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t L, int dstate, int dirs) 
     pl.xmode = kXNone;
   } else {
     // On-chip exchange while at least four workgroups fit a CU's 160 KB LDS.
-    pl.xmode = lds_bytes(pl.S, 2, 8, kXLds, L) <= 40 * 1024 ? kXLds : kXGlobal;
+    pl.xmode = lds_bytes(pl.S, 2, 8, kXLds, L, conv) <= 40 * 1024 ? kXLds : kXGlobal;
     pl.T = pl.xmode == kXLds ? 8 : 16;
   }
-  pl.lds = lds_bytes(pl.S, dirs, pl.T, pl.xmode, L);
+  pl.lds = lds_bytes(pl.S, dirs, pl.T, pl.xmode, L, conv);
   return pl;
 }
 

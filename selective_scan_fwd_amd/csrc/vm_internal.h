@@ -72,6 +72,8 @@ struct DirPtrs {
   int64_t bsb, bsn, bst;
   const float *D;       // [dim]
   const float *bias;    // [dim] or nullptr
+  const float *cw;      // [dim, 4] causal conv weights (conv scans) or nullptr
+  const float *cb;      // [dim] conv bias or nullptr
 };
 
 struct ScanArgs {
@@ -84,9 +86,13 @@ struct ScanArgs {
   int dstate;
   int softplus;
   int zoh;              // zero-order-hold input coefficient instead of dt
+  int conv;             // u holds the conv input x; the scan uses SiLU(conv(x))
   int reverse;          // one-direction scans only
   float scale;          // bidirectional combine scale
 };
+
+// Kernel variants (template bits of the scan kernel).
+enum ScanOpt { kOptZoh = 1, kOptConv = 2 };
 
 // Where a bidirectional scan parks first-visit sums: in LDS (short
 // sequences) or in fp32 global memory.
@@ -102,7 +108,7 @@ struct ScanPlan {
   int64_t blocks;
 };
 
-ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t L, int dstate, int dirs);
+ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t L, int dstate, int dirs, bool conv);
 // Row stride (floats) of the global exchange buffer: rows padded to whole
 // 128-byte lines so that no two channels' parked partials share a line.
 int64_t xchg_global_stride(int64_t L);
@@ -121,6 +127,9 @@ hipError_t launch_repeat_gate(const float *y, const void *z, void *out, int64_t 
                               int64_t W, int axis, float scale, bool bf16, hipStream_t s);
 hipError_t launch_to_f32(const void *src, float *dst, int64_t n, hipStream_t s);
 // [planes][H][W] -> [planes][W][H]
+hipError_t launch_conv1d_silu(const void *x, const float *w, const float *cb, void *out,
+                              int64_t rows, int64_t L, int64_t dim, int reverse, bool bf16,
+                              hipStream_t s);
 hipError_t launch_transpose(const void *in, void *out, int64_t planes, int64_t H, int64_t W, bool bf16,
                             hipStream_t s);
 // out = scale * (yr + transpose(yc)) * SiLU(z); yr [planes][H][W] fp32 (may

@@ -108,6 +108,14 @@ def scan_params(g, dim, dstate=DSTATE, device="cpu", perturb=False):
     return A.contiguous(), D.contiguous(), bias.contiguous()
 
 
+def conv_params(g, dim, device="cpu"):
+    """Depthwise width-4 conv weights [dim, 4] and bias [dim] (fp32), drawn
+    U(-0.5, 0.5) like a fan-in-4 uniform initialisation."""
+    w = torch.rand((dim, 4), generator=g, device=device, dtype=torch.float32) - 0.5
+    b = torch.rand((dim,), generator=g, device=device, dtype=torch.float32) - 0.5
+    return w.contiguous(), b.contiguous()
+
+
 def scan_direction(g, batch, dim, seqlen, dstate=DSTATE, device="cpu", dtype=torch.float32,
                    perturb=False, u_shape=None, delta_len=None, bc_layout="token"):
     """One direction's tensors: u, delta [batch, dim, L]; B, C [batch, dstate, L];

@@ -194,3 +194,37 @@ def test_plane_count_limit(lib):
                                    0, 0, 1, None) == 6
     dirs = (vm.VmScanDir * 4)(*(_dir(FAKE * (k + 4)) for k in range(4)))
     assert lib.vm_ss2d_scan_fwd(dirs, FAKE, None, 1.0, FAKE * 3, big, big, 2, 2, 16, 0, 1, None) == 6
+
+
+def test_conv_argument_checks(lib):
+    def call(x=FAKE, w=FAKE * 2, b=None, out=FAKE * 3, batch=2, dim=4, L=9, rev=0, dtype=0):
+        return lib.vm_causal_conv1d_silu(x, w, b, out, batch, dim, L, rev, dtype, None)
+
+    assert call(x=None) == 1
+    assert call(w=None) == 1
+    assert call(out=None) == 1
+    assert call(L=0) == 2
+    assert call(dim=-1) == 2
+    assert call(rev=2) == 4
+    assert call(dtype=7) == 3
+    assert call(batch=1 << 12, dim=1 << 12) == 6           # 2^24 rows
+    assert call(L=65536 * 1024) == 6                        # 65536 chunks of 1024
+    assert call(out=FAKE + 4) == 5
+    assert call(out=FAKE * 2 + 8) == 5                      # overlaps w
+    assert call(b=FAKE * 3 + 4) == 5
+
+
+def test_fused_conv_only_where_supported(lib):
+    f, b = _dir(FAKE), _dir(FAKE * 2)
+    f.conv_w = FAKE * 5
+    # bidirectional: both directions or neither
+    assert lib.vm_bidir_scan_fwd(ctypes.byref(f), ctypes.byref(b), None, 1.0, FAKE * 3, 2, 4, 5, 16,
+                                 0, 1, None) == 6
+    # pooled and SS2D scans take no fused conv
+    assert lib.vm_pool_scan_repeat(ctypes.byref(f), None, None, 1.0, FAKE * 3, 2, 4, 2, 2, 16, 0, 0, 1,
+                                   None) == 6
+    dirs = (vm.VmScanDir * 4)(*(_dir(FAKE * (k + 6)) for k in range(4)))
+    dirs[1].conv_w = FAKE * 5
+    assert lib.vm_ss2d_scan_fwd(dirs, FAKE, None, 1.0, FAKE * 3, 2, 4, 2, 2, 16, 0, 1, None) == 6
+    # the conv weights count as inputs for the alias check
+    assert _scan(lib, d=f, out=f.conv_w + 4) == 5

@@ -531,3 +531,83 @@ def test_full_vim_tiny_bidir_zoh():
     ref = oracle.bidir_scan(sub_dir(host_dir(fwd), bsel, dsel), sub_dir(host_dir(bwd), bsel, dsel),
                             z=host(z)[bsel][:, dsel], combine_scale=w.combine_scale, zoh=True)
     assert_close(host(out[bsel]), ref, FP32_TOL, "vim-t zoh full (sampled batches)")
+
+
+# ---------------------------------------------------------------- causal conv1d + SiLU
+def _conv_inputs(seed, batch, dim, L, dtype=torch.float32):
+    g = wl.generator(seed, DEV)
+    x = torch.randn((batch, dim, L), generator=g, device=DEV).to(dtype)
+    w, b = wl.conv_params(g, dim, DEV)
+    return x, w, b
+
+
+# L = 2: shorter than the kernel; 2500: three 1024-step chunks (margins
+# across chunk boundaries); 197: one ragged chunk
+@pytest.mark.parametrize("batch,dim,L", [(2, 70, 197), (1, 3, 2500), (2, 5, 2)])
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_conv1d_silu(batch, dim, L, reverse, dtype):
+    _case(f"conv1d b{batch} d{dim} L{L} rev{reverse} {dtype}")
+    x, w, b = _conv_inputs(1600 + L, batch, dim, L, dtype)
+    out = vm.vm_causal_conv1d_silu(x, w, b, reverse=reverse)
+    torch.cuda.synchronize()
+    ref = oracle.causal_conv1d_silu(host(x), host(w), host(b), reverse=reverse)
+    if dtype == torch.float32:
+        assert_close(host(out), ref, FP32_TOL, "conv1d")
+    else:   # one bf16 rounding of the result: within 2^-8 relative per element
+        assert np.all(np.abs(host(out) - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
+
+
+@pytest.mark.parametrize("L,reverse", [(77, False), (77, True), (300, True), (16, False), (3, True)])
+@pytest.mark.parametrize("zoh", [False, True])
+def test_fused_conv_single(L, reverse, zoh):
+    _case(f"fused conv single L{L} rev{reverse} zoh{zoh}")
+    p, z = wl.single_inputs(1700 + L, 2, 70, L, device=DEV, perturb=True)
+    g = wl.generator(1800 + L, DEV)
+    cw, cb = wl.conv_params(g, 70, DEV)
+    out = vm.vm_selective_scan_fwd(**p, z=z, reverse=reverse, zoh=zoh, conv_w=cw, conv_b=cb)
+    torch.cuda.synchronize()
+    hp = host_dir(p)
+    hp["u"] = oracle.causal_conv1d_silu(hp["u"], host(cw), host(cb), reverse=reverse)
+    ref = oracle.selective_scan(**hp, z=host(z), reverse=reverse, zoh=zoh)
+    assert_close(host(out), ref, FP32_TOL, "fused conv single")
+
+
+@pytest.mark.parametrize("L", [197, 600])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_fused_conv_bidir(L, dtype):
+    # both directions read the same content x through their own convolutions:
+    # the backward one runs on the reversed sequence
+    _case(f"fused conv bidir L{L} {dtype}")
+    fwd, bwd, z = wl.bidir_inputs(1900 + L, 2, 70, L, device=DEV, dtype=dtype, perturb=True)
+    bwd["u"] = fwd["u"]
+    g = wl.generator(2000 + L, DEV)
+    for p in (fwd, bwd):
+        p["conv_w"], p["conv_b"] = wl.conv_params(g, 70, DEV)
+    out = vm.vm_bidir_scan_fwd(fwd, bwd, z=z, combine_scale=0.5)
+    torch.cuda.synchronize()
+    hf, hb = host_dir(fwd), host_dir(bwd)
+    for h, rev in ((hf, False), (hb, True)):
+        h["u"] = oracle.causal_conv1d_silu(h["u"], h.pop("conv_w"), h.pop("conv_b"), reverse=rev)
+    ref = oracle.bidir_scan(hf, hb, z=host(z), combine_scale=0.5)
+    assert_close(host(out), ref, FP32_TOL if dtype == torch.float32 else BF16_TOL, "fused conv bidir")
+
+
+@pytest.mark.parametrize("L", [197, 600])
+def test_fused_conv_equals_conv_then_scan(L):
+    # the in-kernel convolution takes the same fp32 operations in the same
+    # order as the standalone kernel, so both routes agree bit for bit
+    _case(f"fused conv == conv then scan L{L}")
+    fwd, bwd, z = wl.bidir_inputs(2100 + L, 2, 70, L, device=DEV, perturb=True)
+    bwd["u"] = fwd["u"]
+    g = wl.generator(2200 + L, DEV)
+    for p in (fwd, bwd):
+        p["conv_w"], p["conv_b"] = wl.conv_params(g, 70, DEV)
+    fused = vm.vm_bidir_scan_fwd(fwd, bwd, z=z)
+    f2 = {k: v for k, v in fwd.items() if not k.startswith("conv")}
+    b2 = {k: v for k, v in bwd.items() if not k.startswith("conv")}
+    f2["u"] = vm.vm_causal_conv1d_silu(fwd["u"], fwd["conv_w"], fwd["conv_b"])
+    b2["u"] = vm.vm_causal_conv1d_silu(bwd["u"], bwd["conv_w"], bwd["conv_b"], reverse=True)
+    two = vm.vm_bidir_scan_fwd(f2, b2, z=z)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, two)
