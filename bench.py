@@ -59,6 +59,9 @@ def parse():
                          "4 FastVim pooled (axes alternate per step), 5 FastVim unpooled L=16384, "
                          "6 SS2D four-direction scan 56x56")
     ap.add_argument("--sets", type=int, default=0, help="input sets to cycle (0 = auto)")
+    ap.add_argument("--conv", choices=["none", "fused", "unfused"], default="none",
+                    help="configs 0-2: the scan input comes from the block's causal conv1d + SiLU, "
+                         "computed inside the scan (fused) or by vm_causal_conv1d_silu first (unfused)")
     ap.add_argument("--zoh", action="store_true",
                     help="zero-order-hold input coefficient instead of dt (the released model uses dt)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -91,7 +94,7 @@ def algorithmic_bytes_scan(batch, dim, L, N, es, dirs, gated):
     return dirs * per_dir + (tok * es if gated else 0) + tok * es
 
 
-def build_step(cfg, seed, sets, dev, zoh=False):
+def build_step(cfg, seed, sets, dev, zoh=False, conv="none"):
     """Returns (step_fn(i), info dict, cpu_fn(budget_s) -> (seconds, bytes, tokens, threads, desc))."""
     import torch
 
@@ -112,9 +115,26 @@ def build_step(cfg, seed, sets, dev, zoh=False):
                 p, z = wl.single_inputs(seed + k, w.batch, w.dim, w.seqlen, device=dev, dtype=dt)
                 inputs.append((p, None, z))
         outs = [torch.empty_like(inputs[k][0]["u"]) for k in range(sets)]
+        if conv != "none":
+            # Vim: both directions read the same content x through their own convolutions
+            gc = wl.generator(seed + 100, dev)
+            for f, b, _ in inputs:
+                if b is not None:
+                    b["u"] = f["u"]
+                for p in (f, b) if b is not None else (f,):
+                    p["conv_w"], p["conv_b"] = wl.conv_params(gc, w.dim, dev)
+        ubuf = [torch.empty_like(outs[0]) for _ in range(dirs)] if conv == "unfused" else None
+
+        def strip(p, u):
+            return {k: (u if k == "u" else v) for k, v in p.items() if not k.startswith("conv")}
 
         def step(i):
             f, b, z = inputs[i % sets]
+            if conv == "unfused":
+                f = strip(f, vm.vm_causal_conv1d_silu(f["u"], f["conv_w"], f["conv_b"], out=ubuf[0]))
+                if b is not None:
+                    b = strip(b, vm.vm_causal_conv1d_silu(b["u"], b["conv_w"], b["conv_b"], reverse=True,
+                                                          out=ubuf[1]))
             if dirs == 2:
                 vm.vm_bidir_scan_fwd(f, b, z=z, combine_scale=w.combine_scale, out=outs[i % sets], zoh=zoh)
             else:
@@ -126,6 +146,8 @@ def build_step(cfg, seed, sets, dev, zoh=False):
         info = dict(workload=w.name, batch=w.batch, dim=w.dim, seqlen=w.seqlen, dstate=N,
                     directions=dirs, combine_scale=w.combine_scale, dtype=w.dtype,
                     bc_layout="token-major")
+        if conv != "none":
+            info["conv1d"] = conv
 
         def cpu(budget):
             import oracle
@@ -133,13 +155,25 @@ def build_step(cfg, seed, sets, dev, zoh=False):
             sub = max(1, min(w.batch, w.batch))          # whole workload, repeated in time
             hf = {k: (v[:sub].double().cpu().numpy() if k in ("u", "delta", "B", "C") else
                       (v.double().cpu().numpy() if v is not None else None)) for k, v in f.items()}
+            cvf = (hf.pop("conv_w", None), hf.pop("conv_b", None))
+            hxf = hf["u"].copy()                         # the conv input, when there is a conv
             hz = z[:sub].double().cpu().numpy()
             if dirs == 2:
                 hb = {k: (v[:sub].double().cpu().numpy() if k in ("u", "delta", "B", "C") else
                           (v.double().cpu().numpy() if v is not None else None)) for k, v in b.items()}
-                run = lambda: oracle.bidir_scan(hf, hb, z=hz, combine_scale=w.combine_scale, zoh=zoh)
+                cvb = (hb.pop("conv_w", None), hb.pop("conv_b", None))
+                hxb = hb["u"].copy()
+
+                def run():
+                    if conv != "none":
+                        hf["u"] = oracle.causal_conv1d_silu(hxf, *cvf)
+                        hb["u"] = oracle.causal_conv1d_silu(hxb, *cvb, reverse=True)
+                    return oracle.bidir_scan(hf, hb, z=hz, combine_scale=w.combine_scale, zoh=zoh)
             else:
-                run = lambda: oracle.selective_scan(**hf, z=hz, zoh=zoh)
+                def run():
+                    if conv != "none":
+                        hf["u"] = oracle.causal_conv1d_silu(hxf, *cvf)
+                    return oracle.selective_scan(**hf, z=hz, zoh=zoh)
             reps, t0 = 0, time.perf_counter()
             while True:
                 run()
@@ -320,7 +354,10 @@ def main():
     vm.load_library()
     dev = torch.device("cuda:0")
     sets = args.sets or (3 if args.config in (0, 1, 2, 3, 6) else 1)
-    step, info, cpu_fn, nbytes, tokens, slots = build_step(args.config, args.seed, sets, dev, args.zoh)
+    if args.conv != "none" and args.config not in (0, 1, 2):
+        raise SystemExit("--conv applies to configs 0-2")
+    step, info, cpu_fn, nbytes, tokens, slots = build_step(args.config, args.seed, sets, dev, args.zoh,
+                                                           args.conv)
     if args.zoh:
         info = dict(info, discretization="zoh")
     torch.cuda.synchronize()

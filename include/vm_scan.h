@@ -187,8 +187,7 @@ int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
  *   x, out [batch, dim, seqlen] (dtype); w [dim, 4] fp32; bias [dim] fp32
  *   (NULL = 0).  The same result feeds the block's projections of delta, B
  *   and C; the scan entry points can recompute it from x (conv_w).
- * Limits: batch * dim <= 2^24 - 1 and seqlen <= 65535 * 1024
- * (VM_ERR_UNSUPPORTED).
+ * Limit: batch * dim * seqlen below 2^33 elements (VM_ERR_UNSUPPORTED).
  */
 int vm_causal_conv1d_silu(const void *x, const float *w, const float *bias,
                           void *out, int64_t batch, int64_t dim,

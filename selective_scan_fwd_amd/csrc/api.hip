@@ -307,8 +307,9 @@ int vm_causal_conv1d_silu(const void *x, const float *w, const float *bias, void
   if (!flag_ok(reverse)) return VM_ERR_FLAG;
   int64_t tok = 0;
   if (!dims_ok({batch, dim, seqlen}, &tok)) return VM_ERR_SHAPE;
-  // one workgroup per (row, 1024-step chunk): rows on grid x, chunks on y
-  if (batch * dim > kMaxPlanes || (seqlen + 1023) / 1024 > 65535) return VM_ERR_UNSUPPORTED;
+  // one 256-thread workgroup per 2048 consecutive elements on grid x, whose
+  // work-item count must stay below 2^32
+  if (tok >= (int64_t{1} << 33)) return VM_ERR_UNSUPPORTED;
   if (x == nullptr || w == nullptr || out == nullptr) return VM_ERR_NULL;
   const int es = dtype == VM_BF16 ? 2 : 4;
   const Span so = span(out, tok * es);

@@ -12,6 +12,8 @@
 //  * bf16 -> fp32 widening of side tensors.
 // All of these are HBM-bound streaming kernels: every element is read once
 // and written once with coalesced accesses.
+#include <initializer_list>
+
 #include "vm_internal.h"
 
 namespace vmk {
@@ -299,6 +301,89 @@ transpose_kernel(const T *__restrict__ in, T *__restrict__ out, int H, int W, in
   }
 }
 
+// Four-wide forms of the two kernels above for H % 4 == 0, W % 4 == 0 and
+// 16-byte aligned planes: 64 x 64 tiles, each thread moving four rows of four
+// consecutive values (16 values per thread and array in flight).
+constexpr int kTile4 = 64;
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+transpose4_kernel(const T *__restrict__ in, T *__restrict__ out, int H, int W, int tiles_w) {
+  __shared__ float tile[kTile4][kTile4 + 1];
+  const int64_t pl = blockIdx.x;
+  const int ti = blockIdx.y / tiles_w, tj = blockIdx.y - (blockIdx.y / tiles_w) * tiles_w;
+  const int i0 = ti * kTile4, j0 = tj * kTile4;
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;   // 16 x 16 threads
+  const T *src = in + pl * H * W;
+  T *dst = out + pl * H * W;
+  float4 v[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = i0 + ty + 16 * k, j = j0 + 4 * tx;
+    v[k] = (i < H && j < W) ? load4(src + static_cast<int64_t>(i) * W + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float *t = &tile[ty + 16 * k][4 * tx];
+    t[0] = v[k].x; t[1] = v[k].y; t[2] = v[k].z; t[3] = v[k].w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = ty + 16 * k, j = j0 + r, i = i0 + 4 * tx;
+    if (i < H && j < W)
+      store4(dst + static_cast<int64_t>(j) * H + i,
+             make_float4(tile[4 * tx][r], tile[4 * tx + 1][r], tile[4 * tx + 2][r], tile[4 * tx + 3][r]));
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+ss2d_merge4_kernel(const float *yr, const float *__restrict__ yc, const T *__restrict__ z, T *out,
+                   int H, int W, int tiles_w, float scale) {
+  __shared__ float tile[kTile4][kTile4 + 1];
+  const int64_t pl = blockIdx.x;
+  const int ti = blockIdx.y / tiles_w, tj = blockIdx.y - (blockIdx.y / tiles_w) * tiles_w;
+  const int i0 = ti * kTile4, j0 = tj * kTile4;
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  const float *c = yc + pl * H * W;
+  const int64_t base = pl * H * W;
+  float4 v[4], r4[4], z4[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {                             // yc rows j, contiguous in i
+    const int j = j0 + ty + 16 * k, i = i0 + 4 * tx;
+    v[k] = (i < H && j < W) ? load4(c + static_cast<int64_t>(j) * H + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {                             // yr and z rows i, contiguous in j
+    const int i = i0 + ty + 16 * k, j = j0 + 4 * tx;
+    const bool ok = i < H && j < W;
+    const int64_t e = base + static_cast<int64_t>(i) * W + j;
+    r4[k] = ok ? load4(yr + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    z4[k] = (ok && z != nullptr) ? load4(z + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float *t = &tile[ty + 16 * k][4 * tx];
+    t[0] = v[k].x; t[1] = v[k].y; t[2] = v[k].z; t[3] = v[k].w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = ty + 16 * k, i = i0 + r, j = j0 + 4 * tx;
+    if (i < H && j < W) {
+      const float cx = tile[4 * tx][r], cy = tile[4 * tx + 1][r], cz = tile[4 * tx + 2][r],
+                  cw = tile[4 * tx + 3][r];
+      float4 o = make_float4(scale * (r4[k].x + cx), scale * (r4[k].y + cy), scale * (r4[k].z + cz),
+                             scale * (r4[k].w + cw));
+      if (z != nullptr) {
+        o.x *= silu_f(z4[k].x); o.y *= silu_f(z4[k].y); o.z *= silu_f(z4[k].z); o.w *= silu_f(z4[k].w);
+      }
+      store4(out + base + static_cast<int64_t>(i) * W + j, o);
+    }
+  }
+}
+
 // out[p][i][j] = scale * (yr[p][i][j] + yc[p][j][i]) * SiLU(z[p][i][j]):
 // yr holds the row traversals' sum ([P][H][W], fp32, may be out itself),
 // yc the column traversals' ([P][W][H], fp32).  z may be NULL.
@@ -331,40 +416,80 @@ ss2d_merge_kernel(const float *yr, const float *__restrict__ yc, const T *__rest
 
 // u[t] = SiLU(cb + sum_k w[k] x[t - 3 + k]) on each row (x outside the row
 // is 0); reverse: the same in reversed order, u[t] = SiLU(cb + sum_k w[k]
-// x[t + 3 - k]).  One workgroup per (row, chunk of kConvChunk steps): the
-// chunk's inputs with a 3-step margin on each side go through LDS, so every
-// input is read from HBM once and each output is one LDS window.
-constexpr int kConvChunk = 4 * kThreads;
+// x[t + 3 - k]).  The [rows x L] tensor is processed as one flat array, so
+// short rows do not leave threads idle: each thread computes kConvPer
+// consecutive outputs from its own inputs plus the four before them
+// (forward) or after them (reverse), which are its neighbour thread's and
+// come from cache; taps that fall outside the element's row are masked.
+// One integer division per thread locates its first element's row; the
+// channel's weights are reloaded only when a row ends inside the thread's run.
+constexpr int kConvPer = 8;
 
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
 conv1d_silu_kernel(const T *__restrict__ x, const float *__restrict__ w, const float *__restrict__ cb,
-                   T *__restrict__ out, int64_t L, int64_t dim, int reverse) {
-  __shared__ float tile[kConvChunk + 6];
-  const int64_t row = blockIdx.x;
-  const int64_t c0 = static_cast<int64_t>(blockIdx.y) * kConvChunk;
-  const T *xr = x + row * L;
-  for (int i = threadIdx.x; i < kConvChunk + 6; i += kThreads) {
-    const int64_t t = c0 - 3 + i;
-    tile[i] = (t >= 0 && t < L) ? to_f32(xr[t]) : 0.0f;
-  }
-  __syncthreads();
-  const int64_t d = row % dim;
-  const float w0 = w[4 * d], w1 = w[4 * d + 1], w2 = w[4 * d + 2], w3 = w[4 * d + 3];
-  const float b = cb != nullptr ? cb[d] : 0.0f;
-  const int dir = reverse ? -1 : 1;           // direction of "earlier" in visit order
-  T *orow = out + row * L;
+                   T *__restrict__ out, int64_t n, int64_t L, int64_t dim, int reverse, int vec) {
+  const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) * kConvPer;
+  if (e0 >= n) return;
+  // xs[4 + j] = x[e0 + j]; xs[0..3] the four before (forward) or, with
+  // reverse, xs[4 + kConvPer ..] the four after; 0 outside [0, n)
+  float xs[kConvPer + 8];
+  const int64_t lo = e0 - 4;
+  if (vec && lo >= 0 && e0 + kConvPer + 4 <= n) {
 #pragma unroll
-  for (int j = 0; j < kConvChunk / kThreads; ++j) {
-    const int i = threadIdx.x + j * kThreads;
-    if (c0 + i < L) {
-      const float *c = tile + i + 3;          // x[c0 + i]
-      float v = __builtin_fmaf(w3, c[0], b);
-      v = __builtin_fmaf(w2, c[-dir], v);
-      v = __builtin_fmaf(w1, c[-2 * dir], v);
-      v = __builtin_fmaf(w0, c[-3 * dir], v);
-      orow[c0 + i] = from_f32<T>(silu_f(v));
+    for (int q = 0; q < kConvPer + 8; q += 4) {
+      const float4 v = load4(x + lo + q);
+      xs[q] = v.x; xs[q + 1] = v.y; xs[q + 2] = v.z; xs[q + 3] = v.w;
     }
+  } else {
+#pragma unroll
+    for (int q = 0; q < kConvPer + 8; ++q) {
+      const int64_t e = lo + q;
+      xs[q] = (e >= 0 && e < n) ? to_f32(x[e]) : 0.0f;
+    }
+  }
+  int64_t t, d;
+  if (n <= 0xffffffffll) {                                 // 32-bit division where it suffices
+    const uint32_t r32 = static_cast<uint32_t>(e0) / static_cast<uint32_t>(L);
+    t = static_cast<uint32_t>(e0) - r32 * static_cast<uint32_t>(L);
+    d = r32 % static_cast<uint32_t>(dim);
+  } else {
+    const int64_t row = e0 / L;
+    t = e0 - row * L;
+    d = row % dim;
+  }
+  float w0 = w[4 * d], w1 = w[4 * d + 1], w2 = w[4 * d + 2], w3 = w[4 * d + 3];
+  float b = cb != nullptr ? cb[d] : 0.0f;
+  float res[kConvPer];
+#pragma unroll
+  for (int j = 0; j < kConvPer; ++j) {
+    const float *c = xs + 4 + j;                           // x[e0 + j]
+    float v = __builtin_fmaf(w3, c[0], b);
+    if (!reverse) {
+      v = __builtin_fmaf(w2, t >= 1 ? c[-1] : 0.0f, v);
+      v = __builtin_fmaf(w1, t >= 2 ? c[-2] : 0.0f, v);
+      v = __builtin_fmaf(w0, t >= 3 ? c[-3] : 0.0f, v);
+    } else {
+      v = __builtin_fmaf(w2, t + 1 < L ? c[1] : 0.0f, v);
+      v = __builtin_fmaf(w1, t + 2 < L ? c[2] : 0.0f, v);
+      v = __builtin_fmaf(w0, t + 3 < L ? c[3] : 0.0f, v);
+    }
+    res[j] = silu_f(v);
+    if (++t == L && j + 1 < kConvPer) {                    // next element starts a new row
+      t = 0;
+      if (++d == dim) d = 0;
+      w0 = w[4 * d]; w1 = w[4 * d + 1]; w2 = w[4 * d + 2]; w3 = w[4 * d + 3];
+      b = cb != nullptr ? cb[d] : 0.0f;
+    }
+  }
+  if (vec && e0 + kConvPer <= n) {
+#pragma unroll
+    for (int q = 0; q < kConvPer; q += 4)
+      store4(out + e0 + q, make_float4(res[q], res[q + 1], res[q + 2], res[q + 3]));
+  } else {
+#pragma unroll
+    for (int j = 0; j < kConvPer; ++j)
+      if (e0 + j < n) out[e0 + j] = from_f32<T>(res[j]);
   }
 }
 
@@ -418,6 +543,17 @@ hipError_t launch_atrous_scatter(const void *streams, void *y, int64_t batch, in
   return hipGetLastError();
 }
 
+bool aligned(const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+// The four-wide transpose and merge read and write rows of both orientations
+// four at a time: H and W multiples of 4, planes aligned to four elements.
+bool tile4_ok(int64_t H, int64_t W, std::initializer_list<const void *> ptrs, bool bf16) {
+  if (H % 4 != 0 || W % 4 != 0) return false;
+  for (const void *p : ptrs)
+    if (!aligned(p, bf16 ? 8 : 16)) return false;
+  return true;
+}
+
 // Four-wide accesses need W % 4 == 0, aligned rows, and (for the lane
 // reduction and the LDS combine) W / 4 a power of two no larger than 64.
 int vec_ok(const void *a, const void *b, const void *c, int64_t W, bool bf16) {
@@ -464,6 +600,19 @@ hipError_t launch_repeat_gate(const float *y, const void *z, void *out, int64_t 
 hipError_t launch_transpose(const void *in, void *out, int64_t planes, int64_t H, int64_t W, bool bf16,
                             hipStream_t s) {
   if (planes * H * W == 0) return hipSuccess;
+  if (tile4_ok(H, W, {in, out}, bf16)) {
+    const int th = static_cast<int>((H + kTile4 - 1) / kTile4), tw = static_cast<int>((W + kTile4 - 1) / kTile4);
+    const dim3 grid(static_cast<unsigned>(planes), static_cast<unsigned>(th * tw));
+    if (bf16)
+      hipLaunchKernelGGL(transpose4_kernel<bf16_t>, grid, dim3(kThreads), 0, s,
+                         static_cast<const bf16_t *>(in), static_cast<bf16_t *>(out),
+                         static_cast<int>(H), static_cast<int>(W), tw);
+    else
+      hipLaunchKernelGGL(transpose4_kernel<float>, grid, dim3(kThreads), 0, s,
+                         static_cast<const float *>(in), static_cast<float *>(out),
+                         static_cast<int>(H), static_cast<int>(W), tw);
+    return hipGetLastError();
+  }
   const int th = static_cast<int>((H + kTile - 1) / kTile), tw = static_cast<int>((W + kTile - 1) / kTile);
   const dim3 grid(static_cast<unsigned>(planes), static_cast<unsigned>(th * tw));
   if (bf16)
@@ -481,6 +630,20 @@ hipError_t launch_ss2d_merge(const float *yr, const float *yc, const void *z, vo
                              int64_t planes, int64_t H, int64_t W, float scale, bool bf16,
                              hipStream_t s) {
   if (planes * H * W == 0) return hipSuccess;
+  if (tile4_ok(H, W, {yr, yc}, false) && tile4_ok(H, W, {out}, bf16) &&
+      (z == nullptr || aligned(z, bf16 ? 8 : 16))) {
+    const int th = static_cast<int>((H + kTile4 - 1) / kTile4), tw = static_cast<int>((W + kTile4 - 1) / kTile4);
+    const dim3 grid(static_cast<unsigned>(planes), static_cast<unsigned>(th * tw));
+    if (bf16)
+      hipLaunchKernelGGL(ss2d_merge4_kernel<bf16_t>, grid, dim3(kThreads), 0, s, yr, yc,
+                         static_cast<const bf16_t *>(z), static_cast<bf16_t *>(out),
+                         static_cast<int>(H), static_cast<int>(W), tw, scale);
+    else
+      hipLaunchKernelGGL(ss2d_merge4_kernel<float>, grid, dim3(kThreads), 0, s, yr, yc,
+                         static_cast<const float *>(z), static_cast<float *>(out),
+                         static_cast<int>(H), static_cast<int>(W), tw, scale);
+    return hipGetLastError();
+  }
   const int th = static_cast<int>((H + kTile - 1) / kTile), tw = static_cast<int>((W + kTile - 1) / kTile);
   const dim3 grid(static_cast<unsigned>(planes), static_cast<unsigned>(th * tw));
   if (bf16)
@@ -497,16 +660,19 @@ hipError_t launch_ss2d_merge(const float *yr, const float *yc, const void *z, vo
 hipError_t launch_conv1d_silu(const void *x, const float *w, const float *cb, void *out,
                               int64_t rows, int64_t L, int64_t dim, int reverse, bool bf16,
                               hipStream_t s) {
-  if (rows * L == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(rows), static_cast<unsigned>((L + kConvChunk - 1) / kConvChunk));
+  const int64_t n = rows * L;
+  if (n == 0) return hipSuccess;
+  const int64_t per_block = static_cast<int64_t>(kConvPer) * kThreads;
+  const dim3 grid(static_cast<unsigned>((n + per_block - 1) / per_block));
+  const int vec = aligned(out, bf16 ? 8 : 16) && aligned(x, bf16 ? 8 : 16) ? 1 : 0;
   if (bf16)
     hipLaunchKernelGGL(conv1d_silu_kernel<bf16_t>, grid, dim3(kThreads), 0, s,
-                       static_cast<const bf16_t *>(x), w, cb, static_cast<bf16_t *>(out), L, dim,
-                       reverse);
+                       static_cast<const bf16_t *>(x), w, cb, static_cast<bf16_t *>(out), n, L, dim,
+                       reverse, vec);
   else
     hipLaunchKernelGGL(conv1d_silu_kernel<float>, grid, dim3(kThreads), 0, s,
-                       static_cast<const float *>(x), w, cb, static_cast<float *>(out), L, dim,
-                       reverse);
+                       static_cast<const float *>(x), w, cb, static_cast<float *>(out), n, L, dim,
+                       reverse, vec);
   return hipGetLastError();
 }
 

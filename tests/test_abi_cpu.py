@@ -207,8 +207,7 @@ def test_conv_argument_checks(lib):
     assert call(dim=-1) == 2
     assert call(rev=2) == 4
     assert call(dtype=7) == 3
-    assert call(batch=1 << 12, dim=1 << 12) == 6           # 2^24 rows
-    assert call(L=65536 * 1024) == 6                        # 65536 chunks of 1024
+    assert call(batch=1 << 13, dim=1 << 10, L=1 << 10) == 6  # 2^33 elements: 2^23 workgroups
     assert call(out=FAKE + 4) == 5
     assert call(out=FAKE * 2 + 8) == 5                      # overlaps w
     assert call(b=FAKE * 3 + 4) == 5

@@ -401,7 +401,9 @@ def _ss2d_ref(u, dirs, z, scale=1.0, softplus=True, bsel=None, dsel=None):
 # (1, 1) degenerate map; (3, 5) and (33, 17) ragged 32 x 32 transpose tiles;
 # (7, 10) single tile; (12, 32) wide rows; (20, 32) and (24, 25): 640 and 600
 # steps, past the on-chip exchange (line-aligned and ragged global exchange).
-@pytest.mark.parametrize("H,W", [(1, 1), (3, 5), (7, 10), (12, 32), (33, 17), (20, 32), (24, 25)])
+# (12, 32), (20, 32), (68, 8): four-wide transpose and merge.
+@pytest.mark.parametrize("H,W", [(1, 1), (3, 5), (7, 10), (12, 32), (33, 17), (20, 32), (24, 25),
+                                 (68, 8)])
 @pytest.mark.parametrize("bc_layout", ["token", "dense"])
 def test_ss2d_fp32(H, W, bc_layout):
     _case(f"ss2d fp32 {H}x{W} bc {bc_layout}")
@@ -423,11 +425,14 @@ def test_ss2d_ungated_no_softplus():
     assert_close(host(out), ref, FP32_TOL, "ss2d ungated")
 
 
-def test_ss2d_column_routing_bit_exact():
+# 13 x 37: scalar transpose and merge; 68 x 132: the four-wide 64 x 64 tiles
+# with ragged edges in both directions
+@pytest.mark.parametrize("H,W", [(13, 37), (68, 132)])
+def test_ss2d_column_routing_bit_exact(H, W):
     # B = 0 and D_k = 1: every traversal returns u at its own pixel, so the
     # merged output is exactly 4u (any misrouted pixel breaks equality)
-    _case("ss2d routing bit-exact 13x37")
-    u, dirs, _ = wl.ss2d_inputs(860, 2, 5, 13, 37, device=DEV, gated=False)
+    _case(f"ss2d routing bit-exact {H}x{W}")
+    u, dirs, _ = wl.ss2d_inputs(860, 2, 5, H, W, device=DEV, gated=False)
     for p in dirs:
         p["B"] = torch.zeros_like(p["B"])
         p["D"] = torch.ones_like(p["D"])
