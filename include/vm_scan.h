@@ -162,7 +162,7 @@ int vm_selective_scan_fwd(const vm_scan_dir *p, const void *z, void *out,
  * combine_scale = 0.5 is the released averaging model, 1 the summed form.
  * z may be NULL (no gate).  out: [batch, dim, seqlen] (dtype).
  * Temporary memory: for sequences too long for the on-chip exchange buffer
- * (seqlen above about 480), an fp32 [batch, dim, seqlen rounded up to 32]
+ * (seqlen above 552; 520 with a fused conv), an fp32 [batch, dim, seqlen rounded up to 32]
  * exchange buffer from the library's stream-ordered pool.  With VM_F32, a
  * seqlen that is a multiple of 32 and a 128-byte aligned `out`, `out` itself
  * serves as the exchange buffer and nothing is allocated.

@@ -148,17 +148,23 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// A wave's LDS area.  The staging side (PREP, BC and the conv rows CX) is
+// live from a tile's staging to its read-back into registers; the partial
+// sums PART from the scan of a tile to their read in the combine.  In a
+// wave's program order these never overlap (scan k, read partials k, stage
+// k+1, read back k+1), so PART shares the area's start with PREP.
 template <int T, int R, bool CV>
 struct Layout {
   static constexpr int PSTR = 2 * T + 2;                  // (dt, dt u) per row; PSTR/2 odd
   static constexpr int QSTR = T + 1;                      // partials per lane, odd
   static constexpr int PREP = R * PSTR;
-  static constexpr int UST = R * T;                       // u per row, for the D u skip
   static constexpr int BC = 32 * T;                       // B in slots 0..15, C in 16..31
   static constexpr int PART = 64 * QSTR;
   static constexpr int XH = T + 4;                        // conv input row: 3 halo, T, 1 spare
   static constexpr int CX = CV ? R * XH : 0;
-  static constexpr int WAVE = PREP + UST + BC + PART + CX;  // floats per wave
+  static constexpr int STAGE = PREP + BC + CX;
+  static constexpr int WAVE = STAGE > PART ? STAGE : PART;  // floats per wave
+  static_assert(WAVE % 2 == 0, "float2 staging of the second wave stays 8-byte aligned");
 };
 
 // Row stride of the LDS exchange block for n parked steps: >= n and
@@ -220,10 +226,9 @@ scan_kernel(const ScanArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   float *const prep = smem + wave * Lay::WAVE;   // [R][PSTR]
-  float *const ust = prep + Lay::PREP;           // [R][T]
-  float *const bcs = ust + Lay::UST;             // [T][32]
-  float *const part = bcs + Lay::BC;             // [64 lanes][QSTR]
-  float *const xs = part + Lay::PART;            // [R][XH] conv input (CONV)
+  float *const bcs = prep + Lay::PREP;           // [T][32]
+  float *const xs = bcs + Lay::BC;               // [R][XH] conv input (CONV)
+  float *const part = prep;                      // [64 lanes][QSTR], shares the staging area
   float *const xlds = smem + DIRS * Lay::WAVE;   // [R][XS]   (kXLds)
 
   const int sp = lane / R;                       // state group
@@ -303,6 +308,7 @@ scan_kernel(const ScanArgs p) {
   // else the row's spare slot.
   float cw[PE][4], cb[PE], xprev[PE];
   int hx[PE];
+  float ukeep[PE];                               // u of the staged tile, for its D u skip
 #pragma unroll
   for (int i = 0; i < PE; ++i) {
     srow[i] = lane / T + i * (64 / T);
@@ -356,8 +362,8 @@ scan_kernel(const ScanArgs p) {
     }
   };
 
-  // Stages (dt, dt u) for the scan ((dt, u) with the zero-order hold) and u
-  // for the skip term, for tile kt.  Steps past L
+  // Stages (dt, dt u) for the scan ((dt, u) with the zero-order hold), for
+  // tile kt, and keeps u in registers for the skip term.  Steps past L
   // and channels past dim stage u = 0, so the state only decays where it is
   // zero (before the first real step) or no longer read; states past dstate
   // stage B = C = 0.
@@ -400,7 +406,7 @@ scan_kernel(const ScanArgs p) {
       const float dtv = sp_on ? softplus_f(x) : x;
       *reinterpret_cast<float2 *>(prep + srow[i] * Lay::PSTR + 2 * sq) =
           make_float2(dtv, ZOH ? uv : dtv * uv);
-      ust[srow[i] * T + sq] = uv;
+      ukeep[i] = uv;
     }
 #pragma unroll
     for (int i = 0; i < BQ; ++i) {
@@ -460,7 +466,7 @@ scan_kernel(const ScanArgs p) {
     for (int i = 0; i < PE; ++i) {
 #pragma unroll
       for (int s = 0; s < SPLIT; ++s) ps[i][s] = part[(s * R + srow[i]) * Lay::QSTR + sq];
-      uk[i] = ust[srow[i] * T + sq];
+      uk[i] = ukeep[i];
       if (XMODE == kXLds && SECOND) xl[i] = xlds[oxl[i] + jT];
     }
   };
@@ -631,8 +637,9 @@ hipError_t dispatch_dtype(const ScanPlan &plan, const ScanArgs &a, hipStream_t s
 
 size_t lds_bytes(int split, int dirs, int T, int xmode, int64_t L, bool conv) {
   const int R = 64 / split;
-  size_t f = static_cast<size_t>(dirs) * (R * (2 * T + 2) + R * T + 32 * T + 64 * (T + 1) +
-                                          (conv ? R * (T + 4) : 0));
+  const size_t stage = R * (2 * T + 2) + 32 * T + (conv ? R * (T + 4) : 0);   // Layout::STAGE
+  const size_t part = 64 * (T + 1);                                            // Layout::PART
+  size_t f = static_cast<size_t>(dirs) * (stage > part ? stage : part);
   if (xmode == kXLds) f += static_cast<size_t>(R) * xchg_stride(L, T);
   return f * sizeof(float);
 }

@@ -86,15 +86,15 @@ def test_single_bf16():
 
 # ---------------------------------------------------------------- bidirectional
 # Shapes chosen to cover: one tile (joint midpoint), odd / even tile counts,
-# the LDS exchange with 8- and 4-step tiles, the global exchange (long L),
-# and both state splits (S = 4 on few row blocks, S = 2 on >= 512 blocks).
-# L = 456 is the longest sequence of the on-chip exchange (its LDS block is
-# 16 x 456 floats); 457 and 500 take the global exchange through a pool
-# buffer, 512 (fp32, L % 32 == 0) parks in `out` itself.
+# the LDS exchange (8-step tiles) and the global exchange (16-step tiles,
+# long L), with many and few row blocks.
+# L = 552 is the longest sequence of the on-chip exchange (its LDS block is
+# 16 x 552 floats); 553 and 600 take the global exchange through a pool
+# buffer, 576 (fp32, L % 32 == 0) parks in `out` itself.
 BIDIR_CASES = [
     (1, 1, 1), (2, 70, 2), (2, 70, 16), (2, 70, 77), (2, 130, 197), (2, 70, 300),
     (512, 64, 20), (512, 64, 197), (256, 128, 300),
-    (2, 40, 456), (2, 40, 457), (1, 33, 500), (2, 20, 512),
+    (2, 40, 456), (2, 40, 552), (2, 40, 553), (1, 33, 600), (2, 20, 576),
 ]
 
 
@@ -578,7 +578,9 @@ def test_fused_conv_single(L, reverse, zoh):
     assert_close(host(out), ref, FP32_TOL, "fused conv single")
 
 
-@pytest.mark.parametrize("L", [197, 600])
+# 520 / 521: the last on-chip-exchange length with the conv rows in LDS, and
+# the first global one
+@pytest.mark.parametrize("L", [197, 520, 521, 600])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_fused_conv_bidir(L, dtype):
     # both directions read the same content x through their own convolutions:
