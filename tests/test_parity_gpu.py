@@ -618,3 +618,40 @@ def test_fused_conv_equals_conv_then_scan(L):
     two = vm.vm_bidir_scan_fwd(f2, b2, z=z)
     torch.cuda.synchronize()
     assert torch.equal(fused, two)
+
+
+# ---------------------------------------------------------------- HIP graph replay
+def test_graph_replay_matches_eager():
+    # the benchmark replays captured steps: every replay, with eager work and
+    # synchronisations between replays, must equal the eager result exactly
+    _case("graph replay: bidir L197 + ES2D 13x10")
+    fwd, bwd, z = wl.bidir_inputs(2300, 4, 64, 197, device=DEV, perturb=True)
+    x, p = wl.es2d_inputs(2301, 2, 32, 13, 10, device=DEV)
+    Lg = vm.vm_atrous_group_len(13, 10)
+    out = torch.empty_like(fwd["u"])
+    s = torch.empty((2, 4, 32, Lg), device=DEV)
+    y = torch.empty((8, 32, Lg), device=DEV)
+    y2 = torch.empty((2, 32, 13, 10), device=DEV)
+
+    def step():
+        vm.vm_bidir_scan_fwd(fwd, bwd, z=z, out=out)
+        vm.vm_atrous_gather(x, out=s)
+        vm.vm_selective_scan_fwd(s.view(8, 32, Lg), **p, out=y)
+        vm.vm_atrous_scatter(y.view(2, 4, 32, Lg), 13, 10, out=y2)
+
+    step()
+    torch.cuda.synchronize()
+    want = (out.clone(), y2.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    other = wl.bidir_inputs(2302, 4, 64, 197, device=DEV)
+    for r in range(3):
+        out.fill_(float("nan"))
+        y2.fill_(float("nan"))
+        vm.vm_bidir_scan_fwd(other[0], other[1], z=other[2])      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want[0]), f"replay {r}: bidir differs"
+        assert torch.equal(y2, want[1]), f"replay {r}: ES2D differs"
