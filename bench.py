@@ -327,7 +327,8 @@ def build_step(cfg, seed, sets, dev, zoh=False, conv="none"):
 def load_traffic(source_hash, workload):
     """HBM bytes per step (the scan kernel; every kernel of the step for the
     multi-kernel workloads) from the committed counter summary, if it was
-    taken on the current kernel sources and this workload."""
+    taken on the current kernel sources and this workload (name plus any
+    "+zoh" / "+conv-..." variant suffix)."""
     path = os.path.join(PROFILE_DIR, "scan_kernel_counters.json")
     try:
         with open(path) as f:
@@ -372,14 +373,24 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # The timed region is K steps.  Workloads whose steps allocate no
-    # temporary memory are captured once in a HIP graph and replayed, which
-    # removes the per-call host overhead between launches; the kernel time is
-    # then the replay's HIP-event time over K (launches back to back on the
-    # replay stream).  Eager steps get HIP events around every launch, on the
-    # launch stream.
+    # Kernel time (the roofline's): K eager steps with HIP events around every
+    # launch, on the launch stream.  Whole-job time (value, ms_per_step): the
+    # same K steps; workloads whose steps allocate no temporary memory are
+    # captured once in a HIP graph and replayed, which removes the per-call
+    # host overhead between launches, the others are these eager steps.
     use_graph = info.pop("graphable", False) and not args.no_graph
     stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
     if use_graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
@@ -387,26 +398,10 @@ def main():
                 step(i)
         graph.replay()                                  # one untimed replay
         torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
-        ev0.record(stream)
         graph.replay()
-        ev1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        launch_ms = ev0.elapsed_time(ev1) / args.steps
-    else:
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            starts[i].record(stream)
-            step(i)
-            ends[i].record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        launch_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
     info["launch"] = "hip-graph" if use_graph else "eager"
 
     ms_per_step = 1e3 * wall / args.steps
@@ -414,7 +409,8 @@ def main():
     achieved_gbs = nbytes / (launch_ms * 1e-3) / 1e9
     achieved_tslots = slots / (launch_ms * 1e-3) / 1e12
     src_hash = kernel_source_hash()
-    traffic = load_traffic(src_hash, info["workload"])
+    variant = ("+zoh" if args.zoh else "") + (f"+conv-{args.conv}" if args.conv != "none" else "")
+    traffic = load_traffic(src_hash, info["workload"] + variant)
     hbm = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
     alu = {"bound": "alu", "achieved": round(achieved_tslots, 2), "peak": round(VALU_PEAK_TSLOTS, 2),
