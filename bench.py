@@ -208,10 +208,13 @@ def build_step(cfg, seed, sets, dev, zoh=False, conv="none"):
             y = vm.vm_selective_scan_fwd(s.view(4 * w.batch, w.dim, Lg), **p, out=ys[i % sets], zoh=zoh)
             vm.vm_atrous_scatter(y.view(w.batch, 4, w.dim, Lg), H, W, out=outs[i % sets])
 
+        # algorithmic bytes of the ES2D step: x read and y written once, plus
+        # the scan's delta, B, C and parameters (the gathered u streams and the
+        # scan's output streams are intermediates of the three launches)
         plane = w.batch * w.dim * H * W * 4
         streams_b = w.batch * 4 * w.dim * Lg * 4
         scan_b = algorithmic_bytes_scan(4 * w.batch, w.dim, Lg, N, 4, 1, False)
-        nbytes = (plane + streams_b) + scan_b + (streams_b + plane)
+        nbytes = scan_b - 2 * streams_b + 2 * plane
         tokens = w.batch * w.dim * H * W
         slots = 4 * w.batch * w.dim * Lg * N * SLOTS_PER_STATE_STEP
         info = dict(workload=f"{w.name}@{H}x{W}", batch=w.batch, dim=w.dim, height=H, width=W,
