@@ -348,7 +348,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the scan shards by batch rows with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(the scan shards by batch rows with no exchange)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -59,7 +59,7 @@ def load_library():
         if _lib is None:
             if not os.path.exists(LIB_PATH):
                 raise RuntimeError(f"{LIB_PATH} is not built; run selective_scan_fwd_amd.build.build() "
-                                   "(or __graft_entry__.build()) first")
+                                   "first")
             lib = ctypes.CDLL(LIB_PATH)
             P, I64, I, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
             D = ctypes.POINTER(VmScanDir)
