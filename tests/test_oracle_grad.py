@@ -1,0 +1,91 @@
+"""Pins for the gradient oracle (no GPU): its forward equals the C oracle's,
+and every gradient it returns equals a central finite difference of the C
+oracle's forward (an independent implementation)."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import grad as og
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _dir(rng, batch, dim, L, N):
+    return dict(u=rng.standard_normal((batch, dim, L)),
+                delta=rng.standard_normal((batch, dim, L)) * 0.5,
+                A=-rng.uniform(0.2, 2.0, size=(dim, N)),
+                B=rng.standard_normal((batch, N, L)),
+                C=rng.standard_normal((batch, N, L)),
+                D=rng.standard_normal(dim),
+                delta_bias=rng.uniform(-1.0, 0.5, size=dim))
+
+
+def _fd(f, p, key, eps=1e-6):
+    """Central differences of the scalar f(p) with respect to p[key]."""
+    base = p[key]
+    g = np.zeros_like(base)
+    it = np.nditer(base, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        hi, lo = base.copy(), base.copy()
+        hi[i] += eps
+        lo[i] -= eps
+        g[i] = (f(dict(p, **{key: hi})) - f(dict(p, **{key: lo}))) / (2 * eps)
+    return g
+
+
+def _check(got, want, what):
+    scale = max(1.0, float(np.max(np.abs(want))))
+    err = float(np.max(np.abs(got - want)))
+    assert err <= 2e-7 * scale, f"{what}: max abs error {err:.3e} (scale {scale:.2e})"
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("softplus", [True, False])
+def test_single_grad_matches_finite_differences(reverse, gated, softplus):
+    rng = _rng(80 + 4 * reverse + 2 * gated + softplus)
+    p = _dir(rng, 2, 2, 5, 3)
+    if not softplus:
+        p["delta"] = rng.uniform(0.05, 0.6, size=p["delta"].shape)
+    z = rng.standard_normal(p["u"].shape) if gated else None
+    dout = rng.standard_normal(p["u"].shape)
+    g, dz, out = og.selective_scan_grad(p, dout, z=z, delta_softplus=softplus, reverse=reverse)
+    f = lambda q, zz=z: float(np.sum(dout * oracle.selective_scan(**q, z=zz, delta_softplus=softplus,
+                                                                   reverse=reverse)))
+    np.testing.assert_allclose(out, oracle.selective_scan(**p, z=z, delta_softplus=softplus,
+                                                          reverse=reverse), rtol=0, atol=1e-12)
+    for k in ("u", "delta", "A", "B", "C", "D", "delta_bias"):
+        _check(g[k], _fd(f, p, k), k)
+    if gated:
+        _check(dz, _fd(lambda q: f(p, q["z"]), dict(z=z), "z"), "z")
+
+
+def test_bidir_grad_matches_finite_differences():
+    rng = _rng(90)
+    f_, b_ = _dir(rng, 1, 2, 6, 3), _dir(rng, 1, 2, 6, 3)
+    z = rng.standard_normal(f_["u"].shape)
+    dout = rng.standard_normal(f_["u"].shape)
+    gf, gb, dz, out = og.bidir_scan_grad(f_, b_, dout, z=z, combine_scale=0.5)
+    fn = lambda ff, bb, zz=z: float(np.sum(dout * oracle.bidir_scan(ff, bb, z=zz, combine_scale=0.5)))
+    np.testing.assert_allclose(out, oracle.bidir_scan(f_, b_, z=z, combine_scale=0.5), rtol=0, atol=1e-12)
+    for k in ("u", "delta", "A", "B", "C", "D", "delta_bias"):
+        _check(gf[k], _fd(lambda q: fn(q, b_), f_, k), "fwd " + k)
+        _check(gb[k], _fd(lambda q: fn(f_, q), b_, k), "bwd " + k)
+    _check(dz, _fd(lambda q: fn(f_, b_, q["z"]), dict(z=z), "z"), "z")
+
+
+def test_grad_of_skip_only_case():
+    # B = 0: the state stays 0, y = D u; so du = D * dout, dD = sum(dout * u),
+    # and nothing reaches delta, A, C (closed form, no finite differences)
+    rng = _rng(91)
+    p = _dir(rng, 2, 3, 4, 2)
+    p["B"] = np.zeros_like(p["B"])
+    dout = rng.standard_normal(p["u"].shape)
+    g, _, _ = og.selective_scan_grad(p, dout)
+    np.testing.assert_allclose(g["u"], p["D"][None, :, None] * dout, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(g["D"], (dout * p["u"]).sum(axis=(0, 2)), rtol=0, atol=1e-13)
+    for k in ("delta", "A", "C", "delta_bias"):
+        assert np.all(g[k] == 0.0), k
