@@ -39,6 +39,8 @@ SLOTS_PER_STATE_STEP = 6         # dt*A, exp (2 slots), dt*u*B, state fma, reado
 # released recurrence's work, not to the longer zero-order-hold coefficient)
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["selective_scan_fwd_amd/csrc/scan_kernel.hip",
+                  "selective_scan_fwd_amd/csrc/scan_bwd.hip",
+                  "selective_scan_fwd_amd/csrc/scan_device.h",
                   "selective_scan_fwd_amd/csrc/layout_kernels.hip",
                   "selective_scan_fwd_amd/csrc/vm_internal.h"]
 

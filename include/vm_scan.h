@@ -274,6 +274,55 @@ int vm_ss2d_scan_fwd(const vm_scan_dir *dirs, const void *u, const void *z,
                      int64_t dstate, int dtype, int options,
                      void *stream);
 
+/*
+ * Gradients of one scan direction (fp32 device buffers, owned by the
+ * caller).  dB and dC are dense [batch, dstate, seqlen] whatever the layout
+ * of B and C; ddelta_bias may be NULL (not computed).
+ */
+typedef struct vm_scan_grad {
+  float *du;           /* [batch, dim, seqlen] */
+  float *ddelta;       /* [batch, dim, seqlen] */
+  float *dA;           /* [dim, dstate]        */
+  float *dB;           /* [batch, dstate, seqlen] */
+  float *dC;           /* [batch, dstate, seqlen] */
+  float *dD;           /* [dim]                */
+  float *ddelta_bias;  /* [dim] or NULL        */
+} vm_scan_grad;
+
+/*
+ * Backward pass of vm_selective_scan_fwd: the gradients of
+ * L = sum(dout * out) with respect to every input, for the same arguments
+ * (the pages pin the backward pass only as automatic differentiation of the
+ * scan loop, [Vim] "A state retains, writes, and reads" and implementation
+ * row 4; the adjoint recurrence it implies is g_t = C_t dy_t + a_{t+1} g_{t+1}).
+ *   dout [batch, dim, seqlen]; g: the gradients (see vm_scan_grad);
+ *   dz [batch, dim, seqlen]: required exactly when z is given.
+ * VM_F32 only, and the released recurrence only (options without VM_ZOH),
+ * no fused conv (VM_ERR_UNSUPPORTED otherwise).  Gradient buffers must not
+ * overlap any input or each other (VM_ERR_ALIAS).  Sums over batch rows (dA,
+ * dD, ddelta_bias) and over channels (dB, dC) are formed from per-block
+ * partials in a fixed order, so results are deterministic.
+ * Temporary memory: state checkpoints ([batch * dim, seqlen / 8, 16] fp32),
+ * the partials ([dim / 16, batch, dstate, seqlen] fp32 for each of dB, dC)
+ * and, with z, the recomputed forward output and dy.
+ */
+int vm_selective_scan_bwd(const vm_scan_dir *p, const void *z,
+                          const void *dout, const vm_scan_grad *g, void *dz,
+                          int64_t batch, int64_t dim, int64_t seqlen,
+                          int64_t dstate, int dtype, int options, int reverse,
+                          void *stream);
+
+/*
+ * Backward pass of vm_bidir_scan_fwd: gf and gb receive the gradients of the
+ * forward and backward directions' inputs, dz (required when z is given) the
+ * gate's.  The same limits and temporary memory as vm_selective_scan_bwd.
+ */
+int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
+                      const void *z, const void *dout, float combine_scale,
+                      const vm_scan_grad *gf, const vm_scan_grad *gb, void *dz,
+                      int64_t batch, int64_t dim, int64_t seqlen,
+                      int64_t dstate, int dtype, int options, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,7 +10,8 @@ library is missing or fails to load, every call raises.
 Names and argument order follow the C ABI:
   vm_selective_scan_fwd, vm_bidir_scan_fwd, vm_atrous_gather,
   vm_atrous_scatter, vm_pool_scan_repeat, vm_ss2d_scan_fwd,
-  vm_causal_conv1d_silu, vm_atrous_group_len.
+  vm_causal_conv1d_silu, vm_selective_scan_bwd, vm_bidir_scan_bwd,
+  vm_atrous_group_len.
 """
 from __future__ import annotations
 
@@ -31,7 +32,7 @@ STATUS_NAMES = {0: "VM_OK", 1: "VM_ERR_NULL", 2: "VM_ERR_SHAPE", 3: "VM_ERR_DTYP
 
 EXPORTED = ("vm_status_string", "vm_version", "vm_selective_scan_fwd", "vm_bidir_scan_fwd",
             "vm_atrous_group_len", "vm_atrous_gather", "vm_atrous_scatter", "vm_pool_scan_repeat",
-            "vm_ss2d_scan_fwd", "vm_causal_conv1d_silu")
+            "vm_ss2d_scan_fwd", "vm_causal_conv1d_silu", "vm_selective_scan_bwd", "vm_bidir_scan_bwd")
 
 
 class VmScanDir(ctypes.Structure):
@@ -40,6 +41,11 @@ class VmScanDir(ctypes.Structure):
                 ("B", ctypes.c_void_p), ("C", ctypes.c_void_p), ("D", ctypes.c_void_p),
                 ("delta_bias", ctypes.c_void_p), ("bc_stride", ctypes.c_int64),
                 ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p)]
+
+
+class VmScanGrad(ctypes.Structure):
+    """struct vm_scan_grad (one direction's gradient buffers)."""
+    _fields_ = [(k, ctypes.c_void_p) for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "ddelta_bias")]
 
 
 class VmError(RuntimeError):
@@ -76,9 +82,12 @@ def load_library():
             lib.vm_pool_scan_repeat.argtypes = [D, D, P, F, P, I64, I64, I64, I64, I64, I, I, I, P]
             lib.vm_ss2d_scan_fwd.argtypes = [D, P, P, F, P, I64, I64, I64, I64, I64, I, I, P]
             lib.vm_causal_conv1d_silu.argtypes = [P, P, P, P, I64, I64, I64, I, I, P]
+            G = ctypes.POINTER(VmScanGrad)
+            lib.vm_selective_scan_bwd.argtypes = [D, P, P, G, P, I64, I64, I64, I64, I, I, I, P]
+            lib.vm_bidir_scan_bwd.argtypes = [D, D, P, P, F, G, G, P, I64, I64, I64, I64, I, I, P]
             for name in ("vm_selective_scan_fwd", "vm_bidir_scan_fwd", "vm_atrous_gather",
                          "vm_atrous_scatter", "vm_pool_scan_repeat", "vm_ss2d_scan_fwd",
-                         "vm_causal_conv1d_silu"):
+                         "vm_causal_conv1d_silu", "vm_selective_scan_bwd", "vm_bidir_scan_bwd"):
                 getattr(lib, name).restype = I
             _lib = lib
     return _lib
@@ -250,6 +259,61 @@ def vm_causal_conv1d_silu(x, w, bias=None, reverse=False, out=None):
     return out
 
 
+def _grad_set(p, batch, dim, L, N, device, with_bias):
+    f = lambda *shape: torch.empty(shape, dtype=torch.float32, device=device)
+    g = dict(u=f(batch, dim, L), delta=f(batch, dim, L), A=f(dim, N), B=f(batch, N, L),
+             C=f(batch, N, L), D=f(dim), delta_bias=f(dim) if with_bias else None)
+    s = VmScanGrad(g["u"].data_ptr(), g["delta"].data_ptr(), g["A"].data_ptr(), g["B"].data_ptr(),
+                   g["C"].data_ptr(), g["D"].data_ptr(),
+                   g["delta_bias"].data_ptr() if with_bias else None)
+    return s, g
+
+
+def vm_selective_scan_bwd(p, dout, z=None, delta_softplus=True, reverse=False):
+    """Gradients of sum(dout * vm_selective_scan_fwd(**p, z=z, ...)).  p: dict
+    u, delta, A, B, C, D, delta_bias (fp32).  Returns (grads, dz): grads has
+    the keys of p (dB, dC dense [batch, N, L]); dz is None without z."""
+    u = p["u"]
+    batch, dim, L = u.shape
+    N = p["A"].shape[-1]
+    d, keep = _direction(p, batch, dim, (batch, dim, L), L, N, torch.float32, u.device, "p")
+    _dev(dout, "dout", torch.float32, u.shape, u.device)
+    if z is not None:
+        _dev(z, "z", torch.float32, u.shape, u.device)
+    gs, g = _grad_set(p, batch, dim, L, N, u.device, p.get("delta_bias") is not None)
+    dz = torch.empty_like(u) if z is not None else None
+    with torch.cuda.device(u.device):
+        st = load_library().vm_selective_scan_bwd(ctypes.byref(d), _ptr(z), _ptr(dout), ctypes.byref(gs),
+                                                  _ptr(dz), batch, dim, L, N, VM_F32,
+                                                  _options(delta_softplus, False), int(bool(reverse)),
+                                                  _stream(u.device))
+    _check(st, "vm_selective_scan_bwd")
+    return g, dz
+
+
+def vm_bidir_scan_bwd(fwd, bwd, dout, z=None, combine_scale=1.0, delta_softplus=True):
+    """Gradients of sum(dout * vm_bidir_scan_fwd(fwd, bwd, z, combine_scale)).
+    Returns (grads of fwd, grads of bwd, dz)."""
+    u = fwd["u"]
+    batch, dim, L = u.shape
+    N = fwd["A"].shape[-1]
+    df, kf = _direction(fwd, batch, dim, (batch, dim, L), L, N, torch.float32, u.device, "fwd")
+    db, kb = _direction(bwd, batch, dim, (batch, dim, L), L, N, torch.float32, u.device, "bwd")
+    _dev(dout, "dout", torch.float32, u.shape, u.device)
+    if z is not None:
+        _dev(z, "z", torch.float32, u.shape, u.device)
+    gsf, gf = _grad_set(fwd, batch, dim, L, N, u.device, fwd.get("delta_bias") is not None)
+    gsb, gb = _grad_set(bwd, batch, dim, L, N, u.device, bwd.get("delta_bias") is not None)
+    dz = torch.empty_like(u) if z is not None else None
+    with torch.cuda.device(u.device):
+        st = load_library().vm_bidir_scan_bwd(ctypes.byref(df), ctypes.byref(db), _ptr(z), _ptr(dout),
+                                              float(combine_scale), ctypes.byref(gsf), ctypes.byref(gsb),
+                                              _ptr(dz), batch, dim, L, N, VM_F32,
+                                              _options(delta_softplus, False), _stream(u.device))
+    _check(st, "vm_bidir_scan_bwd")
+    return gf, gb, dz
+
+
 def vm_atrous_group_len(height: int, width: int) -> int:
     n = int(load_library().vm_atrous_group_len(int(height), int(width)))
     if n < 0:
@@ -346,5 +410,6 @@ def vm_ss2d_scan_fwd(u, dirs, z=None, combine_scale=1.0, delta_softplus=True, ou
 
 
 __all__ = ["vm_selective_scan_fwd", "vm_bidir_scan_fwd", "vm_atrous_gather", "vm_atrous_scatter",
-           "vm_pool_scan_repeat", "vm_ss2d_scan_fwd", "vm_causal_conv1d_silu", "vm_atrous_group_len", "vm_status_string", "vm_version",
+           "vm_pool_scan_repeat", "vm_ss2d_scan_fwd", "vm_causal_conv1d_silu",
+           "vm_selective_scan_bwd", "vm_bidir_scan_bwd", "VmScanGrad", "vm_atrous_group_len", "vm_status_string", "vm_version",
            "VmScanDir", "VmError", "load_library", "LIB_PATH", "EXPORTED"]

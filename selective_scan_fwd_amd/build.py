@@ -9,7 +9,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvmscan.so")
-SOURCES = ["api.hip", "scan_kernel.hip", "layout_kernels.hip"]
+SOURCES = ["api.hip", "scan_kernel.hip", "scan_bwd.hip", "layout_kernels.hip"]
 
 # Packed fp32 VALU forms are turned off for all device code.
 HIPCC_FLAGS = [

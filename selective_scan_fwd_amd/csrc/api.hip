@@ -196,6 +196,95 @@ int launch_bidir(vmk::ScanArgs &a, bool bf16, Scratch &ws, hipStream_t s) {
   return hip_status(vmk::launch_scan(plan, a, bf16, s));
 }
 
+// Temporary memory and launches of one direction's backward pass after dy
+// is known: the kernel, then the reduction of its partial sums into g.
+struct BwdScratch {
+  float *ck = nullptr, *pA = nullptr, *pD = nullptr, *pbias = nullptr, *pB = nullptr, *pC = nullptr;
+  int get(Scratch &ws, int64_t batch, int64_t dim, int64_t L, int64_t dstate) {
+    int st = VM_OK;
+    const int64_t nrb = (dim + 15) / 16;
+    ck = ws.get(batch * dim * vmk::scan_bwd_tiles(L) * 16, &st);
+    pA = ws.get(batch * dim * 16, &st);
+    pD = ws.get(batch * dim, &st);
+    pbias = ws.get(batch * dim, &st);
+    pB = ws.get(nrb * batch * dstate * L, &st);
+    pC = ws.get(nrb * batch * dstate * L, &st);
+    return st;
+  }
+};
+
+int run_bwd(const vm_scan_dir *p, const float *dy, const vm_scan_grad *g, BwdScratch &bs,
+            int64_t batch, int64_t dim, int64_t L, int64_t dstate, int options, int reverse,
+            Scratch &ws, hipStream_t s) {
+  int st = VM_OK;
+  vmk::BwdArgs a = {};
+  a.dir = resolve_dir(p, batch, dstate, L, false, ws, s, &st);
+  if (st != VM_OK) return st;
+  a.dy = dy;
+  a.du = g->du;
+  a.ddelta = g->ddelta;
+  a.ck = bs.ck;
+  a.pA = bs.pA;
+  a.pD = bs.pD;
+  a.pbias = bs.pbias;
+  a.pB = bs.pB;
+  a.pC = bs.pC;
+  a.batch = batch;
+  a.dim = dim;
+  a.L = L;
+  a.dstate = static_cast<int>(dstate);
+  a.softplus = (options & VM_DELTA_SOFTPLUS) != 0;
+  a.reverse = reverse;
+  st = hip_status(vmk::launch_scan_bwd(a, s));
+  if (st != VM_OK) return st;
+  return hip_status(vmk::launch_scan_bwd_reduce(a, g->dA, g->dB, g->dC, g->dD, g->ddelta_bias, s));
+}
+
+// Checks of a gradient set: required pointers, no overlap with the inputs
+// (ins) or with the other outputs (outs, extended here).
+int check_grad(const vm_scan_grad *g, int64_t tok, int64_t bc, int64_t dim, int64_t dstate,
+               const std::vector<Span> &ins, std::vector<Span> &outs) {
+  if (g == nullptr || g->du == nullptr || g->ddelta == nullptr || g->dA == nullptr ||
+      g->dB == nullptr || g->dC == nullptr || g->dD == nullptr)
+    return VM_ERR_NULL;
+  const Span mine[] = {span(g->du, tok * 4), span(g->ddelta, tok * 4), span(g->dA, dim * dstate * 4),
+                       span(g->dB, bc * 4), span(g->dC, bc * 4), span(g->dD, dim * 4),
+                       span(g->ddelta_bias, dim * 4)};
+  for (const Span &m : mine) {
+    for (const Span &i : ins)
+      if (overlaps(m, i)) return VM_ERR_ALIAS;
+    for (const Span &o : outs)
+      if (overlaps(m, o)) return VM_ERR_ALIAS;
+    outs.push_back(m);
+  }
+  return VM_OK;
+}
+
+void dir_spans(const vm_scan_dir *p, int64_t tok, int64_t batch, int64_t L, int64_t dim,
+               int64_t dstate, std::vector<Span> &ins) {
+  const int64_t bc = bc_extent(batch, dstate, L, p->bc_stride);
+  const Span sp[] = {span(p->u, tok * 4), span(p->delta, tok * 4), span(p->A, dim * dstate * 4),
+                     span(p->B, bc * 4), span(p->C, bc * 4), span(p->D, dim * 4),
+                     span(p->delta_bias, dim * 4)};
+  ins.insert(ins.end(), sp, sp + 7);
+}
+
+// Shared checks of the backward entry points (fp32, released recurrence, no
+// fused conv; dz exactly when z).
+int check_bwd_common(int dtype, int options, int64_t batch, int64_t dim, int64_t L, int64_t dstate,
+                     const void *z, const void *dout, const void *dz, int64_t *tok, int64_t *bc) {
+  if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;
+  if (!options_ok(options)) return VM_ERR_FLAG;
+  if (!dims_ok({batch, dim, L}, tok) || dstate <= 0) return VM_ERR_SHAPE;
+  if (dtype != VM_F32 || (options & VM_ZOH) || dstate > 16) return VM_ERR_UNSUPPORTED;
+  if (!dims_ok({batch, dstate, L}, bc)) return VM_ERR_SHAPE;
+  // 32-bit offsets of the kernel's per-block checkpoints and partial sums
+  if (16 * 64 * vmk::scan_bwd_tiles(L) >= (int64_t{1} << 31) || 64 * L >= (int64_t{1} << 31))
+    return VM_ERR_UNSUPPORTED;
+  if (dout == nullptr || (z != nullptr && dz == nullptr)) return VM_ERR_NULL;
+  return VM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -482,6 +571,119 @@ int vm_ss2d_scan_fwd(const vm_scan_dir *dirs, const void *u, const void *z, floa
   if (st != VM_OK) return st;
   return hip_status(vmk::launch_ss2d_merge(yr, yc, z, out, batch * dim, height, width,
                                            combine_scale, bf16, s));
+}
+
+int vm_selective_scan_bwd(const vm_scan_dir *p, const void *z, const void *dout,
+                          const vm_scan_grad *g, void *dz, int64_t batch, int64_t dim,
+                          int64_t seqlen, int64_t dstate, int dtype, int options, int reverse,
+                          void *stream) {
+  int64_t tok = 0, bc = 0;
+  int st = check_bwd_common(dtype, options, batch, dim, seqlen, dstate, z, dout, dz, &tok, &bc);
+  if (st != VM_OK) return st;
+  if (!flag_ok(reverse)) return VM_ERR_FLAG;
+  st = check_dir(p, tok, tok, batch, seqlen, dim, dstate, 4, Span());
+  if (st != VM_OK) return st;
+  if (p->conv_w != nullptr) return VM_ERR_UNSUPPORTED;
+  std::vector<Span> ins, outs;
+  dir_spans(p, tok, batch, seqlen, dim, dstate, ins);
+  ins.push_back(span(z, tok * 4));
+  ins.push_back(span(dout, tok * 4));
+  st = check_grad(g, tok, bc, dim, dstate, ins, outs);
+  if (st != VM_OK) return st;
+  for (const Span &o : outs)
+    if (overlaps(span(dz, tok * 4), o)) return VM_ERR_ALIAS;
+  for (const Span &i : ins)
+    if (overlaps(span(dz, tok * 4), i)) return VM_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Scratch ws(s);
+  const float *dy = static_cast<const float *>(dout);
+  if (z != nullptr) {
+    // the ungated forward output, for dz, then dy = dout * SiLU(z)
+    float *y = ws.get(tok, &st);
+    float *dyb = ws.get(tok, &st);
+    if (st != VM_OK) return st;
+    vmk::ScanArgs a = {};
+    a.dir[0] = a.dir[1] = resolve_dir(p, batch, dstate, seqlen, false, ws, s, &st);
+    a.out = y;
+    a.batch = batch;
+    a.dim = dim;
+    a.L = seqlen;
+    a.dstate = static_cast<int>(dstate);
+    a.softplus = (options & VM_DELTA_SOFTPLUS) != 0;
+    a.reverse = reverse;
+    a.scale = 1.0f;
+    const vmk::ScanPlan plan = vmk::plan_scan(batch, dim, seqlen, a.dstate, 1, false);
+    if (!vmk::scan_offsets_fit(plan, a, false)) return VM_ERR_UNSUPPORTED;
+    st = hip_status(vmk::launch_scan(plan, a, false, s));
+    if (st == VM_OK)
+      st = hip_status(vmk::launch_gate_bwd(y, static_cast<const float *>(z), dy, dyb,
+                                           static_cast<float *>(dz), tok, 1.0f, s));
+    if (st != VM_OK) return st;
+    dy = dyb;
+  }
+  BwdScratch bs;
+  st = bs.get(ws, batch, dim, seqlen, dstate);
+  if (st != VM_OK) return st;
+  return run_bwd(p, dy, g, bs, batch, dim, seqlen, dstate, options, reverse, ws, s);
+}
+
+int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void *z,
+                      const void *dout, float combine_scale, const vm_scan_grad *gf,
+                      const vm_scan_grad *gb, void *dz, int64_t batch, int64_t dim,
+                      int64_t seqlen, int64_t dstate, int dtype, int options, void *stream) {
+  int64_t tok = 0, bc = 0;
+  int st = check_bwd_common(dtype, options, batch, dim, seqlen, dstate, z, dout, dz, &tok, &bc);
+  if (st != VM_OK) return st;
+  if (!std::isfinite(combine_scale)) return VM_ERR_UNSUPPORTED;
+  st = check_dir(fwd, tok, tok, batch, seqlen, dim, dstate, 4, Span());
+  if (st == VM_OK) st = check_dir(bwd, tok, tok, batch, seqlen, dim, dstate, 4, Span());
+  if (st != VM_OK) return st;
+  if (fwd->conv_w != nullptr || bwd->conv_w != nullptr) return VM_ERR_UNSUPPORTED;
+  std::vector<Span> ins, outs;
+  dir_spans(fwd, tok, batch, seqlen, dim, dstate, ins);
+  dir_spans(bwd, tok, batch, seqlen, dim, dstate, ins);
+  ins.push_back(span(z, tok * 4));
+  ins.push_back(span(dout, tok * 4));
+  st = check_grad(gf, tok, bc, dim, dstate, ins, outs);
+  if (st == VM_OK) st = check_grad(gb, tok, bc, dim, dstate, ins, outs);
+  if (st != VM_OK) return st;
+  for (const Span &o : outs)
+    if (overlaps(span(dz, tok * 4), o)) return VM_ERR_ALIAS;
+  for (const Span &i : ins)
+    if (overlaps(span(dz, tok * 4), i)) return VM_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Scratch ws(s);
+  // dy = s * dout * SiLU(z) reaches both directions; dz needs y_f + y_b,
+  // which the forward kernel recomputes ungated with s = 1
+  float *dy = ws.get(tok, &st);
+  float *y = z != nullptr ? ws.get(tok, &st) : nullptr;
+  if (st != VM_OK) return st;
+  if (z != nullptr) {
+    vmk::ScanArgs a = {};
+    a.dir[0] = resolve_dir(fwd, batch, dstate, seqlen, false, ws, s, &st);
+    a.dir[1] = resolve_dir(bwd, batch, dstate, seqlen, false, ws, s, &st);
+    if (st != VM_OK) return st;
+    a.out = y;
+    a.batch = batch;
+    a.dim = dim;
+    a.L = seqlen;
+    a.dstate = static_cast<int>(dstate);
+    a.softplus = (options & VM_DELTA_SOFTPLUS) != 0;
+    a.scale = 1.0f;
+    st = launch_bidir(a, false, ws, s);
+    if (st != VM_OK) return st;
+  }
+  st = hip_status(vmk::launch_gate_bwd(y, static_cast<const float *>(z),
+                                       static_cast<const float *>(dout), dy,
+                                       static_cast<float *>(dz), tok, combine_scale, s));
+  if (st != VM_OK) return st;
+  BwdScratch bs;
+  st = bs.get(ws, batch, dim, seqlen, dstate);
+  if (st == VM_OK) st = run_bwd(fwd, dy, gf, bs, batch, dim, seqlen, dstate, options, 0, ws, s);
+  if (st == VM_OK) st = run_bwd(bwd, dy, gb, bs, batch, dim, seqlen, dstate, options, 1, ws, s);
+  return st;
 }
 
 }  // extern "C"

@@ -1,0 +1,428 @@
+// Backward pass of the selective scan (one direction, fp32) for gfx950.
+//
+// Forward (Vision Mamba page, "A state retains, writes, and reads"): per
+// channel, from h = 0, h_t = a_t h_{t-1} + dt_t B_t u_t with a_t = exp(dt_t A),
+// y_t = sum_n C_t h_t + D u_t, dt = softplus(delta + bias).  Given dy = dL/dy,
+// the adjoint of the state runs against the visit order:
+//   g_t = C_t dy_t + a_{t+1} g_{t+1}                     (g = dL/dh_t)
+// and the gradients collect along it:
+//   dC_t += dy_t h_t          dB_t += g_t dt_t u_t       (summed over channels)
+//   dA   += g_t a_t h_{t-1} dt_t                          (summed over batch)
+//   du_t  = dt_t sum_n g_t B_t + D dy_t
+//   ddt_t = u_t sum_n g_t B_t + sum_n g_t a_t h_{t-1} A
+//   ddelta_t = ddt_t sigmoid(delta_t + bias) (softplus), dbias, dD summed.
+// a_t h_{t-1} is formed as a product from the kept states (the tile's
+// checkpoint for its first step), not as h_t - dt_t B_t u_t, which would
+// leave rounding residue where h_{t-1} is exactly zero.
+//
+// Work decomposition: as the forward kernel, one wave covers 16 channels of
+// one batch row, a lane holding 4 of a channel's 16 states.  Pass 1 runs the
+// state forward over the sequence and stores the state at every tile start
+// (checkpoints).  Pass 2 visits the tiles in reverse: it restarts the state
+// from the tile's checkpoint, keeps the tile's states and decays in
+// registers, then runs the adjoint back through the tile.  Per-channel sums
+// (du, ddelta) meet in LDS like the forward's partial sums; the sums over
+// channels (dB, dC) are reduced over the wave's 16 channels in LDS and
+// written as one partial per channel block; the sums over batch rows (dA, dD,
+// dbias) are written as one partial per batch row.  A second kernel adds the
+// partials.
+#include "scan_device.h"
+#include "vm_internal.h"
+
+namespace vmk {
+namespace {
+
+constexpr int kNS = 4;                 // states per lane
+constexpr int kR = 16;                 // channels per wave
+
+template <int T>
+struct BwdLayout {
+  static constexpr int PST = 4 * T + 4;               // (dt, dt u, dy, -) per step, per row
+  static constexpr int PREP = kR * PST;
+  static constexpr int BC = 32 * T;                   // B in slots 0..15, C in 16..31
+  static constexpr int QSTR = T + 1;
+  static constexpr int PART = 2 * 64 * QSTR;          // per-lane sums of g B and g a h A
+  static constexpr int RED = 2 * 16 * T * kR;         // dC, dB contributions [2][n][q][r]
+  static constexpr int TOTAL = PREP + BC + PART + RED;
+};
+
+// The tile's states and decays stay in registers (64 VGPRs with 8-step
+// tiles); the LDS area (24 KB) allows six workgroups per CU, so the register
+// budget is set for two waves per SIMD.
+template <int T>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+scan_bwd_kernel(const BwdArgs p) {
+  using Lay = BwdLayout<T>;
+  constexpr int PE = kR * T / 64;      // staged elements per lane per tile
+  constexpr int BQ = T / 4;            // B (and C) loads per lane per tile
+  extern __shared__ float smem[];
+  float *const prep = smem;                       // [R][PST]
+  float *const bcs = prep + Lay::PREP;            // [T][32]
+  float *const part = bcs + Lay::BC;              // [2][64][QSTR]
+  float *const red = part + Lay::PART;            // [2][16][T][R]
+
+  const int lane = threadIdx.x;
+  const int sp = lane / kR, r = lane % kR;
+  const bool rev = p.reverse != 0;
+  const int64_t dim = p.dim;
+  const int L = static_cast<int>(p.L);
+  const int nrb = static_cast<int>((dim + kR - 1) / kR);
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int b = blk / nrb;
+  const int rb = blk - b * nrb;
+  const int d0 = rb * kR;
+  const int rows = static_cast<int>(dim - d0 < kR ? dim - d0 : kR);
+  const int nt = (L + T - 1) / T;
+  const int dstate = p.dstate;
+  const DirPtrs P = p.dir;
+
+  const int64_t rowbase = (static_cast<int64_t>(b) * dim + d0) * L;
+  const uint32_t slab = static_cast<uint32_t>(rows) * static_cast<uint32_t>(L) * 4u;
+  const Rsrc rU = make_rsrc(static_cast<const float *>(P.u) + rowbase, slab);
+  const Rsrc rDl = make_rsrc(static_cast<const float *>(P.delta) + rowbase, slab);
+  const Rsrc rDy = make_rsrc(p.dy + rowbase, slab);
+  const Rsrc rDu = make_rsrc(p.du + rowbase, slab);
+  const Rsrc rDd = make_rsrc(p.ddelta + rowbase, slab);
+  const uint32_t bcext = (static_cast<uint32_t>(dstate - 1) * static_cast<uint32_t>(P.bsn) +
+                          static_cast<uint32_t>(L - 1) * static_cast<uint32_t>(P.bst) + 1) * 4u;
+  const Rsrc rB = make_rsrc(static_cast<const float *>(P.B) + static_cast<int64_t>(b) * P.bsb, bcext);
+  const Rsrc rC = make_rsrc(static_cast<const float *>(P.C) + static_cast<int64_t>(b) * P.bsb, bcext);
+  const Rsrc rA = make_rsrc(P.A + static_cast<int64_t>(d0) * dstate,
+                            static_cast<uint32_t>(rows * dstate) * 4u);
+  const Rsrc rDp = make_rsrc(P.D + d0, static_cast<uint32_t>(rows) * 4u);
+  const Rsrc rBias = make_rsrc(P.bias != nullptr ? P.bias + d0 : nullptr,
+                               P.bias != nullptr ? static_cast<uint32_t>(rows) * 4u : 0u);
+  // checkpoints of this block's rows: [row][tile][16 states]
+  const Rsrc rCk = make_rsrc(p.ck + (static_cast<int64_t>(b) * dim + d0) * nt * 16,
+                             static_cast<uint32_t>(rows * nt) * 64u);
+  // partial sums over channels of this block: [n][L] per quantity
+  const int64_t pbc = (static_cast<int64_t>(rb) * p.batch + b) * dstate * L;
+  const uint32_t pbc_bytes = static_cast<uint32_t>(dstate * L) * 4u;
+  const Rsrc rPB = make_rsrc(p.pB + pbc, pbc_bytes);
+  const Rsrc rPC = make_rsrc(p.pC + pbc, pbc_bytes);
+
+  // ---- state role: channel d0 + r, states n0 .. n0 + 3
+  const int n0 = sp * kNS;
+  float A2[kNS], An[kNS];
+#pragma unroll
+  for (int j = 0; j < kNS; ++j) {
+    const int n = n0 + j;
+    An[j] = bload<float>(rA, n < dstate ? static_cast<uint32_t>(r * dstate + n) * 4u : kOob);
+    A2[j] = An[j] * kLog2e;
+  }
+  const int rl = lane & 15;
+  const int bc_slot = rl < kNS ? n0 + rl : (rl < 2 * kNS ? 16 + n0 + rl - kNS : 0);
+
+  // ---- staging role: element i = (row srow[i], visit position sq)
+  const int sq = lane % T;
+  const int tq = rev ? T - 1 - sq : sq;
+  int srow[PE];
+  uint32_t ob[PE];
+  float sbias[PE], sD[PE], accD[PE], accB[PE];
+#pragma unroll
+  for (int i = 0; i < PE; ++i) {
+    srow[i] = lane / T + i * (64 / T);
+    ob[i] = (static_cast<uint32_t>(srow[i]) * static_cast<uint32_t>(L) + tq) * 4u;
+    sbias[i] = bload<float>(rBias, static_cast<uint32_t>(srow[i]) * 4u);
+    sD[i] = bload<float>(rDp, static_cast<uint32_t>(srow[i]) * 4u);
+    accD[i] = 0.0f;
+    accB[i] = 0.0f;
+  }
+  const int n_bc = lane % 16;
+  uint32_t bo[BQ];
+#pragma unroll
+  for (int i = 0; i < BQ; ++i) {
+    const int q = lane / 16 + 4 * i;
+    const int qt = rev ? T - 1 - q : q;
+    bo[i] = n_bc < dstate ? (static_cast<uint32_t>(n_bc) * static_cast<uint32_t>(P.bsn) +
+                             static_cast<uint32_t>(qt) * static_cast<uint32_t>(P.bst)) * 4u
+                          : kOob;
+  }
+  const uint32_t bst_bytes = static_cast<uint32_t>(P.bst) * 4u;
+  const bool sp_on = p.softplus != 0;
+
+  auto tile_of = [&](int k) { return rev ? nt - 1 - k : k; };
+  // Stages tile j: (dt, dt u, dy) per element and B (and C) per step.  Steps
+  // past L and rows past dim read 0.  Returns the element values the combine
+  // of this tile needs in registers.
+  float eu[PE], edt[PE], edy[PE], ex[PE];
+  auto stage = [&](int j, bool with_c) {
+    const int jT = j * T;
+    const bool in_seq = tq < L - jT;
+#pragma unroll
+    for (int i = 0; i < PE; ++i) {
+      const uint32_t o = pin_u(in_seq ? ob[i] + static_cast<uint32_t>(jT) * 4u : kOob);
+      const float uv = bload<float>(rU, o);
+      const float x = bload<float>(rDl, o) + sbias[i];
+      const float dyv = with_c ? bload<float>(rDy, o) : 0.0f;
+      const float dtv = sp_on ? softplus_f(x) : x;
+      eu[i] = uv;
+      edt[i] = dtv;
+      edy[i] = dyv;
+      ex[i] = x;
+      *reinterpret_cast<float4 *>(prep + srow[i] * Lay::PST + 4 * sq) =
+          make_float4(dtv, dtv * uv, dyv, 0.0f);
+    }
+    const uint32_t tb = static_cast<uint32_t>(jT) * bst_bytes;
+#pragma unroll
+    for (int i = 0; i < BQ; ++i) {
+      float *const q = bcs + (lane / 16 + 4 * i) * 32 + n_bc;
+      q[0] = bload<float>(rB, bo[i] + tb);
+      q[16] = with_c ? bload<float>(rC, bo[i] + tb) : 0.0f;
+    }
+  };
+
+  // ---- pass 1: states at every tile start, in visit order
+  float h[kNS];
+#pragma unroll
+  for (int j = 0; j < kNS; ++j) h[j] = 0.0f;
+  const uint32_t ck_lane = static_cast<uint32_t>(r * nt) * 64u + static_cast<uint32_t>(n0) * 4u;
+  for (int k = 0; k < nt; ++k) {
+    const int j = tile_of(k);
+#pragma unroll
+    for (int jn = 0; jn < kNS; ++jn)
+      bstore<float>(rCk, ck_lane + static_cast<uint32_t>(j) * 64u + 4u * jn, h[jn]);
+    stage(j, false);
+#pragma unroll
+    for (int q = 0; q < T; ++q) {
+      const float4 pq = *reinterpret_cast<const float4 *>(prep + r * Lay::PST + 4 * q);
+      const float bv = bcs[q * 32 + bc_slot];
+#pragma unroll
+      for (int jn = 0; jn < kNS; ++jn) {
+        const float a = hw_exp2(pq.x * A2[jn]);
+        float w;
+        switch (jn) {
+          case 0: w = pq.y * row_bcast<0>(bv); break;
+          case 1: w = pq.y * row_bcast<1>(bv); break;
+          case 2: w = pq.y * row_bcast<2>(bv); break;
+          default: w = pq.y * row_bcast<3>(bv); break;
+        }
+        h[jn] = __builtin_fmaf(a, h[jn], w);
+      }
+    }
+  }
+
+  // ---- pass 2: tiles in reverse visit order
+  float gn[kNS], dA[kNS];
+#pragma unroll
+  for (int j = 0; j < kNS; ++j) {
+    gn[j] = 0.0f;
+    dA[j] = 0.0f;
+  }
+  for (int k = nt - 1; k >= 0; --k) {
+    const int j = tile_of(k);
+    stage(j, true);
+    float hc[kNS], h0[kNS];
+#pragma unroll
+    for (int jn = 0; jn < kNS; ++jn) {
+      hc[jn] = bload<float>(rCk, ck_lane + static_cast<uint32_t>(j) * 64u + 4u * jn);
+      h0[jn] = hc[jn];
+    }
+    // recompute the tile's states and decays
+    float hs[T][kNS], as[T][kNS];
+#pragma unroll
+    for (int q = 0; q < T; ++q) {
+      const float4 pq = *reinterpret_cast<const float4 *>(prep + r * Lay::PST + 4 * q);
+      const float bv = bcs[q * 32 + bc_slot];
+#pragma unroll
+      for (int jn = 0; jn < kNS; ++jn) {
+        const float a = hw_exp2(pq.x * A2[jn]);
+        float w;
+        switch (jn) {
+          case 0: w = pq.y * row_bcast<0>(bv); break;
+          case 1: w = pq.y * row_bcast<1>(bv); break;
+          case 2: w = pq.y * row_bcast<2>(bv); break;
+          default: w = pq.y * row_bcast<3>(bv); break;
+        }
+        hc[jn] = __builtin_fmaf(a, hc[jn], w);
+        hs[q][jn] = hc[jn];
+        as[q][jn] = a;
+      }
+    }
+    // adjoint back through the tile
+#pragma unroll
+    for (int q = T - 1; q >= 0; --q) {
+      const float4 pq = *reinterpret_cast<const float4 *>(prep + r * Lay::PST + 4 * q);
+      const float bv = bcs[q * 32 + bc_slot];
+      float sgB = 0.0f, sqA = 0.0f;
+#pragma unroll
+      for (int jn = 0; jn < kNS; ++jn) {
+        float Bb, Cb;
+        switch (jn) {
+          case 0: Bb = row_bcast<0>(bv); Cb = row_bcast<kNS + 0>(bv); break;
+          case 1: Bb = row_bcast<1>(bv); Cb = row_bcast<kNS + 1>(bv); break;
+          case 2: Bb = row_bcast<2>(bv); Cb = row_bcast<kNS + 2>(bv); break;
+          default: Bb = row_bcast<3>(bv); Cb = row_bcast<kNS + 3>(bv); break;
+        }
+        const float g = __builtin_fmaf(Cb, pq.z, gn[jn]);
+        const int n = n0 + jn;
+        red[((0 * 16 + n) * T + q) * kR + r] = pq.z * hs[q][jn];     // dC
+        red[((1 * 16 + n) * T + q) * kR + r] = g * pq.y;             // dB
+        sgB = __builtin_fmaf(g, Bb, sgB);
+        const float ah = as[q][jn] * (q > 0 ? hs[q > 0 ? q - 1 : 0][jn] : h0[jn]);   // a_t h_{t-1}
+        const float gq = g * ah;
+        dA[jn] = __builtin_fmaf(gq, pq.x, dA[jn]);
+        sqA = __builtin_fmaf(gq, An[jn], sqA);
+        gn[jn] = as[q][jn] * g;
+      }
+      part[(0 * 64 + lane) * Lay::QSTR + q] = sgB;
+      part[(1 * 64 + lane) * Lay::QSTR + q] = sqA;
+    }
+    // per element: du, ddelta (the four state groups of the channel summed)
+    const int jT = j * T;
+    const bool in_seq = tq < L - jT;
+#pragma unroll
+    for (int i = 0; i < PE; ++i) {
+      float gB = 0.0f, gA = 0.0f;
+#pragma unroll
+      for (int s = 0; s < 64 / kR; ++s) {
+        gB += part[(0 * 64 + s * kR + srow[i]) * Lay::QSTR + sq];
+        gA += part[(1 * 64 + s * kR + srow[i]) * Lay::QSTR + sq];
+      }
+      const float du = __builtin_fmaf(edt[i], gB, sD[i] * edy[i]);
+      const float ddt = __builtin_fmaf(eu[i], gB, gA);
+      const float sig = hw_rcp(1.0f + hw_exp2(-ex[i] * kLog2e));
+      const float dd = sp_on ? ddt * sig : ddt;
+      const uint32_t o = pin_u(in_seq ? ob[i] + static_cast<uint32_t>(jT) * 4u : kOob);
+      bstore<float>(rDu, o, du);
+      bstore<float>(rDd, o, dd);
+      accD[i] = __builtin_fmaf(edy[i], eu[i], accD[i]);
+      accB[i] += dd;
+    }
+    // dB, dC: this block's sum over its 16 channels, per (n, step)
+#pragma unroll
+    for (int m = 0; m < 2 * 16 * T / 64; ++m) {
+      const int c = lane + 64 * m;                    // (which, n, q), q fastest
+      const int q = c % T, n = (c / T) % 16, which = c / (16 * T);
+      const float4 *src = reinterpret_cast<const float4 *>(red + ((which * 16 + n) * T + q) * kR);
+      float sum = 0.0f;
+#pragma unroll
+      for (int v = 0; v < kR / 4; ++v) {
+        const float4 x4 = src[v];
+        sum += (x4.x + x4.y) + (x4.z + x4.w);
+      }
+      const int t = jT + (rev ? T - 1 - q : q);
+      const uint32_t o = pin_u(t < L && n < dstate ? static_cast<uint32_t>(n * L + t) * 4u : kOob);
+      bstore<float>(which == 0 ? rPC : rPB, o, sum);
+    }
+  }
+
+  // ---- per batch row: dA, and dD, dbias (the T lanes of a channel summed)
+  const int64_t prow = static_cast<int64_t>(b) * dim + d0;
+  const Rsrc rPA = make_rsrc(p.pA + prow * 16, static_cast<uint32_t>(rows) * 64u);
+#pragma unroll
+  for (int jn = 0; jn < kNS; ++jn)
+    bstore<float>(rPA, static_cast<uint32_t>(r * 16 + n0 + jn) * 4u, dA[jn]);
+#pragma unroll
+  for (int i = 0; i < PE; ++i) {
+    part[srow[i] * Lay::QSTR + sq] = accD[i];
+    part[64 * Lay::QSTR + srow[i] * Lay::QSTR + sq] = accB[i];
+  }
+  if (lane < kR) {
+    float sD_ = 0.0f, sB_ = 0.0f;
+    for (int q = 0; q < T; ++q) {
+      sD_ += part[lane * Lay::QSTR + q];
+      sB_ += part[64 * Lay::QSTR + lane * Lay::QSTR + q];
+    }
+    const Rsrc rPD = make_rsrc(p.pD + prow, static_cast<uint32_t>(rows) * 4u);
+    const Rsrc rPb = make_rsrc(p.pbias + prow, static_cast<uint32_t>(rows) * 4u);
+    bstore<float>(rPD, static_cast<uint32_t>(lane) * 4u, sD_);
+    bstore<float>(rPb, static_cast<uint32_t>(lane) * 4u, sB_);
+  }
+}
+
+// Sums of the partials: dB, dC over channel blocks; dA, dD, dbias over batch.
+__global__ void __launch_bounds__(256)
+scan_bwd_reduce_kernel(const float *__restrict__ pB, const float *__restrict__ pC, float *dB,
+                       float *dC, int64_t nbc, int nrb, const float *__restrict__ pA,
+                       float *dA, const float *__restrict__ pD, float *dD,
+                       const float *__restrict__ pbias, float *dbias, int64_t batch, int64_t dim,
+                       int dstate) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < nbc; e += stride) {
+    float sb = 0.0f, sc = 0.0f;
+    for (int k = 0; k < nrb; ++k) {
+      sb += pB[k * nbc + e];
+      sc += pC[k * nbc + e];
+    }
+    dB[e] = sb;
+    dC[e] = sc;
+  }
+  const int64_t na = dim * dstate;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < na; e += stride) {
+    const int64_t d = e / dstate, n = e - d * dstate;
+    float s = 0.0f;
+    for (int64_t bb = 0; bb < batch; ++bb) s += pA[(bb * dim + d) * 16 + n];
+    dA[e] = s;
+  }
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < dim; e += stride) {
+    float s = 0.0f, sb = 0.0f;
+    for (int64_t bb = 0; bb < batch; ++bb) {
+      s += pD[bb * dim + e];
+      sb += pbias[bb * dim + e];
+    }
+    dD[e] = s;
+    if (dbias != nullptr) dbias[e] = sb;
+  }
+}
+
+// dy = scale * dout * SiLU(z) and dz = scale * dout * y * SiLU'(z), with
+// SiLU'(z) = s (1 + z (1 - s)), s = sigmoid(z); without z, dy = scale * dout.
+__global__ void __launch_bounds__(256)
+gate_bwd_kernel(const float *__restrict__ y, const float *__restrict__ z,
+                const float *__restrict__ dout, float *__restrict__ dy, float *__restrict__ dz,
+                int64_t n, float scale) {
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
+       e += static_cast<int64_t>(gridDim.x) * 256) {
+    const float g = scale * dout[e];
+    if (z == nullptr) {
+      dy[e] = g;
+    } else {
+      const float zv = z[e];
+      const float s = hw_rcp(1.0f + hw_exp2(-zv * kLog2e));
+      dy[e] = g * zv * s;
+      dz[e] = g * y[e] * (s * __builtin_fmaf(zv, 1.0f - s, 1.0f));
+    }
+  }
+}
+
+unsigned grid_for(int64_t n) {
+  const int64_t g = (n + 255) / 256;
+  const int64_t cap = 256 * 32;
+  return static_cast<unsigned>(g < 1 ? 1 : (g < cap ? g : cap));
+}
+
+}  // namespace
+
+int64_t scan_bwd_tiles(int64_t L) { return (L + kBwdTile - 1) / kBwdTile; }
+
+hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s) {
+  const int64_t nrb = (a.dim + kR - 1) / kR;
+  const int64_t blocks = a.batch * nrb;
+  if (blocks == 0) return hipSuccess;
+  static_assert(kBwdTile == 8, "tile");
+  const size_t lds = BwdLayout<kBwdTile>::TOTAL * sizeof(float);
+  hipLaunchKernelGGL(scan_bwd_kernel<kBwdTile>, dim3(static_cast<unsigned>(blocks)), dim3(64), lds, s,
+                     a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_bwd_reduce(const BwdArgs &a, float *dA, float *dB, float *dC, float *dD,
+                                  float *dbias, hipStream_t s) {
+  const int nrb = static_cast<int>((a.dim + kR - 1) / kR);
+  const int64_t nbc = a.batch * a.dstate * a.L;
+  const int64_t n = nbc > a.dim * a.dstate ? nbc : a.dim * a.dstate;
+  hipLaunchKernelGGL(scan_bwd_reduce_kernel, dim3(grid_for(n)), dim3(256), 0, s, a.pB, a.pC, dB, dC,
+                     nbc, nrb, a.pA, dA, a.pD, dD, a.pbias, dbias, a.batch, a.dim, a.dstate);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_bwd(const float *y, const float *z, const float *dout, float *dy, float *dz,
+                           int64_t n, float scale, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(gate_bwd_kernel, dim3(grid_for(n)), dim3(256), 0, s, y, z, dout, dy, dz, n,
+                     scale);
+  return hipGetLastError();
+}
+
+}  // namespace vmk

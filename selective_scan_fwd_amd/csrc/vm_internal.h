@@ -116,6 +116,30 @@ int64_t xchg_global_stride(int64_t L);
 bool scan_offsets_fit(const ScanPlan &plan, const ScanArgs &args, bool bf16);
 hipError_t launch_scan(const ScanPlan &plan, const ScanArgs &args, bool bf16, hipStream_t s);
 
+// ---------------------------------------------------------------- backward
+// One direction, fp32.  dy: gradient of the ungated scan output.  The kernel
+// writes du and ddelta per element and partial sums that the reduce kernel
+// adds: pB, pC [nrb][batch][dstate][L] (per block of 16 channels), pA
+// [batch][dim][16], pD, pbias [batch][dim].  ck: [batch * dim][tiles][16]
+// state checkpoints (scratch).
+struct BwdArgs {
+  DirPtrs dir;
+  const float *dy;
+  float *du, *ddelta;
+  float *ck, *pA, *pD, *pbias, *pB, *pC;
+  int64_t batch, dim, L;
+  int dstate;
+  int softplus;
+  int reverse;
+};
+constexpr int kBwdTile = 8;
+int64_t scan_bwd_tiles(int64_t L);
+hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s);
+hipError_t launch_scan_bwd_reduce(const BwdArgs &a, float *dA, float *dB, float *dC, float *dD,
+                                  float *dbias, hipStream_t s);
+hipError_t launch_gate_bwd(const float *y, const float *z, const float *dout, float *dy, float *dz,
+                           int64_t n, float scale, hipStream_t s);
+
 // ---------------------------------------------------------------- layout
 hipError_t launch_atrous_gather(const void *x, void *streams, int64_t batch, int64_t ch,
                                 int64_t H, int64_t W, bool bf16, hipStream_t s);

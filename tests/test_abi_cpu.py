@@ -227,3 +227,46 @@ def test_fused_conv_only_where_supported(lib):
     assert lib.vm_ss2d_scan_fwd(dirs, FAKE, None, 1.0, FAKE * 3, 2, 4, 2, 2, 16, 0, 1, None) == 6
     # the conv weights count as inputs for the alias check
     assert _scan(lib, d=f, out=f.conv_w + 4) == 5
+
+
+def test_bwd_argument_checks(lib):
+    f, b = _dir(FAKE), _dir(FAKE * 2)
+
+    def grads(base):
+        return vm.VmScanGrad(*(base + k * (1 << 32) for k in range(7)))
+
+    gf, gb = grads(FAKE * 5), grads(FAKE * 6)
+
+    def single(p=f, z=None, dout=FAKE * 3, g=gf, dz=None, N=16, dtype=0, opt=1, rev=0, L=5):
+        gp = ctypes.byref(g) if g is not None else None
+        return lib.vm_selective_scan_bwd(ctypes.byref(p), z, dout, gp, dz, 2, 4, L, N, dtype, opt, rev, None)
+
+    assert single(dout=None) == 1
+    assert single(g=None) == 1
+    assert single(z=FAKE * 4) == 1                          # z without dz
+    g0 = grads(FAKE * 5)
+    g0.dC = None
+    assert single(g=g0) == 1
+    assert single(dtype=1) == 6                             # bf16: fp32 only
+    assert single(opt=3) == 6                               # zero-order hold: not here
+    assert single(N=17) == 6
+    assert single(rev=2) == 4
+    assert single(opt=4) == 4
+    ga = grads(FAKE * 5)
+    ga.du = f.u                                             # a gradient over an input
+    assert single(g=ga) == 5
+    ga = grads(FAKE * 5)
+    ga.dB = ga.dA                                           # gradients over each other
+    assert single(g=ga) == 5
+    assert single(z=FAKE * 4, dz=FAKE * 3) == 5             # dz over dout
+    fc = _dir(FAKE)
+    fc.conv_w = FAKE * 7
+    assert single(p=fc) == 6
+
+    def bidir(g2=gb, scale=1.0, dtype=0):
+        return lib.vm_bidir_scan_bwd(ctypes.byref(f), ctypes.byref(b), None, FAKE * 3, scale,
+                                     ctypes.byref(gf), ctypes.byref(g2), None, 2, 4, 5, 16, dtype, 1, None)
+
+    assert bidir(scale=float("inf")) == 6
+    assert bidir(dtype=1) == 6
+    assert bidir(g2=gf) == 5                                # both directions' gradients in one set

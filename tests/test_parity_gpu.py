@@ -655,3 +655,89 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(out, want[0]), f"replay {r}: bidir differs"
         assert torch.equal(y2, want[1]), f"replay {r}: ES2D differs"
+
+
+# ---------------------------------------------------------------- backward
+from oracle import grad as ograd  # noqa: E402
+
+_GRAD_KEYS = ("u", "delta", "A", "B", "C", "D", "delta_bias")
+
+
+def _dense_bc(p):
+    return {k: (v.contiguous() if k in ("B", "C") else v) for k, v in p.items()}
+
+
+@pytest.mark.parametrize("L", [1, 8, 77, 197])
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("gated", [True, False])
+def test_bwd_single(L, reverse, gated):
+    _case(f"bwd single L{L} rev{reverse} gated{gated}")
+    p, z = wl.single_inputs(2500 + L, 2, 70, L, device=DEV, gated=gated, perturb=True)
+    dout = torch.randn(p["u"].shape, generator=wl.generator(2600 + L, DEV), device=DEV)
+    g, dz = vm.vm_selective_scan_bwd(p, dout, z=z, reverse=reverse)
+    torch.cuda.synchronize()
+    want, wdz, _ = ograd.selective_scan_grad(host_dir(p), host(dout), z=host(z), reverse=reverse)
+    for k in _GRAD_KEYS:
+        assert_close(host(g[k]), want[k], FP32_TOL, f"d{k}")
+    if gated:
+        assert_close(host(dz), wdz, FP32_TOL, "dz")
+
+
+def test_bwd_small_dstate_no_softplus_dense_bc():
+    _case("bwd N5 no softplus dense B/C")
+    p, z = wl.single_inputs(2700, 3, 33, 50, dstate=5, device=DEV, bc_layout="dense")
+    p["delta"] = torch.rand_like(p["delta"]) * 0.3
+    p["delta_bias"] = None
+    dout = torch.randn(p["u"].shape, generator=wl.generator(2701, DEV), device=DEV)
+    g, dz = vm.vm_selective_scan_bwd(p, dout, z=z, delta_softplus=False)
+    torch.cuda.synchronize()
+    hp = host_dir(p)
+    want, wdz, _ = ograd.selective_scan_grad(hp, host(dout), z=host(z), delta_softplus=False)
+    for k in _GRAD_KEYS[:-1]:
+        assert_close(host(g[k]), want[k], FP32_TOL, f"d{k}")
+    assert g["delta_bias"] is None
+    assert_close(host(dz), wdz, FP32_TOL, "dz")
+
+
+@pytest.mark.parametrize("L", [77, 600])
+def test_bwd_bidir(L):
+    _case(f"bwd bidir L{L}")
+    fwd, bwd, z = wl.bidir_inputs(2800 + L, 2, 40, L, device=DEV, perturb=True)
+    dout = torch.randn(fwd["u"].shape, generator=wl.generator(2900 + L, DEV), device=DEV)
+    gf, gb, dz = vm.vm_bidir_scan_bwd(fwd, bwd, dout, z=z, combine_scale=0.5)
+    torch.cuda.synchronize()
+    wf, wb, wdz, _ = ograd.bidir_scan_grad(host_dir(fwd), host_dir(bwd), host(dout), z=host(z),
+                                           combine_scale=0.5)
+    for k in _GRAD_KEYS:
+        assert_close(host(gf[k]), wf[k], FP32_TOL, f"fwd d{k}")
+        assert_close(host(gb[k]), wb[k], FP32_TOL, f"bwd d{k}")
+    assert_close(host(dz), wdz, FP32_TOL, "dz")
+
+
+def test_bwd_deterministic():
+    _case("bwd deterministic")
+    fwd, bwd, z = wl.bidir_inputs(3000, 4, 64, 100, device=DEV)
+    dout = torch.randn(fwd["u"].shape, generator=wl.generator(3001, DEV), device=DEV)
+    a = vm.vm_bidir_scan_bwd(fwd, bwd, dout, z=z)
+    b = vm.vm_bidir_scan_bwd(fwd, bwd, dout, z=z)
+    torch.cuda.synchronize()
+    for ga, gb_ in ((a[0], b[0]), (a[1], b[1])):
+        for k in _GRAD_KEYS:
+            assert torch.equal(ga[k], gb_[k]), k
+    assert torch.equal(a[2], b[2])
+
+
+def test_full_vim_tiny_bidir_bwd():
+    # the headline workload's backward, every gradient element
+    w = wl.WORKLOADS[1]
+    _case(f"full {w.name} backward")
+    fwd, bwd, z = wl.bidir_inputs(3100, w.batch, w.dim, w.seqlen, device=DEV, perturb=True)
+    dout = torch.randn(fwd["u"].shape, generator=wl.generator(3101, DEV), device=DEV)
+    gf, gb, dz = vm.vm_bidir_scan_bwd(fwd, bwd, dout, z=z, combine_scale=w.combine_scale)
+    torch.cuda.synchronize()
+    wf, wb, wdz, _ = ograd.bidir_scan_grad(host_dir(fwd), host_dir(bwd), host(dout), z=host(z),
+                                           combine_scale=w.combine_scale)
+    for k in _GRAD_KEYS:
+        assert_close(host(gf[k]), wf[k], FP32_TOL, f"fwd d{k}")
+        assert_close(host(gb[k]), wb[k], FP32_TOL, f"bwd d{k}")
+    assert_close(host(dz), wdz, FP32_TOL, "dz")
