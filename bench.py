@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--config", type=int, default=1,
                     help="0 single, 1 Vim-T bidir (default), 2 bf16 L=4097, 3 ES2D 56x56, "
                          "4 FastVim pooled (axes alternate per step), 5 FastVim unpooled L=16384, "
-                         "6 SS2D four-direction scan 56x56")
+                         "6 SS2D four-direction scan 56x56, 7 backward of the Vim-T bidirectional scan")
     ap.add_argument("--sets", type=int, default=0, help="input sets to cycle (0 = auto)")
     ap.add_argument("--conv", choices=["none", "fused", "unfused"], default="none",
                     help="configs 0-2: the scan input comes from the block's causal conv1d + SiLU, "
@@ -326,6 +326,52 @@ def build_step(cfg, seed, sets, dev, zoh=False, conv="none"):
 
         return step, info, cpu, nbytes, tokens, slots
 
+    if cfg == 7:
+        w = wl.WORKLOADS[1]
+        L = w.seqlen
+        inputs = []
+        for k in range(sets):
+            f, b, z = wl.bidir_inputs(seed + k, w.batch, w.dim, L, device=dev)
+            dout = torch.randn(f["u"].shape, generator=wl.generator(seed + 50 + k, dev), device=dev)
+            inputs.append((f, b, z, dout))
+
+        def step(i):
+            f, b, z, dout = inputs[i % sets]
+            vm.vm_bidir_scan_bwd(f, b, dout, z=z, combine_scale=w.combine_scale)
+
+        tok = w.batch * w.dim * L
+        bc = w.batch * L * N * 4
+        # read u, delta per direction, z and dout once; B, C per direction;
+        # write du, ddelta per direction, dz, and dB, dC per direction
+        nbytes = 2 * (2 * tok * 4 + 2 * bc) + 2 * tok * 4 + 2 * (2 * tok * 4 + 2 * bc) + tok * 4
+        tokens = tok
+        # one state recompute (5 slots) and the adjoint (9 slots) per state step
+        slots = 2 * tok * N * 14
+        info = dict(workload=w.name + "-backward", batch=w.batch, dim=w.dim, seqlen=L, dstate=N,
+                    directions=2, combine_scale=w.combine_scale,
+                    kernels="forward recompute + gate backward + 2 x (backward + reduce)")
+
+        def cpu(budget):
+            from oracle import grad as og
+            f, b, z, dout = inputs[0]
+            sub = 1
+            hd = lambda p: {k: (v[:sub] if k in ("u", "delta", "B", "C") else v).double().cpu().numpy()
+                            for k, v in p.items()}
+            hf, hb = hd(f), hd(b)
+            hz, hdo = z[:sub].double().cpu().numpy(), dout[:sub].double().cpu().numpy()
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                og.bidir_scan_grad(hf, hb, hdo, z=hz, combine_scale=w.combine_scale)
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= budget or reps >= 20:
+                    break
+            frac = sub / w.batch
+            return el / reps, nbytes * frac, tokens * frac, torch.get_num_threads(), \
+                f"fp64 autograd oracle on {sub} of {w.batch} batch rows, {reps} repetitions"
+
+        return step, info, cpu, nbytes, tokens, slots
+
     raise SystemExit(f"unknown --config {cfg}")
 
 
@@ -365,7 +411,7 @@ def main():
         sys.exit(1)
     vm.load_library()
     dev = torch.device("cuda:0")
-    sets = args.sets or (3 if args.config in (0, 1, 2, 3, 6) else 1)
+    sets = args.sets or (3 if args.config in (0, 1, 2, 3, 6, 7) else 1)
     if args.conv != "none" and args.config not in (0, 1, 2):
         raise SystemExit("--conv applies to configs 0-2")
     step, info, cpu_fn, nbytes, tokens, slots = build_step(args.config, args.seed, sets, dev, args.zoh,

@@ -276,7 +276,8 @@ int check_bwd_common(int dtype, int options, int64_t batch, int64_t dim, int64_t
   if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;
   if (!options_ok(options)) return VM_ERR_FLAG;
   if (!dims_ok({batch, dim, L}, tok) || dstate <= 0) return VM_ERR_SHAPE;
-  if (dtype != VM_F32 || (options & VM_ZOH) || dstate > 16) return VM_ERR_UNSUPPORTED;
+  if (dtype != VM_F32 || (options & VM_ZOH) || dstate > 16 || dim > kMaxPlanes)
+    return VM_ERR_UNSUPPORTED;
   if (!dims_ok({batch, dstate, L}, bc)) return VM_ERR_SHAPE;
   // 32-bit offsets of the kernel's per-block checkpoints and partial sums
   if (16 * 64 * vmk::scan_bwd_tiles(L) >= (int64_t{1} << 31) || 64 * L >= (int64_t{1} << 31))

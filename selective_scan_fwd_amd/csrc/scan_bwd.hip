@@ -24,8 +24,8 @@
 // (du, ddelta) meet in LDS like the forward's partial sums; the sums over
 // channels (dB, dC) are reduced over the wave's 16 channels in LDS and
 // written as one partial per channel block; the sums over batch rows (dA, dD,
-// dbias) are written as one partial per batch row.  A second kernel adds the
-// partials.
+// dbias) are written as one partial per batch row.  Two small kernels add
+// the partials, in a fixed order (deterministic).
 #include "scan_device.h"
 #include "vm_internal.h"
 
@@ -47,8 +47,9 @@ struct BwdLayout {
 };
 
 // The tile's states and decays stay in registers (64 VGPRs with 8-step
-// tiles); the LDS area (24 KB) allows six workgroups per CU, so the register
-// budget is set for two waves per SIMD.
+// tiles; 4-step tiles fit more workgroups but measured 1.6x slower for their
+// per-tile reductions); the LDS area (24 KB) allows six workgroups per CU,
+// so the register budget is set for two waves per SIMD.
 template <int T>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 scan_bwd_kernel(const BwdArgs p) {
@@ -142,19 +143,40 @@ scan_bwd_kernel(const BwdArgs p) {
   const bool sp_on = p.softplus != 0;
 
   auto tile_of = [&](int k) { return rev ? nt - 1 - k : k; };
-  // Stages tile j: (dt, dt u, dy) per element and B (and C) per step.  Steps
-  // past L and rows past dim read 0.  Returns the element values the combine
-  // of this tile needs in registers.
-  float eu[PE], edt[PE], edy[PE], ex[PE];
-  auto stage = [&](int j, bool with_c) {
+  // Raw global values of the next tile (loaded one tile ahead, so that their
+  // latency overlaps the current tile's arithmetic).  Steps past L and rows
+  // past dim read 0.
+  float lu[PE], ld[PE], ly[PE], lb[BQ], lc[BQ], lk[kNS];
+  const uint32_t ck_lane = static_cast<uint32_t>(r * nt) * 64u + static_cast<uint32_t>(n0) * 4u;
+  auto stage_load = [&](int j, bool pass2) {
     const int jT = j * T;
     const bool in_seq = tq < L - jT;
 #pragma unroll
     for (int i = 0; i < PE; ++i) {
       const uint32_t o = pin_u(in_seq ? ob[i] + static_cast<uint32_t>(jT) * 4u : kOob);
-      const float uv = bload<float>(rU, o);
-      const float x = bload<float>(rDl, o) + sbias[i];
-      const float dyv = with_c ? bload<float>(rDy, o) : 0.0f;
+      lu[i] = bload<float>(rU, o);
+      ld[i] = bload<float>(rDl, o);
+      ly[i] = pass2 ? bload<float>(rDy, o) : 0.0f;
+    }
+    const uint32_t tb = static_cast<uint32_t>(jT) * bst_bytes;
+#pragma unroll
+    for (int i = 0; i < BQ; ++i) {
+      lb[i] = bload<float>(rB, bo[i] + tb);
+      lc[i] = pass2 ? bload<float>(rC, bo[i] + tb) : 0.0f;
+    }
+#pragma unroll
+    for (int jn = 0; jn < kNS; ++jn)
+      lk[jn] = pass2 ? bload<float>(rCk, ck_lane + static_cast<uint32_t>(j) * 64u + 4u * jn) : 0.0f;
+  };
+  // Stages the loaded tile: (dt, dt u, dy) per element and B, C per step into
+  // LDS, and keeps the element values the tile's combine needs.
+  float eu[PE], edt[PE], edy[PE], ex[PE];
+  auto stage_store = [&]() {
+#pragma unroll
+    for (int i = 0; i < PE; ++i) {
+      const float uv = pin(lu[i]);
+      const float x = pin(ld[i]) + sbias[i];
+      const float dyv = pin(ly[i]);
       const float dtv = sp_on ? softplus_f(x) : x;
       eu[i] = uv;
       edt[i] = dtv;
@@ -163,12 +185,11 @@ scan_bwd_kernel(const BwdArgs p) {
       *reinterpret_cast<float4 *>(prep + srow[i] * Lay::PST + 4 * sq) =
           make_float4(dtv, dtv * uv, dyv, 0.0f);
     }
-    const uint32_t tb = static_cast<uint32_t>(jT) * bst_bytes;
 #pragma unroll
     for (int i = 0; i < BQ; ++i) {
       float *const q = bcs + (lane / 16 + 4 * i) * 32 + n_bc;
-      q[0] = bload<float>(rB, bo[i] + tb);
-      q[16] = with_c ? bload<float>(rC, bo[i] + tb) : 0.0f;
+      q[0] = pin(lb[i]);
+      q[16] = pin(lc[i]);
     }
   };
 
@@ -176,13 +197,14 @@ scan_bwd_kernel(const BwdArgs p) {
   float h[kNS];
 #pragma unroll
   for (int j = 0; j < kNS; ++j) h[j] = 0.0f;
-  const uint32_t ck_lane = static_cast<uint32_t>(r * nt) * 64u + static_cast<uint32_t>(n0) * 4u;
+  stage_load(tile_of(0), false);
   for (int k = 0; k < nt; ++k) {
     const int j = tile_of(k);
 #pragma unroll
     for (int jn = 0; jn < kNS; ++jn)
       bstore<float>(rCk, ck_lane + static_cast<uint32_t>(j) * 64u + 4u * jn, h[jn]);
-    stage(j, false);
+    stage_store();
+    stage_load(tile_of(k + 1 < nt ? k + 1 : nt - 1), false);
 #pragma unroll
     for (int q = 0; q < T; ++q) {
       const float4 pq = *reinterpret_cast<const float4 *>(prep + r * Lay::PST + 4 * q);
@@ -201,6 +223,8 @@ scan_bwd_kernel(const BwdArgs p) {
       }
     }
   }
+  // the checkpoints written above are read back below
+  __syncthreads();
 
   // ---- pass 2: tiles in reverse visit order
   float gn[kNS], dA[kNS];
@@ -209,15 +233,17 @@ scan_bwd_kernel(const BwdArgs p) {
     gn[j] = 0.0f;
     dA[j] = 0.0f;
   }
+  stage_load(tile_of(nt - 1), true);
   for (int k = nt - 1; k >= 0; --k) {
     const int j = tile_of(k);
-    stage(j, true);
+    stage_store();
     float hc[kNS], h0[kNS];
 #pragma unroll
     for (int jn = 0; jn < kNS; ++jn) {
-      hc[jn] = bload<float>(rCk, ck_lane + static_cast<uint32_t>(j) * 64u + 4u * jn);
+      hc[jn] = pin(lk[jn]);
       h0[jn] = hc[jn];
     }
+    stage_load(tile_of(k > 0 ? k - 1 : 0), true);
     // recompute the tile's states and decays
     float hs[T][kNS], as[T][kNS];
 #pragma unroll
@@ -331,38 +357,64 @@ scan_bwd_kernel(const BwdArgs p) {
   }
 }
 
-// Sums of the partials: dB, dC over channel blocks; dA, dD, dbias over batch.
+// Sums of the partials over channel blocks: dB, dC [batch, dstate, L].
 __global__ void __launch_bounds__(256)
-scan_bwd_reduce_kernel(const float *__restrict__ pB, const float *__restrict__ pC, float *dB,
-                       float *dC, int64_t nbc, int nrb, const float *__restrict__ pA,
-                       float *dA, const float *__restrict__ pD, float *dD,
-                       const float *__restrict__ pbias, float *dbias, int64_t batch, int64_t dim,
-                       int dstate) {
+reduce_bc_kernel(const float *__restrict__ pB, const float *__restrict__ pC, float *dB, float *dC,
+                 int64_t nbc, int nrb) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < nbc; e += stride) {
-    float sb = 0.0f, sc = 0.0f;
-    for (int k = 0; k < nrb; ++k) {
-      sb += pB[k * nbc + e];
-      sc += pC[k * nbc + e];
+    float sb[4] = {0.f, 0.f, 0.f, 0.f}, sc[4] = {0.f, 0.f, 0.f, 0.f};
+    int k = 0;
+    for (; k + 4 <= nrb; k += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sb[u] += pB[(k + u) * nbc + e];
+        sc[u] += pC[(k + u) * nbc + e];
+      }
     }
-    dB[e] = sb;
-    dC[e] = sc;
-  }
-  const int64_t na = dim * dstate;
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < na; e += stride) {
-    const int64_t d = e / dstate, n = e - d * dstate;
-    float s = 0.0f;
-    for (int64_t bb = 0; bb < batch; ++bb) s += pA[(bb * dim + d) * 16 + n];
-    dA[e] = s;
-  }
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < dim; e += stride) {
-    float s = 0.0f, sb = 0.0f;
-    for (int64_t bb = 0; bb < batch; ++bb) {
-      s += pD[bb * dim + e];
-      sb += pbias[bb * dim + e];
+    for (; k < nrb; ++k) {
+      sb[0] += pB[k * nbc + e];
+      sc[0] += pC[k * nbc + e];
     }
-    dD[e] = s;
-    if (dbias != nullptr) dbias[e] = sb;
+    dB[e] = (sb[0] + sb[1]) + (sb[2] + sb[3]);
+    dC[e] = (sc[0] + sc[1]) + (sc[2] + sc[3]);
+  }
+}
+
+// Sums of the partials over batch rows, one workgroup per channel d:
+// dA [dim, dstate], dD [dim], dbias [dim].  Thread t adds the rows
+// b = t / 16 (mod 16 slices) for state t % 16; the slices meet in LDS.
+__global__ void __launch_bounds__(256)
+reduce_param_kernel(const float *__restrict__ pA, float *dA, const float *__restrict__ pD, float *dD,
+                    const float *__restrict__ pbias, float *dbias, int64_t batch, int64_t dim,
+                    int dstate) {
+  __shared__ float sa[256], sd[256], sb[256];
+  const int64_t d = blockIdx.x;
+  const int t = threadIdx.x, n = t & 15, slice = t >> 4;
+  float a = 0.f, dd = 0.f, db = 0.f;
+  for (int64_t bb = slice; bb < batch; bb += 16) {
+    a += pA[(bb * dim + d) * 16 + n];
+    if (n == 0) {
+      dd += pD[bb * dim + d];
+      db += pbias[bb * dim + d];
+    }
+  }
+  sa[t] = a;
+  sd[t] = dd;
+  sb[t] = db;
+  __syncthreads();
+  if (t < 16) {
+    float s = 0.f, s2 = 0.f, s3 = 0.f;
+    for (int k = 0; k < 16; ++k) {
+      s += sa[k * 16 + t];
+      s2 += sd[k * 16 + t];
+      s3 += sb[k * 16 + t];
+    }
+    if (t < dstate) dA[d * dstate + t] = s;
+    if (t == 0) {
+      dD[d] = s2;
+      if (dbias != nullptr) dbias[d] = s3;
+    }
   }
 }
 
@@ -400,7 +452,6 @@ hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s) {
   const int64_t nrb = (a.dim + kR - 1) / kR;
   const int64_t blocks = a.batch * nrb;
   if (blocks == 0) return hipSuccess;
-  static_assert(kBwdTile == 8, "tile");
   const size_t lds = BwdLayout<kBwdTile>::TOTAL * sizeof(float);
   hipLaunchKernelGGL(scan_bwd_kernel<kBwdTile>, dim3(static_cast<unsigned>(blocks)), dim3(64), lds, s,
                      a);
@@ -411,9 +462,12 @@ hipError_t launch_scan_bwd_reduce(const BwdArgs &a, float *dA, float *dB, float 
                                   float *dbias, hipStream_t s) {
   const int nrb = static_cast<int>((a.dim + kR - 1) / kR);
   const int64_t nbc = a.batch * a.dstate * a.L;
-  const int64_t n = nbc > a.dim * a.dstate ? nbc : a.dim * a.dstate;
-  hipLaunchKernelGGL(scan_bwd_reduce_kernel, dim3(grid_for(n)), dim3(256), 0, s, a.pB, a.pC, dB, dC,
-                     nbc, nrb, a.pA, dA, a.pD, dD, a.pbias, dbias, a.batch, a.dim, a.dstate);
+  hipLaunchKernelGGL(reduce_bc_kernel, dim3(grid_for(nbc)), dim3(256), 0, s, a.pB, a.pC, dB, dC, nbc,
+                     nrb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(reduce_param_kernel, dim3(static_cast<unsigned>(a.dim)), dim3(256), 0, s, a.pA, dA,
+                     a.pD, dD, a.pbias, dbias, a.batch, a.dim, a.dstate);
   return hipGetLastError();
 }
 
