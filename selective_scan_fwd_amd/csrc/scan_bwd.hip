@@ -244,12 +244,20 @@ scan_bwd_kernel(const BwdArgs p) {
       h0[jn] = hc[jn];
     }
     stage_load(tile_of(k > 0 ? k - 1 : 0), true);
-    // recompute the tile's states and decays
+    // recompute the tile's states and decays (the staged step values and
+    // B, C stay in registers for the adjoint)
     float hs[T][kNS], as[T][kNS];
+    float4 pqs[T];
+    float bvs[T];
 #pragma unroll
     for (int q = 0; q < T; ++q) {
-      const float4 pq = *reinterpret_cast<const float4 *>(prep + r * Lay::PST + 4 * q);
-      const float bv = bcs[q * 32 + bc_slot];
+      pqs[q] = *reinterpret_cast<const float4 *>(prep + r * Lay::PST + 4 * q);
+      bvs[q] = bcs[q * 32 + bc_slot];
+    }
+#pragma unroll
+    for (int q = 0; q < T; ++q) {
+      const float4 pq = pqs[q];
+      const float bv = bvs[q];
 #pragma unroll
       for (int jn = 0; jn < kNS; ++jn) {
         const float a = hw_exp2(pq.x * A2[jn]);
@@ -268,8 +276,8 @@ scan_bwd_kernel(const BwdArgs p) {
     // adjoint back through the tile
 #pragma unroll
     for (int q = T - 1; q >= 0; --q) {
-      const float4 pq = *reinterpret_cast<const float4 *>(prep + r * Lay::PST + 4 * q);
-      const float bv = bcs[q * 32 + bc_slot];
+      const float4 pq = pqs[q];
+      const float bv = bvs[q];
       float sgB = 0.0f, sqA = 0.0f;
 #pragma unroll
       for (int jn = 0; jn < kNS; ++jn) {
