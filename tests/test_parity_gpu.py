@@ -741,3 +741,29 @@ def test_full_vim_tiny_bidir_bwd():
         assert_close(host(gf[k]), wf[k], FP32_TOL, f"fwd d{k}")
         assert_close(host(gb[k]), wb[k], FP32_TOL, f"bwd d{k}")
     assert_close(host(dz), wdz, FP32_TOL, "dz")
+
+
+# ---------------------------------------------------------------- degenerate sizes
+def test_degenerate_sizes_every_entry_point():
+    # one channel, one batch row, shortest sequences / maps, for each entry
+    _case("degenerate sizes")
+    p, z = wl.single_inputs(3200, 1, 1, 1, dstate=1, device=DEV)
+    out = vm.vm_selective_scan_fwd(**p, z=z)
+    fwd, bwd, zb = wl.bidir_inputs(3201, 1, 1, 2, dstate=1, device=DEV)
+    outb = vm.vm_bidir_scan_fwd(fwd, bwd, z=zb)
+    u, dirs, z2 = wl.ss2d_inputs(3202, 1, 1, 1, 3, dstate=2, device=DEV)
+    out2 = vm.vm_ss2d_scan_fwd(u, dirs, z=z2)
+    x, w, b = _conv_inputs(3203, 1, 1, 1)
+    outc = vm.vm_causal_conv1d_silu(x, w, b)
+    dout = torch.randn(fwd["u"].shape, generator=wl.generator(3204, DEV), device=DEV)
+    gf, gb, dz = vm.vm_bidir_scan_bwd(fwd, bwd, dout, z=zb)
+    torch.cuda.synchronize()
+    assert_close(host(out), oracle.selective_scan(**host_dir(p), z=host(z)), FP32_TOL, "single 1x1x1")
+    assert_close(host(outb), oracle.bidir_scan(host_dir(fwd), host_dir(bwd), z=host(zb)), FP32_TOL, "bidir L2")
+    assert_close(host(out2), _ss2d_ref(u, dirs, z2), FP32_TOL, "ss2d 1x3")
+    assert_close(host(outc), oracle.causal_conv1d_silu(host(x), host(w), host(b)), FP32_TOL, "conv L1")
+    wf, wb, wdz, _ = ograd.bidir_scan_grad(host_dir(fwd), host_dir(bwd), host(dout), z=host(zb))
+    for k in _GRAD_KEYS:
+        assert_close(host(gf[k]), wf[k], FP32_TOL, f"fwd d{k}")
+        assert_close(host(gb[k]), wb[k], FP32_TOL, f"bwd d{k}")
+    assert_close(host(dz), wdz, FP32_TOL, "dz")

@@ -45,3 +45,18 @@ def test_bf16_rounding_and_shapes():
     assert f["u"].shape == (2, 3, 4, 6) and f["delta"].shape == (2, 3, 6) and f["B"].shape == (2, 16, 6)
     f, b, z = wl.fastvim_inputs(4, 2, 3, 4, 6, pool_axis=1, full_resolution=True)
     assert f["delta"].shape == (2, 3, 24) and f["B"].shape == (2, 16, 24)
+
+
+def test_ss2d_and_conv_generators():
+    u, dirs, z = wl.ss2d_inputs(7, 2, 3, 5, 4)
+    assert u.shape == (2, 3, 5, 4) and z.shape == u.shape and len(dirs) == 4
+    for p in dirs:
+        assert "u" not in p and p["delta"].shape == (2, 3, 20) and p["B"].shape == (2, 16, 20)
+    # four distinct draws of the per-traversal inputs
+    assert not torch.equal(dirs[0]["delta"], dirs[2]["delta"])
+    w = wl.WORKLOADS[5]
+    assert (w.height, w.width, w.batch, w.dim) == (56, 56, 64, 192)
+    g = wl.generator(3, "cpu")
+    cw, cb = wl.conv_params(g, 10)
+    assert cw.shape == (10, 4) and cb.shape == (10,)
+    assert cw.abs().max().item() <= 0.5 and cb.abs().max().item() <= 0.5
