@@ -598,12 +598,15 @@ int vm_selective_scan_bwd(const vm_scan_dir *p, const void *z, const void *dout,
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   Scratch ws(s);
+  // all temporary memory first, so that a failed allocation launches nothing
+  BwdScratch bs;
+  st = bs.get(ws, batch, dim, seqlen, dstate);
+  float *y = z != nullptr ? ws.get(tok, &st) : nullptr;
+  float *dyb = z != nullptr ? ws.get(tok, &st) : nullptr;
+  if (st != VM_OK) return st;
   const float *dy = static_cast<const float *>(dout);
   if (z != nullptr) {
     // the ungated forward output, for dz, then dy = dout * SiLU(z)
-    float *y = ws.get(tok, &st);
-    float *dyb = ws.get(tok, &st);
-    if (st != VM_OK) return st;
     vmk::ScanArgs a = {};
     a.dir[0] = a.dir[1] = resolve_dir(p, batch, dstate, seqlen, false, ws, s, &st);
     a.out = y;
@@ -623,9 +626,6 @@ int vm_selective_scan_bwd(const vm_scan_dir *p, const void *z, const void *dout,
     if (st != VM_OK) return st;
     dy = dyb;
   }
-  BwdScratch bs;
-  st = bs.get(ws, batch, dim, seqlen, dstate);
-  if (st != VM_OK) return st;
   return run_bwd(p, dy, g, bs, batch, dim, seqlen, dstate, options, reverse, ws, s);
 }
 
@@ -660,6 +660,8 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
   // which the forward kernel recomputes ungated with s = 1
   float *dy = ws.get(tok, &st);
   float *y = z != nullptr ? ws.get(tok, &st) : nullptr;
+  BwdScratch bs;
+  if (st == VM_OK) st = bs.get(ws, batch, dim, seqlen, dstate);
   if (st != VM_OK) return st;
   if (z != nullptr) {
     vmk::ScanArgs a = {};
@@ -680,9 +682,7 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
                                        static_cast<const float *>(dout), dy,
                                        static_cast<float *>(dz), tok, combine_scale, s));
   if (st != VM_OK) return st;
-  BwdScratch bs;
-  st = bs.get(ws, batch, dim, seqlen, dstate);
-  if (st == VM_OK) st = run_bwd(fwd, dy, gf, bs, batch, dim, seqlen, dstate, options, 0, ws, s);
+  st = run_bwd(fwd, dy, gf, bs, batch, dim, seqlen, dstate, options, 0, ws, s);
   if (st == VM_OK) st = run_bwd(bwd, dy, gb, bs, batch, dim, seqlen, dstate, options, 1, ws, s);
   return st;
 }
