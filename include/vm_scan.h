@@ -295,16 +295,18 @@ typedef struct vm_scan_grad {
  * (the pages pin the backward pass only as automatic differentiation of the
  * scan loop, [Vim] "A state retains, writes, and reads" and implementation
  * row 4; the adjoint recurrence it implies is g_t = C_t dy_t + a_{t+1} g_{t+1}).
- *   dout [batch, dim, seqlen]; g: the gradients (see vm_scan_grad);
- *   dz [batch, dim, seqlen]: required exactly when z is given.
- * VM_F32 only, and the released recurrence only (options without VM_ZOH),
- * no fused conv (VM_ERR_UNSUPPORTED otherwise).  Gradient buffers must not
+ *   dout [batch, dim, seqlen] (dtype); g: the gradients (see vm_scan_grad);
+ *   dz [batch, dim, seqlen] fp32: required exactly when z is given.
+ * Gradients are fp32 for either dtype (VM_BF16 inputs are widened exactly
+ * and the pass runs in fp32).  The released recurrence only (options without
+ * VM_ZOH) and no fused conv (VM_ERR_UNSUPPORTED otherwise).  Gradient buffers must not
  * overlap any input or each other (VM_ERR_ALIAS).  Sums over batch rows (dA,
  * dD, ddelta_bias) and over channels (dB, dC) are formed from per-block
  * partials in a fixed order, so results are deterministic.
  * Temporary memory: state checkpoints ([batch * dim, seqlen / 8, 16] fp32),
- * the partials ([dim / 16, batch, dstate, seqlen] fp32 for each of dB, dC)
- * and, with z, the recomputed forward output and dy.
+ * the partials ([dim / 16, batch, dstate, seqlen] fp32 for each of dB, dC),
+ * with z the recomputed forward output and dy, and with VM_BF16 fp32 copies
+ * of the token tensors.
  */
 int vm_selective_scan_bwd(const vm_scan_dir *p, const void *z,
                           const void *dout, const vm_scan_grad *g, void *dz,

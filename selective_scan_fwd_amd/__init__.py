@@ -271,20 +271,22 @@ def _grad_set(p, batch, dim, L, N, device, with_bias):
 
 def vm_selective_scan_bwd(p, dout, z=None, delta_softplus=True, reverse=False):
     """Gradients of sum(dout * vm_selective_scan_fwd(**p, z=z, ...)).  p: dict
-    u, delta, A, B, C, D, delta_bias (fp32).  Returns (grads, dz): grads has
-    the keys of p (dB, dC dense [batch, N, L]); dz is None without z."""
+    u, delta, A, B, C, D, delta_bias (token tensors fp32 or bf16, like dout and
+    z).  Returns (grads, dz), fp32: grads has the keys of p (dB, dC dense
+    [batch, N, L]); dz is None without z."""
     u = p["u"]
+    dt = u.dtype
     batch, dim, L = u.shape
     N = p["A"].shape[-1]
-    d, keep = _direction(p, batch, dim, (batch, dim, L), L, N, torch.float32, u.device, "p")
-    _dev(dout, "dout", torch.float32, u.shape, u.device)
+    d, keep = _direction(p, batch, dim, (batch, dim, L), L, N, dt, u.device, "p")
+    _dev(dout, "dout", dt, u.shape, u.device)
     if z is not None:
-        _dev(z, "z", torch.float32, u.shape, u.device)
+        _dev(z, "z", dt, u.shape, u.device)
     gs, g = _grad_set(p, batch, dim, L, N, u.device, p.get("delta_bias") is not None)
-    dz = torch.empty_like(u) if z is not None else None
+    dz = torch.empty(u.shape, dtype=torch.float32, device=u.device) if z is not None else None
     with torch.cuda.device(u.device):
         st = load_library().vm_selective_scan_bwd(ctypes.byref(d), _ptr(z), _ptr(dout), ctypes.byref(gs),
-                                                  _ptr(dz), batch, dim, L, N, VM_F32,
+                                                  _ptr(dz), batch, dim, L, N, _dtype_code(u),
                                                   _options(delta_softplus, False), int(bool(reverse)),
                                                   _stream(u.device))
     _check(st, "vm_selective_scan_bwd")
@@ -293,22 +295,23 @@ def vm_selective_scan_bwd(p, dout, z=None, delta_softplus=True, reverse=False):
 
 def vm_bidir_scan_bwd(fwd, bwd, dout, z=None, combine_scale=1.0, delta_softplus=True):
     """Gradients of sum(dout * vm_bidir_scan_fwd(fwd, bwd, z, combine_scale)).
-    Returns (grads of fwd, grads of bwd, dz)."""
+    Returns (grads of fwd, grads of bwd, dz), fp32 for fp32 or bf16 inputs."""
     u = fwd["u"]
+    dt = u.dtype
     batch, dim, L = u.shape
     N = fwd["A"].shape[-1]
-    df, kf = _direction(fwd, batch, dim, (batch, dim, L), L, N, torch.float32, u.device, "fwd")
-    db, kb = _direction(bwd, batch, dim, (batch, dim, L), L, N, torch.float32, u.device, "bwd")
-    _dev(dout, "dout", torch.float32, u.shape, u.device)
+    df, kf = _direction(fwd, batch, dim, (batch, dim, L), L, N, dt, u.device, "fwd")
+    db, kb = _direction(bwd, batch, dim, (batch, dim, L), L, N, dt, u.device, "bwd")
+    _dev(dout, "dout", dt, u.shape, u.device)
     if z is not None:
-        _dev(z, "z", torch.float32, u.shape, u.device)
+        _dev(z, "z", dt, u.shape, u.device)
     gsf, gf = _grad_set(fwd, batch, dim, L, N, u.device, fwd.get("delta_bias") is not None)
     gsb, gb = _grad_set(bwd, batch, dim, L, N, u.device, bwd.get("delta_bias") is not None)
-    dz = torch.empty_like(u) if z is not None else None
+    dz = torch.empty(u.shape, dtype=torch.float32, device=u.device) if z is not None else None
     with torch.cuda.device(u.device):
         st = load_library().vm_bidir_scan_bwd(ctypes.byref(df), ctypes.byref(db), _ptr(z), _ptr(dout),
                                               float(combine_scale), ctypes.byref(gsf), ctypes.byref(gsb),
-                                              _ptr(dz), batch, dim, L, N, VM_F32,
+                                              _ptr(dz), batch, dim, L, N, _dtype_code(u),
                                               _options(delta_softplus, False), _stream(u.device))
     _check(st, "vm_bidir_scan_bwd")
     return gf, gb, dz

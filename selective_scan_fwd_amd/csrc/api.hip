@@ -261,12 +261,27 @@ int check_grad(const vm_scan_grad *g, int64_t tok, int64_t bc, int64_t dim, int6
 }
 
 void dir_spans(const vm_scan_dir *p, int64_t tok, int64_t batch, int64_t L, int64_t dim,
-               int64_t dstate, std::vector<Span> &ins) {
+               int64_t dstate, int es, std::vector<Span> &ins) {
   const int64_t bc = bc_extent(batch, dstate, L, p->bc_stride);
-  const Span sp[] = {span(p->u, tok * 4), span(p->delta, tok * 4), span(p->A, dim * dstate * 4),
-                     span(p->B, bc * 4), span(p->C, bc * 4), span(p->D, dim * 4),
+  const Span sp[] = {span(p->u, tok * es), span(p->delta, tok * es), span(p->A, dim * dstate * 4),
+                     span(p->B, bc * es), span(p->C, bc * es), span(p->D, dim * 4),
                      span(p->delta_bias, dim * 4)};
   ins.insert(ins.end(), sp, sp + 7);
+}
+
+// fp32 view of a direction's token tensors for the backward pass: the
+// direction itself, or (bf16) one whose u, delta, B and C are widened copies
+// in the same layout.
+vm_scan_dir widen_dir(const vm_scan_dir *p, int64_t tok, int64_t batch, int64_t L,
+                      int64_t dstate, bool bf16, Scratch &ws, hipStream_t s, int *st) {
+  vm_scan_dir w = *p;
+  if (!bf16) return w;
+  const int64_t bc = bc_extent(batch, dstate, L, p->bc_stride);
+  w.u = as_f32(p->u, tok, true, ws, s, st);
+  w.delta = as_f32(p->delta, tok, true, ws, s, st);
+  w.B = as_f32(p->B, bc, true, ws, s, st);
+  w.C = as_f32(p->C, bc, true, ws, s, st);
+  return w;
 }
 
 // Shared checks of the backward entry points (fp32, released recurrence, no
@@ -276,8 +291,7 @@ int check_bwd_common(int dtype, int options, int64_t batch, int64_t dim, int64_t
   if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;
   if (!options_ok(options)) return VM_ERR_FLAG;
   if (!dims_ok({batch, dim, L}, tok) || dstate <= 0) return VM_ERR_SHAPE;
-  if (dtype != VM_F32 || (options & VM_ZOH) || dstate > 16 || dim > kMaxPlanes)
-    return VM_ERR_UNSUPPORTED;
+  if ((options & VM_ZOH) || dstate > 16 || dim > kMaxPlanes) return VM_ERR_UNSUPPORTED;
   if (!dims_ok({batch, dstate, L}, bc)) return VM_ERR_SHAPE;
   // 32-bit offsets of the kernel's per-block checkpoints and partial sums
   if (16 * 64 * vmk::scan_bwd_tiles(L) >= (int64_t{1} << 31) || 64 * L >= (int64_t{1} << 31))
@@ -582,13 +596,15 @@ int vm_selective_scan_bwd(const vm_scan_dir *p, const void *z, const void *dout,
   int st = check_bwd_common(dtype, options, batch, dim, seqlen, dstate, z, dout, dz, &tok, &bc);
   if (st != VM_OK) return st;
   if (!flag_ok(reverse)) return VM_ERR_FLAG;
-  st = check_dir(p, tok, tok, batch, seqlen, dim, dstate, 4, Span());
+  const bool bf16 = dtype == VM_BF16;
+  const int es = bf16 ? 2 : 4;
+  st = check_dir(p, tok, tok, batch, seqlen, dim, dstate, es, Span());
   if (st != VM_OK) return st;
   if (p->conv_w != nullptr) return VM_ERR_UNSUPPORTED;
   std::vector<Span> ins, outs;
-  dir_spans(p, tok, batch, seqlen, dim, dstate, ins);
-  ins.push_back(span(z, tok * 4));
-  ins.push_back(span(dout, tok * 4));
+  dir_spans(p, tok, batch, seqlen, dim, dstate, es, ins);
+  ins.push_back(span(z, tok * es));
+  ins.push_back(span(dout, tok * es));
   st = check_grad(g, tok, bc, dim, dstate, ins, outs);
   if (st != VM_OK) return st;
   for (const Span &o : outs)
@@ -598,17 +614,21 @@ int vm_selective_scan_bwd(const vm_scan_dir *p, const void *z, const void *dout,
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   Scratch ws(s);
-  // all temporary memory first, so that a failed allocation launches nothing
+  // temporary memory first, so that a failed allocation launches nothing
   BwdScratch bs;
   st = bs.get(ws, batch, dim, seqlen, dstate);
   float *y = z != nullptr ? ws.get(tok, &st) : nullptr;
   float *dyb = z != nullptr ? ws.get(tok, &st) : nullptr;
   if (st != VM_OK) return st;
-  const float *dy = static_cast<const float *>(dout);
+  // bf16 inputs run the fp32 path on widened copies
+  const vm_scan_dir w = widen_dir(p, tok, batch, seqlen, dstate, bf16, ws, s, &st);
+  const float *z32 = as_f32(z, tok, bf16 && z != nullptr, ws, s, &st);
+  const float *dy = as_f32(dout, tok, bf16, ws, s, &st);
+  if (st != VM_OK) return st;
   if (z != nullptr) {
     // the ungated forward output, for dz, then dy = dout * SiLU(z)
     vmk::ScanArgs a = {};
-    a.dir[0] = a.dir[1] = resolve_dir(p, batch, dstate, seqlen, false, ws, s, &st);
+    a.dir[0] = a.dir[1] = resolve_dir(&w, batch, dstate, seqlen, false, ws, s, &st);
     a.out = y;
     a.batch = batch;
     a.dim = dim;
@@ -621,12 +641,11 @@ int vm_selective_scan_bwd(const vm_scan_dir *p, const void *z, const void *dout,
     if (!vmk::scan_offsets_fit(plan, a, false)) return VM_ERR_UNSUPPORTED;
     st = hip_status(vmk::launch_scan(plan, a, false, s));
     if (st == VM_OK)
-      st = hip_status(vmk::launch_gate_bwd(y, static_cast<const float *>(z), dy, dyb,
-                                           static_cast<float *>(dz), tok, 1.0f, s));
+      st = hip_status(vmk::launch_gate_bwd(y, z32, dy, dyb, static_cast<float *>(dz), tok, 1.0f, s));
     if (st != VM_OK) return st;
     dy = dyb;
   }
-  return run_bwd(p, dy, g, bs, batch, dim, seqlen, dstate, options, reverse, ws, s);
+  return run_bwd(&w, dy, g, bs, batch, dim, seqlen, dstate, options, reverse, ws, s);
 }
 
 int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void *z,
@@ -637,15 +656,17 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
   int st = check_bwd_common(dtype, options, batch, dim, seqlen, dstate, z, dout, dz, &tok, &bc);
   if (st != VM_OK) return st;
   if (!std::isfinite(combine_scale)) return VM_ERR_UNSUPPORTED;
-  st = check_dir(fwd, tok, tok, batch, seqlen, dim, dstate, 4, Span());
-  if (st == VM_OK) st = check_dir(bwd, tok, tok, batch, seqlen, dim, dstate, 4, Span());
+  const bool bf16 = dtype == VM_BF16;
+  const int es = bf16 ? 2 : 4;
+  st = check_dir(fwd, tok, tok, batch, seqlen, dim, dstate, es, Span());
+  if (st == VM_OK) st = check_dir(bwd, tok, tok, batch, seqlen, dim, dstate, es, Span());
   if (st != VM_OK) return st;
   if (fwd->conv_w != nullptr || bwd->conv_w != nullptr) return VM_ERR_UNSUPPORTED;
   std::vector<Span> ins, outs;
-  dir_spans(fwd, tok, batch, seqlen, dim, dstate, ins);
-  dir_spans(bwd, tok, batch, seqlen, dim, dstate, ins);
-  ins.push_back(span(z, tok * 4));
-  ins.push_back(span(dout, tok * 4));
+  dir_spans(fwd, tok, batch, seqlen, dim, dstate, es, ins);
+  dir_spans(bwd, tok, batch, seqlen, dim, dstate, es, ins);
+  ins.push_back(span(z, tok * es));
+  ins.push_back(span(dout, tok * es));
   st = check_grad(gf, tok, bc, dim, dstate, ins, outs);
   if (st == VM_OK) st = check_grad(gb, tok, bc, dim, dstate, ins, outs);
   if (st != VM_OK) return st;
@@ -663,10 +684,16 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
   BwdScratch bs;
   if (st == VM_OK) st = bs.get(ws, batch, dim, seqlen, dstate);
   if (st != VM_OK) return st;
+  // bf16 inputs run the fp32 path on widened copies
+  const vm_scan_dir wf = widen_dir(fwd, tok, batch, seqlen, dstate, bf16, ws, s, &st);
+  const vm_scan_dir wb = widen_dir(bwd, tok, batch, seqlen, dstate, bf16, ws, s, &st);
+  const float *z32 = as_f32(z, tok, bf16 && z != nullptr, ws, s, &st);
+  const float *dout32 = as_f32(dout, tok, bf16, ws, s, &st);
+  if (st != VM_OK) return st;
   if (z != nullptr) {
     vmk::ScanArgs a = {};
-    a.dir[0] = resolve_dir(fwd, batch, dstate, seqlen, false, ws, s, &st);
-    a.dir[1] = resolve_dir(bwd, batch, dstate, seqlen, false, ws, s, &st);
+    a.dir[0] = resolve_dir(&wf, batch, dstate, seqlen, false, ws, s, &st);
+    a.dir[1] = resolve_dir(&wb, batch, dstate, seqlen, false, ws, s, &st);
     if (st != VM_OK) return st;
     a.out = y;
     a.batch = batch;
@@ -678,12 +705,11 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
     st = launch_bidir(a, false, ws, s);
     if (st != VM_OK) return st;
   }
-  st = hip_status(vmk::launch_gate_bwd(y, static_cast<const float *>(z),
-                                       static_cast<const float *>(dout), dy,
-                                       static_cast<float *>(dz), tok, combine_scale, s));
+  st = hip_status(vmk::launch_gate_bwd(y, z32, dout32, dy, static_cast<float *>(dz), tok,
+                                       combine_scale, s));
   if (st != VM_OK) return st;
-  st = run_bwd(fwd, dy, gf, bs, batch, dim, seqlen, dstate, options, 0, ws, s);
-  if (st == VM_OK) st = run_bwd(bwd, dy, gb, bs, batch, dim, seqlen, dstate, options, 1, ws, s);
+  st = run_bwd(&wf, dy, gf, bs, batch, dim, seqlen, dstate, options, 0, ws, s);
+  if (st == VM_OK) st = run_bwd(&wb, dy, gb, bs, batch, dim, seqlen, dstate, options, 1, ws, s);
   return st;
 }
 

@@ -247,8 +247,9 @@ def test_bwd_argument_checks(lib):
     g0 = grads(FAKE * 5)
     g0.dC = None
     assert single(g=g0) == 1
-    assert single(dtype=1) == 6                             # bf16: fp32 only
+    assert single(dtype=2) == 3
     assert single(opt=3) == 6                               # zero-order hold: not here
+    assert single(dtype=1, opt=3) == 6
     assert single(N=17) == 6
     assert single(rev=2) == 4
     assert single(opt=4) == 4
@@ -268,5 +269,5 @@ def test_bwd_argument_checks(lib):
                                      ctypes.byref(gf), ctypes.byref(g2), None, 2, 4, 5, 16, dtype, 1, None)
 
     assert bidir(scale=float("inf")) == 6
-    assert bidir(dtype=1) == 6
+    assert bidir(dtype=5) == 3
     assert bidir(g2=gf) == 5                                # both directions' gradients in one set

@@ -714,6 +714,22 @@ def test_bwd_bidir(L):
     assert_close(host(dz), wdz, FP32_TOL, "dz")
 
 
+def test_bwd_bf16():
+    # bf16 inputs: the pass runs in fp32 on their exact widening, so the
+    # gradients match the oracle's (on the same bf16 values) to fp32 accuracy
+    _case("bwd bf16 bidir L150")
+    fwd, bwd, z = wl.bidir_inputs(3050, 2, 40, 150, device=DEV, dtype=torch.bfloat16, perturb=True)
+    dout = torch.randn(fwd["u"].shape, generator=wl.generator(3051, DEV), device=DEV).to(torch.bfloat16)
+    gf, gb, dz = vm.vm_bidir_scan_bwd(fwd, bwd, dout, z=z)
+    torch.cuda.synchronize()
+    assert gf["u"].dtype == torch.float32 and dz.dtype == torch.float32
+    wf, wb, wdz, _ = ograd.bidir_scan_grad(host_dir(fwd), host_dir(bwd), host(dout), z=host(z))
+    for k in _GRAD_KEYS:
+        assert_close(host(gf[k]), wf[k], FP32_TOL, f"fwd d{k}")
+        assert_close(host(gb[k]), wb[k], FP32_TOL, f"bwd d{k}")
+    assert_close(host(dz), wdz, FP32_TOL, "dz")
+
+
 def test_bwd_deterministic():
     _case("bwd deterministic")
     fwd, bwd, z = wl.bidir_inputs(3000, 4, 64, 100, device=DEV)
