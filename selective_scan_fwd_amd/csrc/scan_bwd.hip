@@ -40,16 +40,25 @@ struct BwdLayout {
   static constexpr int PST = 4 * T + 4;               // (dt, dt u, dy, -) per step, per row
   static constexpr int PREP = kR * PST;
   static constexpr int BC = 32 * T;                   // B in slots 0..15, C in 16..31
+  static constexpr int STAGE = PREP + BC;
   static constexpr int QSTR = T + 1;
   static constexpr int PART = 2 * 64 * QSTR;          // per-lane sums of g B and g a h A
-  static constexpr int RED = 2 * 16 * T * kR;         // dC, dB contributions [2][n][q][r]
-  static constexpr int TOTAL = PREP + BC + PART + RED;
+  // The partial sums share the staging area: a tile's staged values are in
+  // registers before its adjoint writes them.
+  static constexpr int AREA = STAGE > PART ? STAGE : PART;
+  // dC, then dB, contributions [n][q][r].  Row (n, q) starts at
+  // (n T + q) RSTR + (n / 4) 16: a lane's 16-byte reads of consecutive rows
+  // then fall in distinct banks, and so do the writes of the four 16-lane
+  // rows of a wave (state groups n / 4).
+  static constexpr int RSTR = kR + 4;
+  static constexpr int RED = 16 * T * RSTR + 64;
+  static constexpr int TOTAL = AREA + RED;
 };
 
 // The tile's states and decays stay in registers (64 VGPRs with 8-step
 // tiles; 4-step tiles fit more workgroups but measured 1.6x slower for their
-// per-tile reductions); the LDS area (24 KB) allows six workgroups per CU,
-// so the register budget is set for two waves per SIMD.
+// per-tile reductions), which sets the register budget at two waves per
+// SIMD; the LDS area (15 KB) is small enough not to lower that.
 template <int T>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 scan_bwd_kernel(const BwdArgs p) {
@@ -59,8 +68,8 @@ scan_bwd_kernel(const BwdArgs p) {
   extern __shared__ float smem[];
   float *const prep = smem;                       // [R][PST]
   float *const bcs = prep + Lay::PREP;            // [T][32]
-  float *const part = bcs + Lay::BC;              // [2][64][QSTR]
-  float *const red = part + Lay::PART;            // [2][16][T][R]
+  float *const part = smem;                       // [2][64][QSTR], over the staging area
+  float *const red = smem + Lay::AREA;            // [16][T][R], padded rows
 
   const int lane = threadIdx.x;
   const int sp = lane / kR, r = lane % kR;
@@ -273,6 +282,32 @@ scan_bwd_kernel(const BwdArgs p) {
         as[q][jn] = a;
       }
     }
+    const int jT = j * T;
+    // dC_t = sum over the block's channels of dy_t h_t, per (n, step): the
+    // contributions meet in LDS, and the dB ones reuse the area afterwards
+    // (a wave's LDS accesses execute in program order).
+    auto reduce_red = [&](const Rsrc &dst) {
+#pragma unroll
+      for (int m = 0; m < 16 * T / 64; ++m) {
+        const int c = lane + 64 * m;                  // (n, q), q fastest
+        const int q = c % T, n = c / T;
+        const float4 *src = reinterpret_cast<const float4 *>(red + c * Lay::RSTR + (n / 4) * 16);
+        float sum = 0.0f;
+#pragma unroll
+        for (int v = 0; v < kR / 4; ++v) {
+          const float4 x4 = src[v];
+          sum += (x4.x + x4.y) + (x4.z + x4.w);
+        }
+        const int t = jT + (rev ? T - 1 - q : q);
+        bstore<float>(dst, pin_u(t < L && n < dstate ? static_cast<uint32_t>(n * L + t) * 4u : kOob), sum);
+      }
+    };
+#pragma unroll
+    for (int q = 0; q < T; ++q)
+#pragma unroll
+      for (int jn = 0; jn < kNS; ++jn)
+        red[((n0 + jn) * T + q) * Lay::RSTR + sp * 16 + r] = pqs[q].z * hs[q][jn];
+    reduce_red(rPC);
     // adjoint back through the tile
 #pragma unroll
     for (int q = T - 1; q >= 0; --q) {
@@ -289,9 +324,7 @@ scan_bwd_kernel(const BwdArgs p) {
           default: Bb = row_bcast<3>(bv); Cb = row_bcast<kNS + 3>(bv); break;
         }
         const float g = __builtin_fmaf(Cb, pq.z, gn[jn]);
-        const int n = n0 + jn;
-        red[((0 * 16 + n) * T + q) * kR + r] = pq.z * hs[q][jn];     // dC
-        red[((1 * 16 + n) * T + q) * kR + r] = g * pq.y;             // dB
+        red[((n0 + jn) * T + q) * Lay::RSTR + sp * 16 + r] = g * pq.y;   // dB
         sgB = __builtin_fmaf(g, Bb, sgB);
         const float ah = as[q][jn] * (q > 0 ? hs[q > 0 ? q - 1 : 0][jn] : h0[jn]);   // a_t h_{t-1}
         const float gq = g * ah;
@@ -303,7 +336,6 @@ scan_bwd_kernel(const BwdArgs p) {
       part[(1 * 64 + lane) * Lay::QSTR + q] = sqA;
     }
     // per element: du, ddelta (the four state groups of the channel summed)
-    const int jT = j * T;
     const bool in_seq = tq < L - jT;
 #pragma unroll
     for (int i = 0; i < PE; ++i) {
@@ -323,22 +355,8 @@ scan_bwd_kernel(const BwdArgs p) {
       accD[i] = __builtin_fmaf(edy[i], eu[i], accD[i]);
       accB[i] += dd;
     }
-    // dB, dC: this block's sum over its 16 channels, per (n, step)
-#pragma unroll
-    for (int m = 0; m < 2 * 16 * T / 64; ++m) {
-      const int c = lane + 64 * m;                    // (which, n, q), q fastest
-      const int q = c % T, n = (c / T) % 16, which = c / (16 * T);
-      const float4 *src = reinterpret_cast<const float4 *>(red + ((which * 16 + n) * T + q) * kR);
-      float sum = 0.0f;
-#pragma unroll
-      for (int v = 0; v < kR / 4; ++v) {
-        const float4 x4 = src[v];
-        sum += (x4.x + x4.y) + (x4.z + x4.w);
-      }
-      const int t = jT + (rev ? T - 1 - q : q);
-      const uint32_t o = pin_u(t < L && n < dstate ? static_cast<uint32_t>(n * L + t) * 4u : kOob);
-      bstore<float>(which == 0 ? rPC : rPB, o, sum);
-    }
+    // dB: this block's sum over its 16 channels, per (n, step)
+    reduce_red(rPB);
   }
 
   // ---- per batch row: dA, and dD, dbias (the T lanes of a channel summed)
