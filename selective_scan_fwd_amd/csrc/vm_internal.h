@@ -150,10 +150,11 @@ hipError_t launch_mean_pool(const void *u, float *pooled, int64_t rows, int64_t 
 hipError_t launch_repeat_gate(const float *y, const void *z, void *out, int64_t rows, int64_t H,
                               int64_t W, int axis, float scale, bool bf16, hipStream_t s);
 hipError_t launch_to_f32(const void *src, float *dst, int64_t n, hipStream_t s);
-// [planes][H][W] -> [planes][W][H]
+// Causal depthwise conv1d (width 4) + SiLU over [rows][L] (row = b * dim + d).
 hipError_t launch_conv1d_silu(const void *x, const float *w, const float *cb, void *out,
                               int64_t rows, int64_t L, int64_t dim, int reverse, bool bf16,
                               hipStream_t s);
+// [planes][H][W] -> [planes][W][H]
 hipError_t launch_transpose(const void *in, void *out, int64_t planes, int64_t H, int64_t W, bool bf16,
                             hipStream_t s);
 // out = scale * (yr + transpose(yc)) * SiLU(z); yr [planes][H][W] fp32 (may
