@@ -22,6 +22,35 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kPlaneLds = 16384;  // floats of a staged H x W plane (64 KB)
 
+typedef float vf4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t vu2_t __attribute__((ext_vector_type(2)));
+
+// Four consecutive values of T moved as one access: 16 bytes of fp32, or 8
+// of bf16.  Streaming (nontemporal) forms serve data touched once.
+template <typename T> struct Raw4;
+template <> struct Raw4<float> {
+  using V = vf4_t;
+  static __device__ __forceinline__ V pack(float a, float b, float c, float d) { return V{a, b, c, d}; }
+};
+template <> struct Raw4<bf16_t> {
+  using V = vu2_t;
+  static __device__ __forceinline__ V pack(bf16_t a, bf16_t b, bf16_t c, bf16_t d) {
+    return V{a | (static_cast<uint32_t>(b) << 16), c | (static_cast<uint32_t>(d) << 16)};
+  }
+};
+template <typename T>
+__device__ __forceinline__ typename Raw4<T>::V load_raw4_stream(const T *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const typename Raw4<T>::V *>(p));
+}
+template <typename T>
+__device__ __forceinline__ void store_raw4(T *p, typename Raw4<T>::V v) {
+  *reinterpret_cast<typename Raw4<T>::V *>(p) = v;
+}
+template <typename T>
+__device__ __forceinline__ void store_raw4_stream(T *p, typename Raw4<T>::V v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<typename Raw4<T>::V *>(p));
+}
+
 // Step t of group k -> (row, col) on the padded grid.  Offsets (0,0), (1,0),
 // (0,1), (1,1); even groups walk the half grid row-major, odd ones
 // column-major.  Position t = a * n + b of a walk with n entries per line
@@ -64,18 +93,63 @@ __device__ __forceinline__ void copy_to_lds(T *dst, const T *__restrict__ src, i
   }
 }
 
+// The same for n a multiple of 4, src and dst aligned to 4 values: one
+// streaming load of 4 values per access (the source is read once).
+template <typename T>
+__device__ __forceinline__ void copy_to_lds4(T *dst, const T *__restrict__ src, int n) {
+  using V = typename Raw4<T>::V;
+  constexpr int U = 4;
+  const int n4 = n / 4;
+  for (int i0 = threadIdx.x; i0 < n4; i0 += U * kThreads) {
+    V v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kThreads;
+      v[u] = i < n4 ? load_raw4_stream(src + 4 * i) : V{};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kThreads;
+      if (i < n4) reinterpret_cast<V *>(dst)[i] = v[u];
+    }
+  }
+}
+
 // One workgroup per (b, c) plane: stage the plane in LDS with coalesced
-// loads, then emit the four streams with coalesced stores.
+// loads, then emit the four streams with coalesced stores.  Vector path
+// (staged, H W and Lg multiples of 4, aligned pointers): 4-value loads and
+// stores, each thread emitting 4 consecutive steps of a group.
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
 atrous_gather_kernel(const T *__restrict__ x, T *__restrict__ streams, int64_t ch, int H, int W,
-                     int staged) {
+                     int staged, int vec) {
   extern __shared__ unsigned char plane_raw[];
   T *plane = reinterpret_cast<T *>(plane_raw);  // H * W values when staged
   const int64_t pid = blockIdx.x;               // b * ch + c
   const int64_t b = pid / ch, c = pid - b * ch;
   const int hr = (H + 1) / 2, hc = (W + 1) / 2, Lg = hr * hc;
   const T *src = x + pid * H * W;
+  if (vec) {
+    copy_to_lds4(plane, src, H * W);
+    __syncthreads();
+    for (int k = 0; k < 4; ++k) {
+      T *dst = streams + ((b * 4 + k) * ch + c) * Lg;
+      const int n = (k & 1) == 0 ? hc : hr;
+      for (int e = threadIdx.x; e < Lg / 4; e += kThreads) {
+        int la = (4 * e) / n, lb = 4 * e - la * n;  // (line, position) of step 4 e
+        T v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = (k & 1) == 0 ? la : lb, cc = (k & 1) == 0 ? lb : la;
+          const int yy = 2 * r + (k & 1), xx = 2 * cc + (k >> 1);
+          v[u] = (yy < H && xx < W) ? plane[yy * W + xx] : T(0);
+          if (++lb == n) { lb = 0; ++la; }
+        }
+        store_raw4(dst + 4 * e, Raw4<T>::pack(v[0], v[1], v[2], v[3]));
+      }
+    }
+    return;
+  }
   if (staged) {
     copy_to_lds(plane, src, H * W);
     __syncthreads();
@@ -98,16 +172,36 @@ atrous_gather_kernel(const T *__restrict__ x, T *__restrict__ streams, int64_t c
 // k = (row & 1) + 2 (col & 1) at step t of that group; copy it, write each
 // output once (no sums).  When the plane's four streams fit in LDS they are
 // staged there first with coalesced loads; the plane is then written with
-// coalesced stores.
+// coalesced stores.  Vector path (staged, Lg and W multiples of 4, aligned
+// pointers): 4-value streaming loads and stores, each thread writing 4
+// consecutive pixels of a row.
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
 atrous_scatter_kernel(const T *__restrict__ streams, T *__restrict__ y, int64_t ch, int H, int W,
-                      int staged) {
+                      int staged, int vec) {
   extern __shared__ unsigned char st_raw[];
   T *st = reinterpret_cast<T *>(st_raw);        // [4][Lg] when staged
   const int64_t pid = blockIdx.x;
   const int64_t b = pid / ch, c = pid - b * ch;
   const int hr = (H + 1) / 2, hc = (W + 1) / 2, Lg = hr * hc;
+  if (vec) {
+    for (int k = 0; k < 4; ++k) copy_to_lds4(st + k * Lg, streams + ((b * 4 + k) * ch + c) * Lg, Lg);
+    __syncthreads();
+    T *dst = y + pid * H * W;
+    for (int e = threadIdx.x; e < H * W / 4; e += kThreads) {
+      const int yy = (4 * e) / W, x0 = 4 * e - yy * W;
+      T v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int xx = x0 + u;
+        const int k = (yy & 1) + 2 * (xx & 1);
+        const int r = yy >> 1, cc = xx >> 1;
+        v[u] = st[k * Lg + ((k & 1) == 0 ? r * hc + cc : cc * hr + r)];
+      }
+      store_raw4_stream(dst + 4 * e, Raw4<T>::pack(v[0], v[1], v[2], v[3]));
+    }
+    return;
+  }
   if (staged) {
     for (int k = 0; k < 4; ++k) copy_to_lds(st + k * Lg, streams + ((b * 4 + k) * ch + c) * Lg, Lg);
     __syncthreads();
@@ -141,8 +235,6 @@ __device__ __forceinline__ void store4(bf16_t *p, float4 v) {
 // Streaming forms (nontemporal hint) for the full-resolution tensors of the
 // pooled path, each touched once: measured 5 % faster there.  The SS2D and
 // conv kernels keep plain accesses, whose outputs the next kernel reads.
-typedef float vf4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t vu2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float4 load4_stream(const float *p) {
   const vf4_t v = __builtin_nontemporal_load(reinterpret_cast<const vf4_t *>(p));
   return make_float4(v.x, v.y, v.z, v.w);
@@ -530,6 +622,8 @@ unsigned stream_grid(int64_t n) {
   return static_cast<unsigned>(g < cap ? g : cap);
 }
 
+bool aligned(const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
 }  // namespace
 
 hipError_t launch_atrous_gather(const void *x, void *streams, int64_t batch, int64_t ch,
@@ -538,14 +632,17 @@ hipError_t launch_atrous_gather(const void *x, void *streams, int64_t batch, int
   if (planes == 0) return hipSuccess;
   const int staged = (H * W <= kPlaneLds) ? 1 : 0;
   const size_t lds = staged ? static_cast<size_t>(H * W) * (bf16 ? 2 : 4) : 0;
+  const int64_t Lg = ((H + 1) / 2) * ((W + 1) / 2);
+  const uintptr_t va = bf16 ? 8 : 16;
+  const int vec = staged && (H * W) % 4 == 0 && Lg % 4 == 0 && aligned(x, va) && aligned(streams, va);
   if (bf16)
     hipLaunchKernelGGL(atrous_gather_kernel<bf16_t>, dim3(planes), dim3(kThreads), lds, s,
                        static_cast<const bf16_t *>(x), static_cast<bf16_t *>(streams), ch,
-                       static_cast<int>(H), static_cast<int>(W), staged);
+                       static_cast<int>(H), static_cast<int>(W), staged, vec);
   else
     hipLaunchKernelGGL(atrous_gather_kernel<float>, dim3(planes), dim3(kThreads), lds, s,
                        static_cast<const float *>(x), static_cast<float *>(streams), ch,
-                       static_cast<int>(H), static_cast<int>(W), staged);
+                       static_cast<int>(H), static_cast<int>(W), staged, vec);
   return hipGetLastError();
 }
 
@@ -556,18 +653,19 @@ hipError_t launch_atrous_scatter(const void *streams, void *y, int64_t batch, in
   const int64_t Lg = ((H + 1) / 2) * ((W + 1) / 2);
   const int staged = (4 * Lg <= kPlaneLds) ? 1 : 0;
   const size_t lds = staged ? static_cast<size_t>(4 * Lg) * (bf16 ? 2 : 4) : 0;
+  const uintptr_t va = bf16 ? 8 : 16;
+  const int vec = staged && Lg % 4 == 0 && W % 4 == 0 && aligned(streams, va) && aligned(y, va);
   if (bf16)
     hipLaunchKernelGGL(atrous_scatter_kernel<bf16_t>, dim3(planes), dim3(kThreads), lds, s,
                        static_cast<const bf16_t *>(streams), static_cast<bf16_t *>(y), ch,
-                       static_cast<int>(H), static_cast<int>(W), staged);
+                       static_cast<int>(H), static_cast<int>(W), staged, vec);
   else
     hipLaunchKernelGGL(atrous_scatter_kernel<float>, dim3(planes), dim3(kThreads), lds, s,
                        static_cast<const float *>(streams), static_cast<float *>(y), ch,
-                       static_cast<int>(H), static_cast<int>(W), staged);
+                       static_cast<int>(H), static_cast<int>(W), staged, vec);
   return hipGetLastError();
 }
 
-bool aligned(const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
 // The four-wide transpose and merge read and write rows of both orientations
 // four at a time: H and W multiples of 4, planes aligned to four elements.

@@ -174,7 +174,11 @@ def test_deterministic():
 
 
 # ---------------------------------------------------------------- atrous
-SHAPES = [(4, 6), (3, 5), (1, 1), (2, 3), (5, 2), (1, 7), (6, 1), (56, 56), (57, 57), (130, 9)]
+# Vector paths: (8, 6) gathers with 4-value accesses but scatters per value
+# (W % 4 != 0); (6, 8), (7, 8), (56, 56), (100, 100) take them both ways,
+# (7, 8) with a padded row; (129, 130) exceeds the LDS staging limit.
+SHAPES = [(4, 6), (3, 5), (1, 1), (2, 3), (5, 2), (1, 7), (6, 1), (56, 56), (57, 57), (130, 9),
+          (8, 6), (6, 8), (7, 8), (100, 100), (129, 130)]
 
 
 @pytest.mark.parametrize("H,W", SHAPES)
@@ -195,6 +199,30 @@ def test_atrous_bit_exact(H, W, dtype):
     y2 = vm.vm_atrous_scatter(s2, H, W)
     torch.cuda.synchronize()
     assert bits_equal(y2, oracle.atrous_scatter(host(s2), H, W))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_atrous_misaligned_views(dtype):
+    """Tensors starting one element past an aligned address take the per-value
+    paths; the results are bit-identical to the aligned call's."""
+    _case(f"atrous misaligned {dtype}")
+    H = W = 56
+    g = wl.generator(311, DEV)
+    x = torch.randn((2, 3, H, W), generator=g, device=DEV).to(dtype)
+    ref_s = vm.vm_atrous_gather(x)
+    ref_y = vm.vm_atrous_scatter(ref_s, H, W)
+    xb = torch.empty(x.numel() + 1, device=DEV, dtype=dtype)
+    xm = xb[1:].view(x.shape)
+    xm.copy_(x)
+    sb = torch.empty(ref_s.numel() + 1, device=DEV, dtype=dtype)
+    sm = sb[1:].view(ref_s.shape)
+    vm.vm_atrous_gather(xm, out=sm)
+    yb = torch.empty(x.numel() + 1, device=DEV, dtype=dtype)
+    ym = yb[1:].view(x.shape)
+    vm.vm_atrous_scatter(sm, H, W, out=ym)
+    torch.cuda.synchronize()
+    assert bits_equal(sm, host(ref_s))
+    assert bits_equal(ym, host(ref_y))
 
 
 def test_atrous_pad_is_positive_zero():
