@@ -157,8 +157,11 @@ __host__ __device__ inline int xchg_stride(int64_t n, int T) {
 // conv, whose weights and carried inputs do not fit 128 VGPRs), 2 with
 // 16-step tiles (whose three tiles in flight and staged copies need about
 // 190 VGPRs, 240 with the conv).
+// A bidirectional workgroup holds one or two row blocks (DIRS waves each):
+// with two, its four waves land on distinct SIMDs and every SIMD of a CU
+// carries the same number of waves.
 template <typename Tin, int SPLIT, int DIRS, int XMODE, int T, int OPT>
-__global__ void __launch_bounds__(64 * DIRS)
+__global__ void __launch_bounds__(DIRS == 2 ? 256 : 64)
 __attribute__((amdgpu_waves_per_eu(T == 16 ? 2 : ((OPT & kOptConv) != 0 ? 3 : 4))))
 scan_kernel(const ScanArgs p) {
   constexpr bool ZOH = (OPT & kOptZoh) != 0;
@@ -175,43 +178,53 @@ scan_kernel(const ScanArgs p) {
 
   extern __shared__ float smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nsub = static_cast<int>(blockDim.x) / (64 * DIRS);   // row blocks per workgroup
+  const int sub = wave / DIRS;                   // row block within the workgroup
+  const int dw = wave - sub * DIRS;              // direction wave of the row block
   const int lane = threadIdx.x & 63;
-  float *const prep = smem + wave * Lay::WAVE;   // [R][PSTR]
+  const int64_t dim = p.dim;
+  const int L = static_cast<int>(p.L);
+  const int XS = xchg_stride(L, T);
+  float *const sbase = smem + sub * (DIRS * Lay::WAVE + (XMODE == kXLds ? R * XS : 0));
+  float *const prep = sbase + dw * Lay::WAVE;    // [R][PSTR]
   float *const bcs = prep + Lay::PREP;           // [T][32]
   float *const xs = bcs + Lay::BC;               // [R][XH] conv input (CONV)
   float *const part = prep;                      // [64 lanes][QSTR], shares the staging area
-  float *const xlds = smem + DIRS * Lay::WAVE;   // [R][XS]   (kXLds)
+  float *const xlds = sbase + DIRS * Lay::WAVE;  // [R][XS]   (kXLds)
 
   const int sp = lane / R;                       // state group
   const int r = lane % R;                        // channel within the block
-  const bool rev = DIRS == 2 ? wave == 1 : p.reverse != 0;
-  const bool fwd_wave = DIRS == 2 && wave == 0;
+  const bool rev = DIRS == 2 ? dw == 1 : p.reverse != 0;
+  const bool fwd_wave = DIRS == 2 && dw == 0;
 
-  const int64_t dim = p.dim;
-  const int L = static_cast<int>(p.L);
+  // Row block blk = (batch row b, channels d0 ..).  A workgroup's last row
+  // blocks may lie past the end: they get no rows, so every access of theirs
+  // is out of range, and they still take part in the barriers.
   const int nrb = static_cast<int>((dim + R - 1) / R);
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int blk_all = xcd_remap(blockIdx.x, gridDim.x) * nsub + sub;
+  const bool valid = blk_all < p.batch * nrb;
+  const int blk = valid ? blk_all : 0;
   const int b = blk / nrb;
   const int d0 = (blk - b * nrb) * R;
-  const int rows = static_cast<int>(dim - d0 < R ? dim - d0 : R);
+  const int rows = valid ? static_cast<int>(dim - d0 < R ? dim - d0 : R) : 0;
   const int nt = (L + T - 1) / T;
   const int half = (nt + 1) / 2;                 // forward wave's first-visit tiles
-  const int XS = xchg_stride(L, T);
   const int dstate = p.dstate;
   const bool gated = p.z != nullptr;
 
   // Resources: the block's [rows x L] slab of each token tensor (rows past
   // dim are out of range), one batch row of B and C, the block's exchange
   // rows (kXGlobal).
-  const DirPtrs P = p.dir[DIRS == 2 ? wave : 0];
+  const DirPtrs P = p.dir[DIRS == 2 ? dw : 0];
   const int64_t rowbase = (static_cast<int64_t>(b) * dim + d0) * L;
   const uint32_t slab = static_cast<uint32_t>(rows) * static_cast<uint32_t>(L) * ES;
   const Rsrc rU = make_rsrc(static_cast<const Tin *>(P.u) + rowbase, slab);
   const Rsrc rD = make_rsrc(static_cast<const Tin *>(P.delta) + rowbase, slab);
   const Rsrc rZ = make_rsrc(gated ? static_cast<const Tin *>(p.z) + rowbase : nullptr, gated ? slab : 0);
   const Rsrc rO = make_rsrc(static_cast<Tin *>(p.out) + rowbase, slab);
-  const uint32_t bcext = (static_cast<uint32_t>(dstate - 1) * static_cast<uint32_t>(P.bsn) +
-                          static_cast<uint32_t>(L - 1) * static_cast<uint32_t>(P.bst) + 1) * ES;
+  const uint32_t bcext = valid ? (static_cast<uint32_t>(dstate - 1) * static_cast<uint32_t>(P.bsn) +
+                                  static_cast<uint32_t>(L - 1) * static_cast<uint32_t>(P.bst) + 1) * ES
+                                : 0u;
   const Rsrc rB = make_rsrc(static_cast<const Tin *>(P.B) + static_cast<int64_t>(b) * P.bsb, bcext);
   const Rsrc rC = make_rsrc(static_cast<const Tin *>(P.C) + static_cast<int64_t>(b) * P.bsb, bcext);
   const uint32_t xstride = static_cast<uint32_t>(p.xstride);
@@ -535,7 +548,7 @@ scan_kernel(const ScanArgs p) {
     lds_barrier();
     constexpr int NT = 64 * DIRS, U = 4;
     const int n = rows * L;
-    const int tid = threadIdx.x;
+    const int tid = static_cast<int>(threadIdx.x) - sub * NT;
     int fr = tid / L, ft = tid % L;
     for (int f0 = tid; f0 < n; f0 += U * NT) {
       float v[U];
@@ -601,25 +614,34 @@ ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t L, int dstate, int dirs, 
   (void)dstate;
   ScanPlan pl{};
   pl.dirs = dirs;
-  pl.threads = 64 * dirs;
   // Each channel's 16 states are split over 4 lanes: a two-lane split needs
   // fewer instructions per state but leaves half the waves, and measured
   // slower on every workload tried (fewer waves to hide latency, and a
   // larger LDS exchange per workgroup).
   pl.S = 4;
-  pl.blocks = batch * ((dim + 64 / pl.S - 1) / (64 / pl.S));
+  pl.threads = 64 * dirs;
+  const int64_t nblk = batch * ((dim + 64 / pl.S - 1) / (64 / pl.S));
   // Tile length: 16 steps where the registers allow it (one direction, or
   // the global exchange: longer row segments per load and half the per-tile
   // overhead); 8 for the on-chip exchange, whose LDS footprint grows with T.
+  pl.sub = 1;
   if (dirs == 1) {
     pl.T = 16;
     pl.xmode = kXNone;
   } else {
-    // On-chip exchange while at least four workgroups fit a CU's 160 KB LDS.
+    // On-chip exchange while a row block's area lets four of them share a
+    // CU's 160 KB LDS.
     pl.xmode = lds_bytes(pl.S, 2, 8, kXLds, L, conv) <= 40 * 1024 ? kXLds : kXGlobal;
     pl.T = pl.xmode == kXLds ? 8 : 16;
+    // Two row blocks per workgroup where there are enough of them to give
+    // every CU several workgroups: the balanced SIMDs measured 4 % faster on
+    // the Vim-T step.  Fewer, larger workgroups would leave CUs idle on small
+    // problems; the global exchange measured 1 % slower with two.
+    if (pl.xmode == kXLds && nblk >= 2048) pl.sub = 2;
   }
-  pl.lds = lds_bytes(pl.S, dirs, pl.T, pl.xmode, L, conv);
+  pl.threads *= pl.sub;
+  pl.blocks = (nblk + pl.sub - 1) / pl.sub;
+  pl.lds = static_cast<size_t>(pl.sub) * lds_bytes(pl.S, dirs, pl.T, pl.xmode, L, conv);
   return pl;
 }
 

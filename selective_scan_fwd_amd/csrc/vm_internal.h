@@ -103,8 +103,9 @@ struct ScanPlan {
   int T;        // tile length in steps
   int dirs;     // 1 or 2
   int xmode;    // XMode
-  size_t lds;   // dynamic LDS bytes per wave
-  int threads;  // workgroup size (one wave)
+  int sub;      // row blocks per workgroup
+  size_t lds;   // dynamic LDS bytes per workgroup
+  int threads;  // workgroup size: 64 dirs sub
   int64_t blocks;
 };
 

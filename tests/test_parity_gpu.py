@@ -111,6 +111,21 @@ def test_bidir_fp32(batch, dim, L, bc_layout):
         assert_close(host(out), ref, FP32_TOL, f"bidir s={scale}")
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("L", [9, 37])
+def test_bidir_two_row_blocks_per_workgroup(dtype, L):
+    """Enough row blocks (83 x 25 = 2075, odd) for workgroups of two row
+    blocks: the last workgroup's second row block is empty, and the last row
+    block of each batch row is partial (dim 397 = 24 x 16 + 13)."""
+    _case(f"bidir two row blocks per workgroup {dtype} L{L}")
+    batch, dim = 83, 397
+    fwd, bwd, z = wl.bidir_inputs(400 + L, batch, dim, L, device=DEV, dtype=dtype, perturb=True)
+    out = vm.vm_bidir_scan_fwd(fwd, bwd, z=z, combine_scale=0.5)
+    torch.cuda.synchronize()
+    ref = oracle.bidir_scan(host_dir(fwd), host_dir(bwd), z=host(z), combine_scale=0.5)
+    assert_close(host(out), ref, FP32_TOL if dtype == torch.float32 else BF16_TOL, "two row blocks")
+
+
 def test_bidir_ungated_small_dstate():
     _case("bidir ungated N=3")
     fwd, bwd, _ = wl.bidir_inputs(9, 2, 66, 41, dstate=3, device=DEV, gated=False, perturb=True)
