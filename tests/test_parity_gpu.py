@@ -643,6 +643,34 @@ def test_fused_conv_bidir(L, dtype):
     assert_close(host(out), ref, FP32_TOL if dtype == torch.float32 else BF16_TOL, "fused conv bidir")
 
 
+def test_full_vim_tiny_bidir_fused_conv():
+    """The Vim-T block with its causal conv1d + SiLU inside the scan, at full
+    size (two row blocks per workgroup): sampled batch rows against the
+    oracle, and every element bit-equal to the conv kernels then the scan."""
+    w = wl.WORKLOADS[1]
+    _case(f"full {w.name} fused conv")
+    fwd, bwd, z = wl.bidir_inputs(1002, w.batch, w.dim, w.seqlen, device=DEV, perturb=True)
+    bwd["u"] = fwd["u"]
+    g = wl.generator(1003, DEV)
+    for p in (fwd, bwd):
+        p["conv_w"], p["conv_b"] = wl.conv_params(g, w.dim, DEV)
+    out = vm.vm_bidir_scan_fwd(fwd, bwd, z=z, combine_scale=w.combine_scale)
+    f2 = {k: v for k, v in fwd.items() if not k.startswith("conv")}
+    b2 = {k: v for k, v in bwd.items() if not k.startswith("conv")}
+    f2["u"] = vm.vm_causal_conv1d_silu(fwd["u"], fwd["conv_w"], fwd["conv_b"])
+    b2["u"] = vm.vm_causal_conv1d_silu(bwd["u"], bwd["conv_w"], bwd["conv_b"], reverse=True)
+    two = vm.vm_bidir_scan_fwd(f2, b2, z=z, combine_scale=w.combine_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, two)
+    bsel = [0, 63, 127]
+    dsel = list(range(w.dim))
+    hf, hb = sub_dir(host_dir(fwd), bsel, dsel), sub_dir(host_dir(bwd), bsel, dsel)
+    for h, rev in ((hf, False), (hb, True)):
+        h["u"] = oracle.causal_conv1d_silu(h["u"], h.pop("conv_w"), h.pop("conv_b"), reverse=rev)
+    ref = oracle.bidir_scan(hf, hb, z=host(z)[bsel][:, dsel], combine_scale=w.combine_scale)
+    assert_close(host(out[bsel]), ref, FP32_TOL, "vim-t fused conv full (sampled batches)")
+
+
 @pytest.mark.parametrize("L", [197, 600])
 def test_fused_conv_equals_conv_then_scan(L):
     # the in-kernel convolution takes the same fp32 operations in the same
