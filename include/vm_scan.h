@@ -59,7 +59,9 @@ enum {
                              limits: 32 rows of seqlen + 16 steps, or one
                              batch row of B or C, must span < 2 GiB; the map
                              calls (atrous, pooled, SS2D) take at most
-                             2^24 - 1 planes (batch * channels)              */
+                             2^24 - 1 planes (batch * channels), the scans
+                             at most 2^24 - 1 row blocks of 16 channels
+                             (batch * ceil(dim / 16))                         */
   VM_ERR_HIP = 7,         /* a HIP launch or runtime call failed              */
   VM_ERR_ALLOC = 8        /* temporary device memory could not be obtained    */
 };

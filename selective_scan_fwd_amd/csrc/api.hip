@@ -21,6 +21,10 @@ constexpr int64_t kMaxElems = int64_t{1} << 40;
 // 256-thread workgroup per [H, W] plane on grid x: planes * 256 work-items
 // must stay below 2^32.
 constexpr int64_t kMaxPlanes = (int64_t{1} << 24) - 1;
+// The scan kernels run one to two 16-channel row blocks per workgroup of up
+// to 256 work-items on grid x; the same bound on the row-block count keeps
+// the work-item count below 2^32.
+bool row_blocks_ok(int64_t batch, int64_t dim) { return batch * ((dim + 15) / 16) <= kMaxPlanes; }
 
 struct Span {
   uintptr_t lo = 0, hi = 0;  // [lo, hi)
@@ -100,7 +104,10 @@ hipError_t pool_for_current_device(hipMemPool_t *out) {
   if (e != hipSuccess) return e;
   uint64_t keep = UINT64_MAX;  // keep freed blocks cached for the next call
   e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess) {
+    (void)hipMemPoolDestroy(pool);
+    return e;
+  }
   g_pools[dev] = pool;
   *out = pool;
   return hipSuccess;
@@ -291,7 +298,9 @@ int check_bwd_common(int dtype, int options, int64_t batch, int64_t dim, int64_t
   if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;
   if (!options_ok(options)) return VM_ERR_FLAG;
   if (!dims_ok({batch, dim, L}, tok) || dstate <= 0) return VM_ERR_SHAPE;
-  if ((options & VM_ZOH) || dstate > 16 || dim > kMaxPlanes) return VM_ERR_UNSUPPORTED;
+  // (the parameter-gradient reduction runs one workgroup per channel)
+  if ((options & VM_ZOH) || dstate > 16 || dim > kMaxPlanes || !row_blocks_ok(batch, dim))
+    return VM_ERR_UNSUPPORTED;
   if (!dims_ok({batch, dstate, L}, bc)) return VM_ERR_SHAPE;
   // 32-bit offsets of the kernel's per-block checkpoints and partial sums
   if (16 * 64 * vmk::scan_bwd_tiles(L) >= (int64_t{1} << 31) || 64 * L >= (int64_t{1} << 31))
@@ -333,7 +342,7 @@ int vm_selective_scan_fwd(const vm_scan_dir *p, const void *z, void *out, int64_
   if (!options_ok(options) || !flag_ok(reverse)) return VM_ERR_FLAG;
   int64_t tok = 0, bc = 0;
   if (!dims_ok({batch, dim, seqlen}, &tok) || dstate <= 0) return VM_ERR_SHAPE;
-  if (dstate > 16) return VM_ERR_UNSUPPORTED;
+  if (dstate > 16 || !row_blocks_ok(batch, dim)) return VM_ERR_UNSUPPORTED;
   if (!dims_ok({batch, dstate, seqlen}, &bc)) return VM_ERR_SHAPE;
   if (out == nullptr) return VM_ERR_NULL;
   const int es = dtype == VM_BF16 ? 2 : 4;
@@ -372,7 +381,8 @@ int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
   if (!options_ok(options)) return VM_ERR_FLAG;
   int64_t tok = 0, bc = 0;
   if (!dims_ok({batch, dim, seqlen}, &tok) || dstate <= 0) return VM_ERR_SHAPE;
-  if (dstate > 16 || !std::isfinite(combine_scale)) return VM_ERR_UNSUPPORTED;
+  if (dstate > 16 || !std::isfinite(combine_scale) || !row_blocks_ok(batch, dim))
+    return VM_ERR_UNSUPPORTED;
   if (!dims_ok({batch, dstate, seqlen}, &bc)) return VM_ERR_SHAPE;
   if (out == nullptr) return VM_ERR_NULL;
   const int es = dtype == VM_BF16 ? 2 : 4;

@@ -196,6 +196,19 @@ def test_plane_count_limit(lib):
     assert lib.vm_ss2d_scan_fwd(dirs, FAKE, None, 1.0, FAKE * 3, big, big, 2, 2, 16, 0, 1, None) == 6
 
 
+def test_row_block_count_limit(lib):
+    # scans run one or two 16-channel row blocks per workgroup on grid x: at
+    # most 2^24 - 1 row blocks (batch * ceil(dim / 16))
+    f, b = _dir(FAKE), _dir(FAKE * 2)
+    batch, dim = 1 << 21, 128                               # 2^24 row blocks, L = 1
+    assert _scan(lib, batch=batch, dim=dim, L=1) == 6
+    assert lib.vm_bidir_scan_fwd(ctypes.byref(f), ctypes.byref(b), None, 1.0, FAKE * 3, batch, dim,
+                                 1, 16, 0, 1, None) == 6
+    g = vm.VmScanGrad(*(FAKE * 5 + k * (1 << 32) for k in range(7)))
+    assert lib.vm_selective_scan_bwd(ctypes.byref(f), None, FAKE * 3, ctypes.byref(g), None, batch,
+                                     dim, 1, 16, 0, 1, 0, None) == 6
+
+
 def test_conv_argument_checks(lib):
     def call(x=FAKE, w=FAKE * 2, b=None, out=FAKE * 3, batch=2, dim=4, L=9, rev=0, dtype=0):
         return lib.vm_causal_conv1d_silu(x, w, b, out, batch, dim, L, rev, dtype, None)
