@@ -319,7 +319,10 @@ int vm_selective_scan_bwd(const vm_scan_dir *p, const void *z,
 /*
  * Backward pass of vm_bidir_scan_fwd: gf and gb receive the gradients of the
  * forward and backward directions' inputs, dz (required when z is given) the
- * gate's.  The same limits and temporary memory as vm_selective_scan_bwd.
+ * gate's.  The same limits and temporary memory as vm_selective_scan_bwd,
+ * plus, with z and sequences too long for the on-chip exchange, the
+ * recomputation's fp32 exchange rows (as vm_bidir_scan_fwd).  All temporary
+ * memory is taken before the first launch.
  */
 int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
                       const void *z, const void *dout, float combine_scale,

@@ -184,20 +184,29 @@ vmk::DirPtrs resolve_dir(const vm_scan_dir *p, int64_t batch, int64_t dstate, in
   return d;
 }
 
-// Plans and launches a bidirectional scan whose arguments are filled in
-// except for the exchange buffer.  fp32 output with line-aligned rows
-// doubles as the exchange buffer; otherwise it comes from the pool.
+// Exchange rows of a long bidirectional scan (global exchange): fp32 output
+// with line-aligned rows doubles as the exchange buffer; otherwise it comes
+// from the pool.  Short scans need none.
+int exchange_for(vmk::ScanArgs &a, bool bf16, Scratch &ws) {
+  const vmk::ScanPlan plan = vmk::plan_scan(a.batch, a.dim, a.L, a.dstate, 2, a.conv != 0);
+  if (plan.xmode != vmk::kXGlobal) return VM_OK;
+  int st = VM_OK;
+  a.xstride = vmk::xchg_global_stride(a.L);
+  if (!bf16 && a.xstride == a.L && reinterpret_cast<uintptr_t>(a.out) % 128 == 0)
+    a.xglobal = static_cast<float *>(a.out);
+  else
+    a.xglobal = ws.get(a.batch * a.dim * a.xstride, &st);
+  return st;
+}
+
+// Plans and launches a bidirectional scan whose arguments are filled in,
+// taking its exchange rows (exchange_for) unless the caller already has.
 int launch_bidir(vmk::ScanArgs &a, bool bf16, Scratch &ws, hipStream_t s) {
   const vmk::ScanPlan plan = vmk::plan_scan(a.batch, a.dim, a.L, a.dstate, 2, a.conv != 0);
   int st = VM_OK;
-  if (plan.xmode == vmk::kXGlobal) {
-    a.xstride = vmk::xchg_global_stride(a.L);
-    if (!bf16 && a.xstride == a.L && reinterpret_cast<uintptr_t>(a.out) % 128 == 0) {
-      a.xglobal = static_cast<float *>(a.out);
-    } else {
-      a.xglobal = ws.get(a.batch * a.dim * a.xstride, &st);
-      if (st != VM_OK) return st;
-    }
+  if (plan.xmode == vmk::kXGlobal && a.xglobal == nullptr) {
+    st = exchange_for(a, bf16, ws);
+    if (st != VM_OK) return st;
   }
   if (!vmk::scan_offsets_fit(plan, a, bf16)) return VM_ERR_UNSUPPORTED;
   return hip_status(vmk::launch_scan(plan, a, bf16, s));
@@ -693,6 +702,13 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
   float *y = z != nullptr ? ws.get(tok, &st) : nullptr;
   BwdScratch bs;
   if (st == VM_OK) st = bs.get(ws, batch, dim, seqlen, dstate);
+  vmk::ScanArgs a = {};                 // the forward recomputation (with z)
+  a.out = y;
+  a.batch = batch;
+  a.dim = dim;
+  a.L = seqlen;
+  a.dstate = static_cast<int>(dstate);
+  if (st == VM_OK && z != nullptr) st = exchange_for(a, false, ws);
   if (st != VM_OK) return st;
   // bf16 inputs run the fp32 path on widened copies
   const vm_scan_dir wf = widen_dir(fwd, tok, batch, seqlen, dstate, bf16, ws, s, &st);
@@ -701,15 +717,9 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
   const float *dout32 = as_f32(dout, tok, bf16, ws, s, &st);
   if (st != VM_OK) return st;
   if (z != nullptr) {
-    vmk::ScanArgs a = {};
     a.dir[0] = resolve_dir(&wf, batch, dstate, seqlen, false, ws, s, &st);
     a.dir[1] = resolve_dir(&wb, batch, dstate, seqlen, false, ws, s, &st);
     if (st != VM_OK) return st;
-    a.out = y;
-    a.batch = batch;
-    a.dim = dim;
-    a.L = seqlen;
-    a.dstate = static_cast<int>(dstate);
     a.softplus = (options & VM_DELTA_SOFTPLUS) != 0;
     a.scale = 1.0f;
     st = launch_bidir(a, false, ws, s);
