@@ -5,7 +5,9 @@ The pages pin the backward pass only as automatic differentiation of the
 scan loop (Vision Mamba page, the reference loop of implementation row 4 and
 its training setting), so the oracle is exactly that: the loop of "A state
 retains, writes, and reads" written with plain PyTorch CPU operations in
-float64, differentiated by torch.autograd.  The forward arithmetic follows
+float64, differentiated by torch.autograd.  With zoh=True the write uses the
+zero-order-hold coefficient of the "Norm or Direction?" page (section 3,
+eq. 2) for diagonal A, expm1(dt A) / A per state, in place of dt.  The forward arithmetic follows
 the C oracle's order (flip, scan, flip for the reverse direction) so that the
 two forwards agree to rounding; tests pin the gradients to central finite
 differences of the C oracle.
@@ -25,7 +27,20 @@ def _t(a, grad=True):
     return t.requires_grad_(grad)
 
 
-def _scan_loop(u, delta, A, B, C, D, bias, delta_softplus):
+def _zoh_coef(dt, A):
+    """expm1(dt A) / A, written as dt phi(x) with phi(x) = expm1(x) / x and
+    x = dt A.  Near x = 0 (A = 0 included, where the coefficient is dt) phi
+    is its Taylor series, so that the value and its derivatives stay exact
+    there."""
+    x = dt * A
+    small = x.abs() < 1e-3
+    xs = torch.where(small, torch.ones_like(x), x)
+    phi = torch.where(small, 1 + x * (1 / 2 + x * (1 / 6 + x * (1 / 24 + x / 120))),
+                      torch.expm1(xs) / xs)
+    return dt * phi
+
+
+def _scan_loop(u, delta, A, B, C, D, bias, delta_softplus, zoh=False):
     """y[b, d, t] of one forward scan from a zero state (plain loop over t)."""
     batch, dim, L = u.shape
     N = A.shape[1]
@@ -36,18 +51,20 @@ def _scan_loop(u, delta, A, B, C, D, bias, delta_softplus):
     h = torch.zeros((batch, dim, N), dtype=_F)
     ys = []
     for t in range(L):
-        a = torch.exp(dt[:, :, t, None] * A[None, :, :])
-        h = a * h + dt[:, :, t, None] * B[:, None, :, t] * u[:, :, t, None]
+        dtt = dt[:, :, t, None]
+        a = torch.exp(dtt * A[None, :, :])
+        k = _zoh_coef(dtt, A[None, :, :]) if zoh else dtt
+        h = a * h + k * B[:, None, :, t] * u[:, :, t, None]
         ys.append((C[:, None, :, t] * h).sum(-1) + D[None, :] * u[:, :, t])
     return torch.stack(ys, dim=-1)
 
 
-def _direction_y(p, delta_softplus, reverse):
+def _direction_y(p, delta_softplus, reverse, zoh=False):
     u, dl, A, B, C, D, bias = p
     if reverse:
         f = lambda v: torch.flip(v, dims=[-1])
-        return f(_scan_loop(f(u), f(dl), A, f(B), f(C), D, bias, delta_softplus))
-    return _scan_loop(u, dl, A, B, C, D, bias, delta_softplus)
+        return f(_scan_loop(f(u), f(dl), A, f(B), f(C), D, bias, delta_softplus, zoh))
+    return _scan_loop(u, dl, A, B, C, D, bias, delta_softplus, zoh)
 
 
 _KEYS = ("u", "delta", "A", "B", "C", "D", "delta_bias")
@@ -61,24 +78,25 @@ def _grads(leaves):
     return {k: (None if v is None else v.grad.numpy().copy()) for k, v in zip(_KEYS, leaves)}
 
 
-def selective_scan_grad(p, dout, z=None, delta_softplus=True, reverse=False):
+def selective_scan_grad(p, dout, z=None, delta_softplus=True, reverse=False, zoh=False):
     """Gradients of L = sum(dout * out) for out = y * SiLU(z) (y without z).
     p: dict u, delta, A, B, C, D, delta_bias (numpy, the forward's shapes).
     Returns (grads dict with the keys of p, dz or None, out)."""
     lv = _leaves(p)
     zt = _t(z)
-    y = _direction_y(lv, delta_softplus, reverse)
+    y = _direction_y(lv, delta_softplus, reverse, zoh)
     out = y * torch.nn.functional.silu(zt) if zt is not None else y
     (out * _t(dout, False)).sum().backward()
     return _grads(lv), (zt.grad.numpy().copy() if zt is not None else None), out.detach().numpy()
 
 
-def bidir_scan_grad(fwd, bwd, dout, z=None, combine_scale=1.0, delta_softplus=True):
+def bidir_scan_grad(fwd, bwd, dout, z=None, combine_scale=1.0, delta_softplus=True, zoh=False):
     """Gradients of L = sum(dout * out), out = s * (y_f + flip(scan(flip(bwd)))) * SiLU(z).
     Returns (grads of fwd, grads of bwd, dz or None, out)."""
     lf, lb = _leaves(fwd), _leaves(bwd)
     zt = _t(z)
-    y = combine_scale * (_direction_y(lf, delta_softplus, False) + _direction_y(lb, delta_softplus, True))
+    y = combine_scale * (_direction_y(lf, delta_softplus, False, zoh) +
+                         _direction_y(lb, delta_softplus, True, zoh))
     out = y * torch.nn.functional.silu(zt) if zt is not None else y
     (out * _t(dout, False)).sum().backward()
     return _grads(lf), _grads(lb), (zt.grad.numpy().copy() if zt is not None else None), \

@@ -63,6 +63,56 @@ def test_single_grad_matches_finite_differences(reverse, gated, softplus):
         _check(dz, _fd(lambda q: f(p, q["z"]), dict(z=z), "z"), "z")
 
 
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("gated", [False, True])
+def test_zoh_grad_matches_finite_differences(reverse, gated):
+    """The zero-order-hold write: one column of A is 0 (coefficient dt, whose
+    A-derivative dt^2 / 2 the series keeps), others span small and large
+    |dt A| on both sides of the oracle's series switch."""
+    rng = _rng(110 + 2 * reverse + gated)
+    p = _dir(rng, 2, 2, 5, 4)
+    p["A"][:, 0] = 0.0
+    p["A"][0, 1] = -1e-4
+    z = rng.standard_normal(p["u"].shape) if gated else None
+    dout = rng.standard_normal(p["u"].shape)
+    g, dz, out = og.selective_scan_grad(p, dout, z=z, reverse=reverse, zoh=True)
+    f = lambda q, zz=z: float(np.sum(dout * oracle.selective_scan(**q, z=zz, reverse=reverse, zoh=True)))
+    np.testing.assert_allclose(out, oracle.selective_scan(**p, z=z, reverse=reverse, zoh=True),
+                               rtol=0, atol=1e-12)
+    for k in ("u", "delta", "A", "B", "C", "D", "delta_bias"):
+        _check(g[k], _fd(f, p, k), k)
+    if gated:
+        _check(dz, _fd(lambda q: f(p, q["z"]), dict(z=z), "z"), "z")
+
+
+def test_zoh_bidir_grad_matches_finite_differences():
+    rng = _rng(120)
+    f_, b_ = _dir(rng, 1, 2, 6, 3), _dir(rng, 1, 2, 6, 3)
+    z = rng.standard_normal(f_["u"].shape)
+    dout = rng.standard_normal(f_["u"].shape)
+    gf, gb, dz, out = og.bidir_scan_grad(f_, b_, dout, z=z, combine_scale=0.5, zoh=True)
+    fn = lambda ff, bb, zz=z: float(np.sum(dout * oracle.bidir_scan(ff, bb, z=zz, combine_scale=0.5,
+                                                                     zoh=True)))
+    np.testing.assert_allclose(out, oracle.bidir_scan(f_, b_, z=z, combine_scale=0.5, zoh=True),
+                               rtol=0, atol=1e-12)
+    for k in ("u", "delta", "A", "B", "C", "D", "delta_bias"):
+        _check(gf[k], _fd(lambda q: fn(q, b_), f_, k), "fwd " + k)
+        _check(gb[k], _fd(lambda q: fn(f_, q), b_, k), "bwd " + k)
+    _check(dz, _fd(lambda q: fn(f_, b_, q["z"]), dict(z=z), "z"), "z")
+
+
+def test_zoh_grad_differs_from_released_write():
+    """Guard against the flag being ignored: on steps with |dt A| near 1 the
+    two discretisations' gradients differ well beyond the tolerance."""
+    rng = _rng(130)
+    p = _dir(rng, 1, 2, 4, 2)
+    dout = rng.standard_normal(p["u"].shape)
+    g0, _, _ = og.selective_scan_grad(p, dout)
+    g1, _, _ = og.selective_scan_grad(p, dout, zoh=True)
+    for k in ("u", "delta", "A", "B"):
+        assert np.max(np.abs(g0[k] - g1[k])) > 1e-3, k
+
+
 def test_bidir_grad_matches_finite_differences():
     rng = _rng(90)
     f_, b_ = _dir(rng, 1, 2, 6, 3), _dir(rng, 1, 2, 6, 3)
