@@ -300,8 +300,9 @@ typedef struct vm_scan_grad {
  *   dout [batch, dim, seqlen] (dtype); g: the gradients (see vm_scan_grad);
  *   dz [batch, dim, seqlen] fp32: required exactly when z is given.
  * Gradients are fp32 for either dtype (VM_BF16 inputs are widened exactly
- * and the pass runs in fp32).  The released recurrence only (options without
- * VM_ZOH) and no fused conv (VM_ERR_UNSUPPORTED otherwise).  Gradient buffers must not
+ * and the pass runs in fp32).  Either write (options as the forward call's:
+ * with VM_ZOH the derivatives of k = expm1(dt A) / A are included, A = 0
+ * among them); no fused conv (VM_ERR_UNSUPPORTED).  Gradient buffers must not
  * overlap any input or each other (VM_ERR_ALIAS).  Sums over batch rows (dA,
  * dD, ddelta_bias) and over channels (dB, dC) are formed from per-block
  * partials in a fixed order, so results are deterministic.

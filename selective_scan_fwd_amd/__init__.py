@@ -269,7 +269,7 @@ def _grad_set(p, batch, dim, L, N, device, with_bias):
     return s, g
 
 
-def vm_selective_scan_bwd(p, dout, z=None, delta_softplus=True, reverse=False):
+def vm_selective_scan_bwd(p, dout, z=None, delta_softplus=True, reverse=False, zoh=False):
     """Gradients of sum(dout * vm_selective_scan_fwd(**p, z=z, ...)).  p: dict
     u, delta, A, B, C, D, delta_bias (token tensors fp32 or bf16, like dout and
     z).  Returns (grads, dz), fp32: grads has the keys of p (dB, dC dense
@@ -287,13 +287,13 @@ def vm_selective_scan_bwd(p, dout, z=None, delta_softplus=True, reverse=False):
     with torch.cuda.device(u.device):
         st = load_library().vm_selective_scan_bwd(ctypes.byref(d), _ptr(z), _ptr(dout), ctypes.byref(gs),
                                                   _ptr(dz), batch, dim, L, N, _dtype_code(u),
-                                                  _options(delta_softplus, False), int(bool(reverse)),
+                                                  _options(delta_softplus, zoh), int(bool(reverse)),
                                                   _stream(u.device))
     _check(st, "vm_selective_scan_bwd")
     return g, dz
 
 
-def vm_bidir_scan_bwd(fwd, bwd, dout, z=None, combine_scale=1.0, delta_softplus=True):
+def vm_bidir_scan_bwd(fwd, bwd, dout, z=None, combine_scale=1.0, delta_softplus=True, zoh=False):
     """Gradients of sum(dout * vm_bidir_scan_fwd(fwd, bwd, z, combine_scale)).
     Returns (grads of fwd, grads of bwd, dz), fp32 for fp32 or bf16 inputs."""
     u = fwd["u"]
@@ -312,7 +312,7 @@ def vm_bidir_scan_bwd(fwd, bwd, dout, z=None, combine_scale=1.0, delta_softplus=
         st = load_library().vm_bidir_scan_bwd(ctypes.byref(df), ctypes.byref(db), _ptr(z), _ptr(dout),
                                               float(combine_scale), ctypes.byref(gsf), ctypes.byref(gsb),
                                               _ptr(dz), batch, dim, L, N, _dtype_code(u),
-                                              _options(delta_softplus, False), _stream(u.device))
+                                              _options(delta_softplus, zoh), _stream(u.device))
     _check(st, "vm_bidir_scan_bwd")
     return gf, gb, dz
 

@@ -250,6 +250,7 @@ int run_bwd(const vm_scan_dir *p, const float *dy, const vm_scan_grad *g, BwdScr
   a.L = L;
   a.dstate = static_cast<int>(dstate);
   a.softplus = (options & VM_DELTA_SOFTPLUS) != 0;
+  a.zoh = (options & VM_ZOH) != 0;
   a.reverse = reverse;
   st = hip_status(vmk::launch_scan_bwd(a, s));
   if (st != VM_OK) return st;
@@ -300,16 +301,15 @@ vm_scan_dir widen_dir(const vm_scan_dir *p, int64_t tok, int64_t batch, int64_t 
   return w;
 }
 
-// Shared checks of the backward entry points (fp32, released recurrence, no
-// fused conv; dz exactly when z).
+// Shared checks of the backward entry points (no fused conv; dz exactly when
+// z).
 int check_bwd_common(int dtype, int options, int64_t batch, int64_t dim, int64_t L, int64_t dstate,
                      const void *z, const void *dout, const void *dz, int64_t *tok, int64_t *bc) {
   if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;
   if (!options_ok(options)) return VM_ERR_FLAG;
   if (!dims_ok({batch, dim, L}, tok) || dstate <= 0) return VM_ERR_SHAPE;
   // (the parameter-gradient reduction runs one workgroup per channel)
-  if ((options & VM_ZOH) || dstate > 16 || dim > kMaxPlanes || !row_blocks_ok(batch, dim))
-    return VM_ERR_UNSUPPORTED;
+  if (dstate > 16 || dim > kMaxPlanes || !row_blocks_ok(batch, dim)) return VM_ERR_UNSUPPORTED;
   if (!dims_ok({batch, dstate, L}, bc)) return VM_ERR_SHAPE;
   // 32-bit offsets of the kernel's per-block checkpoints and partial sums
   if (16 * 64 * vmk::scan_bwd_tiles(L) >= (int64_t{1} << 31) || 64 * L >= (int64_t{1} << 31))
@@ -654,6 +654,7 @@ int vm_selective_scan_bwd(const vm_scan_dir *p, const void *z, const void *dout,
     a.L = seqlen;
     a.dstate = static_cast<int>(dstate);
     a.softplus = (options & VM_DELTA_SOFTPLUS) != 0;
+    a.zoh = (options & VM_ZOH) != 0;
     a.reverse = reverse;
     a.scale = 1.0f;
     const vmk::ScanPlan plan = vmk::plan_scan(batch, dim, seqlen, a.dstate, 1, false);
@@ -721,6 +722,7 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
     a.dir[1] = resolve_dir(&wb, batch, dstate, seqlen, false, ws, s, &st);
     if (st != VM_OK) return st;
     a.softplus = (options & VM_DELTA_SOFTPLUS) != 0;
+    a.zoh = (options & VM_ZOH) != 0;
     a.scale = 1.0f;
     st = launch_bidir(a, false, ws, s);
     if (st != VM_OK) return st;

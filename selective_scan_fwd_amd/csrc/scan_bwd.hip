@@ -14,6 +14,12 @@
 // a_t h_{t-1} is formed as a product from the kept states (the tile's
 // checkpoint for its first step), not as h_t - dt_t B_t u_t, which would
 // leave rounding residue where h_{t-1} is exactly zero.
+// With the zero-order-hold write (ZOH) the write is k_t B_t u_t with
+// k = expm1(dt A) / A per state, so dt u becomes k u in dB and du, and k's
+// derivatives join the rest: dk/ddt = a_t and dk/dA (zoh_coef_dA):
+//   dA   += g_t (a_t h_{t-1} dt_t + B_t u_t dk/dA)
+//   du_t  = sum_n g_t B_t k + D dy_t
+//   ddt_t = sum_n g_t a_t (A h_{t-1} + B_t u_t).
 //
 // Work decomposition: as the forward kernel, one wave covers 16 channels of
 // one batch row, a lane holding 4 of a channel's 16 states.  Pass 1 runs the
@@ -58,9 +64,10 @@ struct BwdLayout {
 // The tile's states and decays stay in registers (64 VGPRs with 8-step
 // tiles; 4-step tiles fit more workgroups but measured 1.6x slower for their
 // per-tile reductions), which sets the register budget at two waves per
-// SIMD; the LDS area (15 KB) is small enough not to lower that.
-template <int T>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+// SIMD; the LDS area (15 KB) is small enough not to lower that.  The ZOH
+// adjoint's extra terms need about 300 registers: one wave per SIMD.
+template <int T, bool ZOH>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)))
 scan_bwd_kernel(const BwdArgs p) {
   using Lay = BwdLayout<T>;
   constexpr int PE = kR * T / 64;      // staged elements per lane per tile
@@ -113,12 +120,13 @@ scan_bwd_kernel(const BwdArgs p) {
 
   // ---- state role: channel d0 + r, states n0 .. n0 + 3
   const int n0 = sp * kNS;
-  float A2[kNS], An[kNS];
+  float A2[kNS], An[kNS], iA[kNS];
 #pragma unroll
   for (int j = 0; j < kNS; ++j) {
     const int n = n0 + j;
     An[j] = bload<float>(rA, n < dstate ? static_cast<uint32_t>(r * dstate + n) * 4u : kOob);
     A2[j] = An[j] * kLog2e;
+    iA[j] = ZOH && An[j] != 0.0f ? 1.0f / An[j] : 0.0f;
   }
   const int rl = lane & 15;
   const int bc_slot = rl < kNS ? n0 + rl : (rl < 2 * kNS ? 16 + n0 + rl - kNS : 0);
@@ -177,8 +185,9 @@ scan_bwd_kernel(const BwdArgs p) {
     for (int jn = 0; jn < kNS; ++jn)
       lk[jn] = pass2 ? bload<float>(rCk, ck_lane + static_cast<uint32_t>(j) * 64u + 4u * jn) : 0.0f;
   };
-  // Stages the loaded tile: (dt, dt u, dy) per element and B, C per step into
-  // LDS, and keeps the element values the tile's combine needs.
+  // Stages the loaded tile: (dt, dt u, dy) per element ((dt, u, dy) with
+  // ZOH) and B, C per step into LDS, and keeps the element values the tile's
+  // combine needs.
   float eu[PE], edt[PE], edy[PE], ex[PE];
   auto stage_store = [&]() {
 #pragma unroll
@@ -192,7 +201,7 @@ scan_bwd_kernel(const BwdArgs p) {
       edy[i] = dyv;
       ex[i] = x;
       *reinterpret_cast<float4 *>(prep + srow[i] * Lay::PST + 4 * sq) =
-          make_float4(dtv, dtv * uv, dyv, 0.0f);
+          make_float4(dtv, ZOH ? uv : dtv * uv, dyv, 0.0f);
     }
 #pragma unroll
     for (int i = 0; i < BQ; ++i) {
@@ -220,7 +229,8 @@ scan_bwd_kernel(const BwdArgs p) {
       const float bv = bcs[q * 32 + bc_slot];
 #pragma unroll
       for (int jn = 0; jn < kNS; ++jn) {
-        const float a = hw_exp2(pq.x * A2[jn]);
+        const float x2 = pq.x * A2[jn];
+        const float a = hw_exp2(x2);
         float w;
         switch (jn) {
           case 0: w = pq.y * row_bcast<0>(bv); break;
@@ -228,6 +238,7 @@ scan_bwd_kernel(const BwdArgs p) {
           case 2: w = pq.y * row_bcast<2>(bv); break;
           default: w = pq.y * row_bcast<3>(bv); break;
         }
+        if constexpr (ZOH) w *= zoh_coef(pq.x, x2, a, iA[jn]);
         h[jn] = __builtin_fmaf(a, h[jn], w);
       }
     }
@@ -269,7 +280,8 @@ scan_bwd_kernel(const BwdArgs p) {
       const float bv = bvs[q];
 #pragma unroll
       for (int jn = 0; jn < kNS; ++jn) {
-        const float a = hw_exp2(pq.x * A2[jn]);
+        const float x2 = pq.x * A2[jn];
+        const float a = hw_exp2(x2);
         float w;
         switch (jn) {
           case 0: w = pq.y * row_bcast<0>(bv); break;
@@ -277,6 +289,7 @@ scan_bwd_kernel(const BwdArgs p) {
           case 2: w = pq.y * row_bcast<2>(bv); break;
           default: w = pq.y * row_bcast<3>(bv); break;
         }
+        if constexpr (ZOH) w *= zoh_coef(pq.x, x2, a, iA[jn]);
         hc[jn] = __builtin_fmaf(a, hc[jn], w);
         hs[q][jn] = hc[jn];
         as[q][jn] = a;
@@ -324,12 +337,24 @@ scan_bwd_kernel(const BwdArgs p) {
           default: Bb = row_bcast<3>(bv); Cb = row_bcast<kNS + 3>(bv); break;
         }
         const float g = __builtin_fmaf(Cb, pq.z, gn[jn]);
-        red[((n0 + jn) * T + q) * Lay::RSTR + sp * 16 + r] = g * pq.y;   // dB
-        sgB = __builtin_fmaf(g, Bb, sgB);
         const float ah = as[q][jn] * (q > 0 ? hs[q > 0 ? q - 1 : 0][jn] : h0[jn]);   // a_t h_{t-1}
         const float gq = g * ah;
-        dA[jn] = __builtin_fmaf(gq, pq.x, dA[jn]);
-        sqA = __builtin_fmaf(gq, An[jn], sqA);
+        if constexpr (ZOH) {
+          // pq.y is u; k and dk/dA are recomputed from the kept decay
+          const float x2 = pq.x * A2[jn];
+          const float kq = zoh_coef(pq.x, x2, as[q][jn], iA[jn]);
+          const float gBu = g * Bb * pq.y;
+          red[((n0 + jn) * T + q) * Lay::RSTR + sp * 16 + r] = g * kq * pq.y;   // dB
+          sgB = __builtin_fmaf(g * Bb, kq, sgB);
+          dA[jn] = __builtin_fmaf(gq, pq.x, __builtin_fmaf(gBu, zoh_coef_dA(pq.x, x2, as[q][jn], iA[jn], kq),
+                                                           dA[jn]));
+          sqA = __builtin_fmaf(gq, An[jn], __builtin_fmaf(gBu, as[q][jn], sqA));
+        } else {
+          red[((n0 + jn) * T + q) * Lay::RSTR + sp * 16 + r] = g * pq.y;   // dB
+          sgB = __builtin_fmaf(g, Bb, sgB);
+          dA[jn] = __builtin_fmaf(gq, pq.x, dA[jn]);
+          sqA = __builtin_fmaf(gq, An[jn], sqA);
+        }
         gn[jn] = as[q][jn] * g;
       }
       part[(0 * 64 + lane) * Lay::QSTR + q] = sgB;
@@ -345,8 +370,9 @@ scan_bwd_kernel(const BwdArgs p) {
         gB += part[(0 * 64 + s * kR + srow[i]) * Lay::QSTR + sq];
         gA += part[(1 * 64 + s * kR + srow[i]) * Lay::QSTR + sq];
       }
-      const float du = __builtin_fmaf(edt[i], gB, sD[i] * edy[i]);
-      const float ddt = __builtin_fmaf(eu[i], gB, gA);
+      // without ZOH the write's dt u factors out of the state sums
+      const float du = ZOH ? __builtin_fmaf(sD[i], edy[i], gB) : __builtin_fmaf(edt[i], gB, sD[i] * edy[i]);
+      const float ddt = ZOH ? gA : __builtin_fmaf(eu[i], gB, gA);
       const float sig = hw_rcp(1.0f + hw_exp2(-ex[i] * kLog2e));
       const float dd = sp_on ? ddt * sig : ddt;
       const uint32_t o = pin_u(in_seq ? ob[i] + static_cast<uint32_t>(jT) * 4u : kOob);
@@ -479,8 +505,12 @@ hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s) {
   const int64_t blocks = a.batch * nrb;
   if (blocks == 0) return hipSuccess;
   const size_t lds = BwdLayout<kBwdTile>::TOTAL * sizeof(float);
-  hipLaunchKernelGGL(scan_bwd_kernel<kBwdTile>, dim3(static_cast<unsigned>(blocks)), dim3(64), lds, s,
-                     a);
+  if (a.zoh)
+    hipLaunchKernelGGL((scan_bwd_kernel<kBwdTile, true>), dim3(static_cast<unsigned>(blocks)), dim3(64),
+                       lds, s, a);
+  else
+    hipLaunchKernelGGL((scan_bwd_kernel<kBwdTile, false>), dim3(static_cast<unsigned>(blocks)), dim3(64),
+                       lds, s, a);
   return hipGetLastError();
 }
 

@@ -58,5 +58,41 @@ template <> __device__ __forceinline__ void bstore<bf16_t>(Rsrc r, uint32_t off,
                                         static_cast<int>(off), 0, 0);
 }
 
+// Zero-order-hold input coefficient ("Norm or Direction?" page, section 3,
+// eq. 2, for diagonal A): k = expm1(x) / A for x = dt A, given x2 = x
+// log2(e), a = 2^x2 and iA = 1 / A (0 where A = 0, whose x = 0 takes the
+// series).  For |x| < 1/8 it is dt g(x), g(x) = expm1(x) / x from its Taylor
+// series to x^4 (truncation below 5e-8 relative); above, (a - 1) / A, where
+// the rounding of a costs at most about 5e-7 relative because |expm1(x)| is
+// then at least 0.117.  Both are computed and one is selected.
+constexpr float kZohThr2 = 0.125f * kLog2e;   // |x| < 1/8 in units of x2
+__device__ __forceinline__ float zoh_coef(float dt, float x2, float a, float iA) {
+  constexpr float c1 = kLn2 / 2, c2 = kLn2 * kLn2 / 6, c3 = kLn2 * kLn2 * kLn2 / 24,
+                  c4 = kLn2 * kLn2 * kLn2 * kLn2 / 120;
+  float g = __builtin_fmaf(x2, c4, c3);
+  g = __builtin_fmaf(x2, g, c2);
+  g = __builtin_fmaf(x2, g, c1);
+  g = __builtin_fmaf(x2, g, 1.0f);
+  const float k_small = g * dt;
+  const float k_large = __builtin_fmaf(a, iA, -iA);
+  return __builtin_fabsf(x2) < kZohThr2 ? k_small : k_large;
+}
+
+// dk/dA of that coefficient (k given): dt^2 g'(x), with g'(x) = 1/2 + x/3 +
+// x^2/8 + x^3/30 + x^4/144 for |x| < 1/8 (truncation below 1e-7 relative);
+// above, (dt a - k) / A, whose cancellation costs at most about 1e-5
+// relative at the switch.  (dk/ddt is a itself.)
+__device__ __forceinline__ float zoh_coef_dA(float dt, float x2, float a, float iA, float k) {
+  constexpr float e1 = 0.5f, e2 = kLn2 / 3, e3 = kLn2 * kLn2 / 8, e4 = kLn2 * kLn2 * kLn2 / 30,
+                  e5 = kLn2 * kLn2 * kLn2 * kLn2 / 144;
+  float g = __builtin_fmaf(x2, e5, e4);
+  g = __builtin_fmaf(x2, g, e3);
+  g = __builtin_fmaf(x2, g, e2);
+  g = __builtin_fmaf(x2, g, e1);
+  const float d_small = g * (dt * dt);
+  const float d_large = __builtin_fmaf(dt, a, -k) * iA;
+  return __builtin_fabsf(x2) < kZohThr2 ? d_small : d_large;
+}
+
 }  // namespace
 }  // namespace vmk

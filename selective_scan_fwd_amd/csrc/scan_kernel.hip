@@ -78,30 +78,16 @@ __device__ __forceinline__ void state_step(float (&h)[NS], const float (&A2)[NS]
 }
 
 // The same step with the zero-order-hold write k_j u B_j, k_j = expm1(x) / A_j
-// for x = dt A_j (here u arrives in place of dt u).  For |x| < 1/8 the
-// coefficient is dt g(x) with g(x) = expm1(x) / x from its Taylor series to
-// x^4 (truncation below 5e-8 relative); above, (2^x2 - 1) / A_j, where the
-// rounding of 2^x2 costs at most about 5e-7 relative because |expm1(x)| is
-// then at least 0.117.  Both are computed and one is selected per state.
-// iA_j = 1 / A_j (0 where A_j = 0, whose |x| = 0 takes the series).
+// for x = dt A_j (here u arrives in place of dt u; zoh_coef has the
+// coefficient and its accuracy).
 template <int NS, int J>
 __device__ __forceinline__ void state_step_zoh(float (&h)[NS], const float (&A2)[NS],
                                                const float (&iA)[NS], float dt, float u,
                                                float bc, float &y) {
   if constexpr (J < NS) {
-    constexpr float kLn2 = 0.6931471805599453f;
-    constexpr float c1 = kLn2 / 2, c2 = kLn2 * kLn2 / 6, c3 = kLn2 * kLn2 * kLn2 / 24,
-                    c4 = kLn2 * kLn2 * kLn2 * kLn2 / 120;
-    constexpr float kThr2 = 0.125f * kLog2e;            // |x| < 1/8 in units of x2 = x log2(e)
     const float x2 = dt * A2[J];
     const float dA = hw_exp2(x2);
-    float g = __builtin_fmaf(x2, c4, c3);
-    g = __builtin_fmaf(x2, g, c2);
-    g = __builtin_fmaf(x2, g, c1);
-    g = __builtin_fmaf(x2, g, 1.0f);
-    const float k_small = g * dt;
-    const float k_large = __builtin_fmaf(dA, iA[J], -iA[J]);
-    const float k = __builtin_fabsf(x2) < kThr2 ? k_small : k_large;
+    const float k = zoh_coef(dt, x2, dA, iA[J]);
     h[J] = __builtin_fmaf(dA, h[J], k * (u * row_bcast<J>(bc)));
     if constexpr (J == 0) y = row_bcast<NS>(bc) * h[0];
     else fmac_row_bcast<NS + J>(y, bc, h[J]);

@@ -131,6 +131,7 @@ struct BwdArgs {
   int64_t batch, dim, L;
   int dstate;
   int softplus;
+  int zoh;              // zero-order-hold write
   int reverse;
 };
 constexpr int kBwdTile = 8;

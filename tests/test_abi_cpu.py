@@ -261,8 +261,8 @@ def test_bwd_argument_checks(lib):
     g0.dC = None
     assert single(g=g0) == 1
     assert single(dtype=2) == 3
-    assert single(opt=3) == 6                               # zero-order hold: not here
-    assert single(dtype=1, opt=3) == 6
+    assert single(opt=3, N=17) == 6                         # zero-order hold accepted, N not
+    assert single(dtype=1, opt=3, rev=2) == 4
     assert single(N=17) == 6
     assert single(rev=2) == 4
     assert single(opt=4) == 4
@@ -276,6 +276,7 @@ def test_bwd_argument_checks(lib):
     fc = _dir(FAKE)
     fc.conv_w = FAKE * 7
     assert single(p=fc) == 6
+    assert single(p=fc, opt=3) == 6                         # no fused conv, either write
 
     def bidir(g2=gb, scale=1.0, dtype=0):
         return lib.vm_bidir_scan_bwd(ctypes.byref(f), ctypes.byref(b), None, FAKE * 3, scale,

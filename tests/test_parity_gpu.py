@@ -754,6 +754,43 @@ def test_bwd_single(L, reverse, gated):
         assert_close(host(dz), wdz, FP32_TOL, "dz")
 
 
+@pytest.mark.parametrize("L", [1, 9, 77])
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("gated", [False, True])
+def test_bwd_zoh_single(L, reverse, gated):
+    """Zero-order-hold write: steps on both sides of the coefficient's series
+    switch, and one state with A = 0 (coefficient dt)."""
+    _case(f"bwd zoh single L{L} rev{reverse} gated{gated}")
+    p, z = wl.single_inputs(2800 + L, 2, 70, L, device=DEV, gated=gated, perturb=True)
+    p["A"][:, 3] = 0.0
+    dout = torch.randn(p["u"].shape, generator=wl.generator(2900 + L, DEV), device=DEV)
+    g, dz = vm.vm_selective_scan_bwd(p, dout, z=z, reverse=reverse, zoh=True)
+    torch.cuda.synchronize()
+    want, wdz, _ = ograd.selective_scan_grad(host_dir(p), host(dout), z=host(z), reverse=reverse,
+                                             zoh=True)
+    for k in _GRAD_KEYS:
+        assert_close(host(g[k]), want[k], FP32_TOL, f"d{k}")
+    if gated:
+        assert_close(host(dz), wdz, FP32_TOL, "dz")
+
+
+@pytest.mark.parametrize("L", [77, 600])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_bwd_zoh_bidir(L, dtype):
+    _case(f"bwd zoh bidir L{L} {dtype}")
+    fwd, bwd, z = wl.bidir_inputs(3000 + L, 2, 40, L, device=DEV, dtype=dtype, perturb=True)
+    dout = torch.randn(z.shape, generator=wl.generator(3100 + L, DEV), device=DEV).to(dtype)
+    gf, gb, dz = vm.vm_bidir_scan_bwd(fwd, bwd, dout, z=z, combine_scale=0.5, zoh=True)
+    torch.cuda.synchronize()
+    wf, wb, wdz, _ = ograd.bidir_scan_grad(host_dir(fwd), host_dir(bwd), host(dout), z=host(z),
+                                           combine_scale=0.5, zoh=True)
+    tol = FP32_TOL          # bf16 inputs are widened exactly; the oracle sees the same values
+    for k in _GRAD_KEYS:
+        assert_close(host(gf[k]), wf[k], tol, f"fwd d{k}")
+        assert_close(host(gb[k]), wb[k], tol, f"bwd d{k}")
+    assert_close(host(dz), wdz, tol, "dz")
+
+
 def test_bwd_small_dstate_no_softplus_dense_bc():
     _case("bwd N5 no softplus dense B/C")
     p, z = wl.single_inputs(2700, 3, 33, 50, dstate=5, device=DEV, bc_layout="dense")
