@@ -337,7 +337,7 @@ def build_step(cfg, seed, sets, dev, zoh=False, conv="none"):
 
         def step(i):
             f, b, z, dout = inputs[i % sets]
-            vm.vm_bidir_scan_bwd(f, b, dout, z=z, combine_scale=w.combine_scale)
+            vm.vm_bidir_scan_bwd(f, b, dout, z=z, combine_scale=w.combine_scale, zoh=zoh)
 
         tok = w.batch * w.dim * L
         bc = w.batch * L * N * 4
@@ -361,7 +361,7 @@ def build_step(cfg, seed, sets, dev, zoh=False, conv="none"):
             hz, hdo = z[:sub].double().cpu().numpy(), dout[:sub].double().cpu().numpy()
             reps, t0 = 0, time.perf_counter()
             while True:
-                og.bidir_scan_grad(hf, hb, hdo, z=hz, combine_scale=w.combine_scale)
+                og.bidir_scan_grad(hf, hb, hdo, z=hz, combine_scale=w.combine_scale, zoh=zoh)
                 reps += 1
                 el = time.perf_counter() - t0
                 if el >= budget or reps >= 20:
