@@ -101,3 +101,27 @@ def bidir_scan_grad(fwd, bwd, dout, z=None, combine_scale=1.0, delta_softplus=Tr
     (out * _t(dout, False)).sum().backward()
     return _grads(lf), _grads(lb), (zt.grad.numpy().copy() if zt is not None else None), \
         out.detach().numpy()
+
+
+def causal_conv1d_silu_grad(x, w, bias, du, reverse=False):
+    """Gradients of L = sum(du * u) for the block's depthwise causal conv of
+    width 4 plus bias, then SiLU (Vision Mamba page, "Inside the released Vim
+    block"): u[t] = SiLU(bias + sum_k w[k] x[t - 3 + k]), taps before the row
+    start reading 0; reverse=True is the backward branch's (flip, convolve,
+    flip back).  Returns (dx, dw, dbias or None, u)."""
+    xt, wt, bt = _t(x), _t(w), _t(bias)
+    f = (lambda v: torch.flip(v, dims=[-1])) if reverse else (lambda v: v)
+    xs = f(xt)
+    L = xs.shape[-1]
+    v = bt[None, :, None].expand(xs.shape[0], -1, L) if bt is not None else torch.zeros_like(xs)
+    for k in range(4):
+        shift = 3 - k                     # tap k reads x[t - shift]
+        if shift >= L:
+            continue
+        xk = torch.nn.functional.pad(xs[:, :, :L - shift], (shift, 0)) if shift else xs
+        v = v + wt[None, :, k, None] * xk
+    u = f(torch.nn.functional.silu(v))
+    (u * _t(du, False)).sum().backward()
+    return xt.grad.numpy().copy(), wt.grad.numpy().copy(), \
+        (bt.grad.numpy().copy() if bt is not None else None), u.detach().numpy()
+

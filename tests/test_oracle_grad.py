@@ -139,3 +139,42 @@ def test_grad_of_skip_only_case():
     np.testing.assert_allclose(g["D"], (dout * p["u"]).sum(axis=(0, 2)), rtol=0, atol=1e-13)
     for k in ("delta", "A", "C", "delta_bias"):
         assert np.all(g[k] == 0.0), k
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("L", [1, 2, 7])
+def test_conv_grad_matches_finite_differences(reverse, L):
+    """Conv + SiLU gradients: rows shorter than the filter (L = 1, 2) keep
+    only the taps inside the row."""
+    rng = _rng(140 + 3 * L + reverse)
+    p = dict(x=rng.standard_normal((2, 3, L)), w=rng.standard_normal((3, 4)) * 0.5,
+             bias=rng.standard_normal(3) * 0.3)
+    du = rng.standard_normal((2, 3, L))
+    dx, dw, db, u = og.causal_conv1d_silu_grad(p["x"], p["w"], p["bias"], du, reverse=reverse)
+    np.testing.assert_allclose(u, oracle.causal_conv1d_silu(p["x"], p["w"], p["bias"], reverse=reverse),
+                               rtol=0, atol=1e-13)
+    f = lambda q: float(np.sum(du * oracle.causal_conv1d_silu(q["x"], q["w"], q["bias"], reverse=reverse)))
+    _check(dx, _fd(f, p, "x"), "x")
+    _check(dw, _fd(f, p, "w"), "w")
+    _check(db, _fd(f, p, "bias"), "bias")
+
+
+def test_conv_grad_without_bias_and_tap_structure():
+    """No bias: dbias is None.  Brute force on one row: dx[s] collects
+    w[k] dv[s + 3 - k] from the outputs that read x[s]."""
+    rng = _rng(150)
+    x = rng.standard_normal((1, 1, 6))
+    w = rng.standard_normal((1, 4))
+    du = rng.standard_normal((1, 1, 6))
+    dx, dw, db, _ = og.causal_conv1d_silu_grad(x, w, None, du)
+    assert db is None
+    v = np.array([sum(w[0, k] * x[0, 0, t - 3 + k] for k in range(4) if t - 3 + k >= 0) for t in range(6)])
+    s = 1 / (1 + np.exp(-v))
+    dv = du[0, 0] * s * (1 + v * (1 - s))
+    want = np.array([sum(w[0, k] * dv[s_ + 3 - k] for k in range(4) if 0 <= s_ + 3 - k < 6)
+                     for s_ in range(6)])
+    np.testing.assert_allclose(dx[0, 0], want, rtol=1e-12, atol=1e-12)
+    want_w = np.array([sum(dv[t] * x[0, 0, t - 3 + k] for t in range(6) if t - 3 + k >= 0)
+                       for k in range(4)])
+    np.testing.assert_allclose(dw[0], want_w, rtol=1e-12, atol=1e-12)
+
