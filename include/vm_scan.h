@@ -197,6 +197,29 @@ int vm_causal_conv1d_silu(const void *x, const float *w, const float *bias,
                           void *stream);
 
 /*
+ * Backward of vm_causal_conv1d_silu: the gradients of L = sum(du * u) for
+ * the same x, w, bias and direction (the pages pin gradients only as
+ * automatic differentiation of the forward loop).  With dv = du SiLU'(v),
+ * v the convolution plus bias:
+ *   dx_t  = sum_k w_d,k dv_{t+3-k}  (forward; reverse: dv_{t-3+k})
+ *   dw_d,k = sum over b, t of dv_t x_{t-3+k}  (reverse: x_{t+3-k})
+ *   dbias_d = sum over b, t of dv_t
+ *   x [batch, dim, seqlen] (dtype); w [dim, 4], bias [dim] (NULL = 0) fp32;
+ *   du [batch, dim, seqlen] fp32 (the scan backward's u gradient);
+ *   dx [batch, dim, seqlen], dw [dim, 4] fp32; dbias [dim] fp32 or NULL
+ *   (not computed).  Outputs must not overlap the inputs or each other
+ *   (VM_ERR_ALIAS).  dw and dbias are summed in a fixed order
+ *   (deterministic).
+ * Temporary memory: per-chunk partial sums, about 2048 * 5 floats.
+ * Limits: dim at most 2^24 - 1, and seqlen times the rows of one chunk below
+ * 2^31 (VM_ERR_UNSUPPORTED).
+ */
+int vm_causal_conv1d_silu_bwd(const void *x, const float *w, const float *bias,
+                              const float *du, float *dx, float *dw, float *dbias,
+                              int64_t batch, int64_t dim, int64_t seqlen, int reverse,
+                              int dtype, void *stream);
+
+/*
  * Number of steps of each p = 2 atrous group: ceil(H/2) * ceil(W/2)
  * ([EVM] implementation row 1).  Returns -VM_ERR_SHAPE for H or W <= 0.
  * Pure host function.

@@ -10,8 +10,8 @@ library is missing or fails to load, every call raises.
 Names and argument order follow the C ABI:
   vm_selective_scan_fwd, vm_bidir_scan_fwd, vm_atrous_gather,
   vm_atrous_scatter, vm_pool_scan_repeat, vm_ss2d_scan_fwd,
-  vm_causal_conv1d_silu, vm_selective_scan_bwd, vm_bidir_scan_bwd,
-  vm_atrous_group_len.
+  vm_causal_conv1d_silu, vm_causal_conv1d_silu_bwd, vm_selective_scan_bwd,
+  vm_bidir_scan_bwd, vm_atrous_group_len.
 """
 from __future__ import annotations
 
@@ -32,7 +32,8 @@ STATUS_NAMES = {0: "VM_OK", 1: "VM_ERR_NULL", 2: "VM_ERR_SHAPE", 3: "VM_ERR_DTYP
 
 EXPORTED = ("vm_status_string", "vm_version", "vm_selective_scan_fwd", "vm_bidir_scan_fwd",
             "vm_atrous_group_len", "vm_atrous_gather", "vm_atrous_scatter", "vm_pool_scan_repeat",
-            "vm_ss2d_scan_fwd", "vm_causal_conv1d_silu", "vm_selective_scan_bwd", "vm_bidir_scan_bwd")
+            "vm_ss2d_scan_fwd", "vm_causal_conv1d_silu", "vm_causal_conv1d_silu_bwd",
+            "vm_selective_scan_bwd", "vm_bidir_scan_bwd")
 
 
 class VmScanDir(ctypes.Structure):
@@ -82,12 +83,14 @@ def load_library():
             lib.vm_pool_scan_repeat.argtypes = [D, D, P, F, P, I64, I64, I64, I64, I64, I, I, I, P]
             lib.vm_ss2d_scan_fwd.argtypes = [D, P, P, F, P, I64, I64, I64, I64, I64, I, I, P]
             lib.vm_causal_conv1d_silu.argtypes = [P, P, P, P, I64, I64, I64, I, I, P]
+            lib.vm_causal_conv1d_silu_bwd.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I, I, P]
             G = ctypes.POINTER(VmScanGrad)
             lib.vm_selective_scan_bwd.argtypes = [D, P, P, G, P, I64, I64, I64, I64, I, I, I, P]
             lib.vm_bidir_scan_bwd.argtypes = [D, D, P, P, F, G, G, P, I64, I64, I64, I64, I, I, P]
             for name in ("vm_selective_scan_fwd", "vm_bidir_scan_fwd", "vm_atrous_gather",
                          "vm_atrous_scatter", "vm_pool_scan_repeat", "vm_ss2d_scan_fwd",
-                         "vm_causal_conv1d_silu", "vm_selective_scan_bwd", "vm_bidir_scan_bwd"):
+                         "vm_causal_conv1d_silu", "vm_causal_conv1d_silu_bwd", "vm_selective_scan_bwd",
+                         "vm_bidir_scan_bwd"):
                 getattr(lib, name).restype = I
             _lib = lib
     return _lib
@@ -259,6 +262,29 @@ def vm_causal_conv1d_silu(x, w, bias=None, reverse=False, out=None):
     return out
 
 
+def vm_causal_conv1d_silu_bwd(x, w, du, bias=None, reverse=False, with_dbias=None):
+    """Gradients of sum(du * vm_causal_conv1d_silu(x, w, bias, reverse)):
+    returns (dx, dw, dbias), fp32; du fp32 [batch, dim, L].  dbias is None
+    when with_dbias is false (default: computed when bias is given)."""
+    _dev(x, "x")
+    batch, dim, L = x.shape
+    _dev(w, "w", torch.float32, (dim, 4), x.device)
+    _dev(du, "du", torch.float32, x.shape, x.device)
+    if bias is not None:
+        _dev(bias, "bias", torch.float32, (dim,), x.device)
+    if with_dbias is None:
+        with_dbias = bias is not None
+    dx = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    dw = torch.empty((dim, 4), dtype=torch.float32, device=x.device)
+    db = torch.empty((dim,), dtype=torch.float32, device=x.device) if with_dbias else None
+    with torch.cuda.device(x.device):
+        st = load_library().vm_causal_conv1d_silu_bwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(du), _ptr(dx),
+                                                      _ptr(dw), _ptr(db), batch, dim, L,
+                                                      int(bool(reverse)), _dtype_code(x), _stream(x.device))
+    _check(st, "vm_causal_conv1d_silu_bwd")
+    return dx, dw, db
+
+
 def _grad_set(p, batch, dim, L, N, device, with_bias):
     f = lambda *shape: torch.empty(shape, dtype=torch.float32, device=device)
     g = dict(u=f(batch, dim, L), delta=f(batch, dim, L), A=f(dim, N), B=f(batch, N, L),
@@ -414,5 +440,6 @@ def vm_ss2d_scan_fwd(u, dirs, z=None, combine_scale=1.0, delta_softplus=True, ou
 
 __all__ = ["vm_selective_scan_fwd", "vm_bidir_scan_fwd", "vm_atrous_gather", "vm_atrous_scatter",
            "vm_pool_scan_repeat", "vm_ss2d_scan_fwd", "vm_causal_conv1d_silu",
+           "vm_causal_conv1d_silu_bwd",
            "vm_selective_scan_bwd", "vm_bidir_scan_bwd", "VmScanGrad", "vm_atrous_group_len", "vm_status_string", "vm_version",
            "VmScanDir", "VmError", "load_library", "LIB_PATH", "EXPORTED"]

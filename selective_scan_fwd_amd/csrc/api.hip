@@ -443,6 +443,40 @@ int vm_causal_conv1d_silu(const void *x, const float *w, const float *bias, void
                                             dtype == VM_BF16, static_cast<hipStream_t>(stream)));
 }
 
+int vm_causal_conv1d_silu_bwd(const void *x, const float *w, const float *bias, const float *du,
+                              float *dx, float *dw, float *dbias, int64_t batch, int64_t dim,
+                              int64_t seqlen, int reverse, int dtype, void *stream) {
+  if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;
+  if (!flag_ok(reverse)) return VM_ERR_FLAG;
+  int64_t tok = 0;
+  if (!dims_ok({batch, dim, seqlen}, &tok)) return VM_ERR_SHAPE;
+  // one workgroup per (channel, chunk of batch rows): dim on grid x, a
+  // chunk's elements counted in 32 bits
+  int rpc = 0;
+  vmk::conv1d_bwd_chunks(batch, dim, &rpc);
+  if (dim > kMaxPlanes || static_cast<int64_t>(rpc) * seqlen >= (int64_t{1} << 31))
+    return VM_ERR_UNSUPPORTED;
+  if (x == nullptr || w == nullptr || du == nullptr || dx == nullptr || dw == nullptr)
+    return VM_ERR_NULL;
+  const int es = dtype == VM_BF16 ? 2 : 4;
+  const Span ins[] = {span(x, tok * es), span(w, dim * 16), span(bias, dim * 4), span(du, tok * 4)};
+  const Span outs[] = {span(dx, tok * 4), span(dw, dim * 16), span(dbias, dim * 4)};
+  for (int o = 0; o < 3; ++o) {
+    for (const Span &i : ins)
+      if (overlaps(outs[o], i)) return VM_ERR_ALIAS;
+    for (int o2 = 0; o2 < o; ++o2)
+      if (overlaps(outs[o], outs[o2])) return VM_ERR_ALIAS;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Scratch ws(s);
+  int st = VM_OK;
+  const int nchunk = vmk::conv1d_bwd_chunks(batch, dim, &rpc);
+  float *partial = ws.get(static_cast<int64_t>(nchunk) * dim * 5, &st);
+  if (st != VM_OK) return st;
+  return hip_status(vmk::launch_conv1d_silu_bwd(x, w, bias, du, dx, dw, dbias, partial, batch, dim,
+                                                seqlen, reverse, dtype == VM_BF16, s));
+}
+
 int vm_atrous_gather(const void *x, void *streams, int64_t batch, int64_t channels,
                      int64_t height, int64_t width, int dtype, void *stream) {
   if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;

@@ -622,6 +622,97 @@ unsigned stream_grid(int64_t n) {
   return static_cast<unsigned>(g < cap ? g : cap);
 }
 
+// Backward of the conv + SiLU, one channel d per grid column and a chunk of
+// batch rows per grid row.  For output t, v[t] = cb + sum_k w[k] x[t - 3 + k]
+// (forward; reverse mirrors it: x[t + 3 - k]), u = SiLU(v), and with
+// dv = du SiLU'(v), SiLU'(v) = s (1 + v (1 - s)), s = sigmoid(v):
+//   dx[t] = sum_k w[k] dv[t + 3 - k]   (reverse: dv[t - 3 + k])
+//   dw[k] = sum over rows and t of dv[t] x[t - 3 + k]   (reverse: x[t + 3 - k])
+//   dcb = sum of dv.
+// One element per thread and iteration, so that every load is coalesced;
+// each element recomputes the four dv it needs from cached x and du (eight
+// consecutive elements per thread, each dv evaluated once, measured 15 %
+// slower for their strided loads).  The workgroup's sums of dw and dcb go
+// to partial [chunk][d][5], which conv1d_silu_bwd_reduce_kernel adds over
+// chunks in a fixed order.
+template <typename T, bool REV>
+__global__ void __launch_bounds__(kThreads)
+conv1d_silu_bwd_kernel(const T *__restrict__ x, const float *__restrict__ w,
+                       const float *__restrict__ cb, const float *__restrict__ du,
+                       float *__restrict__ dx, float *__restrict__ partial, int64_t batch,
+                       int64_t dim, int L, int rows_per_chunk) {
+  constexpr int sgn = REV ? -1 : 1;          // taps lie at t - sgn (3 - k)
+  __shared__ float red[5][kThreads / 64];
+  const int64_t d = blockIdx.x;
+  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * rows_per_chunk;
+  const int nrows = static_cast<int>(batch - b0 < rows_per_chunk ? batch - b0 : rows_per_chunk);
+  const int n = nrows * L;
+  float wk[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) wk[k] = w[d * 4 + k];
+  const float bias = cb != nullptr ? cb[d] : 0.0f;
+  float acc[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};   // dw[0..3], dcb
+  for (int e = threadIdx.x; e < n; e += kThreads) {
+    const int rb = e / L, t = e - rb * L;
+    const int64_t base = ((b0 + rb) * dim + d) * L;
+    // xv[j] = x[t + sgn (j - 3)] for j = 0 .. 6 (0 outside the row)
+    float xv[7];
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+      const int s = t + sgn * (j - 3);
+      xv[j] = (s >= 0 && s < L) ? to_f32(x[base + s]) : 0.0f;
+    }
+    float dxv = 0.0f;
+#pragma unroll
+    for (int o = 0; o < 4; ++o) {           // output t' = t + sgn o reads x[t] through tap 3 - o
+      const int tp = t + sgn * o;
+      if (tp < 0 || tp >= L) continue;
+      float v = bias;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v = __builtin_fmaf(wk[k], xv[o + k], v);
+      const float sg = hw_rcp(1.0f + hw_exp2(-v * kLog2e));
+      const float dv = du[base + tp] * (sg * __builtin_fmaf(v, 1.0f - sg, 1.0f));
+      dxv = __builtin_fmaf(wk[3 - o], dv, dxv);
+      if (o == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[k] = __builtin_fmaf(dv, xv[k], acc[k]);
+        acc[4] += dv;
+      }
+    }
+    dx[base + t] = dxv;
+  }
+  // workgroup sums: within each wave, then across the four waves
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {
+    float v = acc[q];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0) red[q][wv] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < 5) {
+    float v = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kThreads / 64; ++k) v += red[threadIdx.x][k];
+    partial[(static_cast<int64_t>(blockIdx.y) * dim + d) * 5 + threadIdx.x] = v;
+  }
+}
+
+// dw [dim, 4] and dcb [dim] (may be null) from the chunk partials, in chunk order.
+__global__ void __launch_bounds__(kThreads)
+conv1d_silu_bwd_reduce_kernel(const float *__restrict__ partial, float *__restrict__ dw,
+                              float *__restrict__ dcb, int64_t dim, int nchunk) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;   // d * 5 + q
+  if (i >= dim * 5) return;
+  float v = 0.0f;
+  for (int c = 0; c < nchunk; ++c) v += partial[static_cast<int64_t>(c) * dim * 5 + i];
+  const int64_t d = i / 5;
+  const int q = static_cast<int>(i - d * 5);
+  if (q < 4) dw[d * 4 + q] = v;
+  else if (dcb != nullptr) dcb[d] = v;
+}
+
 bool aligned(const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
 }  // namespace
@@ -795,6 +886,44 @@ hipError_t launch_conv1d_silu(const void *x, const float *w, const float *cb, vo
     hipLaunchKernelGGL(conv1d_silu_kernel<float>, grid, dim3(kThreads), 0, s,
                        static_cast<const float *>(x), w, cb, static_cast<float *>(out), n, L, dim,
                        reverse, vec);
+  return hipGetLastError();
+}
+
+int conv1d_bwd_chunks(int64_t batch, int64_t dim, int *rows_per_chunk) {
+  // enough workgroups to fill the chip: about 2048 of them
+  int64_t nchunk = (2048 + dim - 1) / dim;
+  if (nchunk > batch) nchunk = batch;
+  if (nchunk < 1) nchunk = 1;
+  const int64_t rpc = (batch + nchunk - 1) / nchunk;
+  *rows_per_chunk = static_cast<int>(rpc);
+  return static_cast<int>((batch + rpc - 1) / rpc);
+}
+
+hipError_t launch_conv1d_silu_bwd(const void *x, const float *w, const float *cb, const float *du,
+                                  float *dx, float *dw, float *dcb, float *partial, int64_t batch,
+                                  int64_t dim, int64_t L, int reverse, bool bf16, hipStream_t s) {
+  if (batch * dim * L == 0) return hipSuccess;
+  int rpc = 0;
+  const int nchunk = conv1d_bwd_chunks(batch, dim, &rpc);
+  const dim3 grid(static_cast<unsigned>(dim), static_cast<unsigned>(nchunk));
+  const int Li = static_cast<int>(L);
+  if (bf16 && reverse)
+    hipLaunchKernelGGL((conv1d_silu_bwd_kernel<bf16_t, true>), grid, dim3(kThreads), 0, s,
+                       static_cast<const bf16_t *>(x), w, cb, du, dx, partial, batch, dim, Li, rpc);
+  else if (bf16)
+    hipLaunchKernelGGL((conv1d_silu_bwd_kernel<bf16_t, false>), grid, dim3(kThreads), 0, s,
+                       static_cast<const bf16_t *>(x), w, cb, du, dx, partial, batch, dim, Li, rpc);
+  else if (reverse)
+    hipLaunchKernelGGL((conv1d_silu_bwd_kernel<float, true>), grid, dim3(kThreads), 0, s,
+                       static_cast<const float *>(x), w, cb, du, dx, partial, batch, dim, Li, rpc);
+  else
+    hipLaunchKernelGGL((conv1d_silu_bwd_kernel<float, false>), grid, dim3(kThreads), 0, s,
+                       static_cast<const float *>(x), w, cb, du, dx, partial, batch, dim, Li, rpc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nred = dim * 5;
+  hipLaunchKernelGGL(conv1d_silu_bwd_reduce_kernel, dim3(static_cast<unsigned>((nred + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, partial, dw, dcb, dim, nchunk);
   return hipGetLastError();
 }
 

@@ -156,6 +156,12 @@ hipError_t launch_to_f32(const void *src, float *dst, int64_t n, hipStream_t s);
 hipError_t launch_conv1d_silu(const void *x, const float *w, const float *cb, void *out,
                               int64_t rows, int64_t L, int64_t dim, int reverse, bool bf16,
                               hipStream_t s);
+// Its backward: dx [rows][L] fp32, dw [dim][4], dcb [dim] (or null) fp32 from
+// du [rows][L] fp32; partial: conv1d_bwd_chunks(...) * dim * 5 floats.
+int conv1d_bwd_chunks(int64_t batch, int64_t dim, int *rows_per_chunk);
+hipError_t launch_conv1d_silu_bwd(const void *x, const float *w, const float *cb, const float *du,
+                                  float *dx, float *dw, float *dcb, float *partial, int64_t batch,
+                                  int64_t dim, int64_t L, int reverse, bool bf16, hipStream_t s);
 // [planes][H][W] -> [planes][W][H]
 hipError_t launch_transpose(const void *in, void *out, int64_t planes, int64_t H, int64_t W, bool bf16,
                             hipStream_t s);

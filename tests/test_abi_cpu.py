@@ -196,6 +196,25 @@ def test_plane_count_limit(lib):
     assert lib.vm_ss2d_scan_fwd(dirs, FAKE, None, 1.0, FAKE * 3, big, big, 2, 2, 16, 0, 1, None) == 6
 
 
+def test_conv_bwd_argument_checks(lib):
+    def call(x=FAKE, w=FAKE * 2, b=None, du=FAKE * 3, dx=FAKE * 4, dw=FAKE * 5, db=None,
+             batch=2, dim=4, L=9, rev=0, dtype=0):
+        return lib.vm_causal_conv1d_silu_bwd(x, w, b, du, dx, dw, db, batch, dim, L, rev, dtype, None)
+
+    assert call(x=None) == 1
+    assert call(du=None) == 1
+    assert call(dx=None) == 1
+    assert call(dw=None) == 1
+    assert call(L=0) == 2
+    assert call(rev=3) == 4
+    assert call(dtype=9) == 3
+    assert call(dim=1 << 24) == 6                           # one workgroup column per channel
+    assert call(dx=FAKE * 3 + 4) == 5                       # dx over du
+    assert call(dw=FAKE * 4 + 8) == 5                       # dw over dx
+    assert call(db=FAKE * 2) == 5                           # dbias over w
+    assert call(b=FAKE * 6, db=FAKE * 6 + 4) == 5           # dbias over bias
+
+
 def test_row_block_count_limit(lib):
     # scans run one or two 16-channel row blocks per workgroup on grid x: at
     # most 2^24 - 1 row blocks (batch * ceil(dim / 16))

@@ -671,6 +671,67 @@ def test_full_vim_tiny_bidir_fused_conv():
     assert_close(host(out[bsel]), ref, FP32_TOL, "vim-t fused conv full (sampled batches)")
 
 
+@pytest.mark.parametrize("L", [1, 2, 3, 9, 197])
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_conv1d_silu_bwd(L, reverse, dtype):
+    _case(f"conv bwd L{L} rev{reverse} {dtype}")
+    g = wl.generator(3200 + L, DEV)
+    x = torch.randn((3, 70, L), generator=g, device=DEV).to(dtype)
+    w, b = wl.conv_params(g, 70, DEV)
+    du = torch.randn((3, 70, L), generator=g, device=DEV)
+    dx, dw, db = vm.vm_causal_conv1d_silu_bwd(x, w, du, bias=b, reverse=reverse)
+    torch.cuda.synchronize()
+    wx, ww, wb, _ = ograd.causal_conv1d_silu_grad(host(x), host(w), host(b), host(du), reverse=reverse)
+    assert_close(host(dx), wx, FP32_TOL, "dx")
+    assert_close(host(dw), ww, FP32_TOL, "dw")
+    assert_close(host(db), wb, FP32_TOL, "dbias")
+
+
+def test_conv1d_silu_bwd_chunks_and_no_bias():
+    """Many batch rows per channel (several chunks per channel), no bias:
+    dbias of the zero bias is still the sum of dv; deterministic."""
+    _case("conv bwd chunks, no bias")
+    g = wl.generator(3300, DEV)
+    x = torch.randn((300, 24, 50), generator=g, device=DEV)
+    w, _ = wl.conv_params(g, 24, DEV)
+    du = torch.randn(x.shape, generator=g, device=DEV)
+    dx, dw, db = vm.vm_causal_conv1d_silu_bwd(x, w, du, with_dbias=True)
+    dx2, dw2, db2 = vm.vm_causal_conv1d_silu_bwd(x, w, du, with_dbias=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dx, dx2) and torch.equal(dw, dw2) and torch.equal(db, db2)
+    wx, ww, _, _ = ograd.causal_conv1d_silu_grad(host(x), host(w), None, host(du))
+    zb = np.zeros(24)
+    _, _, wb, _ = ograd.causal_conv1d_silu_grad(host(x), host(w), zb, host(du))
+    assert_close(host(dx), wx, FP32_TOL, "dx")
+    assert_close(host(dw), ww, FP32_TOL, "dw")
+    assert_close(host(db), wb, FP32_TOL, "dbias")
+    _, _, none = vm.vm_causal_conv1d_silu_bwd(x, w, du)
+    assert none is None
+
+
+def test_conv_and_scan_backward_chain():
+    """Training a Vim branch: the scan backward's du feeds the conv backward,
+    against the oracle's chained gradients."""
+    _case("conv + scan backward chain")
+    p, z = wl.single_inputs(3400, 2, 40, 60, device=DEV, gated=True, perturb=True)
+    g = wl.generator(3401, DEV)
+    x = p["u"].clone()
+    w, b = wl.conv_params(g, 40, DEV)
+    p["u"] = vm.vm_causal_conv1d_silu(x, w, b)
+    dout = torch.randn(x.shape, generator=g, device=DEV)
+    gs, _ = vm.vm_selective_scan_bwd(p, dout, z=z)
+    dx, dw, db = vm.vm_causal_conv1d_silu_bwd(x, w, gs["u"], bias=b)
+    torch.cuda.synchronize()
+    hp = host_dir(p)
+    hp["u"] = oracle.causal_conv1d_silu(host(x), host(w), host(b))
+    want, _, _ = ograd.selective_scan_grad(hp, host(dout), z=host(z))
+    wx, ww, wb, _ = ograd.causal_conv1d_silu_grad(host(x), host(w), host(b), want["u"])
+    assert_close(host(dx), wx, FP32_TOL, "dx")
+    assert_close(host(dw), ww, FP32_TOL, "dw")
+    assert_close(host(db), wb, FP32_TOL, "dbias")
+
+
 @pytest.mark.parametrize("L", [197, 600])
 def test_fused_conv_equals_conv_then_scan(L):
     # the in-kernel convolution takes the same fp32 operations in the same
