@@ -231,9 +231,10 @@ struct BwdScratch {
 
 int run_bwd(const vm_scan_dir *p, const float *dy, const vm_scan_grad *g, BwdScratch &bs,
             int64_t batch, int64_t dim, int64_t L, int64_t dstate, int options, int reverse,
-            Scratch &ws, hipStream_t s) {
+            Scratch &ws, hipStream_t s, bool ck_ready = false) {
   int st = VM_OK;
   vmk::BwdArgs a = {};
+  a.ck_ready = ck_ready ? 1 : 0;
   a.dir = resolve_dir(p, batch, dstate, L, false, ws, s, &st);
   if (st != VM_OK) return st;
   a.dy = dy;
@@ -732,18 +733,25 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
   hipStream_t s = static_cast<hipStream_t>(stream);
   Scratch ws(s);
   // dy = s * dout * SiLU(z) reaches both directions; dz needs y_f + y_b,
-  // which the forward kernel recomputes ungated with s = 1
+  // which the forward kernel recomputes ungated with s = 1.  For short
+  // sequences (on-chip exchange, 8-step tiles like the backward's) that
+  // recomputation also stores both directions' checkpoints, so that the
+  // backward kernels skip their first pass, and forms dy and dz itself.
+  const bool fuse = z != nullptr &&
+                    vmk::plan_scan(batch, dim, seqlen, static_cast<int>(dstate), 2, false).xmode ==
+                        vmk::kXLds;
   float *dy = ws.get(tok, &st);
-  float *y = z != nullptr ? ws.get(tok, &st) : nullptr;
+  float *y = z != nullptr && !fuse ? ws.get(tok, &st) : nullptr;
   BwdScratch bs;
   if (st == VM_OK) st = bs.get(ws, batch, dim, seqlen, dstate);
+  float *ck_b = fuse ? ws.get(batch * dim * vmk::scan_bwd_tiles(seqlen) * 16, &st) : nullptr;
   vmk::ScanArgs a = {};                 // the forward recomputation (with z)
-  a.out = y;
+  a.out = fuse ? dy : y;                // (not written when fused)
   a.batch = batch;
   a.dim = dim;
   a.L = seqlen;
   a.dstate = static_cast<int>(dstate);
-  if (st == VM_OK && z != nullptr) st = exchange_for(a, false, ws);
+  if (st == VM_OK && z != nullptr && !fuse) st = exchange_for(a, false, ws);
   if (st != VM_OK) return st;
   // bf16 inputs run the fp32 path on widened copies
   const vm_scan_dir wf = widen_dir(fwd, tok, batch, seqlen, dstate, bf16, ws, s, &st);
@@ -758,14 +766,26 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
     a.softplus = (options & VM_DELTA_SOFTPLUS) != 0;
     a.zoh = (options & VM_ZOH) != 0;
     a.scale = 1.0f;
+    if (fuse) {
+      a.ck[0] = bs.ck;
+      a.ck[1] = ck_b;
+      a.gz = z32;
+      a.dout = dout32;
+      a.dy = dy;
+      a.dz = static_cast<float *>(dz);
+      a.gscale = combine_scale;
+    }
     st = launch_bidir(a, false, ws, s);
     if (st != VM_OK) return st;
   }
-  st = hip_status(vmk::launch_gate_bwd(y, z32, dout32, dy, static_cast<float *>(dz), tok,
-                                       combine_scale, s));
-  if (st != VM_OK) return st;
-  st = run_bwd(&wf, dy, gf, bs, batch, dim, seqlen, dstate, options, 0, ws, s);
-  if (st == VM_OK) st = run_bwd(&wb, dy, gb, bs, batch, dim, seqlen, dstate, options, 1, ws, s);
+  if (!fuse) {
+    st = hip_status(vmk::launch_gate_bwd(y, z32, dout32, dy, static_cast<float *>(dz), tok,
+                                         combine_scale, s));
+    if (st != VM_OK) return st;
+  }
+  st = run_bwd(&wf, dy, gf, bs, batch, dim, seqlen, dstate, options, 0, ws, s, fuse);
+  if (st == VM_OK && fuse) bs.ck = ck_b;
+  if (st == VM_OK) st = run_bwd(&wb, dy, gb, bs, batch, dim, seqlen, dstate, options, 1, ws, s, fuse);
   return st;
 }
 

@@ -211,18 +211,20 @@ scan_bwd_kernel(const BwdArgs p) {
     }
   };
 
-  // ---- pass 1: states at every tile start, in visit order
+  // ---- pass 1: states at every tile start, in visit order (unless the
+  // forward kernel that recomputed the output stored them already)
   float h[kNS];
 #pragma unroll
   for (int j = 0; j < kNS; ++j) h[j] = 0.0f;
-  stage_load(tile_of(0), false);
-  for (int k = 0; k < nt; ++k) {
+  const int nt1 = p.ck_ready ? 0 : nt;
+  if (nt1 > 0) stage_load(tile_of(0), false);
+  for (int k = 0; k < nt1; ++k) {
     const int j = tile_of(k);
 #pragma unroll
     for (int jn = 0; jn < kNS; ++jn)
       bstore<float>(rCk, ck_lane + static_cast<uint32_t>(j) * 64u + 4u * jn, h[jn]);
     stage_store();
-    stage_load(tile_of(k + 1 < nt ? k + 1 : nt - 1), false);
+    stage_load(tile_of(k + 1 < nt1 ? k + 1 : nt1 - 1), false);
 #pragma unroll
     for (int q = 0; q < T; ++q) {
       const float4 pq = *reinterpret_cast<const float4 *>(prep + r * Lay::PST + 4 * q);

@@ -152,6 +152,7 @@ __attribute__((amdgpu_waves_per_eu(T == 16 ? 2 : ((OPT & kOptConv) != 0 ? 3 : 4)
 scan_kernel(const ScanArgs p) {
   constexpr bool ZOH = (OPT & kOptZoh) != 0;
   constexpr bool CONV = (OPT & kOptConv) != 0;
+  constexpr bool CK = (OPT & kOptBwdPrep) != 0;  // prepare the backward pass (checkpoints, gate)
   constexpr int NS = 16 / SPLIT;                 // states per lane
   constexpr int R = 64 / SPLIT;                  // channels per workgroup
   constexpr int PE = R * T / 64;                 // staged (dt, u) elements per lane per tile
@@ -161,6 +162,7 @@ scan_kernel(const ScanArgs p) {
   using Lay = Layout<T, R, CONV>;
   static_assert(NS >= 4 && NS <= 8 && R % 16 == 0 && T % 4 == 0 && (R * T) % 64 == 0, "shape");
   static_assert(DIRS == 1 ? XMODE == kXNone : XMODE != kXNone, "mode");
+  static_assert(!CK || (T == kBwdTile && XMODE == kXLds), "checkpoints: the backward pass's tiles");
 
   extern __shared__ float smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -234,6 +236,16 @@ scan_kernel(const ScanArgs p) {
                              CONV ? static_cast<uint32_t>(rows) * 16u : 0u);
   const Rsrc rCb = make_rsrc(CONV && P.cb != nullptr ? P.cb + d0 : nullptr,
                              CONV && P.cb != nullptr ? static_cast<uint32_t>(rows) * 4u : 0u);
+  // Backward preparation (CK): the state entering each tile, as the backward
+  // kernel's first pass would store it (rows past dim fall outside the
+  // resource), and the gate's backward in place of out.
+  const Rsrc rCk = make_rsrc(CK ? p.ck[dw] + (static_cast<int64_t>(b) * dim + d0) * nt * 16 : nullptr,
+                             CK ? static_cast<uint32_t>(rows * nt) * 64u : 0u);
+  const uint32_t ck_lane = static_cast<uint32_t>(r * nt) * 64u + static_cast<uint32_t>(sp * (16 / SPLIT)) * 4u;
+  const Rsrc rGz = make_rsrc(CK ? p.gz + rowbase : nullptr, CK ? slab : 0u);
+  const Rsrc rDo = make_rsrc(CK ? p.dout + rowbase : nullptr, CK ? slab : 0u);
+  const Rsrc rDy = make_rsrc(CK ? p.dy + rowbase : nullptr, CK ? slab : 0u);
+  const Rsrc rDz = make_rsrc(CK ? p.dz + rowbase : nullptr, CK ? slab : 0u);
   float A2[NS], iA[NS], h[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) h[j] = 0.0f;
@@ -460,6 +472,11 @@ scan_kernel(const ScanArgs p) {
     using Qn = std::integral_constant<int, (decltype(slot)::value + 1) % NB>;
     comb_load(k + 1 < nt ? k + 1 : nt - 1, Qn(), second);
     stage_load(k + NB < nt ? k + NB : nt - 1, slot);
+    if constexpr (CK) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j)
+        bstore<float>(rCk, ck_lane + static_cast<uint32_t>(tile_of(k)) * 64u + 4u * j, h[j]);
+    }
     do_scan();
     comb_read(k, second);
     stage_store(Qn(), k + 1 < nt ? k + 1 : nt - 1);
@@ -537,17 +554,34 @@ scan_kernel(const ScanArgs p) {
     const int tid = static_cast<int>(threadIdx.x) - sub * NT;
     int fr = tid / L, ft = tid % L;
     for (int f0 = tid; f0 < n; f0 += U * NT) {
-      float v[U];
+      float v[U], gzv[U], gdo[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {          // reads first, so their latency overlaps
         v[u] = xlds[(fr < R ? fr : R - 1) * XS + ft];
         ft += NT;
         while (ft >= L) { ft -= L; ++fr; }
+        if constexpr (CK) {
+          const int f = f0 + u * NT;
+          const uint32_t o = pin_u(f < n ? static_cast<uint32_t>(f) * 4u : kOob);
+          gzv[u] = bload<float>(rGz, o);
+          gdo[u] = bload<float>(rDo, o);
+        }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int f = f0 + u * NT;
-        bstore<Tin>(rO, pin_u(f < n ? static_cast<uint32_t>(f) * ES : kOob), v[u]);
+        if constexpr (CK) {
+          // v is the ungated y: dy = s dout SiLU(z), dz = s dout y SiLU'(z),
+          // SiLU'(z) = sg (1 + z (1 - sg)), sg = sigmoid(z)
+          const uint32_t o = pin_u(f < n ? static_cast<uint32_t>(f) * 4u : kOob);
+          const float zv = pin(gzv[u]);
+          const float g = p.gscale * pin(gdo[u]);
+          const float sg = hw_rcp(1.0f + hw_exp2(-zv * kLog2e));
+          bstore<float>(rDy, o, g * zv * sg);
+          bstore<float>(rDz, o, g * v[u] * (sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f)));
+        } else {
+          bstore<Tin>(rO, pin_u(f < n ? static_cast<uint32_t>(f) * ES : kOob), v[u]);
+        }
       }
     }
   }
@@ -577,6 +611,15 @@ hipError_t dispatch_mode(const ScanPlan &plan, const ScanArgs &a, hipStream_t s)
 
 template <typename Tin>
 hipError_t dispatch_dtype(const ScanPlan &plan, const ScanArgs &a, hipStream_t s) {
+  if (a.ck[0] != nullptr) {
+    // backward preparation: fp32, no conv, on-chip exchange
+    if constexpr (std::is_same<Tin, float>::value) {
+      if (plan.dirs == 2 && plan.xmode == kXLds && !a.conv)
+        return a.zoh ? launch_one<float, 4, 2, kXLds, 8, kOptBwdPrep | kOptZoh>(plan, a, s)
+                     : launch_one<float, 4, 2, kXLds, 8, kOptBwdPrep>(plan, a, s);
+    }
+    return hipErrorInvalidValue;
+  }
   switch ((a.zoh ? kOptZoh : 0) | (a.conv ? kOptConv : 0)) {
     case 0: return dispatch_mode<Tin, 4, 0>(plan, a, s);
     case kOptZoh: return dispatch_mode<Tin, 4, kOptZoh>(plan, a, s);

@@ -82,6 +82,14 @@ struct ScanArgs {
   void *out;            // [batch, dim, L] (Tin)
   float *xglobal;       // fp32 exchange rows (long bidirectional), row stride xstride
   int64_t xstride;
+  // Backward preparation (kOptBwdPrep): per direction, the state at every
+  // 8-step tile start, [batch * dim][ceil(L / 8)][16] fp32; and in place of
+  // out, the gate's backward from the ungated y: dy = gscale dout SiLU(z),
+  // dz = gscale dout y SiLU'(z) (all [batch, dim, L] fp32).
+  float *ck[2];
+  const float *gz, *dout;
+  float *dy, *dz;
+  float gscale;
   int64_t batch, dim, L;
   int dstate;
   int softplus;
@@ -92,7 +100,7 @@ struct ScanArgs {
 };
 
 // Kernel variants (template bits of the scan kernel).
-enum ScanOpt { kOptZoh = 1, kOptConv = 2 };
+enum ScanOpt { kOptZoh = 1, kOptConv = 2, kOptBwdPrep = 4 };
 
 // Where a bidirectional scan parks first-visit sums: in LDS (short
 // sequences) or in fp32 global memory.
@@ -133,6 +141,7 @@ struct BwdArgs {
   int softplus;
   int zoh;              // zero-order-hold write
   int reverse;
+  int ck_ready;         // ck already holds the checkpoints (the forward kernel wrote them)
 };
 constexpr int kBwdTile = 8;
 int64_t scan_bwd_tiles(int64_t L);
