@@ -312,6 +312,11 @@ typedef struct vm_scan_grad {
   float *dC;           /* [batch, dstate, seqlen] */
   float *dD;           /* [dim]                */
   float *ddelta_bias;  /* [dim] or NULL        */
+  /* With the fused conv (conv_w in the direction, whose u is then the conv
+     input x): du receives the gradient with respect to x, and these the
+     conv parameters' (dconv_b NULL = not computed).  Unused otherwise. */
+  float *dconv_w;      /* [dim, 4]             */
+  float *dconv_b;      /* [dim] or NULL        */
 } vm_scan_grad;
 
 /*
@@ -325,14 +330,15 @@ typedef struct vm_scan_grad {
  * Gradients are fp32 for either dtype (VM_BF16 inputs are widened exactly
  * and the pass runs in fp32).  Either write (options as the forward call's:
  * with VM_ZOH the derivatives of k = expm1(dt A) / A are included, A = 0
- * among them); no fused conv (VM_ERR_UNSUPPORTED).  Gradient buffers must not
+ * among them), with or without the fused conv (see vm_scan_grad).  Gradient buffers must not
  * overlap any input or each other (VM_ERR_ALIAS).  Sums over batch rows (dA,
  * dD, ddelta_bias) and over channels (dB, dC) are formed from per-block
  * partials in a fixed order, so results are deterministic.
  * Temporary memory: state checkpoints ([batch * dim, seqlen / 8, 16] fp32),
  * the partials ([dim / 16, batch, dstate, seqlen] fp32 for each of dB, dC),
- * with z the recomputed forward output and dy, and with VM_BF16 fp32 copies
- * of the token tensors.
+ * with z the recomputed forward output and dy, with VM_BF16 fp32 copies of
+ * the token tensors, and with the fused conv the conv output, its gradient
+ * and the conv backward's partial sums.
  */
 int vm_selective_scan_bwd(const vm_scan_dir *p, const void *z,
                           const void *dout, const vm_scan_grad *g, void *dz,

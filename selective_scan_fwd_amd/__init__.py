@@ -46,7 +46,8 @@ class VmScanDir(ctypes.Structure):
 
 class VmScanGrad(ctypes.Structure):
     """struct vm_scan_grad (one direction's gradient buffers)."""
-    _fields_ = [(k, ctypes.c_void_p) for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "ddelta_bias")]
+    _fields_ = [(k, ctypes.c_void_p) for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "ddelta_bias",
+                                                "dconv_w", "dconv_b")]
 
 
 class VmError(RuntimeError):
@@ -286,12 +287,17 @@ def vm_causal_conv1d_silu_bwd(x, w, du, bias=None, reverse=False, with_dbias=Non
 
 
 def _grad_set(p, batch, dim, L, N, device, with_bias):
+    """Gradient buffers of one direction; with the fused conv (p["conv_w"])
+    also conv_w (and conv_b when p has one), and u is then the conv input's."""
     f = lambda *shape: torch.empty(shape, dtype=torch.float32, device=device)
+    conv = p.get("conv_w") is not None
     g = dict(u=f(batch, dim, L), delta=f(batch, dim, L), A=f(dim, N), B=f(batch, N, L),
              C=f(batch, N, L), D=f(dim), delta_bias=f(dim) if with_bias else None)
-    s = VmScanGrad(g["u"].data_ptr(), g["delta"].data_ptr(), g["A"].data_ptr(), g["B"].data_ptr(),
-                   g["C"].data_ptr(), g["D"].data_ptr(),
-                   g["delta_bias"].data_ptr() if with_bias else None)
+    if conv:
+        g["conv_w"] = f(dim, 4)
+        g["conv_b"] = f(dim) if p.get("conv_b") is not None else None
+    ptr = lambda k: g[k].data_ptr() if g.get(k) is not None else None
+    s = VmScanGrad(*(ptr(k) for k in ("u", "delta", "A", "B", "C", "D", "delta_bias", "conv_w", "conv_b")))
     return s, g
 
 

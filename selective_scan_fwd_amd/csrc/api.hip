@@ -261,13 +261,15 @@ int run_bwd(const vm_scan_dir *p, const float *dy, const vm_scan_grad *g, BwdScr
 // Checks of a gradient set: required pointers, no overlap with the inputs
 // (ins) or with the other outputs (outs, extended here).
 int check_grad(const vm_scan_grad *g, int64_t tok, int64_t bc, int64_t dim, int64_t dstate,
-               const std::vector<Span> &ins, std::vector<Span> &outs) {
+               bool conv, const std::vector<Span> &ins, std::vector<Span> &outs) {
   if (g == nullptr || g->du == nullptr || g->ddelta == nullptr || g->dA == nullptr ||
-      g->dB == nullptr || g->dC == nullptr || g->dD == nullptr)
+      g->dB == nullptr || g->dC == nullptr || g->dD == nullptr || (conv && g->dconv_w == nullptr))
     return VM_ERR_NULL;
   const Span mine[] = {span(g->du, tok * 4), span(g->ddelta, tok * 4), span(g->dA, dim * dstate * 4),
                        span(g->dB, bc * 4), span(g->dC, bc * 4), span(g->dD, dim * 4),
-                       span(g->ddelta_bias, dim * 4)};
+                       span(g->ddelta_bias, dim * 4),
+                       conv ? span(g->dconv_w, dim * 16) : Span(),
+                       conv ? span(g->dconv_b, dim * 4) : Span()};
   for (const Span &m : mine) {
     for (const Span &i : ins)
       if (overlaps(m, i)) return VM_ERR_ALIAS;
@@ -283,8 +285,9 @@ void dir_spans(const vm_scan_dir *p, int64_t tok, int64_t batch, int64_t L, int6
   const int64_t bc = bc_extent(batch, dstate, L, p->bc_stride);
   const Span sp[] = {span(p->u, tok * es), span(p->delta, tok * es), span(p->A, dim * dstate * 4),
                      span(p->B, bc * es), span(p->C, bc * es), span(p->D, dim * 4),
-                     span(p->delta_bias, dim * 4)};
-  ins.insert(ins.end(), sp, sp + 7);
+                     span(p->delta_bias, dim * 4), span(p->conv_w, dim * 16),
+                     span(p->conv_b, dim * 4)};
+  ins.insert(ins.end(), sp, sp + 9);
 }
 
 // fp32 view of a direction's token tensors for the backward pass: the
@@ -302,8 +305,36 @@ vm_scan_dir widen_dir(const vm_scan_dir *p, int64_t tok, int64_t batch, int64_t 
   return w;
 }
 
-// Shared checks of the backward entry points (no fused conv; dz exactly when
-// z).
+// The fused conv around a direction's backward: its input x (fp32), the
+// conv output u it scans (temporary), and the temporary u gradient, which the
+// conv backward turns into the x, weight and bias gradients of g.
+struct ConvBwd {
+  const float *x = nullptr;
+  float *u = nullptr, *du = nullptr, *partial = nullptr;
+  int get(Scratch &ws, int64_t tok, int64_t batch, int64_t dim) {
+    int st = VM_OK, rpc = 0;
+    u = ws.get(tok, &st);
+    du = ws.get(tok, &st);
+    partial = ws.get(static_cast<int64_t>(vmk::conv1d_bwd_chunks(batch, dim, &rpc)) * dim * 5, &st);
+    return st;
+  }
+  // u = SiLU(conv(x)); the direction then scans u without the conv
+  int forward(vm_scan_dir &w, int64_t batch, int64_t dim, int64_t L, int reverse, hipStream_t s) {
+    x = static_cast<const float *>(w.u);
+    const int st = hip_status(vmk::launch_conv1d_silu(x, w.conv_w, w.conv_b, u, batch * dim, L, dim,
+                                                      reverse, false, s));
+    w.u = u;
+    return st;
+  }
+  int backward(const vm_scan_dir &p, const vm_scan_grad *g, int64_t batch, int64_t dim, int64_t L,
+               int reverse, hipStream_t s) {
+    return hip_status(vmk::launch_conv1d_silu_bwd(x, p.conv_w, p.conv_b, du, g->du, g->dconv_w,
+                                                  g->dconv_b, partial, batch, dim, L, reverse,
+                                                  false, s));
+  }
+};
+
+// Shared checks of the backward entry points (dz exactly when z).
 int check_bwd_common(int dtype, int options, int64_t batch, int64_t dim, int64_t L, int64_t dstate,
                      const void *z, const void *dout, const void *dz, int64_t *tok, int64_t *bc) {
   if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;
@@ -654,12 +685,12 @@ int vm_selective_scan_bwd(const vm_scan_dir *p, const void *z, const void *dout,
   const int es = bf16 ? 2 : 4;
   st = check_dir(p, tok, tok, batch, seqlen, dim, dstate, es, Span());
   if (st != VM_OK) return st;
-  if (p->conv_w != nullptr) return VM_ERR_UNSUPPORTED;
+  const bool conv = p->conv_w != nullptr;
   std::vector<Span> ins, outs;
   dir_spans(p, tok, batch, seqlen, dim, dstate, es, ins);
   ins.push_back(span(z, tok * es));
   ins.push_back(span(dout, tok * es));
-  st = check_grad(g, tok, bc, dim, dstate, ins, outs);
+  st = check_grad(g, tok, bc, dim, dstate, conv, ins, outs);
   if (st != VM_OK) return st;
   for (const Span &o : outs)
     if (overlaps(span(dz, tok * 4), o)) return VM_ERR_ALIAS;
@@ -673,12 +704,16 @@ int vm_selective_scan_bwd(const vm_scan_dir *p, const void *z, const void *dout,
   st = bs.get(ws, batch, dim, seqlen, dstate);
   float *y = z != nullptr ? ws.get(tok, &st) : nullptr;
   float *dyb = z != nullptr ? ws.get(tok, &st) : nullptr;
+  ConvBwd cv;
+  if (st == VM_OK && conv) st = cv.get(ws, tok, batch, dim);
   if (st != VM_OK) return st;
   // bf16 inputs run the fp32 path on widened copies
-  const vm_scan_dir w = widen_dir(p, tok, batch, seqlen, dstate, bf16, ws, s, &st);
+  vm_scan_dir w = widen_dir(p, tok, batch, seqlen, dstate, bf16, ws, s, &st);
   const float *z32 = as_f32(z, tok, bf16 && z != nullptr, ws, s, &st);
   const float *dy = as_f32(dout, tok, bf16, ws, s, &st);
+  if (st == VM_OK && conv) st = cv.forward(w, batch, dim, seqlen, reverse, s);
   if (st != VM_OK) return st;
+  w.conv_w = w.conv_b = nullptr;
   if (z != nullptr) {
     // the ungated forward output, for dz, then dy = dout * SiLU(z)
     vmk::ScanArgs a = {};
@@ -700,7 +735,12 @@ int vm_selective_scan_bwd(const vm_scan_dir *p, const void *z, const void *dout,
     if (st != VM_OK) return st;
     dy = dyb;
   }
-  return run_bwd(&w, dy, g, bs, batch, dim, seqlen, dstate, options, reverse, ws, s);
+  if (!conv) return run_bwd(&w, dy, g, bs, batch, dim, seqlen, dstate, options, reverse, ws, s);
+  vm_scan_grad gu = *g;
+  gu.du = cv.du;
+  st = run_bwd(&w, dy, &gu, bs, batch, dim, seqlen, dstate, options, reverse, ws, s);
+  if (st != VM_OK) return st;
+  return cv.backward(*p, g, batch, dim, seqlen, reverse, s);
 }
 
 int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void *z,
@@ -716,14 +756,15 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
   st = check_dir(fwd, tok, tok, batch, seqlen, dim, dstate, es, Span());
   if (st == VM_OK) st = check_dir(bwd, tok, tok, batch, seqlen, dim, dstate, es, Span());
   if (st != VM_OK) return st;
-  if (fwd->conv_w != nullptr || bwd->conv_w != nullptr) return VM_ERR_UNSUPPORTED;
+  if ((fwd->conv_w == nullptr) != (bwd->conv_w == nullptr)) return VM_ERR_UNSUPPORTED;
+  const bool conv = fwd->conv_w != nullptr;
   std::vector<Span> ins, outs;
   dir_spans(fwd, tok, batch, seqlen, dim, dstate, es, ins);
   dir_spans(bwd, tok, batch, seqlen, dim, dstate, es, ins);
   ins.push_back(span(z, tok * es));
   ins.push_back(span(dout, tok * es));
-  st = check_grad(gf, tok, bc, dim, dstate, ins, outs);
-  if (st == VM_OK) st = check_grad(gb, tok, bc, dim, dstate, ins, outs);
+  st = check_grad(gf, tok, bc, dim, dstate, conv, ins, outs);
+  if (st == VM_OK) st = check_grad(gb, tok, bc, dim, dstate, conv, ins, outs);
   if (st != VM_OK) return st;
   for (const Span &o : outs)
     if (overlaps(span(dz, tok * 4), o)) return VM_ERR_ALIAS;
@@ -745,6 +786,9 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
   BwdScratch bs;
   if (st == VM_OK) st = bs.get(ws, batch, dim, seqlen, dstate);
   float *ck_b = fuse ? ws.get(batch * dim * vmk::scan_bwd_tiles(seqlen) * 16, &st) : nullptr;
+  ConvBwd cvf, cvb;
+  if (st == VM_OK && conv) st = cvf.get(ws, tok, batch, dim);
+  if (st == VM_OK && conv) st = cvb.get(ws, tok, batch, dim);
   vmk::ScanArgs a = {};                 // the forward recomputation (with z)
   a.out = fuse ? dy : y;                // (not written when fused)
   a.batch = batch;
@@ -754,11 +798,16 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
   if (st == VM_OK && z != nullptr && !fuse) st = exchange_for(a, false, ws);
   if (st != VM_OK) return st;
   // bf16 inputs run the fp32 path on widened copies
-  const vm_scan_dir wf = widen_dir(fwd, tok, batch, seqlen, dstate, bf16, ws, s, &st);
-  const vm_scan_dir wb = widen_dir(bwd, tok, batch, seqlen, dstate, bf16, ws, s, &st);
+  vm_scan_dir wf = widen_dir(fwd, tok, batch, seqlen, dstate, bf16, ws, s, &st);
+  vm_scan_dir wb = widen_dir(bwd, tok, batch, seqlen, dstate, bf16, ws, s, &st);
   const float *z32 = as_f32(z, tok, bf16 && z != nullptr, ws, s, &st);
   const float *dout32 = as_f32(dout, tok, bf16, ws, s, &st);
+  // with the fused conv each direction scans its own u = SiLU(conv(x)), the
+  // backward direction's convolution running in reversed order
+  if (st == VM_OK && conv) st = cvf.forward(wf, batch, dim, seqlen, 0, s);
+  if (st == VM_OK && conv) st = cvb.forward(wb, batch, dim, seqlen, 1, s);
   if (st != VM_OK) return st;
+  wf.conv_w = wf.conv_b = wb.conv_w = wb.conv_b = nullptr;
   if (z != nullptr) {
     a.dir[0] = resolve_dir(&wf, batch, dstate, seqlen, false, ws, s, &st);
     a.dir[1] = resolve_dir(&wb, batch, dstate, seqlen, false, ws, s, &st);
@@ -783,9 +832,16 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
                                          combine_scale, s));
     if (st != VM_OK) return st;
   }
-  st = run_bwd(&wf, dy, gf, bs, batch, dim, seqlen, dstate, options, 0, ws, s, fuse);
+  vm_scan_grad guf = *gf, gub = *gb;   // the scans' u gradients (temporary with the conv)
+  if (conv) {
+    guf.du = cvf.du;
+    gub.du = cvb.du;
+  }
+  st = run_bwd(&wf, dy, &guf, bs, batch, dim, seqlen, dstate, options, 0, ws, s, fuse);
   if (st == VM_OK && fuse) bs.ck = ck_b;
-  if (st == VM_OK) st = run_bwd(&wb, dy, gb, bs, batch, dim, seqlen, dstate, options, 1, ws, s, fuse);
+  if (st == VM_OK) st = run_bwd(&wb, dy, &gub, bs, batch, dim, seqlen, dstate, options, 1, ws, s, fuse);
+  if (st == VM_OK && conv) st = cvf.backward(*fwd, gf, batch, dim, seqlen, 0, s);
+  if (st == VM_OK && conv) st = cvb.backward(*bwd, gb, batch, dim, seqlen, 1, s);
   return st;
 }
 

@@ -294,8 +294,10 @@ def test_bwd_argument_checks(lib):
     assert single(z=FAKE * 4, dz=FAKE * 3) == 5             # dz over dout
     fc = _dir(FAKE)
     fc.conv_w = FAKE * 7
-    assert single(p=fc) == 6
-    assert single(p=fc, opt=3) == 6                         # no fused conv, either write
+    assert single(p=fc) == 1                                # fused conv: dconv_w required
+    gc = grads(FAKE * 5)
+    gc.dconv_w = FAKE + 8                                   # ... and not over an input (u)
+    assert single(p=fc, g=gc) == 5
 
     def bidir(g2=gb, scale=1.0, dtype=0):
         return lib.vm_bidir_scan_bwd(ctypes.byref(f), ctypes.byref(b), None, FAKE * 3, scale,

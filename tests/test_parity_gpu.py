@@ -852,6 +852,64 @@ def test_bwd_zoh_bidir(L, dtype):
     assert_close(host(dz), wdz, tol, "dz")
 
 
+def _conv_scan_inputs(p):
+    """Host copy of a conv direction with u replaced by the oracle's conv output."""
+    h = host_dir(p)
+    x, w, b = h.pop("u"), h.pop("conv_w"), h.pop("conv_b", None)
+    return h, x, w, b
+
+
+@pytest.mark.parametrize("L", [77, 600])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_bwd_bidir_fused_conv(L, dtype):
+    """Backward of the bidirectional scan with the fused conv (both
+    directions reading the same x through their own convolutions)."""
+    _case(f"bwd bidir fused conv L{L} {dtype}")
+    fwd, bwd, z = wl.bidir_inputs(3500 + L, 2, 40, L, device=DEV, dtype=dtype, perturb=True)
+    bwd["u"] = fwd["u"]
+    g = wl.generator(3600 + L, DEV)
+    for q in (fwd, bwd):
+        q["conv_w"], q["conv_b"] = wl.conv_params(g, 40, DEV)
+    dout = torch.randn(z.shape, generator=g, device=DEV).to(dtype)
+    gf, gb, dz = vm.vm_bidir_scan_bwd(fwd, bwd, dout, z=z, combine_scale=0.5)
+    torch.cuda.synchronize()
+    hf, xf, wf_, bf_ = _conv_scan_inputs(fwd)
+    hb, xb, wb_, bb_ = _conv_scan_inputs(bwd)
+    hf["u"] = oracle.causal_conv1d_silu(xf, wf_, bf_)
+    hb["u"] = oracle.causal_conv1d_silu(xb, wb_, bb_, reverse=True)
+    wantf, wantb, wdz, _ = ograd.bidir_scan_grad(hf, hb, host(dout), z=host(z), combine_scale=0.5)
+    for got, want, x, w, b, rev, tag in ((gf, wantf, xf, wf_, bf_, False, "fwd"),
+                                         (gb, wantb, xb, wb_, bb_, True, "bwd")):
+        dx, dw, db, _ = ograd.causal_conv1d_silu_grad(x, w, b, want["u"], reverse=rev)
+        assert_close(host(got["u"]), dx, FP32_TOL, f"{tag} dx")
+        assert_close(host(got["conv_w"]), dw, FP32_TOL, f"{tag} dconv_w")
+        assert_close(host(got["conv_b"]), db, FP32_TOL, f"{tag} dconv_b")
+        for k in _GRAD_KEYS[1:]:
+            assert_close(host(got[k]), want[k], FP32_TOL, f"{tag} d{k}")
+    assert_close(host(dz), wdz, FP32_TOL, "dz")
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_bwd_single_fused_conv(reverse):
+    _case(f"bwd single fused conv rev{reverse}")
+    p, z = wl.single_inputs(3700 + reverse, 2, 40, 50, device=DEV, gated=True, perturb=True)
+    g = wl.generator(3710 + reverse, DEV)
+    p["conv_w"], _ = wl.conv_params(g, 40, DEV)          # no conv bias
+    dout = torch.randn(p["u"].shape, generator=g, device=DEV)
+    got, dz = vm.vm_selective_scan_bwd(p, dout, z=z, reverse=reverse)
+    torch.cuda.synchronize()
+    assert got["conv_b"] is None
+    h, x, w, _ = _conv_scan_inputs(p)
+    h["u"] = oracle.causal_conv1d_silu(x, w, None, reverse=reverse)
+    want, wdz, _ = ograd.selective_scan_grad(h, host(dout), z=host(z), reverse=reverse)
+    dx, dw, _, _ = ograd.causal_conv1d_silu_grad(x, w, None, want["u"], reverse=reverse)
+    assert_close(host(got["u"]), dx, FP32_TOL, "dx")
+    assert_close(host(got["conv_w"]), dw, FP32_TOL, "dconv_w")
+    for k in _GRAD_KEYS[1:]:
+        assert_close(host(got[k]), want[k], FP32_TOL, f"d{k}")
+    assert_close(host(dz), wdz, FP32_TOL, "dz")
+
+
 def test_bwd_small_dstate_no_softplus_dense_bc():
     _case("bwd N5 no softplus dense B/C")
     p, z = wl.single_inputs(2700, 3, 33, 50, dstate=5, device=DEV, bc_layout="dense")
