@@ -125,3 +125,34 @@ def causal_conv1d_silu_grad(x, w, bias, du, reverse=False):
     return xt.grad.numpy().copy(), wt.grad.numpy().copy(), \
         (bt.grad.numpy().copy() if bt is not None else None), u.detach().numpy()
 
+
+def pool_scan_repeat_grad(fwd, bwd, dout, z=None, combine_scale=1.0, pool_axis=0,
+                          delta_softplus=True, zoh=False):
+    """Gradients of L = sum(dout * out) for the FastVim pooled path (FastVim
+    summary, "Methodology"): u [batch, dim, H, W] is mean-pooled over W
+    (pool_axis 0, Lp = H) or over H (axis 1, Lp = W) as (sum in index order)
+    times 1/w, the pooled sequence is scanned forward (and backward when bwd
+    is given), the sum is repeated along the pooled axis and gated with
+    SiLU(z).  delta, B, C have the pooled length.  Returns (grads of fwd,
+    grads of bwd or None, dz or None, out)."""
+    lf = _leaves(fwd)
+    lb = _leaves(bwd) if bwd is not None else None
+    zt = _t(z)
+
+    def pooled(lv):
+        u = lv[0]
+        w = u.shape[3] if pool_axis == 0 else u.shape[2]
+        ubar = u.sum(dim=3 if pool_axis == 0 else 2) * (1.0 / w)
+        return [ubar] + lv[1:]
+
+    y = _direction_y(pooled(lf), delta_softplus, False, zoh)
+    if lb is not None:
+        y = y + _direction_y(pooled(lb), delta_softplus, True, zoh)
+    rep = y[:, :, :, None] if pool_axis == 0 else y[:, :, None, :]
+    out = combine_scale * rep.expand(fwd["u"].shape)
+    if zt is not None:
+        out = out * torch.nn.functional.silu(zt)
+    (out * _t(dout, False)).sum().backward()
+    return _grads(lf), (_grads(lb) if lb is not None else None), \
+        (zt.grad.numpy().copy() if zt is not None else None), out.detach().numpy()
+

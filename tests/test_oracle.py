@@ -619,3 +619,17 @@ def test_conv_first_tokens_see_zero_padding():
     w = np.array([[1.0, 2.0, 4.0, 8.0]])
     got = oracle.causal_conv1d_silu(x, w)[0, 0]
     _close(got, _silu(np.array([8.0, 12.0, 14.0, 15.0, 15.0, 15.0])), 1e-14)
+
+
+@pytest.mark.parametrize("H,W", [(56, 56), (57, 57), (5, 8), (1, 1)])
+def test_atrous_gather_and_scatter_are_adjoint(H, W):
+    """<gather(x), s> = <x, scatter(s)>: gather is a permutation into the
+    streams with zero padding, scatter its transpose on the valid map, so
+    the backward of either is the other (ES2D training composes from them)."""
+    rng = np.random.default_rng(H * 100 + W)
+    x = rng.standard_normal((2, 3, H, W))
+    st = rng.standard_normal((2, 4, 3, oracle.atrous_group_len(H, W)))
+    lhs = float(np.sum(oracle.atrous_gather(x) * st))
+    rhs = float(np.sum(x * oracle.atrous_scatter(st, H, W)))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+

@@ -178,3 +178,35 @@ def test_conv_grad_without_bias_and_tap_structure():
                        for k in range(4)])
     np.testing.assert_allclose(dw[0], want_w, rtol=1e-12, atol=1e-12)
 
+
+def _pool_dir(rng, batch, dim, H, W, Lp, N):
+    return dict(u=rng.standard_normal((batch, dim, H, W)),
+                delta=rng.standard_normal((batch, dim, Lp)) * 0.5,
+                A=-rng.uniform(0.2, 2.0, size=(dim, N)),
+                B=rng.standard_normal((batch, N, Lp)),
+                C=rng.standard_normal((batch, N, Lp)),
+                D=rng.standard_normal(dim),
+                delta_bias=rng.uniform(-1.0, 0.5, size=dim))
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+@pytest.mark.parametrize("bidir", [False, True])
+def test_pool_grad_matches_finite_differences(axis, bidir):
+    rng = _rng(160 + 2 * axis + bidir)
+    H, W = 3, 4
+    Lp = H if axis == 0 else W
+    f_ = _pool_dir(rng, 1, 2, H, W, Lp, 3)
+    b_ = _pool_dir(rng, 1, 2, H, W, Lp, 3) if bidir else None
+    z = rng.standard_normal(f_["u"].shape)
+    dout = rng.standard_normal(f_["u"].shape)
+    gf, gb, dz, out = og.pool_scan_repeat_grad(f_, b_, dout, z=z, combine_scale=0.5, pool_axis=axis)
+    fn = lambda ff, bb, zz=z: float(np.sum(dout * oracle.pool_scan_repeat(ff, bb, z=zz, combine_scale=0.5,
+                                                                           pool_axis=axis)))
+    np.testing.assert_allclose(out, oracle.pool_scan_repeat(f_, b_, z=z, combine_scale=0.5, pool_axis=axis),
+                               rtol=0, atol=1e-12)
+    for k in ("u", "delta", "A", "B", "C", "D", "delta_bias"):
+        _check(gf[k], _fd(lambda q: fn(q, b_), f_, k), "fwd " + k)
+        if bidir:
+            _check(gb[k], _fd(lambda q: fn(f_, q), b_, k), "bwd " + k)
+    _check(dz, _fd(lambda q: fn(f_, b_, q["z"]), dict(z=z), "z"), "z")
+

@@ -910,6 +910,32 @@ def test_bwd_single_fused_conv(reverse):
     assert_close(host(dz), wdz, FP32_TOL, "dz")
 
 
+@pytest.mark.parametrize("size", [56, 57])
+def test_es2d_backward_by_composition(size):
+    """ES2D gradients from the entry points: gather and scatter are each
+    other's adjoints (pinned on the oracle), so the map gradient is
+    scatter(scan backward(gather(dout))) and pads get none."""
+    _case(f"es2d backward composition {size}")
+    batch, ch, N = 2, 24, 16
+    g = wl.generator(3800 + size, DEV)
+    x = torch.randn((batch, ch, size, size), generator=g, device=DEV)
+    Lg = vm.vm_atrous_group_len(size, size)
+    p, _ = wl.single_inputs(3810 + size, 4 * batch, ch, Lg, device=DEV, gated=False)
+    p["u"] = vm.vm_atrous_gather(x).view(4 * batch, ch, Lg)
+    dout = torch.randn(x.shape, generator=g, device=DEV)
+    dstreams = vm.vm_atrous_gather(dout).view(4 * batch, ch, Lg)
+    gs, _ = vm.vm_selective_scan_bwd(p, dstreams)
+    dx = vm.vm_atrous_scatter(gs["u"].view(batch, 4, ch, Lg), size, size)
+    torch.cuda.synchronize()
+    hp = host_dir(p)
+    hp["u"] = oracle.atrous_gather(host(x)).reshape(4 * batch, ch, Lg)
+    want, _, _ = ograd.selective_scan_grad(hp, oracle.atrous_gather(host(dout)).reshape(4 * batch, ch, Lg))
+    assert_close(host(dx), oracle.atrous_scatter(want["u"].reshape(batch, 4, ch, Lg), size, size),
+                 FP32_TOL, "dx")
+    for k in _GRAD_KEYS[1:]:
+        assert_close(host(gs[k]), want[k], FP32_TOL, f"d{k}")
+
+
 def test_bwd_small_dstate_no_softplus_dense_bc():
     _case("bwd N5 no softplus dense B/C")
     p, z = wl.single_inputs(2700, 3, 33, 50, dstate=5, device=DEV, bc_layout="dense")
