@@ -360,6 +360,25 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
                       int64_t batch, int64_t dim, int64_t seqlen,
                       int64_t dstate, int dtype, int options, void *stream);
 
+/*
+ * Backward pass of vm_pool_scan_repeat ([FVim] "Methodology"), with the same
+ * arguments and dout [batch, dim, H, W] (dtype).  gf (and gb when bwd is
+ * given) receive their direction's gradients: du at full resolution
+ * [batch, dim, H, W] (the mean pool's backward spreads each pooled
+ * gradient times 1/w over its line), the others at the pooled length Lp as
+ * in vm_selective_scan_bwd; dz [batch, dim, H, W] fp32, required exactly
+ * when z is given.  The pooled output's gradient sums the gated dout over
+ * the repeated axis in index order (deterministic).  The same options,
+ * limits and temporary memory as the scan backward (at length Lp), plus
+ * pooled buffers; no fused conv (VM_ERR_UNSUPPORTED).
+ */
+int vm_pool_scan_repeat_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
+                            const void *z, const void *dout, float combine_scale,
+                            const vm_scan_grad *gf, const vm_scan_grad *gb, void *dz,
+                            int64_t batch, int64_t dim, int64_t height, int64_t width,
+                            int64_t dstate, int pool_axis, int dtype, int options,
+                            void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,7 +11,7 @@ Names and argument order follow the C ABI:
   vm_selective_scan_fwd, vm_bidir_scan_fwd, vm_atrous_gather,
   vm_atrous_scatter, vm_pool_scan_repeat, vm_ss2d_scan_fwd,
   vm_causal_conv1d_silu, vm_causal_conv1d_silu_bwd, vm_selective_scan_bwd,
-  vm_bidir_scan_bwd, vm_atrous_group_len.
+  vm_bidir_scan_bwd, vm_pool_scan_repeat_bwd, vm_atrous_group_len.
 """
 from __future__ import annotations
 
@@ -33,7 +33,7 @@ STATUS_NAMES = {0: "VM_OK", 1: "VM_ERR_NULL", 2: "VM_ERR_SHAPE", 3: "VM_ERR_DTYP
 EXPORTED = ("vm_status_string", "vm_version", "vm_selective_scan_fwd", "vm_bidir_scan_fwd",
             "vm_atrous_group_len", "vm_atrous_gather", "vm_atrous_scatter", "vm_pool_scan_repeat",
             "vm_ss2d_scan_fwd", "vm_causal_conv1d_silu", "vm_causal_conv1d_silu_bwd",
-            "vm_selective_scan_bwd", "vm_bidir_scan_bwd")
+            "vm_selective_scan_bwd", "vm_bidir_scan_bwd", "vm_pool_scan_repeat_bwd")
 
 
 class VmScanDir(ctypes.Structure):
@@ -88,10 +88,11 @@ def load_library():
             G = ctypes.POINTER(VmScanGrad)
             lib.vm_selective_scan_bwd.argtypes = [D, P, P, G, P, I64, I64, I64, I64, I, I, I, P]
             lib.vm_bidir_scan_bwd.argtypes = [D, D, P, P, F, G, G, P, I64, I64, I64, I64, I, I, P]
+            lib.vm_pool_scan_repeat_bwd.argtypes = [D, D, P, P, F, G, G, P, I64, I64, I64, I64, I64, I, I, I, P]
             for name in ("vm_selective_scan_fwd", "vm_bidir_scan_fwd", "vm_atrous_gather",
                          "vm_atrous_scatter", "vm_pool_scan_repeat", "vm_ss2d_scan_fwd",
                          "vm_causal_conv1d_silu", "vm_causal_conv1d_silu_bwd", "vm_selective_scan_bwd",
-                         "vm_bidir_scan_bwd"):
+                         "vm_bidir_scan_bwd", "vm_pool_scan_repeat_bwd"):
                 getattr(lib, name).restype = I
             _lib = lib
     return _lib
@@ -413,6 +414,44 @@ def vm_pool_scan_repeat(fwd, bwd=None, z=None, combine_scale=1.0, pool_axis=0, d
     return out
 
 
+def vm_pool_scan_repeat_bwd(fwd, dout, bwd=None, z=None, combine_scale=1.0, pool_axis=0,
+                            delta_softplus=True, zoh=False):
+    """Gradients of sum(dout * vm_pool_scan_repeat(fwd, bwd, z, ...)).
+    Returns (grads of fwd, grads of bwd or None, dz or None), fp32: u's
+    gradient at full resolution, the others at the pooled length."""
+    u = fwd["u"]
+    dt = u.dtype
+    batch, dim, H, W = u.shape
+    Lp = H if pool_axis == 0 else W
+    N = fwd["A"].shape[-1]
+    df, kf = _direction(fwd, batch, dim, (batch, dim, H, W), Lp, N, dt, u.device, "fwd")
+    pb, gsb, gb = None, None, None
+    if bwd is not None:
+        db, kb = _direction(bwd, batch, dim, (batch, dim, H, W), Lp, N, dt, u.device, "bwd")
+        pb = ctypes.byref(db)
+    _dev(dout, "dout", dt, u.shape, u.device)
+    if z is not None:
+        _dev(z, "z", dt, u.shape, u.device)
+
+    def grad_set(p):
+        s_, g_ = _grad_set(p, batch, dim, Lp, N, u.device, p.get("delta_bias") is not None)
+        g_["u"] = torch.empty(u.shape, dtype=torch.float32, device=u.device)   # full resolution
+        s_.du = g_["u"].data_ptr()
+        return s_, g_
+
+    gsf, gf = grad_set(fwd)
+    if bwd is not None:
+        gsb, gb = grad_set(bwd)
+    dz = torch.empty(u.shape, dtype=torch.float32, device=u.device) if z is not None else None
+    with torch.cuda.device(u.device):
+        st = load_library().vm_pool_scan_repeat_bwd(
+            ctypes.byref(df), pb, _ptr(z), _ptr(dout), float(combine_scale), ctypes.byref(gsf),
+            ctypes.byref(gsb) if gsb is not None else None, _ptr(dz), batch, dim, H, W, N,
+            int(pool_axis), _dtype_code(u), _options(delta_softplus, zoh), _stream(u.device))
+    _check(st, "vm_pool_scan_repeat_bwd")
+    return gf, gb, dz
+
+
 def vm_ss2d_scan_fwd(u, dirs, z=None, combine_scale=1.0, delta_softplus=True, out=None, zoh=False):
     """Four-direction 2-D scan with summed merge.  u, z: [batch, dim, H, W].
     dirs: four dicts with delta, A, B, C, D, delta_bias (a "u" key is
@@ -446,6 +485,6 @@ def vm_ss2d_scan_fwd(u, dirs, z=None, combine_scale=1.0, delta_softplus=True, ou
 
 __all__ = ["vm_selective_scan_fwd", "vm_bidir_scan_fwd", "vm_atrous_gather", "vm_atrous_scatter",
            "vm_pool_scan_repeat", "vm_ss2d_scan_fwd", "vm_causal_conv1d_silu",
-           "vm_causal_conv1d_silu_bwd",
+           "vm_causal_conv1d_silu_bwd", "vm_pool_scan_repeat_bwd",
            "vm_selective_scan_bwd", "vm_bidir_scan_bwd", "VmScanGrad", "vm_atrous_group_len", "vm_status_string", "vm_version",
            "VmScanDir", "VmError", "load_library", "LIB_PATH", "EXPORTED"]

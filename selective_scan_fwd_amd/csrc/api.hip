@@ -261,11 +261,13 @@ int run_bwd(const vm_scan_dir *p, const float *dy, const vm_scan_grad *g, BwdScr
 // Checks of a gradient set: required pointers, no overlap with the inputs
 // (ins) or with the other outputs (outs, extended here).
 int check_grad(const vm_scan_grad *g, int64_t tok, int64_t bc, int64_t dim, int64_t dstate,
-               bool conv, const std::vector<Span> &ins, std::vector<Span> &outs) {
+               bool conv, const std::vector<Span> &ins, std::vector<Span> &outs,
+               int64_t tok_u = -1) {
+  if (tok_u < 0) tok_u = tok;       // elements of du (full resolution on the pooled path)
   if (g == nullptr || g->du == nullptr || g->ddelta == nullptr || g->dA == nullptr ||
       g->dB == nullptr || g->dC == nullptr || g->dD == nullptr || (conv && g->dconv_w == nullptr))
     return VM_ERR_NULL;
-  const Span mine[] = {span(g->du, tok * 4), span(g->ddelta, tok * 4), span(g->dA, dim * dstate * 4),
+  const Span mine[] = {span(g->du, tok_u * 4), span(g->ddelta, tok * 4), span(g->dA, dim * dstate * 4),
                        span(g->dB, bc * 4), span(g->dC, bc * 4), span(g->dD, dim * 4),
                        span(g->ddelta_bias, dim * 4),
                        conv ? span(g->dconv_w, dim * 16) : Span(),
@@ -606,6 +608,104 @@ int vm_pool_scan_repeat(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const vo
   if (st != VM_OK) return st;
   return hip_status(vmk::launch_repeat_gate(y, z, out, batch * dim, height, width, pool_axis,
                                             combine_scale, bf16, s));
+}
+
+int vm_pool_scan_repeat_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void *z,
+                            const void *dout, float combine_scale, const vm_scan_grad *gf,
+                            const vm_scan_grad *gb, void *dz, int64_t batch, int64_t dim,
+                            int64_t height, int64_t width, int64_t dstate, int pool_axis, int dtype,
+                            int options, void *stream) {
+  if (!flag_ok(pool_axis)) return VM_ERR_FLAG;
+  const int64_t Lp = pool_axis == 0 ? height : width;
+  int64_t full = 0, pooled = 0, bc = 0;
+  if (!dims_ok({batch, dim, height, width}, &full)) return VM_ERR_SHAPE;
+  int st = check_bwd_common(dtype, options, batch, dim, Lp, dstate, z, dout, dz, &pooled, &bc);
+  if (st != VM_OK) return st;
+  if (!std::isfinite(combine_scale) || batch * dim > kMaxPlanes) return VM_ERR_UNSUPPORTED;
+  const bool bf16 = dtype == VM_BF16;
+  const int es = bf16 ? 2 : 4;
+  st = check_dir(fwd, full, pooled, batch, Lp, dim, dstate, es, Span());
+  if (st == VM_OK && bwd != nullptr) st = check_dir(bwd, full, pooled, batch, Lp, dim, dstate, es, Span());
+  if (st != VM_OK) return st;
+  if (fwd->conv_w != nullptr || (bwd != nullptr && bwd->conv_w != nullptr)) return VM_ERR_UNSUPPORTED;
+  const int ndir = bwd != nullptr ? 2 : 1;
+  const vm_scan_dir *dirs[2] = {fwd, bwd};
+  const vm_scan_grad *grads[2] = {gf, gb};
+  std::vector<Span> ins, outs;
+  for (int k = 0; k < ndir; ++k) {
+    dir_spans(dirs[k], pooled, batch, Lp, dim, dstate, es, ins);
+    ins.push_back(span(dirs[k]->u, full * es));     // u is full resolution here
+  }
+  ins.push_back(span(z, full * es));
+  ins.push_back(span(dout, full * es));
+  for (int k = 0; k < ndir && st == VM_OK; ++k)
+    st = check_grad(grads[k], pooled, bc, dim, dstate, false, ins, outs, full);
+  if (st != VM_OK) return st;
+  for (const Span &o : outs)
+    if (overlaps(span(dz, full * 4), o)) return VM_ERR_ALIAS;
+  for (const Span &i : ins)
+    if (overlaps(span(dz, full * 4), i)) return VM_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Scratch ws(s);
+  // temporary memory first: pooled u per direction, the pooled forward
+  // output and its gradient, the scans' u gradient, the backward scratch
+  float *ubar[2] = {nullptr, nullptr};
+  for (int k = 0; k < ndir; ++k) ubar[k] = ws.get(pooled, &st);
+  float *y = ws.get(pooled, &st);
+  float *dyp = ws.get(pooled, &st);
+  float *dubar = ws.get(pooled, &st);
+  BwdScratch bs;
+  if (st == VM_OK) st = bs.get(ws, batch, dim, Lp, dstate);
+  vmk::ScanArgs a = {};                 // the pooled forward scan (ungated, scale 1)
+  a.out = y;
+  a.batch = batch;
+  a.dim = dim;
+  a.L = Lp;
+  a.dstate = static_cast<int>(dstate);
+  if (st == VM_OK && ndir == 2) st = exchange_for(a, false, ws);
+  if (st != VM_OK) return st;
+  // the directions as the pooled scans see them (fp32)
+  vm_scan_dir w[2];
+  for (int k = 0; k < ndir; ++k) {
+    w[k] = *dirs[k];
+    st = hip_status(vmk::launch_mean_pool(dirs[k]->u, ubar[k], batch * dim, height, width, pool_axis,
+                                          bf16, s));
+    if (st != VM_OK) return st;
+    w[k].u = ubar[k];
+    w[k].delta = as_f32(dirs[k]->delta, pooled, bf16, ws, s, &st);
+    if (bf16) {
+      const int64_t n = bc_extent(batch, dstate, Lp, dirs[k]->bc_stride);
+      w[k].B = as_f32(dirs[k]->B, n, true, ws, s, &st);
+      w[k].C = as_f32(dirs[k]->C, n, true, ws, s, &st);
+    }
+    if (st != VM_OK) return st;
+    a.dir[k] = resolve_dir(&w[k], batch, dstate, Lp, false, ws, s, &st);
+  }
+  if (ndir == 1) a.dir[1] = a.dir[0];
+  if (st != VM_OK) return st;
+  a.softplus = (options & VM_DELTA_SOFTPLUS) != 0;
+  a.zoh = (options & VM_ZOH) != 0;
+  a.scale = 1.0f;
+  if (ndir == 2) {
+    st = launch_bidir(a, false, ws, s);
+  } else {
+    const vmk::ScanPlan plan = vmk::plan_scan(batch, dim, Lp, a.dstate, 1, false);
+    if (!vmk::scan_offsets_fit(plan, a, false)) return VM_ERR_UNSUPPORTED;
+    st = hip_status(vmk::launch_scan(plan, a, false, s));
+  }
+  if (st != VM_OK) return st;
+  // gate and repeat backward: dz, and the pooled output's gradient
+  st = hip_status(vmk::launch_repeat_gate_bwd(y, z, dout, dyp, static_cast<float *>(dz), batch * dim,
+                                              height, width, pool_axis, combine_scale, bf16, s));
+  for (int k = 0; k < ndir && st == VM_OK; ++k) {
+    vm_scan_grad gu = *grads[k];
+    gu.du = dubar;
+    st = run_bwd(&w[k], dyp, &gu, bs, batch, dim, Lp, dstate, options, k, ws, s);
+    if (st == VM_OK)
+      st = hip_status(vmk::launch_pool_bwd(dubar, grads[k]->du, batch * dim, height, width, pool_axis, s));
+  }
+  return st;
 }
 
 int vm_ss2d_scan_fwd(const vm_scan_dir *dirs, const void *u, const void *z, float combine_scale,

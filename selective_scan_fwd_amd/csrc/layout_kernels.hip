@@ -713,6 +713,69 @@ conv1d_silu_bwd_reduce_kernel(const float *__restrict__ partial, float *__restri
   else if (dcb != nullptr) dcb[d] = v;
 }
 
+// Backward of repeat_gate_kernel, one workgroup per grid (row r): with
+// g = scale dout,
+//   dz[i, j] = g y[p] SiLU'(z[i, j]),  SiLU'(z) = sg (1 + z (1 - sg)),
+//   dy[p]    = sum over the repeated axis of g SiLU(z)   (g without z),
+// p = i (axis 0: the sum runs over j) or j (axis 1: over i).  The sums run
+// in index order (deterministic).
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+repeat_gate_bwd_kernel(const float *__restrict__ y, const T *__restrict__ z,
+                       const T *__restrict__ dout, float *__restrict__ dy, float *__restrict__ dz,
+                       int H, int W, int axis, float scale) {
+  const int64_t r = blockIdx.x;
+  const int64_t hw = static_cast<int64_t>(H) * W;
+  const int Lp = axis == 0 ? H : W;
+  const float *yr = y + r * Lp;
+  const T *zr = z != nullptr ? z + r * hw : nullptr;
+  const T *dr = dout + r * hw;
+  float *dzr = dz != nullptr ? dz + r * hw : nullptr;
+  float *dyr = dy + r * Lp;
+  auto term = [&](int i, int j, float yp) __attribute__((always_inline)) {
+    const int64_t e = static_cast<int64_t>(i) * W + j;
+    const float g = scale * to_f32(dr[e]);
+    if (zr == nullptr) return g;
+    const float zv = to_f32(zr[e]);
+    const float sg = hw_rcp(1.0f + hw_exp2(-zv * kLog2e));
+    dzr[e] = g * yp * (sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f));
+    return g * zv * sg;
+  };
+  if (axis == 0) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int i = wave; i < H; i += kThreads / 64) {
+      const float yp = yr[i];
+      float acc = 0.0f;
+      for (int j = lane; j < W; j += 64) acc += term(i, j, yp);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+      if (lane == 0) dyr[i] = acc;
+    }
+  } else {
+    for (int j = threadIdx.x; j < W; j += kThreads) {
+      const float yp = yr[j];
+      float acc = 0.0f;
+      for (int i = 0; i < H; ++i) acc += term(i, j, yp);
+      dyr[j] = acc;
+    }
+  }
+}
+
+// Backward of the mean pool: du[i, j] = dubar[p] inv (p = i for axis 0, j for
+// axis 1), one workgroup per grid.
+__global__ void __launch_bounds__(kThreads)
+pool_bwd_kernel(const float *__restrict__ dubar, float *__restrict__ du, int H, int W, int axis,
+                float inv) {
+  const int64_t r = blockIdx.x;
+  const int Lp = axis == 0 ? H : W;
+  const float *dr = dubar + r * Lp;
+  float *o = du + r * static_cast<int64_t>(H) * W;
+  Walk w;
+  w.init(threadIdx.x, W);
+  for (int e = threadIdx.x; e < H * W; e += kThreads, w.next())
+    o[e] = dr[axis == 0 ? w.a : w.b] * inv;
+}
+
 bool aligned(const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
 }  // namespace
@@ -807,6 +870,30 @@ hipError_t launch_repeat_gate(const float *y, const void *z, void *out, int64_t 
     hipLaunchKernelGGL(repeat_gate_kernel<float>, dim3(static_cast<unsigned>(rows)), dim3(kThreads),
                        0, s, y, static_cast<const float *>(z), static_cast<float *>(out),
                        static_cast<int>(H), static_cast<int>(W), axis, scale, vec);
+  return hipGetLastError();
+}
+
+hipError_t launch_repeat_gate_bwd(const float *y, const void *z, const void *dout, float *dy, float *dz,
+                                  int64_t rows, int64_t H, int64_t W, int axis, float scale, bool bf16,
+                                  hipStream_t s) {
+  if (rows * H * W == 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(repeat_gate_bwd_kernel<bf16_t>, dim3(static_cast<unsigned>(rows)), dim3(kThreads),
+                       0, s, y, static_cast<const bf16_t *>(z), static_cast<const bf16_t *>(dout), dy, dz,
+                       static_cast<int>(H), static_cast<int>(W), axis, scale);
+  else
+    hipLaunchKernelGGL(repeat_gate_bwd_kernel<float>, dim3(static_cast<unsigned>(rows)), dim3(kThreads),
+                       0, s, y, static_cast<const float *>(z), static_cast<const float *>(dout), dy, dz,
+                       static_cast<int>(H), static_cast<int>(W), axis, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_bwd(const float *dubar, float *du, int64_t rows, int64_t H, int64_t W, int axis,
+                           hipStream_t s) {
+  if (rows * H * W == 0) return hipSuccess;
+  const float inv = static_cast<float>(1.0 / static_cast<double>(axis == 0 ? W : H));
+  hipLaunchKernelGGL(pool_bwd_kernel, dim3(static_cast<unsigned>(rows)), dim3(kThreads), 0, s, dubar, du,
+                     static_cast<int>(H), static_cast<int>(W), axis, inv);
   return hipGetLastError();
 }
 

@@ -160,6 +160,13 @@ hipError_t launch_mean_pool(const void *u, float *pooled, int64_t rows, int64_t 
                             int axis, bool bf16, hipStream_t s);
 hipError_t launch_repeat_gate(const float *y, const void *z, void *out, int64_t rows, int64_t H,
                               int64_t W, int axis, float scale, bool bf16, hipStream_t s);
+// Backward of the repeat + gate (dy [rows][Lp] fp32, dz [rows][H][W] fp32 or
+// null without z) and of the mean pool (du [rows][H][W] fp32).
+hipError_t launch_repeat_gate_bwd(const float *y, const void *z, const void *dout, float *dy, float *dz,
+                                  int64_t rows, int64_t H, int64_t W, int axis, float scale, bool bf16,
+                                  hipStream_t s);
+hipError_t launch_pool_bwd(const float *dubar, float *du, int64_t rows, int64_t H, int64_t W, int axis,
+                           hipStream_t s);
 hipError_t launch_to_f32(const void *src, float *dst, int64_t n, hipStream_t s);
 // Causal depthwise conv1d (width 4) + SiLU over [rows][L] (row = b * dim + d).
 hipError_t launch_conv1d_silu(const void *x, const float *w, const float *cb, void *out,

@@ -196,6 +196,29 @@ def test_plane_count_limit(lib):
     assert lib.vm_ss2d_scan_fwd(dirs, FAKE, None, 1.0, FAKE * 3, big, big, 2, 2, 16, 0, 1, None) == 6
 
 
+def test_pool_bwd_argument_checks(lib):
+    f, b = _dir(FAKE), _dir(FAKE * 2)
+    gf = vm.VmScanGrad(*(FAKE * 5 + k * (1 << 32) for k in range(9)))
+    gb = vm.VmScanGrad(*(FAKE * 6 + k * (1 << 32) for k in range(9)))
+
+    def call(fb=None, z=None, dout=FAKE * 3, g2=None, dz=None, axis=0, dtype=0, scale=1.0, N=16):
+        return lib.vm_pool_scan_repeat_bwd(ctypes.byref(f), fb, z, dout, scale, ctypes.byref(gf), g2, dz,
+                                           2, 4, 6, 8, N, axis, dtype, 1, None)
+
+    assert call(dout=None) == 1
+    assert call(z=FAKE * 4) == 1                            # z without dz
+    assert call(fb=ctypes.byref(b)) == 1                    # bwd without its gradients
+    assert call(axis=2) == 4
+    assert call(dtype=4) == 3
+    assert call(N=17) == 6
+    assert call(scale=float("nan")) == 6
+    assert call(z=FAKE * 4, dz=FAKE * 3) == 5               # dz over dout
+    fc = _dir(FAKE)
+    fc.conv_w = FAKE * 7
+    assert lib.vm_pool_scan_repeat_bwd(ctypes.byref(fc), None, None, FAKE * 3, 1.0, ctypes.byref(gf), None,
+                                       None, 2, 4, 6, 8, 16, 0, 0, 1, None) == 6
+
+
 def test_conv_bwd_argument_checks(lib):
     def call(x=FAKE, w=FAKE * 2, b=None, du=FAKE * 3, dx=FAKE * 4, dw=FAKE * 5, db=None,
              batch=2, dim=4, L=9, rev=0, dtype=0):

@@ -313,6 +313,48 @@ def test_pool_bf16(H, W, axis):
     assert_close(host(out), ref, BF16_TOL, "pool bf16")
 
 
+@pytest.mark.parametrize("H,W", [(6, 8), (5, 3)])
+@pytest.mark.parametrize("axis", [0, 1])
+@pytest.mark.parametrize("bidir", [False, True])
+@pytest.mark.parametrize("gated", [False, True])
+def test_pool_scan_repeat_bwd(H, W, axis, bidir, gated):
+    _case(f"pool bwd {H}x{W} axis{axis} bidir{bidir} gated{gated}")
+    fwd, bwd, z = wl.fastvim_inputs(4000 + axis, 2, 40, H, W, axis, device=DEV, perturb=True)
+    dout = torch.randn(z.shape, generator=wl.generator(4010 + axis, DEV), device=DEV)
+    gf, gb, dz = vm.vm_pool_scan_repeat_bwd(fwd, dout, bwd=bwd if bidir else None,
+                                            z=z if gated else None, combine_scale=0.5, pool_axis=axis)
+    torch.cuda.synchronize()
+    wf, wb, wdz, _ = ograd.pool_scan_repeat_grad(host_dir(fwd), host_dir(bwd) if bidir else None,
+                                                 host(dout), z=host(z) if gated else None,
+                                                 combine_scale=0.5, pool_axis=axis)
+    for got, want, tag in ((gf, wf, "fwd"), (gb, wb, "bwd")):
+        if want is None:
+            assert got is None
+            continue
+        for k in _GRAD_KEYS:
+            assert_close(host(got[k]), want[k], FP32_TOL, f"{tag} d{k}")
+    if gated:
+        assert_close(host(dz), wdz, FP32_TOL, "dz")
+    else:
+        assert dz is None
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_pool_scan_repeat_bwd_long_pooled_axis(dtype):
+    """A pooled length past the on-chip exchange (600 > 552), bf16 inputs."""
+    _case(f"pool bwd long pooled axis {dtype}")
+    fwd, bwd, z = wl.fastvim_inputs(4100, 1, 16, 600, 3, 0, device=DEV, dtype=dtype, perturb=True)
+    dout = torch.randn(z.shape, generator=wl.generator(4101, DEV), device=DEV).to(dtype)
+    gf, gb, dz = vm.vm_pool_scan_repeat_bwd(fwd, dout, bwd=bwd, z=z, pool_axis=0)
+    torch.cuda.synchronize()
+    wf, wb, wdz, _ = ograd.pool_scan_repeat_grad(host_dir(fwd), host_dir(bwd), host(dout), z=host(z),
+                                                 pool_axis=0)
+    for got, want, tag in ((gf, wf, "fwd"), (gb, wb, "bwd")):
+        for k in _GRAD_KEYS:
+            assert_close(host(got[k]), want[k], FP32_TOL, f"{tag} d{k}")
+    assert_close(host(dz), wdz, FP32_TOL, "dz")
+
+
 # ---------------------------------------------------------------- full-size workloads
 def test_full_vim_tiny_bidir():
     w = wl.WORKLOADS[1]
