@@ -156,3 +156,32 @@ def pool_scan_repeat_grad(fwd, bwd, dout, z=None, combine_scale=1.0, pool_axis=0
     return _grads(lf), (_grads(lb) if lb is not None else None), \
         (zt.grad.numpy().copy() if zt is not None else None), out.detach().numpy()
 
+
+def ss2d_scan_grad(u, dirs, dout, z=None, combine_scale=1.0, delta_softplus=True, zoh=False):
+    """Gradients of L = sum(dout * out) for the four-direction 2-D scan
+    ("Norm or Direction?" page, section 3, "2D Selective Scan (SS2D)"): the
+    map u [batch, dim, H, W] is traversed row-major (k = 0), reversed (1),
+    column-major (2) and reversed (3); direction k's delta, B, C follow the
+    steps of its base order; the outputs, put back on the map, are summed,
+    scaled and gated with SiLU(z).  dirs: four dicts of delta, A, B, C, D,
+    delta_bias.  Returns (du, grads per direction without u, dz or None,
+    out)."""
+    ut = _t(u)
+    batch, dim, H, W = ut.shape
+    zt = _t(z)
+    keys = _KEYS[1:]
+    leaves = [[_t(d.get(k)) for k in keys] for d in dirs]
+    total = 0.0
+    for k, lv in enumerate(leaves):
+        seq = (ut if k < 2 else ut.transpose(2, 3)).reshape(batch, dim, H * W)
+        y = _direction_y([seq] + lv, delta_softplus, k % 2 == 1, zoh)
+        total = total + (y.reshape(batch, dim, H, W) if k < 2 else
+                         y.reshape(batch, dim, W, H).transpose(2, 3))
+    out = combine_scale * total
+    if zt is not None:
+        out = out * torch.nn.functional.silu(zt)
+    (out * _t(dout, False)).sum().backward()
+    grads = [{k: (None if v is None else v.grad.numpy().copy()) for k, v in zip(keys, lv)} for lv in leaves]
+    return ut.grad.numpy().copy(), grads, (zt.grad.numpy().copy() if zt is not None else None), \
+        out.detach().numpy()
+

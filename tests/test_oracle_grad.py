@@ -210,3 +210,26 @@ def test_pool_grad_matches_finite_differences(axis, bidir):
             _check(gb[k], _fd(lambda q: fn(f_, q), b_, k), "bwd " + k)
     _check(dz, _fd(lambda q: fn(f_, b_, q["z"]), dict(z=z), "z"), "z")
 
+
+@pytest.mark.parametrize("H,W", [(2, 3), (3, 2)])
+def test_ss2d_grad_matches_finite_differences(H, W):
+    rng = _rng(170 + H)
+    L = H * W
+    u = rng.standard_normal((1, 2, H, W))
+    dirs = []
+    for _ in range(4):
+        d = _dir(rng, 1, 2, L, 3)
+        d.pop("u")
+        dirs.append(d)
+    z = rng.standard_normal(u.shape)
+    dout = rng.standard_normal(u.shape)
+    du, gd, dz, out = og.ss2d_scan_grad(u, dirs, dout, z=z, combine_scale=0.5)
+    fn = lambda uu, dd, zz=z: float(np.sum(dout * oracle.ss2d_scan(uu, dd, z=zz, combine_scale=0.5)))
+    np.testing.assert_allclose(out, oracle.ss2d_scan(u, dirs, z=z, combine_scale=0.5), rtol=0, atol=1e-12)
+    _check(du, _fd(lambda q: fn(q["u"], dirs), dict(u=u), "u"), "u")
+    for k in range(4):
+        for key in ("delta", "A", "B", "C", "D", "delta_bias"):
+            f = lambda q, k=k: fn(u, [q if j == k else dirs[j] for j in range(4)])
+            _check(gd[k][key], _fd(f, dirs[k], key), f"dir{k} {key}")
+    _check(dz, _fd(lambda q: fn(u, dirs, q["z"]), dict(z=z), "z"), "z")
+
