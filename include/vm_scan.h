@@ -379,6 +379,23 @@ int vm_pool_scan_repeat_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
                             int64_t dstate, int pool_axis, int dtype, int options,
                             void *stream);
 
+/*
+ * Backward pass of vm_ss2d_scan_fwd ([NoD] section 3, "2D Selective Scan
+ * (SS2D)"), with the same arguments and dout [batch, dim, H, W] (dtype).
+ *   grads: four gradient sets, one per traversal, for its delta, A, B, C, D
+ *   and delta_bias (their du field is ignored); du [batch, dim, H, W] fp32
+ *   receives the map's gradient, summed over the four traversals; dz
+ *   [batch, dim, H, W] fp32, required exactly when z is given.
+ * The same options and limits as the scan backward at length H * W, and
+ * as vm_ss2d_scan_fwd.  Temporary memory: the transposed map, with z the
+ * recomputed row and column sums, the output gradient in both layouts,
+ * four map gradients, the scan backward's scratch.
+ */
+int vm_ss2d_scan_bwd(const vm_scan_dir *dirs, const void *u, const void *z,
+                     const void *dout, float combine_scale, const vm_scan_grad *grads,
+                     float *du, void *dz, int64_t batch, int64_t dim, int64_t height,
+                     int64_t width, int64_t dstate, int dtype, int options, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,7 +11,8 @@ Names and argument order follow the C ABI:
   vm_selective_scan_fwd, vm_bidir_scan_fwd, vm_atrous_gather,
   vm_atrous_scatter, vm_pool_scan_repeat, vm_ss2d_scan_fwd,
   vm_causal_conv1d_silu, vm_causal_conv1d_silu_bwd, vm_selective_scan_bwd,
-  vm_bidir_scan_bwd, vm_pool_scan_repeat_bwd, vm_atrous_group_len.
+  vm_bidir_scan_bwd, vm_pool_scan_repeat_bwd, vm_ss2d_scan_bwd,
+  vm_atrous_group_len.
 """
 from __future__ import annotations
 
@@ -33,7 +34,8 @@ STATUS_NAMES = {0: "VM_OK", 1: "VM_ERR_NULL", 2: "VM_ERR_SHAPE", 3: "VM_ERR_DTYP
 EXPORTED = ("vm_status_string", "vm_version", "vm_selective_scan_fwd", "vm_bidir_scan_fwd",
             "vm_atrous_group_len", "vm_atrous_gather", "vm_atrous_scatter", "vm_pool_scan_repeat",
             "vm_ss2d_scan_fwd", "vm_causal_conv1d_silu", "vm_causal_conv1d_silu_bwd",
-            "vm_selective_scan_bwd", "vm_bidir_scan_bwd", "vm_pool_scan_repeat_bwd")
+            "vm_selective_scan_bwd", "vm_bidir_scan_bwd", "vm_pool_scan_repeat_bwd",
+            "vm_ss2d_scan_bwd")
 
 
 class VmScanDir(ctypes.Structure):
@@ -89,10 +91,11 @@ def load_library():
             lib.vm_selective_scan_bwd.argtypes = [D, P, P, G, P, I64, I64, I64, I64, I, I, I, P]
             lib.vm_bidir_scan_bwd.argtypes = [D, D, P, P, F, G, G, P, I64, I64, I64, I64, I, I, P]
             lib.vm_pool_scan_repeat_bwd.argtypes = [D, D, P, P, F, G, G, P, I64, I64, I64, I64, I64, I, I, I, P]
+            lib.vm_ss2d_scan_bwd.argtypes = [D, P, P, P, F, G, P, P, I64, I64, I64, I64, I64, I, I, P]
             for name in ("vm_selective_scan_fwd", "vm_bidir_scan_fwd", "vm_atrous_gather",
                          "vm_atrous_scatter", "vm_pool_scan_repeat", "vm_ss2d_scan_fwd",
                          "vm_causal_conv1d_silu", "vm_causal_conv1d_silu_bwd", "vm_selective_scan_bwd",
-                         "vm_bidir_scan_bwd", "vm_pool_scan_repeat_bwd"):
+                         "vm_bidir_scan_bwd", "vm_pool_scan_repeat_bwd", "vm_ss2d_scan_bwd"):
                 getattr(lib, name).restype = I
             _lib = lib
     return _lib
@@ -483,8 +486,44 @@ def vm_ss2d_scan_fwd(u, dirs, z=None, combine_scale=1.0, delta_softplus=True, ou
     return out
 
 
+def vm_ss2d_scan_bwd(u, dirs, dout, z=None, combine_scale=1.0, delta_softplus=True, zoh=False):
+    """Gradients of sum(dout * vm_ss2d_scan_fwd(u, dirs, z, combine_scale)).
+    Returns (du [batch, dim, H, W], per-traversal grads (four dicts with the
+    keys of dirs, dB / dC dense [batch, N, H*W]), dz or None), all fp32."""
+    _dev(u, "u")
+    dt = u.dtype
+    batch, dim, H, W = u.shape
+    if len(dirs) != 4:
+        raise ValueError("dirs must hold four traversals")
+    N = dirs[0]["A"].shape[-1]
+    arr = (VmScanDir * 4)()
+    garr = (VmScanGrad * 4)()
+    keep, grads = [], []
+    for k, p in enumerate(dirs):
+        d, kp = _direction(dict(p, u=u), batch, dim, (batch, dim, H, W), H * W, N, dt, u.device,
+                           f"dirs[{k}]")
+        arr[k] = d
+        keep.append(kp)
+        gs, g = _grad_set(dict(p, u=u), batch, dim, H * W, N, u.device, p.get("delta_bias") is not None)
+        del g["u"]                  # the map's gradient is the summed du below
+        gs.du = None
+        garr[k] = gs
+        grads.append(g)
+    _dev(dout, "dout", dt, u.shape, u.device)
+    if z is not None:
+        _dev(z, "z", dt, u.shape, u.device)
+    du = torch.empty(u.shape, dtype=torch.float32, device=u.device)
+    dz = torch.empty(u.shape, dtype=torch.float32, device=u.device) if z is not None else None
+    with torch.cuda.device(u.device):
+        st = load_library().vm_ss2d_scan_bwd(arr, _ptr(u), _ptr(z), _ptr(dout), float(combine_scale), garr,
+                                             _ptr(du), _ptr(dz), batch, dim, H, W, N, _dtype_code(u),
+                                             _options(delta_softplus, zoh), _stream(u.device))
+    _check(st, "vm_ss2d_scan_bwd")
+    return du, grads, dz
+
+
 __all__ = ["vm_selective_scan_fwd", "vm_bidir_scan_fwd", "vm_atrous_gather", "vm_atrous_scatter",
            "vm_pool_scan_repeat", "vm_ss2d_scan_fwd", "vm_causal_conv1d_silu",
-           "vm_causal_conv1d_silu_bwd", "vm_pool_scan_repeat_bwd",
+           "vm_causal_conv1d_silu_bwd", "vm_pool_scan_repeat_bwd", "vm_ss2d_scan_bwd",
            "vm_selective_scan_bwd", "vm_bidir_scan_bwd", "VmScanGrad", "vm_atrous_group_len", "vm_status_string", "vm_version",
            "VmScanDir", "VmError", "load_library", "LIB_PATH", "EXPORTED"]

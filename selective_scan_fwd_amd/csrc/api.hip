@@ -262,9 +262,9 @@ int run_bwd(const vm_scan_dir *p, const float *dy, const vm_scan_grad *g, BwdScr
 // (ins) or with the other outputs (outs, extended here).
 int check_grad(const vm_scan_grad *g, int64_t tok, int64_t bc, int64_t dim, int64_t dstate,
                bool conv, const std::vector<Span> &ins, std::vector<Span> &outs,
-               int64_t tok_u = -1) {
+               int64_t tok_u = -1, bool need_du = true) {
   if (tok_u < 0) tok_u = tok;       // elements of du (full resolution on the pooled path)
-  if (g == nullptr || g->du == nullptr || g->ddelta == nullptr || g->dA == nullptr ||
+  if (g == nullptr || (need_du && g->du == nullptr) || g->ddelta == nullptr || g->dA == nullptr ||
       g->dB == nullptr || g->dC == nullptr || g->dD == nullptr || (conv && g->dconv_w == nullptr))
     return VM_ERR_NULL;
   const Span mine[] = {span(g->du, tok_u * 4), span(g->ddelta, tok * 4), span(g->dA, dim * dstate * 4),
@@ -771,6 +771,118 @@ int vm_ss2d_scan_fwd(const vm_scan_dir *dirs, const void *u, const void *z, floa
   if (st != VM_OK) return st;
   return hip_status(vmk::launch_ss2d_merge(yr, yc, z, out, batch * dim, height, width,
                                            combine_scale, bf16, s));
+}
+
+int vm_ss2d_scan_bwd(const vm_scan_dir *dirs, const void *u, const void *z, const void *dout,
+                     float combine_scale, const vm_scan_grad *grads, float *du, void *dz,
+                     int64_t batch, int64_t dim, int64_t height, int64_t width, int64_t dstate,
+                     int dtype, int options, void *stream) {
+  int64_t tok = 0, bc = 0;
+  if (!dims_ok({batch, dim, height, width}, &tok)) return VM_ERR_SHAPE;
+  const int64_t L = height * width;
+  int st = check_bwd_common(dtype, options, batch, dim, L, dstate, z, dout, dz, &tok, &bc);
+  if (st != VM_OK) return st;
+  if (!std::isfinite(combine_scale) || batch * dim > kMaxPlanes) return VM_ERR_UNSUPPORTED;
+  if (((height + 31) / 32) * ((width + 31) / 32) > 65535) return VM_ERR_UNSUPPORTED;
+  if (dirs == nullptr || u == nullptr || grads == nullptr || du == nullptr) return VM_ERR_NULL;
+  const bool bf16 = dtype == VM_BF16;
+  const int es = bf16 ? 2 : 4;
+  vm_scan_dir d[4];
+  std::vector<Span> ins, outs;
+  for (int k = 0; k < 4 && st == VM_OK; ++k) {
+    d[k] = dirs[k];
+    d[k].u = u;                     // the one map every traversal reads
+    st = check_dir(&d[k], tok, tok, batch, L, dim, dstate, es, Span());
+    if (st == VM_OK && d[k].conv_w != nullptr) st = VM_ERR_UNSUPPORTED;
+    if (st == VM_OK) dir_spans(&d[k], tok, batch, L, dim, dstate, es, ins);
+  }
+  if (st != VM_OK) return st;
+  ins.push_back(span(z, tok * es));
+  ins.push_back(span(dout, tok * es));
+  outs.push_back(span(du, tok * 4));
+  outs.push_back(span(dz, tok * 4));
+  for (const Span &i : ins)
+    if (overlaps(outs[0], i) || overlaps(outs[1], i)) return VM_ERR_ALIAS;
+  if (overlaps(outs[0], outs[1])) return VM_ERR_ALIAS;
+  // each direction's gradients except du (the map's is summed into du)
+  for (int k = 0; k < 4 && st == VM_OK; ++k) {
+    vm_scan_grad gk = grads[k];
+    gk.du = nullptr;
+    st = check_grad(&gk, tok, bc, dim, dstate, false, ins, outs, -1, false);
+  }
+  if (st != VM_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Scratch ws(s);
+  const int64_t planes = batch * dim;
+  // temporary memory first: the transposed map, the recomputed row and
+  // column outputs (with z), the output gradient in both layouts, and the
+  // four directions' map gradients
+  float *ut = ws.get(tok, &st);
+  float *yr = z != nullptr ? ws.get(tok, &st) : nullptr;
+  float *yc = z != nullptr ? ws.get(tok, &st) : nullptr;
+  float *g = ws.get(tok, &st);
+  float *gt = ws.get(tok, &st);
+  float *dus[4];
+  for (int k = 0; k < 4; ++k) dus[k] = ws.get(tok, &st);
+  BwdScratch bs;
+  if (st == VM_OK) st = bs.get(ws, batch, dim, L, dstate);
+  vmk::ScanArgs a[2] = {};
+  for (int pass = 0; pass < 2 && z != nullptr && st == VM_OK; ++pass) {
+    a[pass].out = pass == 0 ? yr : yc;
+    a[pass].batch = batch;
+    a[pass].dim = dim;
+    a[pass].L = L;
+    a[pass].dstate = static_cast<int>(dstate);
+    st = exchange_for(a[pass], false, ws);
+  }
+  if (st != VM_OK) return st;
+  // fp32 views: the map and its transpose; widened delta, B, C with bf16
+  const float *u32 = as_f32(u, tok, bf16, ws, s, &st);
+  vm_scan_dir w[4];
+  for (int k = 0; k < 4 && st == VM_OK; ++k) {
+    w[k] = d[k];
+    w[k].u = k < 2 ? u32 : ut;
+    if (bf16) {
+      const int64_t n = bc_extent(batch, dstate, L, d[k].bc_stride);
+      w[k].delta = as_f32(d[k].delta, tok, true, ws, s, &st);
+      w[k].B = as_f32(d[k].B, n, true, ws, s, &st);
+      w[k].C = as_f32(d[k].C, n, true, ws, s, &st);
+    }
+  }
+  if (st == VM_OK) st = hip_status(vmk::launch_transpose(u32, ut, planes, height, width, false, s));
+  const float *z32 = as_f32(z, tok, bf16 && z != nullptr, ws, s, &st);
+  const float *dout32 = as_f32(dout, tok, bf16, ws, s, &st);
+  if (st != VM_OK) return st;
+  if (z != nullptr) {
+    // the row and column scans' ungated sums, as the forward computes them
+    for (int pass = 0; pass < 2 && st == VM_OK; ++pass) {
+      a[pass].dir[0] = resolve_dir(&w[2 * pass], batch, dstate, L, false, ws, s, &st);
+      a[pass].dir[1] = resolve_dir(&w[2 * pass + 1], batch, dstate, L, false, ws, s, &st);
+      a[pass].softplus = (options & VM_DELTA_SOFTPLUS) != 0;
+      a[pass].zoh = (options & VM_ZOH) != 0;
+      a[pass].scale = 1.0f;
+      if (st == VM_OK) st = launch_bidir(a[pass], false, ws, s);
+    }
+    // y = y_r + transpose(y_c) for dz; the transpose lands in dus[0] (free
+    // until the first backward)
+    if (st == VM_OK) st = hip_status(vmk::launch_transpose(yc, dus[0], planes, width, height, false, s));
+  }
+  if (st == VM_OK)
+    st = hip_status(vmk::launch_gate_bwd(yr, z32, dout32, g, static_cast<float *>(dz), tok, combine_scale,
+                                         s, z != nullptr ? dus[0] : nullptr));
+  if (st == VM_OK) st = hip_status(vmk::launch_transpose(g, gt, planes, height, width, false, s));
+  // the four backward scans: rows on g, columns on its transpose
+  for (int k = 0; k < 4 && st == VM_OK; ++k) {
+    vm_scan_grad gk = grads[k];
+    gk.du = dus[k];
+    st = run_bwd(&w[k], k < 2 ? g : gt, &gk, bs, batch, dim, L, dstate, options, k % 2, ws, s);
+  }
+  // du = du_0 + du_1 + transpose(du_2 + du_3), through g and gt (free now)
+  if (st == VM_OK) st = hip_status(vmk::launch_add(dus[2], dus[3], nullptr, g, tok, s));
+  if (st == VM_OK) st = hip_status(vmk::launch_transpose(g, gt, planes, width, height, false, s));
+  if (st == VM_OK) st = hip_status(vmk::launch_add(dus[0], dus[1], gt, du, tok, s));
+  return st;
 }
 
 int vm_selective_scan_bwd(const vm_scan_dir *p, const void *z, const void *dout,

@@ -473,9 +473,10 @@ reduce_param_kernel(const float *__restrict__ pA, float *dA, const float *__rest
 }
 
 // dy = scale * dout * SiLU(z) and dz = scale * dout * y * SiLU'(z), with
-// SiLU'(z) = s (1 + z (1 - s)), s = sigmoid(z); without z, dy = scale * dout.
+// SiLU'(z) = s (1 + z (1 - s)), s = sigmoid(z), y = y1 (+ y2 when given);
+// without z, dy = scale * dout.
 __global__ void __launch_bounds__(256)
-gate_bwd_kernel(const float *__restrict__ y, const float *__restrict__ z,
+gate_bwd_kernel(const float *__restrict__ y, const float *__restrict__ y2, const float *__restrict__ z,
                 const float *__restrict__ dout, float *__restrict__ dy, float *__restrict__ dz,
                 int64_t n, float scale) {
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
@@ -486,10 +487,20 @@ gate_bwd_kernel(const float *__restrict__ y, const float *__restrict__ z,
     } else {
       const float zv = z[e];
       const float s = hw_rcp(1.0f + hw_exp2(-zv * kLog2e));
+      const float yv = y2 != nullptr ? y[e] + y2[e] : y[e];
       dy[e] = g * zv * s;
-      dz[e] = g * y[e] * (s * __builtin_fmaf(zv, 1.0f - s, 1.0f));
+      dz[e] = g * yv * (s * __builtin_fmaf(zv, 1.0f - s, 1.0f));
     }
   }
+}
+
+// out = a + b (+ c when given), elementwise.
+__global__ void __launch_bounds__(256)
+add_kernel(const float *__restrict__ a, const float *__restrict__ b, const float *__restrict__ c,
+           float *__restrict__ out, int64_t n) {
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
+       e += static_cast<int64_t>(gridDim.x) * 256)
+    out[e] = c != nullptr ? (a[e] + b[e]) + c[e] : a[e] + b[e];
 }
 
 unsigned grid_for(int64_t n) {
@@ -530,10 +541,17 @@ hipError_t launch_scan_bwd_reduce(const BwdArgs &a, float *dA, float *dB, float 
 }
 
 hipError_t launch_gate_bwd(const float *y, const float *z, const float *dout, float *dy, float *dz,
-                           int64_t n, float scale, hipStream_t s) {
+                           int64_t n, float scale, hipStream_t s, const float *y2) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(gate_bwd_kernel, dim3(grid_for(n)), dim3(256), 0, s, y, z, dout, dy, dz, n,
+  hipLaunchKernelGGL(gate_bwd_kernel, dim3(grid_for(n)), dim3(256), 0, s, y, y2, z, dout, dy, dz, n,
                      scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_add(const float *a, const float *b, const float *c, float *out, int64_t n,
+                      hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(add_kernel, dim3(grid_for(n)), dim3(256), 0, s, a, b, c, out, n);
   return hipGetLastError();
 }
 

@@ -148,8 +148,13 @@ int64_t scan_bwd_tiles(int64_t L);
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s);
 hipError_t launch_scan_bwd_reduce(const BwdArgs &a, float *dA, float *dB, float *dC, float *dD,
                                   float *dbias, hipStream_t s);
+// dy = scale dout SiLU(z), dz = scale dout (y + y2) SiLU'(z) (y2 may be null;
+// without z, dy = scale dout).
 hipError_t launch_gate_bwd(const float *y, const float *z, const float *dout, float *dy, float *dz,
-                           int64_t n, float scale, hipStream_t s);
+                           int64_t n, float scale, hipStream_t s, const float *y2 = nullptr);
+// out = a + b (+ c when not null)
+hipError_t launch_add(const float *a, const float *b, const float *c, float *out, int64_t n,
+                      hipStream_t s);
 
 // ---------------------------------------------------------------- layout
 hipError_t launch_atrous_gather(const void *x, void *streams, int64_t batch, int64_t ch,

@@ -329,3 +329,49 @@ def test_bwd_argument_checks(lib):
     assert bidir(scale=float("inf")) == 6
     assert bidir(dtype=5) == 3
     assert bidir(g2=gf) == 5                                # both directions' gradients in one set
+
+
+def test_ss2d_bwd_argument_checks(lib):
+    dirs = (vm.VmScanDir * 4)(*(_dir(FAKE * (k + 4)) for k in range(4)))
+
+    def gsets():
+        return (vm.VmScanGrad * 4)(*(vm.VmScanGrad(*(FAKE * (k + 10) + j * (1 << 32) for j in range(7)))
+                                     for k in range(4)))
+
+    def call(d=dirs, u=FAKE, z=None, dout=FAKE * 3, scale=1.0, g=None, du=FAKE * 20, dz=None, H=6, W=5,
+             N=16, dtype=0, opt=1, conv=False):
+        g = gsets() if g is None else g
+        return lib.vm_ss2d_scan_bwd(d, u, z, dout, scale, g, du, dz, 2, 4, H, W, N, dtype, opt, None)
+
+    assert call(d=None) == 1
+    assert call(u=None) == 1
+    assert call(dout=None) == 1
+    assert call(du=None) == 1
+    assert call(z=FAKE * 21) == 1                           # z without dz
+    assert lib.vm_ss2d_scan_bwd(dirs, FAKE, None, FAKE * 3, 1.0, None, FAKE * 20, None, 2, 4, 6, 5, 16, 0,
+                                1, None) == 1
+    g = gsets()
+    g[2].dC = None
+    assert call(g=g) == 1
+    assert call(H=0) == 2
+    assert call(N=17) == 6
+    assert call(scale=float("inf")) == 6
+    assert call(H=40000, W=40000) == 6
+    assert call(dtype=3) == 3
+    assert call(opt=8) == 4
+    assert call(du=FAKE + 8) == 5                           # du over u
+    assert call(du=dirs[3].B) == 5                          # du over a traversal's B
+    assert call(z=FAKE * 21, dz=FAKE * 3) == 5              # dz over dout
+    assert call(z=FAKE * 21, dz=FAKE * 20 + 4) == 5         # dz over du
+    g = gsets()
+    g[1].ddelta = FAKE * 20                                 # a traversal's gradient over du
+    assert call(g=g) == 5
+    g = gsets()
+    g[3].dB = g[0].dB                                       # two traversals' gradients in one buffer
+    assert call(g=g) == 5
+    g = gsets()
+    g[2].dD = dirs[2].D                                     # a gradient over an input
+    assert call(g=g) == 5
+    bad = (vm.VmScanDir * 4)(*(_dir(FAKE * (k + 4)) for k in range(4)))
+    bad[1].conv_w = FAKE * 30                               # no fused conv on the 2-D scan
+    assert call(d=bad) == 6

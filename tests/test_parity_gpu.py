@@ -1054,6 +1054,80 @@ def test_full_vim_tiny_bidir_bwd():
     assert_close(host(dz), wdz, FP32_TOL, "dz")
 
 
+def _ss2d_bwd_check(u, dirs, dout, z, tag, scale=1.0, softplus=True, zoh=False):
+    du, grads, dz = vm.vm_ss2d_scan_bwd(u, dirs, dout, z=z, combine_scale=scale, delta_softplus=softplus,
+                                        zoh=zoh)
+    torch.cuda.synchronize()
+    wdu, wg, wdz, _ = ograd.ss2d_scan_grad(host(u), [host_dir(p) for p in dirs], host(dout), z=host(z),
+                                           combine_scale=scale, delta_softplus=softplus, zoh=zoh)
+    assert_close(host(du), wdu, FP32_TOL, f"{tag} du")
+    for k in range(4):
+        assert "u" not in grads[k]
+        for key in _GRAD_KEYS[1:]:
+            if wg[k][key] is None:
+                assert grads[k][key] is None
+            else:
+                assert_close(host(grads[k][key]), wg[k][key], FP32_TOL, f"{tag} dir{k} d{key}")
+    if z is None:
+        assert dz is None
+    else:
+        assert_close(host(dz), wdz, FP32_TOL, f"{tag} dz")
+
+
+@pytest.mark.parametrize("H,W,gated,bc_layout", [(5, 7, True, "token"), (8, 8, False, "token"),
+                                                 (6, 9, True, "dense"), (24, 25, True, "token")])
+def test_ss2d_bwd(H, W, gated, bc_layout):
+    """Every gradient of the four-direction 2-D scan, against the oracle's
+    autograd; 24 x 25 = 600 steps is past the on-chip exchange length."""
+    _case(f"ss2d bwd {H}x{W} gated{gated} bc {bc_layout}")
+    u, dirs, z = wl.ss2d_inputs(4200 + H * W, 2, 40, H, W, device=DEV, gated=gated, perturb=True,
+                                bc_layout=bc_layout)
+    dout = torch.randn(u.shape, generator=wl.generator(4201 + H, DEV), device=DEV)
+    _ss2d_bwd_check(u, dirs, dout, z, f"ss2d bwd {H}x{W}", scale=0.5)
+
+
+def test_ss2d_bwd_small_dstate_no_softplus():
+    _case("ss2d bwd N7 no softplus 9x6")
+    u, dirs, z = wl.ss2d_inputs(4300, 2, 33, 9, 6, dstate=7, device=DEV, perturb=True)
+    g = wl.generator(4302, DEV)
+    for k, p in enumerate(dirs):
+        # without softplus the step is delta + bias as given: keep it positive
+        p["delta"] = torch.rand(p["delta"].shape, generator=g, device=DEV) * 0.3
+        p["delta_bias"] = None if k == 2 else torch.rand(p["D"].shape, generator=g, device=DEV) * 0.05
+    dout = torch.randn(u.shape, generator=wl.generator(4301, DEV), device=DEV)
+    _ss2d_bwd_check(u, dirs, dout, z, "ss2d bwd no softplus", softplus=False)
+
+
+def test_ss2d_bwd_bf16_and_zoh():
+    _case("ss2d bwd bf16 7x10, zoh 9x14")
+    u, dirs, z = wl.ss2d_inputs(4400, 2, 40, 7, 10, device=DEV, dtype=torch.bfloat16, perturb=True)
+    dout = torch.randn(u.shape, generator=wl.generator(4401, DEV), device=DEV).to(torch.bfloat16)
+    _ss2d_bwd_check(u, dirs, dout, z, "ss2d bwd bf16")
+    u, dirs, z = wl.ss2d_inputs(4402, 2, 40, 9, 14, device=DEV, perturb=True)
+    dout = torch.randn(u.shape, generator=wl.generator(4403, DEV), device=DEV)
+    _ss2d_bwd_check(u, dirs, dout, z, "ss2d bwd zoh", scale=0.5, zoh=True)
+
+
+def test_full_ss2d_bwd():
+    # the full-size 2-D scan's backward; the map, delta and gate gradients of
+    # sampled (batch row, channel) pairs depend on that pair's inputs only
+    w = wl.WORKLOADS[5]
+    _case(f"full {w.name} backward (sampled)")
+    u, dirs, z = wl.ss2d_inputs(4500, w.batch, w.dim, w.height, w.width, device=DEV, perturb=True)
+    dout = torch.randn(u.shape, generator=wl.generator(4501, DEV), device=DEV)
+    du, grads, dz = vm.vm_ss2d_scan_bwd(u, dirs, dout, z=z, combine_scale=w.combine_scale)
+    torch.cuda.synchronize()
+    bsel, dsel = [0, w.batch - 1], [0, 17, w.dim - 1]
+    hd = [sub_dir(host_dir(p), bsel, dsel) for p in dirs]
+    sel = lambda t: t[bsel][:, dsel]
+    wdu, wg, wdz, _ = ograd.ss2d_scan_grad(sel(host(u)), hd, sel(host(dout)), z=sel(host(z)),
+                                           combine_scale=w.combine_scale)
+    assert_close(sel(host(du)), wdu, FP32_TOL, "full ss2d du (sampled)")
+    assert_close(sel(host(dz)), wdz, FP32_TOL, "full ss2d dz (sampled)")
+    for k in range(4):
+        assert_close(sel(host(grads[k]["delta"])), wg[k]["delta"], FP32_TOL, f"full ss2d dir{k} ddelta")
+
+
 # ---------------------------------------------------------------- degenerate sizes
 def test_degenerate_sizes_every_entry_point():
     # one channel, one batch row, shortest sequences / maps, for each entry
