@@ -181,9 +181,12 @@ scan_bwd_kernel(const BwdArgs p) {
       lb[i] = bload<float>(rB, bo[i] + tb);
       lc[i] = pass2 ? bload<float>(rC, bo[i] + tb) : 0.0f;
     }
+    if (pass2) {
+      bload4(rCk, ck_lane + static_cast<uint32_t>(j) * 64u, lk);
+    } else {
 #pragma unroll
-    for (int jn = 0; jn < kNS; ++jn)
-      lk[jn] = pass2 ? bload<float>(rCk, ck_lane + static_cast<uint32_t>(j) * 64u + 4u * jn) : 0.0f;
+      for (int jn = 0; jn < kNS; ++jn) lk[jn] = 0.0f;
+    }
   };
   // Stages the loaded tile: (dt, dt u, dy) per element ((dt, u, dy) with
   // ZOH) and B, C per step into LDS, and keeps the element values the tile's
@@ -220,9 +223,7 @@ scan_bwd_kernel(const BwdArgs p) {
   if (nt1 > 0) stage_load(tile_of(0), false);
   for (int k = 0; k < nt1; ++k) {
     const int j = tile_of(k);
-#pragma unroll
-    for (int jn = 0; jn < kNS; ++jn)
-      bstore<float>(rCk, ck_lane + static_cast<uint32_t>(j) * 64u + 4u * jn, h[jn]);
+    bstore4(rCk, ck_lane + static_cast<uint32_t>(j) * 64u, h);
     stage_store();
     stage_load(tile_of(k + 1 < nt1 ? k + 1 : nt1 - 1), false);
 #pragma unroll

@@ -57,6 +57,24 @@ template <> __device__ __forceinline__ void bstore<bf16_t>(Rsrc r, uint32_t off,
   __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(from_f32<bf16_t>(v)), r,
                                         static_cast<int>(off), 0, 0);
 }
+// Four consecutive fp32 values at a 16-byte aligned offset, in one access.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void bstore4(Rsrc r, uint32_t off, const float (&v)[4]) {
+  const u32x4_t x = {__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1]),
+                     __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3])};
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, static_cast<int>(off), 0, 0);
+}
+// (The whole vector is reinterpreted: a bit cast of one element of an
+// ext_vector value reads element 0 with this compiler.)
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void bload4(Rsrc r, uint32_t off, float (&v)[4]) {
+  const f32x4_t x =
+      __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
+  v[0] = x.x;
+  v[1] = x.y;
+  v[2] = x.z;
+  v[3] = x.w;
+}
 
 // Zero-order-hold input coefficient ("Norm or Direction?" page, section 3,
 // eq. 2, for diagonal A): k = expm1(x) / A for x = dt A, given x2 = x

@@ -473,9 +473,8 @@ scan_kernel(const ScanArgs p) {
     comb_load(k + 1 < nt ? k + 1 : nt - 1, Qn(), second);
     stage_load(k + NB < nt ? k + NB : nt - 1, slot);
     if constexpr (CK) {
-#pragma unroll
-      for (int j = 0; j < NS; ++j)
-        bstore<float>(rCk, ck_lane + static_cast<uint32_t>(tile_of(k)) * 64u + 4u * j, h[j]);
+      static_assert(NS == 4, "a lane's checkpoint is one 16-byte store");
+      bstore4(rCk, ck_lane + static_cast<uint32_t>(tile_of(k)) * 64u, h);
     }
     do_scan();
     comb_read(k, second);
