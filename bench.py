@@ -61,7 +61,8 @@ def parse():
     ap.add_argument("--config", type=int, default=1,
                     help="0 single, 1 Vim-T bidir (default), 2 bf16 L=4097, 3 ES2D 56x56, "
                          "4 FastVim pooled (axes alternate per step), 5 FastVim unpooled L=16384, "
-                         "6 SS2D four-direction scan 56x56, 7 backward of the Vim-T bidirectional scan")
+                         "6 SS2D four-direction scan 56x56, 7 backward of the Vim-T bidirectional scan, "
+                         "8 backward of the SS2D scan 56x56")
     ap.add_argument("--sets", type=int, default=0, help="input sets to cycle (0 = auto)")
     ap.add_argument("--conv", choices=["none", "fused", "unfused"], default="none",
                     help="configs 0-2: the scan input comes from the block's causal conv1d + SiLU, "
@@ -362,6 +363,53 @@ def build_step(cfg, seed, sets, dev, zoh=False, conv="none"):
             reps, t0 = 0, time.perf_counter()
             while True:
                 og.bidir_scan_grad(hf, hb, hdo, z=hz, combine_scale=w.combine_scale, zoh=zoh)
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= budget or reps >= 20:
+                    break
+            frac = sub / w.batch
+            return el / reps, nbytes * frac, tokens * frac, torch.get_num_threads(), \
+                f"fp64 autograd oracle on {sub} of {w.batch} batch rows, {reps} repetitions"
+
+        return step, info, cpu, nbytes, tokens, slots
+
+    if cfg == 8:
+        w = wl.WORKLOADS[5]
+        H, W = w.height, w.width
+        L = H * W
+        inputs = []
+        for k in range(sets):
+            u, dirs, z = wl.ss2d_inputs(seed + k, w.batch, w.dim, H, W, device=dev)
+            dout = torch.randn(u.shape, generator=wl.generator(seed + 50 + k, dev), device=dev)
+            inputs.append((u, dirs, z, dout))
+
+        def step(i):
+            u, dirs, z, dout = inputs[i % sets]
+            vm.vm_ss2d_scan_bwd(u, dirs, dout, z=z, combine_scale=w.combine_scale, zoh=zoh)
+
+        tok = w.batch * w.dim * L
+        bc = w.batch * L * N * 4
+        # read u, z and dout once, and delta, B, C per traversal; write du and
+        # dz once, and ddelta, dB, dC per traversal
+        nbytes = 3 * tok * 4 + 4 * (tok * 4 + 2 * bc) + 2 * tok * 4 + 4 * (tok * 4 + 2 * bc)
+        tokens = tok
+        # one state recompute (5 slots) and the adjoint (9 slots) per state
+        # step of each traversal
+        slots = 4 * tok * N * 14
+        info = dict(workload=w.name + "-backward", batch=w.batch, dim=w.dim, height=H, width=W, dstate=N,
+                    directions=4, combine_scale=w.combine_scale,
+                    kernels="transposes + 2 bidir recomputes + gate backward + 4 x (backward + reduce) + sum")
+
+        def cpu(budget):
+            from oracle import grad as og
+            u, dirs, z, dout = inputs[0]
+            sub = 1
+            h = lambda t: t[:sub].double().cpu().numpy()
+            hd = [{k: (h(v) if k in ("delta", "B", "C") else v.double().cpu().numpy()) for k, v in p.items()}
+                  for p in dirs]
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                og.ss2d_scan_grad(h(u), hd, h(dout), z=h(z), combine_scale=w.combine_scale, zoh=zoh)
                 reps += 1
                 el = time.perf_counter() - t0
                 if el >= budget or reps >= 20:

@@ -229,14 +229,12 @@ struct BwdScratch {
   }
 };
 
-int run_bwd(const vm_scan_dir *p, const float *dy, const vm_scan_grad *g, BwdScratch &bs,
-            int64_t batch, int64_t dim, int64_t L, int64_t dstate, int options, int reverse,
-            Scratch &ws, hipStream_t s, bool ck_ready = false) {
-  int st = VM_OK;
+vmk::BwdArgs bwd_args(const vm_scan_dir *p, const float *dy, const vm_scan_grad *g, const BwdScratch &bs,
+                      int64_t batch, int64_t dim, int64_t L, int64_t dstate, int options, int reverse,
+                      bool ck_ready, Scratch &ws, hipStream_t s, int *st) {
   vmk::BwdArgs a = {};
   a.ck_ready = ck_ready ? 1 : 0;
-  a.dir = resolve_dir(p, batch, dstate, L, false, ws, s, &st);
-  if (st != VM_OK) return st;
+  a.dir = resolve_dir(p, batch, dstate, L, false, ws, s, st);
   a.dy = dy;
   a.du = g->du;
   a.ddelta = g->ddelta;
@@ -253,9 +251,34 @@ int run_bwd(const vm_scan_dir *p, const float *dy, const vm_scan_grad *g, BwdScr
   a.softplus = (options & VM_DELTA_SOFTPLUS) != 0;
   a.zoh = (options & VM_ZOH) != 0;
   a.reverse = reverse;
-  st = hip_status(vmk::launch_scan_bwd(a, s));
+  return a;
+}
+
+// n (<= 4) directions' backward passes of one shape: one launch of the
+// kernel over all of them (more waves in flight than one direction's), then
+// each direction's reductions.  bs[k] holds direction k's checkpoints and
+// partial sums.
+int run_bwd_group(int n, const vm_scan_dir *const p[], const float *const dy[], const vm_scan_grad *const g[],
+                  const BwdScratch bs[], int64_t batch, int64_t dim, int64_t L, int64_t dstate, int options,
+                  const int reverse[], Scratch &ws, hipStream_t s, bool ck_ready = false) {
+  int st = VM_OK;
+  vmk::BwdGroup grp = {};
+  grp.n = n;
+  for (int k = 0; k < n; ++k)
+    grp.a[k] = bwd_args(p[k], dy[k], g[k], bs[k], batch, dim, L, dstate, options, reverse[k], ck_ready, ws, s,
+                        &st);
   if (st != VM_OK) return st;
-  return hip_status(vmk::launch_scan_bwd_reduce(a, g->dA, g->dB, g->dC, g->dD, g->ddelta_bias, s));
+  st = hip_status(vmk::launch_scan_bwd_group(grp, s));
+  for (int k = 0; k < n && st == VM_OK; ++k)
+    st = hip_status(vmk::launch_scan_bwd_reduce(grp.a[k], g[k]->dA, g[k]->dB, g[k]->dC, g[k]->dD,
+                                                g[k]->ddelta_bias, s));
+  return st;
+}
+
+int run_bwd(const vm_scan_dir *p, const float *dy, const vm_scan_grad *g, const BwdScratch &bs,
+            int64_t batch, int64_t dim, int64_t L, int64_t dstate, int options, int reverse,
+            Scratch &ws, hipStream_t s, bool ck_ready = false) {
+  return run_bwd_group(1, &p, &dy, &g, &bs, batch, dim, L, dstate, options, &reverse, ws, s, ck_ready);
 }
 
 // Checks of a gradient set: required pointers, no overlap with the inputs
@@ -825,8 +848,8 @@ int vm_ss2d_scan_bwd(const vm_scan_dir *dirs, const void *u, const void *z, cons
   float *gt = ws.get(tok, &st);
   float *dus[4];
   for (int k = 0; k < 4; ++k) dus[k] = ws.get(tok, &st);
-  BwdScratch bs;
-  if (st == VM_OK) st = bs.get(ws, batch, dim, L, dstate);
+  BwdScratch bs[4];
+  for (int k = 0; k < 4 && st == VM_OK; ++k) st = bs[k].get(ws, batch, dim, L, dstate);
   vmk::ScanArgs a[2] = {};
   for (int pass = 0; pass < 2 && z != nullptr && st == VM_OK; ++pass) {
     a[pass].out = pass == 0 ? yr : yc;
@@ -872,12 +895,20 @@ int vm_ss2d_scan_bwd(const vm_scan_dir *dirs, const void *u, const void *z, cons
     st = hip_status(vmk::launch_gate_bwd(yr, z32, dout32, g, static_cast<float *>(dz), tok, combine_scale,
                                          s, z != nullptr ? dus[0] : nullptr));
   if (st == VM_OK) st = hip_status(vmk::launch_transpose(g, gt, planes, height, width, false, s));
-  // the four backward scans: rows on g, columns on its transpose
-  for (int k = 0; k < 4 && st == VM_OK; ++k) {
-    vm_scan_grad gk = grads[k];
-    gk.du = dus[k];
-    st = run_bwd(&w[k], k < 2 ? g : gt, &gk, bs, batch, dim, L, dstate, options, k % 2, ws, s);
+  // the four backward scans in one launch: rows on g, columns on its transpose
+  vm_scan_grad gk[4];
+  const vm_scan_dir *pk[4];
+  const vm_scan_grad *gkp[4];
+  const float *dyk[4];
+  const int revk[4] = {0, 1, 0, 1};
+  for (int k = 0; k < 4; ++k) {
+    gk[k] = grads[k];
+    gk[k].du = dus[k];
+    pk[k] = &w[k];
+    gkp[k] = &gk[k];
+    dyk[k] = k < 2 ? g : gt;
   }
+  if (st == VM_OK) st = run_bwd_group(4, pk, dyk, gkp, bs, batch, dim, L, dstate, options, revk, ws, s);
   // du = du_0 + du_1 + transpose(du_2 + du_3), through g and gt (free now)
   if (st == VM_OK) st = hip_status(vmk::launch_add(dus[2], dus[3], nullptr, g, tok, s));
   if (st == VM_OK) st = hip_status(vmk::launch_transpose(g, gt, planes, width, height, false, s));
@@ -995,9 +1026,16 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
                         vmk::kXLds;
   float *dy = ws.get(tok, &st);
   float *y = z != nullptr && !fuse ? ws.get(tok, &st) : nullptr;
-  BwdScratch bs;
-  if (st == VM_OK) st = bs.get(ws, batch, dim, seqlen, dstate);
-  float *ck_b = fuse ? ws.get(batch * dim * vmk::scan_bwd_tiles(seqlen) * 16, &st) : nullptr;
+  // per direction: one backward launch for both; with ZOH (launched one
+  // direction at a time) the second reuses the first's partial sums
+  const bool zoh = (options & VM_ZOH) != 0;
+  BwdScratch bs[2];
+  st = bs[0].get(ws, batch, dim, seqlen, dstate);
+  if (st == VM_OK && !zoh) st = bs[1].get(ws, batch, dim, seqlen, dstate);
+  if (st == VM_OK && zoh) {
+    bs[1] = bs[0];
+    bs[1].ck = ws.get(batch * dim * vmk::scan_bwd_tiles(seqlen) * 16, &st);
+  }
   ConvBwd cvf, cvb;
   if (st == VM_OK && conv) st = cvf.get(ws, tok, batch, dim);
   if (st == VM_OK && conv) st = cvb.get(ws, tok, batch, dim);
@@ -1028,8 +1066,8 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
     a.zoh = (options & VM_ZOH) != 0;
     a.scale = 1.0f;
     if (fuse) {
-      a.ck[0] = bs.ck;
-      a.ck[1] = ck_b;
+      a.ck[0] = bs[0].ck;
+      a.ck[1] = bs[1].ck;
       a.gz = z32;
       a.dout = dout32;
       a.dy = dy;
@@ -1049,9 +1087,16 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
     guf.du = cvf.du;
     gub.du = cvb.du;
   }
-  st = run_bwd(&wf, dy, &guf, bs, batch, dim, seqlen, dstate, options, 0, ws, s, fuse);
-  if (st == VM_OK && fuse) bs.ck = ck_b;
-  if (st == VM_OK) st = run_bwd(&wb, dy, &gub, bs, batch, dim, seqlen, dstate, options, 1, ws, s, fuse);
+  if (zoh) {
+    st = run_bwd(&wf, dy, &guf, bs[0], batch, dim, seqlen, dstate, options, 0, ws, s, fuse);
+    if (st == VM_OK) st = run_bwd(&wb, dy, &gub, bs[1], batch, dim, seqlen, dstate, options, 1, ws, s, fuse);
+  } else {
+    const vm_scan_dir *pk[2] = {&wf, &wb};
+    const float *dyk[2] = {dy, dy};
+    const vm_scan_grad *gk[2] = {&guf, &gub};
+    const int revk[2] = {0, 1};
+    st = run_bwd_group(2, pk, dyk, gk, bs, batch, dim, seqlen, dstate, options, revk, ws, s, fuse);
+  }
   if (st == VM_OK && conv) st = cvf.backward(*fwd, gf, batch, dim, seqlen, 0, s);
   if (st == VM_OK && conv) st = cvb.backward(*bwd, gb, batch, dim, seqlen, 1, s);
   return st;

@@ -66,9 +66,13 @@ struct BwdLayout {
 // per-tile reductions), which sets the register budget at two waves per
 // SIMD; the LDS area (15 KB) is small enough not to lower that.  The ZOH
 // adjoint's extra terms need about 300 registers: one wave per SIMD.
-template <int T, bool ZOH>
+__device__ __forceinline__ const BwdArgs &group_entry(const BwdArgs &a, int) { return a; }
+__device__ __forceinline__ const BwdArgs &group_entry(const BwdGroup &g, int k) { return g.a[k]; }
+
+// Arg: BwdArgs (one direction) or BwdGroup (several in one grid).
+template <int T, bool ZOH, typename Arg>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ZOH ? 1 : 2)))
-scan_bwd_kernel(const BwdArgs p) {
+scan_bwd_kernel(const Arg arg) {
   using Lay = BwdLayout<T>;
   constexpr int PE = kR * T / 64;      // staged elements per lane per tile
   constexpr int BQ = T / 4;            // B (and C) loads per lane per tile
@@ -78,13 +82,21 @@ scan_bwd_kernel(const BwdArgs p) {
   float *const part = smem;                       // [2][64][QSTR], over the staging area
   float *const red = smem + Lay::AREA;            // [16][T][R], padded rows
 
+  // a group's grid covers its directions one after another
+  const int64_t dim = group_entry(arg, 0).dim;
+  const int nrb = static_cast<int>((dim + kR - 1) / kR);
+  int blk = xcd_remap(blockIdx.x, gridDim.x), which = 0;
+  if constexpr (std::is_same<Arg, BwdGroup>::value) {
+    const int nblk = static_cast<int>(arg.a[0].batch) * nrb;
+    which = blk / nblk;
+    blk -= which * nblk;
+  }
+  const BwdArgs &p = group_entry(arg, which);
+
   const int lane = threadIdx.x;
   const int sp = lane / kR, r = lane % kR;
   const bool rev = p.reverse != 0;
-  const int64_t dim = p.dim;
   const int L = static_cast<int>(p.L);
-  const int nrb = static_cast<int>((dim + kR - 1) / kR);
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int b = blk / nrb;
   const int rb = blk - b * nrb;
   const int d0 = rb * kR;
@@ -514,18 +526,42 @@ unsigned grid_for(int64_t n) {
 
 int64_t scan_bwd_tiles(int64_t L) { return (L + kBwdTile - 1) / kBwdTile; }
 
-hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s) {
+hipError_t launch_scan_bwd_group(const BwdGroup &g, hipStream_t s) {
+  if (g.n < 1 || g.n > kBwdGroupMax) return hipErrorInvalidValue;
+  const BwdArgs &a = g.a[0];
+  for (int k = 1; k < g.n; ++k)
+    if (g.a[k].batch != a.batch || g.a[k].dim != a.dim || g.a[k].L != a.L || g.a[k].dstate != a.dstate ||
+        g.a[k].zoh != a.zoh || g.a[k].ck_ready != a.ck_ready)
+      return hipErrorInvalidValue;
   const int64_t nrb = (a.dim + kR - 1) / kR;
   const int64_t blocks = a.batch * nrb;
   if (blocks == 0) return hipSuccess;
   const size_t lds = BwdLayout<kBwdTile>::TOTAL * sizeof(float);
-  if (a.zoh)
-    hipLaunchKernelGGL((scan_bwd_kernel<kBwdTile, true>), dim3(static_cast<unsigned>(blocks)), dim3(64),
-                       lds, s, a);
-  else
-    hipLaunchKernelGGL((scan_bwd_kernel<kBwdTile, false>), dim3(static_cast<unsigned>(blocks)), dim3(64),
-                       lds, s, a);
+  // One direction, or the ZOH variant (one wave per SIMD, whose registers
+  // are tight), takes the single-direction kernel, once per direction.
+  if (g.n == 1 || a.zoh) {
+    for (int k = 0; k < g.n; ++k) {
+      if (a.zoh)
+        hipLaunchKernelGGL((scan_bwd_kernel<kBwdTile, true, BwdArgs>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(64), lds, s, g.a[k]);
+      else
+        hipLaunchKernelGGL((scan_bwd_kernel<kBwdTile, false, BwdArgs>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(64), lds, s, g.a[k]);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  hipLaunchKernelGGL((scan_bwd_kernel<kBwdTile, false, BwdGroup>), dim3(static_cast<unsigned>(blocks * g.n)),
+                     dim3(64), lds, s, g);
   return hipGetLastError();
+}
+
+hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s) {
+  BwdGroup g = {};
+  g.a[0] = a;
+  g.n = 1;
+  return launch_scan_bwd_group(g, s);
 }
 
 hipError_t launch_scan_bwd_reduce(const BwdArgs &a, float *dA, float *dB, float *dC, float *dD,

@@ -146,6 +146,14 @@ struct BwdArgs {
 constexpr int kBwdTile = 8;
 int64_t scan_bwd_tiles(int64_t L);
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s);
+// Up to four directions' backward kernels in one launch (one grid over all
+// of them): the same batch, dim, L and dstate, the same zoh and ck_ready.
+constexpr int kBwdGroupMax = 4;
+struct BwdGroup {
+  BwdArgs a[kBwdGroupMax];
+  int n;
+};
+hipError_t launch_scan_bwd_group(const BwdGroup &g, hipStream_t s);
 hipError_t launch_scan_bwd_reduce(const BwdArgs &a, float *dA, float *dB, float *dC, float *dD,
                                   float *dbias, hipStream_t s);
 // dy = scale dout SiLU(z), dz = scale dout (y + y2) SiLU'(z) (y2 may be null;
