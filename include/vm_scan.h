@@ -350,6 +350,8 @@ int vm_selective_scan_bwd(const vm_scan_dir *p, const void *z,
  * Backward pass of vm_bidir_scan_fwd: gf and gb receive the gradients of the
  * forward and backward directions' inputs, dz (required when z is given) the
  * gate's.  The same limits and temporary memory as vm_selective_scan_bwd,
+ * with checkpoints for each direction and, without VM_ZOH, partials for
+ * each direction (both directions' backward kernels run as one launch),
  * plus, with z and sequences too long for the on-chip exchange, the
  * recomputation's fp32 exchange rows (as vm_bidir_scan_fwd).  All temporary
  * memory is taken before the first launch.
@@ -389,7 +391,8 @@ int vm_pool_scan_repeat_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
  * The same options and limits as the scan backward at length H * W, and
  * as vm_ss2d_scan_fwd.  Temporary memory: the transposed map, with z the
  * recomputed row and column sums, the output gradient in both layouts,
- * four map gradients, the scan backward's scratch.
+ * four map gradients, and the scan backward's checkpoints and partials for
+ * each traversal (the four backward kernels run as one launch).
  */
 int vm_ss2d_scan_bwd(const vm_scan_dir *dirs, const void *u, const void *z,
                      const void *dout, float combine_scale, const vm_scan_grad *grads,
