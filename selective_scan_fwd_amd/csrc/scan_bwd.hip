@@ -537,9 +537,10 @@ hipError_t launch_scan_bwd_group(const BwdGroup &g, hipStream_t s) {
   const int64_t blocks = a.batch * nrb;
   if (blocks == 0) return hipSuccess;
   const size_t lds = BwdLayout<kBwdTile>::TOTAL * sizeof(float);
-  // One direction, or the ZOH variant (one wave per SIMD, whose registers
-  // are tight), takes the single-direction kernel, once per direction.
-  if (g.n == 1 || a.zoh) {
+  // One direction takes the single-direction kernel; so does each direction
+  // of a ZOH group (one wave per SIMD, its registers tight) once one
+  // direction has a wave for every SIMD (256 CUs x 4).
+  if (g.n == 1 || (a.zoh && blocks >= 1024)) {
     for (int k = 0; k < g.n; ++k) {
       if (a.zoh)
         hipLaunchKernelGGL((scan_bwd_kernel<kBwdTile, true, BwdArgs>), dim3(static_cast<unsigned>(blocks)),
@@ -552,8 +553,12 @@ hipError_t launch_scan_bwd_group(const BwdGroup &g, hipStream_t s) {
     }
     return hipSuccess;
   }
-  hipLaunchKernelGGL((scan_bwd_kernel<kBwdTile, false, BwdGroup>), dim3(static_cast<unsigned>(blocks * g.n)),
-                     dim3(64), lds, s, g);
+  if (a.zoh)
+    hipLaunchKernelGGL((scan_bwd_kernel<kBwdTile, true, BwdGroup>), dim3(static_cast<unsigned>(blocks * g.n)),
+                       dim3(64), lds, s, g);
+  else
+    hipLaunchKernelGGL((scan_bwd_kernel<kBwdTile, false, BwdGroup>), dim3(static_cast<unsigned>(blocks * g.n)),
+                       dim3(64), lds, s, g);
   return hipGetLastError();
 }
 
