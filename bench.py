@@ -74,6 +74,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--seed", type=int, default=1001)
+    ap.add_argument("--valu-probe", action="store_true",
+                    help="instead of the benchmark, run the VALU issue-rate probe (libvmprobe.so) and print "
+                         "SIMD cycles per wave-instruction for each form the state step uses")
+    ap.add_argument("--probe-kinds", default="", help="comma-separated probe bodies to run (default: all)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run --steps plain device copies of MIB MiB "
                          "(reference reading for the HBM byte counters)")
@@ -90,6 +94,76 @@ def copy_calibration(mib, steps):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": steps}))
+
+
+PROBE_KINDS = ["fma", "exp", "exp+3fma", "state-step-dpp", "state-step-dpp-no-exp", "permlane32-swap",
+               "exp-latency", "fma-latency", "fma-3vgpr", "mul-2vgpr", "mul-sgpr", "fmac-sgpr", "mul-dpp",
+               "state-step-sgpr", "state-step-sgpr-no-exp", "exp-waves+fma-waves", "state-step-vgpr",
+               "state-step-vgpr-no-exp", "phased-2w-barrier", "phased-2w", "phased-4w-barrier", "phased-4w"]
+SIMDS = 256 * 4
+
+
+def valu_probe(iters=4000, kinds=None):
+    """Issue-rate probe (selective_scan_fwd_amd/csrc/valu_probe.hip).  For
+    each body and W waves per SIMD (256 W workgroups of four waves), the SIMD
+    cycles one wave-instruction takes, chip-wide: launch time x shader clock x
+    1024 SIMDs / wave-instructions issued (the clock is the waves' median
+    s_memtime rate against the 100 MHz real-time counter).  A 16-lane SIMD
+    would take 4 per wave64 instruction.  The latency bodies are one
+    dependent chain at one wave per SIMD: their per-wave figure (elapsed
+    cycles / instructions) is the dependent-issue latency."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "selective_scan_fwd_amd", "libvmprobe.so"))
+    lib.vm_probe_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+    lib.vm_probe_instr.argtypes = [ctypes.c_int]
+    lib.vm_probe_threads.argtypes = [ctypes.c_int]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    inp = (torch.rand(64, device=dev) * 0.5 + 0.25).contiguous()
+    rows = []
+    for kind, name in enumerate(PROBE_KINDS):
+        if kinds is not None and kind not in kinds:
+            continue
+        threads = lib.vm_probe_threads(kind)
+        if "phased" in name:
+            ws = (threads // 256,)          # one workgroup per CU
+        else:
+            ws = (1,) if "latency" in name else (1, 2, 4, 8)
+        for w in ws:
+            blocks = 256 * w * 256 // threads
+            waves = blocks * threads // 64
+            out = torch.empty(blocks * threads, device=dev)
+            clk = torch.zeros(waves * 4, dtype=torch.int64, device=dev)
+            it = iters // 4 if "latency" in name else iters
+            for rep in range(2):                       # the first launch warms up
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                rc = lib.vm_probe_run(kind, blocks, it, inp.data_ptr(), out.data_ptr(), clk.data_ptr(),
+                                      ctypes.c_void_p(stream.cuda_stream))
+                e1.record(stream)
+                if rc != 0:
+                    raise RuntimeError(f"probe {name}: error {rc}")
+                torch.cuda.synchronize()
+            c = clk.cpu().numpy().reshape(-1, 4).astype(np.float64)
+            cyc = c[:, 1] - c[:, 0]
+            rt = (c[:, 3] - c[:, 2]) / 100e6                # 100 MHz real-time counter
+            ninstr = lib.vm_probe_instr(kind)
+            ghz = float(np.median(cyc / rt)) / 1e9
+            ms = e0.elapsed_time(e1)
+            per_chip = ms * 1e-3 * ghz * 1e9 * SIMDS / (waves * it * ninstr)
+            per_wave = np.median(cyc) / (it * ninstr)
+            rows.append({"body": name, "waves_per_simd": w, "instr_per_iter": ninstr, "iters": it,
+                         "simd_cycles_per_wave_instr": round(float(per_chip), 3),
+                         "wave_cycles_per_instr": round(float(per_wave), 3),
+                         "wave_cycles_median": float(np.median(cyc)), "wave_cycles_max": float(cyc.max()),
+                         "shader_clock_ghz": round(ghz, 3), "launch_ms": round(ms, 4)})
+            print(json.dumps(rows[-1]), flush=True)
+    return rows
 
 
 # ---------------------------------------------------------------- workloads
@@ -453,6 +527,9 @@ def main():
 
     if args.copy_calib:
         copy_calibration(args.copy_calib, args.steps)
+        return
+    if args.valu_probe:
+        valu_probe(kinds=[int(k) for k in args.probe_kinds.split(",")] if args.probe_kinds else None)
         return
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

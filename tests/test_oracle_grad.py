@@ -1,11 +1,29 @@
 """Pins for the gradient oracle (no GPU): its forward equals the C oracle's,
 and every gradient it returns equals a central finite difference of the C
 oracle's forward (an independent implementation)."""
+import importlib.util
+import os
+
 import numpy as np
 import pytest
 
 import oracle
-from oracle import grad as og
+
+
+def _grad_oracle():
+    """The gradient oracle; VM_GRAD_ORACLE names a deliberately broken copy
+    of it (tests/test_oracle_grad_mutants.py), never set in normal runs."""
+    path = os.environ.get("VM_GRAD_ORACLE")
+    if not path:
+        from oracle import grad
+        return grad
+    spec = importlib.util.spec_from_file_location("grad_mutant", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+og = _grad_oracle()
 
 
 def _rng(seed):
@@ -233,3 +251,69 @@ def test_ss2d_grad_matches_finite_differences(H, W):
             _check(gd[k][key], _fd(f, dirs[k], key), f"dir{k} {key}")
     _check(dz, _fd(lambda q: fn(u, dirs, q["z"]), dict(z=z), "z"), "z")
 
+
+
+def _zoh_A(A):
+    """One A column at 0 (coefficient dt; the series' A-derivative dt^2 / 2)
+    and one entry small enough to take the oracle's series branch."""
+    A = A.copy()
+    A[:, 0] = 0.0
+    A[0, 1] = -1e-4
+    return A
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+@pytest.mark.parametrize("bidir", [False, True])
+def test_zoh_pool_grad_matches_finite_differences(axis, bidir):
+    """The pooled path with the zero-order-hold write ("Norm or Direction?"
+    page, section 3, eq. 2; FastVim summary, "Methodology": A and B
+    discretised by zero-order hold), on both pooling axes, with and without
+    the backward direction."""
+    rng = _rng(180 + 2 * axis + bidir)
+    H, W = 3, 4
+    Lp = H if axis == 0 else W
+    f_ = _pool_dir(rng, 1, 2, H, W, Lp, 3)
+    f_["A"] = _zoh_A(f_["A"])
+    b_ = _pool_dir(rng, 1, 2, H, W, Lp, 3) if bidir else None
+    if bidir:
+        b_["A"] = _zoh_A(b_["A"])
+    z = rng.standard_normal(f_["u"].shape)
+    dout = rng.standard_normal(f_["u"].shape)
+    gf, gb, dz, out = og.pool_scan_repeat_grad(f_, b_, dout, z=z, combine_scale=0.5, pool_axis=axis,
+                                               zoh=True)
+    fn = lambda ff, bb, zz=z: float(np.sum(dout * oracle.pool_scan_repeat(
+        ff, bb, z=zz, combine_scale=0.5, pool_axis=axis, zoh=True)))
+    np.testing.assert_allclose(out, oracle.pool_scan_repeat(f_, b_, z=z, combine_scale=0.5, pool_axis=axis,
+                                                            zoh=True), rtol=0, atol=1e-12)
+    for k in ("u", "delta", "A", "B", "C", "D", "delta_bias"):
+        _check(gf[k], _fd(lambda q: fn(q, b_), f_, k), "fwd " + k)
+        if bidir:
+            _check(gb[k], _fd(lambda q: fn(f_, q), b_, k), "bwd " + k)
+    _check(dz, _fd(lambda q: fn(f_, b_, q["z"]), dict(z=z), "z"), "z")
+
+
+def test_zoh_ss2d_grad_matches_finite_differences():
+    """SS2D with the zero-order-hold write ("Norm or Direction?" page, section
+    3, eq. 2 and "2D Selective Scan (SS2D)"): every traversal's gradients."""
+    rng = _rng(190)
+    H, W = 2, 3
+    L = H * W
+    u = rng.standard_normal((1, 2, H, W))
+    dirs = []
+    for _ in range(4):
+        d = _dir(rng, 1, 2, L, 3)
+        d.pop("u")
+        d["A"] = _zoh_A(d["A"])
+        dirs.append(d)
+    z = rng.standard_normal(u.shape)
+    dout = rng.standard_normal(u.shape)
+    du, gd, dz, out = og.ss2d_scan_grad(u, dirs, dout, z=z, combine_scale=0.5, zoh=True)
+    fn = lambda uu, dd, zz=z: float(np.sum(dout * oracle.ss2d_scan(uu, dd, z=zz, combine_scale=0.5, zoh=True)))
+    np.testing.assert_allclose(out, oracle.ss2d_scan(u, dirs, z=z, combine_scale=0.5, zoh=True),
+                               rtol=0, atol=1e-12)
+    _check(du, _fd(lambda q: fn(q["u"], dirs), dict(u=u), "u"), "u")
+    for k in range(4):
+        for key in ("delta", "A", "B", "C", "D", "delta_bias"):
+            f = lambda q, k=k: fn(u, [q if j == k else dirs[j] for j in range(4)])
+            _check(gd[k][key], _fd(f, dirs[k], key), f"dir{k} {key}")
+    _check(dz, _fd(lambda q: fn(u, dirs, q["z"]), dict(z=z), "z"), "z")

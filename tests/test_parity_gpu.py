@@ -303,6 +303,41 @@ def test_pool_repeat_indexing_bit_exact(axis):
     assert np.array_equal(host(out), ref)
 
 
+@pytest.mark.parametrize("H,W", [(12, 10), (6, 5), (3, 6), (8, 16)])
+@pytest.mark.parametrize("axis", [0, 1])
+def test_pool_repeat_indexing_bit_exact_any_extent(H, W, axis):
+    """Pool and repeat indexing on every path (W = 10, 5, 6: one value per
+    access; W = 16: four-wide), with pooled extents that are not powers of
+    two.  Each pooled line is an integer c in [-8, 8] plus integer offsets
+    that sum to zero, so its sum is exactly w c on both sides and the mean is
+    exactly c: the device's sum x fl(1/w) rounds to c because w fl(1/w) is
+    within 2^-25 of 1 for these w (checked below in fp32), and the oracle
+    divides exactly.  With B = 0 and D = 1 the scan returns the mean, so an
+    element summed into the wrong line, or repeated along the wrong axis,
+    changes a value."""
+    _case(f"pool bit-exact {H}x{W} axis{axis}")
+    w = W if axis == 0 else H
+    assert abs(w * float(np.float32(1.0 / w)) - 1.0) <= 2.0 ** -25
+    gen = np.random.default_rng(650 + 10 * H + W + axis)
+    fwd, bwd, _ = wl.fastvim_inputs(650 + axis, 2, 3, H, W, axis, device=DEV)
+    for p in (fwd, bwd):
+        batch, dim = p["u"].shape[:2]
+        lines = H if axis == 0 else W
+        c = gen.integers(-8, 9, size=(batch, dim, lines, 1))
+        off = gen.integers(-4, 5, size=(batch, dim, lines, w))
+        off[..., -1] -= off.sum(axis=-1)
+        vals = (c + off).astype(np.float32)          # [batch, dim, line, position in line]
+        if axis == 1:
+            vals = vals.transpose(0, 1, 3, 2)          # lines are columns
+        p["u"] = torch.from_numpy(np.ascontiguousarray(vals)).to(DEV)
+        p["B"] = torch.zeros_like(p["B"])
+        p["D"] = torch.ones_like(p["D"])
+    out = vm.vm_pool_scan_repeat(fwd, bwd, z=None, combine_scale=0.5, pool_axis=axis)
+    torch.cuda.synchronize()
+    ref = oracle.pool_scan_repeat(host_dir(fwd), host_dir(bwd), z=None, combine_scale=0.5, pool_axis=axis)
+    assert bits_equal(out, ref)
+
+
 @pytest.mark.parametrize("H,W,axis", [(16, 12, 1), (20, 16, 0), (20, 16, 1)])
 def test_pool_bf16(H, W, axis):
     _case(f"pool bf16 {H}x{W} axis{axis}")
@@ -317,16 +352,19 @@ def test_pool_bf16(H, W, axis):
 @pytest.mark.parametrize("axis", [0, 1])
 @pytest.mark.parametrize("bidir", [False, True])
 @pytest.mark.parametrize("gated", [False, True])
-def test_pool_scan_repeat_bwd(H, W, axis, bidir, gated):
-    _case(f"pool bwd {H}x{W} axis{axis} bidir{bidir} gated{gated}")
+@pytest.mark.parametrize("zoh", [False, True])
+def test_pool_scan_repeat_bwd(H, W, axis, bidir, gated, zoh):
+    # zoh: the pooled scans discretised by zero-order hold (FastVim summary,
+    # "Methodology"; "Norm or Direction?" page, section 3, eq. 2)
+    _case(f"pool bwd {H}x{W} axis{axis} bidir{bidir} gated{gated} zoh{zoh}")
     fwd, bwd, z = wl.fastvim_inputs(4000 + axis, 2, 40, H, W, axis, device=DEV, perturb=True)
     dout = torch.randn(z.shape, generator=wl.generator(4010 + axis, DEV), device=DEV)
     gf, gb, dz = vm.vm_pool_scan_repeat_bwd(fwd, dout, bwd=bwd if bidir else None,
-                                            z=z if gated else None, combine_scale=0.5, pool_axis=axis)
+                                            z=z if gated else None, combine_scale=0.5, pool_axis=axis, zoh=zoh)
     torch.cuda.synchronize()
     wf, wb, wdz, _ = ograd.pool_scan_repeat_grad(host_dir(fwd), host_dir(bwd) if bidir else None,
                                                  host(dout), z=host(z) if gated else None,
-                                                 combine_scale=0.5, pool_axis=axis)
+                                                 combine_scale=0.5, pool_axis=axis, zoh=zoh)
     for got, want, tag in ((gf, wf, "fwd"), (gb, wb, "bwd")):
         if want is None:
             assert got is None
@@ -667,21 +705,24 @@ def test_fused_conv_single(L, reverse, zoh):
 # the first global one
 @pytest.mark.parametrize("L", [197, 520, 521, 600])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_fused_conv_bidir(L, dtype):
+@pytest.mark.parametrize("zoh", [False, True])
+def test_fused_conv_bidir(L, dtype, zoh):
     # both directions read the same content x through their own convolutions:
-    # the backward one runs on the reversed sequence
-    _case(f"fused conv bidir L{L} {dtype}")
+    # the backward one runs on the reversed sequence; with zoh the write is
+    # the zero-order-hold coefficient ("Norm or Direction?" page, section 3,
+    # eq. 2) on both sides of the on-chip / global exchange boundary
+    _case(f"fused conv bidir L{L} {dtype} zoh{zoh}")
     fwd, bwd, z = wl.bidir_inputs(1900 + L, 2, 70, L, device=DEV, dtype=dtype, perturb=True)
     bwd["u"] = fwd["u"]
     g = wl.generator(2000 + L, DEV)
     for p in (fwd, bwd):
         p["conv_w"], p["conv_b"] = wl.conv_params(g, 70, DEV)
-    out = vm.vm_bidir_scan_fwd(fwd, bwd, z=z, combine_scale=0.5)
+    out = vm.vm_bidir_scan_fwd(fwd, bwd, z=z, combine_scale=0.5, zoh=zoh)
     torch.cuda.synchronize()
     hf, hb = host_dir(fwd), host_dir(bwd)
     for h, rev in ((hf, False), (hb, True)):
         h["u"] = oracle.causal_conv1d_silu(h["u"], h.pop("conv_w"), h.pop("conv_b"), reverse=rev)
-    ref = oracle.bidir_scan(hf, hb, z=host(z), combine_scale=0.5)
+    ref = oracle.bidir_scan(hf, hb, z=host(z), combine_scale=0.5, zoh=zoh)
     assert_close(host(out), ref, FP32_TOL if dtype == torch.float32 else BF16_TOL, "fused conv bidir")
 
 
@@ -903,23 +944,25 @@ def _conv_scan_inputs(p):
 
 @pytest.mark.parametrize("L", [77, 600])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_bwd_bidir_fused_conv(L, dtype):
+@pytest.mark.parametrize("zoh", [False, True])
+def test_bwd_bidir_fused_conv(L, dtype, zoh):
     """Backward of the bidirectional scan with the fused conv (both
-    directions reading the same x through their own convolutions)."""
-    _case(f"bwd bidir fused conv L{L} {dtype}")
+    directions reading the same x through their own convolutions), with
+    either write."""
+    _case(f"bwd bidir fused conv L{L} {dtype} zoh{zoh}")
     fwd, bwd, z = wl.bidir_inputs(3500 + L, 2, 40, L, device=DEV, dtype=dtype, perturb=True)
     bwd["u"] = fwd["u"]
     g = wl.generator(3600 + L, DEV)
     for q in (fwd, bwd):
         q["conv_w"], q["conv_b"] = wl.conv_params(g, 40, DEV)
     dout = torch.randn(z.shape, generator=g, device=DEV).to(dtype)
-    gf, gb, dz = vm.vm_bidir_scan_bwd(fwd, bwd, dout, z=z, combine_scale=0.5)
+    gf, gb, dz = vm.vm_bidir_scan_bwd(fwd, bwd, dout, z=z, combine_scale=0.5, zoh=zoh)
     torch.cuda.synchronize()
     hf, xf, wf_, bf_ = _conv_scan_inputs(fwd)
     hb, xb, wb_, bb_ = _conv_scan_inputs(bwd)
     hf["u"] = oracle.causal_conv1d_silu(xf, wf_, bf_)
     hb["u"] = oracle.causal_conv1d_silu(xb, wb_, bb_, reverse=True)
-    wantf, wantb, wdz, _ = ograd.bidir_scan_grad(hf, hb, host(dout), z=host(z), combine_scale=0.5)
+    wantf, wantb, wdz, _ = ograd.bidir_scan_grad(hf, hb, host(dout), z=host(z), combine_scale=0.5, zoh=zoh)
     for got, want, x, w, b, rev, tag in ((gf, wantf, xf, wf_, bf_, False, "fwd"),
                                          (gb, wantb, xb, wb_, bb_, True, "bwd")):
         dx, dw, db, _ = ograd.causal_conv1d_silu_grad(x, w, b, want["u"], reverse=rev)
@@ -932,18 +975,19 @@ def test_bwd_bidir_fused_conv(L, dtype):
 
 
 @pytest.mark.parametrize("reverse", [False, True])
-def test_bwd_single_fused_conv(reverse):
-    _case(f"bwd single fused conv rev{reverse}")
+@pytest.mark.parametrize("zoh", [False, True])
+def test_bwd_single_fused_conv(reverse, zoh):
+    _case(f"bwd single fused conv rev{reverse} zoh{zoh}")
     p, z = wl.single_inputs(3700 + reverse, 2, 40, 50, device=DEV, gated=True, perturb=True)
     g = wl.generator(3710 + reverse, DEV)
     p["conv_w"], _ = wl.conv_params(g, 40, DEV)          # no conv bias
     dout = torch.randn(p["u"].shape, generator=g, device=DEV)
-    got, dz = vm.vm_selective_scan_bwd(p, dout, z=z, reverse=reverse)
+    got, dz = vm.vm_selective_scan_bwd(p, dout, z=z, reverse=reverse, zoh=zoh)
     torch.cuda.synchronize()
     assert got["conv_b"] is None
     h, x, w, _ = _conv_scan_inputs(p)
     h["u"] = oracle.causal_conv1d_silu(x, w, None, reverse=reverse)
-    want, wdz, _ = ograd.selective_scan_grad(h, host(dout), z=host(z), reverse=reverse)
+    want, wdz, _ = ograd.selective_scan_grad(h, host(dout), z=host(z), reverse=reverse, zoh=zoh)
     dx, dw, _, _ = ograd.causal_conv1d_silu_grad(x, w, None, want["u"], reverse=reverse)
     assert_close(host(got["u"]), dx, FP32_TOL, "dx")
     assert_close(host(got["conv_w"]), dw, FP32_TOL, "dconv_w")
@@ -1106,6 +1150,16 @@ def test_ss2d_bwd_bf16_and_zoh():
     u, dirs, z = wl.ss2d_inputs(4402, 2, 40, 9, 14, device=DEV, perturb=True)
     dout = torch.randn(u.shape, generator=wl.generator(4403, DEV), device=DEV)
     _ss2d_bwd_check(u, dirs, dout, z, "ss2d bwd zoh", scale=0.5, zoh=True)
+
+
+def test_ss2d_bwd_zoh_per_direction_launches():
+    """SS2D backward with the zero-order-hold write where each traversal has
+    at least 1024 row blocks (batch 64 x 16 blocks of 16 channels), so its
+    four backward kernels launch one traversal at a time."""
+    _case("ss2d bwd zoh b64 d256 3x4")
+    u, dirs, z = wl.ss2d_inputs(4450, 64, 256, 3, 4, device=DEV, perturb=True)
+    dout = torch.randn(u.shape, generator=wl.generator(4451, DEV), device=DEV)
+    _ss2d_bwd_check(u, dirs, dout, z, "ss2d bwd zoh per-direction", scale=0.5, zoh=True)
 
 
 def test_full_ss2d_bwd():
