@@ -30,13 +30,16 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
-# VALU issue ceiling with packed fp32 forms disabled: 256 CUs x 4 SIMDs x 16
-# lanes x 2.4 GHz = 39.3 T lane-slots/s.  v_exp_f32 measured at half the FMA
-# issue rate on gfx950, i.e. 2 slots.
-VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
-SLOTS_PER_STATE_STEP = 6         # dt*A, exp (2 slots), dt*u*B, state fma, readout fma
-# (with --zoh the same count is used: the ALU fraction is then relative to the
-# released recurrence's work, not to the longer zero-order-hold coefficient)
+# ALU ceiling of the state step, from the VALU issue-rate probe
+# (csrc/valu_probe.hip, `bench.py --valu-probe`, summary in profiles/): one
+# state update is dt*A, v_exp_f32, dt*u*B, the state fma and the readout fma.
+# v_exp_f32 occupies a SIMD for 8 cycles per wave64 instruction and the other
+# forms pair across waves at about 2.1 cycles only while no exponential is in
+# flight; the best body measured (exponentials and the other operations in
+# barrier-separated phases, 4 waves per SIMD) takes 20.1 SIMD cycles per wave
+# of 64 state updates.  Ceiling: 1024 SIMDs x 64 lanes x 2.4 GHz / 20.1.
+CYCLES_PER_WAVE_STATE_UPDATE = 20.1
+UPDATES_PEAK_T = 256 * 4 * 64 * 2.4e9 / CYCLES_PER_WAVE_STATE_UPDATE / 1e12
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["selective_scan_fwd_amd/csrc/scan_kernel.hip",
                   "selective_scan_fwd_amd/csrc/scan_bwd.hip",
@@ -64,6 +67,8 @@ def parse():
                          "6 SS2D four-direction scan 56x56, 7 backward of the Vim-T bidirectional scan, "
                          "8 backward of the SS2D scan 56x56")
     ap.add_argument("--sets", type=int, default=0, help="input sets to cycle (0 = auto)")
+    ap.add_argument("--replays", type=int, default=5,
+                    help="times the K timed steps are run (graph replays, or eager passes); the median is reported")
     ap.add_argument("--conv", choices=["none", "fused", "unfused"], default="none",
                     help="configs 0-2: the scan input comes from the block's causal conv1d + SiLU, "
                          "computed inside the scan (fused) or by vm_causal_conv1d_silu first (unfused)")
@@ -223,7 +228,7 @@ def build_step(cfg, seed, sets, dev, zoh=False, conv="none"):
 
         nbytes = algorithmic_bytes_scan(w.batch, w.dim, w.seqlen, N, es, dirs, True)
         tokens = w.batch * w.dim * w.seqlen
-        slots = dirs * tokens * N * SLOTS_PER_STATE_STEP
+        slots = dirs * tokens * N
         info = dict(workload=w.name, batch=w.batch, dim=w.dim, seqlen=w.seqlen, dstate=N,
                     directions=dirs, combine_scale=w.combine_scale, dtype=w.dtype,
                     bc_layout="token-major",
@@ -293,7 +298,7 @@ def build_step(cfg, seed, sets, dev, zoh=False, conv="none"):
         scan_b = algorithmic_bytes_scan(4 * w.batch, w.dim, Lg, N, 4, 1, False)
         nbytes = scan_b - 2 * streams_b + 2 * plane
         tokens = w.batch * w.dim * H * W
-        slots = 4 * w.batch * w.dim * Lg * N * SLOTS_PER_STATE_STEP
+        slots = 4 * w.batch * w.dim * Lg * N
         info = dict(workload=f"{w.name}@{H}x{W}", batch=w.batch, dim=w.dim, height=H, width=W,
                     group_len=Lg, dstate=N, kernels="gather+scan+scatter", graphable=True)
 
@@ -340,7 +345,7 @@ def build_step(cfg, seed, sets, dev, zoh=False, conv="none"):
             Lp = H
             nbytes = (2 * tok_full + tok_full + tok_full) * 4 + \
                 2 * (w.batch * w.dim * Lp * 4 + 2 * w.batch * Lp * N * 4 + w.dim * (N + 2) * 4)
-            slots = 2 * w.batch * w.dim * Lp * N * SLOTS_PER_STATE_STEP
+            slots = 2 * w.batch * w.dim * Lp * N
             info = dict(workload=f"{w.name}-pooled", batch=w.batch, dim=w.dim, height=H, width=W,
                         pooled_len=Lp, dstate=N, pool_axis="alternating 0/1",
                         kernels="pool x2 + bidir scan + repeat-gate")
@@ -355,7 +360,7 @@ def build_step(cfg, seed, sets, dev, zoh=False, conv="none"):
                 vm.vm_bidir_scan_fwd(f, b, z=zf, combine_scale=w.combine_scale, out=out, zoh=zoh)
 
             nbytes = algorithmic_bytes_scan(w.batch, w.dim, L, N, 4, 2, True)
-            slots = 2 * w.batch * w.dim * L * N * SLOTS_PER_STATE_STEP
+            slots = 2 * w.batch * w.dim * L * N
             info = dict(workload=f"{w.name}-unpooled", batch=w.batch, dim=w.dim, seqlen=L, dstate=N)
         tokens = w.batch * w.dim * L
         return step, info, None, nbytes, tokens, slots
@@ -375,7 +380,7 @@ def build_step(cfg, seed, sets, dev, zoh=False, conv="none"):
         # u, z and out once; delta, B, C and the parameters once per traversal
         nbytes = 3 * tok * 4 + 4 * (tok * 4 + 2 * w.batch * L * N * 4 + w.dim * (N + 2) * 4)
         tokens = tok
-        slots = 4 * tok * N * SLOTS_PER_STATE_STEP
+        slots = 4 * tok * N
         info = dict(workload=w.name, batch=w.batch, dim=w.dim, height=H, width=W, dstate=N,
                     directions=4, kernels="transpose + 2 bidir scans + merge")
 
@@ -420,8 +425,9 @@ def build_step(cfg, seed, sets, dev, zoh=False, conv="none"):
         # write du, ddelta per direction, dz, and dB, dC per direction
         nbytes = 2 * (2 * tok * 4 + 2 * bc) + 2 * tok * 4 + 2 * (2 * tok * 4 + 2 * bc) + tok * 4
         tokens = tok
-        # one state recompute (5 slots) and the adjoint (9 slots) per state step
-        slots = 2 * tok * N * 14
+        # one state recompute (5 operations) and the adjoint (9) per state
+        # step: 14 / 5 state-update equivalents
+        slots = 2 * tok * N * 14 / 5
         info = dict(workload=w.name + "-backward", batch=w.batch, dim=w.dim, seqlen=L, dstate=N,
                     directions=2, combine_scale=w.combine_scale,
                     kernels="forward recompute + gate backward + 2 x (backward + reduce)")
@@ -467,9 +473,9 @@ def build_step(cfg, seed, sets, dev, zoh=False, conv="none"):
         # dz once, and ddelta, dB, dC per traversal
         nbytes = 3 * tok * 4 + 4 * (tok * 4 + 2 * bc) + 2 * tok * 4 + 4 * (tok * 4 + 2 * bc)
         tokens = tok
-        # one state recompute (5 slots) and the adjoint (9 slots) per state
-        # step of each traversal
-        slots = 4 * tok * N * 14
+        # one state recompute (5 operations) and the adjoint (9) per state
+        # step of each traversal: 14 / 5 state-update equivalents
+        slots = 4 * tok * N * 14 / 5
         info = dict(workload=w.name + "-backward", batch=w.batch, dim=w.dim, height=H, width=W, dstate=N,
                     directions=4, combine_scale=w.combine_scale,
                     kernels="transposes + 2 bidir recomputes + gate backward + 4 x (backward + reduce) + sum")
@@ -550,10 +556,13 @@ def main():
     torch.cuda.synchronize()
 
     # Kernel time (the roofline's): K eager steps with HIP events around every
-    # launch, on the launch stream.  Whole-job time (value, ms_per_step): the
-    # same K steps; workloads whose steps allocate no temporary memory are
-    # captured once in a HIP graph and replayed, which removes the per-call
-    # host overhead between launches, the others are these eager steps.
+    # launch, on the launch stream (mean, median and min per launch).
+    # Whole-job time (value, ms_per_step): exactly K steps between
+    # synchronisations, timed REPLAYS times; the median is reported, with
+    # the min.  Workloads whose steps allocate no temporary memory are
+    # captured once in a HIP graph of the K steps and replayed, which removes
+    # the per-call host overhead between launches; the others repeat the K
+    # eager steps.
     use_graph = info.pop("graphable", False) and not args.no_graph
     stream = torch.cuda.current_stream(dev)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -565,8 +574,11 @@ def main():
         step(i)
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    eager_wall = time.perf_counter() - t0
+    per_launch = sorted(s_.elapsed_time(e_) for s_, e_ in zip(starts, ends))
+    launch_ms = sum(per_launch) / args.steps
+    launch_med = per_launch[len(per_launch) // 2]
+    graph = None
     if use_graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
@@ -574,26 +586,38 @@ def main():
                 step(i)
         graph.replay()                                  # one untimed replay
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        graph.replay()
+    walls = []
+    for r in range(args.replays):
+        if graph is None and r == 0:
+            walls.append(eager_wall)
+            continue
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(args.steps):
+                step(i)
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - t0)
+    walls.sort()
+    wall = walls[len(walls) // 2]
     info["launch"] = "hip-graph" if use_graph else "eager"
 
     ms_per_step = 1e3 * wall / args.steps
     value = nbytes / (wall / args.steps) / 1e9
     achieved_gbs = nbytes / (launch_ms * 1e-3) / 1e9
-    achieved_tslots = slots / (launch_ms * 1e-3) / 1e12
+    achieved_updates = slots / (launch_ms * 1e-3) / 1e12
     src_hash = kernel_source_hash()
     variant = ("+zoh" if args.zoh else "") + (f"+conv-{args.conv}" if args.conv != "none" else "")
     traffic = load_traffic(src_hash, info["workload"] + variant)
-    hbm = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-           "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
-    alu = {"bound": "alu", "achieved": round(achieved_tslots, 2), "peak": round(VALU_PEAK_TSLOTS, 2),
-           "unit": "T VALU lane-slots/s", "frac": round(achieved_tslots / VALU_PEAK_TSLOTS, 4),
-           "traffic": traffic}
-    # The roofline reported is the one the kernel sits closest to.
-    roof, other = (alu, hbm) if alu["frac"] >= hbm["frac"] else (hbm, alu)
+    # The roofline is HBM bandwidth (algorithmic bytes of the step / mean
+    # kernel time); the ALU ceiling of the state step is reported beside it.
+    roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    other = {"bound": "alu", "achieved": round(achieved_updates, 3), "peak": round(UPDATES_PEAK_T, 3),
+             "unit": "T state updates/s", "frac": round(achieved_updates / UPDATES_PEAK_T, 4),
+             "cycles_per_wave_state_update": CYCLES_PER_WAVE_STATE_UPDATE}
 
     cpu = None
     if cpu_fn is not None and args.cpu_seconds > 0:
@@ -619,6 +643,10 @@ def main():
         "tokens_ch_per_s": round(tokens / (wall / args.steps), 1),
         "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         "kernel_ms_events": round(launch_ms, 5),
+        "kernel_ms_events_median": round(launch_med, 5),
+        "kernel_ms_events_min": round(per_launch[0], 5),
+        "ms_per_step_min": round(1e3 * walls[0] / args.steps, 5),
+        "replays": len(walls),
         "roofline": roof,
         "roofline_other": other,
         "cpu_baseline": cpu,

@@ -360,6 +360,18 @@ struct ConvBwd {
 };
 
 // Shared checks of the backward entry points (dz exactly when z).
+// The backward kernel reads one batch row of B and C (fp32, after any
+// widening, which keeps the layout) through a buffer resource with 32-bit
+// byte offsets, up to one tile past the last step: reject layouts whose
+// extent would not fit.
+int check_bwd_bc(const vm_scan_dir *p, int64_t L, int64_t dstate) {
+  if (p == nullptr) return VM_OK;
+  const int64_t bsn = p->bc_stride > 0 ? 1 : L;
+  const int64_t bst = p->bc_stride > 0 ? p->bc_stride : 1;
+  const int64_t ext = (dstate - 1) * bsn + (L + vmk::kBwdTile) * bst + 1;
+  return ext * 4 < (int64_t{1} << 31) ? VM_OK : VM_ERR_UNSUPPORTED;
+}
+
 int check_bwd_common(int dtype, int options, int64_t batch, int64_t dim, int64_t L, int64_t dstate,
                      const void *z, const void *dout, const void *dz, int64_t *tok, int64_t *bc) {
   if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;
@@ -649,6 +661,8 @@ int vm_pool_scan_repeat_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, cons
   const int es = bf16 ? 2 : 4;
   st = check_dir(fwd, full, pooled, batch, Lp, dim, dstate, es, Span());
   if (st == VM_OK && bwd != nullptr) st = check_dir(bwd, full, pooled, batch, Lp, dim, dstate, es, Span());
+  if (st == VM_OK) st = check_bwd_bc(fwd, Lp, dstate);
+  if (st == VM_OK) st = check_bwd_bc(bwd, Lp, dstate);
   if (st != VM_OK) return st;
   if (fwd->conv_w != nullptr || (bwd != nullptr && bwd->conv_w != nullptr)) return VM_ERR_UNSUPPORTED;
   const int ndir = bwd != nullptr ? 2 : 1;
@@ -816,6 +830,7 @@ int vm_ss2d_scan_bwd(const vm_scan_dir *dirs, const void *u, const void *z, cons
     d[k] = dirs[k];
     d[k].u = u;                     // the one map every traversal reads
     st = check_dir(&d[k], tok, tok, batch, L, dim, dstate, es, Span());
+    if (st == VM_OK) st = check_bwd_bc(&d[k], L, dstate);
     if (st == VM_OK && d[k].conv_w != nullptr) st = VM_ERR_UNSUPPORTED;
     if (st == VM_OK) dir_spans(&d[k], tok, batch, L, dim, dstate, es, ins);
   }
@@ -927,6 +942,7 @@ int vm_selective_scan_bwd(const vm_scan_dir *p, const void *z, const void *dout,
   const bool bf16 = dtype == VM_BF16;
   const int es = bf16 ? 2 : 4;
   st = check_dir(p, tok, tok, batch, seqlen, dim, dstate, es, Span());
+  if (st == VM_OK) st = check_bwd_bc(p, seqlen, dstate);
   if (st != VM_OK) return st;
   const bool conv = p->conv_w != nullptr;
   std::vector<Span> ins, outs;
@@ -998,6 +1014,8 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
   const int es = bf16 ? 2 : 4;
   st = check_dir(fwd, tok, tok, batch, seqlen, dim, dstate, es, Span());
   if (st == VM_OK) st = check_dir(bwd, tok, tok, batch, seqlen, dim, dstate, es, Span());
+  if (st == VM_OK) st = check_bwd_bc(fwd, seqlen, dstate);
+  if (st == VM_OK) st = check_bwd_bc(bwd, seqlen, dstate);
   if (st != VM_OK) return st;
   if ((fwd->conv_w == nullptr) != (bwd->conv_w == nullptr)) return VM_ERR_UNSUPPORTED;
   const bool conv = fwd->conv_w != nullptr;

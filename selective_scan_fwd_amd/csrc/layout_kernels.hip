@@ -168,9 +168,12 @@ atrous_gather_kernel(const T *__restrict__ x, T *__restrict__ streams, int64_t c
   }
 }
 
-// Inverse routing: every valid (row, col) has exactly one owner, group
-// k = (row & 1) + 2 (col & 1) at step t of that group; copy it, write each
-// output once (no sums).  When the plane's four streams fit in LDS they are
+// Inverse routing ("EfficientVMamba: Atrous Selective Scan for Light Weight
+// Visual Mamba", "Merge restores coordinates instead of adding directions"):
+// p = 2 routing is a permutation of the padded grid, so scatter inverts it
+// and crops.  Pixel (row, col) of the map comes from group
+// k = (row & 1) + 2 (col & 1) at that group's step t; each output is copied
+// and written once (no sums).  When the plane's four streams fit in LDS they are
 // staged there first with coalesced loads; the plane is then written with
 // coalesced stores.  Vector path (staged, Lg and W multiples of 4, aligned
 // pointers): 4-value streaming loads and stores, each thread writing 4

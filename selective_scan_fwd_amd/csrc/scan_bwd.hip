@@ -236,7 +236,9 @@ scan_bwd_kernel(const Arg arg) {
   for (int k = 0; k < nt1; ++k) {
     const int j = tile_of(k);
     bstore4(rCk, ck_lane + static_cast<uint32_t>(j) * 64u, h);
+    wave_lds_fence();                    // the previous tile's staged values are read
     stage_store();
+    wave_lds_fence();
     stage_load(tile_of(k + 1 < nt1 ? k + 1 : nt1 - 1), false);
 #pragma unroll
     for (int q = 0; q < T; ++q) {
@@ -271,7 +273,9 @@ scan_bwd_kernel(const Arg arg) {
   stage_load(tile_of(nt - 1), true);
   for (int k = nt - 1; k >= 0; --k) {
     const int j = tile_of(k);
+    wave_lds_fence();                    // the previous tile's partial sums are read
     stage_store();
+    wave_lds_fence();
     float hc[kNS], h0[kNS];
 #pragma unroll
     for (int jn = 0; jn < kNS; ++jn) {
@@ -313,7 +317,7 @@ scan_bwd_kernel(const Arg arg) {
     const int jT = j * T;
     // dC_t = sum over the block's channels of dy_t h_t, per (n, step): the
     // contributions meet in LDS, and the dB ones reuse the area afterwards
-    // (a wave's LDS accesses execute in program order).
+    // (each hand-over between lanes ordered by wave_lds_fence).
     auto reduce_red = [&](const Rsrc &dst) {
 #pragma unroll
       for (int m = 0; m < 16 * T / 64; ++m) {
@@ -335,7 +339,9 @@ scan_bwd_kernel(const Arg arg) {
 #pragma unroll
       for (int jn = 0; jn < kNS; ++jn)
         red[((n0 + jn) * T + q) * Lay::RSTR + sp * 16 + r] = pqs[q].z * hs[q][jn];
+    wave_lds_fence();
     reduce_red(rPC);
+    wave_lds_fence();
     // adjoint back through the tile
 #pragma unroll
     for (int q = T - 1; q >= 0; --q) {
@@ -376,6 +382,7 @@ scan_bwd_kernel(const Arg arg) {
       part[(1 * 64 + lane) * Lay::QSTR + q] = sqA;
     }
     // per element: du, ddelta (the four state groups of the channel summed)
+    wave_lds_fence();
     const bool in_seq = tq < L - jT;
 #pragma unroll
     for (int i = 0; i < PE; ++i) {
@@ -406,11 +413,13 @@ scan_bwd_kernel(const Arg arg) {
 #pragma unroll
   for (int jn = 0; jn < kNS; ++jn)
     bstore<float>(rPA, static_cast<uint32_t>(r * 16 + n0 + jn) * 4u, dA[jn]);
+  wave_lds_fence();
 #pragma unroll
   for (int i = 0; i < PE; ++i) {
     part[srow[i] * Lay::QSTR + sq] = accD[i];
     part[64 * Lay::QSTR + srow[i] * Lay::QSTR + sq] = accB[i];
   }
+  wave_lds_fence();
   if (lane < kR) {
     float sD_ = 0.0f, sB_ = 0.0f;
     for (int q = 0; q < T; ++q) {

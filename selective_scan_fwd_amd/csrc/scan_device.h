@@ -30,6 +30,17 @@ __device__ __forceinline__ uint32_t pin_u(uint32_t v) {
   return v;
 }
 
+// Orders one wave's LDS accesses across its lanes: LDS reads after this
+// point see what any lane of the wave wrote before it.  A wave's LDS
+// instructions execute in order, so this emits no instruction; it keeps the
+// compiler from moving LDS accesses across it, which single-lane semantics
+// would allow wherever a lane's own addresses provably differ.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 // Buffer access.  Token tensors, B, C and the exchange rows are read
 // and written through buffer resources (base address and byte size in
 // scalar registers, a 32-bit byte offset per lane).  An offset at or past

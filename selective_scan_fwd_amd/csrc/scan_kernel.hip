@@ -332,8 +332,8 @@ scan_kernel(const ScanArgs p) {
   // CONV: the loaded values are the conv input x.  The wave writes the
   // tile's x (row slots 3..T+2, in visit order) and the previous tile's last
   // three (slots 0..2), then reads each element's three predecessors back:
-  // u = SiLU(cb + w0 x[-3] + w1 x[-2] + w2 x[-1] + w3 x[0]).  A wave's LDS
-  // accesses execute in program order, so the writes land before the reads.
+  // u = SiLU(cb + w0 x[-3] + w1 x[-2] + w2 x[-1] + w3 x[0]); the reads
+  // follow the other lanes' writes (wave_lds_fence).
   auto stage_store = [&](auto par, int kt) __attribute__((always_inline)) {
     constexpr int Q = decltype(par)::value;
     const bool sp_on = p.softplus != 0;
@@ -347,6 +347,7 @@ scan_kernel(const ScanArgs p) {
         xs[srow[i] * Lay::XH + 3 + sq] = xc[i];
         xprev[i] = xc[i];
       }
+      wave_lds_fence();
       const bool in_seq = tq < L - tile_of(kt) * T;
 #pragma unroll
       for (int i = 0; i < PE; ++i) {
@@ -463,8 +464,9 @@ scan_kernel(const ScanArgs p) {
 
   // One iteration k (slot Q = k % NB): finishing loads of k+1, prefetch of
   // tile k+NB into the slot tile k has left, scan k, partial reads of k,
-  // stage and read back k+1, combine k.  A wave's LDS traffic executes in
-  // program order, so none of this needs a barrier.  The prefetch and the
+  // stage and read back k+1, combine k.  Each hand-over of LDS data between
+  // lanes of the wave is ordered by wave_lds_fence (no barrier: only this
+  // wave touches its area).  The prefetch and the
   // staging run on every iteration (past the end they repeat the last tile,
   // whose staged copy is never scanned): a load issued under a branch would
   // make the count of loads in flight path-dependent.
@@ -476,9 +478,13 @@ scan_kernel(const ScanArgs p) {
       static_assert(NS == 4, "a lane's checkpoint is one 16-byte store");
       bstore4(rCk, ck_lane + static_cast<uint32_t>(tile_of(k)) * 64u, h);
     }
+    wave_lds_fence();                    // staged tile k read back before its partials overwrite it
     do_scan();
+    wave_lds_fence();
     comb_read(k, second);
+    wave_lds_fence();
     stage_store(Qn(), k + 1 < nt ? k + 1 : nt - 1);
+    wave_lds_fence();
     read_tile();
     do_combine(k, slot, second);
   };
@@ -523,6 +529,7 @@ scan_kernel(const ScanArgs p) {
     A2[j] = a * kLog2e;
   }
   stage_store(std::integral_constant<int, 0>(), 0);
+  wave_lds_fence();
   read_tile();
   if (DIRS == 1) {
     comb_load(0, std::integral_constant<int, 0>(), First());

@@ -322,6 +322,17 @@ def test_bwd_argument_checks(lib):
     gc.dconv_w = FAKE + 8                                   # ... and not over an input (u)
     assert single(p=fc, g=gc) == 5
 
+    # token-major B and C with a projection-split stride (44) whose batch-row
+    # extent passes the backward kernel's 32-bit byte offsets: rejected
+    # before anything runs (L = 13e6: (L + 8) * 44 * 4 bytes > 2^31)
+    fs = _dir(FAKE)
+    fs.bc_stride = 44
+    Lbig = 13_000_000
+    assert lib.vm_selective_scan_bwd(ctypes.byref(fs), None, FAKE * 3, ctypes.byref(gf), None, 1, 1, Lbig, 16,
+                                     0, 1, 0, None) == 6
+    assert lib.vm_bidir_scan_bwd(ctypes.byref(fs), ctypes.byref(fs), None, FAKE * 3, 1.0, ctypes.byref(gf),
+                                 ctypes.byref(gb), None, 1, 1, Lbig, 16, 0, 1, None) == 6
+
     def bidir(g2=gb, scale=1.0, dtype=0):
         return lib.vm_bidir_scan_bwd(ctypes.byref(f), ctypes.byref(b), None, FAKE * 3, scale,
                                      ctypes.byref(gf), ctypes.byref(g2), None, 2, 4, 5, 16, dtype, 1, None)
