@@ -176,6 +176,28 @@ int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
                       void *stream);
 
 /*
+ * vm_bidir_scan_fwd for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and checks as vm_bidir_scan_fwd, and
+ * the same kernels; it calls no hipMalloc, hipFree or allocating routine.
+ * Where vm_bidir_scan_fwd would take its exchange buffer from the pool (a
+ * sequence past the on-chip exchange whose `out` cannot serve), this entry
+ * uses a library-owned device array of 8 Mi fp32 values (32 MiB; one per
+ * GPU the library runs on, held until the process ends):
+ *   batch * dim * (seqlen rounded up to 32) must be at most 8388608, else
+ *   VM_ERR_UNSUPPORTED (checked on the host before any HIP call).
+ * Every call on one GPU shares that array and leaves its contents behind
+ * (each exchange row is written before it is read, so nothing needs
+ * clearing): calls that overlap in time on one GPU (different streams or
+ * host threads) race and must not be issued.
+ */
+int vm_bidir_scan_fwd_noalloc(const vm_scan_dir *fwd, const vm_scan_dir *bwd,
+                              const void *z, float combine_scale, void *out,
+                              int64_t batch, int64_t dim, int64_t seqlen,
+                              int64_t dstate, int dtype, int options,
+                              void *stream);
+
+/*
  * Depthwise causal convolution of width 4 with bias, then SiLU: the step
  * that produces the scan input u from the block's content x ([Vim] "Inside
  * the released Vim block": each branch's content passes through its own

@@ -32,6 +32,7 @@ STATUS_NAMES = {0: "VM_OK", 1: "VM_ERR_NULL", 2: "VM_ERR_SHAPE", 3: "VM_ERR_DTYP
                 5: "VM_ERR_ALIAS", 6: "VM_ERR_UNSUPPORTED", 7: "VM_ERR_HIP", 8: "VM_ERR_ALLOC"}
 
 EXPORTED = ("vm_status_string", "vm_version", "vm_selective_scan_fwd", "vm_bidir_scan_fwd",
+            "vm_bidir_scan_fwd_noalloc",
             "vm_atrous_group_len", "vm_atrous_gather", "vm_atrous_scatter", "vm_pool_scan_repeat",
             "vm_ss2d_scan_fwd", "vm_causal_conv1d_silu", "vm_causal_conv1d_silu_bwd",
             "vm_selective_scan_bwd", "vm_bidir_scan_bwd", "vm_pool_scan_repeat_bwd",
@@ -79,6 +80,7 @@ def load_library():
             lib.vm_version.restype = I
             lib.vm_selective_scan_fwd.argtypes = [D, P, P, I64, I64, I64, I64, I, I, I, P]
             lib.vm_bidir_scan_fwd.argtypes = [D, D, P, F, P, I64, I64, I64, I64, I, I, P]
+            lib.vm_bidir_scan_fwd_noalloc.argtypes = [D, D, P, F, P, I64, I64, I64, I64, I, I, P]
             lib.vm_atrous_group_len.argtypes = [I64, I64]
             lib.vm_atrous_group_len.restype = I64
             lib.vm_atrous_gather.argtypes = [P, P, I64, I64, I64, I64, I, P]
@@ -92,7 +94,8 @@ def load_library():
             lib.vm_bidir_scan_bwd.argtypes = [D, D, P, P, F, G, G, P, I64, I64, I64, I64, I, I, P]
             lib.vm_pool_scan_repeat_bwd.argtypes = [D, D, P, P, F, G, G, P, I64, I64, I64, I64, I64, I, I, I, P]
             lib.vm_ss2d_scan_bwd.argtypes = [D, P, P, P, F, G, P, P, I64, I64, I64, I64, I64, I, I, P]
-            for name in ("vm_selective_scan_fwd", "vm_bidir_scan_fwd", "vm_atrous_gather",
+            for name in ("vm_selective_scan_fwd", "vm_bidir_scan_fwd", "vm_bidir_scan_fwd_noalloc",
+                         "vm_atrous_gather",
                          "vm_atrous_scatter", "vm_pool_scan_repeat", "vm_ss2d_scan_fwd",
                          "vm_causal_conv1d_silu", "vm_causal_conv1d_silu_bwd", "vm_selective_scan_bwd",
                          "vm_bidir_scan_bwd", "vm_pool_scan_repeat_bwd", "vm_ss2d_scan_bwd"):
@@ -245,6 +248,30 @@ def vm_bidir_scan_fwd(fwd, bwd, z=None, combine_scale=1.0, delta_softplus=True, 
                                               _dtype_code(u), _options(delta_softplus, zoh),
                                               _stream(u.device))
     _check(st, "vm_bidir_scan_fwd")
+    return out
+
+
+def vm_bidir_scan_fwd_noalloc(fwd, bwd, out, z=None, combine_scale=1.0, delta_softplus=True, zoh=False):
+    """vm_bidir_scan_fwd for callers that cannot allocate device memory: the
+    same result, written into the caller's `out`; the exchange buffer of long
+    sequences comes from a library-owned device array (batch * dim * (L
+    rounded up to 32) <= 8388608, else VmError).  Calls on one GPU share that
+    array: calls that overlap in time on one GPU must not be issued."""
+    u = fwd["u"]
+    dt = u.dtype
+    batch, dim, L = u.shape
+    N = fwd["A"].shape[-1]
+    df, kf = _direction(fwd, batch, dim, (batch, dim, L), L, N, dt, u.device, "fwd")
+    db, kb = _direction(bwd, batch, dim, (batch, dim, L), L, N, dt, u.device, "bwd")
+    if z is not None:
+        _dev(z, "z", dt, u.shape, u.device)
+    _dev(out, "out", dt, u.shape, u.device)
+    with torch.cuda.device(u.device):
+        st = load_library().vm_bidir_scan_fwd_noalloc(ctypes.byref(df), ctypes.byref(db), _ptr(z),
+                                                      float(combine_scale), _ptr(out), batch, dim, L, N,
+                                                      _dtype_code(u), _options(delta_softplus, zoh),
+                                                      _stream(u.device))
+    _check(st, "vm_bidir_scan_fwd_noalloc")
     return out
 
 
@@ -522,7 +549,7 @@ def vm_ss2d_scan_bwd(u, dirs, dout, z=None, combine_scale=1.0, delta_softplus=Tr
     return du, grads, dz
 
 
-__all__ = ["vm_selective_scan_fwd", "vm_bidir_scan_fwd", "vm_atrous_gather", "vm_atrous_scatter",
+__all__ = ["vm_selective_scan_fwd", "vm_bidir_scan_fwd", "vm_bidir_scan_fwd_noalloc", "vm_atrous_gather", "vm_atrous_scatter",
            "vm_pool_scan_repeat", "vm_ss2d_scan_fwd", "vm_causal_conv1d_silu",
            "vm_causal_conv1d_silu_bwd", "vm_pool_scan_repeat_bwd", "vm_ss2d_scan_bwd",
            "vm_selective_scan_bwd", "vm_bidir_scan_bwd", "VmScanGrad", "vm_atrous_group_len", "vm_status_string", "vm_version",

@@ -155,8 +155,7 @@ const float *as_f32(const void *src, int64_t n, bool bf16, Scratch &ws, hipStrea
 // dense [batch, dstate, L] and token-major B and C alike.  widen_bc: the
 // kernel runs in fp32 on bf16 B and C (pooled path), so they are widened into
 // temporary memory with the same layout first.
-vmk::DirPtrs resolve_dir(const vm_scan_dir *p, int64_t batch, int64_t dstate, int64_t L,
-                         bool widen_bc, Scratch &ws, hipStream_t s, int *status) {
+vmk::DirPtrs dir_ptrs(const vm_scan_dir *p, int64_t dstate, int64_t L) {
   vmk::DirPtrs d = {};
   d.u = p->u;
   d.delta = p->delta;
@@ -176,6 +175,12 @@ vmk::DirPtrs resolve_dir(const vm_scan_dir *p, int64_t batch, int64_t dstate, in
     d.bsn = L;
     d.bst = 1;
   }
+  return d;
+}
+
+vmk::DirPtrs resolve_dir(const vm_scan_dir *p, int64_t batch, int64_t dstate, int64_t L,
+                         bool widen_bc, Scratch &ws, hipStream_t s, int *status) {
+  vmk::DirPtrs d = dir_ptrs(p, dstate, L);
   if (widen_bc) {
     const int64_t n = bc_extent(batch, dstate, L, p->bc_stride);
     d.B = as_f32(p->B, n, true, ws, s, status);
@@ -451,10 +456,15 @@ int vm_selective_scan_fwd(const vm_scan_dir *p, const void *z, void *out, int64_
   return hip_status(vmk::launch_scan(plan, a, bf16, s));
 }
 
-int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void *z,
-                      float combine_scale, void *out, int64_t batch, int64_t dim,
-                      int64_t seqlen, int64_t dstate, int dtype, int options,
-                      void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Host-side checks of the bidirectional forward entry points, and the
+// kernel arguments of a call that passes them (everything but the exchange).
+int bidir_fwd_args(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void *z, float combine_scale,
+                   void *out, int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate, int dtype,
+                   int options, vmk::ScanArgs *a) {
   if (dtype != VM_F32 && dtype != VM_BF16) return VM_ERR_DTYPE;
   if (!options_ok(options)) return VM_ERR_FLAG;
   int64_t tok = 0, bc = 0;
@@ -470,26 +480,91 @@ int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
   if (st != VM_OK) return st;
   if ((fwd->conv_w == nullptr) != (bwd->conv_w == nullptr)) return VM_ERR_UNSUPPORTED;
   if (overlaps(span(z, tok * es), so)) return VM_ERR_ALIAS;
+  *a = vmk::ScanArgs{};
+  a->dir[0] = dir_ptrs(fwd, dstate, seqlen);
+  a->dir[1] = dir_ptrs(bwd, dstate, seqlen);
+  a->z = z;
+  a->out = out;
+  a->batch = batch;
+  a->dim = dim;
+  a->L = seqlen;
+  a->dstate = static_cast<int>(dstate);
+  a->softplus = (options & VM_DELTA_SOFTPLUS) != 0;
+  a->zoh = (options & VM_ZOH) != 0;
+  a->reverse = 0;
+  a->scale = combine_scale;
+  a->conv = fwd->conv_w != nullptr;
+  return VM_OK;
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool bf16 = dtype == VM_BF16;
-  Scratch ws(s);
-  vmk::ScanArgs a = {};
-  a.dir[0] = resolve_dir(fwd, batch, dstate, seqlen, false, ws, s, &st);
-  a.dir[1] = resolve_dir(bwd, batch, dstate, seqlen, false, ws, s, &st);
+// ---- the exchange buffer of vm_bidir_scan_fwd_noalloc, for callers that
+// cannot allocate: a file-scope device array of kNoAllocFloats fp32 values
+// (32 MiB), one copy per GPU the library runs on, held until the process
+// ends.  Host code never passes the array's name to a kernel: it takes the
+// device address once per device with hipGetSymbolAddress and uses that.
+constexpr int64_t kNoAllocFloats = int64_t{8} << 20;
+static __device__ __align__(256) float scratch[kNoAllocFloats];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_on_current_device(float **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return VM_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return VM_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = static_cast<float *>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return VM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int vm_bidir_scan_fwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void *z,
+                      float combine_scale, void *out, int64_t batch, int64_t dim,
+                      int64_t seqlen, int64_t dstate, int dtype, int options,
+                      void *stream) {
+  vmk::ScanArgs a;
+  int st = bidir_fwd_args(fwd, bwd, z, combine_scale, out, batch, dim, seqlen, dstate, dtype, options, &a);
   if (st != VM_OK) return st;
-  a.z = z;
-  a.out = out;
-  a.batch = batch;
-  a.dim = dim;
-  a.L = seqlen;
-  a.dstate = static_cast<int>(dstate);
-  a.softplus = (options & VM_DELTA_SOFTPLUS) != 0;
-  a.zoh = (options & VM_ZOH) != 0;
-  a.reverse = 0;
-  a.scale = combine_scale;
-  a.conv = fwd->conv_w != nullptr;
-  return launch_bidir(a, bf16, ws, s);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Scratch ws(s);
+  return launch_bidir(a, dtype == VM_BF16, ws, s);
+}
+
+int vm_bidir_scan_fwd_noalloc(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void *z,
+                              float combine_scale, void *out, int64_t batch, int64_t dim,
+                              int64_t seqlen, int64_t dstate, int dtype, int options,
+                              void *stream) {
+  vmk::ScanArgs a;
+  int st = bidir_fwd_args(fwd, bwd, z, combine_scale, out, batch, dim, seqlen, dstate, dtype, options, &a);
+  if (st != VM_OK) return st;
+  const bool bf16 = dtype == VM_BF16;
+  const vmk::ScanPlan plan = vmk::plan_scan(batch, dim, seqlen, static_cast<int>(dstate), 2, a.conv != 0);
+  if (plan.xmode == vmk::kXGlobal) {
+    a.xstride = vmk::xchg_global_stride(seqlen);
+    if (!bf16 && a.xstride == seqlen && reinterpret_cast<uintptr_t>(out) % 128 == 0) {
+      a.xglobal = static_cast<float *>(out);        // out serves as the exchange, as in vm_bidir_scan_fwd
+    } else {
+      if (batch * dim > kNoAllocFloats / a.xstride) return VM_ERR_UNSUPPORTED;
+      st = scratch_on_current_device(&a.xglobal);
+      if (st != VM_OK) return st;
+    }
+  }
+  if (!vmk::scan_offsets_fit(plan, a, bf16)) return VM_ERR_UNSUPPORTED;
+  return hip_status(vmk::launch_scan(plan, a, bf16, static_cast<hipStream_t>(stream)));
 }
 
 int vm_causal_conv1d_silu(const void *x, const float *w, const float *bias, void *out,

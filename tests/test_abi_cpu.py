@@ -126,6 +126,25 @@ def test_bidir_argument_checks(lib):
     assert call(out=b.C) == 5
 
 
+def test_bidir_noalloc_argument_checks(lib):
+    # the same checks as vm_bidir_scan_fwd, then the bound of its exchange
+    # array: 4 x 512 rows x 4128 (4097 rounded up to 32) fp32 values > 8 Mi,
+    # rejected on the host before any HIP call
+    f, b = _dir(FAKE), _dir(FAKE * 2)
+
+    def call(out=FAKE * 3, batch=2, dim=4, L=5, N=16, dtype=0, scale=1.0):
+        return lib.vm_bidir_scan_fwd_noalloc(ctypes.byref(f), ctypes.byref(b), None, scale, out, batch, dim, L,
+                                             N, dtype, 1, None)
+
+    assert call(out=None) == 1
+    assert call(dtype=3) == 3
+    assert call(N=0) == 2
+    assert call(N=17) == 6
+    assert call(scale=float("nan")) == 6
+    assert call(out=f.u) == 5
+    assert call(batch=4, dim=512, L=4097, dtype=1) == 6
+
+
 def test_atrous_argument_checks(lib):
     assert lib.vm_atrous_gather(None, FAKE * 3, 1, 1, 4, 4, 0, None) == 1
     assert lib.vm_atrous_gather(FAKE, None, 1, 1, 4, 4, 0, None) == 1
