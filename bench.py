@@ -42,6 +42,7 @@ CYCLES_PER_WAVE_STATE_UPDATE = 20.1
 UPDATES_PEAK_T = 256 * 4 * 64 * 2.4e9 / CYCLES_PER_WAVE_STATE_UPDATE / 1e12
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["selective_scan_fwd_amd/csrc/scan_kernel.hip",
+                  "selective_scan_fwd_amd/csrc/scan_chunk.hip",
                   "selective_scan_fwd_amd/csrc/scan_bwd.hip",
                   "selective_scan_fwd_amd/csrc/scan_device.h",
                   "selective_scan_fwd_amd/csrc/layout_kernels.hip",
@@ -104,7 +105,8 @@ def copy_calibration(mib, steps):
 PROBE_KINDS = ["fma", "exp", "exp+3fma", "state-step-dpp", "state-step-dpp-no-exp", "permlane32-swap",
                "exp-latency", "fma-latency", "fma-3vgpr", "mul-2vgpr", "mul-sgpr", "fmac-sgpr", "mul-dpp",
                "state-step-sgpr", "state-step-sgpr-no-exp", "exp-waves+fma-waves", "state-step-vgpr",
-               "state-step-vgpr-no-exp", "phased-2w-barrier", "phased-2w", "phased-4w-barrier", "phased-4w"]
+               "state-step-vgpr-no-exp", "phased-2w-barrier", "phased-2w", "phased-4w-barrier", "phased-4w",
+               "fetch-straight-4096", "fetch-loop-64x64"]
 SIMDS = 256 * 4
 
 
@@ -145,6 +147,8 @@ def valu_probe(iters=4000, kinds=None):
             out = torch.empty(blocks * threads, device=dev)
             clk = torch.zeros(waves * 4, dtype=torch.int64, device=dev)
             it = iters // 4 if "latency" in name else iters
+            if name.startswith("fetch"):
+                it = 1 if "straight" in name else 64         # 4096 instructions either way
             for rep in range(2):                       # the first launch warms up
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)

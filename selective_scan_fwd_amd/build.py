@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvmscan.so")
-SOURCES = ["api.hip", "scan_kernel.hip", "scan_bwd.hip", "layout_kernels.hip"]
+SOURCES = ["api.hip", "scan_kernel.hip", "scan_chunk.hip", "scan_bwd.hip", "layout_kernels.hip"]
 # The VALU issue-rate probe behind the benchmark's ALU roofline: a library of
 # its own, so that the scan library holds only the hot path.
 PROBE_LIB = os.path.join(PKG, "libvmprobe.so")

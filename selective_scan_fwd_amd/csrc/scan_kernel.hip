@@ -660,9 +660,25 @@ ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t L, int dstate, int dirs, 
   // the global exchange: longer row segments per load and half the per-tile
   // overhead); 8 for the on-chip exchange, whose LDS footprint grows with T.
   pl.sub = 1;
+  pl.chunks = 1;
+  pl.chunk_len = static_cast<int>(L);
   if (dirs == 1) {
     pl.T = 16;
     pl.xmode = kXNone;
+    // Few row blocks (at most 256, a quarter of a wave per SIMD): the
+    // sequence-parallel kernel, one workgroup of four waves per channel,
+    // each lane on a sub-chunk of ceil(L / 64) steps, the row staged in LDS
+    // (L <= 256).  It does about twice the arithmetic, which pays only where
+    // SIMDs would otherwise sit idle, and only for sequences long enough to
+    // split.
+    if (nblk <= 256 && L >= 32 && L <= 256) {
+      pl.chunks = 64;
+      pl.chunk_len = static_cast<int>((L + 63) / 64);
+      pl.threads = 256;
+      pl.blocks = batch * dim;
+      pl.lds = 0;
+      return pl;
+    }
   } else {
     // On-chip exchange while a row block's area lets four of them share a
     // CU's 160 KB LDS.
@@ -703,6 +719,7 @@ bool scan_offsets_fit(const ScanPlan &plan, const ScanArgs &a, bool bf16) {
 
 hipError_t launch_scan(const ScanPlan &plan, const ScanArgs &args, bool bf16, hipStream_t s) {
   if (plan.blocks <= 0) return hipSuccess;
+  if (plan.chunks > 1) return launch_scan_chunked(plan, args, bf16, s);
   return bf16 ? dispatch_dtype<bf16_t>(plan, args, s) : dispatch_dtype<float>(plan, args, s);
 }
 

@@ -23,6 +23,15 @@
 //   5 permlane 16 independent v_permlane32_swap_b32 exchanges
 //   6 exp-latency  one dependent chain of v_exp_f32 (one wave per SIMD)
 //   7 fma-latency  one dependent chain of v_fma_f32
+//   8-12  operand forms (three VGPRs, two VGPRs, an SGPR, v_fmac with an
+//         SGPR, a DPP row broadcast); 13-14 the state step with B and C in
+//         SGPRs (one lane per channel), with and without the exponential;
+//   15    exp waves and fma waves sharing each SIMD; 16-17 the state step
+//         with every operand in VGPRs; 18-21 the state step in
+//         barrier-separated exponential and non-exponential phases (2 or 4
+//         waves per SIMD from one workgroup; with and without the barrier)
+//   22-23 instruction fetch: 4096 fma as straight-line code run once, or as
+//         a loop of 64
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -69,8 +78,8 @@ __device__ __forceinline__ void state4(float (&h)[4], const float (&a2)[4], floa
 
 // Workgroup size and dynamic LDS of each body: the phased bodies run one
 // workgroup per CU (8 or 16 waves: 2 or 4 per SIMD, 96 KB of LDS each).
-constexpr int probe_threads(int kind) { return kind == 18 || kind == 19 ? 512 : kind >= 20 ? 1024 : 256; }
-constexpr int probe_lds(int kind) { return kind >= 18 ? 96 * 1024 : 0; }
+constexpr int probe_threads(int kind) { return kind == 18 || kind == 19 ? 512 : kind == 20 || kind == 21 ? 1024 : 256; }
+constexpr int probe_lds(int kind) { return kind >= 18 && kind <= 21 ? 96 * 1024 : 0; }
 
 template <int KIND>
 __global__ void __launch_bounds__(probe_threads(KIND)) probe_kernel(const float *in, float *out, uint64_t *clk, int iters) {
@@ -334,6 +343,29 @@ __global__ void __launch_bounds__(probe_threads(KIND)) probe_kernel(const float 
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc += h[j];
+  } else if constexpr (KIND == 22 || KIND == 23) {
+    // instruction fetch: 4096 independent v_fma_f32 as straight-line code
+    // run once (22), or as 64 passes of a 64-instruction loop (23)
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = s + 0.01f * i;
+    for (int it = 0; it < iters; ++it) {
+      if constexpr (KIND == 22) {
+#pragma unroll
+        for (int rep = 0; rep < 256; ++rep)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] = __builtin_fmaf(x[i], 0.999f + 1e-7f * rep, 0.001f);
+      } else {
+#pragma unroll
+        for (int rep = 0; rep < 4; ++rep)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] = __builtin_fmaf(x[i], 0.999f + 1e-7f * rep, 0.001f);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = opaque(x[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc += x[i];
   } else {
     float x = s;
     for (int it = 0; it < iters; ++it) {
@@ -375,8 +407,8 @@ extern "C" {
 
 // Wave-instructions per iteration of each body, as in its disassembly
 // (loop control excluded): VALU forms only.
-const int kProbeInstr[22] = {64, 64, 64, 168, 168, 32, 64, 64, 64, 64, 64, 64, 64, 162, 162, 64, 162, 162,
-                             324, 324, 324, 324};
+const int kProbeInstr[24] = {64, 64, 64, 168, 168, 32, 64, 64, 64, 64, 64, 64, 64, 162, 162, 64, 162, 162,
+                             324, 324, 324, 324, 4096, 64};
 
 // Runs probe `kind` on `blocks` workgroups of vm_probe_threads(kind)
 // threads for `iters` iterations.  in: 64 floats (device); out: blocks *
@@ -411,11 +443,13 @@ int vm_probe_run(int kind, int blocks, int iters, const void *in, void *out, voi
     case 19: return launch<19>(blocks, iters, i, o, c, s);
     case 20: return launch<20>(blocks, iters, i, o, c, s);
     case 21: return launch<21>(blocks, iters, i, o, c, s);
+    case 22: return launch<22>(blocks, iters, i, o, c, s);
+    case 23: return launch<23>(blocks, iters, i, o, c, s);
     default: return 1;
   }
 }
 
-int vm_probe_instr(int kind) { return kind >= 0 && kind < 22 ? kProbeInstr[kind] : 0; }
+int vm_probe_instr(int kind) { return kind >= 0 && kind < 24 ? kProbeInstr[kind] : 0; }
 int vm_probe_threads(int kind) { return probe_threads(kind); }
 
 }  // extern "C"

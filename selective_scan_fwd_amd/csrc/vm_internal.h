@@ -115,6 +115,11 @@ struct ScanPlan {
   size_t lds;   // dynamic LDS bytes per workgroup
   int threads;  // workgroup size: 64 dirs sub
   int64_t blocks;
+  // Sequence-parallel scan (one direction, few rows): chunks > 1 runs the
+  // chunked kernel, one workgroup per channel whose lanes own `chunks`
+  // sub-chunks of chunk_len consecutive steps of the visit order.
+  int chunks;
+  int chunk_len;
 };
 
 ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t L, int dstate, int dirs, bool conv);
@@ -124,6 +129,7 @@ int64_t xchg_global_stride(int64_t L);
 // Whether every in-kernel offset of this launch fits 32 bits.
 bool scan_offsets_fit(const ScanPlan &plan, const ScanArgs &args, bool bf16);
 hipError_t launch_scan(const ScanPlan &plan, const ScanArgs &args, bool bf16, hipStream_t s);
+hipError_t launch_scan_chunked(const ScanPlan &plan, const ScanArgs &args, bool bf16, hipStream_t s);
 
 // ---------------------------------------------------------------- backward
 // One direction, fp32.  dy: gradient of the ungated scan output.  The kernel

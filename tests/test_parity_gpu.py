@@ -51,6 +51,37 @@ def test_single_fp32(batch, dim, L, N, reverse, gated, bc_layout):
     assert_close(host(out), ref, FP32_TOL, "single")
 
 
+# Sequence-parallel scan: one direction with few row blocks (and 32 to 256
+# steps) runs with each lane on a sub-chunk of ceil(L / 64) steps and the
+# lanes' (P, g) carries combined by a lane scan.  L 32 -> 1 step per lane
+# (lanes 32.. idle), 65 -> 2 (lanes 33.. idle), 197 -> 4 (a ragged last
+# lane), 256 -> 4 (every lane full); 257 is past the staged row (the
+# one-wave-per-row-block kernel); dstate 5 as well.
+@pytest.mark.parametrize("L", [32, 65, 197, 256, 257])
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("N", [16, 5])
+def test_single_chunked(L, reverse, N):
+    _case(f"single chunked L{L} rev{reverse} N{N}")
+    p, z = wl.single_inputs(150 + L + N, 1, 70, L, N, device=DEV, perturb=True)
+    out = vm.vm_selective_scan_fwd(**p, z=z, reverse=reverse)
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan(**host_dir(p), z=host(z), reverse=reverse)
+    assert_close(host(out), ref, FP32_TOL, "single chunked")
+
+
+@pytest.mark.parametrize("L", [33, 77])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_single_many_rows_unchunked(L, reverse):
+    """1024 row blocks (batch 64 x 16 blocks of 16 channels): the one-wave-per-
+    row-block kernel, with tiles of 16 steps and a ragged tail."""
+    _case(f"single many rows L{L} rev{reverse}")
+    p, z = wl.single_inputs(160 + L, 64, 256, L, device=DEV, perturb=True)
+    out = vm.vm_selective_scan_fwd(**p, z=z, reverse=reverse)
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan(**host_dir(p), z=host(z), reverse=reverse)
+    assert_close(host(out), ref, FP32_TOL, "single many rows")
+
+
 def test_single_no_softplus_and_no_bias():
     _case("single no softplus")
     p, z = wl.single_inputs(5, 2, 70, 45, device=DEV)
