@@ -68,6 +68,8 @@ def parse():
                          "6 SS2D four-direction scan 56x56, 7 backward of the Vim-T bidirectional scan, "
                          "8 backward of the SS2D scan 56x56")
     ap.add_argument("--sets", type=int, default=0, help="input sets to cycle (0 = auto)")
+    ap.add_argument("--size", type=int, default=56, choices=[56, 57],
+                    help="config 3: the ES2D feature map (56x56, or 57x57 padded to 58x58)")
     ap.add_argument("--replays", type=int, default=5,
                     help="times the K timed steps are run (graph replays, or eager passes); the median is reported")
     ap.add_argument("--conv", choices=["none", "fused", "unfused"], default="none",
@@ -184,7 +186,7 @@ def algorithmic_bytes_scan(batch, dim, L, N, es, dirs, gated):
     return dirs * per_dir + (tok * es if gated else 0) + tok * es
 
 
-def build_step(cfg, seed, sets, dev, zoh=False, conv="none"):
+def build_step(cfg, seed, sets, dev, zoh=False, conv="none", es2d_size=56):
     """Returns (step_fn(i), info dict, cpu_fn(budget_s) -> (seconds, bytes, tokens, threads, desc))."""
     import torch
 
@@ -281,18 +283,31 @@ def build_step(cfg, seed, sets, dev, zoh=False, conv="none"):
 
     if cfg == 3:
         w = wl.WORKLOADS[3]
-        H = W = w.sizes[0]
+        H = W = es2d_size
         inputs = [wl.es2d_inputs(seed + k, w.batch, w.dim, H, W, device=dev) for k in range(sets)]
         Lg = ((H + 1) // 2) * ((W + 1) // 2)
         streams = [torch.empty((w.batch, 4, w.dim, Lg), device=dev) for _ in range(sets)]
         ys = [torch.empty((4 * w.batch, w.dim, Lg), device=dev) for _ in range(sets)]
         outs = [torch.empty((w.batch, w.dim, H, W), device=dev) for _ in range(sets)]
 
+        def gather(i):
+            x, _ = inputs[i % sets]
+            vm.vm_atrous_gather(x, out=streams[i % sets])
+
+        def scan(i):
+            _, p = inputs[i % sets]
+            vm.vm_selective_scan_fwd(streams[i % sets].view(4 * w.batch, w.dim, Lg), **p, out=ys[i % sets], zoh=zoh)
+
+        def scatter(i):
+            vm.vm_atrous_scatter(ys[i % sets].view(w.batch, 4, w.dim, Lg), H, W, out=outs[i % sets])
+
         def step(i):
-            x, p = inputs[i % sets]
-            s = vm.vm_atrous_gather(x, out=streams[i % sets])
-            y = vm.vm_selective_scan_fwd(s.view(4 * w.batch, w.dim, Lg), **p, out=ys[i % sets], zoh=zoh)
-            vm.vm_atrous_scatter(y.view(w.batch, 4, w.dim, Lg), H, W, out=outs[i % sets])
+            gather(i)
+            scan(i)
+            scatter(i)
+
+        # the three launches one by one (timed separately for the per-kernel rooflines)
+        step.parts = (("gather", gather), ("scan", scan), ("scatter", scatter))
 
         # algorithmic bytes of the ES2D step: x read and y written once, plus
         # the scan's delta, B, C and parameters (the gathered u streams and the
@@ -303,6 +318,10 @@ def build_step(cfg, seed, sets, dev, zoh=False, conv="none"):
         nbytes = scan_b - 2 * streams_b + 2 * plane
         tokens = w.batch * w.dim * H * W
         slots = 4 * w.batch * w.dim * Lg * N
+        # per kernel, each kernel's own inputs read once and outputs written
+        # once (the gathered streams and the scan's output streams counted
+        # by both kernels that touch them)
+        step.part_bytes = {"gather": plane + streams_b, "scan": scan_b, "scatter": streams_b + plane}
         info = dict(workload=f"{w.name}@{H}x{W}", batch=w.batch, dim=w.dim, height=H, width=W,
                     group_len=Lg, dstate=N, kernels="gather+scan+scatter", graphable=True)
 
@@ -550,7 +569,7 @@ def main():
     if args.conv != "none" and args.config not in (0, 1, 2):
         raise SystemExit("--conv applies to configs 0-2")
     step, info, cpu_fn, nbytes, tokens, slots = build_step(args.config, args.seed, sets, dev, args.zoh,
-                                                           args.conv)
+                                                           args.conv, args.size)
     if args.zoh:
         info = dict(info, discretization="zoh")
     torch.cuda.synchronize()
@@ -582,6 +601,26 @@ def main():
     per_launch = sorted(s_.elapsed_time(e_) for s_, e_ in zip(starts, ends))
     launch_ms = sum(per_launch) / args.steps
     launch_med = per_launch[len(per_launch) // 2]
+    # multi-kernel steps with separately timed parts: each part over K
+    # steps with HIP events around every launch
+    kernels = None
+    parts = getattr(step, "parts", None)
+    if parts:
+        kernels = {}
+        for name, fn in parts:
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+            torch.cuda.synchronize()
+            for i in range(args.steps):
+                ev[i][0].record(stream)
+                fn(i)
+                ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+            nb = step.part_bytes[name]
+            kernels[name] = {"ms": round(ms, 5), "algorithmic_bytes": nb,
+                             "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
+                             "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     graph = None
     if use_graph:
         graph = torch.cuda.CUDAGraph()
@@ -654,6 +693,7 @@ def main():
         "roofline": roof,
         "roofline_other": other,
         "cpu_baseline": cpu,
+        "kernels": kernels,
         "kernel_source_hash": src_hash,
         "device": torch.cuda.get_device_name(dev),
     }

@@ -163,20 +163,36 @@ def es2d_inputs(seed, batch, channels, height, width, dstate=DSTATE, device="cpu
 
 def fastvim_inputs(seed, batch, dim, height, width, pool_axis, dstate=DSTATE, device="cpu",
                    dtype=torch.float32, perturb=False, full_resolution=False, bc_layout="token"):
-    """Per direction: full-resolution u [batch, dim, H, W], pooled-token delta
-    [batch, dim, Lp] and B, C [batch, dstate, Lp]; then z [batch, dim, H, W].
-    With full_resolution=True the directions instead carry delta [batch, dim,
-    H*W] and B, C [batch, dstate, H*W] (the unpooled scan over the flattened
-    grid, rows slow and columns fast), with the same u and z draws."""
+    """Per direction: full-resolution u [batch, dim, H, W], and delta, B, C
+    drawn at full resolution ([batch, dim, H*W] and [batch, dstate, H*W],
+    rows slow and columns fast); then z [batch, dim, H, W].  The pooled scan
+    (full_resolution=False) takes their means along the pooled axis (over W
+    for pool_axis 0, giving length H; over H for axis 1): a linear projection
+    commutes with the mean, so these are the projections of the pooled
+    tokens, and the pooled and unpooled paths run on the same seeded
+    tensors.  full_resolution=True returns delta, B, C unpooled."""
     g = generator(seed, device)
-    Lp = height if pool_axis == 0 else width
-    L = height * width if full_resolution else Lp
+    L = height * width
+
+    def pooled(t, rows):                      # [batch, rows, H*W] -> [batch, rows, Lp], fp32 mean
+        m = t.float().reshape(batch, rows, height, width).mean(dim=3 if pool_axis == 0 else 2)
+        return m.to(dtype)
+
+    def pooled_bc(t):
+        m = pooled(t, dstate)                 # [batch, dstate, Lp]
+        if bc_layout == "token":              # token-major storage, viewed as [batch, dstate, Lp]
+            return m.transpose(1, 2).contiguous().transpose(1, 2)
+        return m.contiguous()
+
     dirs = []
     for k in range(2):
         u = _normal(g, (batch, dim, height, width), device, dtype)
         delta = _normal(g, (batch, dim, L), device, dtype)
         B, C = _bc_pair(g, batch, dstate, L, device, dtype, bc_layout)
         A, D, bias = scan_params(g, dim, dstate, device, perturb and k == 1)
+        if not full_resolution:
+            delta = pooled(delta, dim).contiguous()
+            B, C = pooled_bc(B), pooled_bc(C)
         dirs.append(dict(u=u, delta=delta, A=A, B=B, C=C, D=D, delta_bias=bias))
     z = _normal(g, (batch, dim, height, width), device, dtype)
     return dirs[0], dirs[1], z

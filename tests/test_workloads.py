@@ -43,8 +43,17 @@ def test_bf16_rounding_and_shapes():
     assert x.shape == (2, 3, 5, 7) and p["delta"].shape == (8, 3, 12) and p["B"].shape == (8, 16, 12)
     f, b, z = wl.fastvim_inputs(4, 2, 3, 4, 6, pool_axis=1)
     assert f["u"].shape == (2, 3, 4, 6) and f["delta"].shape == (2, 3, 6) and f["B"].shape == (2, 16, 6)
-    f, b, z = wl.fastvim_inputs(4, 2, 3, 4, 6, pool_axis=1, full_resolution=True)
-    assert f["delta"].shape == (2, 3, 24) and f["B"].shape == (2, 16, 24)
+    F, Bk, Z = wl.fastvim_inputs(4, 2, 3, 4, 6, pool_axis=1, full_resolution=True)
+    assert F["delta"].shape == (2, 3, 24) and F["B"].shape == (2, 16, 24)
+    # the pooled inputs are the means of the same seeded full-resolution
+    # draws (over H for axis 1), and u, z and the parameters are shared
+    assert torch.equal(f["u"], F["u"]) and torch.equal(z, Z) and torch.equal(f["A"], F["A"])
+    torch.testing.assert_close(f["delta"], F["delta"].reshape(2, 3, 4, 6).mean(2), rtol=0, atol=1e-6)
+    torch.testing.assert_close(f["B"], F["B"].reshape(2, 16, 4, 6).mean(2), rtol=0, atol=1e-6)
+    torch.testing.assert_close(b["C"], Bk["C"].reshape(2, 16, 4, 6).mean(2), rtol=0, atol=1e-6)
+    assert f["B"].stride(1) == 1                       # token-major storage, as the unpooled B
+    f0, _, _ = wl.fastvim_inputs(4, 2, 3, 4, 6, pool_axis=0)
+    torch.testing.assert_close(f0["delta"], F["delta"].reshape(2, 3, 4, 6).mean(3), rtol=0, atol=1e-6)
 
 
 def test_ss2d_and_conv_generators():
