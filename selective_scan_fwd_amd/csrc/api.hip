@@ -221,15 +221,14 @@ int launch_bidir(vmk::ScanArgs &a, bool bf16, Scratch &ws, hipStream_t s) {
 // is known: the kernel, then the reduction of its partial sums into g.
 struct BwdScratch {
   float *ck = nullptr, *pA = nullptr, *pD = nullptr, *pbias = nullptr, *pB = nullptr, *pC = nullptr;
-  int get(Scratch &ws, int64_t batch, int64_t dim, int64_t L, int64_t dstate) {
+  int get(Scratch &ws, int64_t batch, int64_t dim, int64_t L) {
     int st = VM_OK;
-    const int64_t nrb = (dim + 15) / 16;
-    ck = ws.get(batch * dim * vmk::scan_bwd_tiles(L) * 16, &st);
+    ck = ws.get(vmk::scan_bwd_ck_floats(batch, dim, L), &st);
     pA = ws.get(batch * dim * 16, &st);
     pD = ws.get(batch * dim, &st);
     pbias = ws.get(batch * dim, &st);
-    pB = ws.get(nrb * batch * dstate * L, &st);
-    pC = ws.get(nrb * batch * dstate * L, &st);
+    pB = ws.get(vmk::scan_bwd_tiled_floats(batch, dim, L), &st);
+    pC = ws.get(vmk::scan_bwd_tiled_floats(batch, dim, L), &st);
     return st;
   }
 };
@@ -238,7 +237,9 @@ vmk::BwdArgs bwd_args(const vm_scan_dir *p, const float *dy, const vm_scan_grad 
                       int64_t batch, int64_t dim, int64_t L, int64_t dstate, int options, int reverse,
                       bool ck_ready, Scratch &ws, hipStream_t s, int *st) {
   vmk::BwdArgs a = {};
+  // the forward kernel that stores the checkpoints writes dy tile-major
   a.ck_ready = ck_ready ? 1 : 0;
+  a.dy_tiled = ck_ready ? 1 : 0;
   a.dir = resolve_dir(p, batch, dstate, L, false, ws, s, st);
   a.dy = dy;
   a.du = g->du;
@@ -768,7 +769,7 @@ int vm_pool_scan_repeat_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, cons
   float *dyp = ws.get(pooled, &st);
   float *dubar = ws.get(pooled, &st);
   BwdScratch bs;
-  if (st == VM_OK) st = bs.get(ws, batch, dim, Lp, dstate);
+  if (st == VM_OK) st = bs.get(ws, batch, dim, Lp);
   vmk::ScanArgs a = {};                 // the pooled forward scan (ungated, scale 1)
   a.out = y;
   a.batch = batch;
@@ -939,7 +940,7 @@ int vm_ss2d_scan_bwd(const vm_scan_dir *dirs, const void *u, const void *z, cons
   float *dus[4];
   for (int k = 0; k < 4; ++k) dus[k] = ws.get(tok, &st);
   BwdScratch bs[4];
-  for (int k = 0; k < 4 && st == VM_OK; ++k) st = bs[k].get(ws, batch, dim, L, dstate);
+  for (int k = 0; k < 4 && st == VM_OK; ++k) st = bs[k].get(ws, batch, dim, L);
   vmk::ScanArgs a[2] = {};
   for (int pass = 0; pass < 2 && z != nullptr && st == VM_OK; ++pass) {
     a[pass].out = pass == 0 ? yr : yc;
@@ -1035,7 +1036,7 @@ int vm_selective_scan_bwd(const vm_scan_dir *p, const void *z, const void *dout,
   Scratch ws(s);
   // temporary memory first, so that a failed allocation launches nothing
   BwdScratch bs;
-  st = bs.get(ws, batch, dim, seqlen, dstate);
+  st = bs.get(ws, batch, dim, seqlen);
   float *y = z != nullptr ? ws.get(tok, &st) : nullptr;
   float *dyb = z != nullptr ? ws.get(tok, &st) : nullptr;
   ConvBwd cv;
@@ -1117,17 +1118,17 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
   const bool fuse = z != nullptr &&
                     vmk::plan_scan(batch, dim, seqlen, static_cast<int>(dstate), 2, false).xmode ==
                         vmk::kXLds;
-  float *dy = ws.get(tok, &st);
+  float *dy = ws.get(fuse ? vmk::scan_bwd_tiled_floats(batch, dim, seqlen) : tok, &st);
   float *y = z != nullptr && !fuse ? ws.get(tok, &st) : nullptr;
   // per direction: one backward launch for both; with ZOH (launched one
   // direction at a time) the second reuses the first's partial sums
   const bool zoh = (options & VM_ZOH) != 0;
   BwdScratch bs[2];
-  st = bs[0].get(ws, batch, dim, seqlen, dstate);
-  if (st == VM_OK && !zoh) st = bs[1].get(ws, batch, dim, seqlen, dstate);
+  st = bs[0].get(ws, batch, dim, seqlen);
+  if (st == VM_OK && !zoh) st = bs[1].get(ws, batch, dim, seqlen);
   if (st == VM_OK && zoh) {
     bs[1] = bs[0];
-    bs[1].ck = ws.get(batch * dim * vmk::scan_bwd_tiles(seqlen) * 16, &st);
+    bs[1].ck = ws.get(vmk::scan_bwd_ck_floats(batch, dim, seqlen), &st);
   }
   ConvBwd cvf, cvb;
   if (st == VM_OK && conv) st = cvf.get(ws, tok, batch, dim);

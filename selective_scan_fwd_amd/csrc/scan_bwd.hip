@@ -58,14 +58,18 @@ struct BwdLayout {
   // rows of a wave (state groups n / 4).
   static constexpr int RSTR = kR + 4;
   static constexpr int RED = 16 * T * RSTR + 64;
-  static constexpr int TOTAL = AREA + RED;
+  // du, ddelta of the last RING_T steps per row (slot t mod RING_T), until
+  // their 128-byte lines are complete and go out whole.
+  static constexpr int RING_T = 40;
+  static constexpr int RING = 2 * kR * RING_T;
+  static constexpr int TOTAL = AREA + RED + RING;
 };
 
 // The tile's states and decays stay in registers (64 VGPRs with 8-step
 // tiles; 4-step tiles fit more workgroups but measured 1.6x slower for their
 // per-tile reductions), which sets the register budget at two waves per
-// SIMD; the LDS area (15 KB) is small enough not to lower that.  The ZOH
-// adjoint's extra terms need about 300 registers: one wave per SIMD.
+// SIMD; the LDS area (under 20 KB, eight waves per CU) does not lower that.
+// The ZOH adjoint's extra terms need about 300 registers: one wave per SIMD.
 __device__ __forceinline__ const BwdArgs &group_entry(const BwdArgs &a, int) { return a; }
 __device__ __forceinline__ const BwdArgs &group_entry(const BwdGroup &g, int k) { return g.a[k]; }
 
@@ -81,6 +85,8 @@ scan_bwd_kernel(const Arg arg) {
   float *const bcs = prep + Lay::PREP;            // [T][32]
   float *const part = smem;                       // [2][64][QSTR], over the staging area
   float *const red = smem + Lay::AREA;            // [16][T][R], padded rows
+  float *const ring = red + Lay::RED;             // [2][R][RING_T]
+  static_assert(Lay::RING_T % T == 0 && Lay::RING_T >= 32 + T - 1, "ring");
 
   // a group's grid covers its directions one after another
   const int64_t dim = group_entry(arg, 0).dim;
@@ -109,7 +115,9 @@ scan_bwd_kernel(const Arg arg) {
   const uint32_t slab = static_cast<uint32_t>(rows) * static_cast<uint32_t>(L) * 4u;
   const Rsrc rU = make_rsrc(static_cast<const float *>(P.u) + rowbase, slab);
   const Rsrc rDl = make_rsrc(static_cast<const float *>(P.delta) + rowbase, slab);
-  const Rsrc rDy = make_rsrc(p.dy + rowbase, slab);
+  const Rsrc rDy = p.dy_tiled ? make_rsrc(p.dy + (static_cast<int64_t>(b) * nrb + rb) * nt * 16 * T,
+                                          static_cast<uint32_t>(nt * 16 * T) * 4u)
+                             : make_rsrc(p.dy + rowbase, slab);
   const Rsrc rDu = make_rsrc(p.du + rowbase, slab);
   const Rsrc rDd = make_rsrc(p.ddelta + rowbase, slab);
   const uint32_t bcext = (static_cast<uint32_t>(dstate - 1) * static_cast<uint32_t>(P.bsn) +
@@ -121,12 +129,13 @@ scan_bwd_kernel(const Arg arg) {
   const Rsrc rDp = make_rsrc(P.D + d0, static_cast<uint32_t>(rows) * 4u);
   const Rsrc rBias = make_rsrc(P.bias != nullptr ? P.bias + d0 : nullptr,
                                P.bias != nullptr ? static_cast<uint32_t>(rows) * 4u : 0u);
-  // checkpoints of this block's rows: [row][tile][16 states]
-  const Rsrc rCk = make_rsrc(p.ck + (static_cast<int64_t>(b) * dim + d0) * nt * 16,
-                             static_cast<uint32_t>(rows * nt) * 64u);
-  // partial sums over channels of this block: [n][L] per quantity
-  const int64_t pbc = (static_cast<int64_t>(rb) * p.batch + b) * dstate * L;
-  const uint32_t pbc_bytes = static_cast<uint32_t>(dstate * L) * 4u;
+  // checkpoints of this row block: [tile][16 channels][16 states]
+  const Rsrc rCk = make_rsrc(p.ck + (static_cast<int64_t>(b) * nrb + rb) * nt * 256,
+                             static_cast<uint32_t>(nt) * 1024u);
+  // partial sums over channels of this block: [tile][16 states][T steps]
+  // per quantity (positions past L and states past dstate hold zeros)
+  const int64_t pbc = (static_cast<int64_t>(rb) * p.batch + b) * nt * 16 * T;
+  const uint32_t pbc_bytes = static_cast<uint32_t>(nt * 16 * T) * 4u;
   const Rsrc rPB = make_rsrc(p.pB + pbc, pbc_bytes);
   const Rsrc rPC = make_rsrc(p.pC + pbc, pbc_bytes);
 
@@ -147,17 +156,100 @@ scan_bwd_kernel(const Arg arg) {
   const int sq = lane % T;
   const int tq = rev ? T - 1 - sq : sq;
   int srow[PE];
-  uint32_t ob[PE];
+  uint32_t ob[PE], oy[PE];
   float sbias[PE], sD[PE], accD[PE], accB[PE];
 #pragma unroll
   for (int i = 0; i < PE; ++i) {
     srow[i] = lane / T + i * (64 / T);
     ob[i] = (static_cast<uint32_t>(srow[i]) * static_cast<uint32_t>(L) + tq) * 4u;
+    oy[i] = p.dy_tiled ? static_cast<uint32_t>(srow[i] * T + tq) * 4u : ob[i];
     sbias[i] = bload<float>(rBias, static_cast<uint32_t>(srow[i]) * 4u);
     sD[i] = bload<float>(rDp, static_cast<uint32_t>(srow[i]) * 4u);
     accD[i] = 0.0f;
     accB[i] = 0.0f;
   }
+  // Output lines.  A row's element t sits at element offset e0 + row L + t
+  // of du (ddelta is taken to share its alignment); line boundaries are where
+  // that offset is a multiple of 32.  A tile's du and ddelta go into the ring;
+  // every line of a row whose steps are all done then goes out in one burst
+  // (a line stored piecewise, one tile apart, is fetched and written back
+  // several times).  The ZOH variant, whose registers are tight at one wave
+  // per SIMD, stores directly.  A row's items are the lines between its
+  // boundaries and the partial lines at its two ends.  Per row (wave-uniform): tb0, its
+  // first boundary; the tiles j that complete one of its lines are those
+  // with j mod 4 == its class; and such an item starts at 8 j + d (visiting
+  // backward in t) or ends at 8 j + 1 + d (visiting forward in t, rev).
+  static_assert(T == 8, "four tiles per 128-byte line");
+  const uint32_t e0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p.du) >> 2) +
+                      static_cast<uint32_t>(rowbase);
+  uint32_t cls_mask[4] = {0u, 0u, 0u, 0u};
+  uint64_t dtab = 0;                              // d per row, 3 bits each
+#pragma unroll
+  for (int rr = 0; rr < kR; ++rr) {
+    const int tb0 = static_cast<int>((32u - ((e0 + static_cast<uint32_t>(rr) * static_cast<uint32_t>(L)) & 31u)) & 31u);
+    const int key = rev ? ((tb0 - 1) & 31) : tb0;
+    cls_mask[key >> 3] |= 1u << rr;
+    dtab |= static_cast<uint64_t>(key & 7) << (3 * rr);
+  }
+  // Stores the item [lo, hi) of row rr (lanes 32 h .. 32 h + 31) from the ring.
+  auto flush_item = [&](int rr, int lo, int hi) {
+    const int t = lo + (lane & 31);
+    const int s0 = lo % Lay::RING_T + (lane & 31);
+    const int slot = s0 >= Lay::RING_T ? s0 - Lay::RING_T : s0;
+    const float vu = ring[rr * Lay::RING_T + slot];
+    const float vd = ring[(kR + rr) * Lay::RING_T + slot];
+    const uint32_t o = pin_u(t < hi ? (static_cast<uint32_t>(rr) * static_cast<uint32_t>(L) +
+                                       static_cast<uint32_t>(t)) * 4u
+                                    : kOob);
+    bstore<float>(rDu, o, vu);
+    bstore<float>(rDd, o, vd);
+  };
+  auto flush_lines = [&](int j, bool last) {
+    const int w = j * T;
+    uint32_t m = cls_mask[j & 3];
+    while (m != 0) {                              // two rows per pass, 32 lanes each
+      int rr[2], lo[2], hi[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        rr[h] = m != 0 ? __builtin_ctz(m) : 0;
+        const int d = static_cast<int>((dtab >> (3 * rr[h])) & 7u);
+        if (rev) {
+          hi[h] = w + 1 + d;
+          lo[h] = hi[h] - 32 > 0 ? hi[h] - 32 : 0;
+          if (m == 0 || hi[h] > L) hi[h] = lo[h];         // (the tail item takes it)
+        } else {
+          lo[h] = w + d;
+          hi[h] = lo[h] + 32 < L ? lo[h] + 32 : L;
+          if (m == 0) hi[h] = lo[h];
+        }
+        m &= m - 1;
+      }
+      const bool h1 = lane >= 32;
+      flush_item(h1 ? rr[1] : rr[0], h1 ? lo[1] : lo[0], h1 ? hi[1] : hi[0]);
+    }
+    if (last) {                                   // the partial line at the far end of every row
+#pragma unroll 1
+      for (int rr = 0; rr < kR; rr += 2) {
+        int lo2[2], hi2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int tb0 = static_cast<int>(
+              (32u - ((e0 + static_cast<uint32_t>(rr + h) * static_cast<uint32_t>(L)) & 31u)) & 31u);
+          if (rev) {
+            const int tl = L - ((L - tb0) & 31);  // last boundary <= L
+            lo2[h] = tl > 0 ? tl : 0;
+            hi2[h] = L;
+          } else {
+            lo2[h] = 0;
+            hi2[h] = tb0 < L ? tb0 : L;
+          }
+        }
+        const bool h1 = lane >= 32;
+        flush_item(rr + (h1 ? 1 : 0), h1 ? lo2[1] : lo2[0], h1 ? hi2[1] : hi2[0]);
+      }
+    }
+  };
+
   const int n_bc = lane % 16;
   uint32_t bo[BQ];
 #pragma unroll
@@ -176,7 +268,8 @@ scan_bwd_kernel(const Arg arg) {
   // latency overlaps the current tile's arithmetic).  Steps past L and rows
   // past dim read 0.
   float lu[PE], ld[PE], ly[PE], lb[BQ], lc[BQ], lk[kNS];
-  const uint32_t ck_lane = static_cast<uint32_t>(r * nt) * 64u + static_cast<uint32_t>(n0) * 4u;
+  const uint32_t ck_lane = static_cast<uint32_t>(r * 16 + n0) * 4u;
+  const uint32_t dy_tile_bytes = static_cast<uint32_t>(p.dy_tiled ? 16 * T : T) * 4u;
   auto stage_load = [&](int j, bool pass2) {
     const int jT = j * T;
     const bool in_seq = tq < L - jT;
@@ -185,7 +278,8 @@ scan_bwd_kernel(const Arg arg) {
       const uint32_t o = pin_u(in_seq ? ob[i] + static_cast<uint32_t>(jT) * 4u : kOob);
       lu[i] = bload<float>(rU, o);
       ld[i] = bload<float>(rDl, o);
-      ly[i] = pass2 ? bload<float>(rDy, o) : 0.0f;
+      ly[i] = pass2 ? bload<float>(rDy, pin_u(in_seq ? oy[i] + static_cast<uint32_t>(j) * dy_tile_bytes : kOob))
+                    : 0.0f;
     }
     const uint32_t tb = static_cast<uint32_t>(jT) * bst_bytes;
 #pragma unroll
@@ -194,7 +288,7 @@ scan_bwd_kernel(const Arg arg) {
       lc[i] = pass2 ? bload<float>(rC, bo[i] + tb) : 0.0f;
     }
     if (pass2) {
-      bload4(rCk, ck_lane + static_cast<uint32_t>(j) * 64u, lk);
+      bload4(rCk, ck_lane + static_cast<uint32_t>(j) * 1024u, lk);
     } else {
 #pragma unroll
       for (int jn = 0; jn < kNS; ++jn) lk[jn] = 0.0f;
@@ -235,7 +329,7 @@ scan_bwd_kernel(const Arg arg) {
   if (nt1 > 0) stage_load(tile_of(0), false);
   for (int k = 0; k < nt1; ++k) {
     const int j = tile_of(k);
-    bstore4(rCk, ck_lane + static_cast<uint32_t>(j) * 64u, h);
+    bstore4(rCk, ck_lane + static_cast<uint32_t>(j) * 1024u, h);
     wave_lds_fence();                    // the previous tile's staged values are read
     stage_store();
     wave_lds_fence();
@@ -330,8 +424,7 @@ scan_bwd_kernel(const Arg arg) {
           const float4 x4 = src[v];
           sum += (x4.x + x4.y) + (x4.z + x4.w);
         }
-        const int t = jT + (rev ? T - 1 - q : q);
-        bstore<float>(dst, pin_u(t < L && n < dstate ? static_cast<uint32_t>(n * L + t) * 4u : kOob), sum);
+        bstore<float>(dst, static_cast<uint32_t>((j * 16 + n) * T + (rev ? T - 1 - q : q)) * 4u, sum);
       }
     };
 #pragma unroll
@@ -383,7 +476,6 @@ scan_bwd_kernel(const Arg arg) {
     }
     // per element: du, ddelta (the four state groups of the channel summed)
     wave_lds_fence();
-    const bool in_seq = tq < L - jT;
 #pragma unroll
     for (int i = 0; i < PE; ++i) {
       float gB = 0.0f, gA = 0.0f;
@@ -397,11 +489,21 @@ scan_bwd_kernel(const Arg arg) {
       const float ddt = ZOH ? gA : __builtin_fmaf(eu[i], gB, gA);
       const float sig = hw_rcp(1.0f + hw_exp2(-ex[i] * kLog2e));
       const float dd = sp_on ? ddt * sig : ddt;
-      const uint32_t o = pin_u(in_seq ? ob[i] + static_cast<uint32_t>(jT) * 4u : kOob);
-      bstore<float>(rDu, o, du);
-      bstore<float>(rDd, o, dd);
+      if constexpr (ZOH) {
+        const uint32_t o = pin_u(tq < L - jT ? ob[i] + static_cast<uint32_t>(jT) * 4u : kOob);
+        bstore<float>(rDu, o, du);
+        bstore<float>(rDd, o, dd);
+      } else {
+        const int slot = (j % (Lay::RING_T / T)) * T + tq;   // t mod RING_T
+        ring[srow[i] * Lay::RING_T + slot] = du;
+        ring[(kR + srow[i]) * Lay::RING_T + slot] = dd;
+      }
       accD[i] = __builtin_fmaf(edy[i], eu[i], accD[i]);
       accB[i] += dd;
+    }
+    if constexpr (!ZOH) {
+      wave_lds_fence();
+      flush_lines(j, k == 0);
     }
     // dB: this block's sum over its 16 channels, per (n, step)
     reduce_red(rPB);
@@ -433,27 +535,37 @@ scan_bwd_kernel(const Arg arg) {
   }
 }
 
-// Sums of the partials over channel blocks: dB, dC [batch, dstate, L].
+// Sums of the partials over channel blocks: dB, dC [batch, dstate, L].  The
+// partials are [nrb][batch][tiles][16][T]; element e of one block's slab is
+// read in storage order (whole lines) and lands at (b, n, t).
 __global__ void __launch_bounds__(256)
 reduce_bc_kernel(const float *__restrict__ pB, const float *__restrict__ pC, float *dB, float *dC,
-                 int64_t nbc, int nrb) {
+                 int64_t slab, int nrb, int nt, int L, int dstate) {
+  constexpr int T = kBwdTile;
+  const int64_t per_b = static_cast<int64_t>(nt) * 16 * T;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < nbc; e += stride) {
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < slab; e += stride) {
     float sb[4] = {0.f, 0.f, 0.f, 0.f}, sc[4] = {0.f, 0.f, 0.f, 0.f};
     int k = 0;
     for (; k + 4 <= nrb; k += 4) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        sb[u] += pB[(k + u) * nbc + e];
-        sc[u] += pC[(k + u) * nbc + e];
+        sb[u] += pB[(k + u) * slab + e];
+        sc[u] += pC[(k + u) * slab + e];
       }
     }
     for (; k < nrb; ++k) {
-      sb[0] += pB[k * nbc + e];
-      sc[0] += pC[k * nbc + e];
+      sb[0] += pB[k * slab + e];
+      sc[0] += pC[k * slab + e];
     }
-    dB[e] = (sb[0] + sb[1]) + (sb[2] + sb[3]);
-    dC[e] = (sc[0] + sc[1]) + (sc[2] + sc[3]);
+    const int64_t b = e / per_b;
+    const int rem = static_cast<int>(e - b * per_b);
+    const int j = rem / (16 * T), n = (rem / T) % 16, t = j * T + rem % T;
+    if (n < dstate && t < L) {
+      const int64_t o = (b * dstate + n) * L + t;
+      dB[o] = (sb[0] + sb[1]) + (sb[2] + sb[3]);
+      dC[o] = (sc[0] + sc[1]) + (sc[2] + sc[3]);
+    }
   }
 }
 
@@ -534,13 +646,19 @@ unsigned grid_for(int64_t n) {
 }  // namespace
 
 int64_t scan_bwd_tiles(int64_t L) { return (L + kBwdTile - 1) / kBwdTile; }
+int64_t scan_bwd_ck_floats(int64_t batch, int64_t dim, int64_t L) {
+  return batch * ((dim + kR - 1) / kR) * scan_bwd_tiles(L) * 256;
+}
+int64_t scan_bwd_tiled_floats(int64_t batch, int64_t dim, int64_t L) {
+  return ((dim + kR - 1) / kR) * batch * scan_bwd_tiles(L) * 16 * kBwdTile;
+}
 
 hipError_t launch_scan_bwd_group(const BwdGroup &g, hipStream_t s) {
   if (g.n < 1 || g.n > kBwdGroupMax) return hipErrorInvalidValue;
   const BwdArgs &a = g.a[0];
   for (int k = 1; k < g.n; ++k)
     if (g.a[k].batch != a.batch || g.a[k].dim != a.dim || g.a[k].L != a.L || g.a[k].dstate != a.dstate ||
-        g.a[k].zoh != a.zoh || g.a[k].ck_ready != a.ck_ready)
+        g.a[k].zoh != a.zoh || g.a[k].ck_ready != a.ck_ready || g.a[k].dy_tiled != a.dy_tiled)
       return hipErrorInvalidValue;
   const int64_t nrb = (a.dim + kR - 1) / kR;
   const int64_t blocks = a.batch * nrb;
@@ -581,9 +699,10 @@ hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s) {
 hipError_t launch_scan_bwd_reduce(const BwdArgs &a, float *dA, float *dB, float *dC, float *dD,
                                   float *dbias, hipStream_t s) {
   const int nrb = static_cast<int>((a.dim + kR - 1) / kR);
-  const int64_t nbc = a.batch * a.dstate * a.L;
-  hipLaunchKernelGGL(reduce_bc_kernel, dim3(grid_for(nbc)), dim3(256), 0, s, a.pB, a.pC, dB, dC, nbc,
-                     nrb);
+  const int nt = static_cast<int>(scan_bwd_tiles(a.L));
+  const int64_t slab = a.batch * nt * 16 * kBwdTile;
+  hipLaunchKernelGGL(reduce_bc_kernel, dim3(grid_for(slab)), dim3(256), 0, s, a.pB, a.pC, dB, dC, slab,
+                     nrb, nt, static_cast<int>(a.L), a.dstate);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(reduce_param_kernel, dim3(static_cast<unsigned>(a.dim)), dim3(256), 0, s, a.pA, dA,

@@ -237,14 +237,18 @@ scan_kernel(const ScanArgs p) {
   const Rsrc rCb = make_rsrc(CONV && P.cb != nullptr ? P.cb + d0 : nullptr,
                              CONV && P.cb != nullptr ? static_cast<uint32_t>(rows) * 4u : 0u);
   // Backward preparation (CK): the state entering each tile, as the backward
-  // kernel's first pass would store it (rows past dim fall outside the
-  // resource), and the gate's backward in place of out.
-  const Rsrc rCk = make_rsrc(CK ? p.ck[dw] + (static_cast<int64_t>(b) * dim + d0) * nt * 16 : nullptr,
-                             CK ? static_cast<uint32_t>(rows * nt) * 64u : 0u);
-  const uint32_t ck_lane = static_cast<uint32_t>(r * nt) * 64u + static_cast<uint32_t>(sp * (16 / SPLIT)) * 4u;
+  // kernel's first pass would store it, and the gate's backward in place of
+  // out.  Checkpoints are tile-major per row block, [tile][16 channels][16
+  // states], so that a wave's checkpoints of one tile are one contiguous
+  // kilobyte (a row block past the end has none; channels past dim store
+  // zeros).
+  const Rsrc rCk = make_rsrc(CK ? p.ck[dw] + (static_cast<int64_t>(b) * nrb + d0 / R) * nt * 256 : nullptr,
+                             CK && valid ? static_cast<uint32_t>(nt) * 1024u : 0u);
+  const uint32_t ck_lane = static_cast<uint32_t>(r * 16 + sp * (16 / SPLIT)) * 4u;
   const Rsrc rGz = make_rsrc(CK ? p.gz + rowbase : nullptr, CK ? slab : 0u);
   const Rsrc rDo = make_rsrc(CK ? p.dout + rowbase : nullptr, CK ? slab : 0u);
-  const Rsrc rDy = make_rsrc(CK ? p.dy + rowbase : nullptr, CK ? slab : 0u);
+  const Rsrc rDy = make_rsrc(CK ? p.dy + (static_cast<int64_t>(b) * nrb + d0 / R) * nt * 16 * T : nullptr,
+                             CK && valid ? static_cast<uint32_t>(nt * 16 * T) * 4u : 0u);
   const Rsrc rDz = make_rsrc(CK ? p.dz + rowbase : nullptr, CK ? slab : 0u);
   float A2[NS], iA[NS], h[NS];
 #pragma unroll
@@ -476,7 +480,7 @@ scan_kernel(const ScanArgs p) {
     stage_load(k + NB < nt ? k + NB : nt - 1, slot);
     if constexpr (CK) {
       static_assert(NS == 4, "a lane's checkpoint is one 16-byte store");
-      bstore4(rCk, ck_lane + static_cast<uint32_t>(tile_of(k)) * 64u, h);
+      bstore4(rCk, ck_lane + static_cast<uint32_t>(tile_of(k)) * 1024u, h);
     }
     wave_lds_fence();                    // staged tile k read back before its partials overwrite it
     do_scan();
@@ -561,9 +565,11 @@ scan_kernel(const ScanArgs p) {
     int fr = tid / L, ft = tid % L;
     for (int f0 = tid; f0 < n; f0 += U * NT) {
       float v[U], gzv[U], gdo[U];
+      uint32_t oty[U];                       // (CK) tile-major offset of dy
 #pragma unroll
       for (int u = 0; u < U; ++u) {          // reads first, so their latency overlaps
         v[u] = xlds[(fr < R ? fr : R - 1) * XS + ft];
+        if constexpr (CK) oty[u] = static_cast<uint32_t>(((ft / T) * 16 + fr) * T + ft % T) * 4u;
         ft += NT;
         while (ft >= L) { ft -= L; ++fr; }
         if constexpr (CK) {
@@ -583,7 +589,7 @@ scan_kernel(const ScanArgs p) {
           const float zv = pin(gzv[u]);
           const float g = p.gscale * pin(gdo[u]);
           const float sg = hw_rcp(1.0f + hw_exp2(-zv * kLog2e));
-          bstore<float>(rDy, o, g * zv * sg);
+          bstore<float>(rDy, f < n ? oty[u] : kOob, g * zv * sg);
           bstore<float>(rDz, o, g * v[u] * (sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f)));
         } else {
           bstore<Tin>(rO, pin_u(f < n ? static_cast<uint32_t>(f) * ES : kOob), v[u]);

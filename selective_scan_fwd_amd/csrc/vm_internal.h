@@ -83,9 +83,10 @@ struct ScanArgs {
   float *xglobal;       // fp32 exchange rows (long bidirectional), row stride xstride
   int64_t xstride;
   // Backward preparation (kOptBwdPrep): per direction, the state at every
-  // 8-step tile start, [batch * dim][ceil(L / 8)][16] fp32; and in place of
+  // 8-step tile start (checkpoints laid out as BwdArgs::ck); and in place of
   // out, the gate's backward from the ungated y: dy = gscale dout SiLU(z),
-  // dz = gscale dout y SiLU'(z) (all [batch, dim, L] fp32).
+  // tile-major as BwdArgs::dy with dy_tiled, and dz = gscale dout y SiLU'(z)
+  // ([batch, dim, L]), both fp32.
   float *ck[2];
   const float *gz, *dout;
   float *dy, *dz;
@@ -132,11 +133,16 @@ hipError_t launch_scan(const ScanPlan &plan, const ScanArgs &args, bool bf16, hi
 hipError_t launch_scan_chunked(const ScanPlan &plan, const ScanArgs &args, bool bf16, hipStream_t s);
 
 // ---------------------------------------------------------------- backward
-// One direction, fp32.  dy: gradient of the ungated scan output.  The kernel
+// One direction, fp32.  dy: gradient of the ungated scan output, [batch,
+// dim, L], or with dy_tiled [batch][nrb][tiles][16 channels][8 steps] (one
+// contiguous 512-byte block per row block and tile; positions past L are
+// never read).  The kernel
 // writes du and ddelta per element and partial sums that the reduce kernel
-// adds: pB, pC [nrb][batch][dstate][L] (per block of 16 channels), pA
-// [batch][dim][16], pD, pbias [batch][dim].  ck: [batch * dim][tiles][16]
-// state checkpoints (scratch).
+// adds: pB, pC [nrb][batch][tiles][16 states][8 steps] (per block of 16
+// channels, one contiguous 512-byte block per tile), pA [batch][dim][16],
+// pD, pbias [batch][dim].  ck: state checkpoints (scratch),
+// [batch][nrb][tiles][16 channels][16 states], so that one wave's
+// checkpoints of one tile are one contiguous kilobyte.
 struct BwdArgs {
   DirPtrs dir;
   const float *dy;
@@ -148,9 +154,14 @@ struct BwdArgs {
   int zoh;              // zero-order-hold write
   int reverse;
   int ck_ready;         // ck already holds the checkpoints (the forward kernel wrote them)
+  int dy_tiled;         // dy is tile-major (the forward kernel wrote it)
 };
 constexpr int kBwdTile = 8;
 int64_t scan_bwd_tiles(int64_t L);
+// Floats of the checkpoint buffer, and of a tile-major buffer (pB, pC, a
+// tiled dy).
+int64_t scan_bwd_ck_floats(int64_t batch, int64_t dim, int64_t L);
+int64_t scan_bwd_tiled_floats(int64_t batch, int64_t dim, int64_t L);
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s);
 // Up to four directions' backward kernels in one launch (one grid over all
 // of them): the same batch, dim, L and dstate, the same zoh and ck_ready.
