@@ -27,7 +27,11 @@
 //    computed once per element.  B and C of a step are held one value per
 //    lane of each 16-lane row (the row is one state group) and reach the
 //    other lanes as DPP row broadcasts folded into the multiply-adds, so they
-//    cost one 4-byte LDS read per lane per step.
+//    cost one 4-byte LDS read per lane per step.  Long bidirectional
+//    sequences with few rows split a channel's states over 8 lanes instead
+//    (two per lane, eight channels per wave, twice the waves); a 16-lane row
+//    then holds two state groups, and each lane reads its own B and C pair
+//    as one 16-byte LDS value per step.
 //  * Latency is hidden by software pipelining in registers: the global loads
 //    of tile k+2 are issued at the start of iteration k.
 //  * Bidirectional: phase 1 has the forward wave on the first ceil(nt/2)
@@ -95,6 +99,25 @@ __device__ __forceinline__ void state_step_zoh(float (&h)[NS], const float (&A2)
   }
 }
 
+// One step of a lane's two states (eight-lane state split), with the lane's
+// own B and C values (b4 = B_0, B_1, C_0, C_1, read from LDS): there are
+// eight state groups per wave, so a 16-lane row holds two of them and a row
+// broadcast cannot serve both.  With ZOH, dtu is u and the write is k u B.
+template <bool ZOH>
+__device__ __forceinline__ void state_step2(float (&h)[2], const float (&A2)[2], const float (&iA)[2],
+                                            float dt, float dtu, const float4 &b4, float &y) {
+  const float x0 = dt * A2[0], x1 = dt * A2[1];
+  const float a0 = hw_exp2(x0), a1 = hw_exp2(x1);
+  float w0 = dtu * b4.x, w1 = dtu * b4.y;
+  if constexpr (ZOH) {
+    w0 *= zoh_coef(dt, x0, a0, iA[0]);
+    w1 *= zoh_coef(dt, x1, a1, iA[1]);
+  }
+  h[0] = __builtin_fmaf(a0, h[0], w0);
+  h[1] = __builtin_fmaf(a1, h[1], w1);
+  y = __builtin_fmaf(b4.w, h[1], b4.z * h[0]);
+}
+
 // Calls f(std::integral_constant<int, I>()) for I = 0 .. N-1 in order.
 template <typename F, int... I>
 __device__ __forceinline__ void for_slots_impl(F &&f, std::integer_sequence<int, I...>) {
@@ -118,17 +141,23 @@ __device__ __forceinline__ void lds_barrier() {
 // sums PART from the scan of a tile to their read in the combine.  In a
 // wave's program order these never overlap (scan k, read partials k, stage
 // k+1, read back k+1), so PART shares the area's start with PREP.
+// With the eight-lane state split (R = 8) the scan reads B and C from LDS
+// step by step while it writes its partials, so PART gets its own place.
 template <int T, int R, bool CV>
 struct Layout {
   static constexpr int PSTR = 2 * T + 2;                  // (dt, dt u) per row; PSTR/2 odd
   static constexpr int QSTR = T + 1;                      // partials per lane, odd
   static constexpr int PREP = R * PSTR;
-  static constexpr int BC = 32 * T;                       // B in slots 0..15, C in 16..31
+  static constexpr int BC = 32 * T;                       // per step: B 0..15, C 16..31 (R = 8:
+                                                          // per state pair n/2, B B C C)
   static constexpr int PART = 64 * QSTR;
   static constexpr int XH = T + 4;                        // conv input row: 3 halo, T, 1 spare
   static constexpr int CX = CV ? R * XH : 0;
   static constexpr int STAGE = PREP + BC + CX;
-  static constexpr int WAVE = STAGE > PART ? STAGE : PART;  // floats per wave
+  static constexpr bool OVERLAY = R != 8;
+  static constexpr int PART_AT = OVERLAY ? 0 : (STAGE + 3) / 4 * 4;
+  static constexpr int WAVE = OVERLAY ? (STAGE > PART ? STAGE : PART) : PART_AT + PART;  // floats per wave
+  static_assert(WAVE % 4 == 0 || OVERLAY, "16-byte B/C reads of the second wave stay aligned");
   static_assert(WAVE % 2 == 0, "float2 staging of the second wave stays 8-byte aligned");
 };
 
@@ -148,7 +177,8 @@ __host__ __device__ inline int xchg_stride(int64_t n, int T) {
 // carries the same number of waves.
 template <typename Tin, int SPLIT, int DIRS, int XMODE, int T, int OPT>
 __global__ void __launch_bounds__(DIRS == 2 ? 256 : 64)
-__attribute__((amdgpu_waves_per_eu(T == 16 ? 2 : ((OPT & kOptConv) != 0 ? 3 : 4))))
+__attribute__((amdgpu_waves_per_eu(T == 16 ? (SPLIT == 8 && OPT != (kOptZoh | kOptConv) ? 3 : 2)
+                                                     : ((OPT & kOptConv) != 0 ? 3 : 4))))
 scan_kernel(const ScanArgs p) {
   constexpr bool ZOH = (OPT & kOptZoh) != 0;
   constexpr bool CONV = (OPT & kOptConv) != 0;
@@ -160,7 +190,8 @@ scan_kernel(const ScanArgs p) {
   constexpr uint32_t ES = sizeof(Tin);
   constexpr int NB = 3;                          // tiles in flight (prefetch distance)
   using Lay = Layout<T, R, CONV>;
-  static_assert(NS >= 4 && NS <= 8 && R % 16 == 0 && T % 4 == 0 && (R * T) % 64 == 0, "shape");
+  static_assert(((NS >= 4 && NS <= 8 && R % 16 == 0) || (NS == 2 && R == 8)) && T % 4 == 0 &&
+                    (R * T) % 64 == 0, "shape");
   static_assert(DIRS == 1 ? XMODE == kXNone : XMODE != kXNone, "mode");
   static_assert(!CK || (T == kBwdTile && XMODE == kXLds), "checkpoints: the backward pass's tiles");
 
@@ -177,7 +208,7 @@ scan_kernel(const ScanArgs p) {
   float *const prep = sbase + dw * Lay::WAVE;    // [R][PSTR]
   float *const bcs = prep + Lay::PREP;           // [T][32]
   float *const xs = bcs + Lay::BC;               // [R][XH] conv input (CONV)
-  float *const part = prep;                      // [64 lanes][QSTR], shares the staging area
+  float *const part = prep + Lay::PART_AT;       // [64 lanes][QSTR], shares the staging area (R > 8)
   float *const xlds = sbase + DIRS * Lay::WAVE;  // [R][XS]   (kXLds)
 
   const int sp = lane / R;                       // state group
@@ -377,9 +408,9 @@ scan_kernel(const ScanArgs p) {
     }
 #pragma unroll
     for (int i = 0; i < BQ; ++i) {
-      float *const q = bcs + (lane / 16 + 4 * i) * 32 + n_bc;
+      float *const q = bcs + (lane / 16 + 4 * i) * 32 + (NS == 2 ? (n_bc >> 1) * 4 + (n_bc & 1) : n_bc);
       q[0] = pin(rb[Q][i]);
-      q[16] = pin(rc[Q][i]);
+      q[NS == 2 ? 2 : 16] = pin(rc[Q][i]);
     }
   };
 
@@ -394,15 +425,19 @@ scan_kernel(const ScanArgs p) {
 #pragma unroll
     for (int q = 0; q < T; ++q) {
       dus[q] = *reinterpret_cast<const float2 *>(pr_lane + 2 * q);
-      bcv[q] = bc_lane[q * 32];
+      if constexpr (NS != 2) bcv[q] = bc_lane[q * 32];
     }
   };
 
+  // (two-state split: B and C of the lane's state pair, read step by step)
+  const float *const b4_lane = bcs + 4 * sp;
   auto do_scan = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < T; ++q) {
       float y;
-      if constexpr (ZOH) state_step_zoh<NS, 0>(h, A2, iA, dus[q].x, dus[q].y, bcv[q], y);
+      if constexpr (NS == 2)
+        state_step2<ZOH>(h, A2, iA, dus[q].x, dus[q].y, *reinterpret_cast<const float4 *>(b4_lane + q * 32), y);
+      else if constexpr (ZOH) state_step_zoh<NS, 0>(h, A2, iA, dus[q].x, dus[q].y, bcv[q], y);
       else state_step<NS, 0>(h, A2, dus[q].x, dus[q].y, bcv[q], y);
       part_lane[q] = y;
     }
@@ -618,6 +653,7 @@ template <typename Tin, int SPLIT, int OPT>
 hipError_t dispatch_mode(const ScanPlan &plan, const ScanArgs &a, hipStream_t s) {
   if (plan.dirs == 1) return launch_one<Tin, SPLIT, 1, kXNone, 16, OPT>(plan, a, s);
   if (plan.xmode == kXLds) return launch_one<Tin, SPLIT, 2, kXLds, 8, OPT>(plan, a, s);
+  if (plan.S == 8) return launch_one<Tin, 8, 2, kXGlobal, 16, OPT>(plan, a, s);
   return launch_one<Tin, SPLIT, 2, kXGlobal, 16, OPT>(plan, a, s);
 }
 
@@ -644,7 +680,8 @@ size_t lds_bytes(int split, int dirs, int T, int xmode, int64_t L, bool conv) {
   const int R = 64 / split;
   const size_t stage = R * (2 * T + 2) + 32 * T + (conv ? R * (T + 4) : 0);   // Layout::STAGE
   const size_t part = 64 * (T + 1);                                            // Layout::PART
-  size_t f = static_cast<size_t>(dirs) * (stage > part ? stage : part);
+  const size_t wave = R != 8 ? (stage > part ? stage : part) : (stage + 3) / 4 * 4 + part;
+  size_t f = static_cast<size_t>(dirs) * wave;
   if (xmode == kXLds) f += static_cast<size_t>(R) * xchg_stride(L, T);
   return f * sizeof(float);
 }
@@ -658,10 +695,14 @@ ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t L, int dstate, int dirs, 
   // Each channel's 16 states are split over 4 lanes: a two-lane split needs
   // fewer instructions per state but leaves half the waves, and measured
   // slower on every workload tried (fewer waves to hide latency, and a
-  // larger LDS exchange per workgroup).
+  // larger LDS exchange per workgroup).  Long bidirectional sequences with
+  // fewer than two waves per SIMD (1024 SIMDs) split over 8 lanes instead:
+  // a wave alone on a SIMD issues about one instruction per 5 cycles, two
+  // or more share it at about 2.2 each, so twice the waves with 60 % of the
+  // instructions each finish sooner.
   pl.S = 4;
   pl.threads = 64 * dirs;
-  const int64_t nblk = batch * ((dim + 64 / pl.S - 1) / (64 / pl.S));
+  int64_t nblk = batch * ((dim + 64 / pl.S - 1) / (64 / pl.S));
   // Tile length: 16 steps where the registers allow it (one direction, or
   // the global exchange: longer row segments per load and half the per-tile
   // overhead); 8 for the on-chip exchange, whose LDS footprint grows with T.
@@ -690,6 +731,10 @@ ScanPlan plan_scan(int64_t batch, int64_t dim, int64_t L, int dstate, int dirs, 
     // CU's 160 KB LDS.
     pl.xmode = lds_bytes(pl.S, 2, 8, kXLds, L, conv) <= 40 * 1024 ? kXLds : kXGlobal;
     pl.T = pl.xmode == kXLds ? 8 : 16;
+    if (pl.xmode == kXGlobal && nblk * 2 < 2048) {
+      pl.S = 8;
+      nblk = batch * ((dim + 7) / 8);
+    }
     // Two row blocks per workgroup where there are enough of them to give
     // every CU several workgroups: the balanced SIMDs measured 4 % faster on
     // the Vim-T step.  Fewer, larger workgroups would leave CUs idle on small

@@ -757,6 +757,33 @@ def test_fused_conv_bidir(L, dtype, zoh):
     assert_close(host(out), ref, FP32_TOL if dtype == torch.float32 else BF16_TOL, "fused conv bidir")
 
 
+# The global exchange splits a channel's 16 states over 8 lanes (two states
+# each, B and C read per lane) when a 4-lane split would leave fewer than two
+# waves per SIMD: 2 x 44 channels (dim 44 = 5 x 8 + 4, a partial last row
+# block) take the 8-lane split, 64 x 256 (2048 waves) the 4-lane one.  Every
+# write option on both.
+@pytest.mark.parametrize("batch,dim", [(2, 44), (64, 256)])
+@pytest.mark.parametrize("zoh", [False, True])
+@pytest.mark.parametrize("conv", [False, True])
+def test_bidir_global_exchange_state_splits(batch, dim, zoh, conv):
+    L = 600
+    _case(f"bidir global exchange b{batch} d{dim} zoh{zoh} conv{conv}")
+    fwd, bwd, z = wl.bidir_inputs(2100 + dim, batch, dim, L, device=DEV, perturb=True)
+    if conv:
+        bwd["u"] = fwd["u"]
+        g = wl.generator(2200 + dim, DEV)
+        for p in (fwd, bwd):
+            p["conv_w"], p["conv_b"] = wl.conv_params(g, dim, DEV)
+    out = vm.vm_bidir_scan_fwd(fwd, bwd, z=z, combine_scale=0.5, zoh=zoh)
+    torch.cuda.synchronize()
+    hf, hb = host_dir(fwd), host_dir(bwd)
+    if conv:
+        for h, rev in ((hf, False), (hb, True)):
+            h["u"] = oracle.causal_conv1d_silu(h["u"], h.pop("conv_w"), h.pop("conv_b"), reverse=rev)
+    ref = oracle.bidir_scan(hf, hb, z=host(z), combine_scale=0.5, zoh=zoh)
+    assert_close(host(out), ref, FP32_TOL, "global exchange state split")
+
+
 def test_full_vim_tiny_bidir_fused_conv():
     """The Vim-T block with its causal conv1d + SiLU inside the scan, at full
     size (two row blocks per workgroup): sampled batch rows against the
