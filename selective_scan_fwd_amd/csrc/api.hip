@@ -275,9 +275,9 @@ int run_bwd_group(int n, const vm_scan_dir *const p[], const float *const dy[], 
                         &st);
   if (st != VM_OK) return st;
   st = hip_status(vmk::launch_scan_bwd_group(grp, s));
-  for (int k = 0; k < n && st == VM_OK; ++k)
-    st = hip_status(vmk::launch_scan_bwd_reduce(grp.a[k], g[k]->dA, g[k]->dB, g[k]->dC, g[k]->dD,
-                                                g[k]->ddelta_bias, s));
+  vmk::BwdReduceOut out[vmk::kBwdGroupMax] = {};
+  for (int k = 0; k < n; ++k) out[k] = {g[k]->dA, g[k]->dB, g[k]->dC, g[k]->dD, g[k]->ddelta_bias};
+  if (st == VM_OK) st = hip_status(vmk::launch_scan_bwd_reduce_group(grp, out, s));
   return st;
 }
 

@@ -535,56 +535,63 @@ scan_bwd_kernel(const Arg arg) {
   }
 }
 
-// Sums of the partials over channel blocks: dB, dC [batch, dstate, L].  The
-// partials are [nrb][batch][tiles][16][T]; element e of one block's slab is
-// read in storage order (whole lines) and lands at (b, n, t).
-__global__ void __launch_bounds__(256)
-reduce_bc_kernel(const float *__restrict__ pB, const float *__restrict__ pC, float *dB, float *dC,
-                 int64_t slab, int nrb, int nt, int L, int dstate) {
+// The reductions of a group's partial sums, all directions in one launch
+// (blockIdx.y = direction): blocks below bc_blocks add the dB, dC partials
+// over channel blocks, the others (one per channel) the dA, dD, dbias
+// partials over batch rows.  Fixed summation orders: deterministic.
+struct ReduceJob {
+  const float *pB, *pC, *pA, *pD, *pbias;
+  float *dB, *dC, *dA, *dD, *dbias;
+};
+struct ReduceGroup {
+  ReduceJob j[kBwdGroupMax];
+  int64_t batch, dim, slab;       // slab: floats of one channel block's dB (dC) partials
+  int L, dstate, nrb, nt, bc_blocks;
+};
+
+// dB, dC [batch, dstate, L] from partials [nrb][batch][tiles][16][T]:
+// element e of one block's slab is read in storage order (whole lines) and
+// lands at (b, n, t).
+__device__ void reduce_bc(const ReduceGroup &g, const ReduceJob &J) {
   constexpr int T = kBwdTile;
-  const int64_t per_b = static_cast<int64_t>(nt) * 16 * T;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < slab; e += stride) {
+  const int64_t per_b = static_cast<int64_t>(g.nt) * 16 * T;
+  const int64_t stride = static_cast<int64_t>(g.bc_blocks) * 256;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < g.slab; e += stride) {
     float sb[4] = {0.f, 0.f, 0.f, 0.f}, sc[4] = {0.f, 0.f, 0.f, 0.f};
     int k = 0;
-    for (; k + 4 <= nrb; k += 4) {
+    for (; k + 4 <= g.nrb; k += 4) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        sb[u] += pB[(k + u) * slab + e];
-        sc[u] += pC[(k + u) * slab + e];
+        sb[u] += J.pB[(k + u) * g.slab + e];
+        sc[u] += J.pC[(k + u) * g.slab + e];
       }
     }
-    for (; k < nrb; ++k) {
-      sb[0] += pB[k * slab + e];
-      sc[0] += pC[k * slab + e];
+    for (; k < g.nrb; ++k) {
+      sb[0] += J.pB[k * g.slab + e];
+      sc[0] += J.pC[k * g.slab + e];
     }
     const int64_t b = e / per_b;
     const int rem = static_cast<int>(e - b * per_b);
     const int j = rem / (16 * T), n = (rem / T) % 16, t = j * T + rem % T;
-    if (n < dstate && t < L) {
-      const int64_t o = (b * dstate + n) * L + t;
-      dB[o] = (sb[0] + sb[1]) + (sb[2] + sb[3]);
-      dC[o] = (sc[0] + sc[1]) + (sc[2] + sc[3]);
+    if (n < g.dstate && t < g.L) {
+      const int64_t o = (b * g.dstate + n) * g.L + t;
+      J.dB[o] = (sb[0] + sb[1]) + (sb[2] + sb[3]);
+      J.dC[o] = (sc[0] + sc[1]) + (sc[2] + sc[3]);
     }
   }
 }
 
-// Sums of the partials over batch rows, one workgroup per channel d:
-// dA [dim, dstate], dD [dim], dbias [dim].  Thread t adds the rows
-// b = t / 16 (mod 16 slices) for state t % 16; the slices meet in LDS.
-__global__ void __launch_bounds__(256)
-reduce_param_kernel(const float *__restrict__ pA, float *dA, const float *__restrict__ pD, float *dD,
-                    const float *__restrict__ pbias, float *dbias, int64_t batch, int64_t dim,
-                    int dstate) {
+// dA [dim, dstate], dD [dim], dbias [dim] for channel d: thread t adds the
+// rows b = t / 16 (mod 16 slices) for state t % 16; the slices meet in LDS.
+__device__ void reduce_param(const ReduceGroup &g, const ReduceJob &J, int64_t d) {
   __shared__ float sa[256], sd[256], sb[256];
-  const int64_t d = blockIdx.x;
   const int t = threadIdx.x, n = t & 15, slice = t >> 4;
   float a = 0.f, dd = 0.f, db = 0.f;
-  for (int64_t bb = slice; bb < batch; bb += 16) {
-    a += pA[(bb * dim + d) * 16 + n];
+  for (int64_t bb = slice; bb < g.batch; bb += 16) {
+    a += J.pA[(bb * g.dim + d) * 16 + n];
     if (n == 0) {
-      dd += pD[bb * dim + d];
-      db += pbias[bb * dim + d];
+      dd += J.pD[bb * g.dim + d];
+      db += J.pbias[bb * g.dim + d];
     }
   }
   sa[t] = a;
@@ -598,12 +605,18 @@ reduce_param_kernel(const float *__restrict__ pA, float *dA, const float *__rest
       s2 += sd[k * 16 + t];
       s3 += sb[k * 16 + t];
     }
-    if (t < dstate) dA[d * dstate + t] = s;
+    if (t < g.dstate) J.dA[d * g.dstate + t] = s;
     if (t == 0) {
-      dD[d] = s2;
-      if (dbias != nullptr) dbias[d] = s3;
+      J.dD[d] = s2;
+      if (J.dbias != nullptr) J.dbias[d] = s3;
     }
   }
+}
+
+__global__ void __launch_bounds__(256) reduce_kernel(const ReduceGroup g) {
+  const ReduceJob &J = g.j[blockIdx.y];
+  if (static_cast<int>(blockIdx.x) < g.bc_blocks) reduce_bc(g, J);
+  else reduce_param(g, J, static_cast<int64_t>(blockIdx.x) - g.bc_blocks);
 }
 
 // dy = scale * dout * SiLU(z) and dz = scale * dout * y * SiLU'(z), with
@@ -696,17 +709,23 @@ hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t s) {
   return launch_scan_bwd_group(g, s);
 }
 
-hipError_t launch_scan_bwd_reduce(const BwdArgs &a, float *dA, float *dB, float *dC, float *dD,
-                                  float *dbias, hipStream_t s) {
-  const int nrb = static_cast<int>((a.dim + kR - 1) / kR);
-  const int nt = static_cast<int>(scan_bwd_tiles(a.L));
-  const int64_t slab = a.batch * nt * 16 * kBwdTile;
-  hipLaunchKernelGGL(reduce_bc_kernel, dim3(grid_for(slab)), dim3(256), 0, s, a.pB, a.pC, dB, dC, slab,
-                     nrb, nt, static_cast<int>(a.L), a.dstate);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(reduce_param_kernel, dim3(static_cast<unsigned>(a.dim)), dim3(256), 0, s, a.pA, dA,
-                     a.pD, dD, a.pbias, dbias, a.batch, a.dim, a.dstate);
+hipError_t launch_scan_bwd_reduce_group(const BwdGroup &g, const BwdReduceOut out[], hipStream_t s) {
+  if (g.n < 1 || g.n > kBwdGroupMax) return hipErrorInvalidValue;
+  const BwdArgs &a = g.a[0];
+  ReduceGroup r = {};
+  for (int k = 0; k < g.n; ++k)
+    r.j[k] = ReduceJob{g.a[k].pB, g.a[k].pC, g.a[k].pA, g.a[k].pD, g.a[k].pbias,
+                       out[k].dB, out[k].dC, out[k].dA, out[k].dD, out[k].dbias};
+  r.batch = a.batch;
+  r.dim = a.dim;
+  r.L = static_cast<int>(a.L);
+  r.dstate = a.dstate;
+  r.nrb = static_cast<int>((a.dim + kR - 1) / kR);
+  r.nt = static_cast<int>(scan_bwd_tiles(a.L));
+  r.slab = a.batch * r.nt * 16 * kBwdTile;
+  r.bc_blocks = static_cast<int>(grid_for(r.slab));
+  hipLaunchKernelGGL(reduce_kernel, dim3(static_cast<unsigned>(r.bc_blocks + a.dim), static_cast<unsigned>(g.n)),
+                     dim3(256), 0, s, r);
   return hipGetLastError();
 }
 

@@ -171,8 +171,11 @@ struct BwdGroup {
   int n;
 };
 hipError_t launch_scan_bwd_group(const BwdGroup &g, hipStream_t s);
-hipError_t launch_scan_bwd_reduce(const BwdArgs &a, float *dA, float *dB, float *dC, float *dD,
-                                  float *dbias, hipStream_t s);
+// The sums of the partials of every direction of a group, in one launch.
+struct BwdReduceOut {
+  float *dA, *dB, *dC, *dD, *dbias;
+};
+hipError_t launch_scan_bwd_reduce_group(const BwdGroup &g, const BwdReduceOut out[], hipStream_t s);
 // dy = scale dout SiLU(z), dz = scale dout (y + y2) SiLU'(z) (y2 may be null;
 // without z, dy = scale dout).
 hipError_t launch_gate_bwd(const float *y, const float *z, const float *dout, float *dy, float *dz,
