@@ -435,7 +435,10 @@ scan_bwd_kernel(const Arg arg) {
     wave_lds_fence();
     reduce_red(rPC);
     wave_lds_fence();
-    // adjoint back through the tile
+    // adjoint back through the tile: g = C dy + a_{t+1} g_{t+1} per state
+    // (accumulated in place of gn), sum_n g B into sgB, sum_n g a h A into
+    // sqA; the B and C broadcasts fold into the multiply-adds
+    // (v_fmac_f32_dpp) where the write allows it
 #pragma unroll
     for (int q = T - 1; q >= 0; --q) {
       const float4 pq = pqs[q];
@@ -443,18 +446,24 @@ scan_bwd_kernel(const Arg arg) {
       float sgB = 0.0f, sqA = 0.0f;
 #pragma unroll
       for (int jn = 0; jn < kNS; ++jn) {
-        float Bb, Cb;
+        float &g = gn[jn];
         switch (jn) {
-          case 0: Bb = row_bcast<0>(bv); Cb = row_bcast<kNS + 0>(bv); break;
-          case 1: Bb = row_bcast<1>(bv); Cb = row_bcast<kNS + 1>(bv); break;
-          case 2: Bb = row_bcast<2>(bv); Cb = row_bcast<kNS + 2>(bv); break;
-          default: Bb = row_bcast<3>(bv); Cb = row_bcast<kNS + 3>(bv); break;
+          case 0: fmac_row_bcast<kNS + 0>(g, bv, pq.z); break;
+          case 1: fmac_row_bcast<kNS + 1>(g, bv, pq.z); break;
+          case 2: fmac_row_bcast<kNS + 2>(g, bv, pq.z); break;
+          default: fmac_row_bcast<kNS + 3>(g, bv, pq.z); break;
         }
-        const float g = __builtin_fmaf(Cb, pq.z, gn[jn]);
         const float ah = as[q][jn] * (q > 0 ? hs[q > 0 ? q - 1 : 0][jn] : h0[jn]);   // a_t h_{t-1}
         const float gq = g * ah;
         if constexpr (ZOH) {
           // pq.y is u; k and dk/dA are recomputed from the kept decay
+          float Bb;
+          switch (jn) {
+            case 0: Bb = row_bcast<0>(bv); break;
+            case 1: Bb = row_bcast<1>(bv); break;
+            case 2: Bb = row_bcast<2>(bv); break;
+            default: Bb = row_bcast<3>(bv); break;
+          }
           const float x2 = pq.x * A2[jn];
           const float kq = zoh_coef(pq.x, x2, as[q][jn], iA[jn]);
           const float gBu = g * Bb * pq.y;
@@ -464,12 +473,17 @@ scan_bwd_kernel(const Arg arg) {
                                                            dA[jn]));
           sqA = __builtin_fmaf(gq, An[jn], __builtin_fmaf(gBu, as[q][jn], sqA));
         } else {
+          switch (jn) {
+            case 0: sgB = row_bcast<0>(bv) * g; break;
+            case 1: fmac_row_bcast<1>(sgB, bv, g); break;
+            case 2: fmac_row_bcast<2>(sgB, bv, g); break;
+            default: fmac_row_bcast<3>(sgB, bv, g); break;
+          }
           red[((n0 + jn) * T + q) * Lay::RSTR + sp * 16 + r] = g * pq.y;   // dB
-          sgB = __builtin_fmaf(g, Bb, sgB);
           dA[jn] = __builtin_fmaf(gq, pq.x, dA[jn]);
           sqA = __builtin_fmaf(gq, An[jn], sqA);
         }
-        gn[jn] = as[q][jn] * g;
+        g = as[q][jn] * g;
       }
       part[(0 * 64 + lane) * Lay::QSTR + q] = sgB;
       part[(1 * 64 + lane) * Lay::QSTR + q] = sqA;

@@ -16,6 +16,23 @@ __device__ __forceinline__ float row_bcast(float v) {
       float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + J, 0xf, 0xf, true));
 }
 
+// y += row_bcast<J>(c) * h as one v_fmac_f32_dpp.  c must come straight from
+// memory (no VALU write of it just before), which holds for the LDS-loaded
+// B/C values it is used with.
+template <int J> __device__ __forceinline__ void fmac_row_bcast(float &y, float c, float h);
+#define VM_FMAC_BCAST(J)                                                              \
+  template <>                                                                         \
+  __device__ __forceinline__ void fmac_row_bcast<J>(float &y, float c, float h) {     \
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:" #J " row_mask:0xf bank_mask:0xf"    \
+        : "+v"(y)                                                                     \
+        : "v"(c), "v"(h));                                                            \
+  }
+VM_FMAC_BCAST(0) VM_FMAC_BCAST(1) VM_FMAC_BCAST(2) VM_FMAC_BCAST(3)
+VM_FMAC_BCAST(4) VM_FMAC_BCAST(5) VM_FMAC_BCAST(6) VM_FMAC_BCAST(7)
+VM_FMAC_BCAST(8) VM_FMAC_BCAST(9) VM_FMAC_BCAST(10) VM_FMAC_BCAST(11)
+VM_FMAC_BCAST(12) VM_FMAC_BCAST(13) VM_FMAC_BCAST(14) VM_FMAC_BCAST(15)
+#undef VM_FMAC_BCAST
+
 // Ties a loaded value to this point of the program: nothing computed from it
 // can be scheduled earlier (next to its load), where the wait for the load
 // would also wait for the loads issued after it.

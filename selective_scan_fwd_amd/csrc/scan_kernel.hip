@@ -51,22 +51,6 @@
 namespace vmk {
 namespace {
 
-// y += row_bcast<J>(c) * h as one v_fmac_f32_dpp.  c must come straight from
-// memory (no VALU write of it just before), which holds for the LDS-loaded
-// B/C value it is used with.
-template <int J> __device__ __forceinline__ void fmac_row_bcast(float &y, float c, float h);
-#define VM_FMAC_BCAST(J)                                                              \
-  template <>                                                                         \
-  __device__ __forceinline__ void fmac_row_bcast<J>(float &y, float c, float h) {     \
-    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:" #J " row_mask:0xf bank_mask:0xf"    \
-        : "+v"(y)                                                                     \
-        : "v"(c), "v"(h));                                                            \
-  }
-VM_FMAC_BCAST(4) VM_FMAC_BCAST(5) VM_FMAC_BCAST(6) VM_FMAC_BCAST(7)
-VM_FMAC_BCAST(8) VM_FMAC_BCAST(9) VM_FMAC_BCAST(10) VM_FMAC_BCAST(11)
-VM_FMAC_BCAST(12) VM_FMAC_BCAST(13) VM_FMAC_BCAST(14) VM_FMAC_BCAST(15)
-#undef VM_FMAC_BCAST
-
 // One step of the lane's NS states: h_j <- 2^(dt A2_j) h_j + dtu B_j and
 // y = sum_j C_j h_j (B_j, C_j broadcast from lanes j and NS + j of the row).
 template <int NS, int J>
