@@ -233,13 +233,17 @@ struct BwdScratch {
   }
 };
 
+// How a backward pass finds what its forward recomputation prepared.
+enum class Prep { kNone, kCk, kCkDyTiled };
+
 vmk::BwdArgs bwd_args(const vm_scan_dir *p, const float *dy, const vm_scan_grad *g, const BwdScratch &bs,
                       int64_t batch, int64_t dim, int64_t L, int64_t dstate, int options, int reverse,
-                      bool ck_ready, Scratch &ws, hipStream_t s, int *st) {
+                      Prep prep, Scratch &ws, hipStream_t s, int *st) {
   vmk::BwdArgs a = {};
-  // the forward kernel that stores the checkpoints writes dy tile-major
-  a.ck_ready = ck_ready ? 1 : 0;
-  a.dy_tiled = ck_ready ? 1 : 0;
+  // checkpoints from the forward kernel; with the gate's backward fused
+  // there, dy is tile-major too
+  a.ck_ready = prep != Prep::kNone ? 1 : 0;
+  a.dy_tiled = prep == Prep::kCkDyTiled ? 1 : 0;
   a.dir = resolve_dir(p, batch, dstate, L, false, ws, s, st);
   a.dy = dy;
   a.du = g->du;
@@ -266,12 +270,12 @@ vmk::BwdArgs bwd_args(const vm_scan_dir *p, const float *dy, const vm_scan_grad 
 // partial sums.
 int run_bwd_group(int n, const vm_scan_dir *const p[], const float *const dy[], const vm_scan_grad *const g[],
                   const BwdScratch bs[], int64_t batch, int64_t dim, int64_t L, int64_t dstate, int options,
-                  const int reverse[], Scratch &ws, hipStream_t s, bool ck_ready = false) {
+                  const int reverse[], Scratch &ws, hipStream_t s, Prep prep = Prep::kNone) {
   int st = VM_OK;
   vmk::BwdGroup grp = {};
   grp.n = n;
   for (int k = 0; k < n; ++k)
-    grp.a[k] = bwd_args(p[k], dy[k], g[k], bs[k], batch, dim, L, dstate, options, reverse[k], ck_ready, ws, s,
+    grp.a[k] = bwd_args(p[k], dy[k], g[k], bs[k], batch, dim, L, dstate, options, reverse[k], prep, ws, s,
                         &st);
   if (st != VM_OK) return st;
   st = hip_status(vmk::launch_scan_bwd_group(grp, s));
@@ -283,8 +287,8 @@ int run_bwd_group(int n, const vm_scan_dir *const p[], const float *const dy[], 
 
 int run_bwd(const vm_scan_dir *p, const float *dy, const vm_scan_grad *g, const BwdScratch &bs,
             int64_t batch, int64_t dim, int64_t L, int64_t dstate, int options, int reverse,
-            Scratch &ws, hipStream_t s, bool ck_ready = false) {
-  return run_bwd_group(1, &p, &dy, &g, &bs, batch, dim, L, dstate, options, &reverse, ws, s, ck_ready);
+            Scratch &ws, hipStream_t s, Prep prep = Prep::kNone) {
+  return run_bwd_group(1, &p, &dy, &g, &bs, batch, dim, L, dstate, options, &reverse, ws, s, prep);
 }
 
 // Checks of a gradient set: required pointers, no overlap with the inputs
@@ -976,6 +980,9 @@ int vm_ss2d_scan_bwd(const vm_scan_dir *dirs, const void *u, const void *z, cons
       a[pass].softplus = (options & VM_DELTA_SOFTPLUS) != 0;
       a[pass].zoh = (options & VM_ZOH) != 0;
       a[pass].scale = 1.0f;
+      // the two traversals' checkpoints, for the backward kernels
+      a[pass].ck[0] = bs[2 * pass].ck;
+      a[pass].ck[1] = bs[2 * pass + 1].ck;
       if (st == VM_OK) st = launch_bidir(a[pass], false, ws, s);
     }
     // y = y_r + transpose(y_c) for dz; the transpose lands in dus[0] (free
@@ -999,7 +1006,9 @@ int vm_ss2d_scan_bwd(const vm_scan_dir *dirs, const void *u, const void *z, cons
     gkp[k] = &gk[k];
     dyk[k] = k < 2 ? g : gt;
   }
-  if (st == VM_OK) st = run_bwd_group(4, pk, dyk, gkp, bs, batch, dim, L, dstate, options, revk, ws, s);
+  if (st == VM_OK)
+    st = run_bwd_group(4, pk, dyk, gkp, bs, batch, dim, L, dstate, options, revk, ws, s,
+                       z != nullptr ? Prep::kCk : Prep::kNone);
   // du = du_0 + du_1 + transpose(du_2 + du_3), through g and gt (free now)
   if (st == VM_OK) st = hip_status(vmk::launch_add(dus[2], dus[3], nullptr, g, tok, s));
   if (st == VM_OK) st = hip_status(vmk::launch_transpose(g, gt, planes, width, height, false, s));
@@ -1111,10 +1120,10 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
   hipStream_t s = static_cast<hipStream_t>(stream);
   Scratch ws(s);
   // dy = s * dout * SiLU(z) reaches both directions; dz needs y_f + y_b,
-  // which the forward kernel recomputes ungated with s = 1.  For short
-  // sequences (on-chip exchange, 8-step tiles like the backward's) that
+  // which the forward kernel recomputes ungated with s = 1.  That
   // recomputation also stores both directions' checkpoints, so that the
-  // backward kernels skip their first pass, and forms dy and dz itself.
+  // backward kernels skip their first pass; for short sequences (on-chip
+  // exchange) it forms dy and dz itself too.
   const bool fuse = z != nullptr &&
                     vmk::plan_scan(batch, dim, seqlen, static_cast<int>(dstate), 2, false).xmode ==
                         vmk::kXLds;
@@ -1159,9 +1168,11 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
     a.softplus = (options & VM_DELTA_SOFTPLUS) != 0;
     a.zoh = (options & VM_ZOH) != 0;
     a.scale = 1.0f;
+    // both directions' checkpoints, so that the backward kernels skip their
+    // first pass
+    a.ck[0] = bs[0].ck;
+    a.ck[1] = bs[1].ck;
     if (fuse) {
-      a.ck[0] = bs[0].ck;
-      a.ck[1] = bs[1].ck;
       a.gz = z32;
       a.dout = dout32;
       a.dy = dy;
@@ -1171,6 +1182,7 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
     st = launch_bidir(a, false, ws, s);
     if (st != VM_OK) return st;
   }
+  const Prep prep = z == nullptr ? Prep::kNone : fuse ? Prep::kCkDyTiled : Prep::kCk;
   if (!fuse) {
     st = hip_status(vmk::launch_gate_bwd(y, z32, dout32, dy, static_cast<float *>(dz), tok,
                                          combine_scale, s));
@@ -1182,14 +1194,14 @@ int vm_bidir_scan_bwd(const vm_scan_dir *fwd, const vm_scan_dir *bwd, const void
     gub.du = cvb.du;
   }
   if (zoh) {
-    st = run_bwd(&wf, dy, &guf, bs[0], batch, dim, seqlen, dstate, options, 0, ws, s, fuse);
-    if (st == VM_OK) st = run_bwd(&wb, dy, &gub, bs[1], batch, dim, seqlen, dstate, options, 1, ws, s, fuse);
+    st = run_bwd(&wf, dy, &guf, bs[0], batch, dim, seqlen, dstate, options, 0, ws, s, prep);
+    if (st == VM_OK) st = run_bwd(&wb, dy, &gub, bs[1], batch, dim, seqlen, dstate, options, 1, ws, s, prep);
   } else {
     const vm_scan_dir *pk[2] = {&wf, &wb};
     const float *dyk[2] = {dy, dy};
     const vm_scan_grad *gk[2] = {&guf, &gub};
     const int revk[2] = {0, 1};
-    st = run_bwd_group(2, pk, dyk, gk, bs, batch, dim, seqlen, dstate, options, revk, ws, s, fuse);
+    st = run_bwd_group(2, pk, dyk, gk, bs, batch, dim, seqlen, dstate, options, revk, ws, s, prep);
   }
   if (st == VM_OK && conv) st = cvf.backward(*fwd, gf, batch, dim, seqlen, 0, s);
   if (st == VM_OK && conv) st = cvb.backward(*bwd, gb, batch, dim, seqlen, 1, s);

@@ -373,7 +373,9 @@ scan_bwd_kernel(const Arg arg) {
     float hc[kNS], h0[kNS];
 #pragma unroll
     for (int jn = 0; jn < kNS; ++jn) {
-      hc[jn] = pin(lk[jn]);
+      // (channels past dim: a checkpoint written by a forward kernel with
+      // the 8-lane split may not cover them; their state stays zero)
+      hc[jn] = r < rows ? pin(lk[jn]) : 0.0f;
       h0[jn] = hc[jn];
     }
     stage_load(tile_of(k > 0 ? k - 1 : 0), true);

@@ -92,6 +92,12 @@ __device__ __forceinline__ void bstore4(Rsrc r, uint32_t off, const float (&v)[4
                      __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3])};
   __builtin_amdgcn_raw_buffer_store_b128(x, r, static_cast<int>(off), 0, 0);
 }
+// Two consecutive fp32 values at an 8-byte aligned offset, in one access.
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void bstore2(Rsrc r, uint32_t off, const float (&v)[2]) {
+  const u32x2_t x = {__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1])};
+  __builtin_amdgcn_raw_buffer_store_b64(x, r, static_cast<int>(off), 0, 0);
+}
 // (The whole vector is reinterpreted: a bit cast of one element of an
 // ext_vector value reads element 0 with this compiler.)
 typedef float f32x4_t __attribute__((ext_vector_type(4)));

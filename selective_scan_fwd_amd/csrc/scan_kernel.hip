@@ -167,6 +167,7 @@ scan_kernel(const ScanArgs p) {
   constexpr bool ZOH = (OPT & kOptZoh) != 0;
   constexpr bool CONV = (OPT & kOptConv) != 0;
   constexpr bool CK = (OPT & kOptBwdPrep) != 0;  // prepare the backward pass (checkpoints, gate)
+  constexpr bool CKS = CK || (OPT & kOptCk) != 0; // store the backward's checkpoints
   constexpr int NS = 16 / SPLIT;                 // states per lane
   constexpr int R = 64 / SPLIT;                  // channels per workgroup
   constexpr int PE = R * T / 64;                 // staged (dt, u) elements per lane per tile
@@ -177,7 +178,8 @@ scan_kernel(const ScanArgs p) {
   static_assert(((NS >= 4 && NS <= 8 && R % 16 == 0) || (NS == 2 && R == 8)) && T % 4 == 0 &&
                     (R * T) % 64 == 0, "shape");
   static_assert(DIRS == 1 ? XMODE == kXNone : XMODE != kXNone, "mode");
-  static_assert(!CK || (T == kBwdTile && XMODE == kXLds), "checkpoints: the backward pass's tiles");
+  static_assert(!CK || (T == kBwdTile && XMODE == kXLds), "gate backward: the on-chip exchange");
+  static_assert(!CKS || T == kBwdTile || T == 2 * kBwdTile, "checkpoints: at the backward's 8-step tiles");
 
   extern __shared__ float smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -257,15 +259,24 @@ scan_kernel(const ScanArgs p) {
   // states], so that a wave's checkpoints of one tile are one contiguous
   // kilobyte (a row block past the end has none; channels past dim store
   // zeros).
-  const Rsrc rCk = make_rsrc(CK ? p.ck[dw] + (static_cast<int64_t>(b) * nrb + d0 / R) * nt * 256 : nullptr,
-                             CK && valid ? static_cast<uint32_t>(nt) * 1024u : 0u);
-  const uint32_t ck_lane = static_cast<uint32_t>(r * 16 + sp * (16 / SPLIT)) * 4u;
+  // With 16-step tiles a checkpoint goes out at visit positions 0 and 8; with
+  // the 8-lane split a wave fills half of a 16-channel block.
+  const int nt8 = (L + kBwdTile - 1) / kBwdTile;
+  const int nrb16 = static_cast<int>((dim + 15) / 16);
+  const Rsrc rCk = make_rsrc(CKS ? p.ck[dw] + (static_cast<int64_t>(b) * nrb16 + d0 / 16) * nt8 * 256 : nullptr,
+                             CKS && valid ? static_cast<uint32_t>(nt8) * 1024u : 0u);
+  const uint32_t ck_lane = static_cast<uint32_t>((d0 % 16 + r) * 16 + sp * NS) * 4u;
+
   const Rsrc rGz = make_rsrc(CK ? p.gz + rowbase : nullptr, CK ? slab : 0u);
   const Rsrc rDo = make_rsrc(CK ? p.dout + rowbase : nullptr, CK ? slab : 0u);
   const Rsrc rDy = make_rsrc(CK ? p.dy + (static_cast<int64_t>(b) * nrb + d0 / R) * nt * 16 * T : nullptr,
                              CK && valid ? static_cast<uint32_t>(nt * 16 * T) * 4u : 0u);
   const Rsrc rDz = make_rsrc(CK ? p.dz + rowbase : nullptr, CK ? slab : 0u);
   float A2[NS], iA[NS], h[NS];
+  auto store_ck = [&](int tile8) __attribute__((always_inline)) {
+    if constexpr (NS == 4) bstore4(rCk, ck_lane + static_cast<uint32_t>(tile8) * 1024u, h);
+    else if constexpr (NS == 2) bstore2(rCk, ck_lane + static_cast<uint32_t>(tile8) * 1024u, h);
+  };
 #pragma unroll
   for (int j = 0; j < NS; ++j) h[j] = 0.0f;
   // lane j of each 16-lane row holds B[n0 + j] (j < NS) or C[n0 + j - NS]
@@ -415,9 +426,14 @@ scan_kernel(const ScanArgs p) {
 
   // (two-state split: B and C of the lane's state pair, read step by step)
   const float *const b4_lane = bcs + 4 * sp;
-  auto do_scan = [&]() __attribute__((always_inline)) {
+  auto do_scan = [&](int k) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < T; ++q) {
+      if constexpr (CKS && T == 2 * kBwdTile) {
+        // the state entering 8-step tile 2 j + (q / 8) (visit order reversed
+        // within a backward 16-step tile; past the last 8-step tile: dropped)
+        if (q % kBwdTile == 0) store_ck(2 * tile_of(k) + (rev ? 1 - q / kBwdTile : q / kBwdTile));
+      }
       float y;
       if constexpr (NS == 2)
         state_step2<ZOH>(h, A2, iA, dus[q].x, dus[q].y, *reinterpret_cast<const float4 *>(b4_lane + q * 32), y);
@@ -497,12 +513,9 @@ scan_kernel(const ScanArgs p) {
     using Qn = std::integral_constant<int, (decltype(slot)::value + 1) % NB>;
     comb_load(k + 1 < nt ? k + 1 : nt - 1, Qn(), second);
     stage_load(k + NB < nt ? k + NB : nt - 1, slot);
-    if constexpr (CK) {
-      static_assert(NS == 4, "a lane's checkpoint is one 16-byte store");
-      bstore4(rCk, ck_lane + static_cast<uint32_t>(tile_of(k)) * 1024u, h);
-    }
+    if constexpr (CKS && T == kBwdTile) store_ck(tile_of(k));
     wave_lds_fence();                    // staged tile k read back before its partials overwrite it
-    do_scan();
+    do_scan(k);
     wave_lds_fence();
     comb_read(k, second);
     wave_lds_fence();
@@ -644,11 +657,22 @@ hipError_t dispatch_mode(const ScanPlan &plan, const ScanArgs &a, hipStream_t s)
 template <typename Tin>
 hipError_t dispatch_dtype(const ScanPlan &plan, const ScanArgs &a, hipStream_t s) {
   if (a.ck[0] != nullptr) {
-    // backward preparation: fp32, no conv, on-chip exchange
+    // backward preparation: fp32, both directions, no conv; the gate's
+    // backward too (dy set) on the on-chip exchange, else checkpoints only
     if constexpr (std::is_same<Tin, float>::value) {
-      if (plan.dirs == 2 && plan.xmode == kXLds && !a.conv)
+      if (plan.dirs == 2 && !a.conv && a.dy != nullptr && plan.xmode == kXLds)
         return a.zoh ? launch_one<float, 4, 2, kXLds, 8, kOptBwdPrep | kOptZoh>(plan, a, s)
                      : launch_one<float, 4, 2, kXLds, 8, kOptBwdPrep>(plan, a, s);
+      if (plan.dirs == 2 && !a.conv && a.dy == nullptr) {
+        if (plan.xmode == kXLds)
+          return a.zoh ? launch_one<float, 4, 2, kXLds, 8, kOptCk | kOptZoh>(plan, a, s)
+                       : launch_one<float, 4, 2, kXLds, 8, kOptCk>(plan, a, s);
+        if (plan.S == 8)
+          return a.zoh ? launch_one<float, 8, 2, kXGlobal, 16, kOptCk | kOptZoh>(plan, a, s)
+                       : launch_one<float, 8, 2, kXGlobal, 16, kOptCk>(plan, a, s);
+        return a.zoh ? launch_one<float, 4, 2, kXGlobal, 16, kOptCk | kOptZoh>(plan, a, s)
+                     : launch_one<float, 4, 2, kXGlobal, 16, kOptCk>(plan, a, s);
+      }
     }
     return hipErrorInvalidValue;
   }

@@ -82,11 +82,12 @@ struct ScanArgs {
   void *out;            // [batch, dim, L] (Tin)
   float *xglobal;       // fp32 exchange rows (long bidirectional), row stride xstride
   int64_t xstride;
-  // Backward preparation (kOptBwdPrep): per direction, the state at every
-  // 8-step tile start (checkpoints laid out as BwdArgs::ck); and in place of
-  // out, the gate's backward from the ungated y: dy = gscale dout SiLU(z),
-  // tile-major as BwdArgs::dy with dy_tiled, and dz = gscale dout y SiLU'(z)
-  // ([batch, dim, L]), both fp32.
+  // Backward preparation: per direction, the state at every 8-step tile
+  // start (checkpoints laid out as BwdArgs::ck; kOptCk, or kOptBwdPrep when
+  // dy is set); with kOptBwdPrep also, in place of out, the gate's backward
+  // from the ungated y: dy = gscale dout SiLU(z), tile-major as BwdArgs::dy
+  // with dy_tiled, and dz = gscale dout y SiLU'(z) ([batch, dim, L]), both
+  // fp32.
   float *ck[2];
   const float *gz, *dout;
   float *dy, *dz;
@@ -100,8 +101,10 @@ struct ScanArgs {
   float scale;          // bidirectional combine scale
 };
 
-// Kernel variants (template bits of the scan kernel).
-enum ScanOpt { kOptZoh = 1, kOptConv = 2, kOptBwdPrep = 4 };
+// Kernel variants (template bits of the scan kernel).  kOptCk stores the
+// backward's checkpoints (ck) only; kOptBwdPrep also forms the gate's
+// backward in place of out (on-chip exchange).
+enum ScanOpt { kOptZoh = 1, kOptConv = 2, kOptBwdPrep = 4, kOptCk = 8 };
 
 // Where a bidirectional scan parks first-visit sums: in LDS (short
 // sequences) or in fp32 global memory.

@@ -1111,6 +1111,47 @@ def test_bwd_bidir(L):
     assert_close(host(dz), wdz, FP32_TOL, "dz")
 
 
+def test_bwd_bidir_two_row_blocks_per_workgroup():
+    """The fused backward preparation in workgroups of two row blocks (83 x
+    25 = 2075 row blocks: the last workgroup's second one is empty, and the
+    last of each batch row has 13 channels), writing tile-major checkpoints
+    and dy that the backward kernel reads."""
+    _case("bwd bidir two row blocks per workgroup")
+    fwd, bwd, z = wl.bidir_inputs(2950, 83, 397, 9, device=DEV, perturb=True)
+    dout = torch.randn(fwd["u"].shape, generator=wl.generator(2951, DEV), device=DEV)
+    gf, gb, dz = vm.vm_bidir_scan_bwd(fwd, bwd, dout, z=z, combine_scale=0.5)
+    torch.cuda.synchronize()
+    wf, wb, wdz, _ = ograd.bidir_scan_grad(host_dir(fwd), host_dir(bwd), host(dout), z=host(z),
+                                           combine_scale=0.5)
+    for k in _GRAD_KEYS:
+        assert_close(host(gf[k]), wf[k], FP32_TOL, f"fwd d{k}")
+        assert_close(host(gb[k]), wb[k], FP32_TOL, f"bwd d{k}")
+    assert_close(host(dz), wdz, FP32_TOL, "dz")
+
+
+@pytest.mark.parametrize("batch,dim", [(2, 44), (64, 256)])
+@pytest.mark.parametrize("zoh", [False, True])
+def test_bwd_bidir_global_exchange_checkpoints_from_forward(batch, dim, zoh):
+    """Long sequences (the global exchange, 8-lane split at 2 x 44 channels,
+    4-lane at 64 x 256): with z, the forward recomputation stores the
+    backward's checkpoints (at visit positions 0 and 8 of its 16-step tiles);
+    without z, the backward kernel runs its own first pass.  The gated call
+    must match the ungated one on dout SiLU(z) (which differs only in the
+    rounding of dy) in every gradient but dz; the oracle checks the gated
+    small case directly in test_bwd_bidir."""
+    _case(f"bwd bidir global exchange ck from forward b{batch} d{dim} zoh{zoh}")
+    L = 600
+    fwd, bwd, z = wl.bidir_inputs(3100 + dim, batch, dim, L, device=DEV, perturb=True)
+    dout = torch.randn(fwd["u"].shape, generator=wl.generator(3200 + dim, DEV), device=DEV)
+    gf, gb, _ = vm.vm_bidir_scan_bwd(fwd, bwd, dout, z=z, combine_scale=0.5, zoh=zoh)
+    d2 = (dout * torch.nn.functional.silu(z)).contiguous()
+    hf, hb, _ = vm.vm_bidir_scan_bwd(fwd, bwd, d2, z=None, combine_scale=0.5, zoh=zoh)
+    torch.cuda.synchronize()
+    for k in _GRAD_KEYS:
+        assert_close(host(gf[k]), host(hf[k]), FP32_TOL, f"fwd d{k}")
+        assert_close(host(gb[k]), host(hb[k]), FP32_TOL, f"bwd d{k}")
+
+
 def test_bwd_bf16():
     # bf16 inputs: the pass runs in fp32 on their exact widening, so the
     # gradients match the oracle's (on the same bf16 values) to fp32 accuracy
