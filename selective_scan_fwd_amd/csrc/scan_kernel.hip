@@ -155,7 +155,8 @@ __host__ __device__ inline int xchg_stride(int64_t n, int T) {
 // Register budget: 4 waves per SIMD with 8-step tiles (3 with the fused
 // conv, whose weights and carried inputs do not fit 128 VGPRs), 2 with
 // 16-step tiles (whose three tiles in flight and staged copies need about
-// 190 VGPRs, 240 with the conv).
+// 190 VGPRs, 240 with the conv), 3 with 16-step tiles and the 8-lane split
+// (about 150; 2 with ZOH and the conv together).
 // A bidirectional workgroup holds one or two row blocks (DIRS waves each):
 // with two, its four waves land on distinct SIMDs and every SIMD of a CU
 // carries the same number of waves.
