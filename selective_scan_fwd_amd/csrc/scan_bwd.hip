@@ -175,9 +175,9 @@ scan_bwd_kernel(const Arg arg) {
   // (a line stored piecewise, one tile apart, is fetched and written back
   // several times).  The ZOH variant, whose registers are tight at one wave
   // per SIMD, stores directly.  A row's items are the lines between its
-  // boundaries and the partial lines at its two ends.  Per row (wave-uniform): tb0, its
-  // first boundary; the tiles j that complete one of its lines are those
-  // with j mod 4 == its class; and such an item starts at 8 j + d (visiting
+  // boundaries and the partial lines at its two ends.  Per row (wave-uniform):
+  // tb0, its first boundary; the tiles j that complete one of its lines are
+  // those with j mod 4 == its class; such an item starts at 8 j + d (visiting
   // backward in t) or ends at 8 j + 1 + d (visiting forward in t, rev).
   static_assert(T == 8, "four tiles per 128-byte line");
   const uint32_t e0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p.du) >> 2) +
