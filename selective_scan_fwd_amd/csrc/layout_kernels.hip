@@ -115,6 +115,72 @@ __device__ __forceinline__ void copy_to_lds4(T *dst, const T *__restrict__ src, 
   }
 }
 
+// Rows whose length or start is not a multiple of 4 (the 57 x 57 map: 3249
+// pixels per plane, 841 steps per stream), in a tensor whose start is
+// aligned to 4 values.  The n values at element offset `base` go to LDS with
+// aligned 4-value loads: LDS element (base % 4) + e holds value e.  A chunk
+// may cover up to 3 values of the neighbouring rows (read, never used); the
+// tensor's last partial chunk is read value by value.  Returns base % 4.
+template <typename T>
+__device__ __forceinline__ int copy_to_lds_chunks(T *lds, const T *__restrict__ tensor, int64_t base, int n,
+                                                  int64_t total) {
+  using V = typename Raw4<T>::V;
+  constexpr int U = 4;
+  const int off = static_cast<int>(base & 3);
+  const T *a0 = tensor + (base - off);
+  const int n4 = (off + n + 3) / 4;
+  const int64_t inside = (total - (base - off)) / 4;    // chunks wholly inside the tensor
+  for (int i0 = threadIdx.x; i0 < n4; i0 += U * kThreads) {
+    V v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kThreads;
+      v[u] = i < n4 && i < inside ? load_raw4_stream(a0 + 4 * i) : V{};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kThreads;
+      if (i >= n4) continue;
+      if (i < inside) {
+        reinterpret_cast<V *>(lds)[i] = v[u];
+      } else {
+        for (int w = 0; w < 4; ++w)
+          lds[4 * i + w] = base - off + 4 * i + w < total ? a0[4 * i + w] : T(0);
+      }
+    }
+  }
+  return off;
+}
+
+// Writes the n values of a row at element offset `base` of a tensor aligned
+// to 4 values: the values before the first 4-value boundary and after the
+// last one one by one, the rest as aligned 4-value stores.  f4(t, v) gives
+// values t .. t+3 (the last ones may lie past the row: unused).
+template <typename T, typename F4>
+__device__ __forceinline__ void store_row_chunks(T *tensor, int64_t base, int n, F4 &&f4, bool stream) {
+  using V = typename Raw4<T>::V;
+  const int lead = static_cast<int>((4 - (base & 3)) & 3);
+  const int head = lead < n ? lead : n;
+  const int n4 = (n - head) / 4;
+  const int tail = n - head - 4 * n4;
+  T *row = tensor + base;
+  for (int j = threadIdx.x; j < n4; j += kThreads) {
+    const int t = head + 4 * j;
+    T v[4];
+    f4(t, v);
+    const V w = Raw4<T>::pack(v[0], v[1], v[2], v[3]);
+    if (stream) store_raw4_stream(row + t, w);
+    else store_raw4(row + t, w);
+  }
+  const int e = static_cast<int>(threadIdx.x);
+  if (e < head + tail) {
+    const int t = e < head ? e : head + 4 * n4 + (e - head);
+    T v[4];
+    f4(t, v);
+    row[t] = v[0];
+  }
+}
+
 // One workgroup per (b, c) plane: stage the plane in LDS with coalesced
 // loads, then emit the four streams with coalesced stores.  Vector path
 // (staged, H W and Lg multiples of 4, aligned pointers): 4-value loads and
@@ -129,6 +195,28 @@ atrous_gather_kernel(const T *__restrict__ x, T *__restrict__ streams, int64_t c
   const int64_t b = pid / ch, c = pid - b * ch;
   const int hr = (H + 1) / 2, hc = (W + 1) / 2, Lg = hr * hc;
   const T *src = x + pid * H * W;
+  if (vec == 2) {
+    // rows of any length: aligned 4-value chunks (copy_to_lds_chunks,
+    // store_row_chunks); every value computed as on the other paths
+    const int off = copy_to_lds_chunks(plane, x, pid * H * W, H * W, gridDim.x * static_cast<int64_t>(H) * W);
+    __syncthreads();
+    const T *pl = plane + off;
+    for (int k = 0; k < 4; ++k) {
+      const int n = (k & 1) == 0 ? hc : hr;
+      store_row_chunks(streams, ((b * 4 + k) * ch + c) * Lg, Lg,
+                       [&](int t, T (&v)[4]) __attribute__((always_inline)) {
+        int la = t / n, lb = t - la * n;               // (line, position) of step t
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = (k & 1) == 0 ? la : lb, cc = (k & 1) == 0 ? lb : la;
+          const int yy = 2 * r + (k & 1), xx = 2 * cc + (k >> 1);
+          v[u] = (yy < H && xx < W) ? pl[yy * W + xx] : T(0);
+          if (++lb == n) { lb = 0; ++la; }
+        }
+      }, false);
+    }
+    return;
+  }
   if (vec) {
     copy_to_lds4(plane, src, H * W);
     __syncthreads();
@@ -187,6 +275,29 @@ atrous_scatter_kernel(const T *__restrict__ streams, T *__restrict__ y, int64_t 
   const int64_t pid = blockIdx.x;
   const int64_t b = pid / ch, c = pid - b * ch;
   const int hr = (H + 1) / 2, hc = (W + 1) / 2, Lg = hr * hc;
+  if (vec == 2) {
+    // rows of any length (see the gather): each stream at its own LDS slot
+    // of SL values, shifted by its start's offset within a 4-value chunk
+    const int SL = (Lg + 3) / 4 * 4 + 4;
+    const int64_t total = static_cast<int64_t>(gridDim.x) * 4 * Lg;
+    // the four streams' shifts, two bits each (arithmetic, not a table)
+    int offs = 0;
+    for (int k = 0; k < 4; ++k)
+      offs |= copy_to_lds_chunks(st + k * SL, streams, ((b * 4 + k) * ch + c) * Lg, Lg, total) << (2 * k);
+    __syncthreads();
+    store_row_chunks(y, pid * H * W, H * W, [&](int i, T (&v)[4]) __attribute__((always_inline)) {
+      int yy = i / W, xx = i - yy * W;                 // pixel i; then along the row
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = (yy & 1) + 2 * (xx & 1);
+        const int sk = k * SL + ((offs >> (2 * k)) & 3);
+        const int r = yy >> 1, cc = xx >> 1;
+        v[u] = (yy < H) ? st[sk + ((yy & 1) == 0 ? r * hc + cc : cc * hr + r)] : T(0);
+        if (++xx == W) { xx = 0; ++yy; }
+      }
+    }, true);
+    return;
+  }
   if (vec) {
     for (int k = 0; k < 4; ++k) copy_to_lds4(st + k * Lg, streams + ((b * 4 + k) * ch + c) * Lg, Lg);
     __syncthreads();
@@ -787,11 +898,15 @@ hipError_t launch_atrous_gather(const void *x, void *streams, int64_t batch, int
                                 int64_t H, int64_t W, bool bf16, hipStream_t s) {
   const int64_t planes = batch * ch;
   if (planes == 0) return hipSuccess;
-  const int staged = (H * W <= kPlaneLds) ? 1 : 0;
-  const size_t lds = staged ? static_cast<size_t>(H * W) * (bf16 ? 2 : 4) : 0;
   const int64_t Lg = ((H + 1) / 2) * ((W + 1) / 2);
   const uintptr_t va = bf16 ? 8 : 16;
-  const int vec = staged && (H * W) % 4 == 0 && Lg % 4 == 0 && aligned(x, va) && aligned(streams, va);
+  // vec 1: rows that are multiples of 4 values; vec 2: any rows, chunked
+  // (aligned tensors, the staged plane with room for the chunks' margins)
+  const bool al = aligned(x, va) && aligned(streams, va);
+  int vec = (H * W <= kPlaneLds) && (H * W) % 4 == 0 && Lg % 4 == 0 && al ? 1 : 0;
+  if (vec == 0 && H * W + 8 <= kPlaneLds && al && planes * H * W < (int64_t{1} << 31)) vec = 2;
+  const int staged = (vec != 0 || H * W <= kPlaneLds) ? 1 : 0;
+  const size_t lds = staged ? static_cast<size_t>(H * W + 8) * (bf16 ? 2 : 4) : 0;
   if (bf16)
     hipLaunchKernelGGL(atrous_gather_kernel<bf16_t>, dim3(planes), dim3(kThreads), lds, s,
                        static_cast<const bf16_t *>(x), static_cast<bf16_t *>(streams), ch,
@@ -808,10 +923,13 @@ hipError_t launch_atrous_scatter(const void *streams, void *y, int64_t batch, in
   const int64_t planes = batch * ch;
   if (planes == 0) return hipSuccess;
   const int64_t Lg = ((H + 1) / 2) * ((W + 1) / 2);
-  const int staged = (4 * Lg <= kPlaneLds) ? 1 : 0;
-  const size_t lds = staged ? static_cast<size_t>(4 * Lg) * (bf16 ? 2 : 4) : 0;
   const uintptr_t va = bf16 ? 8 : 16;
-  const int vec = staged && Lg % 4 == 0 && W % 4 == 0 && aligned(streams, va) && aligned(y, va);
+  const bool al = aligned(streams, va) && aligned(y, va);
+  const int64_t SL = (Lg + 3) / 4 * 4 + 4;              // the chunked path's LDS slot per stream
+  int vec = (4 * Lg <= kPlaneLds) && Lg % 4 == 0 && W % 4 == 0 && al ? 1 : 0;
+  if (vec == 0 && 4 * SL <= kPlaneLds && al && planes * 4 * Lg < (int64_t{1} << 31)) vec = 2;
+  const int staged = (vec != 0 || 4 * Lg <= kPlaneLds) ? 1 : 0;
+  const size_t lds = staged ? static_cast<size_t>(4 * SL) * (bf16 ? 2 : 4) : 0;
   if (bf16)
     hipLaunchKernelGGL(atrous_scatter_kernel<bf16_t>, dim3(planes), dim3(kThreads), lds, s,
                        static_cast<const bf16_t *>(streams), static_cast<bf16_t *>(y), ch,
