@@ -364,6 +364,33 @@ scan_bwd_kernel(const Arg arg) {
     gn[j] = 0.0f;
     dA[j] = 0.0f;
   }
+  // Sums over the block's channels per (n, step) of tile j: dC_t of dy_t h_t,
+  // dB_t of g_t dt_t u_t.  The contributions meet in LDS, the dB ones in the
+  // same area after the dC ones are read (each hand-over between lanes
+  // ordered by wave_lds_fence).
+  auto reduce_red = [&](const Rsrc &dst, int j) {
+#pragma unroll
+    for (int m = 0; m < 16 * T / 64; ++m) {
+      const int c = lane + 64 * m;                  // (n, q), q fastest
+      const int q = c % T, n = c / T;
+      const float4 *src = reinterpret_cast<const float4 *>(red + c * Lay::RSTR + (n / 4) * 16);
+      float sum = 0.0f;
+#pragma unroll
+      for (int v = 0; v < kR / 4; ++v) {
+        const float4 x4 = src[v];
+        sum += (x4.x + x4.y) + (x4.z + x4.w);
+      }
+      bstore<float>(dst, static_cast<uint32_t>((j * 16 + n) * T + (rev ? T - 1 - q : q)) * 4u, sum);
+    }
+  };
+  // A tile's last stores (its dB sums and the output lines it completes) go
+  // out in the next iteration, before that iteration's loads: vector memory
+  // counts loads and stores in one in-order counter, so stores issued after
+  // a tile's loads would hold up the wait for those loads.
+  auto finish_tile = [&](int j, bool last) {
+    if constexpr (!ZOH) flush_lines(j, last);
+    reduce_red(rPB, j);
+  };
   stage_load(tile_of(nt - 1), true);
   for (int k = nt - 1; k >= 0; --k) {
     const int j = tile_of(k);
@@ -377,6 +404,10 @@ scan_bwd_kernel(const Arg arg) {
       // the 8-lane split may not cover them; their state stays zero)
       hc[jn] = r < rows ? pin(lk[jn]) : 0.0f;
       h0[jn] = hc[jn];
+    }
+    if (k < nt - 1) {
+      finish_tile(tile_of(k + 1), false);
+      wave_lds_fence();                  // its dB sums are read before the dC ones are written
     }
     stage_load(tile_of(k > 0 ? k - 1 : 0), true);
     // recompute the tile's states and decays (the staged step values and
@@ -411,31 +442,13 @@ scan_bwd_kernel(const Arg arg) {
       }
     }
     const int jT = j * T;
-    // dC_t = sum over the block's channels of dy_t h_t, per (n, step): the
-    // contributions meet in LDS, and the dB ones reuse the area afterwards
-    // (each hand-over between lanes ordered by wave_lds_fence).
-    auto reduce_red = [&](const Rsrc &dst) {
-#pragma unroll
-      for (int m = 0; m < 16 * T / 64; ++m) {
-        const int c = lane + 64 * m;                  // (n, q), q fastest
-        const int q = c % T, n = c / T;
-        const float4 *src = reinterpret_cast<const float4 *>(red + c * Lay::RSTR + (n / 4) * 16);
-        float sum = 0.0f;
-#pragma unroll
-        for (int v = 0; v < kR / 4; ++v) {
-          const float4 x4 = src[v];
-          sum += (x4.x + x4.y) + (x4.z + x4.w);
-        }
-        bstore<float>(dst, static_cast<uint32_t>((j * 16 + n) * T + (rev ? T - 1 - q : q)) * 4u, sum);
-      }
-    };
 #pragma unroll
     for (int q = 0; q < T; ++q)
 #pragma unroll
       for (int jn = 0; jn < kNS; ++jn)
         red[((n0 + jn) * T + q) * Lay::RSTR + sp * 16 + r] = pqs[q].z * hs[q][jn];
     wave_lds_fence();
-    reduce_red(rPC);
+    reduce_red(rPC, j);
     wave_lds_fence();
     // adjoint back through the tile: g = C dy + a_{t+1} g_{t+1} per state
     // (accumulated in place of gn), sum_n g B into sgB, sum_n g a h A into
@@ -517,13 +530,9 @@ scan_bwd_kernel(const Arg arg) {
       accD[i] = __builtin_fmaf(edy[i], eu[i], accD[i]);
       accB[i] += dd;
     }
-    if constexpr (!ZOH) {
-      wave_lds_fence();
-      flush_lines(j, k == 0);
-    }
-    // dB: this block's sum over its 16 channels, per (n, step)
-    reduce_red(rPB);
   }
+  wave_lds_fence();
+  finish_tile(tile_of(0), true);
 
   // ---- per batch row: dA, and dD, dbias (the T lanes of a channel summed)
   const int64_t prow = static_cast<int64_t>(b) * dim + d0;
