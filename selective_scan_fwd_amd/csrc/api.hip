@@ -985,14 +985,23 @@ int vm_ss2d_scan_bwd(const vm_scan_dir *dirs, const void *u, const void *z, cons
       a[pass].ck[1] = bs[2 * pass + 1].ck;
       if (st == VM_OK) st = launch_bidir(a[pass], false, ws, s);
     }
-    // y = y_r + transpose(y_c) for dz; the transpose lands in dus[0] (free
-    // until the first backward)
-    if (st == VM_OK) st = hip_status(vmk::launch_transpose(yc, dus[0], planes, width, height, false, s));
   }
-  if (st == VM_OK)
-    st = hip_status(vmk::launch_gate_bwd(yr, z32, dout32, g, static_cast<float *>(dz), tok, combine_scale,
-                                         s, z != nullptr ? dus[0] : nullptr));
-  if (st == VM_OK) st = hip_status(vmk::launch_transpose(g, gt, planes, height, width, false, s));
+  // the output gradient in both layouts (and dz, from y = y_r + transpose(y_c)):
+  // one fused kernel on four-wide tiles, else the transposes and the
+  // elementwise gate (the transpose of y_c lands in dus[0], free until the
+  // first backward)
+  const bool tile4 = vmk::ss2d_tile4_ok(height, width, {yr, yc, z32, dout32, g, gt, dz, du, dus[0], dus[1],
+                                                       dus[2], dus[3]});
+  if (st == VM_OK && tile4) {
+    st = hip_status(vmk::launch_ss2d_gate_bwd(yr, yc, z32, dout32, g, gt, static_cast<float *>(dz), planes,
+                                              height, width, combine_scale, s));
+  } else if (st == VM_OK) {
+    if (z != nullptr) st = hip_status(vmk::launch_transpose(yc, dus[0], planes, width, height, false, s));
+    if (st == VM_OK)
+      st = hip_status(vmk::launch_gate_bwd(yr, z32, dout32, g, static_cast<float *>(dz), tok, combine_scale,
+                                           s, z != nullptr ? dus[0] : nullptr));
+    if (st == VM_OK) st = hip_status(vmk::launch_transpose(g, gt, planes, height, width, false, s));
+  }
   // the four backward scans in one launch: rows on g, columns on its transpose
   vm_scan_grad gk[4];
   const vm_scan_dir *pk[4];
@@ -1009,7 +1018,10 @@ int vm_ss2d_scan_bwd(const vm_scan_dir *dirs, const void *u, const void *z, cons
   if (st == VM_OK)
     st = run_bwd_group(4, pk, dyk, gkp, bs, batch, dim, L, dstate, options, revk, ws, s,
                        z != nullptr ? Prep::kCk : Prep::kNone);
-  // du = du_0 + du_1 + transpose(du_2 + du_3), through g and gt (free now)
+  // du = (du_0 + du_1) + transpose(du_2 + du_3): fused on four-wide tiles,
+  // else through g and gt (free now)
+  if (st == VM_OK && tile4)
+    return hip_status(vmk::launch_ss2d_du_sum(dus[0], dus[1], dus[2], dus[3], du, planes, height, width, s));
   if (st == VM_OK) st = hip_status(vmk::launch_add(dus[2], dus[3], nullptr, g, tok, s));
   if (st == VM_OK) st = hip_status(vmk::launch_transpose(g, gt, planes, width, height, false, s));
   if (st == VM_OK) st = hip_status(vmk::launch_add(dus[0], dus[1], gt, du, tok, s));

@@ -614,6 +614,141 @@ ss2d_merge4_kernel(const float *yr, const float *__restrict__ yc, const T *__res
   }
 }
 
+// The gate's backward for the four-direction scan, writing the output
+// gradient in both layouts the backward scans read: with y = yr[p][i][j] +
+// yc[p][j][i] (the row and column traversals' sums), g = scale dout SiLU(z)
+// goes to dy ([P][H][W]) and dyt ([P][W][H]), and dz = scale dout y SiLU'(z),
+// SiLU'(z) = s (1 + z (1 - s)), s = sigmoid(z).  Without z, g = scale dout
+// (yr, yc, dz unused).  64 x 64 tiles, four values per access, as the merge.
+__global__ void __launch_bounds__(kThreads)
+ss2d_gate_bwd4_kernel(const float *__restrict__ yr, const float *__restrict__ yc,
+                      const float *__restrict__ z, const float *__restrict__ dout,
+                      float *__restrict__ dy, float *__restrict__ dyt, float *__restrict__ dz,
+                      int H, int W, int tiles_w, float scale) {
+  __shared__ float tile[kTile4][kTile4 + 1];
+  const int64_t pl = blockIdx.x;
+  const int ti = blockIdx.y / tiles_w, tj = blockIdx.y - (blockIdx.y / tiles_w) * tiles_w;
+  const int i0 = ti * kTile4, j0 = tj * kTile4;
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  const int64_t base = pl * H * W;
+  float4 g4[4];
+  if (z != nullptr) {
+    float4 v[4], r4[4], z4[4], d4[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {                           // yc rows j, contiguous in i
+      const int j = j0 + ty + 16 * k, i = i0 + 4 * tx;
+      v[k] = (i < H && j < W) ? load4(yc + base + static_cast<int64_t>(j) * H + i)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {                           // yr, z, dout rows i, contiguous in j
+      const int i = i0 + ty + 16 * k, j = j0 + 4 * tx;
+      const bool ok = i < H && j < W;
+      const int64_t e = base + static_cast<int64_t>(i) * W + j;
+      r4[k] = ok ? load4(yr + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+      z4[k] = ok ? load4(z + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+      d4[k] = ok ? load4(dout + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float *t = &tile[ty + 16 * k][4 * tx];
+      t[0] = v[k].x; t[1] = v[k].y; t[2] = v[k].z; t[3] = v[k].w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = ty + 16 * k, i = i0 + r, j = j0 + 4 * tx;
+      const float yv[4] = {r4[k].x + tile[4 * tx][r], r4[k].y + tile[4 * tx + 1][r],
+                           r4[k].z + tile[4 * tx + 2][r], r4[k].w + tile[4 * tx + 3][r]};
+      const float zv[4] = {z4[k].x, z4[k].y, z4[k].z, z4[k].w};
+      const float dv[4] = {d4[k].x, d4[k].y, d4[k].z, d4[k].w};
+      float gy[4], gz[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float g = scale * dv[c];
+        const float sg = hw_rcp(1.0f + hw_exp2(-zv[c] * kLog2e));
+        gy[c] = g * zv[c] * sg;
+        gz[c] = g * yv[c] * (sg * __builtin_fmaf(zv[c], 1.0f - sg, 1.0f));
+      }
+      g4[k] = make_float4(gy[0], gy[1], gy[2], gy[3]);
+      if (i < H && j < W) {
+        const int64_t e = base + static_cast<int64_t>(i) * W + j;
+        store4(dy + e, g4[k]);
+        store4(dz + e, make_float4(gz[0], gz[1], gz[2], gz[3]));
+      }
+    }
+    __syncthreads();                                         // the tile is read before it is refilled
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = i0 + ty + 16 * k, j = j0 + 4 * tx;
+      const int64_t e = base + static_cast<int64_t>(i) * W + j;
+      const float4 d = (i < H && j < W) ? load4(dout + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+      g4[k] = make_float4(scale * d.x, scale * d.y, scale * d.z, scale * d.w);
+      if (i < H && j < W) store4(dy + e, g4[k]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float *t = &tile[ty + 16 * k][4 * tx];
+    t[0] = g4[k].x; t[1] = g4[k].y; t[2] = g4[k].z; t[3] = g4[k].w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {                             // dyt rows j, contiguous in i
+    const int r = ty + 16 * k, j = j0 + r, i = i0 + 4 * tx;
+    if (i < H && j < W)
+      store4(dyt + base + static_cast<int64_t>(j) * H + i,
+             make_float4(tile[4 * tx][r], tile[4 * tx + 1][r], tile[4 * tx + 2][r], tile[4 * tx + 3][r]));
+  }
+}
+
+// The map's gradient from the four traversals' ones:
+// du[p][i][j] = (d0 + d1)[p][i][j] + (d2 + d3)[p][j][i], where d0, d1 are the
+// row traversals' ([P][H][W]) and d2, d3 the column traversals' ([P][W][H]).
+__global__ void __launch_bounds__(kThreads)
+ss2d_du_sum4_kernel(const float *__restrict__ d0, const float *__restrict__ d1,
+                    const float *__restrict__ d2, const float *__restrict__ d3,
+                    float *__restrict__ du, int H, int W, int tiles_w) {
+  __shared__ float tile[kTile4][kTile4 + 1];
+  const int64_t pl = blockIdx.x;
+  const int ti = blockIdx.y / tiles_w, tj = blockIdx.y - (blockIdx.y / tiles_w) * tiles_w;
+  const int i0 = ti * kTile4, j0 = tj * kTile4;
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  const int64_t base = pl * H * W;
+  float4 a4[4], b4[4], c4[4], e4[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {                             // d2, d3 rows j, contiguous in i
+    const int j = j0 + ty + 16 * k, i = i0 + 4 * tx;
+    const bool ok = i < H && j < W;
+    const int64_t e = base + static_cast<int64_t>(j) * H + i;
+    c4[k] = ok ? load4(d2 + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    e4[k] = ok ? load4(d3 + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {                             // d0, d1 rows i, contiguous in j
+    const int i = i0 + ty + 16 * k, j = j0 + 4 * tx;
+    const bool ok = i < H && j < W;
+    const int64_t e = base + static_cast<int64_t>(i) * W + j;
+    a4[k] = ok ? load4(d0 + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    b4[k] = ok ? load4(d1 + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float *t = &tile[ty + 16 * k][4 * tx];
+    t[0] = c4[k].x + e4[k].x; t[1] = c4[k].y + e4[k].y; t[2] = c4[k].z + e4[k].z; t[3] = c4[k].w + e4[k].w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = ty + 16 * k, i = i0 + r, j = j0 + 4 * tx;
+    if (i < H && j < W)
+      store4(du + base + static_cast<int64_t>(i) * W + j,
+             make_float4((a4[k].x + b4[k].x) + tile[4 * tx][r], (a4[k].y + b4[k].y) + tile[4 * tx + 1][r],
+                         (a4[k].z + b4[k].z) + tile[4 * tx + 2][r], (a4[k].w + b4[k].w) + tile[4 * tx + 3][r]));
+  }
+}
+
 // out[p][i][j] = scale * (yr[p][i][j] + yc[p][j][i]) * SiLU(z[p][i][j]):
 // yr holds the row traversals' sum ([P][H][W], fp32, may be out itself),
 // yc the column traversals' ([P][W][H], fp32).  z may be NULL.
@@ -1044,6 +1179,32 @@ hipError_t launch_transpose(const void *in, void *out, int64_t planes, int64_t H
     hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(kThreads), 0, s,
                        static_cast<const float *>(in), static_cast<float *>(out),
                        static_cast<int>(H), static_cast<int>(W), tw);
+  return hipGetLastError();
+}
+
+bool ss2d_tile4_ok(int64_t H, int64_t W, std::initializer_list<const void *> ptrs) {
+  return tile4_ok(H, W, ptrs, false);
+}
+
+hipError_t launch_ss2d_gate_bwd(const float *yr, const float *yc, const float *z, const float *dout,
+                                float *dy, float *dyt, float *dz, int64_t planes, int64_t H, int64_t W,
+                                float scale, hipStream_t s) {
+  if (planes * H * W == 0) return hipSuccess;
+  if (!tile4_ok(H, W, {yr, yc, z, dout, dy, dyt, dz}, false)) return hipErrorInvalidValue;
+  const int th = static_cast<int>((H + kTile4 - 1) / kTile4), tw = static_cast<int>((W + kTile4 - 1) / kTile4);
+  hipLaunchKernelGGL(ss2d_gate_bwd4_kernel, dim3(static_cast<unsigned>(planes), static_cast<unsigned>(th * tw)),
+                     dim3(kThreads), 0, s, yr, yc, z, dout, dy, dyt, dz, static_cast<int>(H),
+                     static_cast<int>(W), tw, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_ss2d_du_sum(const float *d0, const float *d1, const float *d2, const float *d3,
+                              float *du, int64_t planes, int64_t H, int64_t W, hipStream_t s) {
+  if (planes * H * W == 0) return hipSuccess;
+  if (!tile4_ok(H, W, {d0, d1, d2, d3, du}, false)) return hipErrorInvalidValue;
+  const int th = static_cast<int>((H + kTile4 - 1) / kTile4), tw = static_cast<int>((W + kTile4 - 1) / kTile4);
+  hipLaunchKernelGGL(ss2d_du_sum4_kernel, dim3(static_cast<unsigned>(planes), static_cast<unsigned>(th * tw)),
+                     dim3(kThreads), 0, s, d0, d1, d2, d3, du, static_cast<int>(H), static_cast<int>(W), tw);
   return hipGetLastError();
 }
 

@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <initializer_list>
 #include <stdint.h>
 
 namespace vmk {
@@ -222,5 +224,17 @@ hipError_t launch_transpose(const void *in, void *out, int64_t planes, int64_t H
 hipError_t launch_ss2d_merge(const float *yr, const float *yc, const void *z, void *out,
                              int64_t planes, int64_t H, int64_t W, float scale, bool bf16,
                              hipStream_t s);
+// The fused four-wide forms of the SS2D backward's layout steps (fp32): they
+// need H % 4 == 0, W % 4 == 0 and 16-byte aligned tensors (ss2d_tile4_ok),
+// else hipErrorInvalidValue.  Gate backward: y = yr + transpose(yc),
+// dy = scale dout SiLU(z) in [planes][H][W] and dyt = its [planes][W][H]
+// transpose, dz = scale dout y SiLU'(z); z NULL: dy = scale dout.
+bool ss2d_tile4_ok(int64_t H, int64_t W, std::initializer_list<const void *> ptrs);
+hipError_t launch_ss2d_gate_bwd(const float *yr, const float *yc, const float *z, const float *dout,
+                                float *dy, float *dyt, float *dz, int64_t planes, int64_t H, int64_t W,
+                                float scale, hipStream_t s);
+// du = (d0 + d1) + transpose(d2 + d3); d0, d1, du [planes][H][W], d2, d3 [planes][W][H].
+hipError_t launch_ss2d_du_sum(const float *d0, const float *d1, const float *d2, const float *d3,
+                              float *du, int64_t planes, int64_t H, int64_t W, hipStream_t s);
 
 }  // namespace vmk

@@ -1261,6 +1261,40 @@ def test_ss2d_bwd_zoh_per_direction_launches():
     _ss2d_bwd_check(u, dirs, dout, z, "ss2d bwd zoh per-direction", scale=0.5, zoh=True)
 
 
+@pytest.mark.parametrize("H,W,dtype,gated,zoh", [(8, 12, torch.float32, True, False),
+                                                  (12, 8, torch.bfloat16, True, False),
+                                                  (4, 16, torch.float32, True, True),
+                                                  (12, 4, torch.float32, False, False)])
+def test_ss2d_bwd_four_wide_tiles(H, W, dtype, gated, zoh):
+    """Maps with H and W multiples of 4 take the fused four-wide gate and
+    map-gradient kernels (both layouts of the output gradient, the summed
+    map gradient); the other SS2D backward cases take the separate ones."""
+    _case(f"ss2d bwd four-wide {H}x{W} {dtype} gated{gated} zoh{zoh}")
+    u, dirs, z = wl.ss2d_inputs(4460 + H * W, 2, 40, H, W, device=DEV, dtype=dtype, gated=gated,
+                                perturb=True)
+    dout = torch.randn(u.shape, generator=wl.generator(4461 + H, DEV), device=DEV).to(dtype)
+    _ss2d_bwd_check(u, dirs, dout, z, f"ss2d bwd four-wide {H}x{W}", scale=0.5, zoh=zoh)
+
+
+def test_ss2d_bwd_four_wide_tiles_ragged():
+    # 68 x 72: two 64 x 64 tiles per axis, the second one partial; sampled
+    # (batch row, channel) pairs against the oracle
+    _case("ss2d bwd four-wide 68x72 (sampled)")
+    u, dirs, z = wl.ss2d_inputs(4470, 2, 40, 68, 72, device=DEV, perturb=True)
+    dout = torch.randn(u.shape, generator=wl.generator(4471, DEV), device=DEV)
+    du, grads, dz = vm.vm_ss2d_scan_bwd(u, dirs, dout, z=z, combine_scale=0.5)
+    torch.cuda.synchronize()
+    bsel, dsel = [1], [0, 39]
+    hd = [sub_dir(host_dir(p), bsel, dsel) for p in dirs]
+    sel = lambda t: t[bsel][:, dsel]
+    wdu, wg, wdz, _ = ograd.ss2d_scan_grad(sel(host(u)), hd, sel(host(dout)), z=sel(host(z)),
+                                           combine_scale=0.5)
+    assert_close(sel(host(du)), wdu, FP32_TOL, "ss2d 68x72 du (sampled)")
+    assert_close(sel(host(dz)), wdz, FP32_TOL, "ss2d 68x72 dz (sampled)")
+    for k in range(4):
+        assert_close(sel(host(grads[k]["delta"])), wg[k]["delta"], FP32_TOL, f"ss2d 68x72 dir{k} ddelta")
+
+
 def test_full_ss2d_bwd():
     # the full-size 2-D scan's backward; the map, delta and gate gradients of
     # sampled (batch row, channel) pairs depend on that pair's inputs only
