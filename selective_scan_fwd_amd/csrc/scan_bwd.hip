@@ -278,7 +278,10 @@ scan_bwd_kernel(const Arg arg) {
       const uint32_t o = pin_u(in_seq ? ob[i] + static_cast<uint32_t>(jT) * 4u : kOob);
       lu[i] = bload<float>(rU, o);
       ld[i] = bload<float>(rDl, o);
-      ly[i] = pass2 ? bload<float>(rDy, pin_u(in_seq ? oy[i] + static_cast<uint32_t>(j) * dy_tile_bytes : kOob))
+      // (tile-major dy has slots for all 16 rows of the block; rows past dim
+      // read 0, as they do from the flat layout, whose range ends at dim)
+      ly[i] = pass2 ? bload<float>(rDy, pin_u(in_seq && srow[i] < rows
+                                                  ? oy[i] + static_cast<uint32_t>(j) * dy_tile_bytes : kOob))
                     : 0.0f;
     }
     const uint32_t tb = static_cast<uint32_t>(jT) * bst_bytes;

@@ -590,9 +590,13 @@ scan_kernel(const ScanArgs p) {
 
   // ---- short sequences: the block's [rows x L] slab of out is complete in
   // LDS (scaled and gated); write it in flat order (coalesced, whole lines).
+  // With the backward preparation each element also loads z and dout: 16
+  // elements per thread per pass keep those loads in flight together (the
+  // scan's registers are free by now).  (Done here rather than per tile in
+  // the scan loop, whose issue slots the extra exponentials would take.)
   if (XMODE == kXLds) {
     lds_barrier();
-    constexpr int NT = 64 * DIRS, U = 4;
+    constexpr int NT = 64 * DIRS, U = CK ? 16 : 4;
     const int n = rows * L;
     const int tid = static_cast<int>(threadIdx.x) - sub * NT;
     int fr = tid / L, ft = tid % L;

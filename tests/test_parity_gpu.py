@@ -1129,6 +1129,29 @@ def test_bwd_bidir_two_row_blocks_per_workgroup():
     assert_close(host(dz), wdz, FP32_TOL, "dz")
 
 
+def test_bwd_bidir_tiled_dy_rows_past_dim_ignored():
+    """The tile-major output gradient has slots for all 16 channels of a
+    block; with 29 channels the last block's three spare slots are never
+    written, and the backward must not read them.  A first call with 32
+    channels and a NaN output gradient (the same workspace sizes) leaves NaN
+    in the workspace the second call is likely to be given back; the second
+    call's gradients must still match the oracle."""
+    _case("bwd bidir tiled dy rows past dim")
+    fwd, bwd, z = wl.bidir_inputs(2960, 3, 32, 40, device=DEV, perturb=True)
+    dout = torch.full(fwd["u"].shape, float("nan"), device=DEV)
+    vm.vm_bidir_scan_bwd(fwd, bwd, dout, z=z, combine_scale=0.5)
+    fwd, bwd, z = wl.bidir_inputs(2961, 3, 29, 40, device=DEV, perturb=True)
+    dout = torch.randn(fwd["u"].shape, generator=wl.generator(2962, DEV), device=DEV)
+    gf, gb, dz = vm.vm_bidir_scan_bwd(fwd, bwd, dout, z=z, combine_scale=0.5)
+    torch.cuda.synchronize()
+    wf, wb, wdz, _ = ograd.bidir_scan_grad(host_dir(fwd), host_dir(bwd), host(dout), z=host(z),
+                                           combine_scale=0.5)
+    for k in _GRAD_KEYS:
+        assert_close(host(gf[k]), wf[k], FP32_TOL, f"fwd d{k}")
+        assert_close(host(gb[k]), wb[k], FP32_TOL, f"bwd d{k}")
+    assert_close(host(dz), wdz, FP32_TOL, "dz")
+
+
 @pytest.mark.parametrize("batch,dim", [(2, 44), (64, 256)])
 @pytest.mark.parametrize("zoh", [False, True])
 def test_bwd_bidir_global_exchange_checkpoints_from_forward(batch, dim, zoh):
