@@ -101,6 +101,7 @@ struct ScanArgs {
   int conv;             // u holds the conv input x; the scan uses SiLU(conv(x))
   int reverse;          // one-direction scans only
   float scale;          // bidirectional combine scale
+  int prio_from;        // (set at launch) first workgroup past the first round
 };
 
 // Kernel variants (template bits of the scan kernel).  kOptCk stores the
