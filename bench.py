@@ -8,10 +8,12 @@ token-major, as the block's projection produces them).
 
 Reported on one JSON line: whole-job throughput in algorithmic HBM GB/s (each
 input read once, the output written once), tokens*channels/s, the roofline
-record of the scan kernel (kernel time from HIP events recorded around every
-launch on the launch stream; HBM traffic from the committed rocprofv3 counter
-summary when it belongs to the current kernel source), and the fp64 CPU
-oracle timed on the host's cores on the same workload.
+record of the scan kernel (kernel time from HIP events on the launch stream:
+around each replay of the graph of the K timed launches, over K, for the
+graph-replayed steps, else around every launch; HBM traffic from the
+committed rocprofv3 counter summary when it belongs to the current kernel
+source), and the fp64 CPU oracle timed on the host's cores on the same
+workload.
 
 Inputs are resident in HBM before timing; the step cycles through several
 independent input sets so that consecutive steps cannot be served from the
@@ -22,6 +24,7 @@ K timed steps and replayed; the others launch eagerly (`launch` in config).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -81,6 +84,9 @@ def parse():
                     help="zero-order-hold input coefficient instead of dt (the released model uses dt)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="configs 0-2: another batch size at the same shape (0 = the config's); "
+                         "the kernel time against batch shows how the launch fills the chip")
     ap.add_argument("--seed", type=int, default=1001)
     ap.add_argument("--valu-probe", action="store_true",
                     help="instead of the benchmark, run the VALU issue-rate probe (libvmprobe.so) and print "
@@ -108,7 +114,8 @@ PROBE_KINDS = ["fma", "exp", "exp+3fma", "state-step-dpp", "state-step-dpp-no-ex
                "exp-latency", "fma-latency", "fma-3vgpr", "mul-2vgpr", "mul-sgpr", "fmac-sgpr", "mul-dpp",
                "state-step-sgpr", "state-step-sgpr-no-exp", "exp-waves+fma-waves", "state-step-vgpr",
                "state-step-vgpr-no-exp", "phased-2w-barrier", "phased-2w", "phased-4w-barrier", "phased-4w",
-               "fetch-straight-4096", "fetch-loop-64x64"]
+               "fetch-straight-4096", "fetch-loop-64x64", "state-step-vgpr-exp-groups-16",
+               "state-step-vgpr-exp-groups-32", "state-step-vgpr-exp-groups-64"]
 SIMDS = 256 * 4
 
 
@@ -186,7 +193,7 @@ def algorithmic_bytes_scan(batch, dim, L, N, es, dirs, gated):
     return dirs * per_dir + (tok * es if gated else 0) + tok * es
 
 
-def build_step(cfg, seed, sets, dev, zoh=False, conv="none", es2d_size=56):
+def build_step(cfg, seed, sets, dev, zoh=False, conv="none", es2d_size=56, batch=0):
     """Returns (step_fn(i), info dict, cpu_fn(budget_s) -> (seconds, bytes, tokens, threads, desc))."""
     import torch
 
@@ -196,6 +203,8 @@ def build_step(cfg, seed, sets, dev, zoh=False, conv="none", es2d_size=56):
     N = wl.DSTATE
     if cfg in (0, 1, 2):
         w = wl.WORKLOADS[cfg]
+        if batch:
+            w = dataclasses.replace(w, batch=batch, name=f"{w.name}@batch{batch}")
         dt = wl.torch_dtype(w.dtype)
         es = 2 if w.dtype == "bf16" else 4
         dirs = 2 if w.kind == "bidir" else 1
@@ -568,8 +577,10 @@ def main():
     sets = args.sets or (3 if args.config in (0, 1, 2, 3, 6, 7) else 1)
     if args.conv != "none" and args.config not in (0, 1, 2):
         raise SystemExit("--conv applies to configs 0-2")
+    if args.batch and args.config not in (0, 1, 2):
+        raise SystemExit("--batch applies to configs 0-2")
     step, info, cpu_fn, nbytes, tokens, slots = build_step(args.config, args.seed, sets, dev, args.zoh,
-                                                           args.conv, args.size)
+                                                           args.conv, args.size, args.batch)
     if args.zoh:
         info = dict(info, discretization="zoh")
     torch.cuda.synchronize()
@@ -630,6 +641,7 @@ def main():
         graph.replay()                                  # one untimed replay
         torch.cuda.synchronize()
     walls = []
+    graph_ms = []      # HIP events on the launch stream around each replay of the K steps
     for r in range(args.replays):
         if graph is None and r == 0:
             walls.append(eager_wall)
@@ -637,20 +649,31 @@ def main():
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         if graph is not None:
+            g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g0.record(stream)
             graph.replay()
+            g1.record(stream)
         else:
             for i in range(args.steps):
                 step(i)
         torch.cuda.synchronize()
         walls.append(time.perf_counter() - t0)
+        if graph is not None:
+            graph_ms.append(g0.elapsed_time(g1) / args.steps)
     walls.sort()
     wall = walls[len(walls) // 2]
+    graph_ms.sort()
     info["launch"] = "hip-graph" if use_graph else "eager"
 
     ms_per_step = 1e3 * wall / args.steps
     value = nbytes / (wall / args.steps) / 1e9
-    achieved_gbs = nbytes / (launch_ms * 1e-3) / 1e9
-    achieved_updates = slots / (launch_ms * 1e-3) / 1e12
+    # Kernel time of the roofline: in a replayed graph, the launches of the
+    # timed region run back to back, and events around each replay over K
+    # give their mean duration (median replay); eager steps take the mean of
+    # the per-launch events.
+    roof_ms = graph_ms[len(graph_ms) // 2] if graph_ms else launch_ms
+    achieved_gbs = nbytes / (roof_ms * 1e-3) / 1e9
+    achieved_updates = slots / (roof_ms * 1e-3) / 1e12
     src_hash = kernel_source_hash()
     variant = ("+zoh" if args.zoh else "") + (f"+conv-{args.conv}" if args.conv != "none" else "")
     traffic = load_traffic(src_hash, info["workload"] + variant)
@@ -685,6 +708,8 @@ def main():
         "config": dict(info, input_sets=sets),
         "tokens_ch_per_s": round(tokens / (wall / args.steps), 1),
         "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "kernel_ms": round(roof_ms, 5),
+        "kernel_ms_from": "graph-replay events / K" if graph_ms else "per-launch events (eager)",
         "kernel_ms_events": round(launch_ms, 5),
         "kernel_ms_events_median": round(launch_med, 5),
         "kernel_ms_events_min": round(per_launch[0], 5),

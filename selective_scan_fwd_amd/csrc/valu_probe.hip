@@ -32,6 +32,11 @@
 //         waves per SIMD from one workgroup; with and without the barrier)
 //   22-23 instruction fetch: 4096 fma as straight-line code run once, or as
 //         a loop of 64
+//   24-26 the state step with every operand in VGPRs (as 16), its
+//         exponentials grouped per wave: each iteration first takes the
+//         exponentials of 1, 2 or 4 steps (16, 32 or 64 in a row), then the
+//         writes, state updates and readouts of those steps; no barrier, so
+//         the waves sharing a SIMD drift in and out of phase
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -343,6 +348,46 @@ __global__ void __launch_bounds__(probe_threads(KIND)) probe_kernel(const float 
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc += h[j];
+  } else if constexpr (KIND >= 24 && KIND <= 26) {
+    constexpr int QS = KIND == 24 ? 1 : KIND == 25 ? 2 : 4;   // steps per group
+    float h[16], a2[16], bv[16], cv[16], e[QS][16], dt[QS], dtu[QS];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      h[j] = 0.0f;
+      a2[j] = opaque(-(j + 1) * 1.4426950408889634f);
+      bv[j] = opaque(in[j]);
+      cv[j] = opaque(in[16 + j]);
+    }
+#pragma unroll
+    for (int q = 0; q < QS; ++q) {
+      dt[q] = 0.01f + 0.0001f * (lane + q);
+      dtu[q] = s * dt[q];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) e[q][j] = dt[q] * a2[j];
+    }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int q = 0; q < QS; ++q)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) e[q][j] = __builtin_amdgcn_exp2f(e[q][j]);
+      __builtin_amdgcn_sched_barrier(0);     // the compiler keeps the groups apart
+#pragma unroll
+      for (int q = 0; q < QS; ++q) {
+        dt[q] = opaque(dt[q]);
+        dtu[q] = opaque(dtu[q]);
+        float y = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          h[j] = __builtin_fmaf(e[q][j], h[j], dtu[q] * bv[j]);
+          y = __builtin_fmaf(cv[j], h[j], y);
+          e[q][j] = dt[q] * a2[j];
+        }
+        acc += y;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc += h[j];
   } else if constexpr (KIND == 22 || KIND == 23) {
     // instruction fetch: 4096 independent v_fma_f32 as straight-line code
     // run once (22), or as 64 passes of a 64-instruction loop (23)
@@ -407,8 +452,8 @@ extern "C" {
 
 // Wave-instructions per iteration of each body, as in its disassembly
 // (loop control excluded): VALU forms only.
-const int kProbeInstr[24] = {64, 64, 64, 168, 168, 32, 64, 64, 64, 64, 64, 64, 64, 162, 162, 64, 162, 162,
-                             324, 324, 324, 324, 4096, 64};
+const int kProbeInstr[27] = {64, 64, 64, 168, 168, 32, 64, 64, 64, 64, 64, 64, 64, 162, 162, 64, 162, 162,
+                             324, 324, 324, 324, 4096, 64, 97, 162, 324};
 
 // Runs probe `kind` on `blocks` workgroups of vm_probe_threads(kind)
 // threads for `iters` iterations.  in: 64 floats (device); out: blocks *
@@ -445,11 +490,14 @@ int vm_probe_run(int kind, int blocks, int iters, const void *in, void *out, voi
     case 21: return launch<21>(blocks, iters, i, o, c, s);
     case 22: return launch<22>(blocks, iters, i, o, c, s);
     case 23: return launch<23>(blocks, iters, i, o, c, s);
+    case 24: return launch<24>(blocks, iters, i, o, c, s);
+    case 25: return launch<25>(blocks, iters, i, o, c, s);
+    case 26: return launch<26>(blocks, iters, i, o, c, s);
     default: return 1;
   }
 }
 
-int vm_probe_instr(int kind) { return kind >= 0 && kind < 24 ? kProbeInstr[kind] : 0; }
+int vm_probe_instr(int kind) { return kind >= 0 && kind < 27 ? kProbeInstr[kind] : 0; }
 int vm_probe_threads(int kind) { return probe_threads(kind); }
 
 }  // extern "C"
