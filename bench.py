@@ -73,8 +73,10 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="input sets to cycle (0 = auto)")
     ap.add_argument("--size", type=int, default=56, choices=[56, 57],
                     help="config 3: the ES2D feature map (56x56, or 57x57 padded to 58x58)")
-    ap.add_argument("--replays", type=int, default=5,
-                    help="times the K timed steps are run (graph replays, or eager passes); the median is reported")
+    ap.add_argument("--replays", type=int, default=0,
+                    help="times the K timed steps are run (graph replays, or eager passes); the median is "
+                         "reported (0 = at least 5, and at least 1000 steps in all: short passes of a few "
+                         "milliseconds run on a GPU whose clock is still rising)")
     ap.add_argument("--conv", choices=["none", "fused", "unfused"], default="none",
                     help="configs 0-2: the scan input comes from the block's causal conv1d + SiLU, "
                          "computed inside the scan (fused) or by vm_causal_conv1d_silu first (unfused)")
@@ -642,7 +644,8 @@ def main():
         torch.cuda.synchronize()
     walls = []
     graph_ms = []      # HIP events on the launch stream around each replay of the K steps
-    for r in range(args.replays):
+    replays = args.replays or max(5, -(-1000 // args.steps))
+    for r in range(replays):
         if graph is None and r == 0:
             walls.append(eager_wall)
             continue
