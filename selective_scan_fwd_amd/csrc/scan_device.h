@@ -85,6 +85,16 @@ template <> __device__ __forceinline__ void bstore<bf16_t>(Rsrc r, uint32_t off,
   __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(from_f32<bf16_t>(v)), r,
                                         static_cast<int>(off), 0, 0);
 }
+// The same with a wave-uniform byte offset added in the scalar operand.
+template <typename Tin> __device__ __forceinline__ void bstore_s(Rsrc r, uint32_t off, uint32_t soff, float v);
+template <> __device__ __forceinline__ void bstore_s<float>(Rsrc r, uint32_t off, uint32_t soff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, static_cast<int>(off),
+                                        static_cast<int>(soff), 0);
+}
+template <> __device__ __forceinline__ void bstore_s<bf16_t>(Rsrc r, uint32_t off, uint32_t soff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(from_f32<bf16_t>(v)), r,
+                                        static_cast<int>(off), static_cast<int>(soff), 0);
+}
 // Four consecutive fp32 values at a 16-byte aligned offset, in one access.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void bstore4(Rsrc r, uint32_t off, const float (&v)[4]) {

@@ -348,10 +348,16 @@ scan_kernel(const ScanArgs p) {
   // in flight.
   float ru[NB][PE], rd[NB][PE], rb[NB][BQ], rc[NB][BQ];
 
-  auto stage_load = [&](int k, auto par) __attribute__((always_inline)) {
+  // Steps past L must stage u = 0 only where they come before real steps
+  // of the visit: in the first tile of a reversed visit, which the prologue
+  // loads.  Later tiles take the plain offsets: past L the slab's last row
+  // reads 0 (its offsets leave the slab), the others the next row's values,
+  // which only feed states after the last real step and outputs that land
+  // in the exchange rows' padding or are masked at the store.
+  auto stage_load = [&](int k, auto par, auto masked) __attribute__((always_inline)) {
     constexpr int Q = decltype(par)::value;
     const int jT = tile_of(k) * T;
-    const bool in_seq = tq < L - jT;
+    const bool in_seq = !decltype(masked)::value || tq < L - jT;
 #pragma unroll
     for (int i = 0; i < PE; ++i) {
       const uint32_t o = tok_off(i, jT, in_seq);
@@ -524,7 +530,7 @@ scan_kernel(const ScanArgs p) {
   auto iteration = [&](int k, auto slot, auto second) __attribute__((always_inline)) {
     using Qn = std::integral_constant<int, (decltype(slot)::value + 1) % NB>;
     comb_load(k + 1 < nt ? k + 1 : nt - 1, Qn(), second);
-    stage_load(k + NB < nt ? k + NB : nt - 1, slot);
+    stage_load(k + NB < nt ? k + NB : nt - 1, slot, std::false_type());
     if constexpr (CKS && T == kBwdTile) store_ck(tile_of(k));
     wave_lds_fence();                    // staged tile k read back before its partials overwrite it
     do_scan(k);
@@ -552,7 +558,7 @@ scan_kernel(const ScanArgs p) {
 
   // First tiles, then the parameters, all in flight together.
   for_slots<NB>([&](auto s) __attribute__((always_inline)) {
-    stage_load(decltype(s)::value < nt ? decltype(s)::value : nt - 1, s);
+    stage_load(decltype(s)::value < nt ? decltype(s)::value : nt - 1, s, std::true_type());
   });
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
@@ -605,7 +611,26 @@ scan_kernel(const ScanArgs p) {
   // elements per thread per pass keep those loads in flight together (the
   // scan's registers are free by now).  (Done here rather than per tile in
   // the scan loop, whose issue slots the extra exponentials would take.)
-  if (XMODE == kXLds) {
+  if (XMODE == kXLds && !CK) {
+    // Row by row (rows are consecutive in out, L values each): thread tid
+    // takes steps tid + c NT of every row, so the addresses are a lane
+    // offset per pass plus a per-row constant (an LDS immediate, a scalar
+    // store offset).
+    lds_barrier();
+    constexpr int NT = 64 * DIRS;
+    const int tid = static_cast<int>(threadIdx.x) - sub * NT;
+    for (int t0 = 0; t0 < L; t0 += NT) {     // uniform passes
+      const int t = t0 + tid;
+      const bool in = t < L;
+      const uint32_t o = in ? static_cast<uint32_t>(t) * ES : kOob;
+      const float *const xc = xlds + (in ? t : 0);
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) {
+        if (rr < rows)
+          bstore_s<Tin>(rO, o, static_cast<uint32_t>(rr) * static_cast<uint32_t>(L) * ES, xc[rr * XS]);
+      }
+    }
+  } else if (XMODE == kXLds) {
     lds_barrier();
     constexpr int NT = 64 * DIRS, U = CK ? 16 : 4;
     const int n = rows * L;

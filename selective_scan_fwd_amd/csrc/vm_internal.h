@@ -42,11 +42,19 @@ __device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(
 // error of s, which removes it to first order; leaving out its division by s
 // changes the result by at most 2^-24 * e / (1 + e), below fp32 resolution of
 // log1p(e).  Small e thus keeps full relative accuracy.
+// (max(x, 0) is one v_max_f32: written as fmaxf it would first quiet a
+// signalling NaN in x with an extra instruction, which a NaN input does not
+// need here, since the log term is NaN then too.)
+__device__ __forceinline__ float relu_f(float x) {
+  float r;
+  asm("v_max_f32 %0, 0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
 __device__ __forceinline__ float softplus_f(float x) {
   float e = hw_exp2(-__builtin_fabsf(x) * kLog2e);
   float s = 1.0f + e;
   float corr = (s - 1.0f) - e;
-  return __builtin_fmaxf(x, 0.0f) + __builtin_fmaf(hw_log2(s), kLn2, -corr);
+  return relu_f(x) + __builtin_fmaf(hw_log2(s), kLn2, -corr);
 }
 
 // SiLU(z) = z * sigmoid(z) = z / (1 + e^-z).
