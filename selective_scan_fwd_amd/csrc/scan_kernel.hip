@@ -606,11 +606,11 @@ scan_kernel(const ScanArgs p) {
   run(n1, nt, Second());
 
   // ---- short sequences: the block's [rows x L] slab of out is complete in
-  // LDS (scaled and gated); write it in flat order (coalesced, whole lines).
-  // With the backward preparation each element also loads z and dout: 16
-  // elements per thread per pass keep those loads in flight together (the
-  // scan's registers are free by now).  (Done here rather than per tile in
-  // the scan loop, whose issue slots the extra exponentials would take.)
+  // LDS (scaled and gated); write it out with coalesced stores.  With the
+  // backward preparation each element also loads z and dout, in flat order:
+  // 16 elements per thread per pass keep those loads in flight together
+  // (the scan's registers are free by now).  (Done here rather than per tile
+  // in the scan loop, whose issue slots the extra exponentials would take.)
   if (XMODE == kXLds && !CK) {
     // Row by row (rows are consecutive in out, L values each): thread tid
     // takes steps tid + c NT of every row, so the addresses are a lane
